@@ -1,0 +1,228 @@
+"""Pins for the oracle's pool placement, gather and fp64 attention.
+
+Checks against: the direct quantization of the inputs (gather must return
+exactly those bytes), page-table permutation invariance, sentinel bytes,
+a negative control, pure-Python brute-force softmax on tiny contexts,
+scipy's Hadamard matrix, closed forms (one cell, zero query, two cells),
+the rotate-before / un-rotate-after identity on unquantized data, and the
+GQA head mapping.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+from long_context_decode_append_amd import synth
+
+H_SCI = scipy.linalg.hadamard(256).astype(np.float64)
+
+
+def _pool_with(orc, fmt, P, n_pages, n_table, n_tok, seed, identity=False, dtype=np.float16):
+    pt = synth.page_table(seed, n_table, n_pages, identity=identity)
+    k, v = synth.kv_tokens(seed, 0, 0, n_tok, 2, 256, dtype)
+    pool = orc.OraclePool(fmt, n_pages, P, 2)
+    pool.append(pt, k, v, 0)
+    return pool, pt, k, v
+
+
+# ------------------------------------------------------------------ placement and gather
+
+@pytest.mark.parametrize("fmt", [3, 1, 2])
+def test_gather_returns_direct_quantization(orc, fmt):
+    pool, pt, k, v = _pool_with(orc, fmt, P=16, n_pages=12, n_table=10, n_tok=150, seed=1)
+    g = pool.gather(pt, 0, 150)
+    kf, vf = k.astype(np.float32), v.astype(np.float32)
+    if fmt == 3:
+        kc, ks = orc.quant_int8(kf)
+        vb = orc.quant_q4(orc.fwht256(vf))
+        exp = (kc, ks, vb)
+    elif fmt == 1:
+        kc, ks = orc.quant_int8(kf)
+        vc, vs = orc.quant_int8(vf)
+        exp = (kc, ks, vc, vs)
+    else:
+        exp = (orc.quant_q4(orc.fwht256(kf)), orc.quant_q4(orc.fwht256(vf)))
+    assert len(g) == len(exp)
+    for a, b in zip(g, exp):
+        assert a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_pool_bytes_at_documented_offsets(orc):
+    P, H = 16, 2
+    pool, pt, k, v = _pool_with(orc, 3, P=P, n_pages=6, n_table=5, n_tok=70, seed=2)
+    kc, ks, vb = pool.gather(pt, 0, 70)
+    r0, r1, r2, _ = pool.runs
+    for p in (0, 1, 15, 16, 33, 69):
+        page, slot = pt[p // P], p % P
+        for g in range(H):
+            cell = (page * H + g) * P + slot
+            assert np.array_equal(r0[cell * 256:(cell + 1) * 256].view(np.int8), kc[p, g])
+            assert np.array_equal(r1[cell * 8:(cell + 1) * 8].view(np.float32), ks[p, g])
+            tile = (page * H + g) * 144 * P
+            for b in range(8):
+                q = r2[tile + slot * 128 + b * 16: tile + slot * 128 + b * 16 + 16]
+                s = r2[tile + 128 * P + (b * P + slot) * 2: tile + 128 * P + (b * P + slot) * 2 + 2]
+                assert np.array_equal(q, vb[p, g, b, 2:]) and np.array_equal(s, vb[p, g, b, :2])
+
+
+def test_identity_vs_permuted_page_table(orc):
+    a, pta, _, _ = _pool_with(orc, 3, P=16, n_pages=8, n_table=8, n_tok=128, seed=3, identity=True)
+    b, ptb, _, _ = _pool_with(orc, 3, P=16, n_pages=8, n_table=8, n_tok=128, seed=3)
+    assert not np.array_equal(pta, ptb)
+    for x, y in zip(a.gather(pta, 0, 128), b.gather(ptb, 0, 128)):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+    # the images are equal up to the page permutation
+    per_page = [16 * 2 * 256, 16 * 2 * 8, 16 * 2 * 144]
+    for r in range(3):
+        ra = a.runs[r].reshape(8, per_page[r])
+        rb = b.runs[r].reshape(8, per_page[r])
+        assert np.array_equal(ra[pta], rb[ptb])
+
+
+def test_unwritten_cells_keep_sentinel_and_wrong_table_is_detected(orc):
+    P = 16
+    pool, pt, _, _ = _pool_with(orc, 3, P=P, n_pages=10, n_table=6, n_tok=40, seed=4)
+    used = set(int(x) for x in pt[:3])            # 40 tokens touch 3 pages, the third partly
+    r0 = pool.runs[0].reshape(10, 2, P, 256)
+    for page in range(10):
+        if page not in used:
+            assert np.all(r0[page] == 0xA5)
+    third = int(pt[2])
+    assert np.all(r0[third, :, 8:] == 0xA5) and not np.any(np.all(r0[third, :, :8] == 0xA5, axis=-1))
+    # negative control: a table with two entries swapped reads other bytes
+    bad = pt.copy()
+    bad[[0, 1]] = bad[[1, 0]]
+    good = pool.gather(pt, 0, 32)
+    wrong = pool.gather(bad, 0, 32)
+    assert not np.array_equal(good[0], wrong[0])
+
+
+def test_append_in_pieces_equals_one_call(orc):
+    pt = synth.page_table(5, 8, 8)
+    k, v = synth.kv_tokens(5, 0, 0, 100, 2, 256)
+    a = orc.OraclePool(3, 8, 16, 2)
+    a.append(pt, k, v, 0)
+    b = orc.OraclePool(3, 8, 16, 2)
+    for s, e in ((0, 1), (1, 17), (17, 50), (50, 100)):
+        b.append(pt, k[s:e], v[s:e], s)
+    for x, y in zip(a.runs, b.runs):
+        if x is not None:
+            assert np.array_equal(x, y)
+
+
+def test_out_of_range_append_is_rejected(orc):
+    pool = orc.OraclePool(3, 4, 16, 2)
+    pt = np.arange(4, dtype=np.int32)
+    k = np.zeros((10, 2, 256), np.float16)
+    with pytest.raises(ValueError):
+        pool.append(pt, k, k, 60)
+
+
+# ------------------------------------------------------------------ attention
+
+def _brute(kd, vd, q, n, scale, rotated=True):
+    """Pure-Python softmax attention for one (row, head) pair, fp64."""
+    s = [scale * sum(float(q[c]) * kd[t][c] for c in range(256)) for t in range(n)]
+    mx = max(s)
+    w = [math.exp(x - mx) for x in s]
+    W = sum(w)
+    u = [sum(w[t] * vd[t][c] for t in range(n)) / W for c in range(256)]
+    u = np.array(u)
+    return H_SCI @ u / 16.0 if rotated else u
+
+
+def test_attention_matches_brute_force_tiny(orc):
+    pool, pt, _, _ = _pool_with(orc, 3, P=16, n_pages=2, n_table=2, n_tok=6, seed=6)
+    q = synth.queries(6, 0, 0, 1, 16, 256, np.float16)
+    kd, vd = orc.dequant_gathered(3, pool.gather(pt, 0, 6))
+    for n in (1, 2, 3, 6):
+        out = orc.attention(kd, vd, q, [n])
+        for h in (0, 7, 8, 15):
+            g = h // 8
+            ref = _brute(kd[:, g].tolist(), vd[:, g].tolist(), q[0, h], n, 1 / 16)
+            assert np.allclose(out[0, h], ref, rtol=0, atol=1e-12)
+
+
+def test_one_cell_returns_unrotated_value(orc):
+    rng = np.random.default_rng(0)
+    kd = rng.standard_normal((5, 2, 256))
+    vd = rng.standard_normal((5, 2, 256))
+    q = rng.standard_normal((1, 16, 256)).astype(np.float32)
+    out = orc.attention(kd, vd, q, [1])
+    for h in range(16):
+        assert np.allclose(out[0, h], H_SCI @ vd[0, h // 8] / 16, atol=1e-13)
+
+
+def test_zero_query_averages_and_two_cell_closed_form(orc):
+    rng = np.random.default_rng(1)
+    kd = rng.standard_normal((9, 2, 256))
+    vd = rng.standard_normal((9, 2, 256))
+    q0 = np.zeros((1, 16, 256), np.float32)
+    out = orc.attention(kd, vd, q0, [9], v_rotated=False)
+    assert np.allclose(out[0, 3], vd[:, 0].mean(0), atol=1e-13)
+    assert np.allclose(out[0, 12], vd[:, 1].mean(0), atol=1e-13)
+    q = rng.standard_normal((1, 16, 256)).astype(np.float32)
+    out = orc.attention(kd, vd, q, [2], scale=0.05, v_rotated=False)
+    for h in (0, 9):
+        g = h // 8
+        s0 = 0.05 * float(q[0, h].astype(np.float64) @ kd[0, g])
+        s1 = 0.05 * float(q[0, h].astype(np.float64) @ kd[1, g])
+        w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+        assert np.allclose(out[0, h], w0 * vd[0, g] + (1 - w0) * vd[1, g], atol=1e-13)
+
+
+def test_rotate_before_unrotate_after_identity(orc):
+    """(1/16) H attn(q, K, (H/16) V) equals attn(q, K, V) on unquantized data."""
+    rng = np.random.default_rng(2)
+    kd = rng.standard_normal((40, 2, 256))
+    vd = rng.standard_normal((40, 2, 256))
+    q = rng.standard_normal((3, 16, 256)).astype(np.float32)
+    vrot = vd @ H_SCI.T / 16
+    a = orc.attention(kd, vd, q, [40, 17, 1], v_rotated=False)
+    b = orc.attention(kd, vrot, q, [40, 17, 1], v_rotated=True)
+    assert np.allclose(a, b, atol=1e-12)
+    # q4_0 format: rotating both q and K leaves the scores unchanged
+    krot = kd @ H_SCI.T / 16
+    c = orc.attention(krot, vrot, q, [40, 17, 1], q_rotate=True, v_rotated=True)
+    assert np.allclose(a, c, atol=1e-12)
+
+
+def test_rows_with_step_limits_match_single_rows(orc):
+    """Batched rows with a per-row step array equal one-row calls (the
+    verify form against the decode form) and the prefill row rule."""
+    rng = np.random.default_rng(3)
+    kd = rng.standard_normal((30, 2, 256))
+    vd = rng.standard_normal((30, 2, 256))
+    q = rng.standard_normal((5, 16, 256)).astype(np.float32)
+    nv = [26, 27, 28, 29, 30]
+    batched = orc.attention(kd, vd, q, nv)
+    for i in range(5):
+        single = orc.attention(kd, vd, q[i:i + 1], [nv[i]])
+        assert np.array_equal(batched[i], single[0])
+
+
+def test_gqa_head_mapping(orc):
+    rng = np.random.default_rng(4)
+    kd = rng.standard_normal((7, 2, 256))
+    vd = np.zeros((7, 2, 256))
+    vd[:, 0] = 1.0
+    vd[:, 1] = -2.0
+    q = rng.standard_normal((1, 16, 256)).astype(np.float32)
+    out = orc.attention(kd, vd, q, [7], v_rotated=False)
+    assert np.allclose(out[0, :8], 1.0) and np.allclose(out[0, 8:], -2.0)
+
+
+def test_quantized_attention_close_to_exact(orc):
+    """Sanity: k8v4 attention stays near fp64 attention on the raw inputs."""
+    n = 512
+    pool, pt, k, v = _pool_with(orc, 3, P=16, n_pages=32, n_table=32, n_tok=n, seed=7)
+    q = synth.queries(7, 0, 0, 1, 16, 256, np.float16)
+    out = orc.attention_from_pool(pool, pt, q, [n])
+    exact = orc.attention(k.astype(np.float64), v.astype(np.float64), q, [n], v_rotated=False)
+    rel = np.abs(out - exact).max(-1) / np.abs(exact).max(-1)
+    assert rel.max() < 0.25            # 4-bit V: about 8 % noise per element
+    pool8, pt8, _, _ = _pool_with(orc, 1, P=16, n_pages=32, n_table=32, n_tok=n, seed=7)
+    out8 = orc.attention_from_pool(pool8, pt8, q, [n])
+    rel8 = np.abs(out8 - exact).max(-1) / np.abs(exact).max(-1)
+    assert rel8.max() < 0.03 and rel8.max() < rel.max()
