@@ -1,0 +1,216 @@
+/*
+ * k8v4.h -- C ABI of libk8v4.so: the hybrid "k8v4" quantized KV cache
+ * (INT8 K + Walsh-Hadamard-rotated Q4_0 V) and the fused attention that
+ * reads it, for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the pages
+ *   "#120 --kv k8v4: hybrid KV cache -- INT8 K + Hadamard-rotated Q4_0 V
+ *    (816 B/cell)"  (sections What, How, Tests)  and
+ *   "kv: --kv k8v4 streams with --kv-resident" (section How: a k8v4 block
+ *    is moved as three byte runs -- K codes, K scales, V q4_0).
+ *
+ * Conventions for every call below:
+ *   - Pointers named "device" are HIP device memory owned by the caller;
+ *     "host" pointers are read during the call only.  The library never
+ *     allocates, frees or synchronizes.
+ *   - Calls that take a stream only enqueue work on it (a hipStream_t, or
+ *     NULL for the null stream) and return; device faults surface at the
+ *     caller's next synchronization.
+ *   - Every call returns KV_OK (0) or a negative KV_ERR_* code and launches
+ *     nothing when it returns an error.  A required pointer that is NULL is
+ *     an error (KV_ERR_NULL), never a silent skip: the pages report silent
+ *     wrong output from writers that tested a pointer for presence and
+ *     skipped the write.
+ *   - Shapes supported: head_dim 256, query heads = 8 * KV heads (GQA 8),
+ *     page_size a positive multiple of 16.  Anything else is
+ *     KV_ERR_UNSUPPORTED.
+ *   - Page-table contents live in device memory and are the caller's
+ *     contract: entries must lie in [0, n_pages) and be distinct.  The
+ *     kernels never access memory through an out-of-range entry: appends
+ *     through one write nothing, attention rows that meet one return NaN.
+ *     kv_check_page_table() validates a table synchronously.
+ */
+#ifndef K8V4_H
+#define K8V4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* KV formats.  The numbering keeps k8v4 = 3, the number the pages give it
+ * in the engine's format enum ("kv: --kv k8v4 streams with --kv-resident",
+ * How).  1 and 2 are the int8 and q4_0 formats the pages compare against. */
+enum { KV_FMT_INT8 = 1, KV_FMT_Q4_0 = 2, KV_FMT_K8V4 = 3 };
+
+/* element type of K/V/q inputs */
+enum { KV_DTYPE_F16 = 0, KV_DTYPE_F32 = 1 };
+
+enum {
+  KV_OK = 0,
+  KV_ERR_NULL = -1,        /* a required pointer is NULL                       */
+  KV_ERR_SHAPE = -2,       /* inconsistent sizes (negative counts, ...)         */
+  KV_ERR_RANGE = -3,       /* positions / context outside the table or pool     */
+  KV_ERR_DTYPE = -4,       /* unknown dtype code                                */
+  KV_ERR_UNSUPPORTED = -5, /* format / head_dim / GQA / page size not supported */
+  KV_ERR_WORKSPACE = -6,   /* workspace missing or too small                    */
+  KV_ERR_ALIGN = -7,       /* a device pointer is not 16-byte aligned           */
+  KV_ERR_LAUNCH = -8       /* the HIP runtime refused a launch                  */
+};
+
+/*
+ * A paged cell pool.  Each run is one device allocation indexed
+ * [physical page][kv head][slot], P = page_size slots per page, D = 256.
+ *
+ * k8v4 (fmt 3), 816 bytes per cell for 2 KV heads (408 per head):
+ *   run[0] K codes  int8, byte ((page*H + g)*P + slot)*256 + c
+ *   run[1] K scales fp32, element ((page*H + g)*P + slot)*2 + j, one scale
+ *                   per 128 dims (j = c / 128)
+ *   run[2] V q4_0   one tile of 144*P bytes per (page, head) at
+ *                   (page*H + g)*144*P: the 16 nibble bytes of block b
+ *                   (dims 32b..32b+31, rotated basis) of a slot at
+ *                   slot*128 + b*16 (byte i = element i | element i+16 << 4),
+ *                   and the block's fp16 scale at 128*P + (b*P + slot)*2.
+ *   run[3] unused (may be NULL).
+ * Keeping a block's scale in a strip beside the nibbles (rather than in
+ * front of them) keeps every load 8- or 16-byte aligned; kv_gather returns
+ * the conventional 18-byte blocks.
+ */
+typedef struct kv_pool {
+  int32_t fmt;        /* KV_FMT_*                               */
+  int32_t n_pages;    /* physical pages held by each run        */
+  int32_t page_size;  /* cells per page, a multiple of 16       */
+  int32_t n_kv_heads; /* H                                      */
+  int32_t head_dim;   /* D, must be 256                         */
+  int32_t reserved;   /* set to 0                               */
+  void *run[4];       /* device pointers, 256-byte aligned      */
+} kv_pool;
+
+/* One sequence: logical page i of the sequence lives in physical page
+ * page_table[i].  Logical cell p is slot p % P of logical page p / P.   */
+typedef struct kv_seq {
+  const int32_t *page_table; /* device, [n_table] entries in [0, n_pages) */
+  int32_t n_table;           /* number of entries                         */
+  int32_t reserved;          /* set to 0                                  */
+} kv_seq;
+
+/* Bytes per cell for all KV heads: 816 (k8v4), 1056 (int8), 576 (q4_0) at
+ * 2 heads x 256 dims ("#120 --kv k8v4: hybrid KV cache", What).  0 when
+ * the format or head_dim is not supported. */
+size_t kv_cell_bytes(int fmt, int n_kv_heads, int head_dim);
+
+/* Bytes of run `run` (0..3) of a pool; 0 for an unused run. */
+size_t kv_run_bytes(int fmt, int run, int n_pages, int page_size, int n_kv_heads, int head_dim);
+
+/*
+ * Append n_tokens tokens at logical cells [pos0, pos0 + n_tokens) of a k8v4
+ * pool ("#120 --kv k8v4: hybrid KV cache", What and How; Tests: bitwise
+ * append through a non-identity page table).
+ *   k, v: device, [n_tokens][n_kv_heads][256], fp16 or fp32 (dtype), the
+ *         keys after any positional encoding.
+ * K per 128-dim group: d = max|x| / 127, code = round-half-even(x * (1/d))
+ * clamped to +-127 (d = 0 gives codes 0), stored unrotated with fp32 d.
+ * V per head: rotated by the 256-point Walsh-Hadamard transform scaled by
+ * 1/16 (butterflies in ascending stride order, fp32), then per 32-block:
+ * m = value of largest magnitude (first on ties), d = m / -8,
+ * code = min(15, trunc(y * (1/d) + 8.5)), fp16 d (round to nearest even).
+ * Errors: KV_ERR_NULL, _UNSUPPORTED (fmt != 3), _DTYPE, _RANGE (pos0 < 0,
+ * n_tokens < 0, or pos0 + n_tokens > n_table * page_size).
+ * n_tokens == 0 is a no-op returning KV_OK.
+ */
+int kv_append_k8v4(const kv_pool *pool, const kv_seq *seq, const void *k, const void *v,
+                   int dtype, int32_t pos0, int32_t n_tokens, void *stream);
+
+/*
+ * Copy the stored bytes of cells [pos0, pos0 + n) of a k8v4 pool, in
+ * logical order, to contiguous device buffers ("#120 --kv k8v4: hybrid KV
+ * cache", Tests: bitwise gather through a non-identity page table):
+ *   k_codes  int8  [n][H][256]
+ *   k_scales fp32  [n][H][2]
+ *   v_blocks uint8 [n][H][8][18]  (fp16 scale little-endian, then 16 bytes)
+ * Errors: KV_ERR_NULL, _UNSUPPORTED, _RANGE.
+ */
+int kv_gather(const kv_pool *pool, const kv_seq *seq, int32_t pos0, int32_t n, void *k_codes,
+              void *k_scales, void *v_blocks, void *stream);
+
+/*
+ * Device workspace needed by attn_decode / attn_verify for n_q query rows
+ * (1 for decode) over at most max_ctx cells: split-K partial results plus
+ * arrival counters.  The workspace must be zero-filled once before its
+ * first use (kv_workspace_init does it); the kernels leave the counters at
+ * zero after every completed call.  Calls that share a workspace must be
+ * ordered on one stream.
+ */
+size_t attn_workspace_bytes(const kv_pool *pool, int n_q_heads, int32_t n_q, int32_t max_ctx);
+
+/* Zero the counters of a workspace of ws_bytes bytes (a small fill kernel
+ * on `stream`, safe inside graph capture). */
+int kv_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * One decode step: the query attends to cells [0, n_ctx)
+ * ("#120 --kv k8v4: hybrid KV cache", How: the fused attention gathers the
+ * pages, reads K through the INT8 path and V through the rotated q4_0 path,
+ * and rotates the output back; q is never rotated).
+ *   q:   device, [n_q_heads][256], fp16 or fp32 (q_dtype)
+ *   out: device fp32 [n_q_heads][256]; head h uses KV head h / 8.
+ *   scale: softmax scale; <= 0 selects 1/sqrt(256).
+ * out = H/16 * softmax(scale * q K^T) V_rot, with K = code * d and
+ * V_rot = (code - 8) * d16 (fp32 accumulation).
+ * Errors: KV_ERR_NULL, _UNSUPPORTED, _DTYPE, _RANGE (n_ctx < 1 or beyond
+ * the table), _WORKSPACE.
+ */
+int attn_decode(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
+                int n_q_heads, int32_t n_ctx, float scale, float *out, void *ws,
+                size_t ws_bytes, void *stream);
+
+/*
+ * Verify window of speculative decoding: n_q query rows read the cache
+ * once, row i attending to cells [0, n_visible[i]) -- the batched form with
+ * a per-query step array ("#120 --kv k8v4: hybrid KV cache", Tests).
+ *   q:   device, [n_q][n_q_heads][256];  out: device fp32 [n_q][n_q_heads][256]
+ *   n_visible: host, [n_q], each in [1, n_table * page_size]
+ *   1 <= n_q <= 16.
+ * Errors as attn_decode, plus KV_ERR_SHAPE for n_q outside [1, 16].
+ */
+int attn_verify(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
+                int n_q_heads, int32_t n_q, const int32_t *n_visible, float scale, float *out,
+                void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Causal attention of a chunk of n_new new queries at logical positions
+ * [pos0, pos0 + n_new) over the cache, whose cells [0, pos0 + n_new) must
+ * already be appended; row i attends to cells [0, pos0 + i]
+ * ("#120 --kv k8v4: hybrid KV cache", How: the same fused attention serves
+ * prefill).  Dense contractions on the matrix cores (fp16 inputs, fp32
+ * accumulation).
+ *   q:   device, [n_new][n_q_heads][256];  out: device fp32 [n_new][n_q_heads][256]
+ * Needs no workspace (ws may be NULL).
+ * Errors: KV_ERR_NULL, _UNSUPPORTED, _DTYPE, _RANGE.
+ */
+int attn_prefill_chunk(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
+                       int n_q_heads, int32_t pos0, int32_t n_new, float scale, float *out,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Debug check of a page table (synchronous: copies the table to the host).
+ * Counts entries of the first ceil(n_cells / page_size) that are out of
+ * [0, n_pages) or repeated; writes the count to *n_bad.
+ * Errors: KV_ERR_NULL, _RANGE, _LAUNCH (copy failed).
+ */
+int kv_check_page_table(const kv_pool *pool, const kv_seq *seq, int32_t n_cells, int32_t *n_bad);
+
+/* Static description of an error code. */
+const char *kv_strerror(int code);
+
+/* Name and description of the HIP error behind the calling thread's most
+ * recent KV_ERR_LAUNCH ("no error" if there was none). */
+const char *kv_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* K8V4_H */

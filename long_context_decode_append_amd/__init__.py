@@ -1,0 +1,272 @@
+"""MI355X-native k8v4 KV cache and fused long-context attention.
+
+Thin Python binding over ``lib/libk8v4.so`` (the C ABI of
+``include/k8v4.h``).  This module only marshals arguments: torch tensors
+provide device memory and the current HIP stream, every step of the path
+runs in the library's HIP kernels.  There is no CPU fallback: when the
+library is missing every call raises.
+
+The format and operations follow the pages "#120 --kv k8v4: hybrid KV cache
+-- INT8 K + Hadamard-rotated Q4_0 V (816 B/cell)" (What, How, Tests) and
+"kv: --kv k8v4 streams with --kv-resident" (How).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libk8v4.so")
+
+KV_FMT_INT8, KV_FMT_Q4_0, KV_FMT_K8V4 = 1, 2, 3
+KV_DTYPE_F16, KV_DTYPE_F32 = 0, 1
+HEAD_DIM = 256
+GQA = 8
+
+
+class KvPoolStruct(C.Structure):
+    _fields_ = [("fmt", C.c_int32), ("n_pages", C.c_int32), ("page_size", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("reserved", C.c_int32),
+                ("run", C.c_void_p * 4)]
+
+
+class KvSeqStruct(C.Structure):
+    _fields_ = [("page_table", C.c_void_p), ("n_table", C.c_int32), ("reserved", C.c_int32)]
+
+
+# name -> (restype, argtypes); the exported symbols of include/k8v4.h
+_P, _I, _SZ, _F = C.c_void_p, C.c_int, C.c_size_t, C.c_float
+_PP, _PS = C.POINTER(KvPoolStruct), C.POINTER(KvSeqStruct)
+SIGNATURES = {
+    "kv_cell_bytes": (_SZ, [_I, _I, _I]),
+    "kv_run_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "kv_append_k8v4": (_I, [_PP, _PS, _P, _P, _I, C.c_int32, C.c_int32, _P]),
+    "kv_gather": (_I, [_PP, _PS, C.c_int32, C.c_int32, _P, _P, _P, _P]),
+    "attn_workspace_bytes": (_SZ, [_PP, _I, C.c_int32, C.c_int32]),
+    "kv_workspace_init": (_I, [_P, _SZ, _P]),
+    "attn_decode": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, _F, _P, _P, _SZ, _P]),
+    "attn_verify": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, _P, _F, _P, _P, _SZ, _P]),
+    "attn_prefill_chunk": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, C.c_int32, _F, _P, _P, _SZ, _P]),
+    "kv_check_page_table": (_I, [_PP, _PS, C.c_int32, _P]),
+    "kv_strerror": (C.c_char_p, [_I]),
+    "kv_last_hip_error": (C.c_char_p, []),
+}
+
+_lib = None
+
+
+class KvError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        detail = ""
+        if code == -8:
+            detail = f" [{lib().kv_last_hip_error().decode()}]"
+        super().__init__(f"{what}: {strerror(code)} ({code}){detail}")
+
+
+def lib():
+    """Load libk8v4.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        # torch ships its own HIP runtime (same soname as the system one):
+        # loading torch first makes libk8v4 bind to that runtime, so streams
+        # and device pointers from torch are valid in the library.
+        _torch()
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(there is no fallback path)")
+        handle = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().kv_strerror(code).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise KvError(rc, what)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _dev_ptr(t, name: str, dtypes=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return C.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return KV_DTYPE_F16
+    if t.dtype == torch.float32:
+        return KV_DTYPE_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def cell_bytes(fmt: int = KV_FMT_K8V4, n_kv_heads: int = 2, head_dim: int = HEAD_DIM) -> int:
+    return int(lib().kv_cell_bytes(fmt, n_kv_heads, head_dim))
+
+
+class K8V4Pool:
+    """A k8v4 paged pool in device memory: three runs (K codes, K scales, V q4_0)."""
+
+    def __init__(self, n_pages: int, page_size: int, n_kv_heads: int = 2, device="cuda",
+                 fill: int | None = None):
+        torch = _torch()
+        L = lib()
+        self.n_pages, self.page_size, self.n_kv_heads = n_pages, page_size, n_kv_heads
+        self.fmt = KV_FMT_K8V4
+        self.runs = []
+        for r in range(4):
+            nb = int(L.kv_run_bytes(self.fmt, r, n_pages, page_size, n_kv_heads, HEAD_DIM))
+            if nb == 0:
+                self.runs.append(None)
+                continue
+            t = torch.empty(nb, dtype=torch.uint8, device=device)
+            if fill is not None:
+                t.fill_(fill)
+            self.runs.append(t)
+        self._struct = KvPoolStruct(self.fmt, n_pages, page_size, n_kv_heads, HEAD_DIM, 0,
+                                    (C.c_void_p * 4)(*[None if t is None else t.data_ptr()
+                                                       for t in self.runs]))
+
+    @property
+    def struct(self) -> KvPoolStruct:
+        return self._struct
+
+    @property
+    def nbytes(self) -> int:
+        return sum(t.numel() for t in self.runs if t is not None)
+
+
+def _seq(page_table) -> KvSeqStruct:
+    torch = _torch()
+    if page_table.dtype != torch.int32:
+        raise ValueError("page_table must be int32")
+    return KvSeqStruct(_dev_ptr(page_table, "page_table"), page_table.numel(), 0)
+
+
+def kv_append_k8v4(pool: K8V4Pool, page_table, k, v, pos0: int, stream=None) -> None:
+    """Quantize and place k, v ([n][H][256], fp16 or fp32) at cells [pos0, pos0+n)."""
+    if k.shape != v.shape or k.dtype != v.dtype:
+        raise ValueError("k and v must have the same shape and dtype")
+    if k.dim() != 3 or k.shape[1] != pool.n_kv_heads or k.shape[2] != HEAD_DIM:
+        raise ValueError("k, v must be [n][n_kv_heads][256]")
+    seq = _seq(page_table)
+    rc = lib().kv_append_k8v4(C.byref(pool.struct), C.byref(seq), _dev_ptr(k, "k"),
+                              _dev_ptr(v, "v"), _dtype_code(k), int(pos0), int(k.shape[0]),
+                              _stream(stream))
+    _check(rc, "kv_append_k8v4")
+
+
+def kv_gather(pool: K8V4Pool, page_table, pos0: int, n: int, stream=None):
+    """Stored bytes of cells [pos0, pos0+n): (k_codes int8 [n][H][256],
+    k_scales fp32 [n][H][2], v_blocks uint8 [n][H][8][18])."""
+    torch = _torch()
+    H = pool.n_kv_heads
+    dev = pool.runs[0].device
+    kc = torch.empty((n, H, HEAD_DIM), dtype=torch.int8, device=dev)
+    ks = torch.empty((n, H, 2), dtype=torch.float32, device=dev)
+    vb = torch.empty((n, H, 8, 18), dtype=torch.uint8, device=dev)
+    seq = _seq(page_table)
+    rc = lib().kv_gather(C.byref(pool.struct), C.byref(seq), int(pos0), int(n), _dev_ptr(kc, "kc"),
+                         _dev_ptr(ks, "ks"), _dev_ptr(vb, "vb"), _stream(stream))
+    _check(rc, "kv_gather")
+    return kc, ks, vb
+
+
+def attn_workspace(pool: K8V4Pool, n_q: int, max_ctx: int, stream=None):
+    """Allocate and zero a workspace for decode (n_q = 1) or verify calls."""
+    torch = _torch()
+    nb = int(lib().attn_workspace_bytes(C.byref(pool.struct), GQA * pool.n_kv_heads, n_q, max_ctx))
+    if nb == 0:
+        raise ValueError("bad workspace request")
+    ws = torch.empty(nb, dtype=torch.uint8, device=pool.runs[0].device)
+    _check(lib().kv_workspace_init(_dev_ptr(ws, "ws"), nb, _stream(stream)), "kv_workspace_init")
+    return ws
+
+
+def attn_decode(pool: K8V4Pool, page_table, q, n_ctx: int, ws, scale: float = 0.0, out=None,
+                stream=None):
+    """q: [Hq][256] fp16/fp32 -> out fp32 [Hq][256], attending cells [0, n_ctx)."""
+    torch = _torch()
+    if q.dim() != 2 or q.shape[1] != HEAD_DIM:
+        raise ValueError("q must be [n_q_heads][256]")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    seq = _seq(page_table)
+    rc = lib().attn_decode(C.byref(pool.struct), C.byref(seq), _dev_ptr(q, "q"), _dtype_code(q),
+                           int(q.shape[0]), int(n_ctx), float(scale),
+                           _dev_ptr(out, "out", (torch.float32,)), _dev_ptr(ws, "ws"),
+                           ws.numel(), _stream(stream))
+    _check(rc, "attn_decode")
+    return out
+
+
+def attn_verify(pool: K8V4Pool, page_table, q, n_visible, ws, scale: float = 0.0, out=None,
+                stream=None):
+    """q: [n_q][Hq][256]; row i attends cells [0, n_visible[i]) -> out fp32 [n_q][Hq][256]."""
+    torch = _torch()
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [n_q][n_q_heads][256]")
+    n_q = int(q.shape[0])
+    nv = (C.c_int32 * n_q)(*[int(x) for x in n_visible])
+    if len(n_visible) != n_q:
+        raise ValueError("n_visible must have one entry per query row")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    seq = _seq(page_table)
+    rc = lib().attn_verify(C.byref(pool.struct), C.byref(seq), _dev_ptr(q, "q"), _dtype_code(q),
+                           int(q.shape[1]), n_q, nv, float(scale),
+                           _dev_ptr(out, "out", (torch.float32,)), _dev_ptr(ws, "ws"),
+                           ws.numel(), _stream(stream))
+    _check(rc, "attn_verify")
+    return out
+
+
+def attn_prefill_chunk(pool: K8V4Pool, page_table, q, pos0: int, scale: float = 0.0, out=None,
+                       stream=None):
+    """q: [n_new][Hq][256] at positions [pos0, pos0+n_new); row i attends [0, pos0+i]."""
+    torch = _torch()
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [n_new][n_q_heads][256]")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    seq = _seq(page_table)
+    rc = lib().attn_prefill_chunk(C.byref(pool.struct), C.byref(seq), _dev_ptr(q, "q"),
+                                  _dtype_code(q), int(q.shape[1]), int(pos0), int(q.shape[0]),
+                                  float(scale), _dev_ptr(out, "out", (torch.float32,)), None, 0,
+                                  _stream(stream))
+    _check(rc, "attn_prefill_chunk")
+    return out
+
+
+def check_page_table(pool: K8V4Pool, page_table, n_cells: int) -> int:
+    """Synchronous debug check: number of bad (out of range or repeated) entries."""
+    seq = _seq(page_table)
+    bad = C.c_int32(0)
+    _check(lib().kv_check_page_table(C.byref(pool.struct), C.byref(seq), int(n_cells),
+                                     C.byref(bad)), "kv_check_page_table")
+    return int(bad.value)

@@ -1,0 +1,199 @@
+// extern "C" entry points of libk8v4.so (declared in include/k8v4.h):
+// validate on the host, then enqueue the kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <vector>
+
+#include "launch.hpp"
+#include "validate.hpp"
+
+using namespace k8v4;
+
+static thread_local char g_last_hip_error[256] = "no error";
+
+namespace k8v4 {
+int launch_status() {
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return KV_OK;
+  snprintf(g_last_hip_error, sizeof g_last_hip_error, "%s: %s", hipGetErrorName(e),
+           hipGetErrorString(e));
+  return KV_ERR_LAUNCH;
+}
+}  // namespace k8v4
+
+extern "C" {
+
+size_t kv_cell_bytes(int fmt, int n_kv_heads, int head_dim) {
+  return cell_bytes(fmt, n_kv_heads, head_dim);
+}
+
+size_t kv_run_bytes(int fmt, int run, int n_pages, int page_size, int n_kv_heads, int head_dim) {
+  if (run < 0 || run > 3) return 0;
+  return run_bytes(fmt, run, n_pages, page_size, n_kv_heads, head_dim);
+}
+
+const char *kv_strerror(int code) {
+  switch (code) {
+    case KV_OK: return "ok";
+    case KV_ERR_NULL: return "a required pointer is NULL";
+    case KV_ERR_SHAPE: return "inconsistent sizes";
+    case KV_ERR_RANGE: return "positions or context outside the page table or pool";
+    case KV_ERR_DTYPE: return "unknown dtype";
+    case KV_ERR_UNSUPPORTED: return "unsupported format, head_dim, GQA ratio or page size";
+    case KV_ERR_WORKSPACE: return "workspace missing or too small";
+    case KV_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case KV_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown error";
+  }
+}
+
+const char *kv_last_hip_error(void) { return g_last_hip_error; }
+
+int kv_append_k8v4(const kv_pool *pool, const kv_seq *seq, const void *k, const void *v,
+                   int dtype, int32_t pos0, int32_t n_tokens, void *stream) {
+  if (int e = check_pool(pool, KV_FMT_K8V4)) return e;
+  if (int e = check_seq(seq, pool)) return e;
+  if (!k || !v) return KV_ERR_NULL;
+  if (int e = check_dtype(dtype)) return e;
+  if (int e = check_range(pool, seq, pos0, n_tokens)) return e;
+  if (check_aligned16(k) || check_aligned16(v)) return KV_ERR_ALIGN;
+  if (n_tokens == 0) return KV_OK;
+  return launch_append_k8v4(pool, seq, k, v, dtype, pos0, n_tokens, (hipStream_t)stream);
+}
+
+int kv_gather(const kv_pool *pool, const kv_seq *seq, int32_t pos0, int32_t n, void *k_codes,
+              void *k_scales, void *v_blocks, void *stream) {
+  if (int e = check_pool(pool, KV_FMT_K8V4)) return e;
+  if (int e = check_seq(seq, pool)) return e;
+  if (!k_codes || !k_scales || !v_blocks) return KV_ERR_NULL;
+  if (int e = check_range(pool, seq, pos0, n)) return e;
+  if (check_aligned16(k_codes) || ((uintptr_t)k_scales & 7u)) return KV_ERR_ALIGN;
+  if (n == 0) return KV_OK;
+  return launch_gather_k8v4(pool, seq, pos0, n, k_codes, k_scales, v_blocks, (hipStream_t)stream);
+}
+
+size_t attn_workspace_bytes(const kv_pool *pool, int n_q_heads, int32_t n_q, int32_t max_ctx) {
+  if (!pool || pool->n_kv_heads <= 0 || n_q < 1 || n_q > kMaxQ || max_ctx < 1) return 0;
+  if (n_q_heads != kGqa * pool->n_kv_heads) return 0;
+  return ws_bytes_bound(pool->n_kv_heads, n_q * kGqa, max_ctx);
+}
+
+int kv_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+  if (!ws) return KV_ERR_NULL;
+  if (check_aligned16(ws)) return KV_ERR_ALIGN;
+  return launch_fill_zero(ws, ws_bytes, (hipStream_t)stream);
+}
+
+static int check_attn_common(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
+                             int n_q_heads, const float *out) {
+  if (int e = check_pool(pool, KV_FMT_K8V4)) return e;
+  if (int e = check_seq(seq, pool)) return e;
+  if (!q || !out) return KV_ERR_NULL;
+  if (int e = check_dtype(q_dtype)) return e;
+  if (n_q_heads != kGqa * pool->n_kv_heads) return KV_ERR_UNSUPPORTED;
+  if (check_aligned16(q) || check_aligned16(out)) return KV_ERR_ALIGN;
+  return KV_OK;
+}
+
+static float pick_scale(float scale) {
+  return scale > 0.0f ? scale : 1.0f / std::sqrt((float)kHeadDim);
+}
+
+int attn_decode(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
+                int n_q_heads, int32_t n_ctx, float scale, float *out, void *ws,
+                size_t ws_bytes, void *stream) {
+  if (int e = check_attn_common(pool, seq, q, q_dtype, n_q_heads, out)) return e;
+  if (n_ctx < 1) return KV_ERR_RANGE;
+  if (int e = check_range(pool, seq, 0, n_ctx)) return e;
+  if (!ws) return KV_ERR_WORKSPACE;
+  if (check_aligned16(ws)) return KV_ERR_ALIGN;
+  AttnCall c;
+  c.pool = pool;
+  c.seq = seq;
+  c.q = q;
+  c.q_dtype = q_dtype;
+  c.n_q_heads = n_q_heads;
+  c.n_q = 1;
+  for (int i = 0; i < kMaxQ; i++) c.limits[i] = 0;
+  c.limits[0] = n_ctx;
+  c.max_limit = n_ctx;
+  c.scale = pick_scale(scale);
+  c.out = out;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  c.stream = (hipStream_t)stream;
+  return launch_attn_splitk(c);
+}
+
+int attn_verify(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
+                int n_q_heads, int32_t n_q, const int32_t *n_visible, float scale, float *out,
+                void *ws, size_t ws_bytes, void *stream) {
+  if (int e = check_attn_common(pool, seq, q, q_dtype, n_q_heads, out)) return e;
+  if (!n_visible) return KV_ERR_NULL;
+  if (n_q < 1 || n_q > kMaxQ) return KV_ERR_SHAPE;
+  if (!ws) return KV_ERR_WORKSPACE;
+  if (check_aligned16(ws)) return KV_ERR_ALIGN;
+  AttnCall c;
+  c.max_limit = 0;
+  for (int i = 0; i < kMaxQ; i++) c.limits[i] = 0;
+  for (int i = 0; i < n_q; i++) {
+    if (n_visible[i] < 1) return KV_ERR_RANGE;
+    if (int e = check_range(pool, seq, 0, n_visible[i])) return e;
+    c.limits[i] = n_visible[i];
+    if (n_visible[i] > c.max_limit) c.max_limit = n_visible[i];
+  }
+  c.pool = pool;
+  c.seq = seq;
+  c.q = q;
+  c.q_dtype = q_dtype;
+  c.n_q_heads = n_q_heads;
+  c.n_q = n_q;
+  c.scale = pick_scale(scale);
+  c.out = out;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  c.stream = (hipStream_t)stream;
+  return launch_attn_splitk(c);
+}
+
+int attn_prefill_chunk(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
+                       int n_q_heads, int32_t pos0, int32_t n_new, float scale, float *out,
+                       void *ws, size_t ws_bytes, void *stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (int e = check_attn_common(pool, seq, q, q_dtype, n_q_heads, out)) return e;
+  if (pos0 < 0 || n_new < 0) return KV_ERR_RANGE;
+  if (int e = check_range(pool, seq, 0, (int64_t)pos0 + n_new)) return e;
+  if (n_new == 0) return KV_OK;
+  return launch_attn_prefill(pool, seq, q, q_dtype, n_q_heads, pos0, n_new, pick_scale(scale), out,
+                             (hipStream_t)stream);
+}
+
+int kv_check_page_table(const kv_pool *pool, const kv_seq *seq, int32_t n_cells, int32_t *n_bad) {
+  if (int e = check_pool(pool, 0)) return e;
+  if (int e = check_seq(seq, pool)) return e;
+  if (!n_bad) return KV_ERR_NULL;
+  if (int e = check_range(pool, seq, 0, n_cells)) return e;
+  const int n_pages_used = (int)(((int64_t)n_cells + pool->page_size - 1) / pool->page_size);
+  std::vector<int32_t> host(n_pages_used > 0 ? n_pages_used : 1);
+  if (n_pages_used > 0 &&
+      hipMemcpy(host.data(), seq->page_table, sizeof(int32_t) * n_pages_used, hipMemcpyDeviceToHost) !=
+          hipSuccess)
+    return KV_ERR_LAUNCH;
+  std::vector<unsigned char> seen(pool->n_pages, 0);
+  int bad = 0;
+  for (int i = 0; i < n_pages_used; i++) {
+    const int p = host[i];
+    if (p < 0 || p >= pool->n_pages || seen[p]) {
+      bad++;
+      continue;
+    }
+    seen[p] = 1;
+  }
+  *n_bad = bad;
+  return KV_OK;
+}
+
+}  // extern "C"

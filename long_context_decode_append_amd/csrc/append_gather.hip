@@ -1,0 +1,226 @@
+// k8v4 append (quantize + place) and gather kernels for gfx950.
+//
+// Append follows "#120 --kv k8v4: hybrid KV cache -- INT8 K + Hadamard-
+// rotated Q4_0 V (816 B/cell)", sections What/How/Tests: K is stored as
+// INT8 codes with round-half-even and a scale per 128-dim group, unrotated;
+// V is rotated by the 256-point Walsh-Hadamard transform (scaled by 1/16)
+// and stored as Q4_0 blocks of 32 with an fp16 scale.  Cells are placed
+// through the page table.  One wave (64 lanes x 4 dims) handles one
+// (token, KV head) pair: K and V are quantized in the same pass, so there
+// is no duplicate write of a folded half.
+//
+// Every quantizer step is one IEEE fp32 operation rounded as written: this
+// file is built with -ffp-contract=off and the functions also disable
+// contraction locally, so x * r + 8.5 is never fused.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace k8v4 {
+
+struct AppendArgs {
+  int8_t *kc;      // run 0
+  float *ks;       // run 1
+  uint8_t *vq;     // run 2
+  const int32_t *pt;
+  const void *k;
+  const void *v;
+  int dtype;       // 0 fp16, 1 fp32
+  int pos0, n_tokens, n_pages, P, H;
+};
+
+__device__ __forceinline__ void load4(const void *base, int dtype, size_t idx, float x[4]) {
+  if (dtype == 0) {
+    const u32x2 w = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint16_t *>(base) + idx);
+    x[0] = f16_bits_to_f32((uint16_t)(w.x & 0xffff));
+    x[1] = f16_bits_to_f32((uint16_t)(w.x >> 16));
+    x[2] = f16_bits_to_f32((uint16_t)(w.y & 0xffff));
+    x[3] = f16_bits_to_f32((uint16_t)(w.y >> 16));
+  } else {
+    const f32x4 w = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(base) + idx);
+    x[0] = w.x; x[1] = w.y; x[2] = w.z; x[3] = w.w;
+  }
+}
+
+// INT8 rule on the 4 values of this lane; lanes 0-31 form group 0 (dims
+// 0..127), lanes 32-63 group 1.  Returns 4 packed codes and the scale.
+__device__ __forceinline__ uint32_t quant_k(const float x[4], float &d_out) {
+#pragma clang fp contract(off)
+  float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+  for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, lane_xor(amax, m));
+  const float d = amax / 127.0f;                 // correctly rounded division
+  const float r = (d != 0.0f) ? 1.0f / d : 0.0f;
+  uint32_t packed = 0;
+  for (int i = 0; i < 4; i++) {
+    float q = __builtin_rintf(x[i] * r);         // v_rndne_f32: nearest, ties to even
+    q = fminf(fmaxf(q, -127.0f), 127.0f);
+    packed |= ((uint32_t)(int)q & 0xffu) << (8 * i);
+  }
+  d_out = d;
+  return packed;
+}
+
+// Q4_0 rule on a 32-block spread over 8 lanes (4 values each).  Returns the
+// 4 codes of this lane packed as bytes and the fp16 scale bits.
+__device__ __forceinline__ uint32_t quant_q4(const float y[4], int lane, uint16_t &d16) {
+#pragma clang fp contract(off)
+  // value of largest magnitude, first index on ties
+  int bi = 0;
+  float bm = fabsf(y[0]);
+  for (int i = 1; i < 4; i++) {
+    const float a = fabsf(y[i]);
+    if (a > bm) { bm = a; bi = i; }
+  }
+  float bv = y[bi];
+  int bidx = 4 * (lane & 7) + bi;
+  for (int m = 1; m < 8; m <<= 1) {
+    const float om = lane_xor(bm, m);
+    const float ov = lane_xor(bv, m);
+    const int oi = lane_xor(bidx, m);
+    if (om > bm || (om == bm && oi < bidx)) { bm = om; bv = ov; bidx = oi; }
+  }
+  const float d = bv / -8.0f;
+  const float r = (d != 0.0f) ? 1.0f / d : 0.0f;
+  uint32_t codes = 0;
+  for (int i = 0; i < 4; i++) {
+    const float t = y[i] * r;
+    const float u = t + 8.5f;
+    int c = (int)u;                              // v_cvt_i32_f32 truncates toward zero
+    c = c > 15 ? 15 : c;
+    codes |= (uint32_t)c << (8 * i);
+  }
+  d16 = f32_to_f16_bits(d);
+  return codes;
+}
+
+__global__ __launch_bounds__(256) void append_k8v4_kernel(const AppendArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (token, head)
+  if (item >= (int64_t)a.n_tokens * a.H) return;                       // whole wave exits
+  const int t = (int)(item / a.H), g = (int)(item % a.H);
+  const int p = a.pos0 + t;
+  const int page = a.pt[p / a.P];
+  if (page < 0 || page >= a.n_pages) return;                           // never write outside the pool
+  const int slot = p % a.P;
+  const size_t src = ((size_t)t * a.H + g) * 256 + 4 * lane;
+  const size_t tile = (size_t)page * a.H + g;
+  const size_t cell = tile * a.P + slot;
+
+  float x[4];
+  load4(a.k, a.dtype, src, x);
+  float d;
+  const uint32_t kcodes = quant_k(x, d);
+  *reinterpret_cast<uint32_t *>(a.kc + cell * 256 + 4 * lane) = kcodes;
+  if ((lane & 31) == 0) a.ks[cell * 2 + (lane >> 5)] = d;
+
+  load4(a.v, a.dtype, src, x);
+  fwht256_lane4(x, lane);
+  uint16_t d16;
+  const uint32_t vcodes = quant_q4(x, lane, d16);
+  // byte i of a block = code[i] | code[i+16] << 4: lanes j < 4 of the block
+  // hold elements 4j..4j+3, lane j + 4 holds elements 16 + 4j..
+  const uint32_t hi = (uint32_t)__shfl_xor((int)vcodes, 4, 64);
+  const int b = lane >> 3, j = lane & 7;
+  uint8_t *vt = a.vq + tile * 144 * a.P;
+  if (j < 4) {
+    *reinterpret_cast<uint32_t *>(vt + (size_t)slot * 128 + b * 16 + 4 * j) = vcodes | (hi << 4);
+  }
+  if (j == 0) {
+    *reinterpret_cast<uint16_t *>(vt + (size_t)128 * a.P + ((size_t)b * a.P + slot) * 2) = d16;
+  }
+}
+
+struct GatherArgs {
+  const int8_t *kc;
+  const float *ks;
+  const uint8_t *vq;
+  const int32_t *pt;
+  int8_t *okc;
+  float *oks;
+  uint8_t *ovb;
+  int pos0, n, n_pages, P, H;
+};
+
+__global__ __launch_bounds__(256) void gather_k8v4_kernel(const GatherArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= (int64_t)a.n * a.H) return;
+  const int t = (int)(item / a.H), g = (int)(item % a.H);
+  const int p = a.pos0 + t;
+  int page = a.pt[p / a.P];
+  const bool bad = page < 0 || page >= a.n_pages;
+  const int slot = p % a.P;
+  const size_t tile = (size_t)(bad ? 0 : page) * a.H + g;
+  const size_t cell = tile * a.P + slot;
+  const size_t o = (size_t)t * a.H + g;
+  // an out-of-range table entry yields 0xff bytes / NaN scales, never a read outside the pool
+  uint32_t w = bad ? 0xffffffffu : *reinterpret_cast<const uint32_t *>(a.kc + cell * 256 + 4 * lane);
+  *reinterpret_cast<uint32_t *>(a.okc + o * 256 + 4 * lane) = w;
+  if (lane < 2) a.oks[o * 2 + lane] = bad ? __builtin_nanf("") : a.ks[cell * 2 + lane];
+  const uint8_t *vt = a.vq + tile * 144 * a.P;
+  for (int e = lane; e < 144; e += 64) {
+    const int b = e / 18, off = e % 18;
+    uint8_t byte;
+    if (off < 2) byte = vt[(size_t)128 * a.P + ((size_t)b * a.P + slot) * 2 + off];
+    else byte = vt[(size_t)slot * 128 + b * 16 + (off - 2)];
+    a.ovb[o * 144 + e] = bad ? 0xff : byte;
+  }
+}
+
+__global__ void fill_zero_kernel(uint32_t *p, size_t n_words) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+int launch_append_k8v4(const kv_pool *pool, const kv_seq *seq, const void *k, const void *v,
+                       int dtype, int pos0, int n, hipStream_t s) {
+  AppendArgs a;
+  a.kc = (int8_t *)pool->run[0];
+  a.ks = (float *)pool->run[1];
+  a.vq = (uint8_t *)pool->run[2];
+  a.pt = seq->page_table;
+  a.k = k;
+  a.v = v;
+  a.dtype = dtype;
+  a.pos0 = pos0;
+  a.n_tokens = n;
+  a.n_pages = pool->n_pages;
+  a.P = pool->page_size;
+  a.H = pool->n_kv_heads;
+  const int64_t items = (int64_t)n * a.H;
+  const unsigned blocks = (unsigned)((items + 3) / 4);
+  hipLaunchKernelGGL(append_k8v4_kernel, dim3(blocks), dim3(256), 0, s, a);
+  return launch_status();
+}
+
+int launch_gather_k8v4(const kv_pool *pool, const kv_seq *seq, int pos0, int n, void *okc,
+                       void *oks, void *ovb, hipStream_t s) {
+  GatherArgs a;
+  a.kc = (const int8_t *)pool->run[0];
+  a.ks = (const float *)pool->run[1];
+  a.vq = (const uint8_t *)pool->run[2];
+  a.pt = seq->page_table;
+  a.okc = (int8_t *)okc;
+  a.oks = (float *)oks;
+  a.ovb = (uint8_t *)ovb;
+  a.pos0 = pos0;
+  a.n = n;
+  a.n_pages = pool->n_pages;
+  a.P = pool->page_size;
+  a.H = pool->n_kv_heads;
+  const int64_t items = (int64_t)n * a.H;
+  const unsigned blocks = (unsigned)((items + 3) / 4);
+  hipLaunchKernelGGL(gather_k8v4_kernel, dim3(blocks), dim3(256), 0, s, a);
+  return launch_status();
+}
+
+int launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
+  const size_t words = bytes / 4;
+  if (words == 0) return KV_OK;
+  unsigned blocks = (unsigned)((words + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, s, (uint32_t *)p, words);
+  return launch_status();
+}
+
+}  // namespace k8v4

@@ -1,0 +1,46 @@
+// Kernel launchers of libk8v4 (host side; arguments already validated).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "validate.hpp"
+
+namespace k8v4 {
+
+// KV_OK after a successful launch, else KV_ERR_LAUNCH (the HIP error is kept
+// per thread for kv_last_hip_error).
+int launch_status();
+
+int launch_append_k8v4(const kv_pool *pool, const kv_seq *seq, const void *k, const void *v,
+                       int dtype, int pos0, int n, hipStream_t s);
+int launch_gather_k8v4(const kv_pool *pool, const kv_seq *seq, int pos0, int n, void *okc,
+                       void *oks, void *ovb, hipStream_t s);
+int launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+
+// Decode / verify: n_q query rows of 8 heads per KV head, row i of query
+// q_index attends to cells [0, limits[i]).
+struct AttnCall {
+  const kv_pool *pool;
+  const kv_seq *seq;
+  const void *q;
+  int q_dtype;
+  int n_q_heads;
+  int n_q;
+  int limits[kMaxQ];
+  int max_limit;
+  float scale;
+  float *out;
+  void *ws;
+  size_t ws_bytes;
+  hipStream_t stream;
+};
+int launch_attn_splitk(const AttnCall &c);
+
+// Target number of split-K workgroups per KV head on the current device.
+int attn_target_splits(int n_kv_heads, int n_rows);
+
+int launch_attn_prefill(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
+                        int n_q_heads, int pos0, int n_new, float scale, float *out,
+                        hipStream_t s);
+
+}  // namespace k8v4

@@ -1,0 +1,342 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: quantized codes, scales, pool bytes and gathered bytes bit-exact;
+attention outputs within 2e-3 max relative error per (query row, head),
+i.e. max_c |o - r| / max_c |r| over the 256 output dims, with fp32
+accumulation on the GPU and fp64 in the oracle.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from long_context_decode_append_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def k8():
+    import long_context_decode_append_amd as k8
+    k8.lib()
+    return k8
+
+
+def t_(x, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+def rel_err(out, ref):
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    num = np.abs(out - ref).max(axis=-1)
+    den = np.abs(ref).max(axis=-1)
+    return float((num / den).max())
+
+
+class Case:
+    """Same seeded tokens appended to a GPU pool and an oracle pool."""
+
+    def __init__(self, orc, k8, dev, seed, ctx, P, n_pages, n_table, dtype=np.float16,
+                 outlier_frac=0.0, identity=False, chunk=8192, fill=0xA5):
+        self.pt = synth.page_table(seed, n_table, n_pages, identity=identity)
+        outl = synth.outlier_channels(seed, 2, 256, outlier_frac) if outlier_frac else None
+        self.gpool = k8.K8V4Pool(n_pages, P, 2, device=dev, fill=fill)
+        self.opool = orc.OraclePool(3, n_pages, P, 2, sentinel=fill)
+        self.gpt = t_(self.pt, dev)
+        self.ctx, self.P = ctx, P
+        for s in range(0, ctx, chunk):
+            n = min(chunk, ctx - s)
+            k, v = synth.kv_tokens(seed, 0, s, n, 2, 256, dtype, outl)
+            k8.kv_append_k8v4(self.gpool, self.gpt, t_(k, dev), t_(v, dev), s)
+            self.opool.append(self.pt, k, v, s)
+
+    def oracle_attention(self, orc, q, n_vis):
+        return orc.attention_from_pool(self.opool, self.pt, q, n_vis)
+
+
+# ------------------------------------------------------------------ append / gather
+
+@pytest.mark.parametrize("dtype,ctx,P,n_pages", [(np.float32, 1024, 16, 64),
+                                                 (np.float16, 1000, 16, 70),
+                                                 (np.float16, 700, 256, 4)])
+def test_append_pool_bytes_and_gather_bitwise(orc, k8, dev, dtype, ctx, P, n_pages):
+    say(f"append/gather dtype={dtype.__name__} ctx={ctx} P={P}")
+    n_table = (ctx + P - 1) // P
+    c = Case(orc, k8, dev, 0, ctx, P, n_pages, n_table, dtype=dtype, chunk=333)
+    for r in range(3):
+        g = c.gpool.runs[r].cpu().numpy()
+        assert np.array_equal(g, c.opool.runs[r]), f"run {r} differs"
+    gk, gs, gv = [x.cpu().numpy() for x in k8.kv_gather(c.gpool, c.gpt, 0, ctx)]
+    ok, os_, ov = c.opool.gather(c.pt, 0, ctx)
+    assert np.array_equal(gk, ok)
+    assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(gv, ov)
+    # a ragged window
+    gk2, _, gv2 = [x.cpu().numpy() for x in k8.kv_gather(c.gpool, c.gpt, 37, 101)]
+    assert np.array_equal(gk2, ok[37:138]) and np.array_equal(gv2, ov[37:138])
+
+
+def test_append_token_by_token_equals_one_call(orc, k8, dev):
+    say("append token by token")
+    pt = synth.page_table(1, 8, 8)
+    k, v = synth.kv_tokens(1, 0, 0, 120, 2, 256, np.float16)
+    a = k8.K8V4Pool(8, 16, 2, device=dev, fill=0)
+    b = k8.K8V4Pool(8, 16, 2, device=dev, fill=0)
+    gpt = t_(pt, dev)
+    k8.kv_append_k8v4(a, gpt, t_(k, dev), t_(v, dev), 0)
+    for s in range(40):
+        k8.kv_append_k8v4(b, gpt, t_(k[s:s + 1], dev), t_(v[s:s + 1], dev), s)
+    k8.kv_append_k8v4(b, gpt, t_(k[40:], dev), t_(v[40:], dev), 40)
+    for r in range(3):
+        assert np.array_equal(a.runs[r].cpu().numpy(), b.runs[r].cpu().numpy())
+
+
+def test_quantizer_edge_values(orc, k8, dev):
+    """Crafted K/V heads: ties, zero groups and blocks, signed zeros, equal magnitudes."""
+    say("quantizer edge values")
+    x = np.zeros((6, 2, 256), np.float32)
+    x[0, 0, :12] = [127.0, 0.5, 1.5, 2.5, -2.5, 126.5, -126.5, 3.5, -0.5, -127.0, 64.49, -1.5]
+    x[1, 1, 0] = -0.0
+    x[2, 0, ::2] = 3.0
+    x[2, 0, 1::2] = -3.0
+    x[3] = np.linspace(-5, 5, 512).reshape(2, 256)
+    x[4, 0, 7] = 1e-6
+    x[5, :, 128:] = 2.0 ** -20
+    pt = np.arange(1, dtype=np.int32)
+    g = k8.K8V4Pool(1, 16, 2, device=dev, fill=0x5A)
+    o = orc.OraclePool(3, 1, 16, 2, sentinel=0x5A)
+    k8.kv_append_k8v4(g, t_(pt, dev), t_(x, dev), t_(x, dev), 0)
+    o.append(pt, x, x, 0)
+    for r in range(3):
+        assert np.array_equal(g.runs[r].cpu().numpy(), o.runs[r])
+
+
+# ------------------------------------------------------------------ decode / verify
+
+@pytest.fixture(scope="module")
+def tiny(orc, k8, dev):
+    # the tiny round trip: fp32 K/V/q, 1,024 cells in 16-cell pages, permuted table
+    return Case(orc, k8, dev, 0, 1024, 16, 64, 64, dtype=np.float32, chunk=1024)
+
+
+@pytest.mark.parametrize("n_ctx", [1, 2, 15, 16, 17, 31, 32, 33, 100, 511, 1000, 1024])
+@pytest.mark.parametrize("qdtype", [np.float32, np.float16])
+def test_decode_parity_tiny(orc, k8, dev, tiny, n_ctx, qdtype):
+    say(f"decode tiny n_ctx={n_ctx} q={qdtype.__name__}")
+    q = synth.queries(0, 0, n_ctx, 1, 16, 256, qdtype)
+    ws = k8.attn_workspace(tiny.gpool, 1, 1024)
+    out = k8.attn_decode(tiny.gpool, tiny.gpt, t_(q[0], dev), n_ctx, ws).cpu().numpy()
+    ref = tiny.oracle_attention(orc, q, [n_ctx])[0]
+    err = rel_err(out, ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("n_vis", [[1020, 1021, 1022, 1023, 1024], [1, 2, 3], [700, 33],
+                                   list(range(1009, 1025)), [5, 1024, 64, 900, 17, 33, 1, 1000, 2]])
+def test_verify_parity_tiny(orc, k8, dev, tiny, n_vis):
+    say(f"verify tiny n_q={len(n_vis)}")
+    q = synth.queries(0, 0, 77, len(n_vis), 16, 256, np.float16)
+    ws = k8.attn_workspace(tiny.gpool, len(n_vis), 1024)
+    out = k8.attn_verify(tiny.gpool, tiny.gpt, t_(q, dev), n_vis, ws).cpu().numpy()
+    ref = tiny.oracle_attention(orc, q, n_vis)
+    err = rel_err(out, ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+
+
+def test_verify_one_row_equals_decode_bitwise(k8, dev, tiny):
+    q = synth.queries(0, 0, 5, 1, 16, 256, np.float16)
+    ws = k8.attn_workspace(tiny.gpool, 1, 1024)
+    a = k8.attn_decode(tiny.gpool, tiny.gpt, t_(q[0], dev), 999, ws).cpu().numpy()
+    b = k8.attn_verify(tiny.gpool, tiny.gpt, t_(q, dev), [999], ws).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b[0].view(np.uint32))
+
+
+def test_identity_and_permuted_tables_bitwise_equal_and_rerun(orc, k8, dev):
+    say("identity vs permuted")
+    a = Case(orc, k8, dev, 3, 3000, 16, 200, 188, identity=True, chunk=3000)
+    b = Case(orc, k8, dev, 3, 3000, 16, 200, 188, identity=False, chunk=3000)
+    assert not np.array_equal(a.pt, b.pt)
+    for x, y in zip(k8.kv_gather(a.gpool, a.gpt, 0, 3000), k8.kv_gather(b.gpool, b.gpt, 0, 3000)):
+        assert np.array_equal(x.cpu().numpy().view(np.uint8), y.cpu().numpy().view(np.uint8))
+    q = synth.queries(3, 0, 0, 5, 16, 256, np.float16)
+    nv = [2996, 2997, 2998, 2999, 3000]
+    ws = k8.attn_workspace(a.gpool, 5, 3000)
+    oa = k8.attn_verify(a.gpool, a.gpt, t_(q, dev), nv, ws).cpu().numpy()
+    ob = k8.attn_verify(b.gpool, b.gpt, t_(q, dev), nv, ws).cpu().numpy()
+    ob2 = k8.attn_verify(b.gpool, b.gpt, t_(q, dev), nv, ws).cpu().numpy()
+    assert np.array_equal(oa.view(np.uint32), ob.view(np.uint32))
+    assert np.array_equal(ob.view(np.uint32), ob2.view(np.uint32))
+    da = k8.attn_decode(a.gpool, a.gpt, t_(q[0], dev), 3000, ws).cpu().numpy()
+    db = k8.attn_decode(b.gpool, b.gpt, t_(q[0], dev), 3000, ws).cpu().numpy()
+    assert np.array_equal(da.view(np.uint32), db.view(np.uint32))
+    assert rel_err(oa, a.oracle_attention(orc, q, nv)) <= TOL
+
+
+def test_negative_controls_are_detected(orc, k8, dev):
+    """A flipped V nibble, a wrong page table and a lost K scale must each be
+    caught by the same comparisons the parity tests use."""
+    say("negative controls")
+    c = Case(orc, k8, dev, 4, 512, 16, 40, 32, chunk=512)
+    q = synth.queries(4, 0, 0, 1, 16, 256, np.float16)
+    ws = k8.attn_workspace(c.gpool, 1, 512)
+    good = k8.attn_decode(c.gpool, c.gpt, t_(q[0], dev), 512, ws).cpu().numpy()
+    ok, os_, ov = c.opool.gather(c.pt, 0, 512)
+    # wrong table: swap two entries
+    bad_pt = c.pt.copy()
+    bad_pt[[3, 4]] = bad_pt[[4, 3]]
+    gk, _, _ = k8.kv_gather(c.gpool, t_(bad_pt, dev), 0, 512)
+    assert not np.array_equal(gk.cpu().numpy(), ok)
+    # flip one nibble of cell 100 (logical), head 1, block 2
+    p = 100
+    page, slot = int(c.pt[p // 16]), p % 16
+    tile = (page * 2 + 1) * 144 * 16
+    off = tile + slot * 128 + 2 * 16 + 5
+    v = c.gpool.runs[2]
+    v[off] = v[off] ^ 0x0F
+    _, _, gv = k8.kv_gather(c.gpool, c.gpt, 0, 512)
+    diff = np.argwhere(gv.cpu().numpy() != ov)
+    assert diff.shape[0] == 1 and tuple(diff[0][:3]) == (100, 1, 2)
+    flipped = k8.attn_decode(c.gpool, c.gpt, t_(q[0], dev), 512, ws).cpu().numpy()
+    assert not np.array_equal(flipped, good)
+    v[off] = v[off] ^ 0x0F
+    # lost K scale: zero the scale of cell 200, head 0, group 0
+    p = 200
+    page, slot = int(c.pt[p // 16]), p % 16
+    ks = c.gpool.runs[1].view(dtype=__import__("torch").float32)
+    idx = ((page * 2 + 0) * 16 + slot) * 2
+    saved = ks[idx].item()
+    ks[idx] = 0.0
+    _, gs, _ = k8.kv_gather(c.gpool, c.gpt, 0, 512)
+    assert not np.array_equal(gs.cpu().numpy(), os_)
+    ks[idx] = saved
+    again = k8.attn_decode(c.gpool, c.gpt, t_(q[0], dev), 512, ws).cpu().numpy()
+    assert np.array_equal(again.view(np.uint32), good.view(np.uint32))
+
+
+# ------------------------------------------------------------------ workload sizes
+
+def test_decode_32k_outlier_channels(orc, k8, dev):
+    """Decode at 32,768 cells, fp16 inputs with 1 % outlier channels at 8x,
+    256-cell pages drawn from a 256-page pool by permutation."""
+    say("decode 32k outliers")
+    c = Case(orc, k8, dev, 2, 32768, 256, 256, 128, outlier_frac=0.01)
+    q = synth.queries(2, 0, 0, 1, 16, 256, np.float16)
+    ws = k8.attn_workspace(c.gpool, 1, 32768)
+    out = k8.attn_decode(c.gpool, c.gpt, t_(q[0], dev), 32768, ws).cpu().numpy()
+    err = rel_err(out, c.oracle_attention(orc, q, [32768])[0])
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+    # sampled gathered bytes at the chunk seams
+    for p0 in (0, 8191, 16384, 32760):
+        gk, gs, gv = [x.cpu().numpy() for x in k8.kv_gather(c.gpool, c.gpt, p0, 8)]
+        ok, os_, ov = c.opool.gather(c.pt, p0, 8)
+        assert np.array_equal(gk, ok) and np.array_equal(gv, ov)
+        assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32))
+
+
+@pytest.mark.slow
+def test_decode_118750_filled_in_chunks(orc, k8, dev):
+    """118,750 cells appended in 8,192-token chunks (the last one ragged),
+    one layer of the 48-layer decode workload, checked against the oracle."""
+    say("decode 118750")
+    c = Case(orc, k8, dev, 3, 118750, 256, 464, 464, chunk=8192)
+    q = synth.queries(3, 0, 0, 1, 16, 256, np.float16)
+    ws = k8.attn_workspace(c.gpool, 1, 118750)
+    out = k8.attn_decode(c.gpool, c.gpt, t_(q[0], dev), 118750, ws).cpu().numpy()
+    err = rel_err(out, c.oracle_attention(orc, q, [118750])[0])
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+    for r in range(3):
+        assert np.array_equal(c.gpool.runs[r].cpu().numpy(), c.opool.runs[r])
+
+
+@pytest.mark.slow
+def test_verify_240000_sampled_rows(orc, k8, dev):
+    """Verify window at 240,000 cells in a 262,144-cell pool: 5 rows with
+    per-row limits 239,996..240,000; rows 0 and 4 checked against the oracle,
+    all rows against decode-equivalent single rows on the GPU."""
+    say("verify 240000")
+    c = Case(orc, k8, dev, 4, 240000, 256, 1024, 1024, chunk=8192)
+    q = synth.queries(4, 0, 0, 5, 16, 256, np.float16)
+    nv = [239996, 239997, 239998, 239999, 240000]
+    ws = k8.attn_workspace(c.gpool, 5, 240000)
+    out = k8.attn_verify(c.gpool, c.gpt, t_(q, dev), nv, ws).cpu().numpy()
+    sample = [0, 4]
+    ref = c.oracle_attention(orc, q[sample], [nv[i] for i in sample])
+    err = rel_err(out[sample], ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+    ws1 = k8.attn_workspace(c.gpool, 1, 240000)
+    for i in range(5):
+        d = k8.attn_decode(c.gpool, c.gpt, t_(q[i], dev), nv[i], ws1).cpu().numpy()
+        assert rel_err(out[i], d) <= 1e-5
+
+
+# ------------------------------------------------------------------ runtime / prefill
+
+def test_one_hip_runtime_in_process(k8, dev):
+    """libk8v4 must bind to the HIP runtime torch loaded (streams and device
+    pointers come from torch)."""
+    maps = open("/proc/self/maps").read()
+    paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(paths) == 1, paths
+    assert any("libk8v4.so" in line for line in maps.splitlines())
+
+
+@pytest.mark.parametrize("n_new", [1, 15, 16, 17, 100])
+@pytest.mark.parametrize("qdtype", [np.float16, np.float32])
+def test_prefill_parity_tiny(orc, k8, dev, tiny, n_new, qdtype):
+    say(f"prefill tiny n_new={n_new} q={qdtype.__name__}")
+    pos0 = 1024 - n_new
+    q = synth.queries(0, 0, 500 + n_new, n_new, 16, 256, qdtype)
+    out = k8.attn_prefill_chunk(tiny.gpool, tiny.gpt, t_(q, dev), pos0).cpu().numpy()
+    ref = tiny.oracle_attention(orc, q, [pos0 + i + 1 for i in range(n_new)])
+    err = rel_err(out, ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+
+
+def test_prefill_rows_match_verify(k8, dev, tiny):
+    n_new, pos0 = 16, 1000
+    q = synth.queries(0, 0, 9, n_new, 16, 256, np.float16)
+    pf = k8.attn_prefill_chunk(tiny.gpool, tiny.gpt, t_(q, dev), pos0).cpu().numpy()
+    ws = k8.attn_workspace(tiny.gpool, 16, 1024)
+    vf = k8.attn_verify(tiny.gpool, tiny.gpt, t_(q, dev), [pos0 + i + 1 for i in range(n_new)],
+                        ws).cpu().numpy()
+    assert rel_err(pf, vf) <= TOL   # both sit within TOL of the oracle
+
+
+@pytest.mark.slow
+def test_prefill_chunk_8192_at_231808_sampled_rows(orc, k8, dev):
+    """Prefill chunk of 8,192 fp16 queries at positions [231,808, 240,000)
+    over a 262,144-cell pool; 4 sampled rows checked against the oracle."""
+    say("prefill 8192 @ 231808")
+    c = Case(orc, k8, dev, 5, 240000, 256, 1024, 1024, chunk=8192)
+    pos0, n_new = 231808, 8192
+    q = synth.queries(5, 0, 0, n_new, 16, 256, np.float16)
+    out = k8.attn_prefill_chunk(c.gpool, c.gpt, t_(q, dev), pos0).cpu().numpy()
+    assert np.all(np.isfinite(out))
+    rows = [0, 1, 4097, 8191]
+    ref = c.oracle_attention(orc, q[rows], [pos0 + i + 1 for i in rows])
+    err = rel_err(out[rows], ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
