@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark: k8v4 decode attention at 118,750 cells x 48 layers on one MI355X.
+
+One step = one decoded token across 48 layers: for every layer, append the
+token's K/V at cell 118,749 (kv_append_k8v4) and attend over cells
+[0, 118,750) (attn_decode).  Each layer has its own pool (96.9 MB of k8v4
+pages, 4.65 GB in all, far beyond the 256 MB Infinity Cache), so every step
+streams its KV from HBM.  The step is captured once per step index in a HIP
+graph (torch.cuda.CUDAGraph) and replayed; W untimed steps, then K timed
+steps between two synchronizations.
+
+Prints one JSON line on stdout:
+  value = KV bytes read per second over the whole step (GB/s, 1e9 B/s),
+  ms_per_step, us_per_layer, hbm_frac (value / 8 TB/s),
+  roofline: the decode kernel alone, algorithmic bytes (cells x 816 B per
+            launch) over its mean duration from start/stop events recorded
+            by hipExtLaunchKernelGGL around each launch,
+  cpu_baseline: the CPU oracle on a bounded sample (one layer's decode),
+  extra: decode / verify at 240,000 cells and the 8,192-query prefill chunk.
+Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix, published
+CELL_BYTES = 816               # k8v4, 2 KV heads x 256 dims
+METRIC = "decode-attn µs/step and KV-read GB/s (% of HBM peak) at 119K/240K ctx"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def fill_pool(k8, synth, pool, pt, seed, layer, ctx, dev):
+    for c, s in enumerate(range(0, ctx, synth.CHUNK)):
+        n = min(synth.CHUNK, ctx - s)
+        k, v = synth.kv_chunk_device(seed, layer, c, n, 2, 256, dev)
+        k8.kv_append_k8v4(pool, pt, k, v, s)
+
+
+def make_table(torch, synth, seed, layer, n_table, n_pages, dev):
+    pt = synth.page_table(seed * 1000 + layer, n_table, n_pages)
+    return torch.from_numpy(pt).to(dev)
+
+
+def event_mean_ms(torch, pairs):
+    torch.cuda.synchronize()
+    ts = [a.elapsed_time(b) for a, b in pairs]
+    return sum(ts) / len(ts), ts
+
+
+def timed_launches(torch, k8, fn, n):
+    """Run fn() n times, each single kernel bracketed by start/stop events."""
+    pairs = []
+    for i in range(n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()  # torch creates the HIP event on first record
+        e1.record()
+        k8.time_next_launch(e0, e1)
+        fn(i)
+        pairs.append((e0, e1))
+    return event_mean_ms(torch, pairs)
+
+
+def cpu_baseline(ctx: int, target_s: float = 12.0):
+    """Time the oracle's decode attention (gather, dequantize, fp64 softmax
+    attention) for one layer at ctx cells, from an oracle pool built from
+    the numpy stream of the same recipe."""
+    import numpy as np
+
+    import oracle
+    from long_context_decode_append_amd import synth
+    P = 256
+    n_table = (ctx + P - 1) // P
+    pt = synth.page_table(3, n_table, n_table)
+    pool = oracle.OraclePool(3, n_table, P, 2)
+    for s in range(0, ctx, synth.CHUNK):
+        n = min(synth.CHUNK, ctx - s)
+        k, v = synth.kv_tokens(3, 0, s, n, 2, 256, np.float16)
+        pool.append(pt, k, v, s)
+    q = synth.queries(3, 0, 0, 1, 16, 256, np.float16)
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.attention_from_pool(pool, pt, q, [ctx])
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > target_s or len(times) >= 5:
+            break
+    t = sum(times) / len(times)
+    return {"value": round(ctx * CELL_BYTES / t / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"one layer of the 48: a {ctx}-cell decode step (gather, dequantize, fp64 "
+                      f"attention for 16 heads), {len(times)} run(s), {t:.2f} s each, "
+                      f"single-threaded C"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the k8v4 attention path here is a single-GPU "
+              "kernel library (no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_decode_append_amd as k8
+    from long_context_decode_append_amd import synth
+
+    dev = torch.device("cuda:0")
+    k8.lib()
+    layers, ctx, P = 48, 118750, 256
+    n_pages = (ctx + P - 1) // P                     # 464 pages, the last one partly used
+    seed = 3
+    W, K = args.warmup, args.steps
+
+    log(f"filling {layers} layer pools of {ctx} cells ...")
+    pools, tables = [], []
+    for l in range(layers):
+        pool = k8.K8V4Pool(n_pages, P, 2, device=dev)
+        pt = make_table(torch, synth, seed, l, n_pages, n_pages, dev)
+        fill_pool(k8, synth, pool, pt, seed, l, ctx, dev)
+        pools.append(pool)
+        tables.append(pt)
+    ws = k8.attn_workspace(pools[0], 1, ctx)
+    outs = [torch.empty((16, 256), dtype=torch.float32, device=dev) for _ in range(layers)]
+    n_steps = W + K
+    q_all = [[synth.queries_device(seed, l, s, 1, 16, 256, dev)[0] for l in range(layers)]
+             for s in range(n_steps)]
+    kv_new = [[synth.kv_chunk_device(seed, l, 10_000 + s, 1, 2, 256, dev) for l in range(layers)]
+              for s in range(n_steps)]
+    torch.cuda.synchronize()
+
+    def step(s):
+        for l in range(layers):
+            kn, vn = kv_new[s][l]
+            k8.kv_append_k8v4(pools[l], tables[l], kn, vn, ctx - 1)
+            k8.attn_decode(pools[l], tables[l], q_all[s][l], ctx, ws, out=outs[l])
+
+    # eager run of every step once (also warms the library's device cache)
+    log("eager pass ...")
+    t0 = time.perf_counter()
+    for s in range(n_steps):
+        step(s)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / n_steps
+
+    log("capturing graphs ...")
+    graphs = []
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        for s in range(n_steps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                step(s)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+
+    log(f"warmup {W}, timed {K} steps ...")
+    for s in range(W):
+        graphs[s].replay()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record()
+    for s in range(W, W + K):
+        graphs[s].replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    step_ms = ev0.elapsed_time(ev1) / K
+    kv_bytes_step = layers * ctx * CELL_BYTES
+    value = kv_bytes_step / (step_ms * 1e-3) / 1e9
+
+    # the decode kernel on its own: start/stop events around each launch
+    log("per-kernel timing ...")
+    dec_ms, _ = timed_launches(torch, k8, lambda i: k8.attn_decode(
+        pools[i % layers], tables[i % layers], q_all[0][i % layers], ctx, ws,
+        out=outs[i % layers]), 2 * layers)
+    app_ms, _ = timed_launches(torch, k8, lambda i: k8.kv_append_k8v4(
+        pools[i % layers], tables[i % layers], kv_new[0][i % layers][0],
+        kv_new[0][i % layers][1], ctx - 1), layers)
+    dec_gbs = ctx * CELL_BYTES / (dec_ms * 1e-3) / 1e9
+
+    extra = {}
+    if not args.no_extra:
+        del graphs
+        extra = bench_extra(torch, k8, synth, dev, log)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(ctx)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "decode_118750x48", "ctx": ctx, "layers": layers, "batch": 1,
+                   "q_heads": 16, "kv_heads": 2, "head_dim": 256, "page_size": P,
+                   "kv_format": "k8v4 (816 B/cell)", "per_step": "48 x (append 1 token + decode)",
+                   "launch": "HIP graph per step"},
+        "us_per_step": round(step_ms * 1e3, 2),
+        "us_per_layer": round(step_ms * 1e3 / layers, 3),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "eager_ms_per_step": round(eager_ms, 3),
+        "wall_s_timed": round(t_wall, 4),
+        "roofline": {"kernel": "attn_splitk_kernel (decode, 1 query)", "bound": "hbm",
+                     "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": ctx * CELL_BYTES, "mean_us": round(dec_ms * 1e3, 3),
+                     "append_mean_us": round(app_ms * 1e3, 3)},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_extra(torch, k8, synth, dev, log):
+    """Decode and verify at 240,000 cells (6 rotated 262,144-cell pools,
+    1.28 GB, beyond the Infinity Cache) and the 8,192-query prefill chunk."""
+    out = {}
+    ctx, P, n_pages, n_pools = 240000, 256, 1024, 6
+    n_table = (ctx + P - 1) // P
+    log(f"extra: filling {n_pools} pools of {ctx} cells ...")
+    pools, tables = [], []
+    for i in range(n_pools):
+        pool = k8.K8V4Pool(n_pages, P, 2, device=dev)
+        pt = make_table(torch, synth, 4, i, n_table, n_pages, dev)
+        fill_pool(k8, synth, pool, pt, 4, i, ctx, dev)
+        pools.append(pool)
+        tables.append(pt)
+    q1 = synth.queries_device(4, 0, 0, 1, 16, 256, dev)[0]
+    q5 = synth.queries_device(4, 0, 1, 5, 16, 256, dev)
+    ws1 = k8.attn_workspace(pools[0], 1, ctx)
+    ws5 = k8.attn_workspace(pools[0], 5, ctx)
+    nv = [ctx - 4, ctx - 3, ctx - 2, ctx - 1, ctx]
+    for i in range(n_pools):  # warm
+        k8.attn_decode(pools[i], tables[i], q1, ctx, ws1)
+        k8.attn_verify(pools[i], tables[i], q5, nv, ws5)
+    reps = 8 * n_pools
+    d_ms, _ = timed_launches(torch, k8, lambda i: k8.attn_decode(
+        pools[i % n_pools], tables[i % n_pools], q1, ctx, ws1), reps)
+    v_ms, _ = timed_launches(torch, k8, lambda i: k8.attn_verify(
+        pools[i % n_pools], tables[i % n_pools], q5, nv, ws5), reps)
+    b = ctx * CELL_BYTES
+    out["decode_240000"] = {"us": round(d_ms * 1e3, 3), "gbs": round(b / d_ms / 1e6, 2),
+                            "hbm_frac": round(b / d_ms / 1e6 / HBM_PEAK_GBS, 4),
+                            "pools_rotated": n_pools}
+    out["verify5_240000"] = {"us": round(v_ms * 1e3, 3), "gbs": round(b / v_ms / 1e6, 2),
+                             "hbm_frac": round(b / v_ms / 1e6 / HBM_PEAK_GBS, 4),
+                             "n_visible": nv}
+    # prefill chunk: 8,192 queries at [231,808, 240,000)
+    pos0, n_new = 231808, 8192
+    qp = synth.queries_device(5, 0, 0, n_new, 16, 256, dev)
+    outp = torch.empty((n_new, 16, 256), dtype=torch.float32, device=dev)
+    k8.attn_prefill_chunk(pools[0], tables[0], qp, pos0, out=outp)
+    p_ms, _ = timed_launches(torch, k8, lambda i: k8.attn_prefill_chunk(
+        pools[i % 2], tables[i % 2], qp, pos0, out=outp), 3)
+    flops = sum(1024.0 * 16 * (pos0 + i + 1) for i in range(n_new))
+    out["prefill_8192_at_231808"] = {"ms": round(p_ms, 3), "tflops": round(flops / p_ms / 1e9, 2),
+                                     "mfma_frac": round(flops / p_ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
+                                     "flop": flops}
+    log(f"extra: {json.dumps(out)}")
+    return out
+
+
+if __name__ == "__main__":
+    main()

@@ -209,6 +209,17 @@ const char *kv_strerror(int code);
  * recent KV_ERR_LAUNCH ("no error" if there was none). */
 const char *kv_last_hip_error(void);
 
+/*
+ * Profiling hook: the calling thread's next kernel launch by this library
+ * records start_event when the kernel starts and stop_event when it ends
+ * (hipExtLaunchKernelGGL), so hipEventElapsedTime gives that one kernel's
+ * duration.  Both are hipEvent_t created by the caller on the device of
+ * the launch.  Every entry point above launches exactly one kernel, except
+ * calls that return before launching (errors, empty work), which leave the
+ * hook armed.  Errors: KV_ERR_NULL.
+ */
+int kv_time_next_launch(void *start_event, void *stop_event);
+
 #ifdef __cplusplus
 }
 #endif

@@ -50,6 +50,7 @@ SIGNATURES = {
     "kv_check_page_table": (_I, [_PP, _PS, C.c_int32, _P]),
     "kv_strerror": (C.c_char_p, [_I]),
     "kv_last_hip_error": (C.c_char_p, []),
+    "kv_time_next_launch": (_I, [_P, _P]),
 }
 
 _lib = None
@@ -261,6 +262,16 @@ def attn_prefill_chunk(pool: K8V4Pool, page_table, q, pos0: int, scale: float = 
                                   _stream(stream))
     _check(rc, "attn_prefill_chunk")
     return out
+
+
+def time_next_launch(start_event, stop_event) -> None:
+    """Arm torch.cuda.Event pair (enable_timing=True, already recorded once so
+    that torch has created the HIP events) around the next kernel this
+    library launches on the calling thread."""
+    if not start_event.cuda_event or not stop_event.cuda_event:
+        raise ValueError("record the events once before arming them")
+    _check(lib().kv_time_next_launch(C.c_void_p(start_event.cuda_event),
+                                     C.c_void_p(stop_event.cuda_event)), "kv_time_next_launch")
 
 
 def check_page_table(pool: K8V4Pool, page_table, n_cells: int) -> int:

@@ -12,6 +12,7 @@
 using namespace k8v4;
 
 static thread_local char g_last_hip_error[256] = "no error";
+static thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 
 namespace k8v4 {
 int launch_status() {
@@ -20,6 +21,12 @@ int launch_status() {
   snprintf(g_last_hip_error, sizeof g_last_hip_error, "%s: %s", hipGetErrorName(e),
            hipGetErrorString(e));
   return KV_ERR_LAUNCH;
+}
+
+void take_launch_events(hipEvent_t *start, hipEvent_t *stop) {
+  *start = g_ev_start;
+  *stop = g_ev_stop;
+  g_ev_start = g_ev_stop = nullptr;
 }
 }  // namespace k8v4
 
@@ -50,6 +57,13 @@ const char *kv_strerror(int code) {
 }
 
 const char *kv_last_hip_error(void) { return g_last_hip_error; }
+
+int kv_time_next_launch(void *start_event, void *stop_event) {
+  if (!start_event || !stop_event) return KV_ERR_NULL;
+  g_ev_start = (hipEvent_t)start_event;
+  g_ev_stop = (hipEvent_t)stop_event;
+  return KV_OK;
+}
 
 int kv_append_k8v4(const kv_pool *pool, const kv_seq *seq, const void *k, const void *v,
                    int dtype, int32_t pos0, int32_t n_tokens, void *stream) {

@@ -189,7 +189,7 @@ int launch_append_k8v4(const kv_pool *pool, const kv_seq *seq, const void *k, co
   a.H = pool->n_kv_heads;
   const int64_t items = (int64_t)n * a.H;
   const unsigned blocks = (unsigned)((items + 3) / 4);
-  hipLaunchKernelGGL(append_k8v4_kernel, dim3(blocks), dim3(256), 0, s, a);
+  launch(append_k8v4_kernel, dim3(blocks), dim3(256), s, a);
   return launch_status();
 }
 
@@ -210,7 +210,7 @@ int launch_gather_k8v4(const kv_pool *pool, const kv_seq *seq, int pos0, int n, 
   a.H = pool->n_kv_heads;
   const int64_t items = (int64_t)n * a.H;
   const unsigned blocks = (unsigned)((items + 3) / 4);
-  hipLaunchKernelGGL(gather_k8v4_kernel, dim3(blocks), dim3(256), 0, s, a);
+  launch(gather_k8v4_kernel, dim3(blocks), dim3(256), s, a);
   return launch_status();
 }
 
@@ -219,7 +219,7 @@ int launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
   if (words == 0) return KV_OK;
   unsigned blocks = (unsigned)((words + 255) / 256);
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, s, (uint32_t *)p, words);
+  launch(fill_zero_kernel, dim3(blocks), dim3(256), s, (uint32_t *)p, words);
   return launch_status();
 }
 

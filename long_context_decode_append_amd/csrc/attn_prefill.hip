@@ -283,9 +283,9 @@ int launch_attn_prefill(const kv_pool *pool, const kv_seq *seq, const void *q, i
   a.scale2 = scale * 1.4426950408889634f;
   dim3 grid((n_new + kPfPos - 1) / kPfPos, a.H);
   if (q_dtype == KV_DTYPE_F32)
-    hipLaunchKernelGGL(attn_prefill_kernel<true>, grid, dim3(256), 0, s, a);
+    launch(attn_prefill_kernel<true>, grid, dim3(256), s, a);
   else
-    hipLaunchKernelGGL(attn_prefill_kernel<false>, grid, dim3(256), 0, s, a);
+    launch(attn_prefill_kernel<false>, grid, dim3(256), s, a);
   return launch_status();
 }
 

@@ -10,8 +10,10 @@
 //
 // Mapping onto MI355X:
 //   * grid (splits, KV heads, row passes); a workgroup = 4 waves owns one
-//     contiguous logical cell range ("split"), its waves take 32-cell steps
-//     round robin.  The split plan depends only on the context length, so
+//     contiguous logical cell range ("split") and one tile of 16 query rows
+//     (decode: the 8 heads of the KV head; verify: 2 queries per pass), its
+//     waves take 32-cell steps round robin, the loads of a wave's next step
+//     in flight while it computes the current one.  The split plan depends only on the context length, so
 //     identity and permuted page tables give bitwise-equal outputs.
 //   * per step a wave loads K codes / K scales / V nibbles / V scales
 //     straight into registers in the operand layouts of
@@ -29,11 +31,15 @@
 //     the last workgroup of each group of 16 splits to merge the group, and
 //     the last group merger per (KV head, row pass) merges the groups in
 //     fixed order, normalizes and applies the inverse Walsh-Hadamard
-//     transform.  No float atomics: results are deterministic.
+//     transform.  No float atomics: results are deterministic.  Partials
+//     move between workgroups through device-scope (L2-bypassing) 8-byte
+//     accesses, so no cache write-back fences are needed.
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace k8v4 {
+
+constexpr float kLazy = 8.0f;  // log2 headroom of the lazy softmax reference
 
 
 struct SplitArgs {
@@ -68,26 +74,110 @@ __device__ __forceinline__ f16x8 pack8(uint32_t a, uint32_t b, uint32_t c, uint3
   return __builtin_bit_cast(f16x8, u);
 }
 
-// merge the (m, l, O) rows [row0, row0+rows) of `count` partials into one
-__device__ __forceinline__ void merge_rows(const float2 *src_ml, const float *src_o, int count,
-                                           int stride_rows, int row0, int rows, float2 *dst_ml,
-                                           float *dst_o, int lane, int wave) {
-  for (int r = wave; r < rows; r += kWaves) {
-    const int row = row0 + r;
-    float M = -1e30f;
-    for (int s = 0; s < count; s++) M = fmaxf(M, src_ml[(size_t)s * stride_rows + row].x);
-    float L = 0.0f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < count; s++) {
-      const float2 ml = src_ml[(size_t)s * stride_rows + row];
-      const float f = exp2f(ml.x - M);
-      L += ml.y * f;
-      const f32x4 o = *reinterpret_cast<const f32x4 *>(src_o + ((size_t)s * stride_rows + row) * 256 + 4 * lane);
-      acc += f * o;
-    }
-    if (lane == 0) dst_ml[row] = make_float2(M, L);
-    *reinterpret_cast<f32x4 *>(dst_o + (size_t)row * 256 + 4 * lane) = acc;
+// Raw operands of one 32-cell step of one wave, as loaded from the pool.
+struct StepRaw {
+  u32x4 k[2][4];   // K codes: half h2, 16-byte chunk j (cell n, bytes 64j + 16lg ..)
+  f32x4 ks[2][2];  // K scales of cells 4lg..4lg+3 of half h2, groups 0/1 interleaved
+  u32x2 v[2][4];   // V nibbles: cell 4lg+i of half h2, bytes [8n, 8n+8) of its 128
+  u32x2 vd[2];     // V scales d16[block n/2][cells 4lg..4lg+3] of half h2
+};
+
+// Logical position whose page serves half h2 of the step at c: a half that
+// starts past the split end reuses the step's first half (its cells are
+// masked and its V scales zeroed).
+__device__ __forceinline__ int half_pos(int c, int h2, int c_end) {
+  const int cb = c + 16 * h2;
+  return cb < c_end ? cb : c;
+}
+
+// Page-table entries of the two halves of the step at c (wave-uniform:
+// scalar loads).  Steps past the end are clamped to a valid entry.
+__device__ __forceinline__ int2 step_pages(const SplitArgs &a, int c, int c_end) {
+  const int cl = min(c, c_end - 1);
+  const int p0 = a.pt[cl / a.P];
+  const int p1 = a.pt[half_pos(cl, 1, c_end) / a.P];
+  return make_int2(p0, p1);
+}
+
+__device__ __forceinline__ bool page_bad(const SplitArgs &a, int p) { return p < 0 || p >= a.n_pages; }
+
+__device__ __forceinline__ void issue_step(StepRaw &d, const SplitArgs &a, int g, int c, int c_end,
+                                           int2 pg, int n, int lg) {
+  const size_t q4_tile = (size_t)144 * a.P;
+  for (int h2 = 0; h2 < 2; h2++) {
+    int page = h2 ? pg.y : pg.x;
+    page = page_bad(a, page) ? 0 : page;
+    const int slot0 = half_pos(c, h2, c_end) % a.P;
+    const size_t tile = (size_t)page * a.H + g;
+    const int8_t *kp = a.kc + (tile * a.P + slot0 + n) * 256 + 16 * lg;
+    for (int j = 0; j < 4; j++) d.k[h2][j] = *reinterpret_cast<const u32x4 *>(kp + 64 * j);
+    const float *ksp = a.ks + (tile * a.P + slot0 + 4 * lg) * 2;
+    d.ks[h2][0] = *reinterpret_cast<const f32x4 *>(ksp);
+    d.ks[h2][1] = *reinterpret_cast<const f32x4 *>(ksp + 4);
+    const uint8_t *vt = a.vq + tile * q4_tile;
+    for (int i = 0; i < 4; i++)
+      d.v[h2][i] = *reinterpret_cast<const u32x2 *>(vt + (size_t)(slot0 + 4 * lg + i) * 128 + 8 * n);
+    d.vd[h2] = *reinterpret_cast<const u32x2 *>(vt + (size_t)128 * a.P +
+                                                 ((size_t)(n >> 1) * a.P + slot0 + 4 * lg) * 2);
   }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Partials cross workgroups (and XCDs, whose L2s are not coherent with each
+// other) through device-scope relaxed 8-byte atomic stores and loads: the
+// device scope bit makes them write through / miss the per-XCD L2, so no
+// L2 write-back or invalidate fence is needed.  A writer waits for its
+// stores to complete before the arrival counter is bumped; the last arrival
+// reads them after the counter returns.
+__device__ __forceinline__ void st_dev2(void *p, float x, float y) {
+  const uint64_t u = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
+  __hip_atomic_store((uint64_t *)p, u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_dev2(const void *p) {
+  const uint64_t u = __hip_atomic_load((uint64_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
+}
+__device__ __forceinline__ void st_dev4(float *p, f32x4 v) {
+  st_dev2(p, v.x, v.y);
+  st_dev2(p + 2, v.z, v.w);
+}
+__device__ __forceinline__ f32x4 ld_dev4(const float *p) {
+  const float2 a = ld_dev2(p), b = ld_dev2(p + 2);
+  return f32x4{a.x, a.y, b.x, b.y};
+}
+// wait until every memory access this wave issued has completed
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+__device__ __forceinline__ float readlane(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// Wave-level merge of `count` (<= 64) partial (m, l, O) rows for one row:
+// lane s reads partial s's (m, l); the O rows are loaded 8 at a time before
+// being combined in ascending partial order (deterministic).
+__device__ __forceinline__ void merge_row(const float2 *ml_base, const float *o_base, int count,
+                                          size_t stride_rows, int row, int lane, float &M_out,
+                                          float &L_out, f32x4 &acc_out) {
+  float2 ml = make_float2(-1e30f, 0.f);
+  if (lane < count) ml = ld_dev2(ml_base + (size_t)lane * stride_rows + row);
+  float M = ml.x;
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, lane_xor(M, m));
+  const float w = lane < count ? fast_exp2(ml.x - M) : 0.f;
+  float L = w * ml.y;
+  for (int m = 32; m >= 1; m >>= 1) L += lane_xor(L, m);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < count; s0 += 8) {
+    f32x4 o[8];
+    for (int i = 0; i < 8; i++)
+      if (s0 + i < count)
+        o[i] = ld_dev4(o_base + ((size_t)(s0 + i) * stride_rows + row) * 256 + 4 * lane);
+    for (int i = 0; i < 8; i++)
+      if (s0 + i < count) acc += readlane(w, s0 + i) * o[i];
+  }
+  M_out = M;
+  L_out = L;
+  acc_out = acc;
 }
 
 template <int NQT, bool QF32>
@@ -97,7 +187,8 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(const SplitArgs a) {
   __shared__ float lds_l[NQT * 16];
   __shared__ int lds_flag;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, lg = lane >> 4;
   const int split = blockIdx.x, g = blockIdx.y, pass = blockIdx.z;
   const int row_base = pass * a.rows_per_pass;
@@ -168,43 +259,19 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(const SplitArgs a) {
   const int c_end = min(a.max_limit, c_begin + a.steps_per_split * kStep);
   int lim_eff[NQT];
   for (int t = 0; t < NQT; t++) lim_eff[t] = min(lim[t], c_end);
-  const size_t q4_tile = (size_t)144 * a.P;
 
-  for (int c0 = c_begin + wave * kStep; c0 < c_end; c0 += kWaves * kStep) {
-    u32x4 kraw[2][4];
-    f32x4 ksr[2][2];
-    u32x2 vraw[2][4];
-    u32x2 vdr[2];
-    bool badp[2];
-    for (int h2 = 0; h2 < 2; h2++) {
-      const int cb = c0 + 16 * h2;
-      const int cl = cb < c_end ? cb : c0;  // a half past the end reads (masked) cells of c0's page
-      int page = a.pt[cl / a.P];
-      badp[h2] = page < 0 || page >= a.n_pages;
-      page = badp[h2] ? 0 : page;
-      const int slot0 = cl % a.P;
-      const size_t tile = (size_t)page * a.H + g;
-      const int8_t *kp = a.kc + (tile * a.P + slot0 + n) * 256 + 16 * lg;
-      for (int j = 0; j < 4; j++) kraw[h2][j] = *reinterpret_cast<const u32x4 *>(kp + 64 * j);
-      const float *ksp = a.ks + (tile * a.P + slot0 + 4 * lg) * 2;
-      ksr[h2][0] = *reinterpret_cast<const f32x4 *>(ksp);
-      ksr[h2][1] = *reinterpret_cast<const f32x4 *>(ksp + 4);
-      const uint8_t *vt = a.vq + tile * q4_tile;
-      for (int i = 0; i < 4; i++)
-        vraw[h2][i] = *reinterpret_cast<const u32x2 *>(vt + (size_t)(slot0 + 4 * lg + i) * 128 + 8 * n);
-      vdr[h2] = *reinterpret_cast<const u32x2 *>(vt + (size_t)128 * a.P + ((size_t)(n >> 1) * a.P + slot0 + 4 * lg) * 2);
-    }
-
-    // ---- scores S^T = K . Q^T  (A = K codes + 1152 as fp16, B = q)
+  // one 32-cell step: scores, online softmax, P.V
+  auto compute = [&](const StepRaw &d, int c0, int2 pg) {
+    const bool badp[2] = {page_bad(a, pg.x), page_bad(a, pg.y)};
     float s[NQT][8];
     for (int h2 = 0; h2 < 2; h2++) {
       f16x8 kf[8];
       for (int j = 0; j < 4; j++) {
         uint32_t l0, h0, l1, h1, l2, h2w, l3, h3;
-        i8x4_to_f16_biased(kraw[h2][j].x, l0, h0);
-        i8x4_to_f16_biased(kraw[h2][j].y, l1, h1);
-        i8x4_to_f16_biased(kraw[h2][j].z, l2, h2w);
-        i8x4_to_f16_biased(kraw[h2][j].w, l3, h3);
+        i8x4_to_f16_biased(d.k[h2][j].x, l0, h0);
+        i8x4_to_f16_biased(d.k[h2][j].y, l1, h1);
+        i8x4_to_f16_biased(d.k[h2][j].z, l2, h2w);
+        i8x4_to_f16_biased(d.k[h2][j].w, l3, h3);
         kf[2 * j] = pack8(l0, h0, l1, h1);
         kf[2 * j + 1] = pack8(l2, h2w, l3, h3);
       }
@@ -219,7 +286,7 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(const SplitArgs a) {
           if (QF32) acc1 = mfma16x16x32(kf[kk], qlo[t][kk], acc1);
         }
         for (int i = 0; i < 4; i++) {
-          const f32x4 kq = ksr[h2][i >> 1];
+          const f32x4 kq = d.ks[h2][i >> 1];
           const float d0 = kq[2 * (i & 1)], d1 = kq[2 * (i & 1) + 1];
           float sv = a.scale2 * (d0 * (acc0[i] - cbias[t][0]) + d1 * (acc1[i] - cbias[t][1]));
           const int cell = c0 + 16 * h2 + 4 * lg + i;
@@ -230,51 +297,55 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(const SplitArgs a) {
       }
     }
 
-    // ---- online softmax (base 2) and the P operand
+    // online softmax against a reference max m[t] that only moves when a
+    // row's max exceeds it by more than 2^kLazy: p <= 2^kLazy stays exact
+    // enough in fp16 and the 64 accumulators are rarely touched
     f16x8 pop[NQT];
     for (int t = 0; t < NQT; t++) {
       float mx = s[t][0];
       for (int e = 1; e < 8; e++) mx = fmaxf(mx, s[t][e]);
       mx = fmaxf(mx, lane_xor(mx, 16));
       mx = fmaxf(mx, lane_xor(mx, 32));
-      const float mnew = fmaxf(m[t], mx);
-      const float alpha = exp2f(m[t] - mnew);
+      if (__any(mx > m[t] + kLazy)) {
+        const float mnew = fmaxf(m[t], mx);
+        const float alpha = fast_exp2(m[t] - mnew);
+        lsum[t] *= alpha;
+        m[t] = mnew;
+        // O rows in the accumulator layout are 4*lg + i: fetch their factor
+        float al[4];
+        for (int i = 0; i < 4; i++) al[i] = lane_get(alpha, 4 * lg + i);
+        for (int j = 0; j < 16; j++)
+          for (int i = 0; i < 4; i++) o[t][j][i] *= al[i];
+      }
       float ps = 0.f;
       for (int e = 0; e < 8; e++) {
-        const float p = exp2f(s[t][e] - mnew);
+        const float p = fast_exp2(s[t][e] - m[t]);
         ps += p;
         pop[t][e] = (_Float16)p;
       }
-      lsum[t] = lsum[t] * alpha + ps;
-      m[t] = mnew;
-      // O rows in the accumulator layout are 4*lg + i: fetch their factor
-      float al[4];
-      for (int i = 0; i < 4; i++) al[i] = lane_get(alpha, 4 * lg + i);
-      for (int j = 0; j < 16; j++)
-        for (int i = 0; i < 4; i++) o[t][j][i] *= al[i];
+      lsum[t] += ps;
     }
 
-    // ---- O += P . V  (B = (code - 8) * d16 in fp16, 4 tiles per byte pair)
     uint32_t dsc[4];
     for (int k = 0; k < 4; k++) {
       const int h2 = k >> 1;
-      uint32_t w = (k & 1) ? vdr[h2].y : vdr[h2].x;
+      uint32_t w = (k & 1) ? d.vd[h2].y : d.vd[h2].x;
       const int ca = c0 + 16 * h2 + 4 * lg + 2 * (k & 1);
       if (ca >= c_end) w &= 0xffff0000u;      // zero the scale of cells past the split
       if (ca + 1 >= c_end) w &= 0x0000ffffu;
       dsc[k] = w;
     }
+    const f16x2 c1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
     for (int grp = 0; grp < 4; grp++) {
       const int dw = grp >> 1;
       const uint32_t sel = (grp & 1) ? 0x07060302u : 0x05040100u;
       uint32_t b0[4], b1[4], b2[4], b3[4];
       for (int k = 0; k < 4; k++) {
         const int h2 = k >> 1, ia = 2 * (k & 1);
-        const uint32_t wa = dw ? vraw[h2][ia].y : vraw[h2][ia].x;
-        const uint32_t wb = dw ? vraw[h2][ia + 1].y : vraw[h2][ia + 1].x;
+        const uint32_t wa = dw ? d.v[h2][ia].y : d.v[h2][ia].x;
+        const uint32_t wb = dw ? d.v[h2][ia + 1].y : d.v[h2][ia + 1].x;
         const uint32_t x = perm(wb, wa, sel);  // [a.byte, a.byte+1, b.byte, b.byte+1]
         const f16x2 dd = as_f16x2(dsc[k]);
-        const f16x2 c1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
         b0[k] = as_u32((as_f16x2((x & 0x000F000Fu) | 0x64006400u) - c1032) * dd);
         b1[k] = as_u32((as_f16x2(((x >> 4) & 0x000F000Fu) | 0x64006400u) - c1032) * dd);
         b2[k] = as_u32((as_f16x2(((x >> 8) & 0x000F000Fu) | 0x64006400u) - c1032) * dd);
@@ -290,6 +361,41 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(const SplitArgs a) {
         o[t][jb + 8] = mfma16x16x32(pop[t], B1, o[t][jb + 8]);
         o[t][jb + 1] = mfma16x16x32(pop[t], B2, o[t][jb + 1]);
         o[t][jb + 9] = mfma16x16x32(pop[t], B3, o[t][jb + 9]);
+      }
+    }
+  };
+
+  // two register buffers: the loads of the next step are in flight while
+  // the current one is computed; page-table entries are read two steps
+  // ahead.  The prefetch is issued unconditionally (a step past the end
+  // re-reads the wave's last valid step) so every wait for the current
+  // step's data leaves the next step's loads outstanding.
+  {
+    const int stride = kWaves * kStep;
+    const int c_first = c_begin + wave * kStep;
+    if (c_first < c_end) {
+      // last step start of this wave (wave-uniform)
+      const int c_last = c_first + ((c_end - 1 - c_first) / stride) * stride;
+      StepRaw A, B;
+      int c = c_first;
+      int2 pgA = step_pages(a, c, c_end);
+      issue_step(A, a, g, c, c_end, pgA, n, lg);
+      int2 pgB = step_pages(a, min(c + stride, c_last), c_end);
+      while (true) {
+        const int cn = c + stride;
+        issue_step(B, a, g, min(cn, c_last), c_end, pgB, n, lg);
+        const int2 pgA_next = step_pages(a, min(cn + stride, c_last), c_end);
+        compute(A, c, pgA);
+        c = cn;
+        if (c > c_last) break;
+        const int cn2 = c + stride;
+        issue_step(A, a, g, min(cn2, c_last), c_end, pgA_next, n, lg);
+        const int2 pgB_next = step_pages(a, min(cn2 + stride, c_last), c_end);
+        compute(B, c, pgB);
+        c = cn2;
+        if (c > c_last) break;
+        pgA = pgA_next;
+        pgB = pgB_next;
       }
     }
   }
@@ -309,8 +415,8 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(const SplitArgs a) {
           lold = lds_l[t * 16 + n];
           mn = fmaxf(mold, m[t]);
         }
-        const float a_old = w > 0 ? exp2f(mold - mn) : 0.f;
-        const float a_new = exp2f(m[t] - mn);
+        const float a_old = w > 0 ? fast_exp2(mold - mn) : 0.f;
+        const float a_new = fast_exp2(m[t] - mn);
         for (int i = 0; i < 4; i++) {
           fo[i] = lane_get(a_old, 4 * lg + i);
           fw[i] = lane_get(a_new, 4 * lg + i);
@@ -319,11 +425,13 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(const SplitArgs a) {
           lds_m[t * 16 + n] = mn;
           lds_l[t * 16 + n] = lold * a_old + lsum[t] * a_new;
         }
-        for (int j = 0; j < 16; j++) {
-          const int dim = o_dim(n, j);
-          for (int i = 0; i < 4; i++) {
-            float *p = &lds_o[(t * 16 + 4 * lg + i) * 256 + dim];
-            *p = (w > 0 ? *p * fo[i] : 0.f) + o[t][j][i] * fw[i];
+        if (t * 16 + 4 * lg < rows_here) {
+          for (int j = 0; j < 16; j++) {
+            const int dim = o_dim(n, j);
+            for (int i = 0; i < 4; i++) {
+              float *p = &lds_o[(t * 16 + 4 * lg + i) * 256 + dim];
+              *p = (w > 0 ? *p * fo[i] : 0.f) + o[t][j][i] * fw[i];
+            }
           }
         }
       }
@@ -339,17 +447,18 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(const SplitArgs a) {
     for (int idx = threadIdx.x; idx < rows_here * 64; idx += 256) {
       const int r = idx >> 6, c = (idx & 63) * 4;
       const f32x4 v = *reinterpret_cast<const f32x4 *>(&lds_o[r * 256 + c]);
-      *reinterpret_cast<f32x4 *>(a.part_o + (sp * rows_total + row_base + r) * 256 + c) = v;
+      st_dev4(a.part_o + (sp * rows_total + row_base + r) * 256 + c, v);
     }
     for (int r = threadIdx.x; r < rows_here; r += 256)
-      a.part_ml[sp * rows_total + row_base + r] = make_float2(lds_m[r], lds_l[r]);
+      st_dev2(a.part_ml + sp * rows_total + row_base + r, lds_m[r], lds_l[r]);
   }
 
   // ---------------------------------------------------------------- first-level combine
+  // every wave's partial stores complete before the arrival is counted
   uint32_t *cnt = a.counters + ((size_t)pass * H + g) * kCounterStride;
   const int grp = split / kGroup;
   const int gsize = min(kGroup, a.n_splits - grp * kGroup);
-  __threadfence();
+  wait_all_memory();
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t prev = atomicAdd(&cnt[grp], 1u);
@@ -357,15 +466,20 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(const SplitArgs a) {
   }
   __syncthreads();
   if (!lds_flag) return;
-  __threadfence();
   {
     const size_t s0 = (size_t)g * a.n_splits + (size_t)grp * kGroup;
     const size_t gi = (size_t)g * a.n_groups + grp;
-    merge_rows(a.part_ml + s0 * rows_total, a.part_o + s0 * rows_total * 256, gsize, (int)rows_total,
-               row_base, rows_here, a.grp_ml + gi * rows_total, a.grp_o + gi * rows_total * 256,
-               lane, wave);
+    for (int r = wave; r < rows_here; r += kWaves) {
+      const int row = row_base + r;
+      float M, L;
+      f32x4 acc;
+      merge_row(a.part_ml + s0 * rows_total, a.part_o + s0 * rows_total * 256, gsize, rows_total,
+                row, lane, M, L, acc);
+      if (lane == 0) st_dev2(a.grp_ml + gi * rows_total + row, M, L);
+      st_dev4(a.grp_o + (gi * rows_total + row) * 256 + 4 * lane, acc);
+    }
   }
-  __threadfence();
+  wait_all_memory();
   __syncthreads();
   if (threadIdx.x == 0) {
     atomicExch(&cnt[grp], 0u);
@@ -374,23 +488,15 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(const SplitArgs a) {
   }
   __syncthreads();
   if (!lds_flag) return;
-  __threadfence();
 
   // ---------------------------------------------------------------- final combine
   for (int r = wave; r < rows_here; r += kWaves) {
     const int row = row_base + r;
-    const float2 *gml = a.grp_ml + (size_t)g * a.n_groups * rows_total;
-    const float *go = a.grp_o + (size_t)g * a.n_groups * rows_total * 256;
-    float M = -1e30f;
-    for (int q = 0; q < a.n_groups; q++) M = fmaxf(M, gml[(size_t)q * rows_total + row].x);
-    float L = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int q = 0; q < a.n_groups; q++) {
-      const float2 ml = gml[(size_t)q * rows_total + row];
-      const float f = exp2f(ml.x - M);
-      L += ml.y * f;
-      acc += f * *reinterpret_cast<const f32x4 *>(go + ((size_t)q * rows_total + row) * 256 + 4 * lane);
-    }
+    const size_t g0 = (size_t)g * a.n_groups;
+    float M, L;
+    f32x4 acc;
+    merge_row(a.grp_ml + g0 * rows_total, a.grp_o + g0 * rows_total * 256, a.n_groups, rows_total,
+              row, lane, M, L, acc);
     float y[4];
     const float inv = 1.0f / L;
     for (int i = 0; i < 4; i++) y[i] = acc[i] * inv;
@@ -429,14 +535,16 @@ int launch_attn_splitk(const AttnCall &c) {
   const int H = pool->n_kv_heads;
   const int n_rows = c.n_q * kGqa;
   const bool qf32 = c.q_dtype == KV_DTYPE_F32;
-  const int tiles = (n_rows + 15) / 16;
-  const int nqt = qf32 ? 1 : (tiles < 3 ? tiles : 3);
-  const int rows_per_pass = nqt * 16;
+  // one 16-row tile per workgroup; more rows run as passes (blockIdx.z) over
+  // the same splits, which share the split's KV reads through L2 / MALL
+  const int rows_per_pass = 16;
   const int passes = (n_rows + rows_per_pass - 1) / rows_per_pass;
-  const SplitPlan plan = plan_splits(c.max_limit, attn_target_splits(H, n_rows));
+  if (passes > kMaxPasses) return KV_ERR_UNSUPPORTED;
+  int target = attn_target_splits(H, n_rows) / passes;
+  if (target < 1) target = 1;
+  const SplitPlan plan = plan_splits(c.max_limit, target);
   const WsLayout ws = ws_layout(H, n_rows, plan.n_splits, plan.n_groups);
   if (ws.total > c.ws_bytes) return KV_ERR_WORKSPACE;
-  if (passes > kMaxPasses) return KV_ERR_UNSUPPORTED;
 
   SplitArgs a;
   char *base = (char *)c.ws;
@@ -465,15 +573,10 @@ int launch_attn_splitk(const AttnCall &c) {
   a.n_groups = plan.n_groups;
 
   dim3 grid(plan.n_splits, H, passes);
-  if (qf32) {
-    hipLaunchKernelGGL((attn_splitk_kernel<1, true>), grid, dim3(256), 0, c.stream, a);
-  } else if (nqt == 1) {
-    hipLaunchKernelGGL((attn_splitk_kernel<1, false>), grid, dim3(256), 0, c.stream, a);
-  } else if (nqt == 2) {
-    hipLaunchKernelGGL((attn_splitk_kernel<2, false>), grid, dim3(256), 0, c.stream, a);
-  } else {
-    hipLaunchKernelGGL((attn_splitk_kernel<3, false>), grid, dim3(256), 0, c.stream, a);
-  }
+  if (qf32)
+    launch((attn_splitk_kernel<1, true>), grid, dim3(256), c.stream, a);
+  else
+    launch((attn_splitk_kernel<1, false>), grid, dim3(256), c.stream, a);
   return launch_status();
 }
 

@@ -1,6 +1,7 @@
 // Kernel launchers of libk8v4 (host side; arguments already validated).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "validate.hpp"
@@ -10,6 +11,19 @@ namespace k8v4 {
 // KV_OK after a successful launch, else KV_ERR_LAUNCH (the HIP error is kept
 // per thread for kv_last_hip_error).
 int launch_status();
+
+// Start/stop events armed by kv_time_next_launch for the calling thread's
+// next kernel launch (both NULL when none); taking them disarms the hook.
+void take_launch_events(hipEvent_t *start, hipEvent_t *stop);
+
+// Enqueue `kernel` on stream s (static shared memory only), recording the
+// armed timing events around it if any.
+template <typename Kernel, typename... Args>
+inline void launch(Kernel kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  hipEvent_t e0, e1;
+  take_launch_events(&e0, &e1);
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
+}
 
 int launch_append_k8v4(const kv_pool *pool, const kv_seq *seq, const void *k, const void *v,
                        int dtype, int pos0, int n, hipStream_t s);

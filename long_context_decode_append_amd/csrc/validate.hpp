@@ -17,7 +17,7 @@ constexpr int kMaxRows = 128;    // verify: at most 16 queries x 8 heads
 constexpr int kMaxQ = 16;
 constexpr int kMaxSplitsPerHead = 512;
 constexpr int kGroup = 16;       // splits merged by one first-level combine
-constexpr int kMaxPasses = 4;    // row passes of one verify call (3 row tiles each)
+constexpr int kMaxPasses = 8;    // row passes (16 rows each) of one verify call
 constexpr int kCounterStride = kMaxSplitsPerHead / kGroup + 1;  // group counters + head counter
 
 int check_pool(const kv_pool *pool, int need_fmt);

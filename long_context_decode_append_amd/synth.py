@@ -103,3 +103,34 @@ WORKLOADS = {
     "prefill_chunk_240k": dict(ctx=240000, page_size=256, n_pages=1024, dtype="float16", seed=5,
                                n_new=8192, outlier_frac=0.0),
 }
+
+
+# ---------------------------------------------------------------- device-side draws
+# For benchmark-scale fills (gigabytes of K/V) the same recipe is drawn on the
+# GPU with torch's Philox generator: standard normal fp32, cast to fp16,
+# one generator per (seed, layer, chunk) seeded with seed_of(...).  These
+# values differ from the numpy stream above; they only feed timing runs.
+
+def seed_of(seed: int, layer: int, chunk: int) -> int:
+    return (seed * 1_000_003 + layer) * 1_000_033 + chunk
+
+
+def kv_chunk_device(seed: int, layer: int, chunk: int, n: int, n_kv_heads: int, head_dim: int,
+                    device, dtype=None):
+    import torch
+    dtype = dtype or torch.float16
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed_of(seed, layer, chunk))
+    k = torch.randn((n, n_kv_heads, head_dim), generator=gen, device=device, dtype=torch.float32)
+    v = torch.randn((n, n_kv_heads, head_dim), generator=gen, device=device, dtype=torch.float32)
+    return k.to(dtype), v.to(dtype)
+
+
+def queries_device(seed: int, layer: int, step: int, rows: int, n_q_heads: int, head_dim: int,
+                   device, dtype=None):
+    import torch
+    dtype = dtype or torch.float16
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed_of(seed, layer, Q_STREAM + step))
+    return torch.randn((rows, n_q_heads, head_dim), generator=gen, device=device,
+                       dtype=torch.float32).to(dtype)

@@ -288,7 +288,9 @@ def test_verify_240000_sampled_rows(orc, k8, dev):
     ws1 = k8.attn_workspace(c.gpool, 1, 240000)
     for i in range(5):
         d = k8.attn_decode(c.gpool, c.gpt, t_(q[i], dev), nv[i], ws1).cpu().numpy()
-        assert rel_err(out[i], d) <= 1e-5
+        # verify and decode split the context differently (verify runs
+        # row passes over fewer splits), so they agree to the tolerance only
+        assert rel_err(out[i], d) <= TOL
 
 
 # ------------------------------------------------------------------ runtime / prefill
