@@ -41,6 +41,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE record (copy-calibrated), or None when the kernel source has
+    changed since those counters were taken."""
+    import hashlib
+    rec_path = os.path.join(ROOT, "profiles", "attn_splitk_decode_118750_traffic.json")
+    try:
+        rec = json.load(open(rec_path))
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec["bytes_per_launch"]
+
+
 def fill_pool(k8, synth, pool, pt, seed, layer, ctx, dev):
     for c, s in enumerate(range(0, ctx, synth.CHUNK)):
         n = min(synth.CHUNK, ctx - s)
@@ -113,6 +129,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--only", choices=["decode", "copy"], default=None,
+                    help="profiling aids: 'decode' runs 24 eager decode calls at 118,750 cells "
+                         "(8 layer pools); 'copy' runs 4 plain 1 GiB device copies (calibrates "
+                         "the HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -127,6 +147,9 @@ def main():
 
     dev = torch.device("cuda:0")
     k8.lib()
+    if args.only is not None:
+        profile_only(args.only, torch, k8, synth, dev)
+        return
     layers, ctx, P = 48, 118750, 256
     n_pages = (ctx + P - 1) // P                     # 464 pages, the last one partly used
     seed = 3
@@ -202,6 +225,8 @@ def main():
         pools[i % layers], tables[i % layers], kv_new[0][i % layers][0],
         kv_new[0][i % layers][1], ctx - 1), layers)
     dec_gbs = ctx * CELL_BYTES / (dec_ms * 1e-3) / 1e9
+    traffic_bytes = measured_traffic()
+    traffic = None if traffic_bytes is None else round(traffic_bytes / (dec_ms * 1e-3) / 1e9, 2)
 
     extra = {}
     if not args.no_extra:
@@ -237,13 +262,44 @@ def main():
         "wall_s_timed": round(t_wall, 4),
         "roofline": {"kernel": "attn_splitk_kernel (decode, 1 query)", "bound": "hbm",
                      "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": ctx * CELL_BYTES, "mean_us": round(dec_ms * 1e3, 3),
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_launch": ctx * CELL_BYTES, "traffic_bytes_per_launch": traffic_bytes,
+                     "mean_us": round(dec_ms * 1e3, 3),
                      "append_mean_us": round(app_ms * 1e3, 3)},
         "cpu_baseline": cpu,
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def profile_only(what, torch, k8, synth, dev):
+    """Short, fixed workloads for counter collection under rocprofv3."""
+    if what == "copy":
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        src.fill_(7)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {n} bytes x 4")
+        return
+    ctx, P, layers = 118750, 256, 8
+    n_pages = (ctx + P - 1) // P
+    pools, tables = [], []
+    for l in range(layers):
+        pool = k8.K8V4Pool(n_pages, P, 2, device=dev)
+        pt = make_table(torch, synth, 3, l, n_pages, n_pages, dev)
+        fill_pool(k8, synth, pool, pt, 3, l, ctx, dev)
+        pools.append(pool)
+        tables.append(pt)
+    ws = k8.attn_workspace(pools[0], 1, ctx)
+    q = synth.queries_device(3, 0, 0, 1, 16, 256, dev)[0]
+    out = torch.empty((16, 256), dtype=torch.float32, device=dev)
+    for i in range(3 * layers):
+        k8.attn_decode(pools[i % layers], tables[i % layers], q, ctx, ws, out=out)
+    torch.cuda.synchronize()
+    log(f"{3 * layers} decode calls at {ctx} cells")
 
 
 def bench_extra(torch, k8, synth, dev, log):
