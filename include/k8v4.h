@@ -137,16 +137,15 @@ int kv_gather(const kv_pool *pool, const kv_seq *seq, int32_t pos0, int32_t n, v
 
 /*
  * Device workspace needed by attn_decode / attn_verify for n_q query rows
- * (1 for decode) over at most max_ctx cells: split-K partial results plus
- * arrival counters.  The workspace must be zero-filled once before its
- * first use (kv_workspace_init does it); the kernels leave the counters at
- * zero after every completed call.  Calls that share a workspace must be
- * ordered on one stream.
+ * (1 for decode) over at most max_ctx cells: the split-K partial results.
+ * Its contents need no initialization and are overwritten by every call;
+ * calls that share a workspace must be ordered on one stream.  0 for an
+ * unsupported request.
  */
 size_t attn_workspace_bytes(const kv_pool *pool, int n_q_heads, int32_t n_q, int32_t max_ctx);
 
-/* Zero the counters of a workspace of ws_bytes bytes (a small fill kernel
- * on `stream`, safe inside graph capture). */
+/* Zero-fill a workspace of ws_bytes bytes with a small fill kernel on
+ * `stream` (optional: the attention calls do not need it). */
 int kv_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /*
@@ -214,9 +213,10 @@ const char *kv_last_hip_error(void);
  * records start_event when the kernel starts and stop_event when it ends
  * (hipExtLaunchKernelGGL), so hipEventElapsedTime gives that one kernel's
  * duration.  Both are hipEvent_t created by the caller on the device of
- * the launch.  Every entry point above launches exactly one kernel, except
- * calls that return before launching (errors, empty work), which leave the
- * hook armed.  Errors: KV_ERR_NULL.
+ * the launch.  attn_decode and attn_verify launch the split kernel and then
+ * a small combine kernel, so the hook times the split kernel; every other
+ * entry point launches one kernel.  Calls that return before launching
+ * (errors, empty work) leave the hook armed.  Errors: KV_ERR_NULL.
  */
 int kv_time_next_launch(void *start_event, void *stop_event);
 

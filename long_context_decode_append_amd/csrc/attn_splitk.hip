@@ -26,14 +26,13 @@
 //     the 16-wide row tiles, so the QK output already sits in the layout the
 //     PV A-operand needs and P never leaves registers.
 //   * online softmax in base 2 with fp32 running max / sum per row.
-//   * the 4 wave states merge through LDS in fixed order, then the
-//     workgroup writes one partial (m, l, O) per row; arrival counters pick
-//     the last workgroup of each group of 16 splits to merge the group, and
-//     the last group merger per (KV head, row pass) merges the groups in
-//     fixed order, normalizes and applies the inverse Walsh-Hadamard
-//     transform.  No float atomics: results are deterministic.  Partials
-//     move between workgroups through device-scope (L2-bypassing) 8-byte
-//     accesses, so no cache write-back fences are needed.
+//   * the 4 wave states merge through LDS, and the workgroup writes one
+//     partial (m, l, O) per row; a second, small kernel merges the partials
+//     of each row in fixed split order, normalizes and applies the inverse
+//     Walsh-Hadamard transform.  The kernel boundary makes the partials
+//     visible across XCDs (an in-kernel arrival-counter combine cost several
+//     device-scope round trips).  No float atomics: results are
+//     deterministic.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -49,17 +48,16 @@ struct SplitArgs {
   const int32_t *pt;
   const void *q;
   float *out;
-  uint32_t *counters;   // [passes][H][kCounterStride]
-  float2 *part_ml;      // [H][splits][rows]
-  float *part_o;        // [H][splits][rows][256]
-  float2 *grp_ml;       // [H][groups][rows]
-  float *grp_o;         // [H][groups][rows][256]
+  float2 *part_ml;      // [H][splits][rows]: (m, l) of each split partial
+  float *part_o;        // [H][splits][rows][256]: unnormalized O (rotated basis)
   int n_pages, P, H;
+  int p_shift;          // log2(P) when P is a power of two, else -1
+  int k_bytes, ks_bytes, v_bytes;  // run sizes (each < 2^31)
   int n_q_heads, n_rows, rows_per_pass;
   int limits[kMaxQ];
   int max_limit;
   float scale2;         // softmax scale * log2(e)
-  int steps_per_split, n_splits, n_groups;
+  int steps_per_split, n_splits;
 };
 
 // dim of output tile j held by column n of the PV MFMA: column n reads bytes
@@ -74,118 +72,58 @@ __device__ __forceinline__ f16x8 pack8(uint32_t a, uint32_t b, uint32_t c, uint3
   return __builtin_bit_cast(f16x8, u);
 }
 
-// Raw operands of one 32-cell step of one wave, as loaded from the pool.
-struct StepRaw {
-  u32x4 k[2][4];   // K codes: half h2, 16-byte chunk j (cell n, bytes 64j + 16lg ..)
-  f32x4 ks[2][2];  // K scales of cells 4lg..4lg+3 of half h2, groups 0/1 interleaved
-  u32x2 v[2][4];   // V nibbles: cell 4lg+i of half h2, bytes [8n, 8n+8) of its 128
-  u32x2 vd[2];     // V scales d16[block n/2][cells 4lg..4lg+3] of half h2
-};
-
-// Logical position whose page serves half h2 of the step at c: a half that
-// starts past the split end reuses the step's first half (its cells are
-// masked and its V scales zeroed).
-__device__ __forceinline__ int half_pos(int c, int h2, int c_end) {
-  const int cb = c + 16 * h2;
-  return cb < c_end ? cb : c;
-}
-
-// Page-table entries of the two halves of the step at c (wave-uniform:
-// scalar loads).  Steps past the end are clamped to a valid entry.
-__device__ __forceinline__ int2 step_pages(const SplitArgs &a, int c, int c_end) {
-  const int cl = min(c, c_end - 1);
-  const int p0 = a.pt[cl / a.P];
-  const int p1 = a.pt[half_pos(cl, 1, c_end) / a.P];
-  return make_int2(p0, p1);
-}
-
-__device__ __forceinline__ bool page_bad(const SplitArgs &a, int p) { return p < 0 || p >= a.n_pages; }
-
-__device__ __forceinline__ void issue_step(StepRaw &d, const SplitArgs &a, int g, int c, int c_end,
-                                           int2 pg, int n, int lg) {
-  const size_t q4_tile = (size_t)144 * a.P;
-  for (int h2 = 0; h2 < 2; h2++) {
-    int page = h2 ? pg.y : pg.x;
-    page = page_bad(a, page) ? 0 : page;
-    const int slot0 = half_pos(c, h2, c_end) % a.P;
-    const size_t tile = (size_t)page * a.H + g;
-    const int8_t *kp = a.kc + (tile * a.P + slot0 + n) * 256 + 16 * lg;
-    for (int j = 0; j < 4; j++) d.k[h2][j] = *reinterpret_cast<const u32x4 *>(kp + 64 * j);
-    const float *ksp = a.ks + (tile * a.P + slot0 + 4 * lg) * 2;
-    d.ks[h2][0] = *reinterpret_cast<const f32x4 *>(ksp);
-    d.ks[h2][1] = *reinterpret_cast<const f32x4 *>(ksp + 4);
-    const uint8_t *vt = a.vq + tile * q4_tile;
-    for (int i = 0; i < 4; i++)
-      d.v[h2][i] = *reinterpret_cast<const u32x2 *>(vt + (size_t)(slot0 + 4 * lg + i) * 128 + 8 * n);
-    d.vd[h2] = *reinterpret_cast<const u32x2 *>(vt + (size_t)128 * a.P +
-                                                 ((size_t)(n >> 1) * a.P + slot0 + 4 * lg) * 2);
-  }
-}
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit elements (gfx9 family)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Partials cross workgroups (and XCDs, whose L2s are not coherent with each
-// other) through device-scope relaxed 8-byte atomic stores and loads: the
-// device scope bit makes them write through / miss the per-XCD L2, so no
-// L2 write-back or invalidate fence is needed.  A writer waits for its
-// stores to complete before the arrival counter is bumped; the last arrival
-// reads them after the counter returns.
-__device__ __forceinline__ void st_dev2(void *p, float x, float y) {
-  const uint64_t u = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
-  __hip_atomic_store((uint64_t *)p, u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float2 ld_dev2(const void *p) {
-  const uint64_t u = __hip_atomic_load((uint64_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
-}
-__device__ __forceinline__ void st_dev4(float *p, f32x4 v) {
-  st_dev2(p, v.x, v.y);
-  st_dev2(p + 2, v.z, v.w);
-}
-__device__ __forceinline__ f32x4 ld_dev4(const float *p) {
-  const float2 a = ld_dev2(p), b = ld_dev2(p + 2);
-  return f32x4{a.x, a.y, b.x, b.y};
-}
-// wait until every memory access this wave issued has completed
-__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
 __device__ __forceinline__ float readlane(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
 
-// Wave-level merge of `count` (<= 64) partial (m, l, O) rows for one row:
-// lane s reads partial s's (m, l); the O rows are loaded 8 at a time before
-// being combined in ascending partial order (deterministic).
-__device__ __forceinline__ void merge_row(const float2 *ml_base, const float *o_base, int count,
-                                          size_t stride_rows, int row, int lane, float &M_out,
-                                          float &L_out, f32x4 &acc_out) {
-  float2 ml = make_float2(-1e30f, 0.f);
-  if (lane < count) ml = ld_dev2(ml_base + (size_t)lane * stride_rows + row);
-  float M = ml.x;
-  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, lane_xor(M, m));
-  const float w = lane < count ? fast_exp2(ml.x - M) : 0.f;
-  float L = w * ml.y;
-  for (int m = 32; m >= 1; m >>= 1) L += lane_xor(L, m);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < count; s0 += 8) {
-    f32x4 o[8];
-    for (int i = 0; i < 8; i++)
-      if (s0 + i < count)
-        o[i] = ld_dev4(o_base + ((size_t)(s0 + i) * stride_rows + row) * 256 + 4 * lane);
-    for (int i = 0; i < 8; i++)
-      if (s0 + i < count) acc += readlane(w, s0 + i) * o[i];
-  }
-  M_out = M;
-  L_out = L;
-  acc_out = acc;
+// Position, page and byte offsets (all wave-uniform) of one 16-cell half of
+// a step.  A half that starts past the split end reuses the step's first
+// half (its cells are masked and its V scales zeroed).
+struct Half {
+  int bad;        // page-table entry out of range: rows that read it return NaN
+  int k_soff;     // byte offset of the half's first cell in the K-code run
+  int ks_soff;    // ... in the K-scale run
+  int v_soff;     // ... of its nibble bytes in the V run
+  int vd_soff;    // ... of its block-0 scale in the V run
+};
+
+__device__ __forceinline__ int page_of(const SplitArgs &a, int pos) {
+  return a.p_shift >= 0 ? (pos >> a.p_shift) : pos / a.P;
+}
+
+__device__ __forceinline__ Half make_half(const SplitArgs &a, int g, int pos, int page) {
+  Half h;
+  h.bad = page < 0 || page >= a.n_pages;
+  const int pg = h.bad ? 0 : page;
+  const int slot0 = pos - page_of(a, pos) * a.P;
+  const int tile = pg * a.H + g;
+  h.k_soff = (tile * a.P + slot0) * 256;
+  h.ks_soff = (tile * a.P + slot0) * 8;
+  h.v_soff = tile * 144 * a.P + slot0 * 128;
+  h.vd_soff = tile * 144 * a.P + 128 * a.P + slot0 * 2;
+  return h;
+}
+
+// the two halves of the step at c (c < c_end); page entries read here are
+// scalar loads
+__device__ __forceinline__ void step_halves(const SplitArgs &a, int g, int c, int c_end, Half &h0,
+                                            Half &h1) {
+  const int p1pos = (c + 16 < c_end) ? c + 16 : c;
+  const int pg0 = a.pt[page_of(a, c)];
+  const int pg1 = a.pt[page_of(a, p1pos)];
+  h0 = make_half(a, g, c, pg0);
+  h1 = make_half(a, g, p1pos, pg1);
 }
 
 template <int NQT, bool QF32>
-__global__ __launch_bounds__(256) void attn_splitk_kernel(const SplitArgs a) {
-  __shared__ float lds_o[NQT * 16 * 256];
-  __shared__ float lds_m[NQT * 16];
-  __shared__ float lds_l[NQT * 16];
-  __shared__ int lds_flag;
+__global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) {
+  __shared__ float lds_o[kWaves * 16 * 64 * 4];   // wave states, accumulator layout
+  __shared__ float lds_m[kWaves * 16];
+  __shared__ float lds_l[kWaves * 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -194,18 +132,56 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(const SplitArgs a) {
   const int row_base = pass * a.rows_per_pass;
   const int rows_here = min(a.rows_per_pass, a.n_rows - row_base);
 
+  const int c_begin = split * a.steps_per_split * kStep;
+  const int c_end = min(a.max_limit, c_begin + a.steps_per_split * kStep);
+  const int stride = kWaves * kStep;
+  const int c_first = c_begin + wave * kStep;
+  const bool has_work = c_first < c_end;
+  // last step start of this wave (wave-uniform)
+  const int c_last = has_work ? c_first + ((c_end - 1 - c_first) / stride) * stride : c_first;
+
+  // buffer descriptors over whole runs; the hardware range check returns
+  // zeros for any offset past a run
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)a.kc, (short)0, a.k_bytes, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc((void *)a.ks, (short)0, a.ks_bytes, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)a.vq, (short)0, a.v_bytes, kRsrcFlags);
+  // lane-constant parts of the operand-layout loads
+  const int k_voff = n * 256 + 16 * lg;            // + 64 j: 16 bytes of cell n
+  const int ks_voff = 32 * lg;                     // scales of cells 4lg..4lg+3
+  const int v_voff = 4 * lg * 128 + 8 * n;         // + 128 i: bytes [8n, 8n+8) of cell 4lg+i
+  const int vd_voff = ((n >> 1) * a.P + 4 * lg) * 2;  // d16[block n/2][cells 4lg..4lg+3]
+
+  u32x4 kr[2][4];
+  f32x4 ksr[2][2];
+  u32x2 vr[2][4];
+  u32x2 vdr[2];
+  Half cur0, cur1, nxt0, nxt1;
+  if (has_work) {
+    step_halves(a, g, c_first, c_end, cur0, cur1);
+    const Half *hs[2] = {&cur0, &cur1};
+    for (int h2 = 0; h2 < 2; h2++) {
+      const Half &h = *hs[h2];
+      for (int j = 0; j < 4; j++) kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + 64 * j, h.k_soff, 0);
+      ksr[h2][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, ks_voff, h.ks_soff, 0));
+      ksr[h2][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, ks_voff + 16, h.ks_soff, 0));
+      for (int i = 0; i < 4; i++) vr[h2][i] = __builtin_amdgcn_raw_buffer_load_b64(rv, v_voff + 128 * i, h.v_soff, 0);
+      vdr[h2] = __builtin_amdgcn_raw_buffer_load_b64(rv, vd_voff, h.vd_soff, 0);
+    }
+    step_halves(a, g, min(c_first + stride, c_last), c_end, nxt0, nxt1);
+  }
+
   // ---------------------------------------------------------------- queries
   // B operand of the QK MFMA for row tile t and k-step kk: lane (n, lg)
   // holds q[row t*16+n][dims 64*(kk/2) + 16*lg + 8*(kk%2) + 0..7].
   f16x8 qop[NQT][8];
   f16x8 qlo[QF32 ? NQT : 1][QF32 ? 8 : 1];
   float cbias[NQT][2];
-  int lim[NQT];
+  int lim_eff[NQT];
   for (int t = 0; t < NQT; t++) {
     const int r = t * 16 + n;
     const int row = row_base + r;
-    const bool rv = r < rows_here;
-    lim[t] = rv ? a.limits[row >> 3] : 0;
+    const bool rv_ok = r < rows_here;
+    lim_eff[t] = min(rv_ok ? a.limits[row >> 3] : 0, c_end);
     const int qi = row >> 3, hl = row & 7;
     const size_t qbase = ((size_t)qi * a.n_q_heads + (size_t)g * kGqa + hl) * 256;
     float s0 = 0.f, s1 = 0.f;
@@ -214,14 +190,14 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(const SplitArgs a) {
       f16x8 hi, lo;
       if (!QF32) {
         u32x4 w = {0u, 0u, 0u, 0u};
-        if (rv) w = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.q) + qbase + d0);
+        if (rv_ok) w = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.q) + qbase + d0);
         hi = __builtin_bit_cast(f16x8, w);
         float ss = 0.f;
         for (int e = 0; e < 8; e++) ss += (float)hi[e];
         if (kk < 4) s0 += ss; else s1 += ss;
       } else {
         f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
-        if (rv) {
+        if (rv_ok) {
           x0 = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(a.q) + qbase + d0);
           x1 = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(a.q) + qbase + d0 + 4);
         }
@@ -246,8 +222,23 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(const SplitArgs a) {
     cbias[t][0] = 1152.0f * s0;
     cbias[t][1] = 1152.0f * s1;
   }
+  // smallest visible-cell limit over the valid rows of this tile (wave-
+  // uniform): steps that end below it need no masking at all
+  int lim_min = 0x7fffffff;
+  for (int t = 0; t < NQT; t++) {
+    int lm = (t * 16 + n < rows_here) ? lim_eff[t] : 0x7fffffff;
+    for (int msk = 1; msk < 16; msk <<= 1) lm = min(lm, lane_xor(lm, msk));
+    lim_min = min(lim_min, __builtin_amdgcn_readfirstlane(lm));
+  }
 
   // ---------------------------------------------------------------- main loop
+  // One register buffer per operand; each part is refilled with the next
+  // step's data as soon as the current step has consumed it (K after its
+  // conversion, K scales after the scores, V after the B operands are
+  // built), so those loads fly during the rest of the step.  Page-table
+  // entries are read two steps ahead.  The refill is unconditional (past the
+  // end it re-reads the wave's last step) so every wait for current data
+  // leaves the next step's loads outstanding.
   float m[NQT], lsum[NQT];
   f32x4 o[NQT][16];
   for (int t = 0; t < NQT; t++) {
@@ -255,278 +246,313 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(const SplitArgs a) {
     lsum[t] = 0.f;
     for (int j = 0; j < 16; j++) o[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const int c_begin = split * a.steps_per_split * kStep;
-  const int c_end = min(a.max_limit, c_begin + a.steps_per_split * kStep);
-  int lim_eff[NQT];
-  for (int t = 0; t < NQT; t++) lim_eff[t] = min(lim[t], c_end);
+  const f16x2 c1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const f16x2 c72 = {(_Float16)72.0f, (_Float16)72.0f};
 
-  // one 32-cell step: scores, online softmax, P.V
-  auto compute = [&](const StepRaw &d, int c0, int2 pg) {
-    const bool badp[2] = {page_bad(a, pg.x), page_bad(a, pg.y)};
-    float s[NQT][8];
-    for (int h2 = 0; h2 < 2; h2++) {
-      f16x8 kf[8];
-      for (int j = 0; j < 4; j++) {
-        uint32_t l0, h0, l1, h1, l2, h2w, l3, h3;
-        i8x4_to_f16_biased(d.k[h2][j].x, l0, h0);
-        i8x4_to_f16_biased(d.k[h2][j].y, l1, h1);
-        i8x4_to_f16_biased(d.k[h2][j].z, l2, h2w);
-        i8x4_to_f16_biased(d.k[h2][j].w, l3, h3);
-        kf[2 * j] = pack8(l0, h0, l1, h1);
-        kf[2 * j + 1] = pack8(l2, h2w, l3, h3);
+  if (has_work) {
+    int c = c_first;
+    while (true) {
+      // pages of the step after next
+      Half nn0, nn1;
+      step_halves(a, g, min(c + 2 * stride, c_last), c_end, nn0, nn1);
+      const int badp[2] = {cur0.bad, cur1.bad};
+      // whole step inside every valid row's limit and on valid pages: no
+      // masking (rows past rows_here then hold harmless values that are never
+      // written out)
+      const bool full_step = c + kStep <= lim_min && !(cur0.bad | cur1.bad);
+      const Half *nx[2] = {&nxt0, &nxt1};
+
+      // ---- scores S^T = K . Q^T (A = K codes + 1152 as fp16, B = q)
+      float s[NQT][8];
+      for (int h2 = 0; h2 < 2; h2++) {
+        f32x4 acc0[NQT], acc1[NQT];
+        for (int t = 0; t < NQT; t++) {
+          acc0[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          acc1[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        for (int j = 0; j < 4; j++) {
+          uint32_t l0, h0, l1, h1, l2, h2w, l3, h3;
+          i8x4_to_f16_biased(kr[h2][j].x, l0, h0);
+          i8x4_to_f16_biased(kr[h2][j].y, l1, h1);
+          i8x4_to_f16_biased(kr[h2][j].z, l2, h2w);
+          i8x4_to_f16_biased(kr[h2][j].w, l3, h3);
+          const f16x8 ka = pack8(l0, h0, l1, h1), kb = pack8(l2, h2w, l3, h3);
+          for (int t = 0; t < NQT; t++) {
+            if (j < 2) {
+              acc0[t] = mfma16x16x32(ka, qop[t][2 * j], acc0[t]);
+              acc0[t] = mfma16x16x32(kb, qop[t][2 * j + 1], acc0[t]);
+              if (QF32) {
+                acc0[t] = mfma16x16x32(ka, qlo[t][2 * j], acc0[t]);
+                acc0[t] = mfma16x16x32(kb, qlo[t][2 * j + 1], acc0[t]);
+              }
+            } else {
+              acc1[t] = mfma16x16x32(ka, qop[t][2 * j], acc1[t]);
+              acc1[t] = mfma16x16x32(kb, qop[t][2 * j + 1], acc1[t]);
+              if (QF32) {
+                acc1[t] = mfma16x16x32(ka, qlo[t][2 * j], acc1[t]);
+                acc1[t] = mfma16x16x32(kb, qlo[t][2 * j + 1], acc1[t]);
+              }
+            }
+          }
+          // K chunk j of this half consumed: refill with the next step's
+          kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + 64 * j, nx[h2]->k_soff, 0);
+        }
+        for (int t = 0; t < NQT; t++) {
+          for (int i = 0; i < 4; i++) {
+            const f32x4 kq = ksr[h2][i >> 1];
+            const float d0 = kq[2 * (i & 1)], d1 = kq[2 * (i & 1) + 1];
+            s[t][4 * h2 + i] = a.scale2 * (d0 * (acc0[t][i] - cbias[t][0]) + d1 * (acc1[t][i] - cbias[t][1]));
+          }
+          if (!full_step) {
+            for (int i = 0; i < 4; i++) {
+              const int cell = c + 16 * h2 + 4 * lg + i;
+              float sv = cell < lim_eff[t] ? s[t][4 * h2 + i] : -INFINITY;
+              s[t][4 * h2 + i] = badp[h2] ? __builtin_nanf("") : sv;
+            }
+          }
+        }
+        ksr[h2][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, ks_voff, nx[h2]->ks_soff, 0));
+        ksr[h2][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, ks_voff + 16, nx[h2]->ks_soff, 0));
       }
+
+      // ---- online softmax against a reference max m[t] that only moves
+      // when a row's max exceeds it by more than 2^kLazy: p <= 2^kLazy stays
+      // exact enough in fp16 and the accumulators are rarely rescaled
+      f16x8 pop[NQT];
       for (int t = 0; t < NQT; t++) {
-        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-        for (int kk = 0; kk < 4; kk++) {
-          acc0 = mfma16x16x32(kf[kk], qop[t][kk], acc0);
-          if (QF32) acc0 = mfma16x16x32(kf[kk], qlo[t][kk], acc0);
+        float mx = s[t][0];
+        for (int e = 1; e < 8; e++) mx = fmaxf(mx, s[t][e]);
+        mx = fmaxf(mx, lane_xor(mx, 16));
+        mx = fmaxf(mx, lane_xor(mx, 32));
+        if (__any(mx > m[t] + kLazy)) {
+          const float mnew = fmaxf(m[t], mx);
+          const float alpha = fast_exp2(m[t] - mnew);
+          lsum[t] *= alpha;
+          m[t] = mnew;
+          // O rows in the accumulator layout are 4*lg + i: fetch their factor
+          float al[4];
+          for (int i = 0; i < 4; i++) al[i] = lane_get(alpha, 4 * lg + i);
+          for (int j = 0; j < 16; j++)
+            for (int i = 0; i < 4; i++) o[t][j][i] *= al[i];
         }
-        for (int kk = 4; kk < 8; kk++) {
-          acc1 = mfma16x16x32(kf[kk], qop[t][kk], acc1);
-          if (QF32) acc1 = mfma16x16x32(kf[kk], qlo[t][kk], acc1);
+        float ps = 0.f;
+        for (int e = 0; e < 8; e++) {
+          const float p = fast_exp2(s[t][e] - m[t]);
+          ps += p;
+          pop[t][e] = (_Float16)p;
         }
-        for (int i = 0; i < 4; i++) {
-          const f32x4 kq = d.ks[h2][i >> 1];
-          const float d0 = kq[2 * (i & 1)], d1 = kq[2 * (i & 1) + 1];
-          float sv = a.scale2 * (d0 * (acc0[i] - cbias[t][0]) + d1 * (acc1[i] - cbias[t][1]));
-          const int cell = c0 + 16 * h2 + 4 * lg + i;
-          sv = cell < lim_eff[t] ? sv : -INFINITY;
-          sv = badp[h2] ? __builtin_nanf("") : sv;
-          s[t][4 * h2 + i] = sv;
-        }
+        lsum[t] += ps;
       }
-    }
 
-    // online softmax against a reference max m[t] that only moves when a
-    // row's max exceeds it by more than 2^kLazy: p <= 2^kLazy stays exact
-    // enough in fp16 and the 64 accumulators are rarely touched
-    f16x8 pop[NQT];
-    for (int t = 0; t < NQT; t++) {
-      float mx = s[t][0];
-      for (int e = 1; e < 8; e++) mx = fmaxf(mx, s[t][e]);
-      mx = fmaxf(mx, lane_xor(mx, 16));
-      mx = fmaxf(mx, lane_xor(mx, 32));
-      if (__any(mx > m[t] + kLazy)) {
-        const float mnew = fmaxf(m[t], mx);
-        const float alpha = fast_exp2(m[t] - mnew);
-        lsum[t] *= alpha;
-        m[t] = mnew;
-        // O rows in the accumulator layout are 4*lg + i: fetch their factor
-        float al[4];
-        for (int i = 0; i < 4; i++) al[i] = lane_get(alpha, 4 * lg + i);
-        for (int j = 0; j < 16; j++)
-          for (int i = 0; i < 4; i++) o[t][j][i] *= al[i];
-      }
-      float ps = 0.f;
-      for (int e = 0; e < 8; e++) {
-        const float p = fast_exp2(s[t][e] - m[t]);
-        ps += p;
-        pop[t][e] = (_Float16)p;
-      }
-      lsum[t] += ps;
-    }
-
-    uint32_t dsc[4];
-    for (int k = 0; k < 4; k++) {
-      const int h2 = k >> 1;
-      uint32_t w = (k & 1) ? d.vd[h2].y : d.vd[h2].x;
-      const int ca = c0 + 16 * h2 + 4 * lg + 2 * (k & 1);
-      if (ca >= c_end) w &= 0xffff0000u;      // zero the scale of cells past the split
-      if (ca + 1 >= c_end) w &= 0x0000ffffu;
-      dsc[k] = w;
-    }
-    const f16x2 c1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
-    for (int grp = 0; grp < 4; grp++) {
-      const int dw = grp >> 1;
-      const uint32_t sel = (grp & 1) ? 0x07060302u : 0x05040100u;
-      uint32_t b0[4], b1[4], b2[4], b3[4];
+      // ---- O += P . V  (B = (code - 8) * d16 in fp16, 4 tiles per byte pair)
+      uint32_t dsc[4];
       for (int k = 0; k < 4; k++) {
-        const int h2 = k >> 1, ia = 2 * (k & 1);
-        const uint32_t wa = dw ? d.v[h2][ia].y : d.v[h2][ia].x;
-        const uint32_t wb = dw ? d.v[h2][ia + 1].y : d.v[h2][ia + 1].x;
-        const uint32_t x = perm(wb, wa, sel);  // [a.byte, a.byte+1, b.byte, b.byte+1]
-        const f16x2 dd = as_f16x2(dsc[k]);
-        b0[k] = as_u32((as_f16x2((x & 0x000F000Fu) | 0x64006400u) - c1032) * dd);
-        b1[k] = as_u32((as_f16x2(((x >> 4) & 0x000F000Fu) | 0x64006400u) - c1032) * dd);
-        b2[k] = as_u32((as_f16x2(((x >> 8) & 0x000F000Fu) | 0x64006400u) - c1032) * dd);
-        b3[k] = as_u32((as_f16x2(((x >> 12) & 0x000F000Fu) | 0x64006400u) - c1032) * dd);
+        const int h2 = k >> 1;
+        uint32_t w = (k & 1) ? vdr[h2].y : vdr[h2].x;
+        if (c + kStep > c_end) {
+          const int ca = c + 16 * h2 + 4 * lg + 2 * (k & 1);
+          if (ca >= c_end) w &= 0xffff0000u;      // zero the scale of cells past the split
+          if (ca + 1 >= c_end) w &= 0x0000ffffu;
+        }
+        dsc[k] = w;
       }
-      const int jb = 2 * grp;
-      const f16x8 B0 = pack8(b0[0], b0[1], b0[2], b0[3]);  // tile jb     (byte lo nibble)
-      const f16x8 B1 = pack8(b1[0], b1[1], b1[2], b1[3]);  // tile jb + 8 (byte hi nibble)
-      const f16x8 B2 = pack8(b2[0], b2[1], b2[2], b2[3]);  // tile jb + 1
-      const f16x8 B3 = pack8(b3[0], b3[1], b3[2], b3[3]);  // tile jb + 9
-      for (int t = 0; t < NQT; t++) {
-        o[t][jb] = mfma16x16x32(pop[t], B0, o[t][jb]);
-        o[t][jb + 8] = mfma16x16x32(pop[t], B1, o[t][jb + 8]);
-        o[t][jb + 1] = mfma16x16x32(pop[t], B2, o[t][jb + 1]);
-        o[t][jb + 9] = mfma16x16x32(pop[t], B3, o[t][jb + 9]);
+      for (int h2 = 0; h2 < 2; h2++)
+        vdr[h2] = __builtin_amdgcn_raw_buffer_load_b64(rv, vd_voff, nx[h2]->vd_soff, 0);
+      for (int grp = 0; grp < 4; grp++) {
+        const int dw = grp >> 1;
+        const uint32_t sel = (grp & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t b0[4], b1[4], b2[4], b3[4];
+        for (int k = 0; k < 4; k++) {
+          const int h2 = k >> 1, ia = 2 * (k & 1);
+          const uint32_t wa = dw ? vr[h2][ia].y : vr[h2][ia].x;
+          const uint32_t wb = dw ? vr[h2][ia + 1].y : vr[h2][ia + 1].x;
+          const uint32_t x = perm(wb, wa, sel);  // [a.byte, a.byte+1, b.byte, b.byte+1]
+          const uint32_t y = x >> 8;
+          const f16x2 dd = as_f16x2(dsc[k]);
+          // a low nibble under exponent 25 reads 1024 + n, a high nibble
+          // left in bits 4..7 under exponent 21 reads 64 + n
+          b0[k] = as_u32((as_f16x2((x & 0x000F000Fu) | 0x64006400u) - c1032) * dd);
+          b1[k] = as_u32((as_f16x2((x & 0x00F000F0u) | 0x54005400u) - c72) * dd);
+          b2[k] = as_u32((as_f16x2((y & 0x000F000Fu) | 0x64006400u) - c1032) * dd);
+          b3[k] = as_u32((as_f16x2((y & 0x00F000F0u) | 0x54005400u) - c72) * dd);
+        }
+        if (grp == 3) {
+          // every V byte of this step consumed: refill with the next step's
+          for (int h2 = 0; h2 < 2; h2++)
+            for (int i = 0; i < 4; i++)
+              vr[h2][i] = __builtin_amdgcn_raw_buffer_load_b64(rv, v_voff + 128 * i, nx[h2]->v_soff, 0);
+        }
+        const int jb = 2 * grp;
+        const f16x8 B0 = pack8(b0[0], b0[1], b0[2], b0[3]);  // tile jb     (byte lo nibble)
+        const f16x8 B1 = pack8(b1[0], b1[1], b1[2], b1[3]);  // tile jb + 8 (byte hi nibble)
+        const f16x8 B2 = pack8(b2[0], b2[1], b2[2], b2[3]);  // tile jb + 1
+        const f16x8 B3 = pack8(b3[0], b3[1], b3[2], b3[3]);  // tile jb + 9
+        for (int t = 0; t < NQT; t++) {
+          o[t][jb] = mfma16x16x32(pop[t], B0, o[t][jb]);
+          o[t][jb + 8] = mfma16x16x32(pop[t], B1, o[t][jb + 8]);
+          o[t][jb + 1] = mfma16x16x32(pop[t], B2, o[t][jb + 1]);
+          o[t][jb + 9] = mfma16x16x32(pop[t], B3, o[t][jb + 9]);
+        }
       }
-    }
-  };
 
-  // two register buffers: the loads of the next step are in flight while
-  // the current one is computed; page-table entries are read two steps
-  // ahead.  The prefetch is issued unconditionally (a step past the end
-  // re-reads the wave's last valid step) so every wait for the current
-  // step's data leaves the next step's loads outstanding.
-  {
-    const int stride = kWaves * kStep;
-    const int c_first = c_begin + wave * kStep;
-    if (c_first < c_end) {
-      // last step start of this wave (wave-uniform)
-      const int c_last = c_first + ((c_end - 1 - c_first) / stride) * stride;
-      StepRaw A, B;
-      int c = c_first;
-      int2 pgA = step_pages(a, c, c_end);
-      issue_step(A, a, g, c, c_end, pgA, n, lg);
-      int2 pgB = step_pages(a, min(c + stride, c_last), c_end);
-      while (true) {
-        const int cn = c + stride;
-        issue_step(B, a, g, min(cn, c_last), c_end, pgB, n, lg);
-        const int2 pgA_next = step_pages(a, min(cn + stride, c_last), c_end);
-        compute(A, c, pgA);
-        c = cn;
-        if (c > c_last) break;
-        const int cn2 = c + stride;
-        issue_step(A, a, g, min(cn2, c_last), c_end, pgA_next, n, lg);
-        const int2 pgB_next = step_pages(a, min(cn2 + stride, c_last), c_end);
-        compute(B, c, pgB);
-        c = cn2;
-        if (c > c_last) break;
-        pgA = pgA_next;
-        pgB = pgB_next;
-      }
+      c += stride;
+      if (c > c_last) break;
+      cur0 = nxt0;
+      cur1 = nxt1;
+      nxt0 = nn0;
+      nxt1 = nn1;
     }
   }
 
   // ---------------------------------------------------------------- workgroup merge
+  // every wave parks its state in LDS (accumulator layout), then all threads
+  // merge the 4 states element-wise in wave order
   for (int t = 0; t < NQT; t++) {
     lsum[t] += lane_xor(lsum[t], 16);
     lsum[t] += lane_xor(lsum[t], 32);
   }
-  for (int w = 0; w < kWaves; w++) {
-    if (wave == w) {
-      for (int t = 0; t < NQT; t++) {
-        float fo[4], fw[4];
-        float mold = 0.f, lold = 0.f, mn = m[t];
-        if (w > 0) {
-          mold = lds_m[t * 16 + n];
-          lold = lds_l[t * 16 + n];
-          mn = fmaxf(mold, m[t]);
-        }
-        const float a_old = w > 0 ? fast_exp2(mold - mn) : 0.f;
-        const float a_new = fast_exp2(m[t] - mn);
-        for (int i = 0; i < 4; i++) {
-          fo[i] = lane_get(a_old, 4 * lg + i);
-          fw[i] = lane_get(a_new, 4 * lg + i);
-        }
-        if (lg == 0) {
-          lds_m[t * 16 + n] = mn;
-          lds_l[t * 16 + n] = lold * a_old + lsum[t] * a_new;
-        }
-        if (t * 16 + 4 * lg < rows_here) {
-          for (int j = 0; j < 16; j++) {
-            const int dim = o_dim(n, j);
-            for (int i = 0; i < 4; i++) {
-              float *p = &lds_o[(t * 16 + 4 * lg + i) * 256 + dim];
-              *p = (w > 0 ? *p * fo[i] : 0.f) + o[t][j][i] * fw[i];
-            }
-          }
-        }
-      }
-    }
-    __syncthreads();
+  static_assert(NQT == 1, "the workgroup merge handles one 16-row tile");
+  if (lg == 0) {
+    lds_m[wave * 16 + n] = m[0];
+    lds_l[wave * 16 + n] = lsum[0];
   }
+  for (int j = 0; j < 16; j++)
+    *reinterpret_cast<f32x4 *>(&lds_o[((wave * 16 + j) * 64 + lane) * 4]) = o[0][j];
+  __syncthreads();
 
-  // ---------------------------------------------------------------- partial out
-  const int H = a.H;
   const size_t rows_total = (size_t)a.n_rows;
+  const size_t sp = (size_t)g * a.n_splits + split;
   {
-    const size_t sp = (size_t)g * a.n_splits + split;
-    for (int idx = threadIdx.x; idx < rows_here * 64; idx += 256) {
-      const int r = idx >> 6, c = (idx & 63) * 4;
-      const f32x4 v = *reinterpret_cast<const f32x4 *>(&lds_o[r * 256 + c]);
-      st_dev4(a.part_o + (sp * rows_total + row_base + r) * 256 + c, v);
-    }
-    for (int r = threadIdx.x; r < rows_here; r += 256)
-      st_dev2(a.part_ml + sp * rows_total + row_base + r, lds_m[r], lds_l[r]);
-  }
-
-  // ---------------------------------------------------------------- first-level combine
-  // every wave's partial stores complete before the arrival is counted
-  uint32_t *cnt = a.counters + ((size_t)pass * H + g) * kCounterStride;
-  const int grp = split / kGroup;
-  const int gsize = min(kGroup, a.n_splits - grp * kGroup);
-  wait_all_memory();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = atomicAdd(&cnt[grp], 1u);
-    lds_flag = (prev == (uint32_t)(gsize - 1));
-  }
-  __syncthreads();
-  if (!lds_flag) return;
-  {
-    const size_t s0 = (size_t)g * a.n_splits + (size_t)grp * kGroup;
-    const size_t gi = (size_t)g * a.n_groups + grp;
-    for (int r = wave; r < rows_here; r += kWaves) {
-      const int row = row_base + r;
-      float M, L;
-      f32x4 acc;
-      merge_row(a.part_ml + s0 * rows_total, a.part_o + s0 * rows_total * 256, gsize, rows_total,
-                row, lane, M, L, acc);
-      if (lane == 0) st_dev2(a.grp_ml + gi * rows_total + row, M, L);
-      st_dev4(a.grp_o + (gi * rows_total + row) * 256 + 4 * lane, acc);
+    // thread -> accumulator lane L, tiles 4*(tid/64) .. +3, rows 4*(L/16)+i
+    const int L = threadIdx.x & 63, jq = threadIdx.x >> 6;
+    const int Ln = L & 15, Llg = L >> 4;
+    for (int i = 0; i < 4; i++) {
+      const int r = 4 * Llg + i;
+      if (r >= rows_here) continue;
+      float mw[kWaves], M = -1e30f;
+      for (int w = 0; w < kWaves; w++) {
+        mw[w] = lds_m[w * 16 + r];
+        M = fmaxf(M, mw[w]);
+      }
+      float f[kWaves], Ls = 0.f;
+      for (int w = 0; w < kWaves; w++) {
+        f[w] = fast_exp2(mw[w] - M);
+        Ls += lds_l[w * 16 + r] * f[w];
+      }
+      float val[4];
+      for (int jj = 0; jj < 4; jj++) {
+        const int j = 4 * jq + jj;
+        float acc = 0.f;
+        for (int w = 0; w < kWaves; w++) acc += f[w] * lds_o[((w * 16 + j) * 64 + L) * 4 + i];
+        val[jj] = acc;
+      }
+      float *prow = a.part_o + (sp * rows_total + row_base + r) * 256;
+      // tiles j, j+1 hold dims d, d+1 (j even, same group of 8)
+      *reinterpret_cast<float2 *>(prow + o_dim(Ln, 4 * jq)) = make_float2(val[0], val[1]);
+      *reinterpret_cast<float2 *>(prow + o_dim(Ln, 4 * jq + 2)) = make_float2(val[2], val[3]);
+      if (jq == 0 && Ln == 0) a.part_ml[sp * rows_total + row_base + r] = make_float2(M, Ls);
     }
   }
-  wait_all_memory();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    atomicExch(&cnt[grp], 0u);
-    const uint32_t prev = atomicAdd(&cnt[kCounterStride - 1], 1u);
-    lds_flag = (prev == (uint32_t)(a.n_groups - 1));
-  }
-  __syncthreads();
-  if (!lds_flag) return;
+}
 
-  // ---------------------------------------------------------------- final combine
-  for (int r = wave; r < rows_here; r += kWaves) {
-    const int row = row_base + r;
-    const size_t g0 = (size_t)g * a.n_groups;
-    float M, L;
-    f32x4 acc;
-    merge_row(a.grp_ml + g0 * rows_total, a.grp_o + g0 * rows_total * 256, a.n_groups, rows_total,
-              row, lane, M, L, acc);
-    float y[4];
-    const float inv = 1.0f / L;
-    for (int i = 0; i < 4; i++) y[i] = acc[i] * inv;
-    fwht256_lane4(y, lane);
-    const int qi = row >> 3, hl = row & 7;
-    float *op = a.out + ((size_t)qi * a.n_q_heads + (size_t)g * kGqa + hl) * 256 + 4 * lane;
-    *reinterpret_cast<f32x4 *>(op) = f32x4{y[0], y[1], y[2], y[3]};
+// Combine of the split partials of one query row of one KV head, after the
+// split kernel (the kernel boundary makes every partial visible): the m of
+// all splits give the common max, each wave sums its strided share of the
+// O rows (loaded before they are needed) in ascending split order, the 8
+// wave sums add in fixed order, then O / l goes through the inverse
+// Walsh-Hadamard transform.  Deterministic for a given split plan.
+constexpr int kCombineWaves = 8;
+constexpr int kCombineBatch = 16;
+
+__global__ __launch_bounds__(kCombineWaves * 64) void attn_combine_kernel(const SplitArgs a) {
+  __shared__ float lds_w[kMaxSplitsPerHead];
+  __shared__ float lds_red[kCombineWaves];
+  __shared__ f32x4 lds_acc[kCombineWaves][64];
+  const int row = blockIdx.x, g = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int S = a.n_splits;
+  const size_t rows_total = (size_t)a.n_rows;
+  const size_t base = (size_t)g * S;
+  const float *po = a.part_o + (base * rows_total + row) * 256 + 4 * lane;
+  const size_t sstride = rows_total * 256;
+
+  // first batch of this wave's O rows, issued before the (m, l) pass
+  f32x4 ov[kCombineBatch];
+  for (int k = 0; k < kCombineBatch; k++) {
+    const int sidx = wave + kCombineWaves * k;
+    if (sidx < S) ov[k] = *reinterpret_cast<const f32x4 *>(po + (size_t)sidx * sstride);
   }
-  if (threadIdx.x == 0) atomicExch(&cnt[kCounterStride - 1], 0u);
+  float2 ml = make_float2(-1e30f, 0.f);
+  if (tid < S) ml = a.part_ml[(base + tid) * rows_total + row];
+  // common max over the splits
+  float mx = ml.x;
+  for (int msk = 32; msk >= 1; msk >>= 1) mx = fmaxf(mx, lane_xor(mx, msk));
+  if (lane == 0) lds_red[wave] = mx;
+  __syncthreads();
+  float M = lds_red[0];
+  for (int w = 1; w < kCombineWaves; w++) M = fmaxf(M, lds_red[w]);
+  const float wgt = tid < S ? fast_exp2(ml.x - M) : 0.f;
+  if (tid < S) lds_w[tid] = wgt;
+  float lw = wgt * ml.y;
+  for (int msk = 32; msk >= 1; msk >>= 1) lw += lane_xor(lw, msk);
+  __syncthreads();  // lds_red reads above are done before it is reused
+  if (lane == 0) lds_red[wave] = lw;
+  __syncthreads();
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < kCombineBatch; k++) {
+    const int sidx = wave + kCombineWaves * k;
+    if (sidx < S) acc += lds_w[sidx] * ov[k];
+  }
+  for (int k0 = kCombineBatch; wave + kCombineWaves * k0 < S; k0 += kCombineBatch) {
+    for (int k = 0; k < kCombineBatch; k++) {
+      const int sidx = wave + kCombineWaves * (k0 + k);
+      if (sidx < S) ov[k] = *reinterpret_cast<const f32x4 *>(po + (size_t)sidx * sstride);
+    }
+    for (int k = 0; k < kCombineBatch; k++) {
+      const int sidx = wave + kCombineWaves * (k0 + k);
+      if (sidx < S) acc += lds_w[sidx] * ov[k];
+    }
+  }
+  lds_acc[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  float L = 0.f;
+  for (int w = 0; w < kCombineWaves; w++) L += lds_red[w];
+  f32x4 tot = lds_acc[0][lane];
+  for (int w = 1; w < kCombineWaves; w++) tot += lds_acc[w][lane];
+  float y[4];
+  const float inv = 1.0f / L;
+  for (int i = 0; i < 4; i++) y[i] = tot[i] * inv;
+  fwht256_lane4(y, lane);
+  const int qi = row >> 3, hl = row & 7;
+  float *op = a.out + ((size_t)qi * a.n_q_heads + (size_t)g * kGqa + hl) * 256 + 4 * lane;
+  *reinterpret_cast<f32x4 *>(op) = f32x4{y[0], y[1], y[2], y[3]};
 }
 
 // ---------------------------------------------------------------- host side
 
-template <int NQT, bool QF32>
-static const void *kernel_ptr() {
-  return reinterpret_cast<const void *>(&attn_splitk_kernel<NQT, QF32>);
-}
-
-int attn_target_splits(int n_kv_heads, int n_rows) {
+// Compute units of the current device, cached per device.  The split plan
+// targets one 4-wave workgroup per CU and KV head share: measured on
+// MI355X, one workgroup per CU (1 wave per SIMD, 128 splits per KV head)
+// beats two (256 splits) for decode at 118,750 and 240,000 cells.
+static int device_cus() {
   static int cached_dev = -1, cached_cus = 0;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 64;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
   if (dev != cached_dev) {
     hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 64;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 256;
     cached_cus = prop.multiProcessorCount;
     cached_dev = dev;
   }
+  return cached_cus;
+}
+
+int attn_target_splits(int n_kv_heads, int n_rows) {
   (void)n_rows;
-  int per_head = cached_cus / (n_kv_heads > 0 ? n_kv_heads : 1);
+  const int per_head = device_cus() / (n_kv_heads > 0 ? n_kv_heads : 1);
   return per_head < 1 ? 1 : per_head;
 }
 
@@ -540,10 +566,11 @@ int launch_attn_splitk(const AttnCall &c) {
   const int rows_per_pass = 16;
   const int passes = (n_rows + rows_per_pass - 1) / rows_per_pass;
   if (passes > kMaxPasses) return KV_ERR_UNSUPPORTED;
+  if (c.max_limit > (1 << 30)) return KV_ERR_UNSUPPORTED;
   int target = attn_target_splits(H, n_rows) / passes;
   if (target < 1) target = 1;
   const SplitPlan plan = plan_splits(c.max_limit, target);
-  const WsLayout ws = ws_layout(H, n_rows, plan.n_splits, plan.n_groups);
+  const WsLayout ws = ws_layout(H, n_rows, plan.n_splits);
   if (ws.total > c.ws_bytes) return KV_ERR_WORKSPACE;
 
   SplitArgs a;
@@ -554,14 +581,23 @@ int launch_attn_splitk(const AttnCall &c) {
   a.pt = c.seq->page_table;
   a.q = c.q;
   a.out = c.out;
-  a.counters = (uint32_t *)(base + ws.counters);
   a.part_ml = (float2 *)(base + ws.part_ml);
   a.part_o = (float *)(base + ws.part_o);
-  a.grp_ml = (float2 *)(base + ws.grp_ml);
-  a.grp_o = (float *)(base + ws.grp_o);
   a.n_pages = pool->n_pages;
   a.P = pool->page_size;
   a.H = H;
+  a.p_shift = -1;
+  for (int sh = 0; sh < 31; sh++)
+    if ((1 << sh) == a.P) a.p_shift = sh;
+  {
+    const size_t kb = run_bytes(pool->fmt, 0, pool->n_pages, a.P, H, kHeadDim);
+    const size_t sb = run_bytes(pool->fmt, 1, pool->n_pages, a.P, H, kHeadDim);
+    const size_t vb = run_bytes(pool->fmt, 2, pool->n_pages, a.P, H, kHeadDim);
+    if (kb > 0x7fffffffu || sb > 0x7fffffffu || vb > 0x7fffffffu) return KV_ERR_UNSUPPORTED;
+    a.k_bytes = (int)kb;
+    a.ks_bytes = (int)sb;
+    a.v_bytes = (int)vb;
+  }
   a.n_q_heads = c.n_q_heads;
   a.n_rows = n_rows;
   a.rows_per_pass = rows_per_pass;
@@ -570,13 +606,14 @@ int launch_attn_splitk(const AttnCall &c) {
   a.scale2 = c.scale * 1.4426950408889634f;
   a.steps_per_split = plan.steps_per_split;
   a.n_splits = plan.n_splits;
-  a.n_groups = plan.n_groups;
 
   dim3 grid(plan.n_splits, H, passes);
   if (qf32)
     launch((attn_splitk_kernel<1, true>), grid, dim3(256), c.stream, a);
   else
     launch((attn_splitk_kernel<1, false>), grid, dim3(256), c.stream, a);
+  if (int e = launch_status()) return e;
+  launch(attn_combine_kernel, dim3(n_rows, H), dim3(kCombineWaves * 64), c.stream, a);
   return launch_status();
 }
 

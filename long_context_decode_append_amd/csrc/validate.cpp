@@ -81,34 +81,36 @@ SplitPlan plan_splits(int64_t n_ctx, int target_splits_per_head) {
   const int64_t by_work = (steps + kWaves - 1) / kWaves;  // at least one step per wave
   if (s > by_work) s = by_work;
   if (s < 1) s = 1;
-  p.steps_per_split = (int)((steps + s - 1) / s);
+  // whole rounds of the workgroup's waves, so they finish together
+  int64_t per = (steps + s - 1) / s;
+  per = (per + kWaves - 1) / kWaves * kWaves;
+  p.steps_per_split = (int)per;
   p.n_splits = (int)((steps + p.steps_per_split - 1) / p.steps_per_split);
-  p.n_groups = (p.n_splits + kGroup - 1) / kGroup;
   return p;
 }
 
 static size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-WsLayout ws_layout(int n_kv_heads, int n_rows, int n_splits, int n_groups) {
+WsLayout ws_layout(int n_kv_heads, int n_rows, int n_splits) {
   WsLayout w;
   size_t off = 0;
-  w.counters = off;
-  off = up256(off + sizeof(uint32_t) * (size_t)kMaxPasses * n_kv_heads * kCounterStride);
   w.part_ml = off;
   off = up256(off + 8 * (size_t)n_kv_heads * n_splits * n_rows);
   w.part_o = off;
   off = up256(off + 4 * (size_t)kHeadDim * n_kv_heads * n_splits * n_rows);
-  w.grp_ml = off;
-  off = up256(off + 8 * (size_t)n_kv_heads * n_groups * n_rows);
-  w.grp_o = off;
-  off = up256(off + 4 * (size_t)kHeadDim * n_kv_heads * n_groups * n_rows);
   w.total = off;
   return w;
 }
 
 size_t ws_bytes_bound(int n_kv_heads, int n_rows, int64_t max_ctx) {
-  SplitPlan p = plan_splits(max_ctx, kMaxSplitsPerHead);
-  return ws_layout(n_kv_heads, n_rows, p.n_splits, p.n_groups).total;
+  // plan_splits never returns more splits than min(kMaxSplitsPerHead,
+  // ceil(steps / kWaves)), which grows with the context: a bound for every
+  // context up to max_ctx and every device
+  const int64_t steps = (max_ctx + kStep - 1) / kStep;
+  int64_t s = (steps + kWaves - 1) / kWaves;
+  if (s > kMaxSplitsPerHead) s = kMaxSplitsPerHead;
+  if (s < 1) s = 1;
+  return ws_layout(n_kv_heads, n_rows, (int)s).total;
 }
 
 }  // namespace k8v4

@@ -15,10 +15,8 @@ constexpr int kStep = 32;        // cells per attention step of one wave
 constexpr int kWaves = 4;        // waves per attention workgroup
 constexpr int kMaxRows = 128;    // verify: at most 16 queries x 8 heads
 constexpr int kMaxQ = 16;
-constexpr int kMaxSplitsPerHead = 512;
-constexpr int kGroup = 16;       // splits merged by one first-level combine
+constexpr int kMaxSplitsPerHead = 256;
 constexpr int kMaxPasses = 8;    // row passes (16 rows each) of one verify call
-constexpr int kCounterStride = kMaxSplitsPerHead / kGroup + 1;  // group counters + head counter
 
 int check_pool(const kv_pool *pool, int need_fmt);
 int check_seq(const kv_seq *seq, const kv_pool *pool);
@@ -28,22 +26,18 @@ int check_aligned16(const void *p);
 
 // Split-K plan for decode/verify over cells [0, n_ctx).
 struct SplitPlan {
-  int steps_per_split;  // kStep-cell steps per split
+  int steps_per_split;  // kStep-cell steps per split (a multiple of kWaves)
   int n_splits;         // splits per KV head
-  int n_groups;         // first-level combine groups per KV head
 };
 SplitPlan plan_splits(int64_t n_ctx, int target_splits_per_head);
 
 // Workspace layout (byte offsets) for n_rows query rows and a plan.
 struct WsLayout {
-  size_t counters;  // uint32 [kMaxPasses][H][kCounterStride]
   size_t part_ml;   // float2 [H][n_splits][n_rows]
   size_t part_o;    // float  [H][n_splits][n_rows][256]
-  size_t grp_ml;    // float2 [H][n_groups][n_rows]
-  size_t grp_o;     // float  [H][n_groups][n_rows][256]
   size_t total;
 };
-WsLayout ws_layout(int n_kv_heads, int n_rows, int n_splits, int n_groups);
+WsLayout ws_layout(int n_kv_heads, int n_rows, int n_splits);
 
 // Upper bound used by attn_workspace_bytes: the largest plan any device
 // can choose for max_ctx cells.
