@@ -72,11 +72,14 @@ enum {
  *                   (page*H + g)*144*P: the 16 nibble bytes of block b
  *                   (dims 32b..32b+31, rotated basis) of a slot at
  *                   slot*128 + b*16 (byte i = element i | element i+16 << 4),
- *                   and the block's fp16 scale at 128*P + (b*P + slot)*2.
+ *                   and the block's fp16 scale after the 128*P nibble
+ *                   bytes, grouped by 16 slots:
+ *                   128*P + (slot/16)*256 + b*32 + (slot%16)*2.
  *   run[3] unused (may be NULL).
- * Keeping a block's scale in a strip beside the nibbles (rather than in
- * front of them) keeps every load 8- or 16-byte aligned; kv_gather returns
- * the conventional 18-byte blocks.
+ * Keeping the scales apart from the nibbles (rather than in front of each
+ * block) keeps every load 8- or 16-byte aligned, and grouping them by 16
+ * slots makes the scales of 16 consecutive cells one 256-byte read;
+ * kv_gather returns the conventional 18-byte blocks.
  */
 typedef struct kv_pool {
   int32_t fmt;        /* KV_FMT_*                               */

@@ -26,10 +26,11 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include")]
 
-# per-source extra flags: the quantizers must not fuse multiply and add
+# per-source extra flags: the quantizers must not fuse multiply and add; the
+# split attention kernel keeps its MFMA accumulators in VGPRs
 SOURCES = {
     "append_gather.hip": ["-ffp-contract=off"],
-    "attn_splitk.hip": [],
+    "attn_splitk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "attn_prefill.hip": [],
     "api.cpp": ["-x", "hip"],
     "validate.cpp": ["-x", "hip"],

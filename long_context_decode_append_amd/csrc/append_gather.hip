@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void append_k8v4_kernel(const AppendArgs a) {
     *reinterpret_cast<uint32_t *>(vt + (size_t)slot * 128 + b * 16 + 4 * j) = vcodes | (hi << 4);
   }
   if (j == 0) {
-    *reinterpret_cast<uint16_t *>(vt + (size_t)128 * a.P + ((size_t)b * a.P + slot) * 2) = d16;
+    *reinterpret_cast<uint16_t *>(vt + q4_scale_off(a.P, slot, b)) = d16;
   }
 }
 
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void gather_k8v4_kernel(const GatherArgs a) {
   for (int e = lane; e < 144; e += 64) {
     const int b = e / 18, off = e % 18;
     uint8_t byte;
-    if (off < 2) byte = vt[(size_t)128 * a.P + ((size_t)b * a.P + slot) * 2 + off];
+    if (off < 2) byte = vt[q4_scale_off(a.P, slot, b) + off];
     else byte = vt[(size_t)slot * 128 + b * 16 + (off - 2)];
     a.ovb[o * 144 + e] = bad ? 0xff : byte;
   }

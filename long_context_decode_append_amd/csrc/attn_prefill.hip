@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const PrefillArgs a) 
         // V: block `part` of this cell: 16 nibble bytes + fp16 scale
         const uint8_t *vt = a.vq + tile * q4_tile;
         vw = *reinterpret_cast<const u32x4 *>(vt + (size_t)slot * 128 + 16 * part);
-        vd = *reinterpret_cast<const uint16_t *>(vt + (size_t)128 * a.P + ((size_t)part * a.P + slot) * 2);
+        vd = *reinterpret_cast<const uint16_t *>(vt + q4_scale_off(a.P, slot, part));
       }
       (void)d1;
       // K -> exact fp16 codes

@@ -72,6 +72,13 @@ __device__ __forceinline__ f16x8 pack8(uint32_t a, uint32_t b, uint32_t c, uint3
   return __builtin_bit_cast(f16x8, u);
 }
 
+// (x & m) | c in one VALU op (the compiler splits it when both are literals)
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
+  return r;
+}
+
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit elements (gfx9 family)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -88,7 +95,7 @@ struct Half {
   int k_soff;     // byte offset of the half's first cell in the K-code run
   int ks_soff;    // ... in the K-scale run
   int v_soff;     // ... of its nibble bytes in the V run
-  int vd_soff;    // ... of its block-0 scale in the V run
+  int vd_soff;    // ... of its 256-byte scale group in the V run
 };
 
 __device__ __forceinline__ int page_of(const SplitArgs &a, int pos) {
@@ -104,7 +111,7 @@ __device__ __forceinline__ Half make_half(const SplitArgs &a, int g, int pos, in
   h.k_soff = (tile * a.P + slot0) * 256;
   h.ks_soff = (tile * a.P + slot0) * 8;
   h.v_soff = tile * 144 * a.P + slot0 * 128;
-  h.vd_soff = tile * 144 * a.P + 128 * a.P + slot0 * 2;
+  h.vd_soff = tile * 144 * a.P + 128 * a.P + slot0 * 16;  // slot0 % 16 == 0: group slot0 / 16
   return h;
 }
 
@@ -121,9 +128,9 @@ __device__ __forceinline__ void step_halves(const SplitArgs &a, int g, int c, in
 
 template <int NQT, bool QF32>
 __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) {
-  __shared__ float lds_o[kWaves * 16 * 64 * 4];   // wave states, accumulator layout
-  __shared__ float lds_m[kWaves * 16];
-  __shared__ float lds_l[kWaves * 16];
+  __shared__ __attribute__((aligned(16))) float lds_o[kWaves * 16 * 64 * 4];  // wave states, accumulator layout
+  __shared__ __attribute__((aligned(16))) float lds_m[kWaves * 16];
+  __shared__ __attribute__((aligned(16))) float lds_l[kWaves * 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -149,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
   const int k_voff = n * 256 + 16 * lg;            // + 64 j: 16 bytes of cell n
   const int ks_voff = 32 * lg;                     // scales of cells 4lg..4lg+3
   const int v_voff = 4 * lg * 128 + 8 * n;         // + 128 i: bytes [8n, 8n+8) of cell 4lg+i
-  const int vd_voff = ((n >> 1) * a.P + 4 * lg) * 2;  // d16[block n/2][cells 4lg..4lg+3]
+  const int vd_voff = (n >> 1) * 32 + 8 * lg;       // d16[block n/2][cells 4lg..4lg+3] of the group
 
   u32x4 kr[2][4];
   f32x4 ksr[2][2];
@@ -371,10 +378,10 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
           const f16x2 dd = as_f16x2(dsc[k]);
           // a low nibble under exponent 25 reads 1024 + n, a high nibble
           // left in bits 4..7 under exponent 21 reads 64 + n
-          b0[k] = as_u32((as_f16x2((x & 0x000F000Fu) | 0x64006400u) - c1032) * dd);
-          b1[k] = as_u32((as_f16x2((x & 0x00F000F0u) | 0x54005400u) - c72) * dd);
-          b2[k] = as_u32((as_f16x2((y & 0x000F000Fu) | 0x64006400u) - c1032) * dd);
-          b3[k] = as_u32((as_f16x2((y & 0x00F000F0u) | 0x54005400u) - c72) * dd);
+          b0[k] = as_u32((as_f16x2(and_or(x, 0x000F000Fu, 0x64006400u)) - c1032) * dd);
+          b1[k] = as_u32((as_f16x2(and_or(x, 0x00F000F0u, 0x54005400u)) - c72) * dd);
+          b2[k] = as_u32((as_f16x2(and_or(y, 0x000F000Fu, 0x64006400u)) - c1032) * dd);
+          b3[k] = as_u32((as_f16x2(and_or(y, 0x00F000F0u, 0x54005400u)) - c72) * dd);
         }
         if (grp == 3) {
           // every V byte of this step consumed: refill with the next step's
@@ -423,34 +430,39 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
   const size_t rows_total = (size_t)a.n_rows;
   const size_t sp = (size_t)g * a.n_splits + split;
   {
-    // thread -> accumulator lane L, tiles 4*(tid/64) .. +3, rows 4*(L/16)+i
+    // thread -> accumulator lane L and tiles 4 jq .. 4 jq + 3; the lane holds
+    // rows 4 (L / 16) + i, i = 0..3, of each tile
     const int L = threadIdx.x & 63, jq = threadIdx.x >> 6;
     const int Ln = L & 15, Llg = L >> 4;
+    f32x4 mw[kWaves], lw[kWaves];
+    for (int w = 0; w < kWaves; w++) {
+      mw[w] = *reinterpret_cast<const f32x4 *>(&lds_m[w * 16 + 4 * Llg]);
+      lw[w] = *reinterpret_cast<const f32x4 *>(&lds_l[w * 16 + 4 * Llg]);
+    }
+    f32x4 M = mw[0];
+    for (int w = 1; w < kWaves; w++)
+      for (int i = 0; i < 4; i++) M[i] = fmaxf(M[i], mw[w][i]);
+    f32x4 f[kWaves], Ls = {0.f, 0.f, 0.f, 0.f};
+    for (int w = 0; w < kWaves; w++)
+      for (int i = 0; i < 4; i++) {
+        f[w][i] = fast_exp2(mw[w][i] - M[i]);
+        Ls[i] += lw[w][i] * f[w][i];
+      }
+    f32x4 val[4];
+    for (int jj = 0; jj < 4; jj++) {
+      const int j = 4 * jq + jj;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int w = 0; w < kWaves; w++) acc += f[w] * *reinterpret_cast<const f32x4 *>(&lds_o[((w * 16 + j) * 64 + L) * 4]);
+      val[jj] = acc;
+    }
     for (int i = 0; i < 4; i++) {
       const int r = 4 * Llg + i;
       if (r >= rows_here) continue;
-      float mw[kWaves], M = -1e30f;
-      for (int w = 0; w < kWaves; w++) {
-        mw[w] = lds_m[w * 16 + r];
-        M = fmaxf(M, mw[w]);
-      }
-      float f[kWaves], Ls = 0.f;
-      for (int w = 0; w < kWaves; w++) {
-        f[w] = fast_exp2(mw[w] - M);
-        Ls += lds_l[w * 16 + r] * f[w];
-      }
-      float val[4];
-      for (int jj = 0; jj < 4; jj++) {
-        const int j = 4 * jq + jj;
-        float acc = 0.f;
-        for (int w = 0; w < kWaves; w++) acc += f[w] * lds_o[((w * 16 + j) * 64 + L) * 4 + i];
-        val[jj] = acc;
-      }
       float *prow = a.part_o + (sp * rows_total + row_base + r) * 256;
       // tiles j, j+1 hold dims d, d+1 (j even, same group of 8)
-      *reinterpret_cast<float2 *>(prow + o_dim(Ln, 4 * jq)) = make_float2(val[0], val[1]);
-      *reinterpret_cast<float2 *>(prow + o_dim(Ln, 4 * jq + 2)) = make_float2(val[2], val[3]);
-      if (jq == 0 && Ln == 0) a.part_ml[sp * rows_total + row_base + r] = make_float2(M, Ls);
+      *reinterpret_cast<float2 *>(prow + o_dim(Ln, 4 * jq)) = make_float2(val[0][i], val[1][i]);
+      *reinterpret_cast<float2 *>(prow + o_dim(Ln, 4 * jq + 2)) = make_float2(val[2][i], val[3][i]);
+      if (jq == 0 && Ln == 0) a.part_ml[sp * rows_total + row_base + r] = make_float2(M[i], Ls[i]);
     }
   }
 }

@@ -42,6 +42,14 @@ __device__ __forceinline__ void i8x4_to_f16_biased(uint32_t w, uint32_t &lo, uin
   hi = perm(0x64646464u, u, 0x04030402u);
 }
 
+// Byte offset, inside the 144 * P byte q4_0 tile of one (page, KV head), of
+// the fp16 scale of block b of slot s: the nibble bytes fill the first
+// 128 * P bytes (slot s at 128 s); the scales follow in groups of 16 slots,
+// 256 bytes per group laid out [block][slot % 16].
+__host__ __device__ __forceinline__ size_t q4_scale_off(int P, int slot, int b) {
+  return (size_t)128 * P + (size_t)(slot >> 4) * 256 + (size_t)b * 32 + (size_t)(slot & 15) * 2;
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }

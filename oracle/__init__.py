@@ -165,7 +165,8 @@ class OraclePool:
     run 2: V q4_0 tile (k8v4, q4_0) or V codes (int8 format)
     run 3: V scales (int8 format only)
     A q4_0 (page, head) tile is 144*P bytes: nibble bytes of block b of slot s
-    at s*128 + b*16, the fp16 scale at 128*P + (b*P + s)*2.
+    at s*128 + b*16; the fp16 scale of block b of slot s at
+    128*P + (s//16)*256 + b*32 + (s%16)*2 (scales grouped by 16 slots).
     """
 
     def __init__(self, fmt: int, n_pages: int, page_size: int, n_kv_heads: int,

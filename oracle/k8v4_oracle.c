@@ -191,7 +191,9 @@ long orc_cell_bytes(int fmt, int n_kv_heads, int D) {
 /* [PR711, How: three runs for k8v4].  A logical cell p lives in       */
 /* physical page pt[p / P] at slot p % P.  Q4_0 data inside a          */
 /* (page, head) tile of 144*P bytes: the 16 nibble bytes of block b of */
-/* slot s at s*128 + b*16, the fp16 scale at 128*P + (b*P + s)*2.      */
+/* slot s at s*128 + b*16; the fp16 scales after the 128*P nibble     */
+/* bytes, in groups of 16 slots (256 bytes each, [block][slot % 16]):  */
+/* block b of slot s at 128*P + (s/16)*256 + b*32 + (s%16)*2.          */
 /* ------------------------------------------------------------------ */
 
 typedef struct {
@@ -208,12 +210,16 @@ static void put_int8_head(uint8_t *codes_run, uint8_t *scales_run, size_t ti, in
          4 * (ORC_D / ORC_KGROUP));
 }
 
+static size_t q4_scale_pos(int P, int slot, int b) {
+  return (size_t)128 * P + (size_t)(slot / 16) * 256 + (size_t)b * 32 + (size_t)(slot % 16) * 2;
+}
+
 static void put_q4_head(uint8_t *run, size_t ti, int P, int slot, const uint8_t *blocks) {
   uint8_t *tile = run + ti * (size_t)144 * P;
   for (int b = 0; b < ORC_D / ORC_QBLK; b++) {
     const uint8_t *blk = blocks + b * ORC_QBYTES;
     memcpy(tile + (size_t)slot * 128 + b * 16, blk + 2, 16);
-    memcpy(tile + (size_t)128 * P + ((size_t)b * P + slot) * 2, blk, 2);
+    memcpy(tile + q4_scale_pos(P, slot, b), blk, 2);
   }
 }
 
@@ -221,7 +227,7 @@ static void get_q4_head(const uint8_t *run, size_t ti, int P, int slot, uint8_t 
   const uint8_t *tile = run + ti * (size_t)144 * P;
   for (int b = 0; b < ORC_D / ORC_QBLK; b++) {
     uint8_t *blk = blocks + b * ORC_QBYTES;
-    memcpy(blk, tile + (size_t)128 * P + ((size_t)b * P + slot) * 2, 2);
+    memcpy(blk, tile + q4_scale_pos(P, slot, b), 2);
     memcpy(blk + 2, tile + (size_t)slot * 128 + b * 16, 16);
   }
 }

@@ -62,7 +62,8 @@ def test_pool_bytes_at_documented_offsets(orc):
             tile = (page * H + g) * 144 * P
             for b in range(8):
                 q = r2[tile + slot * 128 + b * 16: tile + slot * 128 + b * 16 + 16]
-                s = r2[tile + 128 * P + (b * P + slot) * 2: tile + 128 * P + (b * P + slot) * 2 + 2]
+                so = tile + 128 * P + (slot // 16) * 256 + b * 32 + (slot % 16) * 2
+                s = r2[so: so + 2]
                 assert np.array_equal(q, vb[p, g, b, 2:]) and np.array_equal(s, vb[p, g, b, :2])
 
 
