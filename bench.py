@@ -89,6 +89,32 @@ def timed_launches(torch, k8, fn, n):
     return event_mean_ms(torch, pairs)
 
 
+def timed_calls(torch, fn, n):
+    """Run fn() n times, each call (all its kernels) bracketed by events."""
+    pairs = []
+    for i in range(n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn(i)
+        e1.record()
+        pairs.append((e0, e1))
+    return event_mean_ms(torch, pairs)
+
+
+def stream_read_ceiling(torch, k8, dev):
+    """Attainable read bandwidth: a plain streaming read of 1 GiB (beyond the
+    Infinity Cache) by the library's yardstick kernel."""
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(4096, dtype=torch.uint8, device=dev)
+    k8.probe_read(buf, sink)
+    ms, _ = timed_calls(torch, lambda i: k8.probe_read(buf, sink), 5)
+    del buf
+    return {"gbs": round((1 << 30) / ms / 1e6, 1), "bytes": 1 << 30,
+            "kernel": "probe_read_kernel: 1,024 workgroups x 256 lanes, 4 x 16 B non-temporal loads in flight per lane"}
+
+
 def cpu_baseline(ctx: int, target_s: float = 12.0):
     """Time the oracle's decode attention (gather, dequantize, fp64 softmax
     attention) for one layer at ctx cells, from an oracle pool built from
@@ -232,6 +258,13 @@ def main():
     if not args.no_extra:
         del graphs
         extra = bench_extra(torch, k8, synth, dev, log)
+        extra["stream_read_ceiling"] = stream_read_ceiling(torch, k8, dev)
+        dc_ms, _ = timed_calls(torch, lambda i: k8.attn_decode(
+            pools[i % layers], tables[i % layers], q_all[0][i % layers], ctx, ws,
+            out=outs[i % layers]), 2 * layers)
+        extra["decode_118750_split_plus_combine"] = {
+            "us": round(dc_ms * 1e3, 3),
+            "hbm_frac": round(ctx * CELL_BYTES / dc_ms / 1e6 / HBM_PEAK_GBS, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -327,12 +360,26 @@ def bench_extra(torch, k8, synth, dev, log):
     reps = 8 * n_pools
     d_ms, _ = timed_launches(torch, k8, lambda i: k8.attn_decode(
         pools[i % n_pools], tables[i % n_pools], q1, ctx, ws1), reps)
+    dc_ms, _ = timed_calls(torch, lambda i: k8.attn_decode(
+        pools[i % n_pools], tables[i % n_pools], q1, ctx, ws1), reps)
     v_ms, _ = timed_launches(torch, k8, lambda i: k8.attn_verify(
         pools[i % n_pools], tables[i % n_pools], q5, nv, ws5), reps)
     b = ctx * CELL_BYTES
     out["decode_240000"] = {"us": round(d_ms * 1e3, 3), "gbs": round(b / d_ms / 1e6, 2),
                             "hbm_frac": round(b / d_ms / 1e6 / HBM_PEAK_GBS, 4),
-                            "pools_rotated": n_pools}
+                            "pools_rotated": n_pools, "kernel": "split kernel alone",
+                            "us_split_plus_combine": round(dc_ms * 1e3, 3),
+                            "hbm_frac_split_plus_combine": round(b / dc_ms / 1e6 / HBM_PEAK_GBS, 4)}
+    # context sweep on the same pools: whole decode call (split + combine)
+    sweep = {}
+    for n in (1024, 4096, 16384, 32768, 65536, 118750, 131072, 240000):
+        for i in range(n_pools):
+            k8.attn_decode(pools[i], tables[i], q1, n, ws1)
+        s_ms, _ = timed_calls(torch, lambda i: k8.attn_decode(
+            pools[i % n_pools], tables[i % n_pools], q1, n, ws1), 4 * n_pools)
+        sweep[str(n)] = {"us": round(s_ms * 1e3, 2), "gbs": round(n * CELL_BYTES / s_ms / 1e6, 1),
+                         "hbm_frac": round(n * CELL_BYTES / s_ms / 1e6 / HBM_PEAK_GBS, 4)}
+    out["decode_sweep_split_plus_combine"] = sweep
     out["verify5_240000"] = {"us": round(v_ms * 1e3, 3), "gbs": round(b / v_ms / 1e6, 2),
                              "hbm_frac": round(b / v_ms / 1e6 / HBM_PEAK_GBS, 4),
                              "n_visible": nv}

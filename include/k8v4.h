@@ -151,6 +151,14 @@ size_t attn_workspace_bytes(const kv_pool *pool, int n_q_heads, int32_t n_q, int
  * `stream` (optional: the attention calls do not need it). */
 int kv_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
+/* Measurement aid, not part of the method: one plain streaming read of the
+ * first bytes / 16 16-byte words of buf (device, 16-byte aligned) with
+ * non-temporal loads from 1,024 workgroups, the yardstick against which the
+ * attention kernels' bytes per second are read.  sink: device, 16-byte
+ * aligned, 4 KiB, written only in a case a repeated-byte fill cannot produce.
+ * Returns KV_ERR_NULL / KV_ERR_ALIGN before launching. */
+int kv_probe_read(const void *buf, size_t bytes, void *sink, void *stream);
+
 /*
  * One decode step: the query attends to cells [0, n_ctx)
  * ("#120 --kv k8v4: hybrid KV cache", How: the fused attention gathers the

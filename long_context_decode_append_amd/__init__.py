@@ -44,6 +44,7 @@ SIGNATURES = {
     "kv_gather": (_I, [_PP, _PS, C.c_int32, C.c_int32, _P, _P, _P, _P]),
     "attn_workspace_bytes": (_SZ, [_PP, _I, C.c_int32, C.c_int32]),
     "kv_workspace_init": (_I, [_P, _SZ, _P]),
+    "kv_probe_read": (_I, [_P, _SZ, _P, _P]),
     "attn_decode": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, _F, _P, _P, _SZ, _P]),
     "attn_verify": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, _P, _F, _P, _P, _SZ, _P]),
     "attn_prefill_chunk": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, C.c_int32, _F, _P, _P, _SZ, _P]),
@@ -207,6 +208,12 @@ def attn_workspace(pool: K8V4Pool, n_q: int, max_ctx: int, stream=None):
     ws = torch.empty(nb, dtype=torch.uint8, device=pool.runs[0].device)
     _check(lib().kv_workspace_init(_dev_ptr(ws, "ws"), nb, _stream(stream)), "kv_workspace_init")
     return ws
+
+
+def probe_read(buf, sink, stream=None):
+    """One plain streaming read of the device tensor buf (a bandwidth yardstick)."""
+    _check(lib().kv_probe_read(_dev_ptr(buf, "buf"), buf.numel() * buf.element_size(),
+                               _dev_ptr(sink, "sink"), _stream(stream)), "kv_probe_read")
 
 
 def attn_decode(pool: K8V4Pool, page_table, q, n_ctx: int, ws, scale: float = 0.0, out=None,

@@ -100,6 +100,12 @@ int kv_workspace_init(void *ws, size_t ws_bytes, void *stream) {
   return launch_fill_zero(ws, ws_bytes, (hipStream_t)stream);
 }
 
+int kv_probe_read(const void *buf, size_t bytes, void *sink, void *stream) {
+  if (!buf || !sink) return KV_ERR_NULL;
+  if (check_aligned16(buf) || check_aligned16(sink)) return KV_ERR_ALIGN;
+  return launch_probe_read(buf, bytes, sink, (hipStream_t)stream);
+}
+
 static int check_attn_common(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
                              int n_q_heads, const float *out) {
   if (int e = check_pool(pool, KV_FMT_K8V4)) return e;

@@ -30,6 +30,7 @@ int launch_append_k8v4(const kv_pool *pool, const kv_seq *seq, const void *k, co
 int launch_gather_k8v4(const kv_pool *pool, const kv_seq *seq, int pos0, int n, void *okc,
                        void *oks, void *ovb, hipStream_t s);
 int launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+int launch_probe_read(const void *buf, size_t bytes, void *sink, hipStream_t s);
 
 // Decode / verify: n_q query rows of 8 heads per KV head, row i of query
 // q_index attends to cells [0, limits[i]).

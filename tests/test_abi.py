@@ -104,6 +104,10 @@ def test_validation_errors_before_launch(k8):
     assert L.attn_prefill_chunk(P(pool), P(seq), dummy, 0, 16, 60, 5, 0.0, out, None, 0, None) == -3
     assert L.attn_prefill_chunk(P(pool), P(seq), dummy, 0, 16, 10, 0, 0.0, out, None, 0, None) == 0
     assert L.kv_strerror(-6) == b"workspace missing or too small"
+    # the streaming-read yardstick
+    assert L.kv_probe_read(None, 1024, dummy, None) == -1
+    assert L.kv_probe_read(dummy, 1024, None, None) == -1
+    assert L.kv_probe_read(C.c_void_p(24), 1024, dummy, None) == -7
 
 
 def test_workspace_size_is_monotone_in_context(k8):
