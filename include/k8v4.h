@@ -80,6 +80,14 @@ enum {
  * block) keeps every load 8- or 16-byte aligned, and grouping them by 16
  * slots makes the scales of 16 consecutive cells one 256-byte read;
  * kv_gather returns the conventional 18-byte blocks.
+ *
+ * The comparison formats of the same pages ("#120", Measured) use the same
+ * two kinds of half:
+ * int8 (fmt 1), 1056 bytes per cell: run[0]/run[1] K codes/scales and
+ *   run[2]/run[3] V codes/scales, each laid out like k8v4's run[0]/run[1]
+ *   (V by the K rule, unrotated).
+ * q4_0 (fmt 2), 576 bytes per cell: run[0] K and run[2] V, each a q4_0 tile
+ *   run like k8v4's run[2] (both halves rotated); run[1], run[3] unused.
  */
 typedef struct kv_pool {
   int32_t fmt;        /* KV_FMT_*                               */
@@ -127,6 +135,16 @@ int kv_append_k8v4(const kv_pool *pool, const kv_seq *seq, const void *k, const 
                    int dtype, int32_t pos0, int32_t n_tokens, void *stream);
 
 /*
+ * The same append for a pool of any of the three formats (fmt 1, 2, 3):
+ * each half follows its kind's rule above (int8: K and V by the INT8 rule;
+ * q4_0: K and V both rotated and Q4_0-coded; k8v4: as kv_append_k8v4).
+ * Same arguments and errors as kv_append_k8v4, _UNSUPPORTED for an unknown
+ * format.
+ */
+int kv_append(const kv_pool *pool, const kv_seq *seq, const void *k, const void *v, int dtype,
+              int32_t pos0, int32_t n_tokens, void *stream);
+
+/*
  * Copy the stored bytes of cells [pos0, pos0 + n) of a k8v4 pool, in
  * logical order, to contiguous device buffers ("#120 --kv k8v4: hybrid KV
  * cache", Tests: bitwise gather through a non-identity page table):
@@ -137,6 +155,20 @@ int kv_append_k8v4(const kv_pool *pool, const kv_seq *seq, const void *k, const 
  */
 int kv_gather(const kv_pool *pool, const kv_seq *seq, int32_t pos0, int32_t n, void *k_codes,
               void *k_scales, void *v_blocks, void *stream);
+
+/*
+ * kv_gather for any format: stored bytes of cells [pos0, pos0 + n) in
+ * logical order.  An int8-coded half goes to a codes array int8 [n][H][256]
+ * (16-byte aligned) and a scales array fp32 [n][H][2] (8-byte aligned); a
+ * q4_0-coded half to one block array uint8 [n][H][8][18].
+ *   k8v4: out0 K codes, out1 K scales, out2 V blocks (out3 unused)
+ *   int8: out0 K codes, out1 K scales, out2 V codes, out3 V scales
+ *   q4_0: out0 K blocks, out2 V blocks (out1, out3 unused)
+ * A table entry outside [0, n_pages) gives 0xff bytes and NaN scales for
+ * its cells.  Errors: KV_ERR_NULL (a required output), _ALIGN, _RANGE.
+ */
+int kv_gather_runs(const kv_pool *pool, const kv_seq *seq, int32_t pos0, int32_t n, void *out0,
+                   void *out1, void *out2, void *out3, void *stream);
 
 /*
  * Device workspace needed by attn_decode / attn_verify for n_q query rows
@@ -169,6 +201,10 @@ int kv_probe_read(const void *buf, size_t bytes, void *sink, void *stream);
  *   scale: softmax scale; <= 0 selects 1/sqrt(256).
  * out = H/16 * softmax(scale * q K^T) V_rot, with K = code * d and
  * V_rot = (code - 8) * d16 (fp32 accumulation).
+ * The comparison formats run through the same entry: int8 scores q against
+ * K = code * d and returns softmax(.) V with V = code * d (no rotation);
+ * q4_0 scores (H q / 16) against the rotated K_rot = (code - 8) * d16 and
+ * rotates the output back as k8v4 does.
  * Errors: KV_ERR_NULL, _UNSUPPORTED, _DTYPE, _RANGE (n_ctx < 1 or beyond
  * the table), _WORKSPACE.
  */
@@ -197,7 +233,8 @@ int attn_verify(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dty
  * prefill).  Dense contractions on the matrix cores (fp16 inputs, fp32
  * accumulation).
  *   q:   device, [n_new][n_q_heads][256];  out: device fp32 [n_new][n_q_heads][256]
- * Needs no workspace (ws may be NULL).
+ * Needs no workspace (ws may be NULL).  k8v4 pools only (_UNSUPPORTED for
+ * the comparison formats).
  * Errors: KV_ERR_NULL, _UNSUPPORTED, _DTYPE, _RANGE.
  */
 int attn_prefill_chunk(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,

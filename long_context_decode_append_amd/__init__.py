@@ -45,6 +45,8 @@ SIGNATURES = {
     "attn_workspace_bytes": (_SZ, [_PP, _I, C.c_int32, C.c_int32]),
     "kv_workspace_init": (_I, [_P, _SZ, _P]),
     "kv_probe_read": (_I, [_P, _SZ, _P, _P]),
+    "kv_append": (_I, [_PP, _PS, _P, _P, _I, C.c_int32, C.c_int32, _P]),
+    "kv_gather_runs": (_I, [_PP, _PS, C.c_int32, C.c_int32, _P, _P, _P, _P, _P]),
     "attn_decode": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, _F, _P, _P, _SZ, _P]),
     "attn_verify": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, _P, _F, _P, _P, _SZ, _P]),
     "attn_prefill_chunk": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, C.c_int32, _F, _P, _P, _SZ, _P]),
@@ -131,15 +133,16 @@ def cell_bytes(fmt: int = KV_FMT_K8V4, n_kv_heads: int = 2, head_dim: int = HEAD
     return int(lib().kv_cell_bytes(fmt, n_kv_heads, head_dim))
 
 
-class K8V4Pool:
-    """A k8v4 paged pool in device memory: three runs (K codes, K scales, V q4_0)."""
+class KvPool:
+    """A paged pool in device memory of format fmt (KV_FMT_INT8, KV_FMT_Q4_0
+    or KV_FMT_K8V4): its runs as the header lays them out."""
 
-    def __init__(self, n_pages: int, page_size: int, n_kv_heads: int = 2, device="cuda",
+    def __init__(self, fmt: int, n_pages: int, page_size: int, n_kv_heads: int = 2, device="cuda",
                  fill: int | None = None):
         torch = _torch()
         L = lib()
         self.n_pages, self.page_size, self.n_kv_heads = n_pages, page_size, n_kv_heads
-        self.fmt = KV_FMT_K8V4
+        self.fmt = int(fmt)
         self.runs = []
         for r in range(4):
             nb = int(L.kv_run_bytes(self.fmt, r, n_pages, page_size, n_kv_heads, HEAD_DIM))
@@ -163,6 +166,14 @@ class K8V4Pool:
         return sum(t.numel() for t in self.runs if t is not None)
 
 
+class K8V4Pool(KvPool):
+    """A k8v4 paged pool: three runs (K codes, K scales, V q4_0)."""
+
+    def __init__(self, n_pages: int, page_size: int, n_kv_heads: int = 2, device="cuda",
+                 fill: int | None = None):
+        super().__init__(KV_FMT_K8V4, n_pages, page_size, n_kv_heads, device, fill)
+
+
 def _seq(page_table) -> KvSeqStruct:
     torch = _torch()
     if page_table.dtype != torch.int32:
@@ -183,6 +194,54 @@ def kv_append_k8v4(pool: K8V4Pool, page_table, k, v, pos0: int, stream=None) -> 
     _check(rc, "kv_append_k8v4")
 
 
+def kv_append(pool: KvPool, page_table, k, v, pos0: int, stream=None) -> None:
+    """kv_append_k8v4 for a pool of any format."""
+    if k.shape != v.shape or k.dtype != v.dtype:
+        raise ValueError("k and v must have the same shape and dtype")
+    if k.dim() != 3 or k.shape[1] != pool.n_kv_heads or k.shape[2] != HEAD_DIM:
+        raise ValueError("k, v must be [n][n_kv_heads][256]")
+    seq = _seq(page_table)
+    rc = lib().kv_append(C.byref(pool.struct), C.byref(seq), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                         _dtype_code(k), int(pos0), int(k.shape[0]), _stream(stream))
+    _check(rc, "kv_append")
+
+
+def kv_gather_runs(pool: KvPool, page_table, pos0: int, n: int, stream=None):
+    """Stored bytes of cells [pos0, pos0+n) for any format, as kv_gather_runs
+    documents: int8-coded halves as (codes int8 [n][H][256], scales fp32
+    [n][H][2]), q4_0-coded halves as blocks uint8 [n][H][8][18].  Returns
+    (K..., V...) flattened: k8v4 (kc, ks, vb), int8 (kc, ks, vc, vs),
+    q4_0 (kb, vb)."""
+    torch = _torch()
+    H = pool.n_kv_heads
+    dev = pool.runs[0].device
+
+    def codes():
+        return torch.empty((n, H, HEAD_DIM), dtype=torch.int8, device=dev)
+
+    def scales():
+        return torch.empty((n, H, 2), dtype=torch.float32, device=dev)
+
+    def blocks():
+        return torch.empty((n, H, 8, 18), dtype=torch.uint8, device=dev)
+
+    if pool.fmt == KV_FMT_INT8:
+        outs = [codes(), scales(), codes(), scales()]
+        ptrs = outs
+    elif pool.fmt == KV_FMT_Q4_0:
+        outs = [blocks(), blocks()]
+        ptrs = [outs[0], None, outs[1], None]
+    else:
+        outs = [codes(), scales(), blocks()]
+        ptrs = outs + [None]
+    seq = _seq(page_table)
+    args = [None if t is None else _dev_ptr(t, "out") for t in ptrs]
+    rc = lib().kv_gather_runs(C.byref(pool.struct), C.byref(seq), int(pos0), int(n), *args,
+                              _stream(stream))
+    _check(rc, "kv_gather_runs")
+    return tuple(outs)
+
+
 def kv_gather(pool: K8V4Pool, page_table, pos0: int, n: int, stream=None):
     """Stored bytes of cells [pos0, pos0+n): (k_codes int8 [n][H][256],
     k_scales fp32 [n][H][2], v_blocks uint8 [n][H][8][18])."""
@@ -199,7 +258,7 @@ def kv_gather(pool: K8V4Pool, page_table, pos0: int, n: int, stream=None):
     return kc, ks, vb
 
 
-def attn_workspace(pool: K8V4Pool, n_q: int, max_ctx: int, stream=None):
+def attn_workspace(pool: KvPool, n_q: int, max_ctx: int, stream=None):
     """Allocate and zero a workspace for decode (n_q = 1) or verify calls."""
     torch = _torch()
     nb = int(lib().attn_workspace_bytes(C.byref(pool.struct), GQA * pool.n_kv_heads, n_q, max_ctx))
@@ -216,7 +275,7 @@ def probe_read(buf, sink, stream=None):
                                _dev_ptr(sink, "sink"), _stream(stream)), "kv_probe_read")
 
 
-def attn_decode(pool: K8V4Pool, page_table, q, n_ctx: int, ws, scale: float = 0.0, out=None,
+def attn_decode(pool: KvPool, page_table, q, n_ctx: int, ws, scale: float = 0.0, out=None,
                 stream=None):
     """q: [Hq][256] fp16/fp32 -> out fp32 [Hq][256], attending cells [0, n_ctx)."""
     torch = _torch()
@@ -233,7 +292,7 @@ def attn_decode(pool: K8V4Pool, page_table, q, n_ctx: int, ws, scale: float = 0.
     return out
 
 
-def attn_verify(pool: K8V4Pool, page_table, q, n_visible, ws, scale: float = 0.0, out=None,
+def attn_verify(pool: KvPool, page_table, q, n_visible, ws, scale: float = 0.0, out=None,
                 stream=None):
     """q: [n_q][Hq][256]; row i attends cells [0, n_visible[i]) -> out fp32 [n_q][Hq][256]."""
     torch = _torch()

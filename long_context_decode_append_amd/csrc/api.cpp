@@ -74,7 +74,19 @@ int kv_append_k8v4(const kv_pool *pool, const kv_seq *seq, const void *k, const 
   if (int e = check_range(pool, seq, pos0, n_tokens)) return e;
   if (check_aligned16(k) || check_aligned16(v)) return KV_ERR_ALIGN;
   if (n_tokens == 0) return KV_OK;
-  return launch_append_k8v4(pool, seq, k, v, dtype, pos0, n_tokens, (hipStream_t)stream);
+  return launch_append(pool, seq, k, v, dtype, pos0, n_tokens, (hipStream_t)stream);
+}
+
+int kv_append(const kv_pool *pool, const kv_seq *seq, const void *k, const void *v, int dtype, int32_t pos0,
+              int32_t n_tokens, void *stream) {
+  if (int e = check_pool(pool, 0)) return e;
+  if (int e = check_seq(seq, pool)) return e;
+  if (!k || !v) return KV_ERR_NULL;
+  if (int e = check_dtype(dtype)) return e;
+  if (int e = check_range(pool, seq, pos0, n_tokens)) return e;
+  if (check_aligned16(k) || check_aligned16(v)) return KV_ERR_ALIGN;
+  if (n_tokens == 0) return KV_OK;
+  return launch_append(pool, seq, k, v, dtype, pos0, n_tokens, (hipStream_t)stream);
 }
 
 int kv_gather(const kv_pool *pool, const kv_seq *seq, int32_t pos0, int32_t n, void *k_codes,
@@ -85,7 +97,25 @@ int kv_gather(const kv_pool *pool, const kv_seq *seq, int32_t pos0, int32_t n, v
   if (int e = check_range(pool, seq, pos0, n)) return e;
   if (check_aligned16(k_codes) || ((uintptr_t)k_scales & 7u)) return KV_ERR_ALIGN;
   if (n == 0) return KV_OK;
-  return launch_gather_k8v4(pool, seq, pos0, n, k_codes, k_scales, v_blocks, (hipStream_t)stream);
+  void *const out[4] = {k_codes, k_scales, v_blocks, nullptr};
+  return launch_gather(pool, seq, pos0, n, out, (hipStream_t)stream);
+}
+
+int kv_gather_runs(const kv_pool *pool, const kv_seq *seq, int32_t pos0, int32_t n, void *out0, void *out1,
+                   void *out2, void *out3, void *stream) {
+  if (int e = check_pool(pool, 0)) return e;
+  if (int e = check_seq(seq, pool)) return e;
+  const int fmt = pool->fmt;
+  void *const out[4] = {out0, out1, out2, out3};
+  // int8-coded halves: codes (16-byte aligned) + scales (8-byte aligned);
+  // q4_0-coded halves: one block array (any alignment)
+  const bool k_int8 = fmt != KV_FMT_Q4_0, v_int8 = fmt == KV_FMT_INT8;
+  if (!out0 || !out2 || (k_int8 && !out1) || (v_int8 && !out3)) return KV_ERR_NULL;
+  if (int e = check_range(pool, seq, pos0, n)) return e;
+  if (k_int8 && (check_aligned16(out0) || ((uintptr_t)out1 & 7u))) return KV_ERR_ALIGN;
+  if (v_int8 && (check_aligned16(out2) || ((uintptr_t)out3 & 7u))) return KV_ERR_ALIGN;
+  if (n == 0) return KV_OK;
+  return launch_gather(pool, seq, pos0, n, out, (hipStream_t)stream);
 }
 
 size_t attn_workspace_bytes(const kv_pool *pool, int n_q_heads, int32_t n_q, int32_t max_ctx) {
@@ -107,8 +137,8 @@ int kv_probe_read(const void *buf, size_t bytes, void *sink, void *stream) {
 }
 
 static int check_attn_common(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
-                             int n_q_heads, const float *out) {
-  if (int e = check_pool(pool, KV_FMT_K8V4)) return e;
+                             int n_q_heads, const float *out, int need_fmt) {
+  if (int e = check_pool(pool, need_fmt)) return e;
   if (int e = check_seq(seq, pool)) return e;
   if (!q || !out) return KV_ERR_NULL;
   if (int e = check_dtype(q_dtype)) return e;
@@ -124,7 +154,7 @@ static float pick_scale(float scale) {
 int attn_decode(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
                 int n_q_heads, int32_t n_ctx, float scale, float *out, void *ws,
                 size_t ws_bytes, void *stream) {
-  if (int e = check_attn_common(pool, seq, q, q_dtype, n_q_heads, out)) return e;
+  if (int e = check_attn_common(pool, seq, q, q_dtype, n_q_heads, out, 0)) return e;
   if (n_ctx < 1) return KV_ERR_RANGE;
   if (int e = check_range(pool, seq, 0, n_ctx)) return e;
   if (!ws) return KV_ERR_WORKSPACE;
@@ -150,7 +180,7 @@ int attn_decode(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dty
 int attn_verify(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
                 int n_q_heads, int32_t n_q, const int32_t *n_visible, float scale, float *out,
                 void *ws, size_t ws_bytes, void *stream) {
-  if (int e = check_attn_common(pool, seq, q, q_dtype, n_q_heads, out)) return e;
+  if (int e = check_attn_common(pool, seq, q, q_dtype, n_q_heads, out, 0)) return e;
   if (!n_visible) return KV_ERR_NULL;
   if (n_q < 1 || n_q > kMaxQ) return KV_ERR_SHAPE;
   if (!ws) return KV_ERR_WORKSPACE;
@@ -183,7 +213,7 @@ int attn_prefill_chunk(const kv_pool *pool, const kv_seq *seq, const void *q, in
                        void *ws, size_t ws_bytes, void *stream) {
   (void)ws;
   (void)ws_bytes;
-  if (int e = check_attn_common(pool, seq, q, q_dtype, n_q_heads, out)) return e;
+  if (int e = check_attn_common(pool, seq, q, q_dtype, n_q_heads, out, KV_FMT_K8V4)) return e;
   if (pos0 < 0 || n_new < 0) return KV_ERR_RANGE;
   if (int e = check_range(pool, seq, 0, (int64_t)pos0 + n_new)) return e;
   if (n_new == 0) return KV_OK;

@@ -9,6 +9,11 @@
 // (token, KV head) pair: K and V are quantized in the same pass, so there
 // is no duplicate write of a folded half.
 //
+// The two comparison formats of the same pages use the same rules on other
+// halves: int8 (K and V both INT8, unrotated, 1,056 B/cell) and q4_0 (K and
+// V both rotated Q4_0, 576 B/cell) ("#120", Measured: the k8v4 / int8 /
+// q4_0 rows; "#711", How: the format numbers).
+//
 // Every quantizer step is one IEEE fp32 operation rounded as written: this
 // file is built with -ffp-contract=off and the functions also disable
 // contraction locally, so x * r + 8.5 is never fused.
@@ -18,9 +23,7 @@
 namespace k8v4 {
 
 struct AppendArgs {
-  int8_t *kc;      // run 0
-  float *ks;       // run 1
-  uint8_t *vq;     // run 2
+  uint8_t *run[4];
   const int32_t *pt;
   const void *k;
   const void *v;
@@ -92,7 +95,28 @@ __device__ __forceinline__ uint32_t quant_q4(const float y[4], int lane, uint16_
   return codes;
 }
 
-__global__ __launch_bounds__(256) void append_k8v4_kernel(const AppendArgs a) {
+// INT8 half of one head: codes [cell][256], fp32 scales [cell][2]
+__device__ __forceinline__ void store_int8(uint8_t *codes_run, uint8_t *scales_run, size_t cell, int lane,
+                                           uint32_t codes, float d) {
+  *reinterpret_cast<uint32_t *>(codes_run + cell * 256 + 4 * lane) = codes;
+  if ((lane & 31) == 0) reinterpret_cast<float *>(scales_run)[cell * 2 + (lane >> 5)] = d;
+}
+
+// Q4_0 half of one head into its (page, head) tile: byte i of a block =
+// code[i] | code[i+16] << 4; lanes j < 4 of the block hold elements
+// 4j..4j+3, lane j + 4 holds elements 16 + 4j..
+__device__ __forceinline__ void store_q4(uint8_t *run, size_t tile, int P, int slot, int lane, uint32_t codes,
+                                         uint16_t d16) {
+  const uint32_t hi = (uint32_t)__shfl_xor((int)codes, 4, 64);
+  const int b = lane >> 3, j = lane & 7;
+  uint8_t *vt = run + tile * 144 * P;
+  if (j < 4) *reinterpret_cast<uint32_t *>(vt + (size_t)slot * 128 + b * 16 + 4 * j) = codes | (hi << 4);
+  if (j == 0) *reinterpret_cast<uint16_t *>(vt + q4_scale_off(P, slot, b)) = d16;
+}
+
+// one wave per (token, KV head); FMT selects the rule of each half
+template <int FMT>
+__global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (token, head)
   if (item >= (int64_t)a.n_tokens * a.H) return;                       // whole wave exits
@@ -107,40 +131,61 @@ __global__ __launch_bounds__(256) void append_k8v4_kernel(const AppendArgs a) {
 
   float x[4];
   load4(a.k, a.dtype, src, x);
-  float d;
-  const uint32_t kcodes = quant_k(x, d);
-  *reinterpret_cast<uint32_t *>(a.kc + cell * 256 + 4 * lane) = kcodes;
-  if ((lane & 31) == 0) a.ks[cell * 2 + (lane >> 5)] = d;
+  if (FMT == KV_FMT_Q4_0) {
+    fwht256_lane4(x, lane);
+    uint16_t d16;
+    const uint32_t codes = quant_q4(x, lane, d16);
+    store_q4(a.run[0], tile, a.P, slot, lane, codes, d16);
+  } else {
+    float d;
+    const uint32_t codes = quant_k(x, d);
+    store_int8(a.run[0], a.run[1], cell, lane, codes, d);
+  }
 
   load4(a.v, a.dtype, src, x);
-  fwht256_lane4(x, lane);
-  uint16_t d16;
-  const uint32_t vcodes = quant_q4(x, lane, d16);
-  // byte i of a block = code[i] | code[i+16] << 4: lanes j < 4 of the block
-  // hold elements 4j..4j+3, lane j + 4 holds elements 16 + 4j..
-  const uint32_t hi = (uint32_t)__shfl_xor((int)vcodes, 4, 64);
-  const int b = lane >> 3, j = lane & 7;
-  uint8_t *vt = a.vq + tile * 144 * a.P;
-  if (j < 4) {
-    *reinterpret_cast<uint32_t *>(vt + (size_t)slot * 128 + b * 16 + 4 * j) = vcodes | (hi << 4);
-  }
-  if (j == 0) {
-    *reinterpret_cast<uint16_t *>(vt + q4_scale_off(a.P, slot, b)) = d16;
+  if (FMT == KV_FMT_INT8) {
+    float d;
+    const uint32_t codes = quant_k(x, d);
+    store_int8(a.run[2], a.run[3], cell, lane, codes, d);
+  } else {
+    fwht256_lane4(x, lane);
+    uint16_t d16;
+    const uint32_t codes = quant_q4(x, lane, d16);
+    store_q4(a.run[2], tile, a.P, slot, lane, codes, d16);
   }
 }
 
 struct GatherArgs {
-  const int8_t *kc;
-  const float *ks;
-  const uint8_t *vq;
+  const uint8_t *run[4];
   const int32_t *pt;
-  int8_t *okc;
-  float *oks;
-  uint8_t *ovb;
+  uint8_t *out[4];
   int pos0, n, n_pages, P, H;
 };
 
-__global__ __launch_bounds__(256) void gather_k8v4_kernel(const GatherArgs a) {
+__device__ __forceinline__ void gather_int8(const uint8_t *codes_run, const uint8_t *scales_run, bool bad,
+                                            size_t cell, size_t o, int lane, uint8_t *oc, uint8_t *os) {
+  uint32_t w = bad ? 0xffffffffu : *reinterpret_cast<const uint32_t *>(codes_run + cell * 256 + 4 * lane);
+  *reinterpret_cast<uint32_t *>(oc + o * 256 + 4 * lane) = w;
+  if (lane < 2)
+    reinterpret_cast<float *>(os)[o * 2 + lane] =
+        bad ? __builtin_nanf("") : reinterpret_cast<const float *>(scales_run)[cell * 2 + lane];
+}
+
+__device__ __forceinline__ void gather_q4(const uint8_t *run, bool bad, size_t tile, int P, int slot, size_t o,
+                                          int lane, uint8_t *ob) {
+  const uint8_t *vt = run + tile * 144 * P;
+  for (int e = lane; e < 144; e += 64) {
+    const int b = e / 18, off = e % 18;
+    uint8_t byte;
+    if (off < 2) byte = vt[q4_scale_off(P, slot, b) + off];
+    else byte = vt[(size_t)slot * 128 + b * 16 + (off - 2)];
+    ob[o * 144 + e] = bad ? 0xff : byte;
+  }
+}
+
+// one wave per (cell, KV head); outputs per format as kv_gather_runs documents
+template <int FMT>
+__global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= (int64_t)a.n * a.H) return;
@@ -153,17 +198,10 @@ __global__ __launch_bounds__(256) void gather_k8v4_kernel(const GatherArgs a) {
   const size_t cell = tile * a.P + slot;
   const size_t o = (size_t)t * a.H + g;
   // an out-of-range table entry yields 0xff bytes / NaN scales, never a read outside the pool
-  uint32_t w = bad ? 0xffffffffu : *reinterpret_cast<const uint32_t *>(a.kc + cell * 256 + 4 * lane);
-  *reinterpret_cast<uint32_t *>(a.okc + o * 256 + 4 * lane) = w;
-  if (lane < 2) a.oks[o * 2 + lane] = bad ? __builtin_nanf("") : a.ks[cell * 2 + lane];
-  const uint8_t *vt = a.vq + tile * 144 * a.P;
-  for (int e = lane; e < 144; e += 64) {
-    const int b = e / 18, off = e % 18;
-    uint8_t byte;
-    if (off < 2) byte = vt[q4_scale_off(a.P, slot, b) + off];
-    else byte = vt[(size_t)slot * 128 + b * 16 + (off - 2)];
-    a.ovb[o * 144 + e] = bad ? 0xff : byte;
-  }
+  if (FMT == KV_FMT_Q4_0) gather_q4(a.run[0], bad, tile, a.P, slot, o, lane, a.out[0]);
+  else gather_int8(a.run[0], a.run[1], bad, cell, o, lane, a.out[0], a.out[1]);
+  if (FMT == KV_FMT_INT8) gather_int8(a.run[2], a.run[3], bad, cell, o, lane, a.out[2], a.out[3]);
+  else gather_q4(a.run[2], bad, tile, a.P, slot, o, lane, a.out[2]);
 }
 
 __global__ void fill_zero_kernel(uint32_t *p, size_t n_words) {
@@ -172,12 +210,10 @@ __global__ void fill_zero_kernel(uint32_t *p, size_t n_words) {
     p[i] = 0;
 }
 
-int launch_append_k8v4(const kv_pool *pool, const kv_seq *seq, const void *k, const void *v,
-                       int dtype, int pos0, int n, hipStream_t s) {
+int launch_append(const kv_pool *pool, const kv_seq *seq, const void *k, const void *v, int dtype, int pos0,
+                  int n, hipStream_t s) {
   AppendArgs a;
-  a.kc = (int8_t *)pool->run[0];
-  a.ks = (float *)pool->run[1];
-  a.vq = (uint8_t *)pool->run[2];
+  for (int r = 0; r < 4; r++) a.run[r] = (uint8_t *)pool->run[r];
   a.pt = seq->page_table;
   a.k = k;
   a.v = v;
@@ -189,20 +225,21 @@ int launch_append_k8v4(const kv_pool *pool, const kv_seq *seq, const void *k, co
   a.H = pool->n_kv_heads;
   const int64_t items = (int64_t)n * a.H;
   const unsigned blocks = (unsigned)((items + 3) / 4);
-  launch(append_k8v4_kernel, dim3(blocks), dim3(256), s, a);
+  switch (pool->fmt) {
+    case KV_FMT_INT8: launch(append_kernel<KV_FMT_INT8>, dim3(blocks), dim3(256), s, a); break;
+    case KV_FMT_Q4_0: launch(append_kernel<KV_FMT_Q4_0>, dim3(blocks), dim3(256), s, a); break;
+    default: launch(append_kernel<KV_FMT_K8V4>, dim3(blocks), dim3(256), s, a); break;
+  }
   return launch_status();
 }
 
-int launch_gather_k8v4(const kv_pool *pool, const kv_seq *seq, int pos0, int n, void *okc,
-                       void *oks, void *ovb, hipStream_t s) {
+int launch_gather(const kv_pool *pool, const kv_seq *seq, int pos0, int n, void *const out[4], hipStream_t s) {
   GatherArgs a;
-  a.kc = (const int8_t *)pool->run[0];
-  a.ks = (const float *)pool->run[1];
-  a.vq = (const uint8_t *)pool->run[2];
+  for (int r = 0; r < 4; r++) {
+    a.run[r] = (const uint8_t *)pool->run[r];
+    a.out[r] = (uint8_t *)out[r];
+  }
   a.pt = seq->page_table;
-  a.okc = (int8_t *)okc;
-  a.oks = (float *)oks;
-  a.ovb = (uint8_t *)ovb;
   a.pos0 = pos0;
   a.n = n;
   a.n_pages = pool->n_pages;
@@ -210,7 +247,11 @@ int launch_gather_k8v4(const kv_pool *pool, const kv_seq *seq, int pos0, int n, 
   a.H = pool->n_kv_heads;
   const int64_t items = (int64_t)n * a.H;
   const unsigned blocks = (unsigned)((items + 3) / 4);
-  launch(gather_k8v4_kernel, dim3(blocks), dim3(256), s, a);
+  switch (pool->fmt) {
+    case KV_FMT_INT8: launch(gather_kernel<KV_FMT_INT8>, dim3(blocks), dim3(256), s, a); break;
+    case KV_FMT_Q4_0: launch(gather_kernel<KV_FMT_Q4_0>, dim3(blocks), dim3(256), s, a); break;
+    default: launch(gather_kernel<KV_FMT_K8V4>, dim3(blocks), dim3(256), s, a); break;
+  }
   return launch_status();
 }
 

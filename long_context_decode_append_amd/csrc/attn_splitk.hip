@@ -45,14 +45,16 @@ struct SplitArgs {
   const int8_t *kc;
   const float *ks;
   const uint8_t *vq;
+  const float *vs;      // V scales (int8 format only)
   const int32_t *pt;
   const void *q;
   float *out;
   float2 *part_ml;      // [H][splits][rows]: (m, l) of each split partial
-  float *part_o;        // [H][splits][rows][256]: unnormalized O (rotated basis)
+  float *part_o;        // [H][splits][rows][256]: unnormalized O (V's basis)
   int n_pages, P, H;
   int p_shift;          // log2(P) when P is a power of two, else -1
-  int k_bytes, ks_bytes, v_bytes;  // run sizes (each < 2^31)
+  int k_bytes, ks_bytes, v_bytes, vs_bytes;  // run sizes (each < 2^31)
+  int v_rotated;        // V stored rotated: the combine applies H / 16
   int n_q_heads, n_rows, rows_per_pass;
   int limits[kMaxQ];
   int max_limit;
@@ -60,11 +62,13 @@ struct SplitArgs {
   int steps_per_split, n_splits;
 };
 
-// dim of output tile j held by column n of the PV MFMA: column n reads bytes
-// [8n, 8n+8) of a cell's 128 nibble bytes (block n/2), tile j takes byte
-// j % 8, low nibble for j < 8 and high nibble for j >= 8.
+// dim of output tile j held by column n of the PV MFMA.  q4_0 V: column n
+// reads bytes [8n, 8n+8) of a cell's 128 nibble bytes (block n/2), tile j
+// takes byte j % 8, low nibble for j < 8 and high nibble for j >= 8.  INT8
+// V: column n reads bytes [16n, 16n+16), tile j takes byte j.
+template <bool kQ4V>
 __device__ __forceinline__ int o_dim(int n, int j) {
-  return 32 * (n >> 1) + 8 * (n & 1) + (j & 7) + 16 * (j >> 3);
+  return kQ4V ? 32 * (n >> 1) + 8 * (n & 1) + (j & 7) + 16 * (j >> 3) : 16 * n + j;
 }
 
 __device__ __forceinline__ f16x8 pack8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -87,50 +91,69 @@ __device__ __forceinline__ float readlane(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
 
-// Position, page and byte offsets (all wave-uniform) of one 16-cell half of
-// a step.  A half that starts past the split end reuses the step's first
-// half (its cells are masked and its V scales zeroed).
+// Byte offsets of one 16-cell half of a step, per format (all wave-uniform).
+// A half that starts past the split end reuses the step's first half (its
+// cells are masked and its V scales zeroed).
 struct Half {
   int bad;        // page-table entry out of range: rows that read it return NaN
-  int k_soff;     // byte offset of the half's first cell in the K-code run
-  int ks_soff;    // ... in the K-scale run
-  int v_soff;     // ... of its nibble bytes in the V run
-  int vd_soff;    // ... of its 256-byte scale group in the V run
+  int k_soff;     // K data of the half's first cell (int8 codes, or q4_0 nibbles)
+  int ks_soff;    // K scales (fp32 pairs, or the q4_0 scale group)
+  int v_soff;     // V data (q4_0 nibbles, or int8 codes)
+  int vd_soff;    // V scales (the q4_0 scale group, or fp32 pairs)
 };
 
 __device__ __forceinline__ int page_of(const SplitArgs &a, int pos) {
   return a.p_shift >= 0 ? (pos >> a.p_shift) : pos / a.P;
 }
 
+template <int FMT>
 __device__ __forceinline__ Half make_half(const SplitArgs &a, int g, int pos, int page) {
   Half h;
   h.bad = page < 0 || page >= a.n_pages;
   const int pg = h.bad ? 0 : page;
-  const int slot0 = pos - page_of(a, pos) * a.P;
+  const int slot0 = pos - page_of(a, pos) * a.P;  // a multiple of 16
   const int tile = pg * a.H + g;
-  h.k_soff = (tile * a.P + slot0) * 256;
-  h.ks_soff = (tile * a.P + slot0) * 8;
-  h.v_soff = tile * 144 * a.P + slot0 * 128;
-  h.vd_soff = tile * 144 * a.P + 128 * a.P + slot0 * 16;  // slot0 % 16 == 0: group slot0 / 16
+  const int cell = tile * a.P + slot0;
+  const int q4_tile = tile * 144 * a.P;
+  if (FMT == KV_FMT_Q4_0) {
+    h.k_soff = q4_tile + slot0 * 128;
+    h.ks_soff = q4_tile + 128 * a.P + slot0 * 16;  // scale group slot0 / 16
+  } else {
+    h.k_soff = cell * 256;
+    h.ks_soff = cell * 8;
+  }
+  if (FMT == KV_FMT_INT8) {
+    h.v_soff = cell * 256;
+    h.vd_soff = cell * 8;
+  } else {
+    h.v_soff = q4_tile + slot0 * 128;
+    h.vd_soff = q4_tile + 128 * a.P + slot0 * 16;
+  }
   return h;
 }
 
 // the two halves of the step at c (c < c_end); page entries read here are
 // scalar loads
-__device__ __forceinline__ void step_halves(const SplitArgs &a, int g, int c, int c_end, Half &h0,
-                                            Half &h1) {
+template <int FMT>
+__device__ __forceinline__ void step_halves(const SplitArgs &a, int g, int c, int c_end, Half &h0, Half &h1) {
   const int p1pos = (c + 16 < c_end) ? c + 16 : c;
   const int pg0 = a.pt[page_of(a, c)];
   const int pg1 = a.pt[page_of(a, p1pos)];
-  h0 = make_half(a, g, c, pg0);
-  h1 = make_half(a, g, p1pos, pg1);
+  h0 = make_half<FMT>(a, g, c, pg0);
+  h1 = make_half<FMT>(a, g, p1pos, pg1);
 }
 
-template <int NQT, bool QF32>
+// k-slot order inside an 8-dim q4_0 K operand: the nibble unpack yields the
+// elements of a 4-byte word as (0, 2) then (1, 3)
+__device__ __forceinline__ int q4_kslot(int t) { return (t & 4) | ((t & 1) << 1) | ((t >> 1) & 1); }
+
+template <bool QF32, int FMT>
 __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) {
   __shared__ __attribute__((aligned(16))) float lds_o[kWaves * 16 * 64 * 4];  // wave states, accumulator layout
   __shared__ __attribute__((aligned(16))) float lds_m[kWaves * 16];
   __shared__ __attribute__((aligned(16))) float lds_l[kWaves * 16];
+  constexpr bool kInt8K = FMT != KV_FMT_Q4_0;   // K as INT8 codes (else rotated q4_0)
+  constexpr bool kQ4V = FMT != KV_FMT_INT8;     // V as rotated q4_0 (else INT8 codes)
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -152,90 +175,160 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)a.kc, (short)0, a.k_bytes, kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc((void *)a.ks, (short)0, a.ks_bytes, kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)a.vq, (short)0, a.v_bytes, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc((void *)a.vs, (short)0, a.vs_bytes, kRsrcFlags);
   // lane-constant parts of the operand-layout loads
-  const int k_voff = n * 256 + 16 * lg;            // + 64 j: 16 bytes of cell n
-  const int ks_voff = 32 * lg;                     // scales of cells 4lg..4lg+3
-  const int v_voff = 4 * lg * 128 + 8 * n;         // + 128 i: bytes [8n, 8n+8) of cell 4lg+i
-  const int vd_voff = (n >> 1) * 32 + 8 * lg;       // d16[block n/2][cells 4lg..4lg+3] of the group
+  //   INT8 K:  + 64 j: 16 bytes (dims 64 j + 16 lg ..) of cell n
+  //   q4_0 K:  + 32 j: the 16 nibble bytes of block 2 j + lg / 2 of cell n
+  //            (low nibbles for even lg, high for odd), its scale at + 64 j
+  //   q4_0 V:  + 128 i: bytes [8n, 8n+8) of cell 4lg+i; scales of block n/2
+  //   INT8 V:  + 256 i: bytes [16n, 16n+16) of cell 4lg+i; scales of 4 cells
+  const int k_voff = kInt8K ? n * 256 + 16 * lg : n * 128 + 16 * (lg >> 1);
+  const int ks_voff = kInt8K ? 32 * lg : 32 * (lg >> 1) + 2 * n;
+  const int v_voff = kQ4V ? 4 * lg * 128 + 8 * n : 4 * lg * 256 + 16 * n;
+  const int vd_voff = kQ4V ? (n >> 1) * 32 + 8 * lg : 32 * lg;
+  const int kstep_j = kInt8K ? 64 : 32;
+  const uint32_t q4_shift = (lg & 1) ? 4u : 0u;  // q4_0 K: high nibbles for odd lg
+  const int v8_grp = n >> 3;                     // INT8 V: scale group of this lane's dims
 
   u32x4 kr[2][4];
-  f32x4 ksr[2][2];
-  u32x2 vr[2][4];
+  f32x4 ksr[2][2];      // INT8 K scales
+  uint32_t kdr[2][4];   // q4_0 K scales (fp16 bits)
+  u32x2 vr[2][4];       // q4_0 V
   u32x2 vdr[2];
+  u32x4 vr8[2][4];      // INT8 V
+  f32x4 vsr[2][2];
   Half cur0, cur1, nxt0, nxt1;
-  if (has_work) {
-    step_halves(a, g, c_first, c_end, cur0, cur1);
-    const Half *hs[2] = {&cur0, &cur1};
-    for (int h2 = 0; h2 < 2; h2++) {
-      const Half &h = *hs[h2];
-      for (int j = 0; j < 4; j++) kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + 64 * j, h.k_soff, 0);
+  auto load_k = [&](int h2, const Half &h) {
+    for (int j = 0; j < 4; j++) kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + kstep_j * j, h.k_soff, 0);
+  };
+  auto load_ks = [&](int h2, const Half &h) {
+    if (kInt8K) {
       ksr[h2][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, ks_voff, h.ks_soff, 0));
       ksr[h2][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, ks_voff + 16, h.ks_soff, 0));
-      for (int i = 0; i < 4; i++) vr[h2][i] = __builtin_amdgcn_raw_buffer_load_b64(rv, v_voff + 128 * i, h.v_soff, 0);
-      vdr[h2] = __builtin_amdgcn_raw_buffer_load_b64(rv, vd_voff, h.vd_soff, 0);
+    } else {
+      for (int j = 0; j < 4; j++) kdr[h2][j] = __builtin_amdgcn_raw_buffer_load_b16(rk, ks_voff + 64 * j, h.ks_soff, 0);
     }
-    step_halves(a, g, min(c_first + stride, c_last), c_end, nxt0, nxt1);
+  };
+  auto load_v = [&](int h2, const Half &h) {
+    if (kQ4V) {
+      for (int i = 0; i < 4; i++) vr[h2][i] = __builtin_amdgcn_raw_buffer_load_b64(rv, v_voff + 128 * i, h.v_soff, 0);
+    } else {
+      for (int i = 0; i < 4; i++) vr8[h2][i] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_voff + 256 * i, h.v_soff, 0);
+    }
+  };
+  auto load_vd = [&](int h2, const Half &h) {
+    if (kQ4V) {
+      vdr[h2] = __builtin_amdgcn_raw_buffer_load_b64(rv, vd_voff, h.vd_soff, 0);
+    } else {
+      vsr[h2][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs, vd_voff, h.vd_soff, 0));
+      vsr[h2][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs, vd_voff + 16, h.vd_soff, 0));
+    }
+  };
+  if (has_work) {
+    step_halves<FMT>(a, g, c_first, c_end, cur0, cur1);
+    const Half *hs[2] = {&cur0, &cur1};
+    for (int h2 = 0; h2 < 2; h2++) {
+      load_k(h2, *hs[h2]);
+      load_ks(h2, *hs[h2]);
+      load_v(h2, *hs[h2]);
+      load_vd(h2, *hs[h2]);
+    }
+    step_halves<FMT>(a, g, min(c_first + stride, c_last), c_end, nxt0, nxt1);
   }
 
   // ---------------------------------------------------------------- queries
-  // B operand of the QK MFMA for row tile t and k-step kk: lane (n, lg)
-  // holds q[row t*16+n][dims 64*(kk/2) + 16*lg + 8*(kk%2) + 0..7].
-  f16x8 qop[NQT][8];
-  f16x8 qlo[QF32 ? NQT : 1][QF32 ? 8 : 1];
-  float cbias[NQT][2];
-  int lim_eff[NQT];
-  for (int t = 0; t < NQT; t++) {
-    const int r = t * 16 + n;
-    const int row = row_base + r;
-    const bool rv_ok = r < rows_here;
-    lim_eff[t] = min(rv_ok ? a.limits[row >> 3] : 0, c_end);
+  // B operand of the QK MFMA for k-step kk: lane (n, lg) holds row n, dims
+  // 64 (kk/2) + 16 lg + 8 (kk%2) + 0..7 (q4_0 K: in q4_kslot order).  The
+  // q4_0 format scores against rotated keys, so q is rotated first,
+  // q~ = H q / 16 (through this wave's part of lds_o).
+  f16x8 qop[8];
+  f16x8 qlo[QF32 ? 8 : 1];
+  float cbias[2] = {0.f, 0.f};
+  const int row = row_base + n;
+  const bool row_ok = n < rows_here;
+  const int lim_eff = min(row_ok ? a.limits[row >> 3] : 0, c_end);
+  {
     const int qi = row >> 3, hl = row & 7;
     const size_t qbase = ((size_t)qi * a.n_q_heads + (size_t)g * kGqa + hl) * 256;
-    float s0 = 0.f, s1 = 0.f;
+    float qv[8][8];
     for (int kk = 0; kk < 8; kk++) {
       const int d0 = 64 * (kk >> 1) + 16 * lg + 8 * (kk & 1);
-      f16x8 hi, lo;
       if (!QF32) {
         u32x4 w = {0u, 0u, 0u, 0u};
-        if (rv_ok) w = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.q) + qbase + d0);
-        hi = __builtin_bit_cast(f16x8, w);
-        float ss = 0.f;
-        for (int e = 0; e < 8; e++) ss += (float)hi[e];
-        if (kk < 4) s0 += ss; else s1 += ss;
+        if (row_ok) w = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.q) + qbase + d0);
+        const f16x8 h = __builtin_bit_cast(f16x8, w);
+        for (int e = 0; e < 8; e++) qv[kk][e] = (float)h[e];
       } else {
         f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
-        if (rv_ok) {
+        if (row_ok) {
           x0 = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(a.q) + qbase + d0);
           x1 = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(a.q) + qbase + d0 + 4);
         }
-        float ss = 0.f;
-        for (int e = 0; e < 8; e++) {
-          const float x = e < 4 ? x0[e] : x1[e - 4];
-          const _Float16 h = (_Float16)x;
+        for (int e = 0; e < 4; e++) {
+          qv[kk][e] = x0[e];
+          qv[kk][4 + e] = x1[e];
+        }
+      }
+    }
+    if (!kInt8K) {
+      float *qs = &lds_o[wave * 16 * 64 * 4];  // [16 rows][256] fp32 of this wave
+      for (int kk = 0; kk < 8; kk++) {
+        const int d0 = 64 * (kk >> 1) + 16 * lg + 8 * (kk & 1);
+        *reinterpret_cast<f32x4 *>(&qs[n * 256 + d0]) = f32x4{qv[kk][0], qv[kk][1], qv[kk][2], qv[kk][3]};
+        *reinterpret_cast<f32x4 *>(&qs[n * 256 + d0 + 4]) = f32x4{qv[kk][4], qv[kk][5], qv[kk][6], qv[kk][7]};
+      }
+      for (int r = 0; r < 16; r++) {
+        f32x4 y4 = *reinterpret_cast<const f32x4 *>(&qs[r * 256 + 4 * lane]);
+        float y[4] = {y4[0], y4[1], y4[2], y4[3]};
+        fwht256_lane4(y, lane);
+        *reinterpret_cast<f32x4 *>(&qs[r * 256 + 4 * lane]) = f32x4{y[0], y[1], y[2], y[3]};
+      }
+      for (int kk = 0; kk < 8; kk++) {
+        const int d0 = 64 * (kk >> 1) + 16 * lg + 8 * (kk & 1);
+        const f32x4 x0 = *reinterpret_cast<const f32x4 *>(&qs[n * 256 + d0]);
+        const f32x4 x1 = *reinterpret_cast<const f32x4 *>(&qs[n * 256 + d0 + 4]);
+        for (int t = 0; t < 8; t++) {
+          const int e = q4_kslot(t);
+          qv[kk][t] = e < 4 ? x0[e] : x1[e - 4];
+        }
+      }
+    }
+    float s0 = 0.f, s1 = 0.f;
+    for (int kk = 0; kk < 8; kk++) {
+      f16x8 hi, lo;
+      float ss = 0.f;
+      for (int e = 0; e < 8; e++) {
+        const float x = qv[kk][e];
+        const _Float16 h = (_Float16)x;
+        hi[e] = h;
+        if (QF32) {
           const _Float16 l = (_Float16)(x - (float)h);
-          hi[e] = h;
           lo[e] = l;
           ss += (float)h + (float)l;
+        } else {
+          ss += (float)h;
         }
-        if (kk < 4) s0 += ss; else s1 += ss;
       }
-      qop[t][kk] = hi;
-      if (QF32) qlo[t][kk] = lo;
+      if (kk < 4) s0 += ss; else s1 += ss;
+      qop[kk] = hi;
+      if (QF32) qlo[kk] = lo;
     }
-    s0 += lane_xor(s0, 16);
-    s0 += lane_xor(s0, 32);
-    s1 += lane_xor(s1, 16);
-    s1 += lane_xor(s1, 32);
-    cbias[t][0] = 1152.0f * s0;
-    cbias[t][1] = 1152.0f * s1;
+    if (kInt8K) {
+      s0 += lane_xor(s0, 16);
+      s0 += lane_xor(s0, 32);
+      s1 += lane_xor(s1, 16);
+      s1 += lane_xor(s1, 32);
+      cbias[0] = 1152.0f * s0;
+      cbias[1] = 1152.0f * s1;
+    }
   }
   // smallest visible-cell limit over the valid rows of this tile (wave-
   // uniform): steps that end below it need no masking at all
-  int lim_min = 0x7fffffff;
-  for (int t = 0; t < NQT; t++) {
-    int lm = (t * 16 + n < rows_here) ? lim_eff[t] : 0x7fffffff;
+  int lim_min;
+  {
+    int lm = row_ok ? lim_eff : 0x7fffffff;
     for (int msk = 1; msk < 16; msk <<= 1) lm = min(lm, lane_xor(lm, msk));
-    lim_min = min(lim_min, __builtin_amdgcn_readfirstlane(lm));
+    lim_min = __builtin_amdgcn_readfirstlane(lm);
   }
 
   // ---------------------------------------------------------------- main loop
@@ -246,22 +339,19 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
   // entries are read two steps ahead.  The refill is unconditional (past the
   // end it re-reads the wave's last step) so every wait for current data
   // leaves the next step's loads outstanding.
-  float m[NQT], lsum[NQT];
-  f32x4 o[NQT][16];
-  for (int t = 0; t < NQT; t++) {
-    m[t] = -1e30f;
-    lsum[t] = 0.f;
-    for (int j = 0; j < 16; j++) o[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  float m = -1e30f, lsum = 0.f;
+  f32x4 o[16];
+  for (int j = 0; j < 16; j++) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const f16x2 c1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
   const f16x2 c72 = {(_Float16)72.0f, (_Float16)72.0f};
+  const f16x2 c1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
 
   if (has_work) {
     int c = c_first;
     while (true) {
       // pages of the step after next
       Half nn0, nn1;
-      step_halves(a, g, min(c + 2 * stride, c_last), c_end, nn0, nn1);
+      step_halves<FMT>(a, g, min(c + 2 * stride, c_last), c_end, nn0, nn1);
       const int badp[2] = {cur0.bad, cur1.bad};
       // whole step inside every valid row's limit and on valid pages: no
       // masking (rows past rows_here then hold harmless values that are never
@@ -269,93 +359,115 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
       const bool full_step = c + kStep <= lim_min && !(cur0.bad | cur1.bad);
       const Half *nx[2] = {&nxt0, &nxt1};
 
-      // ---- scores S^T = K . Q^T (A = K codes + 1152 as fp16, B = q)
-      float s[NQT][8];
+      // ---- scores S^T = K . Q^T
+      float s[8];
       for (int h2 = 0; h2 < 2; h2++) {
-        f32x4 acc0[NQT], acc1[NQT];
-        for (int t = 0; t < NQT; t++) {
-          acc0[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-          acc1[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
         for (int j = 0; j < 4; j++) {
-          uint32_t l0, h0, l1, h1, l2, h2w, l3, h3;
-          i8x4_to_f16_biased(kr[h2][j].x, l0, h0);
-          i8x4_to_f16_biased(kr[h2][j].y, l1, h1);
-          i8x4_to_f16_biased(kr[h2][j].z, l2, h2w);
-          i8x4_to_f16_biased(kr[h2][j].w, l3, h3);
-          const f16x8 ka = pack8(l0, h0, l1, h1), kb = pack8(l2, h2w, l3, h3);
-          for (int t = 0; t < NQT; t++) {
-            if (j < 2) {
-              acc0[t] = mfma16x16x32(ka, qop[t][2 * j], acc0[t]);
-              acc0[t] = mfma16x16x32(kb, qop[t][2 * j + 1], acc0[t]);
-              if (QF32) {
-                acc0[t] = mfma16x16x32(ka, qlo[t][2 * j], acc0[t]);
-                acc0[t] = mfma16x16x32(kb, qlo[t][2 * j + 1], acc0[t]);
-              }
-            } else {
-              acc1[t] = mfma16x16x32(ka, qop[t][2 * j], acc1[t]);
-              acc1[t] = mfma16x16x32(kb, qop[t][2 * j + 1], acc1[t]);
-              if (QF32) {
-                acc1[t] = mfma16x16x32(ka, qlo[t][2 * j], acc1[t]);
-                acc1[t] = mfma16x16x32(kb, qlo[t][2 * j + 1], acc1[t]);
-              }
+          f16x8 ka, kb;
+          if (kInt8K) {
+            // INT8 codes -> fp16 code + 1152 (exact); the bias leaves the
+            // score through cbias
+            uint32_t l0, h0, l1, h1, l2, h2w, l3, h3;
+            i8x4_to_f16_biased(kr[h2][j].x, l0, h0);
+            i8x4_to_f16_biased(kr[h2][j].y, l1, h1);
+            i8x4_to_f16_biased(kr[h2][j].z, l2, h2w);
+            i8x4_to_f16_biased(kr[h2][j].w, l3, h3);
+            ka = pack8(l0, h0, l1, h1);
+            kb = pack8(l2, h2w, l3, h3);
+          } else {
+            // q4_0 nibbles -> fp16 (code - 8) * d16 of this cell's block
+            const uint32_t d = kdr[h2][j] & 0xffffu;
+            const f16x2 dd = as_f16x2(d | (d << 16));
+            uint32_t w[8];
+            for (int q = 0; q < 4; q++) {
+              const uint32_t x = kr[h2][j][q] >> q4_shift;
+              const uint32_t y = x >> 8;
+              w[2 * q] = as_u32((as_f16x2(and_or(x, 0x000F000Fu, 0x64006400u)) - c1032) * dd);
+              w[2 * q + 1] = as_u32((as_f16x2(and_or(y, 0x000F000Fu, 0x64006400u)) - c1032) * dd);
+            }
+            ka = pack8(w[0], w[1], w[2], w[3]);
+            kb = pack8(w[4], w[5], w[6], w[7]);
+          }
+          if (!kInt8K || j < 2) {
+            acc0 = mfma16x16x32(ka, qop[2 * j], acc0);
+            acc0 = mfma16x16x32(kb, qop[2 * j + 1], acc0);
+            if (QF32) {
+              acc0 = mfma16x16x32(ka, qlo[2 * j], acc0);
+              acc0 = mfma16x16x32(kb, qlo[2 * j + 1], acc0);
+            }
+          } else {
+            acc1 = mfma16x16x32(ka, qop[2 * j], acc1);
+            acc1 = mfma16x16x32(kb, qop[2 * j + 1], acc1);
+            if (QF32) {
+              acc1 = mfma16x16x32(ka, qlo[2 * j], acc1);
+              acc1 = mfma16x16x32(kb, qlo[2 * j + 1], acc1);
             }
           }
           // K chunk j of this half consumed: refill with the next step's
-          kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + 64 * j, nx[h2]->k_soff, 0);
+          kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + kstep_j * j, nx[h2]->k_soff, 0);
         }
-        for (int t = 0; t < NQT; t++) {
-          for (int i = 0; i < 4; i++) {
+        for (int i = 0; i < 4; i++) {
+          if (kInt8K) {
             const f32x4 kq = ksr[h2][i >> 1];
             const float d0 = kq[2 * (i & 1)], d1 = kq[2 * (i & 1) + 1];
-            s[t][4 * h2 + i] = a.scale2 * (d0 * (acc0[t][i] - cbias[t][0]) + d1 * (acc1[t][i] - cbias[t][1]));
-          }
-          if (!full_step) {
-            for (int i = 0; i < 4; i++) {
-              const int cell = c + 16 * h2 + 4 * lg + i;
-              float sv = cell < lim_eff[t] ? s[t][4 * h2 + i] : -INFINITY;
-              s[t][4 * h2 + i] = badp[h2] ? __builtin_nanf("") : sv;
-            }
+            s[4 * h2 + i] = a.scale2 * (d0 * (acc0[i] - cbias[0]) + d1 * (acc1[i] - cbias[1]));
+          } else {
+            s[4 * h2 + i] = a.scale2 * acc0[i];
           }
         }
-        ksr[h2][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, ks_voff, nx[h2]->ks_soff, 0));
-        ksr[h2][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, ks_voff + 16, nx[h2]->ks_soff, 0));
+        if (!full_step) {
+          for (int i = 0; i < 4; i++) {
+            const int cell = c + 16 * h2 + 4 * lg + i;
+            const float sv = cell < lim_eff ? s[4 * h2 + i] : -INFINITY;
+            s[4 * h2 + i] = badp[h2] ? __builtin_nanf("") : sv;
+          }
+        }
+        load_ks(h2, *nx[h2]);
       }
 
-      // ---- online softmax against a reference max m[t] that only moves
-      // when a row's max exceeds it by more than 2^kLazy: p <= 2^kLazy stays
-      // exact enough in fp16 and the accumulators are rarely rescaled
-      f16x8 pop[NQT];
-      for (int t = 0; t < NQT; t++) {
-        float mx = s[t][0];
-        for (int e = 1; e < 8; e++) mx = fmaxf(mx, s[t][e]);
+      // ---- online softmax against a reference max m that only moves when
+      // a row's max exceeds it by more than 2^kLazy: p <= 2^kLazy stays exact
+      // enough in fp16 and the accumulators are rarely rescaled
+      f16x8 pop;
+      {
+        float mx = s[0];
+        for (int e = 1; e < 8; e++) mx = fmaxf(mx, s[e]);
         mx = fmaxf(mx, lane_xor(mx, 16));
         mx = fmaxf(mx, lane_xor(mx, 32));
-        if (__any(mx > m[t] + kLazy)) {
-          const float mnew = fmaxf(m[t], mx);
-          const float alpha = fast_exp2(m[t] - mnew);
-          lsum[t] *= alpha;
-          m[t] = mnew;
+        if (__any(mx > m + kLazy)) {
+          const float mnew = fmaxf(m, mx);
+          const float alpha = fast_exp2(m - mnew);
+          lsum *= alpha;
+          m = mnew;
           // O rows in the accumulator layout are 4*lg + i: fetch their factor
           float al[4];
           for (int i = 0; i < 4; i++) al[i] = lane_get(alpha, 4 * lg + i);
           for (int j = 0; j < 16; j++)
-            for (int i = 0; i < 4; i++) o[t][j][i] *= al[i];
+            for (int i = 0; i < 4; i++) o[j][i] *= al[i];
         }
         float ps = 0.f;
         for (int e = 0; e < 8; e++) {
-          const float p = fast_exp2(s[t][e] - m[t]);
+          const float p = fast_exp2(s[e] - m);
           ps += p;
-          pop[t][e] = (_Float16)p;
+          pop[e] = (_Float16)p;
         }
-        lsum[t] += ps;
+        lsum += ps;
       }
 
-      // ---- O += P . V  (B = (code - 8) * d16 in fp16, 4 tiles per byte pair)
+      // ---- O += P . V; the V scales of the cell pairs (k-slots 2k, 2k+1)
+      // as fp16 pairs, zeroed for cells past the split
       uint32_t dsc[4];
       for (int k = 0; k < 4; k++) {
         const int h2 = k >> 1;
-        uint32_t w = (k & 1) ? vdr[h2].y : vdr[h2].x;
+        uint32_t w;
+        if (kQ4V) {
+          w = (k & 1) ? vdr[h2].y : vdr[h2].x;
+        } else {
+          const f32x4 vs = vsr[h2][k & 1];
+          const float da = v8_grp ? vs[1] : vs[0], db = v8_grp ? vs[3] : vs[2];
+          w = as_u32(f16x2{(_Float16)da, (_Float16)db});
+        }
         if (c + kStep > c_end) {
           const int ca = c + 16 * h2 + 4 * lg + 2 * (k & 1);
           if (ca >= c_end) w &= 0xffff0000u;      // zero the scale of cells past the split
@@ -363,42 +475,52 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
         }
         dsc[k] = w;
       }
-      for (int h2 = 0; h2 < 2; h2++)
-        vdr[h2] = __builtin_amdgcn_raw_buffer_load_b64(rv, vd_voff, nx[h2]->vd_soff, 0);
-      for (int grp = 0; grp < 4; grp++) {
-        const int dw = grp >> 1;
-        const uint32_t sel = (grp & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t b0[4], b1[4], b2[4], b3[4];
-        for (int k = 0; k < 4; k++) {
-          const int h2 = k >> 1, ia = 2 * (k & 1);
-          const uint32_t wa = dw ? vr[h2][ia].y : vr[h2][ia].x;
-          const uint32_t wb = dw ? vr[h2][ia + 1].y : vr[h2][ia + 1].x;
-          const uint32_t x = perm(wb, wa, sel);  // [a.byte, a.byte+1, b.byte, b.byte+1]
-          const uint32_t y = x >> 8;
-          const f16x2 dd = as_f16x2(dsc[k]);
-          // a low nibble under exponent 25 reads 1024 + n, a high nibble
-          // left in bits 4..7 under exponent 21 reads 64 + n
-          b0[k] = as_u32((as_f16x2(and_or(x, 0x000F000Fu, 0x64006400u)) - c1032) * dd);
-          b1[k] = as_u32((as_f16x2(and_or(x, 0x00F000F0u, 0x54005400u)) - c72) * dd);
-          b2[k] = as_u32((as_f16x2(and_or(y, 0x000F000Fu, 0x64006400u)) - c1032) * dd);
-          b3[k] = as_u32((as_f16x2(and_or(y, 0x00F000F0u, 0x54005400u)) - c72) * dd);
+      for (int h2 = 0; h2 < 2; h2++) load_vd(h2, *nx[h2]);
+      if (kQ4V) {
+        // B = (code - 8) * d16 in fp16, 4 tiles per byte pair
+        for (int grp = 0; grp < 4; grp++) {
+          const int dw = grp >> 1;
+          const uint32_t sel = (grp & 1) ? 0x07060302u : 0x05040100u;
+          uint32_t b0[4], b1[4], b2[4], b3[4];
+          for (int k = 0; k < 4; k++) {
+            const int h2 = k >> 1, ia = 2 * (k & 1);
+            const uint32_t wa = dw ? vr[h2][ia].y : vr[h2][ia].x;
+            const uint32_t wb = dw ? vr[h2][ia + 1].y : vr[h2][ia + 1].x;
+            const uint32_t x = perm(wb, wa, sel);  // [a.byte, a.byte+1, b.byte, b.byte+1]
+            const uint32_t y = x >> 8;
+            const f16x2 dd = as_f16x2(dsc[k]);
+            // a low nibble under exponent 25 reads 1024 + n, a high nibble
+            // left in bits 4..7 under exponent 21 reads 64 + n
+            b0[k] = as_u32((as_f16x2(and_or(x, 0x000F000Fu, 0x64006400u)) - c1032) * dd);
+            b1[k] = as_u32((as_f16x2(and_or(x, 0x00F000F0u, 0x54005400u)) - c72) * dd);
+            b2[k] = as_u32((as_f16x2(and_or(y, 0x000F000Fu, 0x64006400u)) - c1032) * dd);
+            b3[k] = as_u32((as_f16x2(and_or(y, 0x00F000F0u, 0x54005400u)) - c72) * dd);
+          }
+          if (grp == 3) {
+            // every V byte of this step consumed: refill with the next step's
+            for (int h2 = 0; h2 < 2; h2++) load_v(h2, *nx[h2]);
+          }
+          const int jb = 2 * grp;
+          o[jb] = mfma16x16x32(pop, pack8(b0[0], b0[1], b0[2], b0[3]), o[jb]);          // tile jb     (byte lo nibble)
+          o[jb + 8] = mfma16x16x32(pop, pack8(b1[0], b1[1], b1[2], b1[3]), o[jb + 8]);  // tile jb + 8 (byte hi nibble)
+          o[jb + 1] = mfma16x16x32(pop, pack8(b2[0], b2[1], b2[2], b2[3]), o[jb + 1]);  // tile jb + 1
+          o[jb + 9] = mfma16x16x32(pop, pack8(b3[0], b3[1], b3[2], b3[3]), o[jb + 9]);  // tile jb + 9
         }
-        if (grp == 3) {
-          // every V byte of this step consumed: refill with the next step's
-          for (int h2 = 0; h2 < 2; h2++)
-            for (int i = 0; i < 4; i++)
-              vr[h2][i] = __builtin_amdgcn_raw_buffer_load_b64(rv, v_voff + 128 * i, nx[h2]->v_soff, 0);
-        }
-        const int jb = 2 * grp;
-        const f16x8 B0 = pack8(b0[0], b0[1], b0[2], b0[3]);  // tile jb     (byte lo nibble)
-        const f16x8 B1 = pack8(b1[0], b1[1], b1[2], b1[3]);  // tile jb + 8 (byte hi nibble)
-        const f16x8 B2 = pack8(b2[0], b2[1], b2[2], b2[3]);  // tile jb + 1
-        const f16x8 B3 = pack8(b3[0], b3[1], b3[2], b3[3]);  // tile jb + 9
-        for (int t = 0; t < NQT; t++) {
-          o[t][jb] = mfma16x16x32(pop[t], B0, o[t][jb]);
-          o[t][jb + 8] = mfma16x16x32(pop[t], B1, o[t][jb + 8]);
-          o[t][jb + 1] = mfma16x16x32(pop[t], B2, o[t][jb + 1]);
-          o[t][jb + 9] = mfma16x16x32(pop[t], B3, o[t][jb + 9]);
+      } else {
+        // INT8 V: tile j holds dim 16 n + j; B = code * d in fp16, the code
+        // made exact as fp16 1152 + code by one xor under the 0x64 exponent
+        for (int j = 0; j < 16; j++) {
+          const uint32_t sel = (0x0cu << 24) | ((4u + (j & 3)) << 16) | (0x0cu << 8) | (uint32_t)(j & 3);
+          uint32_t b[4];
+          for (int k = 0; k < 4; k++) {
+            const int h2 = k >> 1, ia = 2 * (k & 1);
+            const uint32_t x = perm(vr8[h2][ia + 1][j >> 2], vr8[h2][ia][j >> 2], sel);  // [a_j, 0, b_j, 0]
+            b[k] = as_u32((as_f16x2(x ^ 0x64806480u) - c1152) * as_f16x2(dsc[k]));
+          }
+          if (j == 15) {
+            for (int h2 = 0; h2 < 2; h2++) load_v(h2, *nx[h2]);
+          }
+          o[j] = mfma16x16x32(pop, pack8(b[0], b[1], b[2], b[3]), o[j]);
         }
       }
 
@@ -414,17 +536,13 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
   // ---------------------------------------------------------------- workgroup merge
   // every wave parks its state in LDS (accumulator layout), then all threads
   // merge the 4 states element-wise in wave order
-  for (int t = 0; t < NQT; t++) {
-    lsum[t] += lane_xor(lsum[t], 16);
-    lsum[t] += lane_xor(lsum[t], 32);
-  }
-  static_assert(NQT == 1, "the workgroup merge handles one 16-row tile");
+  lsum += lane_xor(lsum, 16);
+  lsum += lane_xor(lsum, 32);
   if (lg == 0) {
-    lds_m[wave * 16 + n] = m[0];
-    lds_l[wave * 16 + n] = lsum[0];
+    lds_m[wave * 16 + n] = m;
+    lds_l[wave * 16 + n] = lsum;
   }
-  for (int j = 0; j < 16; j++)
-    *reinterpret_cast<f32x4 *>(&lds_o[((wave * 16 + j) * 64 + lane) * 4]) = o[0][j];
+  for (int j = 0; j < 16; j++) *reinterpret_cast<f32x4 *>(&lds_o[((wave * 16 + j) * 64 + lane) * 4]) = o[j];
   __syncthreads();
 
   const size_t rows_total = (size_t)a.n_rows;
@@ -459,9 +577,9 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
       const int r = 4 * Llg + i;
       if (r >= rows_here) continue;
       float *prow = a.part_o + (sp * rows_total + row_base + r) * 256;
-      // tiles j, j+1 hold dims d, d+1 (j even, same group of 8)
-      *reinterpret_cast<float2 *>(prow + o_dim(Ln, 4 * jq)) = make_float2(val[0][i], val[1][i]);
-      *reinterpret_cast<float2 *>(prow + o_dim(Ln, 4 * jq + 2)) = make_float2(val[2][i], val[3][i]);
+      // tiles j, j+1 hold dims d, d+1 (j even)
+      *reinterpret_cast<float2 *>(prow + o_dim<kQ4V>(Ln, 4 * jq)) = make_float2(val[0][i], val[1][i]);
+      *reinterpret_cast<float2 *>(prow + o_dim<kQ4V>(Ln, 4 * jq + 2)) = make_float2(val[2][i], val[3][i]);
       if (jq == 0 && Ln == 0) a.part_ml[sp * rows_total + row_base + r] = make_float2(M[i], Ls[i]);
     }
   }
@@ -537,7 +655,7 @@ __global__ __launch_bounds__(kCombineWaves * 64) void attn_combine_kernel(const 
   float y[4];
   const float inv = 1.0f / L;
   for (int i = 0; i < 4; i++) y[i] = tot[i] * inv;
-  fwht256_lane4(y, lane);
+  if (a.v_rotated) fwht256_lane4(y, lane);
   const int qi = row >> 3, hl = row & 7;
   float *op = a.out + ((size_t)qi * a.n_q_heads + (size_t)g * kGqa + hl) * 256 + 4 * lane;
   *reinterpret_cast<f32x4 *>(op) = f32x4{y[0], y[1], y[2], y[3]};
@@ -590,6 +708,7 @@ int launch_attn_splitk(const AttnCall &c) {
   a.kc = (const int8_t *)pool->run[0];
   a.ks = (const float *)pool->run[1];
   a.vq = (const uint8_t *)pool->run[2];
+  a.vs = (const float *)pool->run[3];
   a.pt = c.seq->page_table;
   a.q = c.q;
   a.out = c.out;
@@ -605,10 +724,12 @@ int launch_attn_splitk(const AttnCall &c) {
     const size_t kb = run_bytes(pool->fmt, 0, pool->n_pages, a.P, H, kHeadDim);
     const size_t sb = run_bytes(pool->fmt, 1, pool->n_pages, a.P, H, kHeadDim);
     const size_t vb = run_bytes(pool->fmt, 2, pool->n_pages, a.P, H, kHeadDim);
-    if (kb > 0x7fffffffu || sb > 0x7fffffffu || vb > 0x7fffffffu) return KV_ERR_UNSUPPORTED;
+    const size_t vsb = run_bytes(pool->fmt, 3, pool->n_pages, a.P, H, kHeadDim);
+    if (kb > 0x7fffffffu || sb > 0x7fffffffu || vb > 0x7fffffffu || vsb > 0x7fffffffu) return KV_ERR_UNSUPPORTED;
     a.k_bytes = (int)kb;
     a.ks_bytes = (int)sb;
     a.v_bytes = (int)vb;
+    a.vs_bytes = (int)vsb;
   }
   a.n_q_heads = c.n_q_heads;
   a.n_rows = n_rows;
@@ -620,10 +741,15 @@ int launch_attn_splitk(const AttnCall &c) {
   a.n_splits = plan.n_splits;
 
   dim3 grid(plan.n_splits, H, passes);
-  if (qf32)
-    launch((attn_splitk_kernel<1, true>), grid, dim3(256), c.stream, a);
-  else
-    launch((attn_splitk_kernel<1, false>), grid, dim3(256), c.stream, a);
+  a.v_rotated = pool->fmt != KV_FMT_INT8;
+  switch (pool->fmt * 2 + (qf32 ? 1 : 0)) {
+    case KV_FMT_INT8 * 2: launch((attn_splitk_kernel<false, KV_FMT_INT8>), grid, dim3(256), c.stream, a); break;
+    case KV_FMT_INT8 * 2 + 1: launch((attn_splitk_kernel<true, KV_FMT_INT8>), grid, dim3(256), c.stream, a); break;
+    case KV_FMT_Q4_0 * 2: launch((attn_splitk_kernel<false, KV_FMT_Q4_0>), grid, dim3(256), c.stream, a); break;
+    case KV_FMT_Q4_0 * 2 + 1: launch((attn_splitk_kernel<true, KV_FMT_Q4_0>), grid, dim3(256), c.stream, a); break;
+    case KV_FMT_K8V4 * 2: launch((attn_splitk_kernel<false, KV_FMT_K8V4>), grid, dim3(256), c.stream, a); break;
+    default: launch((attn_splitk_kernel<true, KV_FMT_K8V4>), grid, dim3(256), c.stream, a); break;
+  }
   if (int e = launch_status()) return e;
   launch(attn_combine_kernel, dim3(n_rows, H), dim3(kCombineWaves * 64), c.stream, a);
   return launch_status();

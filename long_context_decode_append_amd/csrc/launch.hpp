@@ -25,10 +25,9 @@ inline void launch(Kernel kernel, dim3 grid, dim3 block, hipStream_t s, Args... 
   hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
 }
 
-int launch_append_k8v4(const kv_pool *pool, const kv_seq *seq, const void *k, const void *v,
-                       int dtype, int pos0, int n, hipStream_t s);
-int launch_gather_k8v4(const kv_pool *pool, const kv_seq *seq, int pos0, int n, void *okc,
-                       void *oks, void *ovb, hipStream_t s);
+int launch_append(const kv_pool *pool, const kv_seq *seq, const void *k, const void *v, int dtype, int pos0,
+                  int n, hipStream_t s);
+int launch_gather(const kv_pool *pool, const kv_seq *seq, int pos0, int n, void *const out[4], hipStream_t s);
 int launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 int launch_probe_read(const void *buf, size_t bytes, void *sink, hipStream_t s);
 

@@ -104,6 +104,26 @@ def test_validation_errors_before_launch(k8):
     assert L.attn_prefill_chunk(P(pool), P(seq), dummy, 0, 16, 60, 5, 0.0, out, None, 0, None) == -3
     assert L.attn_prefill_chunk(P(pool), P(seq), dummy, 0, 16, 10, 0, 0.0, out, None, 0, None) == 0
     assert L.kv_strerror(-6) == b"workspace missing or too small"
+    # generic append / gather over the three formats
+    for fmt, ptrs in ((1, (16, 32, 48, 64)), (2, (16, 0, 48, 0)), (3, (16, 32, 48, 0))):
+        pl = _pool(k8, fmt=fmt, ptrs=ptrs)
+        assert L.kv_append(P(pl), P(seq), dummy, dummy, 0, 0, 0, None) == 0
+        assert L.kv_append(P(pl), P(seq), None, dummy, 0, 0, 1, None) == -1
+        assert L.kv_gather_runs(P(pl), P(seq), 0, 65, dummy, dummy, dummy, dummy, None) == -3
+        assert L.kv_gather_runs(P(pl), P(seq), 0, 4, dummy, dummy, None, dummy, None) == -1
+    # int8 needs its fourth run (V scales) and a V-scales output
+    assert L.kv_append(P(_pool(k8, fmt=1, ptrs=(16, 32, 48, 0))), P(seq), dummy, dummy, 0, 0, 1,
+                       None) == -1
+    assert L.kv_gather_runs(P(_pool(k8, fmt=1, ptrs=(16, 32, 48, 64))), P(seq), 0, 4, dummy, dummy,
+                            dummy, None, None) == -1
+    # q4_0 needs no scale outputs
+    assert L.kv_gather_runs(P(_pool(k8, fmt=2, ptrs=(16, 0, 48, 0))), P(seq), 0, 0, dummy, None,
+                            dummy, None, None) == 0
+    # attention accepts the three formats, prefill only k8v4
+    assert L.attn_decode(P(_pool(k8, fmt=2, ptrs=(16, 0, 48, 0))), P(seq), dummy, 0, 16, 65, 0.0,
+                         out, dummy, 1 << 20, None) == -3
+    assert L.attn_prefill_chunk(P(_pool(k8, fmt=1, ptrs=(16, 32, 48, 64))), P(seq), dummy, 0, 16, 0,
+                                1, 0.0, out, None, 0, None) == -5
     # the streaming-read yardstick
     assert L.kv_probe_read(None, 1024, dummy, None) == -1
     assert L.kv_probe_read(dummy, 1024, None, None) == -1

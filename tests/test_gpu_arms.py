@@ -1,0 +1,161 @@
+"""GPU parity of the comparison formats (int8: INT8 K and V, 1,056 B/cell;
+q4_0: rotated Q4_0 K and V, 576 B/cell) through the C ABI against the CPU
+oracle: pool bytes and gathered bytes bit-exact, decode and verify within
+2e-3 max relative error per (query row, head)."""
+import sys
+
+import numpy as np
+import pytest
+
+from long_context_decode_append_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+FMT_INT8, FMT_Q4_0, FMT_K8V4 = 1, 2, 3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def k8():
+    import long_context_decode_append_amd as k8
+    k8.lib()
+    return k8
+
+
+def t_(x, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+def rel_err(out, ref):
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float((np.abs(out - ref).max(axis=-1) / np.abs(ref).max(axis=-1)).max())
+
+
+class ArmCase:
+    """The same seeded tokens appended to a GPU pool and an oracle pool of one format."""
+
+    def __init__(self, orc, k8, dev, fmt, seed, ctx, P, n_pages, n_table, dtype=np.float16,
+                 outlier_frac=0.0, chunk=8192, fill=0xA5):
+        self.fmt = fmt
+        self.pt = synth.page_table(seed, n_table, n_pages)
+        outl = synth.outlier_channels(seed, 2, 256, outlier_frac) if outlier_frac else None
+        self.gpool = k8.KvPool(fmt, n_pages, P, 2, device=dev, fill=fill)
+        self.opool = orc.OraclePool(fmt, n_pages, P, 2, sentinel=fill)
+        self.gpt = t_(self.pt, dev)
+        for s in range(0, ctx, chunk):
+            n = min(chunk, ctx - s)
+            k, v = synth.kv_tokens(seed, 0, s, n, 2, 256, dtype, outl)
+            k8.kv_append(self.gpool, self.gpt, t_(k, dev), t_(v, dev), s)
+            self.opool.append(self.pt, k, v, s)
+
+
+@pytest.mark.parametrize("fmt", [FMT_INT8, FMT_Q4_0])
+@pytest.mark.parametrize("dtype,ctx,P,n_pages", [(np.float32, 1024, 16, 64),
+                                                 (np.float16, 1000, 16, 70),
+                                                 (np.float16, 700, 256, 4)])
+def test_arm_pool_bytes_and_gather_bitwise(orc, k8, dev, fmt, dtype, ctx, P, n_pages):
+    say(f"arm append/gather fmt={fmt} dtype={dtype.__name__} ctx={ctx} P={P}")
+    c = ArmCase(orc, k8, dev, fmt, 0, ctx, P, n_pages, (ctx + P - 1) // P, dtype=dtype, chunk=333)
+    for r in range(4):
+        if c.opool.runs[r] is None:
+            assert c.gpool.runs[r] is None
+            continue
+        assert np.array_equal(c.gpool.runs[r].cpu().numpy(), c.opool.runs[r]), f"run {r} differs"
+    g = [x.cpu().numpy() for x in k8.kv_gather_runs(c.gpool, c.gpt, 0, ctx)]
+    o = c.opool.gather(c.pt, 0, ctx)
+    assert len(g) == len(o)
+    for x, y in zip(g, o):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+    w = [x.cpu().numpy() for x in k8.kv_gather_runs(c.gpool, c.gpt, 37, 101)]
+    for x, y in zip(w, o):
+        assert np.array_equal(x.view(np.uint8), y[37:138].view(np.uint8))
+
+
+def test_k8v4_append_through_generic_entry_equals_k8v4_entry(k8, dev):
+    pt = synth.page_table(1, 8, 8)
+    k, v = synth.kv_tokens(1, 0, 0, 120, 2, 256, np.float16)
+    a = k8.K8V4Pool(8, 16, 2, device=dev, fill=0)
+    b = k8.KvPool(FMT_K8V4, 8, 16, 2, device=dev, fill=0)
+    gpt = t_(pt, dev)
+    k8.kv_append_k8v4(a, gpt, t_(k, dev), t_(v, dev), 0)
+    k8.kv_append(b, gpt, t_(k, dev), t_(v, dev), 0)
+    for r in range(3):
+        assert np.array_equal(a.runs[r].cpu().numpy(), b.runs[r].cpu().numpy())
+
+
+@pytest.fixture(scope="module", params=[FMT_INT8, FMT_Q4_0])
+def arm_tiny(request, orc, k8, dev):
+    return ArmCase(orc, k8, dev, request.param, 0, 1024, 16, 64, 64, dtype=np.float32, chunk=1024)
+
+
+@pytest.mark.parametrize("n_ctx", [1, 2, 31, 33, 300, 1000, 1024])
+@pytest.mark.parametrize("qdtype", [np.float16, np.float32])
+def test_arm_decode_parity_tiny(orc, k8, dev, arm_tiny, n_ctx, qdtype):
+    say(f"arm decode fmt={arm_tiny.fmt} n_ctx={n_ctx} q={qdtype.__name__}")
+    q = synth.queries(0, 0, n_ctx, 1, 16, 256, qdtype)
+    ws = k8.attn_workspace(arm_tiny.gpool, 1, 1024)
+    out = k8.attn_decode(arm_tiny.gpool, arm_tiny.gpt, t_(q[0], dev), n_ctx, ws).cpu().numpy()
+    ref = orc.attention_from_pool(arm_tiny.opool, arm_tiny.pt, q, [n_ctx])[0]
+    err = rel_err(out, ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("n_vis", [[1020, 1021, 1022, 1023, 1024], [700, 33, 1],
+                                   [5, 1024, 64, 900, 17, 33, 1, 1000, 2]])
+def test_arm_verify_parity_tiny(orc, k8, dev, arm_tiny, n_vis):
+    say(f"arm verify fmt={arm_tiny.fmt} n_q={len(n_vis)}")
+    q = synth.queries(0, 0, 77, len(n_vis), 16, 256, np.float16)
+    ws = k8.attn_workspace(arm_tiny.gpool, len(n_vis), 1024)
+    out = k8.attn_verify(arm_tiny.gpool, arm_tiny.gpt, t_(q, dev), n_vis, ws).cpu().numpy()
+    ref = orc.attention_from_pool(arm_tiny.opool, arm_tiny.pt, q, n_vis)
+    err = rel_err(out, ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+
+
+def test_arm_verify_one_row_equals_decode_bitwise(k8, dev, arm_tiny):
+    q = synth.queries(0, 0, 5, 1, 16, 256, np.float16)
+    ws = k8.attn_workspace(arm_tiny.gpool, 1, 1024)
+    a = k8.attn_decode(arm_tiny.gpool, arm_tiny.gpt, t_(q[0], dev), 999, ws).cpu().numpy()
+    b = k8.attn_verify(arm_tiny.gpool, arm_tiny.gpt, t_(q, dev), [999], ws).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b[0].view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", [FMT_INT8, FMT_Q4_0, FMT_K8V4])
+def test_arms_decode_32768_with_outlier_channels(orc, k8, dev, fmt):
+    """The three formats on the same raw inputs: 32,768 cells, 3 outlier
+    channels per KV head (x8 on K and V), P = 256, 128 pages drawn from a
+    256-page pool."""
+    say(f"arms 32768 fmt={fmt}")
+    c = ArmCase(orc, k8, dev, fmt, 2, 32768, 256, 256, 128, outlier_frac=0.01)
+    q = synth.queries(2, 0, 0, 1, 16, 256, np.float16)
+    ws = k8.attn_workspace(c.gpool, 1, 32768)
+    out = k8.attn_decode(c.gpool, c.gpt, t_(q[0], dev), 32768, ws).cpu().numpy()
+    ref = orc.attention_from_pool(c.opool, c.pt, q, [32768])[0]
+    err = rel_err(out, ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+
+
+def test_arm_prefill_is_unsupported(k8, dev):
+    pool = k8.KvPool(FMT_INT8, 4, 16, 2, device=dev, fill=0)
+    pt = t_(np.arange(4, dtype=np.int32), dev)
+    q = t_(np.zeros((4, 16, 256), np.float16), dev)
+    with pytest.raises(k8.KvError):
+        k8.attn_prefill_chunk(pool, pt, q, 0)
