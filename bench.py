@@ -102,6 +102,29 @@ def timed_calls(torch, fn, n):
     return event_mean_ms(torch, pairs)
 
 
+def graph_calls_ms(torch, fn, n_calls, replays=4):
+    """Device time per call of fn(0..n_calls-1) captured back to back in one
+    HIP graph (so host launch overhead is excluded), mean over replays."""
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(n_calls):
+                fn(i)
+    torch.cuda.current_stream().wait_stream(cap)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (replays * n_calls)
+
+
 def stream_read_ceiling(torch, k8, dev):
     """Attainable read bandwidth: a plain streaming read of 1 GiB (beyond the
     Infinity Cache) by the library's yardstick kernel."""
@@ -109,7 +132,7 @@ def stream_read_ceiling(torch, k8, dev):
     buf.fill_(1)
     sink = torch.zeros(4096, dtype=torch.uint8, device=dev)
     k8.probe_read(buf, sink)
-    ms, _ = timed_calls(torch, lambda i: k8.probe_read(buf, sink), 5)
+    ms = graph_calls_ms(torch, lambda i: k8.probe_read(buf, sink), 5)
     del buf
     return {"gbs": round((1 << 30) / ms / 1e6, 1), "bytes": 1 << 30,
             "kernel": "probe_read_kernel: 1,024 workgroups x 256 lanes, 4 x 16 B non-temporal loads in flight per lane"}
@@ -259,9 +282,9 @@ def main():
         del graphs
         extra = bench_extra(torch, k8, synth, dev, log)
         extra["stream_read_ceiling"] = stream_read_ceiling(torch, k8, dev)
-        dc_ms, _ = timed_calls(torch, lambda i: k8.attn_decode(
+        dc_ms = graph_calls_ms(torch, lambda i: k8.attn_decode(
             pools[i % layers], tables[i % layers], q_all[0][i % layers], ctx, ws,
-            out=outs[i % layers]), 2 * layers)
+            out=outs[i % layers]), layers, replays=2)
         extra["decode_118750_split_plus_combine"] = {
             "us": round(dc_ms * 1e3, 3),
             "hbm_frac": round(ctx * CELL_BYTES / dc_ms / 1e6 / HBM_PEAK_GBS, 4)}
@@ -360,8 +383,8 @@ def bench_extra(torch, k8, synth, dev, log):
     reps = 8 * n_pools
     d_ms, _ = timed_launches(torch, k8, lambda i: k8.attn_decode(
         pools[i % n_pools], tables[i % n_pools], q1, ctx, ws1), reps)
-    dc_ms, _ = timed_calls(torch, lambda i: k8.attn_decode(
-        pools[i % n_pools], tables[i % n_pools], q1, ctx, ws1), reps)
+    dc_ms = graph_calls_ms(torch, lambda i: k8.attn_decode(
+        pools[i % n_pools], tables[i % n_pools], q1, ctx, ws1), 2 * n_pools)
     v_ms, _ = timed_launches(torch, k8, lambda i: k8.attn_verify(
         pools[i % n_pools], tables[i % n_pools], q5, nv, ws5), reps)
     b = ctx * CELL_BYTES
@@ -370,13 +393,12 @@ def bench_extra(torch, k8, synth, dev, log):
                             "pools_rotated": n_pools, "kernel": "split kernel alone",
                             "us_split_plus_combine": round(dc_ms * 1e3, 3),
                             "hbm_frac_split_plus_combine": round(b / dc_ms / 1e6 / HBM_PEAK_GBS, 4)}
-    # context sweep on the same pools: whole decode call (split + combine)
+    # context sweep on the same pools: whole decode call (split + combine),
+    # calls replayed back to back from a graph
     sweep = {}
     for n in (1024, 4096, 16384, 32768, 65536, 118750, 131072, 240000):
-        for i in range(n_pools):
-            k8.attn_decode(pools[i], tables[i], q1, n, ws1)
-        s_ms, _ = timed_calls(torch, lambda i: k8.attn_decode(
-            pools[i % n_pools], tables[i % n_pools], q1, n, ws1), 4 * n_pools)
+        s_ms = graph_calls_ms(torch, lambda i, n=n: k8.attn_decode(
+            pools[i % n_pools], tables[i % n_pools], q1, n, ws1), 2 * n_pools)
         sweep[str(n)] = {"us": round(s_ms * 1e3, 2), "gbs": round(n * CELL_BYTES / s_ms / 1e6, 1),
                          "hbm_frac": round(n * CELL_BYTES / s_ms / 1e6 / HBM_PEAK_GBS, 4)}
     out["decode_sweep_split_plus_combine"] = sweep
@@ -394,8 +416,43 @@ def bench_extra(torch, k8, synth, dev, log):
     out["prefill_8192_at_231808"] = {"ms": round(p_ms, 3), "tflops": round(flops / p_ms / 1e9, 2),
                                      "mfma_frac": round(flops / p_ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
                                      "flop": flops}
+    out["formats_32768"] = bench_formats_32768(torch, k8, synth, dev, log)
     log(f"extra: {json.dumps(out)}")
     return out
+
+
+def bench_formats_32768(torch, k8, synth, dev, log):
+    """Decode at 32,768 cells for the three formats on the same raw inputs:
+    3 outlier channels per KV head (x8 on K and V), P = 256, 128 pages drawn
+    from a 256-page pool, 16 layer pools per format rotated (beyond the
+    Infinity Cache).  Whole calls replayed from a graph."""
+    ctx, P, n_pages, n_table, layers = 32768, 256, 256, 128, 16
+    outl = synth.outlier_channels(2, 2, 256, 0.01)
+    q = synth.queries_device(2, 0, 0, 1, 16, 256, dev)[0]
+    res = {}
+    for fmt, name in ((3, "k8v4"), (1, "int8"), (2, "q4_0")):
+        log(f"formats: filling {layers} {name} pools of {ctx} cells ...")
+        pools, tables = [], []
+        for l in range(layers):
+            pool = k8.KvPool(fmt, n_pages, P, 2, device=dev)
+            pt = make_table(torch, synth, 2, l, n_table, n_pages, dev)
+            for c, s in enumerate(range(0, ctx, synth.CHUNK)):
+                n = min(synth.CHUNK, ctx - s)
+                kk, vv = synth.kv_chunk_device(2, l, c, n, 2, 256, dev, outliers=outl)
+                k8.kv_append(pool, pt, kk, vv, s)
+            pools.append(pool)
+            tables.append(pt)
+        ws = k8.attn_workspace(pools[0], 1, ctx)
+        ms = graph_calls_ms(torch, lambda i: k8.attn_decode(pools[i % layers], tables[i % layers], q, ctx, ws),
+                            layers)
+        cell = int(k8.lib().kv_cell_bytes(fmt, 2, 256))
+        b = ctx * cell
+        res[name] = {"us": round(ms * 1e3, 2), "mb_per_step": round(b / 1e6, 2),
+                     "gbs": round(b / ms / 1e6, 1), "hbm_frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4),
+                     "cell_bytes": cell}
+        del pools, tables
+        torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":

@@ -27,11 +27,13 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-I", os.path.join(ROOT, "include")]
 
 # per-source extra flags: the quantizers must not fuse multiply and add; the
-# split attention kernel keeps its MFMA accumulators in VGPRs
+# attention kernels keep their MFMA accumulators in VGPRs (the prefill
+# kernel's conditional rescale of O otherwise copies all of O between AGPRs
+# and VGPRs every tile)
 SOURCES = {
     "append_gather.hip": ["-ffp-contract=off"],
     "attn_splitk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-    "attn_prefill.hip": [],
+    "attn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "api.cpp": ["-x", "hip"],
     "validate.cpp": ["-x", "hip"],
 }

@@ -5,29 +5,35 @@
 // Hadamard-rotated Q4_0 V (816 B/cell)", How: one fused attention serves
 // decode, verify and prefill), row i attending cells [0, pos0 + i].
 //
-// Here Q.K^T and P.V are dense contractions (128 query rows share every K/V
+// Here Q.K^T and P.V are dense contractions (256 query rows share every K/V
 // tile), so both run on the matrix cores (v_mfma_f32_16x16x32_f16):
 //   * workgroup = 4 waves = 16 query positions x 8 GQA heads of one KV head
-//     (128 rows); each wave owns 32 rows (2 row tiles of 16);
+//     (128 rows), two workgroups per CU; each wave owns 32 rows (2 row
+//     tiles of 16);
 //   * per 32-cell tile the workgroup loads the raw pages once and
 //     dequantizes into LDS: K codes as exact fp16 (scales kept per cell and
 //     128-dim group, applied to the two half-dots), V as (code - 8) * d16 in
-//     fp16, stored transposed [dim][cell] so the P.V B-operand is two 8-byte
-//     reads;
+//     fp16, stored transposed [dim][cell] (two cells per 4-byte write) so the
+//     P.V B-operand is two 8-byte reads; while one workgroup loads a tile
+//     the other one on the CU computes;
 //   * S^T = K.Q^T keeps P in registers in the P.V A-operand layout; online
-//     softmax in base 2; causal mask only where the tile reaches the rows;
-//   * epilogue: O / l, then the inverse Walsh-Hadamard transform across the
-//     accumulator layout (dims 16j + n: 4 butterfly stages across lanes,
-//     4 across registers).
+//     softmax in base 2 against a lazily moved reference max; the causal
+//     mask only in the tiles that reach a wave's rows;
+//   * epilogue: O / l, then the inverse Walsh-Hadamard transform one row at
+//     a time through LDS (4 dims per lane).
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace k8v4 {
 
-constexpr int kPfPos = 16;           // query positions per workgroup
+constexpr int kPfWaves = 4;
+constexpr int kPfPos = 16;           // query positions per workgroup (x 8 heads = 128 rows)
 constexpr int kPfTile = 32;          // cells per tile
 constexpr int kKRow = 256 + 8;       // fp16 elements per K row in LDS (padded)
 constexpr int kVRow = kPfTile + 4;   // fp16 elements per transposed V row (72 bytes)
+constexpr int kVBlockPad = 32;      // fp16 elements after every 32 rows (one block)
+__device__ __forceinline__ int v_row(int d) { return d * kVRow + (d >> 5) * kVBlockPad; }
+constexpr float kPfLazy = 8.0f;      // log2 headroom of the lazy softmax reference
 
 struct PrefillArgs {
   const int8_t *kc;
@@ -38,22 +44,148 @@ struct PrefillArgs {
   float *out;
   int n_pages, P, H;
   int n_q_heads;
+  int p_shift;          // log2(P) when P is a power of two, else -1
   int pos0, n_new;
   float scale2;
 };
 
-template <bool QF32>
-__global__ __launch_bounds__(256) void attn_prefill_kernel(const PrefillArgs a) {
-  __shared__ _Float16 lds_k[kPfTile * kKRow];
-  __shared__ _Float16 lds_v[256 * kVRow];
-  __shared__ float lds_ks[kPfTile * 2];
+// (x & m) | c in one VALU op (the compiler splits it when both are literals)
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
+  return r;
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// raw pages of one tile, in the registers of the thread that dequantizes them
+struct PfRaw {
+  u32x4 k;       // 16 K codes: cell tid / 16, dims 16 (tid % 16) ..
+  float kd;      // K scale (threads < 64): cell tid / 2, group tid % 2
+  u32x2 va, vb;  // 8 nibble bytes of block b for cells 2cp, 2cp + 1
+  uint32_t vd;   // their fp16 scales (lo: cell 2cp, hi: cell 2cp + 1)
+};
+
+// Per tile: the physical (page, head) tile of each 16-cell half (P is a
+// multiple of 16 and tiles start at multiples of 32, so a half never
+// straddles a page) and the slot of its first cell; wave-uniform.
+struct PfHalves {
+  int tile[2];
+  int slot0[2];
+};
+
+__device__ __forceinline__ PfHalves pf_halves(const PrefillArgs &a, int g, int c0, int n_cells) {
+  PfHalves h;
+  for (int i = 0; i < 2; i++) {
+    const int c = c0 + 16 * i;
+    h.tile[i] = 0;
+    h.slot0[i] = 0;
+    if (c < n_cells) {  // page-table entries past the visible cells are never read
+      const int pidx = a.p_shift >= 0 ? (c >> a.p_shift) : c / a.P;
+      int page = a.pt[pidx];
+      page = (page < 0 || page >= a.n_pages) ? 0 : page;
+      h.tile[i] = page * a.H + g;
+      h.slot0[i] = c - pidx * a.P;
+    }
+  }
+  return h;
+}
+
+__device__ __forceinline__ void pf_load(const PrefillArgs &a, const PfHalves &hv, int c0, int n_cells, int u,
+                                        PfRaw &r) {
+  // work unit u in [0, 512): K codes of cell u / 16, dims 16 (u % 16) ..;
+  // K scale (u < 64) of cell u / 2, group u % 2; V bytes 8 (u / 256) .. of
+  // block (u / 16) % 8 of the cells 2 (u % 16), 2 (u % 16) + 1
+  {
+    const int cl = u >> 4, hf = cl >> 4;
+    r.k = u32x4{0u, 0u, 0u, 0u};
+    if (c0 + cl < n_cells)
+      r.k = *reinterpret_cast<const u32x4 *>(a.kc + ((size_t)hv.tile[hf] * a.P + hv.slot0[hf] + (cl & 15)) * 256 +
+                                             16 * (u & 15));
+  }
+  r.kd = 0.f;
+  if (u < 2 * kPfTile) {
+    const int cl = u >> 1, hf = cl >> 4;
+    if (c0 + cl < n_cells) r.kd = a.ks[((size_t)hv.tile[hf] * a.P + hv.slot0[hf] + (cl & 15)) * 2 + (u & 1)];
+  }
+  {
+    const int cp = u & 15, b = (u >> 4) & 7, qq = u >> 8;
+    const int hf = cp >> 3;  // cells 2cp, 2cp+1 lie in half cp / 8
+    const uint8_t *vt = a.vq + (size_t)hv.tile[hf] * 144 * a.P;
+    const int slot = hv.slot0[hf] + 2 * (cp & 7);
+    r.va = u32x2{0u, 0u};
+    r.vb = u32x2{0u, 0u};
+    r.vd = 0u;
+    if (c0 + 2 * cp < n_cells) {
+      r.va = *reinterpret_cast<const u32x2 *>(vt + (size_t)slot * 128 + 16 * b + 8 * qq);
+      r.vd = *reinterpret_cast<const uint16_t *>(vt + q4_scale_off(a.P, slot, b));
+    }
+    if (c0 + 2 * cp + 1 < n_cells) {
+      r.vb = *reinterpret_cast<const u32x2 *>(vt + (size_t)(slot + 1) * 128 + 16 * b + 8 * qq);
+      r.vd |= (uint32_t)*reinterpret_cast<const uint16_t *>(vt + q4_scale_off(a.P, slot + 1, b)) << 16;
+    }
+  }
+}
+
+__device__ __forceinline__ void pf_store(const PfRaw &r, int u, _Float16 *lk, _Float16 *lv, float *lks) {
+  const f16x2 c1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const f16x2 c1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const f16x2 c72 = {(_Float16)72.0f, (_Float16)72.0f};
+  {
+    // K -> exact fp16 codes, row-major [cell][dim]
+    uint32_t kf[8];
+    const uint32_t kw[4] = {r.k.x, r.k.y, r.k.z, r.k.w};
+    for (int i = 0; i < 4; i++) {
+      uint32_t lo, hi;
+      i8x4_to_f16_biased(kw[i], lo, hi);
+      kf[2 * i] = as_u32(as_f16x2(lo) - c1152);
+      kf[2 * i + 1] = as_u32(as_f16x2(hi) - c1152);
+    }
+    _Float16 *kd = lk + (u >> 4) * kKRow + 16 * (u & 15);
+    *reinterpret_cast<u32x4 *>(kd) = u32x4{kf[0], kf[1], kf[2], kf[3]};
+    *reinterpret_cast<u32x4 *>(kd + 8) = u32x4{kf[4], kf[5], kf[6], kf[7]};
+  }
+  if (u < 2 * kPfTile) lks[u] = r.kd;
+  {
+    // V -> (code - 8) * d16 in fp16, transposed [dim][cell]; byte i of the
+    // block holds element i (low nibble) and element 16 + i (high nibble)
+    const int cp = u & 15, b = (u >> 4) & 7, qq = u >> 8;
+    const f16x2 dd = as_f16x2(r.vd);
+    const uint32_t wa[2] = {r.va.x, r.va.y}, wb[2] = {r.vb.x, r.vb.y};
+    for (int w = 0; w < 2; w++) {
+      for (int e = 0; e < 4; e++) {
+        // [a.byte, 0, b.byte, 0] for byte e of word w of each cell
+        const uint32_t sel = (0x0cu << 24) | ((4u + e) << 16) | (0x0cu << 8) | (uint32_t)e;
+        const uint32_t x = perm(wb[w], wa[w], sel);
+        const int el = 8 * qq + 4 * w + e;  // element index within the low half
+        const uint32_t lo = as_u32((as_f16x2(and_or(x, 0x000F000Fu, 0x64006400u)) - c1032) * dd);
+        const uint32_t hi = as_u32((as_f16x2(and_or(x, 0x00F000F0u, 0x54005400u)) - c72) * dd);
+        *reinterpret_cast<uint32_t *>(lv + v_row(32 * b + el) + 2 * cp) = lo;
+        *reinterpret_cast<uint32_t *>(lv + v_row(32 * b + 16 + el) + 2 * cp) = hi;
+      }
+    }
+  }
+}
+
+template <bool QF32>
+__global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const PrefillArgs a) {
+  // K tile, then V tile, in one array that also holds the epilogue's
+  // per-wave row slices (kPfWaves x 16 rows x 256 fp32)
+  constexpr int kKElems = kPfTile * kKRow, kVElems = 256 * kVRow + 8 * kVBlockPad;
+  constexpr int kTileElems = kKElems + kVElems;
+  constexpr int kEpiElems = kPfWaves * 16 * 256 * 2;  // fp16 units
+  __shared__ __attribute__((aligned(16))) _Float16 lds_kv[kTileElems > kEpiElems ? kTileElems : kEpiElems];
+  __shared__ __attribute__((aligned(16))) float lds_ks[kPfTile * 2];
+  _Float16 *const lds_k = lds_kv;
+  _Float16 *const lds_v = lds_kv + kKElems;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, lg = lane >> 4;
   const int g = blockIdx.y;
   const int qb0 = blockIdx.x * kPfPos;                    // first query (chunk-relative)
   const int q_last = min(qb0 + kPfPos, a.n_new) - 1;      // last valid query of the block
   const int n_cells = a.pos0 + q_last + 1;                // cells any row of the block sees
+  // first cell at which this wave's rows need the causal mask
+  const int mask_from = a.pos0 + qb0 + 4 * wave;  // rows 32 wave .. +31: positions qb0 + 4 wave ..
 
   // ---- queries: B operand of S^T = K.Q^T; row r = 32*wave + 16*t + n,
   // position qb0 + r/8, head g*8 + r%8; k-step kk holds dims 32kk + 8lg..+7
@@ -97,169 +229,119 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const PrefillArgs a) 
   for (int t = 0; t < 2; t++)
     for (int j = 0; j < 16; j++) o[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const size_t q4_tile = (size_t)144 * a.P;
-  const f16x2 c1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
-  const f16x2 c1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
-
+  // raw pages of the next tile, loaded while the current one is computed
+  PfRaw raw[2];
+  {
+    const PfHalves hv = pf_halves(a, g, 0, n_cells);
+    for (int h = 0; h < 2; h++) pf_load(a, hv, 0, n_cells, tid + 256 * h, raw[h]);
+  }
   for (int c0 = 0; c0 < n_cells; c0 += kPfTile) {
-    // ---------------- cooperative load + dequant into LDS
-    {
-      // K codes: thread -> cell tid/8, 32 bytes at 32*(tid%8)
-      const int cl = tid >> 3, part = tid & 7;
-      const int cell = c0 + cl;
-      u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
-      float d0 = 0.f, d1 = 0.f;
-      uint32_t vd = 0;
-      u32x4 vw = {0u, 0u, 0u, 0u};
-      if (cell < n_cells) {
-        int page = a.pt[cell / a.P];
-        page = (page < 0 || page >= a.n_pages) ? 0 : page;
-        const int slot = cell % a.P;
-        const size_t tile = (size_t)page * a.H + g;
-        const int8_t *kp = a.kc + (tile * a.P + slot) * 256 + 32 * part;
-        w0 = *reinterpret_cast<const u32x4 *>(kp);
-        w1 = *reinterpret_cast<const u32x4 *>(kp + 16);
-        if (part < 2) {
-          const float *ksp = a.ks + (tile * a.P + slot) * 2;
-          d0 = ksp[part];
-        }
-        // V: block `part` of this cell: 16 nibble bytes + fp16 scale
-        const uint8_t *vt = a.vq + tile * q4_tile;
-        vw = *reinterpret_cast<const u32x4 *>(vt + (size_t)slot * 128 + 16 * part);
-        vd = *reinterpret_cast<const uint16_t *>(vt + q4_scale_off(a.P, slot, part));
-      }
-      (void)d1;
-      // K -> exact fp16 codes
-      uint32_t kf[16];
-      const uint32_t kw[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-      for (int i = 0; i < 8; i++) {
-        uint32_t lo, hi;
-        i8x4_to_f16_biased(kw[i], lo, hi);
-        kf[2 * i] = as_u32(as_f16x2(lo) - c1152);
-        kf[2 * i + 1] = as_u32(as_f16x2(hi) - c1152);
-      }
-      _Float16 *kd = lds_k + cl * kKRow + 32 * part;
-      for (int i = 0; i < 4; i++)
-        *reinterpret_cast<u32x4 *>(kd + 8 * i) = u32x4{kf[4 * i], kf[4 * i + 1], kf[4 * i + 2], kf[4 * i + 3]};
-      if (part < 2) lds_ks[cl * 2 + part] = d0;
-      // V -> (code - 8) * d16 as fp16, transposed to [dim][cell]
-      const f16x2 dd = as_f16x2(vd | (vd << 16));
-      const uint32_t vwa[4] = {vw.x, vw.y, vw.z, vw.w};
-      for (int i = 0; i < 4; i++) {
-        // byte 4i + e: element 4i + e (low nibble) and 16 + 4i + e (high)
-        const uint32_t x = vwa[i];
-        for (int e = 0; e < 4; e++) {
-          const uint32_t by = (x >> (8 * e)) & 0xffu;
-          const uint32_t pr = (by & 15u) | ((by >> 4) << 16) | 0x64006400u;
-          const f16x2 val = (as_f16x2(pr) - c1032) * dd;
-          const int el = 4 * i + e;
-          lds_v[(32 * part + el) * kVRow + cl] = val.x;
-          lds_v[(32 * part + 16 + el) * kVRow + cl] = val.y;
-        }
-      }
-    }
+    // ---------------- the tile's pages, dequantized into LDS (two work
+    // units per thread), then the next tile's loads issued
+    for (int h = 0; h < 2; h++) pf_store(raw[h], tid + 256 * h, lds_k, lds_v, lds_ks);
     __syncthreads();
+    if (c0 + kPfTile < n_cells) {
+      const PfHalves hv = pf_halves(a, g, c0 + kPfTile, n_cells);
+      for (int h = 0; h < 2; h++) pf_load(a, hv, c0 + kPfTile, n_cells, tid + 256 * h, raw[h]);
+    }
+    const _Float16 *lk = lds_k;
+    const _Float16 *lv = lds_v;
+    const float *lks = lds_ks;
+    const bool masked = c0 + kPfTile - 1 >= mask_from;
 
-    // ---------------- S^T = K . Q^T for 2 cell tiles x 2 row tiles
+    // ---------------- S^T = K . Q^T for 2 cell tiles x 2 row tiles (each K
+    // operand read once from LDS and used for both row tiles)
     float s[2][8];
     for (int ct = 0; ct < 2; ct++) {
-      f16x8 kop[8];
-      const _Float16 *kr = lds_k + (16 * ct + n) * kKRow + 8 * lg;
-      for (int kk = 0; kk < 8; kk++) kop[kk] = *reinterpret_cast<const f16x8 *>(kr + 32 * kk);
-      float dk[4][2];
-      for (int i = 0; i < 4; i++) {
-        dk[i][0] = lds_ks[(16 * ct + 4 * lg + i) * 2];
-        dk[i][1] = lds_ks[(16 * ct + 4 * lg + i) * 2 + 1];
+      const _Float16 *kr = lk + (16 * ct + n) * kKRow + 8 * lg;
+      f32x4 acc[2][2];
+      for (int t = 0; t < 2; t++) acc[t][0] = acc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kk = 0; kk < 8; kk++) {
+        const f16x8 kop = *reinterpret_cast<const f16x8 *>(kr + 32 * kk);
+        for (int t = 0; t < 2; t++) {
+          acc[t][kk >> 2] = mfma16x16x32(kop, qop[t][kk], acc[t][kk >> 2]);
+          if (QF32) acc[t][kk >> 2] = mfma16x16x32(kop, qlo[t][kk], acc[t][kk >> 2]);
+        }
+        if ((kk & 3) == 3) __builtin_amdgcn_sched_barrier(0);
       }
-      for (int t = 0; t < 2; t++) {
-        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-        for (int kk = 0; kk < 4; kk++) {
-          acc0 = mfma16x16x32(kop[kk], qop[t][kk], acc0);
-          if (QF32) acc0 = mfma16x16x32(kop[kk], qlo[t][kk], acc0);
-        }
-        for (int kk = 4; kk < 8; kk++) {
-          acc1 = mfma16x16x32(kop[kk], qop[t][kk], acc1);
-          if (QF32) acc1 = mfma16x16x32(kop[kk], qlo[t][kk], acc1);
-        }
-        for (int i = 0; i < 4; i++) {
-          const int cell = c0 + 16 * ct + 4 * lg + i;
-          float sv = a.scale2 * (dk[i][0] * acc0[i] + dk[i][1] * acc1[i]);
-          sv = (rvalid[t] && cell <= qpos[t]) ? sv : -INFINITY;
+      for (int i = 0; i < 4; i++) {
+        const float2 dk = *reinterpret_cast<const float2 *>(&lks[(16 * ct + 4 * lg + i) * 2]);
+        for (int t = 0; t < 2; t++) {
+          float sv = a.scale2 * (dk.x * acc[t][0][i] + dk.y * acc[t][1][i]);
+          if (masked) {
+            const int cell = c0 + 16 * ct + 4 * lg + i;
+            sv = (rvalid[t] && cell <= qpos[t]) ? sv : -INFINITY;
+          }
           s[t][4 * ct + i] = sv;
         }
       }
     }
 
-    // ---------------- online softmax, P operand
+    // ---------------- online softmax, P operand; the reference max moves
+    // only when a row's max exceeds it by more than 2^kPfLazy
     f16x8 pop[2];
     for (int t = 0; t < 2; t++) {
       float mx = s[t][0];
       for (int e = 1; e < 8; e++) mx = fmaxf(mx, s[t][e]);
       mx = fmaxf(mx, lane_xor(mx, 16));
       mx = fmaxf(mx, lane_xor(mx, 32));
-      const float mnew = fmaxf(m[t], mx);
-      const float alpha = exp2f(m[t] - mnew);
+      if (__any(mx > m[t] + kPfLazy)) {
+        const float mnew = fmaxf(m[t], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m[t] - mnew);
+        lsum[t] *= alpha;
+        m[t] = mnew;
+        float al[4];
+        for (int i = 0; i < 4; i++) al[i] = lane_get(alpha, 4 * lg + i);
+        for (int j = 0; j < 16; j++)
+          for (int i = 0; i < 4; i++) o[t][j][i] *= al[i];
+      }
       float ps = 0.f;
       for (int e = 0; e < 8; e++) {
-        const float p = exp2f(s[t][e] - mnew);
+        const float p = __builtin_amdgcn_exp2f(s[t][e] - m[t]);
         ps += p;
         pop[t][e] = (_Float16)p;
       }
-      lsum[t] = lsum[t] * alpha + ps;
-      m[t] = mnew;
-      float al[4];
-      for (int i = 0; i < 4; i++) al[i] = lane_get(alpha, 4 * lg + i);
-      for (int j = 0; j < 16; j++)
-        for (int i = 0; i < 4; i++) o[t][j][i] *= al[i];
+      lsum[t] += ps;
     }
 
     // ---------------- O += P . V; B for dim tile j, column n: dim 16j + n,
     // k-slots = cells 4lg + 0..3 and 16 + 4lg + 0..3
     for (int j = 0; j < 16; j++) {
-      const _Float16 *vr = lds_v + (16 * j + n) * kVRow + 4 * lg;
+      const _Float16 *vr = lv + v_row(16 * j + n) + 4 * lg;
       const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr);
       const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 16);
       const f16x8 B = __builtin_bit_cast(f16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
       for (int t = 0; t < 2; t++) o[t][j] = mfma16x16x32(pop[t], B, o[t][j]);
+      // keep at most four tiles' operands in flight (register budget)
+      if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
+
+    __syncthreads();  // the tile's LDS is free for the next one
   }
 
-  // ---------------- epilogue: normalize, inverse Walsh-Hadamard, store
+  // ---------------- epilogue: normalize, then the inverse Walsh-Hadamard
+  // transform row by row through LDS (this wave's 16 x 256 fp32 slice of
+  // the tile buffers, free after the last barrier), and store
+  float *ws = reinterpret_cast<float *>(lds_kv);  // [kPfWaves][16][256] fp32
+  float *wrow = ws + wave * 16 * 256;
   for (int t = 0; t < 2; t++) {
     lsum[t] += lane_xor(lsum[t], 16);
     lsum[t] += lane_xor(lsum[t], 32);
     float inv[4];
     for (int i = 0; i < 4; i++) inv[i] = 1.0f / lane_get(lsum[t], 4 * lg + i);
     // value (row 4lg + i, dim 16j + n) lives in o[t][j][i]
-    float y[16][4];
     for (int j = 0; j < 16; j++)
-      for (int i = 0; i < 4; i++) y[j][i] = o[t][j][i] * inv[i];
-    // dim bits 0..3 = lane bits 0..3 (n): butterflies across lanes
-    for (int mbit = 1; mbit < 16; mbit <<= 1) {
-      const bool upper = (n & mbit) != 0;
-      for (int j = 0; j < 16; j++)
-        for (int i = 0; i < 4; i++) {
-          const float p = lane_xor(y[j][i], mbit);
-          y[j][i] = upper ? (p - y[j][i]) : (y[j][i] + p);
-        }
-    }
-    // dim bits 4..7 = tile index j: butterflies across registers
-    for (int jb = 1; jb < 16; jb <<= 1)
-      for (int j = 0; j < 16; j++) {
-        if (j & jb) continue;
-        for (int i = 0; i < 4; i++) {
-          const float x0 = y[j][i], x1 = y[j + jb][i];
-          y[j][i] = x0 + x1;
-          y[j + jb][i] = x0 - x1;
-        }
-      }
-    for (int i = 0; i < 4; i++) {
-      const int r = 32 * wave + 16 * t + 4 * lg + i;
+      for (int i = 0; i < 4; i++) wrow[(4 * lg + i) * 256 + 16 * j + n] = o[t][j][i] * inv[i];
+    for (int rr = 0; rr < 16; rr++) {
+      const int r = 32 * wave + 16 * t + rr;
       const int qi = qb0 + (r >> 3);
-      if (qi > q_last) continue;
-      float *op = a.out + ((size_t)qi * a.n_q_heads + (size_t)g * kGqa + (r & 7)) * 256;
-      for (int j = 0; j < 16; j++) op[16 * j + n] = y[j][i] * 0.0625f;
+      f32x4 y4 = *reinterpret_cast<const f32x4 *>(&wrow[rr * 256 + 4 * lane]);
+      float y[4] = {y4[0], y4[1], y4[2], y4[3]};
+      fwht256_lane4(y, lane);
+      if (qi <= q_last) {
+        float *op = a.out + ((size_t)qi * a.n_q_heads + (size_t)g * kGqa + (r & 7)) * 256 + 4 * lane;
+        *reinterpret_cast<f32x4 *>(op) = f32x4{y[0], y[1], y[2], y[3]};
+      }
     }
   }
 }
@@ -277,15 +359,18 @@ int launch_attn_prefill(const kv_pool *pool, const kv_seq *seq, const void *q, i
   a.n_pages = pool->n_pages;
   a.P = pool->page_size;
   a.H = pool->n_kv_heads;
+  a.p_shift = -1;
+  for (int sh = 0; sh < 31; sh++)
+    if ((1 << sh) == a.P) a.p_shift = sh;
   a.n_q_heads = n_q_heads;
   a.pos0 = pos0;
   a.n_new = n_new;
   a.scale2 = scale * 1.4426950408889634f;
   dim3 grid((n_new + kPfPos - 1) / kPfPos, a.H);
   if (q_dtype == KV_DTYPE_F32)
-    launch(attn_prefill_kernel<true>, grid, dim3(256), s, a);
+    launch(attn_prefill_kernel<true>, grid, dim3(kPfWaves * 64), s, a);
   else
-    launch(attn_prefill_kernel<false>, grid, dim3(256), s, a);
+    launch(attn_prefill_kernel<false>, grid, dim3(kPfWaves * 64), s, a);
   return launch_status();
 }
 

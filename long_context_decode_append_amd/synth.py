@@ -116,13 +116,19 @@ def seed_of(seed: int, layer: int, chunk: int) -> int:
 
 
 def kv_chunk_device(seed: int, layer: int, chunk: int, n: int, n_kv_heads: int, head_dim: int,
-                    device, dtype=None):
+                    device, dtype=None, outliers=None, outlier_scale: float = 8.0):
+    """outliers: optional [n_kv_heads][k] channel indices scaled on K and V."""
     import torch
     dtype = dtype or torch.float16
     gen = torch.Generator(device=device)
     gen.manual_seed(seed_of(seed, layer, chunk))
     k = torch.randn((n, n_kv_heads, head_dim), generator=gen, device=device, dtype=torch.float32)
     v = torch.randn((n, n_kv_heads, head_dim), generator=gen, device=device, dtype=torch.float32)
+    if outliers is not None:
+        for g in range(n_kv_heads):
+            ch = torch.as_tensor(outliers[g], device=device)
+            k[:, g, ch] *= outlier_scale
+            v[:, g, ch] *= outlier_scale
     return k.to(dtype), v.to(dtype)
 
 
