@@ -24,15 +24,34 @@
 #include "device.hpp"
 #include "launch.hpp"
 
+#ifndef PF_WAVES
+#define PF_WAVES 8
+#endif
+#ifndef PF_ROWT
+#define PF_ROWT 1
+#endif
+#ifndef PF_STAGGER
+#define PF_STAGGER 1
+#endif
+#ifndef PF_SB
+#define PF_SB 1
+#endif
+#ifndef PF_OCC
+#define PF_OCC 1
+#endif
+
 namespace k8v4 {
 
-constexpr int kPfWaves = 4;
-constexpr int kPfPos = 16;           // query positions per workgroup (x 8 heads = 128 rows)
+constexpr int kPfWaves = PF_WAVES;
+constexpr int kRowT = PF_ROWT;       // 16-row tiles per wave
+constexpr int kPfPos = kPfWaves * 16 * kRowT / 8;  // query positions per workgroup (x 8 heads)
+constexpr int kUnits = 512 / (kPfWaves * 64);      // tile load units per thread
 constexpr int kPfTile = 32;          // cells per tile
 constexpr int kKRow = 256 + 8;       // fp16 elements per K row in LDS (padded)
 constexpr int kVRow = kPfTile + 4;   // fp16 elements per transposed V row (72 bytes)
 constexpr int kVBlockPad = 32;      // fp16 elements after every 32 rows (one block)
-__device__ __forceinline__ int v_row(int d) { return d * kVRow + (d >> 5) * kVBlockPad; }
+// offset of dim d0 + d (d0 a multiple of 32, 0 <= d < 32) in the V tile
+__device__ __forceinline__ int v_row(int d0, int d) { return (d0 + d) * kVRow + (d0 >> 5) * kVBlockPad; }
 constexpr float kPfLazy = 8.0f;      // log2 headroom of the lazy softmax reference
 
 struct PrefillArgs {
@@ -60,7 +79,7 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
 struct PfRaw {
   u32x4 k;       // 16 K codes: cell tid / 16, dims 16 (tid % 16) ..
   float kd;      // K scale (threads < 64): cell tid / 2, group tid % 2
-  u32x2 va, vb;  // 8 nibble bytes of block b for cells 2cp, 2cp + 1
+  uint32_t va, vb;  // 4 nibble bytes of block b for cells 2cp, 2cp + 1
   uint32_t vd;   // their fp16 scales (lo: cell 2cp, hi: cell 2cp + 1)
 };
 
@@ -70,10 +89,18 @@ struct PfRaw {
 struct PfHalves {
   int tile[2];
   int slot0[2];
+  // first cell of half hf in the pool's cell order (a select: hf varies by lane)
+  __device__ __forceinline__ size_t cell(int hf) const {
+    return hf ? (size_t)tile[1] * P + slot0[1] : (size_t)tile[0] * P + slot0[0];
+  }
+  __device__ __forceinline__ int tile_of(int hf) const { return hf ? tile[1] : tile[0]; }
+  __device__ __forceinline__ int slot_of(int hf) const { return hf ? slot0[1] : slot0[0]; }
+  int P;
 };
 
 __device__ __forceinline__ PfHalves pf_halves(const PrefillArgs &a, int g, int c0, int n_cells) {
   PfHalves h;
+  h.P = a.P;
   for (int i = 0; i < 2; i++) {
     const int c = c0 + 16 * i;
     h.tile[i] = 0;
@@ -92,34 +119,33 @@ __device__ __forceinline__ PfHalves pf_halves(const PrefillArgs &a, int g, int c
 __device__ __forceinline__ void pf_load(const PrefillArgs &a, const PfHalves &hv, int c0, int n_cells, int u,
                                         PfRaw &r) {
   // work unit u in [0, 512): K codes of cell u / 16, dims 16 (u % 16) ..;
-  // K scale (u < 64) of cell u / 2, group u % 2; V bytes 8 (u / 256) .. of
-  // block (u / 16) % 8 of the cells 2 (u % 16), 2 (u % 16) + 1
+  // K scale (u < 64) of cell u / 2, group u % 2; V bytes 4 (u / 128) ..
+  // 4 (u / 128) + 3 of block (u / 16) % 8 of the cells 2 (u % 16), 2 (u % 16) + 1
   {
     const int cl = u >> 4, hf = cl >> 4;
     r.k = u32x4{0u, 0u, 0u, 0u};
     if (c0 + cl < n_cells)
-      r.k = *reinterpret_cast<const u32x4 *>(a.kc + ((size_t)hv.tile[hf] * a.P + hv.slot0[hf] + (cl & 15)) * 256 +
-                                             16 * (u & 15));
+      r.k = *reinterpret_cast<const u32x4 *>(a.kc + (hv.cell(hf) + (cl & 15)) * 256 + 16 * (u & 15));
   }
   r.kd = 0.f;
   if (u < 2 * kPfTile) {
     const int cl = u >> 1, hf = cl >> 4;
-    if (c0 + cl < n_cells) r.kd = a.ks[((size_t)hv.tile[hf] * a.P + hv.slot0[hf] + (cl & 15)) * 2 + (u & 1)];
+    if (c0 + cl < n_cells) r.kd = a.scale2 * a.ks[(hv.cell(hf) + (cl & 15)) * 2 + (u & 1)];
   }
   {
-    const int cp = u & 15, b = (u >> 4) & 7, qq = u >> 8;
+    const int cp = u & 15, b = (u >> 4) & 7, qq = u >> 7;
     const int hf = cp >> 3;  // cells 2cp, 2cp+1 lie in half cp / 8
-    const uint8_t *vt = a.vq + (size_t)hv.tile[hf] * 144 * a.P;
-    const int slot = hv.slot0[hf] + 2 * (cp & 7);
-    r.va = u32x2{0u, 0u};
-    r.vb = u32x2{0u, 0u};
+    const uint8_t *vt = a.vq + (size_t)hv.tile_of(hf) * 144 * a.P;
+    const int slot = hv.slot_of(hf) + 2 * (cp & 7);
+    r.va = 0u;
+    r.vb = 0u;
     r.vd = 0u;
     if (c0 + 2 * cp < n_cells) {
-      r.va = *reinterpret_cast<const u32x2 *>(vt + (size_t)slot * 128 + 16 * b + 8 * qq);
+      r.va = *reinterpret_cast<const uint32_t *>(vt + (size_t)slot * 128 + 16 * b + 4 * qq);
       r.vd = *reinterpret_cast<const uint16_t *>(vt + q4_scale_off(a.P, slot, b));
     }
     if (c0 + 2 * cp + 1 < n_cells) {
-      r.vb = *reinterpret_cast<const u32x2 *>(vt + (size_t)(slot + 1) * 128 + 16 * b + 8 * qq);
+      r.vb = *reinterpret_cast<const uint32_t *>(vt + (size_t)(slot + 1) * 128 + 16 * b + 4 * qq);
       r.vd |= (uint32_t)*reinterpret_cast<const uint16_t *>(vt + q4_scale_off(a.P, slot + 1, b)) << 16;
     }
   }
@@ -143,37 +169,36 @@ __device__ __forceinline__ void pf_store(const PfRaw &r, int u, _Float16 *lk, _F
     *reinterpret_cast<u32x4 *>(kd) = u32x4{kf[0], kf[1], kf[2], kf[3]};
     *reinterpret_cast<u32x4 *>(kd + 8) = u32x4{kf[4], kf[5], kf[6], kf[7]};
   }
-  if (u < 2 * kPfTile) lks[u] = r.kd;
+  if (u < 2 * kPfTile) lks[u] = r.kd;  // already times scale * log2(e)
   {
     // V -> (code - 8) * d16 in fp16, transposed [dim][cell]; byte i of the
     // block holds element i (low nibble) and element 16 + i (high nibble)
-    const int cp = u & 15, b = (u >> 4) & 7, qq = u >> 8;
+    const int cp = u & 15, b = (u >> 4) & 7, qq = u >> 7;
     const f16x2 dd = as_f16x2(r.vd);
-    const uint32_t wa[2] = {r.va.x, r.va.y}, wb[2] = {r.vb.x, r.vb.y};
-    for (int w = 0; w < 2; w++) {
-      for (int e = 0; e < 4; e++) {
-        // [a.byte, 0, b.byte, 0] for byte e of word w of each cell
-        const uint32_t sel = (0x0cu << 24) | ((4u + e) << 16) | (0x0cu << 8) | (uint32_t)e;
-        const uint32_t x = perm(wb[w], wa[w], sel);
-        const int el = 8 * qq + 4 * w + e;  // element index within the low half
-        const uint32_t lo = as_u32((as_f16x2(and_or(x, 0x000F000Fu, 0x64006400u)) - c1032) * dd);
-        const uint32_t hi = as_u32((as_f16x2(and_or(x, 0x00F000F0u, 0x54005400u)) - c72) * dd);
-        *reinterpret_cast<uint32_t *>(lv + v_row(32 * b + el) + 2 * cp) = lo;
-        *reinterpret_cast<uint32_t *>(lv + v_row(32 * b + 16 + el) + 2 * cp) = hi;
-      }
+    _Float16 *vb = lv + v_row(32 * b, 4 * qq) + 2 * cp;  // element 4qq of block b
+    for (int e = 0; e < 4; e++) {
+      // [a.byte, 0, b.byte, 0] for byte e of each cell: elements 4qq + e
+      // (low nibbles) and 16 + 4qq + e (high nibbles)
+      const uint32_t sel = (0x0cu << 24) | ((4u + e) << 16) | (0x0cu << 8) | (uint32_t)e;
+      const uint32_t x = perm(r.vb, r.va, sel);
+      const uint32_t lo = as_u32((as_f16x2(and_or(x, 0x000F000Fu, 0x64006400u)) - c1032) * dd);
+      const uint32_t hi = as_u32((as_f16x2(and_or(x, 0x00F000F0u, 0x54005400u)) - c72) * dd);
+      *reinterpret_cast<uint32_t *>(vb + e * kVRow) = lo;
+      *reinterpret_cast<uint32_t *>(vb + (16 + e) * kVRow) = hi;
     }
   }
 }
 
 template <bool QF32>
-__global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(kPfWaves * 64, PF_OCC) void attn_prefill_kernel(const PrefillArgs a) {
   // K tile, then V tile, in one array that also holds the epilogue's
   // per-wave row slices (kPfWaves x 16 rows x 256 fp32)
   constexpr int kKElems = kPfTile * kKRow, kVElems = 256 * kVRow + 8 * kVBlockPad;
-  constexpr int kTileElems = kKElems + kVElems;
+  constexpr int kBufElems = kKElems + kVElems;  // one buffer: K tile, then V tile
+  constexpr int kTileElems = 2 * kBufElems;
   constexpr int kEpiElems = kPfWaves * 16 * 256 * 2;  // fp16 units
   __shared__ __attribute__((aligned(16))) _Float16 lds_kv[kTileElems > kEpiElems ? kTileElems : kEpiElems];
-  __shared__ __attribute__((aligned(16))) float lds_ks[kPfTile * 2];
+  __shared__ __attribute__((aligned(16))) float lds_ks[2 * kPfTile * 2];
   _Float16 *const lds_k = lds_kv;
   _Float16 *const lds_v = lds_kv + kKElems;
 
@@ -185,16 +210,16 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
   const int q_last = min(qb0 + kPfPos, a.n_new) - 1;      // last valid query of the block
   const int n_cells = a.pos0 + q_last + 1;                // cells any row of the block sees
   // first cell at which this wave's rows need the causal mask
-  const int mask_from = a.pos0 + qb0 + 4 * wave;  // rows 32 wave .. +31: positions qb0 + 4 wave ..
+  const int mask_from = a.pos0 + qb0 + 2 * kRowT * wave;  // first position of the wave's rows
 
   // ---- queries: B operand of S^T = K.Q^T; row r = 32*wave + 16*t + n,
   // position qb0 + r/8, head g*8 + r%8; k-step kk holds dims 32kk + 8lg..+7
-  f16x8 qop[2][8];
-  f16x8 qlo[QF32 ? 2 : 1][QF32 ? 8 : 1];
-  int qpos[2];
-  bool rvalid[2];
-  for (int t = 0; t < 2; t++) {
-    const int r = 32 * wave + 16 * t + n;
+  f16x8 qop[kRowT][8];
+  f16x8 qlo[QF32 ? kRowT : 1][QF32 ? 8 : 1];
+  int qpos[kRowT];
+  bool rvalid[kRowT];
+  for (int t = 0; t < kRowT; t++) {
+    const int r = 16 * kRowT * wave + 16 * t + n;
     const int qi = qb0 + (r >> 3);
     rvalid[t] = qi <= q_last;
     qpos[t] = a.pos0 + qi;
@@ -224,50 +249,48 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
     }
   }
 
-  float m[2] = {-1e30f, -1e30f}, lsum[2] = {0.f, 0.f};
-  f32x4 o[2][16];
-  for (int t = 0; t < 2; t++)
+  float m[kRowT], lsum[kRowT];
+  f32x4 o[kRowT][16];
+  for (int t = 0; t < kRowT; t++) m[t] = -1e30f, lsum[t] = 0.f;
+  for (int t = 0; t < kRowT; t++)
     for (int j = 0; j < 16; j++) o[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // raw pages of the next tile, loaded while the current one is computed
-  PfRaw raw[2];
-  {
-    const PfHalves hv = pf_halves(a, g, 0, n_cells);
-    for (int h = 0; h < 2; h++) pf_load(a, hv, 0, n_cells, tid + 256 * h, raw[h]);
-  }
-  for (int c0 = 0; c0 < n_cells; c0 += kPfTile) {
-    // ---------------- the tile's pages, dequantized into LDS (two work
-    // units per thread), then the next tile's loads issued
-    for (int h = 0; h < 2; h++) pf_store(raw[h], tid + 256 * h, lds_k, lds_v, lds_ks);
-    __syncthreads();
-    if (c0 + kPfTile < n_cells) {
-      const PfHalves hv = pf_halves(a, g, c0 + kPfTile, n_cells);
-      for (int h = 0; h < 2; h++) pf_load(a, hv, c0 + kPfTile, n_cells, tid + 256 * h, raw[h]);
-    }
-    const _Float16 *lk = lds_k;
-    const _Float16 *lv = lds_v;
-    const float *lks = lds_ks;
+  // Two LDS tile buffers: while tile i is computed from one, tile i + 1 is
+  // dequantized into the other from registers loaded during tile i - 1.
+  // The waves sharing a SIMD (w, w + 4) do the two halves in opposite
+  // order, so one's dequantization overlaps the other's MFMAs.
+  PfRaw raw[kUnits];
+  auto load_tile = [&](int c) {
+    const PfHalves hv = pf_halves(a, g, c, n_cells);
+    for (int h = 0; h < kUnits; h++) pf_load(a, hv, c, n_cells, tid + 64 * kPfWaves * h, raw[h]);
+  };
+  auto store_tile = [&](int buf) {
+    for (int h = 0; h < kUnits; h++)
+      pf_store(raw[h], tid + 64 * kPfWaves * h, lds_k + buf * kBufElems, lds_v + buf * kBufElems,
+               lds_ks + buf * 2 * kPfTile);
+  };
+  auto compute_tile = [&](int c0, const _Float16 *lk, const _Float16 *lv, const float *lks) {
     const bool masked = c0 + kPfTile - 1 >= mask_from;
 
     // ---------------- S^T = K . Q^T for 2 cell tiles x 2 row tiles (each K
     // operand read once from LDS and used for both row tiles)
-    float s[2][8];
+    float s[kRowT][8];
     for (int ct = 0; ct < 2; ct++) {
       const _Float16 *kr = lk + (16 * ct + n) * kKRow + 8 * lg;
-      f32x4 acc[2][2];
-      for (int t = 0; t < 2; t++) acc[t][0] = acc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 acc[kRowT][2];
+      for (int t = 0; t < kRowT; t++) acc[t][0] = acc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
       for (int kk = 0; kk < 8; kk++) {
         const f16x8 kop = *reinterpret_cast<const f16x8 *>(kr + 32 * kk);
-        for (int t = 0; t < 2; t++) {
+        for (int t = 0; t < kRowT; t++) {
           acc[t][kk >> 2] = mfma16x16x32(kop, qop[t][kk], acc[t][kk >> 2]);
           if (QF32) acc[t][kk >> 2] = mfma16x16x32(kop, qlo[t][kk], acc[t][kk >> 2]);
         }
-        if ((kk & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        if (PF_SB && (kk & 3) == 3) __builtin_amdgcn_sched_barrier(0);
       }
       for (int i = 0; i < 4; i++) {
         const float2 dk = *reinterpret_cast<const float2 *>(&lks[(16 * ct + 4 * lg + i) * 2]);
-        for (int t = 0; t < 2; t++) {
-          float sv = a.scale2 * (dk.x * acc[t][0][i] + dk.y * acc[t][1][i]);
+        for (int t = 0; t < kRowT; t++) {
+          float sv = dk.x * acc[t][0][i] + dk.y * acc[t][1][i];
           if (masked) {
             const int cell = c0 + 16 * ct + 4 * lg + i;
             sv = (rvalid[t] && cell <= qpos[t]) ? sv : -INFINITY;
@@ -279,8 +302,8 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
 
     // ---------------- online softmax, P operand; the reference max moves
     // only when a row's max exceeds it by more than 2^kPfLazy
-    f16x8 pop[2];
-    for (int t = 0; t < 2; t++) {
+    f16x8 pop[kRowT];
+    for (int t = 0; t < kRowT; t++) {
       float mx = s[t][0];
       for (int e = 1; e < 8; e++) mx = fmaxf(mx, s[t][e]);
       mx = fmaxf(mx, lane_xor(mx, 16));
@@ -307,16 +330,33 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
     // ---------------- O += P . V; B for dim tile j, column n: dim 16j + n,
     // k-slots = cells 4lg + 0..3 and 16 + 4lg + 0..3
     for (int j = 0; j < 16; j++) {
-      const _Float16 *vr = lv + v_row(16 * j + n) + 4 * lg;
+      const _Float16 *vr = lv + v_row(32 * (j >> 1), 16 * (j & 1) + n) + 4 * lg;
       const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr);
       const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 16);
       const f16x8 B = __builtin_bit_cast(f16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-      for (int t = 0; t < 2; t++) o[t][j] = mfma16x16x32(pop[t], B, o[t][j]);
+      for (int t = 0; t < kRowT; t++) o[t][j] = mfma16x16x32(pop[t], B, o[t][j]);
       // keep at most four tiles' operands in flight (register budget)
-      if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      if (PF_SB && (j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
-
-    __syncthreads();  // the tile's LDS is free for the next one
+  };
+  load_tile(0);
+  store_tile(0);
+  load_tile(kPfTile);
+  __syncthreads();
+  const bool store_first = PF_STAGGER ? (wave & 4) == 0 : true;
+  int buf = 0;
+  for (int c0 = 0; c0 < n_cells; c0 += kPfTile, buf ^= 1) {
+    // tiles past the visible cells load nothing and store zeros (unread)
+    if (store_first) {
+      store_tile(buf ^ 1);
+      load_tile(c0 + 2 * kPfTile);
+    }
+    compute_tile(c0, lds_k + buf * kBufElems, lds_v + buf * kBufElems, lds_ks + buf * 2 * kPfTile);
+    if (!store_first) {
+      store_tile(buf ^ 1);
+      load_tile(c0 + 2 * kPfTile);
+    }
+    __syncthreads();
   }
 
   // ---------------- epilogue: normalize, then the inverse Walsh-Hadamard
@@ -324,7 +364,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
   // the tile buffers, free after the last barrier), and store
   float *ws = reinterpret_cast<float *>(lds_kv);  // [kPfWaves][16][256] fp32
   float *wrow = ws + wave * 16 * 256;
-  for (int t = 0; t < 2; t++) {
+  for (int t = 0; t < kRowT; t++) {
     lsum[t] += lane_xor(lsum[t], 16);
     lsum[t] += lane_xor(lsum[t], 32);
     float inv[4];
@@ -333,7 +373,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
     for (int j = 0; j < 16; j++)
       for (int i = 0; i < 4; i++) wrow[(4 * lg + i) * 256 + 16 * j + n] = o[t][j][i] * inv[i];
     for (int rr = 0; rr < 16; rr++) {
-      const int r = 32 * wave + 16 * t + rr;
+      const int r = 16 * kRowT * wave + 16 * t + rr;
       const int qi = qb0 + (r >> 3);
       f32x4 y4 = *reinterpret_cast<const f32x4 *>(&wrow[rr * 256 + 4 * lane]);
       float y[4] = {y4[0], y4[1], y4[2], y4[3]};
