@@ -140,14 +140,15 @@ __device__ __forceinline__ void pf_load(const PrefillArgs &a, const PfHalves &hv
     r.va = 0u;
     r.vb = 0u;
     r.vd = 0u;
+    // slot is even, so the two cells' block-b scales are one aligned word
     if (c0 + 2 * cp < n_cells) {
       r.va = *reinterpret_cast<const uint32_t *>(vt + (size_t)slot * 128 + 16 * b + 4 * qq);
-      r.vd = *reinterpret_cast<const uint16_t *>(vt + q4_scale_off(a.P, slot, b));
+      r.vd = *reinterpret_cast<const uint32_t *>(vt + q4_scale_off(a.P, slot, b));
     }
-    if (c0 + 2 * cp + 1 < n_cells) {
+    if (c0 + 2 * cp + 1 < n_cells)
       r.vb = *reinterpret_cast<const uint32_t *>(vt + (size_t)(slot + 1) * 128 + 16 * b + 4 * qq);
-      r.vd |= (uint32_t)*reinterpret_cast<const uint16_t *>(vt + q4_scale_off(a.P, slot + 1, b)) << 16;
-    }
+    else
+      r.vd &= 0xFFFFu;  // the unwritten slot's scale may be anything
   }
 }
 

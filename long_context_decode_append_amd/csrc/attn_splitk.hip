@@ -102,6 +102,12 @@ struct Half {
   int vd_soff;    // V scales (the q4_0 scale group, or fp32 pairs)
 };
 
+// page-table entry i through the constant address space: a scalar load
+// (the table is never written while a kernel reads it)
+__device__ __forceinline__ int pt_entry(const SplitArgs &a, int i) {
+  return ((const __attribute__((address_space(4))) int32_t *)a.pt)[i];
+}
+
 __device__ __forceinline__ int page_of(const SplitArgs &a, int pos) {
   return a.p_shift >= 0 ? (pos >> a.p_shift) : pos / a.P;
 }
@@ -137,10 +143,30 @@ __device__ __forceinline__ Half make_half(const SplitArgs &a, int g, int pos, in
 template <int FMT>
 __device__ __forceinline__ void step_halves(const SplitArgs &a, int g, int c, int c_end, Half &h0, Half &h1) {
   const int p1pos = (c + 16 < c_end) ? c + 16 : c;
-  const int pg0 = a.pt[page_of(a, c)];
-  const int pg1 = a.pt[page_of(a, p1pos)];
+  const int pg0 = pt_entry(a, page_of(a, c));
+  const int pg1 = pt_entry(a, page_of(a, p1pos));
   h0 = make_half<FMT>(a, g, c, pg0);
   h1 = make_half<FMT>(a, g, p1pos, pg1);
+}
+
+// The halves of the first two steps of a wave (at c0 and c1): the four
+// page-table entries are read together, so the kernel start waits for one
+// scalar round trip instead of two.
+template <int FMT>
+__device__ __forceinline__ void first_halves(const SplitArgs &a, int g, int c0, int c1, int c_end, Half &h0, Half &h1,
+                                             Half &n0, Half &n1) {
+  const int pos[4] = {c0, (c0 + 16 < c_end) ? c0 + 16 : c0, c1, (c1 + 16 < c_end) ? c1 + 16 : c1};
+  int pidx[4], pg[4];
+  if (a.p_shift >= 0) {
+    for (int i = 0; i < 4; i++) pidx[i] = pos[i] >> a.p_shift;
+  } else {
+    for (int i = 0; i < 4; i++) pidx[i] = pos[i] / a.P;
+  }
+  for (int i = 0; i < 4; i++) pg[i] = pt_entry(a, pidx[i]);
+  h0 = make_half<FMT>(a, g, pos[0], pg[0]);
+  h1 = make_half<FMT>(a, g, pos[1], pg[1]);
+  n0 = make_half<FMT>(a, g, pos[2], pg[2]);
+  n1 = make_half<FMT>(a, g, pos[3], pg[3]);
 }
 
 // k-slot order inside an 8-dim q4_0 K operand: the nibble unpack yields the
@@ -155,6 +181,9 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
   constexpr bool kInt8K = FMT != KV_FMT_Q4_0;   // K as INT8 codes (else rotated q4_0)
   constexpr bool kQ4V = FMT != KV_FMT_INT8;     // V as rotated q4_0 (else INT8 codes)
 
+  // one field from each 64-byte line of the argument block, so all four
+  // lines are fetched in one scalar round trip rather than one after another
+  asm volatile("" ::"s"(a.kc), "s"(a.n_pages), "s"(a.limits[4]), "s"(a.steps_per_split));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, lg = lane >> 4;
@@ -224,8 +253,36 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
       vsr[h2][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs, vd_voff + 16, h.vd_soff, 0));
     }
   };
-  if (has_work) {
-    step_halves<FMT>(a, g, c_first, c_end, cur0, cur1);
+  // the query loads go first: they depend only on the kernel arguments, so
+  // their latency overlaps the page-table round trip of the first K/V loads
+  const int row = row_base + n;
+  const bool row_ok = n < rows_here;
+  int lim_row = a.limits[0];  // selects over the argument array keep it in scalar loads
+  for (int i = 1; i < kMaxQ; i++) lim_row = ((row >> 3) == i) ? a.limits[i] : lim_row;
+  const int lim_eff = min(row_ok ? lim_row : 0, c_end);
+  u32x4 qraw[QF32 ? 16 : 8];
+  {
+    // padding rows read row_base's query (always present) and are zeroed
+    // after the loads, which keeps the loads free of branches (so waiting
+    // for them does not also wait for the K/V loads issued later)
+    const int rr = row_ok ? row : row_base;
+    const int qi = rr >> 3, hl = rr & 7;
+    const size_t qbase = ((size_t)qi * a.n_q_heads + (size_t)g * kGqa + hl) * 256;
+    for (int kk = 0; kk < 8; kk++) {
+      const int d0 = 64 * (kk >> 1) + 16 * lg + 8 * (kk & 1);
+      if (!QF32) {
+        qraw[kk] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.q) + qbase + d0);
+      } else {
+        qraw[2 * kk] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const float *>(a.q) + qbase + d0);
+        qraw[2 * kk + 1] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const float *>(a.q) + qbase + d0 + 4);
+      }
+    }
+  }
+  {
+    // unconditional (a wave without work loads cell 0's step and never uses
+    // it), so no control-flow join makes the compiler over-wait below
+    const int cf = has_work ? c_first : 0, ce = has_work ? c_end : 16;
+    first_halves<FMT>(a, g, cf, has_work ? min(c_first + stride, c_last) : 0, ce, cur0, cur1, nxt0, nxt1);
     const Half *hs[2] = {&cur0, &cur1};
     for (int h2 = 0; h2 < 2; h2++) {
       load_k(h2, *hs[h2]);
@@ -233,7 +290,8 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
       load_v(h2, *hs[h2]);
       load_vd(h2, *hs[h2]);
     }
-    step_halves<FMT>(a, g, min(c_first + stride, c_last), c_end, nxt0, nxt1);
+    // keep these loads ahead of the query conversion (which waits for q)
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---------------------------------------------------------------- queries
@@ -244,26 +302,16 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
   f16x8 qop[8];
   f16x8 qlo[QF32 ? 8 : 1];
   float cbias[2] = {0.f, 0.f};
-  const int row = row_base + n;
-  const bool row_ok = n < rows_here;
-  const int lim_eff = min(row_ok ? a.limits[row >> 3] : 0, c_end);
   {
-    const int qi = row >> 3, hl = row & 7;
-    const size_t qbase = ((size_t)qi * a.n_q_heads + (size_t)g * kGqa + hl) * 256;
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
     float qv[8][8];
     for (int kk = 0; kk < 8; kk++) {
-      const int d0 = 64 * (kk >> 1) + 16 * lg + 8 * (kk & 1);
       if (!QF32) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (row_ok) w = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.q) + qbase + d0);
-        const f16x8 h = __builtin_bit_cast(f16x8, w);
+        const f16x8 h = __builtin_bit_cast(f16x8, row_ok ? qraw[kk] : zero4);
         for (int e = 0; e < 8; e++) qv[kk][e] = (float)h[e];
       } else {
-        f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
-        if (row_ok) {
-          x0 = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(a.q) + qbase + d0);
-          x1 = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(a.q) + qbase + d0 + 4);
-        }
+        const f32x4 x0 = __builtin_bit_cast(f32x4, row_ok ? qraw[2 * kk] : zero4);
+        const f32x4 x1 = __builtin_bit_cast(f32x4, row_ok ? qraw[2 * kk + 1] : zero4);
         for (int e = 0; e < 4; e++) {
           qv[kk][e] = x0[e];
           qv[kk][4 + e] = x1[e];
@@ -542,7 +590,9 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
     lds_m[wave * 16 + n] = m;
     lds_l[wave * 16 + n] = lsum;
   }
-  for (int j = 0; j < 16; j++) *reinterpret_cast<f32x4 *>(&lds_o[((wave * 16 + j) * 64 + lane) * 4]) = o[j];
+  // lanes whose 4 rows are all padding (decode fills 8 of the 16) park nothing
+  if (4 * lg < rows_here)
+    for (int j = 0; j < 16; j++) *reinterpret_cast<f32x4 *>(&lds_o[((wave * 16 + j) * 64 + lane) * 4]) = o[j];
   __syncthreads();
 
   const size_t rows_total = (size_t)a.n_rows;
@@ -552,6 +602,7 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
     // rows 4 (L / 16) + i, i = 0..3, of each tile
     const int L = threadIdx.x & 63, jq = threadIdx.x >> 6;
     const int Ln = L & 15, Llg = L >> 4;
+    if (4 * Llg >= rows_here) return;  // rows 4 Llg .. 4 Llg + 3 are all padding
     f32x4 mw[kWaves], lw[kWaves];
     for (int w = 0; w < kWaves; w++) {
       mw[w] = *reinterpret_cast<const f32x4 *>(&lds_m[w * 16 + 4 * Llg]);
