@@ -33,6 +33,8 @@
 //     visible across XCDs (an in-kernel arrival-counter combine cost several
 //     device-scope round trips).  No float atomics: results are
 //     deterministic.
+#include <numeric>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -749,6 +751,13 @@ int launch_attn_splitk(const AttnCall &c) {
   if (passes > kMaxPasses) return KV_ERR_UNSUPPORTED;
   if (c.max_limit > (1 << 30)) return KV_ERR_UNSUPPORTED;
   int target = attn_target_splits(H, n_rows) / passes;
+  // passes of one split read the same cells: with splits x KV heads a
+  // multiple of 8, their workgroups (block ids S * H apart) land on the same
+  // XCD (workgroups go round-robin over the 8) and share its L2
+  if (passes > 1) {
+    const int m = 8 / std::gcd(H, 8);
+    if (target >= m) target -= target % m;
+  }
   if (target < 1) target = 1;
   const SplitPlan plan = plan_splits(c.max_limit, target);
   const WsLayout ws = ws_layout(H, n_rows, plan.n_splits);
