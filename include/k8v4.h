@@ -213,6 +213,28 @@ int attn_decode(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dty
                 size_t ws_bytes, void *stream);
 
 /*
+ * One decode step with its append fused in ("#120 --kv k8v4: hybrid KV
+ * cache", How: a decode step appends the new token's K/V, then attends over
+ * the cache including it).  Equivalent to kv_append_k8v4(pool, seq, k_new,
+ * v_new, kv_dtype, pos, 1) followed by attn_decode(..., n_ctx = pos + 1):
+ * the cell pos receives exactly the bytes kv_append_k8v4 would write, and
+ * the token enters the attention through the same dequantization as a
+ * stored cell (its score summed in a different order, so the output agrees
+ * with the two-call sequence to rounding, not bitwise).  One launch fewer
+ * per step: the last split-K workgroup of each KV head quantizes the token.
+ *   k_new, v_new: device, [n_kv_heads][256], fp16 or fp32 (kv_dtype),
+ *                 16-byte aligned
+ *   q, out, scale, ws: as attn_decode; ws sized for n_ctx = pos + 1.
+ *   pos >= 0, within the table (pos = 0 attends to the new token alone).
+ * k8v4 pools only (_UNSUPPORTED otherwise).  An out-of-range table entry for
+ * cell pos leaves the pool unwritten and gives NaN rows.
+ * Errors: KV_ERR_NULL, _UNSUPPORTED, _DTYPE, _ALIGN, _RANGE, _WORKSPACE.
+ */
+int attn_decode_append(const kv_pool *pool, const kv_seq *seq, const void *k_new, const void *v_new,
+                       int kv_dtype, const void *q, int q_dtype, int n_q_heads, int32_t pos, float scale,
+                       float *out, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Verify window of speculative decoding: n_q query rows read the cache
  * once, row i attending to cells [0, n_visible[i]) -- the batched form with
  * a per-query step array ("#120 --kv k8v4: hybrid KV cache", Tests).

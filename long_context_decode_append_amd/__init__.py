@@ -48,6 +48,7 @@ SIGNATURES = {
     "kv_append": (_I, [_PP, _PS, _P, _P, _I, C.c_int32, C.c_int32, _P]),
     "kv_gather_runs": (_I, [_PP, _PS, C.c_int32, C.c_int32, _P, _P, _P, _P, _P]),
     "attn_decode": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, _F, _P, _P, _SZ, _P]),
+    "attn_decode_append": (_I, [_PP, _PS, _P, _P, _I, _P, _I, _I, C.c_int32, _F, _P, _P, _SZ, _P]),
     "attn_verify": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, _P, _F, _P, _P, _SZ, _P]),
     "attn_prefill_chunk": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, C.c_int32, _F, _P, _P, _SZ, _P]),
     "kv_check_page_table": (_I, [_PP, _PS, C.c_int32, _P]),
@@ -289,6 +290,30 @@ def attn_decode(pool: KvPool, page_table, q, n_ctx: int, ws, scale: float = 0.0,
                            _dev_ptr(out, "out", (torch.float32,)), _dev_ptr(ws, "ws"),
                            ws.numel(), _stream(stream))
     _check(rc, "attn_decode")
+    return out
+
+
+def attn_decode_append(pool: K8V4Pool, page_table, k, v, q, pos: int, ws, scale: float = 0.0,
+                       out=None, stream=None):
+    """Append token k, v ([H][256], fp16/fp32, same dtype) at cell pos of a
+    k8v4 pool and attend q ([Hq][256]) over cells [0, pos] in one launch
+    sequence -> out fp32 [Hq][256]."""
+    torch = _torch()
+    if q.dim() != 2 or q.shape[1] != HEAD_DIM:
+        raise ValueError("q must be [n_q_heads][256]")
+    if k.shape != v.shape or k.dim() != 2 or k.shape[1] != HEAD_DIM:
+        raise ValueError("k, v must be [n_kv_heads][256]")
+    if k.dtype != v.dtype:
+        raise ValueError("k and v must share a dtype")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    seq = _seq(page_table)
+    rc = lib().attn_decode_append(C.byref(pool.struct), C.byref(seq), _dev_ptr(k, "k"),
+                                  _dev_ptr(v, "v"), _dtype_code(k), _dev_ptr(q, "q"), _dtype_code(q),
+                                  int(q.shape[0]), int(pos), float(scale),
+                                  _dev_ptr(out, "out", (torch.float32,)), _dev_ptr(ws, "ws"),
+                                  ws.numel(), _stream(stream))
+    _check(rc, "attn_decode_append")
     return out
 
 

@@ -177,6 +177,39 @@ int attn_decode(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dty
   return launch_attn_splitk(c);
 }
 
+int attn_decode_append(const kv_pool *pool, const kv_seq *seq, const void *k_new, const void *v_new,
+                       int kv_dtype, const void *q, int q_dtype, int n_q_heads, int32_t pos, float scale,
+                       float *out, void *ws, size_t ws_bytes, void *stream) {
+  if (int e = check_attn_common(pool, seq, q, q_dtype, n_q_heads, out, KV_FMT_K8V4)) return e;
+  if (!k_new || !v_new) return KV_ERR_NULL;
+  if (int e = check_dtype(kv_dtype)) return e;
+  if (check_aligned16(k_new) || check_aligned16(v_new)) return KV_ERR_ALIGN;
+  if (pos < 0) return KV_ERR_RANGE;
+  if (int e = check_range(pool, seq, 0, (int64_t)pos + 1)) return e;
+  if (!ws) return KV_ERR_WORKSPACE;
+  if (check_aligned16(ws)) return KV_ERR_ALIGN;
+  AttnCall c;
+  c.pool = pool;
+  c.seq = seq;
+  c.q = q;
+  c.q_dtype = q_dtype;
+  c.n_q_heads = n_q_heads;
+  c.n_q = 1;
+  for (int i = 0; i < kMaxQ; i++) c.limits[i] = 0;
+  c.limits[0] = pos;  // cells streamed from the pool; the new one is added by the kernel
+  c.max_limit = pos;
+  c.scale = pick_scale(scale);
+  c.out = out;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  c.stream = (hipStream_t)stream;
+  c.k_new = k_new;
+  c.v_new = v_new;
+  c.kv_dtype = kv_dtype;
+  c.append_pos = pos;
+  return launch_attn_splitk(c);
+}
+
 int attn_verify(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
                 int n_q_heads, int32_t n_q, const int32_t *n_visible, float scale, float *out,
                 void *ws, size_t ws_bytes, void *stream) {

@@ -19,6 +19,7 @@
 // contraction locally, so x * r + 8.5 is never fused.
 #include "device.hpp"
 #include "launch.hpp"
+#include "quant.hpp"
 
 namespace k8v4 {
 
@@ -30,89 +31,6 @@ struct AppendArgs {
   int dtype;       // 0 fp16, 1 fp32
   int pos0, n_tokens, n_pages, P, H;
 };
-
-__device__ __forceinline__ void load4(const void *base, int dtype, size_t idx, float x[4]) {
-  if (dtype == 0) {
-    const u32x2 w = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint16_t *>(base) + idx);
-    x[0] = f16_bits_to_f32((uint16_t)(w.x & 0xffff));
-    x[1] = f16_bits_to_f32((uint16_t)(w.x >> 16));
-    x[2] = f16_bits_to_f32((uint16_t)(w.y & 0xffff));
-    x[3] = f16_bits_to_f32((uint16_t)(w.y >> 16));
-  } else {
-    const f32x4 w = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(base) + idx);
-    x[0] = w.x; x[1] = w.y; x[2] = w.z; x[3] = w.w;
-  }
-}
-
-// INT8 rule on the 4 values of this lane; lanes 0-31 form group 0 (dims
-// 0..127), lanes 32-63 group 1.  Returns 4 packed codes and the scale.
-__device__ __forceinline__ uint32_t quant_k(const float x[4], float &d_out) {
-#pragma clang fp contract(off)
-  float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
-  for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, lane_xor(amax, m));
-  const float d = amax / 127.0f;                 // correctly rounded division
-  const float r = (d != 0.0f) ? 1.0f / d : 0.0f;
-  uint32_t packed = 0;
-  for (int i = 0; i < 4; i++) {
-    float q = __builtin_rintf(x[i] * r);         // v_rndne_f32: nearest, ties to even
-    q = fminf(fmaxf(q, -127.0f), 127.0f);
-    packed |= ((uint32_t)(int)q & 0xffu) << (8 * i);
-  }
-  d_out = d;
-  return packed;
-}
-
-// Q4_0 rule on a 32-block spread over 8 lanes (4 values each).  Returns the
-// 4 codes of this lane packed as bytes and the fp16 scale bits.
-__device__ __forceinline__ uint32_t quant_q4(const float y[4], int lane, uint16_t &d16) {
-#pragma clang fp contract(off)
-  // value of largest magnitude, first index on ties
-  int bi = 0;
-  float bm = fabsf(y[0]);
-  for (int i = 1; i < 4; i++) {
-    const float a = fabsf(y[i]);
-    if (a > bm) { bm = a; bi = i; }
-  }
-  float bv = y[bi];
-  int bidx = 4 * (lane & 7) + bi;
-  for (int m = 1; m < 8; m <<= 1) {
-    const float om = lane_xor(bm, m);
-    const float ov = lane_xor(bv, m);
-    const int oi = lane_xor(bidx, m);
-    if (om > bm || (om == bm && oi < bidx)) { bm = om; bv = ov; bidx = oi; }
-  }
-  const float d = bv / -8.0f;
-  const float r = (d != 0.0f) ? 1.0f / d : 0.0f;
-  uint32_t codes = 0;
-  for (int i = 0; i < 4; i++) {
-    const float t = y[i] * r;
-    const float u = t + 8.5f;
-    int c = (int)u;                              // v_cvt_i32_f32 truncates toward zero
-    c = c > 15 ? 15 : c;
-    codes |= (uint32_t)c << (8 * i);
-  }
-  d16 = f32_to_f16_bits(d);
-  return codes;
-}
-
-// INT8 half of one head: codes [cell][256], fp32 scales [cell][2]
-__device__ __forceinline__ void store_int8(uint8_t *codes_run, uint8_t *scales_run, size_t cell, int lane,
-                                           uint32_t codes, float d) {
-  *reinterpret_cast<uint32_t *>(codes_run + cell * 256 + 4 * lane) = codes;
-  if ((lane & 31) == 0) reinterpret_cast<float *>(scales_run)[cell * 2 + (lane >> 5)] = d;
-}
-
-// Q4_0 half of one head into its (page, head) tile: byte i of a block =
-// code[i] | code[i+16] << 4; lanes j < 4 of the block hold elements
-// 4j..4j+3, lane j + 4 holds elements 16 + 4j..
-__device__ __forceinline__ void store_q4(uint8_t *run, size_t tile, int P, int slot, int lane, uint32_t codes,
-                                         uint16_t d16) {
-  const uint32_t hi = (uint32_t)__shfl_xor((int)codes, 4, 64);
-  const int b = lane >> 3, j = lane & 7;
-  uint8_t *vt = run + tile * 144 * P;
-  if (j < 4) *reinterpret_cast<uint32_t *>(vt + (size_t)slot * 128 + b * 16 + 4 * j) = codes | (hi << 4);
-  if (j == 0) *reinterpret_cast<uint16_t *>(vt + q4_scale_off(P, slot, b)) = d16;
-}
 
 // one wave per (token, KV head); FMT selects the rule of each half
 template <int FMT>

@@ -37,6 +37,7 @@
 
 #include "device.hpp"
 #include "launch.hpp"
+#include "quant.hpp"
 
 namespace k8v4 {
 
@@ -62,6 +63,14 @@ struct SplitArgs {
   int max_limit;
   float scale2;         // softmax scale * log2(e)
   int steps_per_split, n_splits;
+  // fused append (k8v4 decode only): the token k_new / v_new ([H][256],
+  // kv_dtype) is quantized into cell append_pos (-1: no append) by the last
+  // split, which also adds it to its partial; the other cells come from the
+  // pool as usual (max_limit = append_pos)
+  const void *k_new;
+  const void *v_new;
+  int kv_dtype;
+  int append_pos;
 };
 
 // dim of output tile j held by column n of the PV MFMA.  q4_0 V: column n
@@ -180,6 +189,8 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
   __shared__ __attribute__((aligned(16))) float lds_o[kWaves * 16 * 64 * 4];  // wave states, accumulator layout
   __shared__ __attribute__((aligned(16))) float lds_m[kWaves * 16];
   __shared__ __attribute__((aligned(16))) float lds_l[kWaves * 16];
+  __shared__ __attribute__((aligned(16))) float lds_vnew[256];  // fused append: the token's V (rotated)
+  __shared__ __attribute__((aligned(16))) float lds_snew[16];   // and its score per row
   constexpr bool kInt8K = FMT != KV_FMT_Q4_0;   // K as INT8 codes (else rotated q4_0)
   constexpr bool kQ4V = FMT != KV_FMT_INT8;     // V as rotated q4_0 (else INT8 codes)
 
@@ -372,6 +383,50 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
       cbias[1] = 1152.0f * s1;
     }
   }
+  // ---------------------------------------------------------------- fused append
+  // The last split of a k8v4 decode with an append: wave 0 quantizes the
+  // new token of this KV head with the append kernel's rules, stores it into
+  // its cell, and leaves its dequantized values for the merge: the score
+  // (q . K) * scale * log2(e) of each row and the rotated V, (code - 8) * d
+  // rounded to fp16 as the streamed cells are.  A cell whose page-table
+  // entry is out of range is not written and gives the rows NaN.
+  const bool appender = FMT == KV_FMT_K8V4 && a.append_pos >= 0 && split == a.n_splits - 1 && pass == 0;
+  if (appender && wave == 0) {
+    const int pos = a.append_pos;
+    const int page = pt_entry(a, page_of(a, pos));
+    const bool bad = page < 0 || page >= a.n_pages;
+    const int slot = pos - page_of(a, pos) * a.P;
+    const size_t tile = (size_t)(bad ? 0 : page) * a.H + g;
+    float x[4], y[4];
+    load4(a.k_new, a.kv_dtype, (size_t)g * 256 + 4 * lane, x);
+    load4(a.v_new, a.kv_dtype, (size_t)g * 256 + 4 * lane, y);
+    float dk;
+    const uint32_t kcodes = quant_k(x, dk);
+    fwht256_lane4(y, lane);
+    uint16_t d16;
+    const uint32_t vcodes = quant_q4(y, lane, d16);
+    if (!bad) {
+      store_int8(const_cast<uint8_t *>(reinterpret_cast<const uint8_t *>(a.kc)),
+                 const_cast<uint8_t *>(reinterpret_cast<const uint8_t *>(a.ks)), tile * a.P + slot, lane, kcodes, dk);
+      store_q4(const_cast<uint8_t *>(a.vq), tile, a.P, slot, lane, vcodes, d16);
+    }
+    const _Float16 dh = __builtin_bit_cast(_Float16, d16);
+    float kd[4];
+    for (int i = 0; i < 4; i++) {
+      kd[i] = (float)(int8_t)(kcodes >> (8 * i)) * dk;
+      lds_vnew[4 * lane + i] = (float)((_Float16)(float)((int)((vcodes >> (8 * i)) & 0xffu) - 8) * dh);
+    }
+    for (int r = 0; r < rows_here; r++) {
+      const int rw = row_base + r;
+      const size_t qb = ((size_t)(rw >> 3) * a.n_q_heads + (size_t)g * kGqa + (rw & 7)) * 256 + 4 * lane;
+      float qx[4];
+      load4(a.q, QF32 ? 1 : 0, qb, qx);
+      float dot = qx[0] * kd[0] + qx[1] * kd[1] + qx[2] * kd[2] + qx[3] * kd[3];
+      for (int msk = 32; msk >= 1; msk >>= 1) dot += lane_xor(dot, msk);
+      if (lane == 0) lds_snew[r] = bad ? __builtin_nanf("") : dot * a.scale2;
+    }
+  }
+
   // smallest visible-cell limit over the valid rows of this tile (wave-
   // uniform): steps that end below it need no masking at all
   int lim_min;
@@ -613,17 +668,30 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
     f32x4 M = mw[0];
     for (int w = 1; w < kWaves; w++)
       for (int i = 0; i < 4; i++) M[i] = fmaxf(M[i], mw[w][i]);
+    // the fused append's token is one more state: m = its score, l = 1
+    f32x4 sn = {0.f, 0.f, 0.f, 0.f};
+    if (appender) {
+      sn = *reinterpret_cast<const f32x4 *>(&lds_snew[4 * Llg]);
+      for (int i = 0; i < 4; i++) M[i] = fmaxf(M[i], sn[i]);
+    }
     f32x4 f[kWaves], Ls = {0.f, 0.f, 0.f, 0.f};
     for (int w = 0; w < kWaves; w++)
       for (int i = 0; i < 4; i++) {
         f[w][i] = fast_exp2(mw[w][i] - M[i]);
         Ls[i] += lw[w][i] * f[w][i];
       }
+    f32x4 fn = {0.f, 0.f, 0.f, 0.f};
+    if (appender)
+      for (int i = 0; i < 4; i++) {
+        fn[i] = fast_exp2(sn[i] - M[i]);
+        Ls[i] += fn[i];
+      }
     f32x4 val[4];
     for (int jj = 0; jj < 4; jj++) {
       const int j = 4 * jq + jj;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int w = 0; w < kWaves; w++) acc += f[w] * *reinterpret_cast<const f32x4 *>(&lds_o[((w * 16 + j) * 64 + L) * 4]);
+      if (appender) acc += fn * lds_vnew[o_dim<kQ4V>(Ln, j)];
       val[jj] = acc;
     }
     for (int i = 0; i < 4; i++) {
@@ -759,7 +827,8 @@ int launch_attn_splitk(const AttnCall &c) {
     if (target >= m) target -= target % m;
   }
   if (target < 1) target = 1;
-  const SplitPlan plan = plan_splits(c.max_limit, target);
+  // (a fused append onto an empty cache streams no cells: one empty split)
+  const SplitPlan plan = plan_splits(c.max_limit > 0 ? c.max_limit : 1, target);
   const WsLayout ws = ws_layout(H, n_rows, plan.n_splits);
   if (ws.total > c.ws_bytes) return KV_ERR_WORKSPACE;
 
@@ -799,6 +868,10 @@ int launch_attn_splitk(const AttnCall &c) {
   a.scale2 = c.scale * 1.4426950408889634f;
   a.steps_per_split = plan.steps_per_split;
   a.n_splits = plan.n_splits;
+  a.k_new = c.k_new;
+  a.v_new = c.v_new;
+  a.kv_dtype = c.kv_dtype;
+  a.append_pos = c.append_pos;
 
   dim3 grid(plan.n_splits, H, passes);
   a.v_rotated = pool->fmt != KV_FMT_INT8;

@@ -47,6 +47,12 @@ struct AttnCall {
   void *ws;
   size_t ws_bytes;
   hipStream_t stream;
+  // fused append (decode of a k8v4 pool only): token [H][256] of kv_dtype
+  // stored at cell append_pos = max_limit before attending; -1 for none
+  const void *k_new = nullptr;
+  const void *v_new = nullptr;
+  int kv_dtype = 0;
+  int append_pos = -1;
 };
 int launch_attn_splitk(const AttnCall &c);
 

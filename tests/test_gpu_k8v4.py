@@ -342,3 +342,81 @@ def test_prefill_chunk_8192_at_231808_sampled_rows(orc, k8, dev):
     err = rel_err(out[rows], ref)
     say(f"  rel err {err:.3e}")
     assert err <= TOL
+
+
+# ------------------------------------------------------------------ fused append + decode
+
+def _append_case(orc, k8, dev, seed, pos, dtype, P=16, n_pages=70, n_table=66):
+    """A pool holding cells [0, pos) and the token of cell pos, not yet appended."""
+    c = Case(orc, k8, dev, seed, pos, P, n_pages, n_table, dtype=dtype, chunk=4096)
+    k, v = synth.kv_tokens(seed, 0, pos, 1, 2, 256, dtype)
+    return c, k, v
+
+
+@pytest.mark.parametrize("pos", [0, 1, 15, 16, 17, 100, 511, 1055])
+@pytest.mark.parametrize("dtype", [np.float32, np.float16])
+def test_decode_append_parity_and_bytes(orc, k8, dev, pos, dtype):
+    say(f"decode_append pos={pos} dtype={dtype.__name__}")
+    import torch
+    c, k, v = _append_case(orc, k8, dev, 11, pos, dtype)
+    twin, _, _ = _append_case(orc, k8, dev, 11, pos, dtype)
+    q = synth.queries(11, 0, pos, 1, 16, 256, dtype)
+    ws = k8.attn_workspace(c.gpool, 1, pos + 1)
+    out = k8.attn_decode_append(c.gpool, c.gpt, t_(k[0], dev), t_(v[0], dev), t_(q[0], dev), pos, ws)
+    torch.cuda.synchronize()
+    # the cell's bytes: exactly what the append kernel writes, and nothing else changes
+    k8.kv_append_k8v4(twin.gpool, twin.gpt, t_(k, dev), t_(v, dev), pos)
+    for ra, rb in zip(c.gpool.runs, twin.gpool.runs):
+        if ra is not None:
+            assert torch.equal(ra, rb)
+    # ... and what the oracle's rules give
+    c.opool.append(c.pt, k, v, pos)
+    g_gpu = k8.kv_gather(c.gpool, c.gpt, pos, 1)
+    g_orc = c.opool.gather(c.pt, pos, 1)
+    for a_, b_ in zip(g_gpu, g_orc):
+        assert np.array_equal(a_.cpu().numpy().view(np.uint8), np.ascontiguousarray(b_).view(np.uint8))
+    ref = c.oracle_attention(orc, q, [pos + 1])[0]
+    err = rel_err(out.cpu().numpy(), ref)
+    say(f"  rel err vs oracle {err:.3e}")
+    assert err <= TOL
+    # the two-call sequence on the twin: the same attention up to rounding
+    # (the streamed path scores an fp32 q as two fp16 halves; the fused token
+    # is scored in fp32 directly), so to the same tolerance
+    ws2 = k8.attn_workspace(twin.gpool, 1, pos + 1)
+    two = k8.attn_decode(twin.gpool, twin.gpt, t_(q[0], dev), pos + 1, ws2).cpu().numpy()
+    err2 = rel_err(out.cpu().numpy(), two)
+    say(f"  rel diff vs append + decode {err2:.3e}")
+    assert err2 <= TOL
+
+
+def test_decode_append_out_of_range_entry_gives_nan_and_no_write(orc, k8, dev):
+    import torch
+    c, k, v = _append_case(orc, k8, dev, 12, 40, np.float16)
+    pt = c.pt.copy()
+    pt[40 // 16] = 10_000  # the new cell's page is out of the pool
+    gpt = t_(pt, dev)
+    before = [None if r is None else r.clone() for r in c.gpool.runs]
+    q = synth.queries(12, 0, 40, 1, 16, 256, np.float16)
+    ws = k8.attn_workspace(c.gpool, 1, 41)
+    # cells 32..39 share the bad page as well: the streamed rows see it too
+    out = k8.attn_decode_append(c.gpool, gpt, t_(k[0], dev), t_(v[0], dev), t_(q[0], dev), 40, ws)
+    assert torch.isnan(out).all()
+    for ra, rb in zip(c.gpool.runs, before):
+        if ra is not None:
+            assert torch.equal(ra, rb)
+
+
+def test_decode_append_32768_outliers(orc, k8, dev):
+    say("decode_append at 32,767 with outlier channels")
+    pos = 32767
+    c = Case(orc, k8, dev, 13, pos, 256, 130, 128, outlier_frac=0.01)
+    outl = synth.outlier_channels(13, 2, 256, 0.01)
+    k, v = synth.kv_tokens(13, 0, pos, 1, 2, 256, np.float16, outl)
+    q = synth.queries(13, 0, pos, 1, 16, 256, np.float16)
+    ws = k8.attn_workspace(c.gpool, 1, pos + 1)
+    out = k8.attn_decode_append(c.gpool, c.gpt, t_(k[0], dev), t_(v[0], dev), t_(q[0], dev), pos, ws)
+    c.opool.append(c.pt, k, v, pos)
+    ref = c.oracle_attention(orc, q, [pos + 1])[0]
+    err = rel_err(out.cpu().numpy(), ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
