@@ -2,8 +2,9 @@
 """Benchmark: k8v4 decode attention at 118,750 cells x 48 layers on one MI355X.
 
 One step = one decoded token across 48 layers: for every layer, append the
-token's K/V at cell 118,749 (kv_append_k8v4) and attend over cells
-[0, 118,750) (attn_decode).  Each layer has its own pool (96.9 MB of k8v4
+token's K/V at cell 118,749 and attend over cells [0, 118,750), in one
+fused call (attn_decode_append; the two-call form kv_append_k8v4 +
+attn_decode is timed beside it in extra).  Each layer has its own pool (96.9 MB of k8v4
 pages, 4.65 GB in all, far beyond the 256 MB Infinity Cache), so every step
 streams its KV from HBM.  The step is captured once per step index in a HIP
 graph (torch.cuda.CUDAGraph) and replayed; W untimed steps, then K timed
@@ -224,8 +225,8 @@ def main():
     def step(s):
         for l in range(layers):
             kn, vn = kv_new[s][l]
-            k8.kv_append_k8v4(pools[l], tables[l], kn, vn, ctx - 1)
-            k8.attn_decode(pools[l], tables[l], q_all[s][l], ctx, ws, out=outs[l])
+            k8.attn_decode_append(pools[l], tables[l], kn[0], vn[0], q_all[s][l], ctx - 1, ws,
+                                  out=outs[l])
 
     # eager run of every step once (also warms the library's device cache)
     log("eager pass ...")
@@ -267,9 +268,9 @@ def main():
 
     # the decode kernel on its own: start/stop events around each launch
     log("per-kernel timing ...")
-    dec_ms, _ = timed_launches(torch, k8, lambda i: k8.attn_decode(
-        pools[i % layers], tables[i % layers], q_all[0][i % layers], ctx, ws,
-        out=outs[i % layers]), 2 * layers)
+    dec_ms, _ = timed_launches(torch, k8, lambda i: k8.attn_decode_append(
+        pools[i % layers], tables[i % layers], kv_new[0][i % layers][0][0], kv_new[0][i % layers][1][0],
+        q_all[0][i % layers], ctx - 1, ws, out=outs[i % layers]), 2 * layers)
     app_ms, _ = timed_launches(torch, k8, lambda i: k8.kv_append_k8v4(
         pools[i % layers], tables[i % layers], kv_new[0][i % layers][0],
         kv_new[0][i % layers][1], ctx - 1), layers)
@@ -288,6 +289,22 @@ def main():
         extra["decode_118750_split_plus_combine"] = {
             "us": round(dc_ms * 1e3, 3),
             "hbm_frac": round(ctx * CELL_BYTES / dc_ms / 1e6 / HBM_PEAK_GBS, 4)}
+
+        def two_call(i):
+            l = i % layers
+            kn, vn = kv_new[0][l]
+            k8.kv_append_k8v4(pools[l], tables[l], kn, vn, ctx - 1)
+            k8.attn_decode(pools[l], tables[l], q_all[0][l], ctx, ws, out=outs[l])
+
+        def fused(i):
+            l = i % layers
+            kn, vn = kv_new[0][l]
+            k8.attn_decode_append(pools[l], tables[l], kn[0], vn[0], q_all[0][l], ctx - 1, ws,
+                                  out=outs[l])
+        extra["layer_118750_append_and_decode_us"] = {
+            "fused (attn_decode_append)": round(graph_calls_ms(torch, fused, layers, replays=2) * 1e3, 3),
+            "two calls (kv_append_k8v4 + attn_decode)": round(
+                graph_calls_ms(torch, two_call, layers, replays=2) * 1e3, 3)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -309,14 +326,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode_118750x48", "ctx": ctx, "layers": layers, "batch": 1,
                    "q_heads": 16, "kv_heads": 2, "head_dim": 256, "page_size": P,
-                   "kv_format": "k8v4 (816 B/cell)", "per_step": "48 x (append 1 token + decode)",
+                   "kv_format": "k8v4 (816 B/cell)", "per_step": "48 x (append 1 token + decode), fused (attn_decode_append)",
                    "launch": "HIP graph per step"},
         "us_per_step": round(step_ms * 1e3, 2),
         "us_per_layer": round(step_ms * 1e3 / layers, 3),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "eager_ms_per_step": round(eager_ms, 3),
         "wall_s_timed": round(t_wall, 4),
-        "roofline": {"kernel": "attn_splitk_kernel (decode, 1 query)", "bound": "hbm",
+        "roofline": {"kernel": "attn_splitk_kernel (decode with fused append, 1 query)", "bound": "hbm",
                      "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": ctx * CELL_BYTES, "traffic_bytes_per_launch": traffic_bytes,

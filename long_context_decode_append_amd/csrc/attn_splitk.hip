@@ -63,10 +63,11 @@ struct SplitArgs {
   int max_limit;
   float scale2;         // softmax scale * log2(e)
   int steps_per_split, n_splits;
+  int n_parts;          // partials per (KV head, row): n_splits, + 1 with a fused append
   // fused append (k8v4 decode only): the token k_new / v_new ([H][256],
-  // kv_dtype) is quantized into cell append_pos (-1: no append) by the last
-  // split, which also adds it to its partial; the other cells come from the
-  // pool as usual (max_limit = append_pos)
+  // kv_dtype) goes into cell append_pos (-1: no append); workgroup x =
+  // n_splits of each KV head quantizes it and writes it as one more partial,
+  // while the splits stream cells [0, append_pos) (max_limit = append_pos)
   const void *k_new;
   const void *v_new;
   int kv_dtype;
@@ -184,13 +185,58 @@ __device__ __forceinline__ void first_halves(const SplitArgs &a, int g, int c0, 
 // elements of a 4-byte word as (0, 2) then (1, 3)
 __device__ __forceinline__ int q4_kslot(int t) { return (t & 4) | ((t & 1) << 1) | ((t >> 1) & 1); }
 
+// Fused append of a decode (one wave, 4 dims per lane): quantize the new
+// token of KV head g with the append kernel's rules, store it into cell
+// append_pos, and write it as one more split partial of the 8 rows: m = its
+// score (q . K) * scale * log2(e) with K = code * d, l = 1, O = its rotated
+// V, (code - 8) * d rounded to fp16 as the streamed cells are.  A cell whose
+// page-table entry is out of range is not written and gives the rows NaN.
+template <bool QF32>
+__device__ __forceinline__ void append_token_partial(const SplitArgs &a, int g, int lane) {
+  const int pos = a.append_pos;
+  const int page = pt_entry(a, page_of(a, pos));
+  const bool bad = page < 0 || page >= a.n_pages;
+  const int slot = pos - page_of(a, pos) * a.P;
+  const size_t tile = (size_t)(bad ? 0 : page) * a.H + g;
+  float x[4], y[4];
+  load4(a.k_new, a.kv_dtype, (size_t)g * 256 + 4 * lane, x);
+  load4(a.v_new, a.kv_dtype, (size_t)g * 256 + 4 * lane, y);
+  float qx[kGqa][4];  // the 8 query heads of this KV head (a decode has one query)
+  for (int r = 0; r < kGqa; r++) load4(a.q, QF32 ? 1 : 0, ((size_t)g * kGqa + r) * 256 + 4 * lane, qx[r]);
+  float dk;
+  const uint32_t kcodes = quant_k(x, dk);
+  fwht256_lane4(y, lane);
+  uint16_t d16;
+  const uint32_t vcodes = quant_q4(y, lane, d16);
+  if (!bad) {
+    store_int8(const_cast<uint8_t *>(reinterpret_cast<const uint8_t *>(a.kc)),
+               const_cast<uint8_t *>(reinterpret_cast<const uint8_t *>(a.ks)), tile * a.P + slot, lane, kcodes, dk);
+    store_q4(const_cast<uint8_t *>(a.vq), tile, a.P, slot, lane, vcodes, d16);
+  }
+  const _Float16 dh = __builtin_bit_cast(_Float16, d16);
+  float kd[4];
+  f32x4 vo;
+  for (int i = 0; i < 4; i++) {
+    kd[i] = (float)(int8_t)(kcodes >> (8 * i)) * dk;
+    vo[i] = (float)((_Float16)(float)((int)((vcodes >> (8 * i)) & 0xffu) - 8) * dh);
+  }
+  float dot[kGqa];
+  for (int r = 0; r < kGqa; r++) dot[r] = qx[r][0] * kd[0] + qx[r][1] * kd[1] + qx[r][2] * kd[2] + qx[r][3] * kd[3];
+  for (int msk = 32; msk >= 1; msk >>= 1)
+    for (int r = 0; r < kGqa; r++) dot[r] += lane_xor(dot[r], msk);
+  const size_t rows_total = (size_t)a.n_rows;
+  const size_t sp = (size_t)g * a.n_parts + a.n_splits;
+  for (int r = 0; r < kGqa; r++) {
+    *reinterpret_cast<f32x4 *>(a.part_o + (sp * rows_total + r) * 256 + 4 * lane) = vo;
+    if (lane == 0) a.part_ml[sp * rows_total + r] = make_float2(bad ? __builtin_nanf("") : dot[r] * a.scale2, 1.0f);
+  }
+}
+
 template <bool QF32, int FMT>
 __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) {
   __shared__ __attribute__((aligned(16))) float lds_o[kWaves * 16 * 64 * 4];  // wave states, accumulator layout
   __shared__ __attribute__((aligned(16))) float lds_m[kWaves * 16];
   __shared__ __attribute__((aligned(16))) float lds_l[kWaves * 16];
-  __shared__ __attribute__((aligned(16))) float lds_vnew[256];  // fused append: the token's V (rotated)
-  __shared__ __attribute__((aligned(16))) float lds_snew[16];   // and its score per row
   constexpr bool kInt8K = FMT != KV_FMT_Q4_0;   // K as INT8 codes (else rotated q4_0)
   constexpr bool kQ4V = FMT != KV_FMT_INT8;     // V as rotated q4_0 (else INT8 codes)
 
@@ -201,6 +247,12 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, lg = lane >> 4;
   const int split = blockIdx.x, g = blockIdx.y, pass = blockIdx.z;
+  if (FMT == KV_FMT_K8V4 && split == a.n_splits) {
+    // the fused append's own workgroup (exists only with one), on a CU of
+    // its own beside the streaming splits
+    if (wave == 0) append_token_partial<QF32>(a, g, lane);
+    return;
+  }
   const int row_base = pass * a.rows_per_pass;
   const int rows_here = min(a.rows_per_pass, a.n_rows - row_base);
 
@@ -383,50 +435,6 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
       cbias[1] = 1152.0f * s1;
     }
   }
-  // ---------------------------------------------------------------- fused append
-  // The last split of a k8v4 decode with an append: wave 0 quantizes the
-  // new token of this KV head with the append kernel's rules, stores it into
-  // its cell, and leaves its dequantized values for the merge: the score
-  // (q . K) * scale * log2(e) of each row and the rotated V, (code - 8) * d
-  // rounded to fp16 as the streamed cells are.  A cell whose page-table
-  // entry is out of range is not written and gives the rows NaN.
-  const bool appender = FMT == KV_FMT_K8V4 && a.append_pos >= 0 && split == a.n_splits - 1 && pass == 0;
-  if (appender && wave == 0) {
-    const int pos = a.append_pos;
-    const int page = pt_entry(a, page_of(a, pos));
-    const bool bad = page < 0 || page >= a.n_pages;
-    const int slot = pos - page_of(a, pos) * a.P;
-    const size_t tile = (size_t)(bad ? 0 : page) * a.H + g;
-    float x[4], y[4];
-    load4(a.k_new, a.kv_dtype, (size_t)g * 256 + 4 * lane, x);
-    load4(a.v_new, a.kv_dtype, (size_t)g * 256 + 4 * lane, y);
-    float dk;
-    const uint32_t kcodes = quant_k(x, dk);
-    fwht256_lane4(y, lane);
-    uint16_t d16;
-    const uint32_t vcodes = quant_q4(y, lane, d16);
-    if (!bad) {
-      store_int8(const_cast<uint8_t *>(reinterpret_cast<const uint8_t *>(a.kc)),
-                 const_cast<uint8_t *>(reinterpret_cast<const uint8_t *>(a.ks)), tile * a.P + slot, lane, kcodes, dk);
-      store_q4(const_cast<uint8_t *>(a.vq), tile, a.P, slot, lane, vcodes, d16);
-    }
-    const _Float16 dh = __builtin_bit_cast(_Float16, d16);
-    float kd[4];
-    for (int i = 0; i < 4; i++) {
-      kd[i] = (float)(int8_t)(kcodes >> (8 * i)) * dk;
-      lds_vnew[4 * lane + i] = (float)((_Float16)(float)((int)((vcodes >> (8 * i)) & 0xffu) - 8) * dh);
-    }
-    for (int r = 0; r < rows_here; r++) {
-      const int rw = row_base + r;
-      const size_t qb = ((size_t)(rw >> 3) * a.n_q_heads + (size_t)g * kGqa + (rw & 7)) * 256 + 4 * lane;
-      float qx[4];
-      load4(a.q, QF32 ? 1 : 0, qb, qx);
-      float dot = qx[0] * kd[0] + qx[1] * kd[1] + qx[2] * kd[2] + qx[3] * kd[3];
-      for (int msk = 32; msk >= 1; msk >>= 1) dot += lane_xor(dot, msk);
-      if (lane == 0) lds_snew[r] = bad ? __builtin_nanf("") : dot * a.scale2;
-    }
-  }
-
   // smallest visible-cell limit over the valid rows of this tile (wave-
   // uniform): steps that end below it need no masking at all
   int lim_min;
@@ -653,7 +661,7 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
   __syncthreads();
 
   const size_t rows_total = (size_t)a.n_rows;
-  const size_t sp = (size_t)g * a.n_splits + split;
+  const size_t sp = (size_t)g * a.n_parts + split;
   {
     // thread -> accumulator lane L and tiles 4 jq .. 4 jq + 3; the lane holds
     // rows 4 (L / 16) + i, i = 0..3, of each tile
@@ -668,30 +676,17 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
     f32x4 M = mw[0];
     for (int w = 1; w < kWaves; w++)
       for (int i = 0; i < 4; i++) M[i] = fmaxf(M[i], mw[w][i]);
-    // the fused append's token is one more state: m = its score, l = 1
-    f32x4 sn = {0.f, 0.f, 0.f, 0.f};
-    if (appender) {
-      sn = *reinterpret_cast<const f32x4 *>(&lds_snew[4 * Llg]);
-      for (int i = 0; i < 4; i++) M[i] = fmaxf(M[i], sn[i]);
-    }
     f32x4 f[kWaves], Ls = {0.f, 0.f, 0.f, 0.f};
     for (int w = 0; w < kWaves; w++)
       for (int i = 0; i < 4; i++) {
         f[w][i] = fast_exp2(mw[w][i] - M[i]);
         Ls[i] += lw[w][i] * f[w][i];
       }
-    f32x4 fn = {0.f, 0.f, 0.f, 0.f};
-    if (appender)
-      for (int i = 0; i < 4; i++) {
-        fn[i] = fast_exp2(sn[i] - M[i]);
-        Ls[i] += fn[i];
-      }
     f32x4 val[4];
     for (int jj = 0; jj < 4; jj++) {
       const int j = 4 * jq + jj;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int w = 0; w < kWaves; w++) acc += f[w] * *reinterpret_cast<const f32x4 *>(&lds_o[((w * 16 + j) * 64 + L) * 4]);
-      if (appender) acc += fn * lds_vnew[o_dim<kQ4V>(Ln, j)];
       val[jj] = acc;
     }
     for (int i = 0; i < 4; i++) {
@@ -722,7 +717,7 @@ __global__ __launch_bounds__(kCombineWaves * 64) void attn_combine_kernel(const 
   const int row = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int S = a.n_splits;
+  const int S = a.n_parts;
   const size_t rows_total = (size_t)a.n_rows;
   const size_t base = (size_t)g * S;
   const float *po = a.part_o + (base * rows_total + row) * 256 + 4 * lane;
@@ -827,9 +822,13 @@ int launch_attn_splitk(const AttnCall &c) {
     if (target >= m) target -= target % m;
   }
   if (target < 1) target = 1;
-  // (a fused append onto an empty cache streams no cells: one empty split)
+  // a fused append adds one partial per KV head (its own workgroup); onto an
+  // empty cache it streams no cells (one empty split)
+  const bool fused = c.append_pos >= 0;
+  if (fused && target > kMaxSplitsPerHead - 1) target = kMaxSplitsPerHead - 1;
   const SplitPlan plan = plan_splits(c.max_limit > 0 ? c.max_limit : 1, target);
-  const WsLayout ws = ws_layout(H, n_rows, plan.n_splits);
+  const int n_parts = plan.n_splits + (fused ? 1 : 0);
+  const WsLayout ws = ws_layout(H, n_rows, n_parts);
   if (ws.total > c.ws_bytes) return KV_ERR_WORKSPACE;
 
   SplitArgs a;
@@ -868,12 +867,13 @@ int launch_attn_splitk(const AttnCall &c) {
   a.scale2 = c.scale * 1.4426950408889634f;
   a.steps_per_split = plan.steps_per_split;
   a.n_splits = plan.n_splits;
+  a.n_parts = n_parts;
   a.k_new = c.k_new;
   a.v_new = c.v_new;
   a.kv_dtype = c.kv_dtype;
   a.append_pos = c.append_pos;
 
-  dim3 grid(plan.n_splits, H, passes);
+  dim3 grid(n_parts, H, passes);
   a.v_rotated = pool->fmt != KV_FMT_INT8;
   switch (pool->fmt * 2 + (qf32 ? 1 : 0)) {
     case KV_FMT_INT8 * 2: launch((attn_splitk_kernel<false, KV_FMT_INT8>), grid, dim3(256), c.stream, a); break;

@@ -108,8 +108,9 @@ size_t ws_bytes_bound(int n_kv_heads, int n_rows, int64_t max_ctx) {
   // context up to max_ctx and every device
   const int64_t steps = (max_ctx + kStep - 1) / kStep;
   int64_t s = (steps + kWaves - 1) / kWaves;
-  if (s > kMaxSplitsPerHead) s = kMaxSplitsPerHead;
   if (s < 1) s = 1;
+  s += 1;  // the partial of a fused append (attn_decode_append)
+  if (s > kMaxSplitsPerHead) s = kMaxSplitsPerHead;
   return ws_layout(n_kv_heads, n_rows, (int)s).total;
 }
 
