@@ -179,10 +179,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", choices=["decode", "copy"], default=None,
-                    help="profiling aids: 'decode' runs 24 eager decode calls at 118,750 cells "
-                         "(8 layer pools); 'copy' runs 4 plain 1 GiB device copies (calibrates "
-                         "the HBM byte counters)")
+    ap.add_argument("--only", choices=["decode", "copy", "prefill", "verify"], default=None,
+                    help="profiling aids: 'decode' runs 24 eager fused append + decode calls at "
+                         "118,750 cells (8 layer pools); 'copy' runs 4 plain 1 GiB device copies "
+                         "(calibrates the HBM byte counters); 'prefill' runs the 8,192-query chunk "
+                         "at 231,808 twice; 'verify' runs 4 five-query verify calls at 240,000")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -347,6 +348,27 @@ def main():
 
 def profile_only(what, torch, k8, synth, dev):
     """Short, fixed workloads for counter collection under rocprofv3."""
+    if what in ("prefill", "verify"):
+        ctx, P, n_pages = 240000, 256, 1024
+        pool = k8.K8V4Pool(n_pages, P, 2, device=dev)
+        pt = make_table(torch, synth, 4, 0, (ctx + P - 1) // P, n_pages, dev)
+        fill_pool(k8, synth, pool, pt, 4, 0, ctx, dev)
+        if what == "prefill":
+            pos0, n_new = 231808, 8192
+            q = synth.queries_device(4, 0, 0, n_new, 16, 256, dev)
+            out = torch.empty((n_new, 16, 256), dtype=torch.float32, device=dev)
+            for _ in range(2):
+                k8.attn_prefill_chunk(pool, pt, q, pos0, out=out)
+            log(f"2 prefill chunks of {n_new} at {pos0}")
+        else:
+            nv = [ctx - 4 + i for i in range(5)]
+            q = synth.queries_device(4, 0, 0, 5, 16, 256, dev)
+            ws = k8.attn_workspace(pool, 5, ctx)
+            for _ in range(4):
+                k8.attn_verify(pool, pt, q, nv, ws)
+            log(f"4 verify calls of 5 queries at {ctx}")
+        torch.cuda.synchronize()
+        return
     if what == "copy":
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -369,10 +391,12 @@ def profile_only(what, torch, k8, synth, dev):
     ws = k8.attn_workspace(pools[0], 1, ctx)
     q = synth.queries_device(3, 0, 0, 1, 16, 256, dev)[0]
     out = torch.empty((16, 256), dtype=torch.float32, device=dev)
+    kn, vn = synth.kv_chunk_device(3, 0, 10_000, 1, 2, 256, dev)
     for i in range(3 * layers):
-        k8.attn_decode(pools[i % layers], tables[i % layers], q, ctx, ws, out=out)
+        # the bench step's call: the token of cell ctx - 1, then attention over [0, ctx)
+        k8.attn_decode_append(pools[i % layers], tables[i % layers], kn[0], vn[0], q, ctx - 1, ws, out=out)
     torch.cuda.synchronize()
-    log(f"{3 * layers} decode calls at {ctx} cells")
+    log(f"{3 * layers} decode calls (fused append) at {ctx} cells")
 
 
 def bench_extra(torch, k8, synth, dev, log):
