@@ -255,8 +255,9 @@ int attn_verify(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dty
  * prefill).  Dense contractions on the matrix cores (fp16 inputs, fp32
  * accumulation).
  *   q:   device, [n_new][n_q_heads][256];  out: device fp32 [n_new][n_q_heads][256]
- * Needs no workspace (ws may be NULL).  k8v4 pools only (_UNSUPPORTED for
- * the comparison formats).
+ * Needs no workspace (ws may be NULL).  Any of the three formats, with the
+ * same rules as attn_decode (q4_0 scores the rotated query against rotated
+ * keys; int8 returns softmax(.) V unrotated).
  * Errors: KV_ERR_NULL, _UNSUPPORTED, _DTYPE, _RANGE.
  */
 int attn_prefill_chunk(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,

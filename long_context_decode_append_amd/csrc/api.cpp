@@ -246,7 +246,7 @@ int attn_prefill_chunk(const kv_pool *pool, const kv_seq *seq, const void *q, in
                        void *ws, size_t ws_bytes, void *stream) {
   (void)ws;
   (void)ws_bytes;
-  if (int e = check_attn_common(pool, seq, q, q_dtype, n_q_heads, out, KV_FMT_K8V4)) return e;
+  if (int e = check_attn_common(pool, seq, q, q_dtype, n_q_heads, out, 0)) return e;
   if (pos0 < 0 || n_new < 0) return KV_ERR_RANGE;
   if (int e = check_range(pool, seq, 0, (int64_t)pos0 + n_new)) return e;
   if (n_new == 0) return KV_OK;

@@ -119,11 +119,16 @@ def test_validation_errors_before_launch(k8):
     # q4_0 needs no scale outputs
     assert L.kv_gather_runs(P(_pool(k8, fmt=2, ptrs=(16, 0, 48, 0))), P(seq), 0, 0, dummy, None,
                             dummy, None, None) == 0
-    # attention accepts the three formats, prefill only k8v4
+    # attention (decode, verify, prefill) accepts the three formats
     assert L.attn_decode(P(_pool(k8, fmt=2, ptrs=(16, 0, 48, 0))), P(seq), dummy, 0, 16, 65, 0.0,
                          out, dummy, 1 << 20, None) == -3
     assert L.attn_prefill_chunk(P(_pool(k8, fmt=1, ptrs=(16, 32, 48, 64))), P(seq), dummy, 0, 16, 0,
-                                1, 0.0, out, None, 0, None) == -5
+                                0, 0.0, out, None, 0, None) == 0
+    assert L.attn_prefill_chunk(P(_pool(k8, fmt=2, ptrs=(16, 0, 48, 0))), P(seq), dummy, 0, 16, 60,
+                                5, 0.0, out, None, 0, None) == -3
+    # the fused append + decode is k8v4 only
+    assert L.attn_decode_append(P(_pool(k8, fmt=1, ptrs=(16, 32, 48, 64))), P(seq), dummy, dummy, 0,
+                                dummy, 0, 16, 3, 0.0, out, dummy, 1 << 20, None) == -5
     # the streaming-read yardstick
     assert L.kv_probe_read(None, 1024, dummy, None) == -1
     assert L.kv_probe_read(dummy, 1024, None, None) == -1

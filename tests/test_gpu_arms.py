@@ -153,9 +153,46 @@ def test_arms_decode_32768_with_outlier_channels(orc, k8, dev, fmt):
     assert err <= TOL
 
 
-def test_arm_prefill_is_unsupported(k8, dev):
-    pool = k8.KvPool(FMT_INT8, 4, 16, 2, device=dev, fill=0)
-    pt = t_(np.arange(4, dtype=np.int32), dev)
-    q = t_(np.zeros((4, 16, 256), np.float16), dev)
-    with pytest.raises(k8.KvError):
-        k8.attn_prefill_chunk(pool, pt, q, 0)
+@pytest.mark.parametrize("fmt", [FMT_INT8, FMT_Q4_0])
+@pytest.mark.parametrize("n_new", [1, 17, 100])
+@pytest.mark.parametrize("qdtype", [np.float16, np.float32])
+def test_arm_prefill_parity(orc, k8, dev, fmt, n_new, qdtype):
+    """Prefill chunks over the comparison formats: q4_0 scores the rotated
+    query against rotated keys, int8 returns unrotated values."""
+    say(f"arm prefill fmt={fmt} n_new={n_new} q={qdtype.__name__}")
+    ctx = 1000
+    c = ArmCase(orc, k8, dev, fmt, 5, ctx, 16, 70, 64, dtype=np.float32)
+    pos0 = ctx - n_new
+    q = synth.queries(5, 0, 3, n_new, 16, 256, qdtype)
+    out = k8.attn_prefill_chunk(c.gpool, c.gpt, t_(q, dev), pos0).cpu().numpy()
+    ref = orc.attention_from_pool(c.opool, c.pt, q, [pos0 + i + 1 for i in range(n_new)])
+    err = rel_err(out, ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("fmt", [FMT_INT8, FMT_Q4_0])
+def test_arm_prefill_32768_outliers_matches_verify(orc, k8, dev, fmt):
+    """64 queries at the end of 32,768 cells with outlier channels: against
+    the oracle, and row by row against the verify kernel (same limits)."""
+    say(f"arm prefill 32768 fmt={fmt}")
+    ctx, n_new = 32768, 64
+    c = ArmCase(orc, k8, dev, fmt, 6, ctx, 256, 256, 128, outlier_frac=0.01)
+    pos0 = ctx - n_new
+    q = synth.queries(6, 0, 4, n_new, 16, 256, np.float16)
+    out = k8.attn_prefill_chunk(c.gpool, c.gpt, t_(q, dev), pos0).cpu().numpy()
+    rows = [0, 31, 63]
+    ref = orc.attention_from_pool(c.opool, c.pt, q[rows], [pos0 + i + 1 for i in rows])
+    err = rel_err(out[rows], ref)
+    say(f"  rel err vs oracle {err:.3e}")
+    assert err <= TOL
+    ws = k8.attn_workspace(c.gpool, 16, ctx)
+    ver = k8.attn_verify(c.gpool, c.gpt, t_(q[48:], dev), [pos0 + i + 1 for i in range(48, 64)],
+                         ws).cpu().numpy()
+    err_v = rel_err(ver[[15]], ref[[2]])
+    say(f"  verify rel err vs oracle (row 63) {err_v:.3e}")
+    assert err_v <= TOL
+    # two approximations of the same rows, each within TOL of the oracle
+    err2 = rel_err(out[48:], ver)
+    say(f"  rel diff vs verify {err2:.3e}")
+    assert err2 <= 2 * TOL
