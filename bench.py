@@ -457,6 +457,22 @@ def bench_extra(torch, k8, synth, dev, log):
     out["prefill_8192_at_231808"] = {"ms": round(p_ms, 3), "tflops": round(flops / p_ms / 1e9, 2),
                                      "mfma_frac": round(flops / p_ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
                                      "flop": flops}
+    # the same chunk over the comparison formats (one 240,000-cell pool each)
+    fm = {}
+    for fmt, name in ((1, "int8"), (2, "q4_0")):
+        log(f"extra: prefill chunk over a {name} pool ...")
+        pool = k8.KvPool(fmt, n_pages, P, 2, device=dev)
+        for c, s in enumerate(range(0, ctx, synth.CHUNK)):
+            n = min(synth.CHUNK, ctx - s)
+            kk, vv = synth.kv_chunk_device(4, 0, c, n, 2, 256, dev)
+            k8.kv_append(pool, tables[0], kk, vv, s)
+        k8.attn_prefill_chunk(pool, tables[0], qp, pos0, out=outp)
+        f_ms, _ = timed_launches(torch, k8, lambda i: k8.attn_prefill_chunk(
+            pool, tables[0], qp, pos0, out=outp), 2)
+        fm[name] = {"ms": round(f_ms, 3), "mfma_frac": round(flops / f_ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 4)}
+        del pool
+        torch.cuda.empty_cache()
+    out["prefill_8192_formats"] = fm
     out["formats_32768"] = bench_formats_32768(torch, k8, synth, dev, log)
     log(f"extra: {json.dumps(out)}")
     return out
