@@ -1,0 +1,84 @@
+"""Quantization error against depth (the pages' "no growth with depth"
+claim for the KV formats, tested without a model).
+
+The same seeded N(0,1) K/V (fp16) are appended to an int8, a k8v4 and a
+q4_0 pool of 240,000 cells; one decode query attends to the first n cells
+for n from 15,000 to 240,000.  Each GPU output is compared with the exact
+attention over the unquantized K/V (the oracle in fp64, no rotation).  The
+pages ("#729 KV int8 vs fp16 KLD compare at 240K context", the depth table
+and its remarks) report that int8 KV does not get worse with depth because
+the quantization noise of K and V averages out with the attention's
+averaging; here the relative error of each format must stay flat from 15K
+to 240K, and the formats must order by their bits (int8 < k8v4 < q4_0).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from long_context_decode_append_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEPTHS = [15000, 30000, 60000, 120000, 240000]
+FMTS = [(1, "int8"), (3, "k8v4"), (2, "q4_0")]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def rel_errs(out, ref):
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    mx = np.abs(out - ref).max(axis=-1) / np.abs(ref).max(axis=-1)
+    rms = np.sqrt(((out - ref) ** 2).mean(axis=-1) / (ref ** 2).mean(axis=-1))
+    return float(mx.max()), float(rms.mean())
+
+
+def test_error_does_not_grow_with_depth(orc):
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import long_context_decode_append_amd as k8
+    dev = torch.device("cuda:0")
+    ctx, P, seed = DEPTHS[-1], 256, 31
+    n_pages = (ctx + P - 1) // P
+    pt = synth.page_table(seed, n_pages, n_pages)
+    gpt = torch.from_numpy(pt).to(dev)
+    pools = {fmt: k8.KvPool(fmt, n_pages, P, 2, device=dev) for fmt, _ in FMTS}
+    ks, vs = [], []
+    for s in range(0, ctx, synth.CHUNK):
+        n = min(synth.CHUNK, ctx - s)
+        k, v = synth.kv_tokens(seed, 0, s, n, 2, 256, np.float16)
+        kt, vt = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
+        for fmt, _ in FMTS:
+            k8.kv_append(pools[fmt], gpt, kt, vt, s)
+        ks.append(k)
+        vs.append(v)
+    kd = np.concatenate(ks).astype(np.float64)
+    vd = np.concatenate(vs).astype(np.float64)
+    del ks, vs
+    q = synth.queries(seed, 0, 0, 1, 16, 256, np.float16)
+    qt = torch.from_numpy(q[0]).to(dev)
+    table = {name: [] for _, name in FMTS}
+    say("depth    " + "  ".join(f"{name:>22s}" for _, name in FMTS) + "   (max rel / mean rms rel)")
+    for n in DEPTHS:
+        ref = orc.attention(kd[:n], vd[:n], q, [n], v_rotated=False)[0]
+        row = []
+        for fmt, name in FMTS:
+            ws = k8.attn_workspace(pools[fmt], 1, n)
+            out = k8.attn_decode(pools[fmt], gpt, qt, n, ws).cpu().numpy()
+            e = rel_errs(out, ref)
+            table[name].append(e)
+            row.append(f"{e[0]:.3e} / {e[1]:.3e}")
+        say(f"{n:7d}  " + "  ".join(f"{r:>22s}" for r in row))
+    for _, name in FMTS:
+        rms = [e[1] for e in table[name]]
+        # flat: the deepest point within 1.5x of the shallowest, and no point
+        # more than 1.5x the median
+        assert rms[-1] <= 1.5 * rms[0], (name, rms)
+        assert max(rms) <= 1.5 * float(np.median(rms)), (name, rms)
+    for i in range(len(DEPTHS)):
+        assert table["int8"][i][1] < table["k8v4"][i][1] < table["q4_0"][i][1]
