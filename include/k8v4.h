@@ -235,6 +235,23 @@ int attn_decode_append(const kv_pool *pool, const kv_seq *seq, const void *k_new
                        float *out, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * One decode step for a batch of n_seq independent sequences in one launch
+ * sequence (the engine decodes two sequences at once in the RTX 5090 field
+ * report of "kv: --kv k8v4 streams with --kv-resident"): sequence i has its own page
+ * table seqs[i] into the shared pool and attends its query to its cells
+ * [0, n_ctx[i]).  Each sequence's output equals attn_decode on it alone,
+ * to rounding (the split plan differs).
+ *   seqs:  host array [n_seq] of tables into `pool`;  n_ctx: host [n_seq]
+ *   q:     device, [n_seq][n_q_heads][256];  out: device fp32 [n_seq][n_q_heads][256]
+ *   ws:    attn_workspace_bytes(pool, n_q_heads, n_seq, max n_ctx) bytes
+ *   1 <= n_seq <= 16.  Any format.
+ * Errors as attn_decode, plus KV_ERR_SHAPE for n_seq outside [1, 16].
+ */
+int attn_decode_batch(const kv_pool *pool, const kv_seq *seqs, int32_t n_seq, const void *q, int q_dtype,
+                      int n_q_heads, const int32_t *n_ctx, float scale, float *out, void *ws, size_t ws_bytes,
+                      void *stream);
+
+/*
  * Verify window of speculative decoding: n_q query rows read the cache
  * once, row i attending to cells [0, n_visible[i]) -- the batched form with
  * a per-query step array ("#120 --kv k8v4: hybrid KV cache", Tests).

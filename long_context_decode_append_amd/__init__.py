@@ -49,6 +49,7 @@ SIGNATURES = {
     "kv_gather_runs": (_I, [_PP, _PS, C.c_int32, C.c_int32, _P, _P, _P, _P, _P]),
     "attn_decode": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, _F, _P, _P, _SZ, _P]),
     "attn_decode_append": (_I, [_PP, _PS, _P, _P, _I, _P, _I, _I, C.c_int32, _F, _P, _P, _SZ, _P]),
+    "attn_decode_batch": (_I, [_PP, _PS, C.c_int32, _P, _I, _I, _P, _F, _P, _P, _SZ, _P]),
     "attn_verify": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, _P, _F, _P, _P, _SZ, _P]),
     "attn_prefill_chunk": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, C.c_int32, _F, _P, _P, _SZ, _P]),
     "kv_check_page_table": (_I, [_PP, _PS, C.c_int32, _P]),
@@ -314,6 +315,29 @@ def attn_decode_append(pool: K8V4Pool, page_table, k, v, q, pos: int, ws, scale:
                                   _dev_ptr(out, "out", (torch.float32,)), _dev_ptr(ws, "ws"),
                                   ws.numel(), _stream(stream))
     _check(rc, "attn_decode_append")
+    return out
+
+
+def attn_decode_batch(pool: KvPool, page_tables, q, n_ctx, ws, scale: float = 0.0, out=None,
+                      stream=None):
+    """A batch of sequences in one launch sequence: q [n_seq][Hq][256],
+    page_tables a list of n_seq int32 device tables, n_ctx a list of lengths
+    -> out fp32 [n_seq][Hq][256]."""
+    torch = _torch()
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [n_seq][n_q_heads][256]")
+    n_seq = int(q.shape[0])
+    if len(page_tables) != n_seq or len(n_ctx) != n_seq:
+        raise ValueError("one page table and one length per sequence")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    seqs = (KvSeqStruct * n_seq)(*[_seq(t) for t in page_tables])
+    lens = (C.c_int32 * n_seq)(*[int(x) for x in n_ctx])
+    rc = lib().attn_decode_batch(C.byref(pool.struct), seqs, n_seq, _dev_ptr(q, "q"), _dtype_code(q),
+                                 int(q.shape[1]), lens, float(scale),
+                                 _dev_ptr(out, "out", (torch.float32,)), _dev_ptr(ws, "ws"),
+                                 ws.numel(), _stream(stream))
+    _check(rc, "attn_decode_batch")
     return out
 
 

@@ -210,6 +210,40 @@ int attn_decode_append(const kv_pool *pool, const kv_seq *seq, const void *k_new
   return launch_attn_splitk(c);
 }
 
+int attn_decode_batch(const kv_pool *pool, const kv_seq *seqs, int32_t n_seq, const void *q, int q_dtype,
+                      int n_q_heads, const int32_t *n_ctx, float scale, float *out, void *ws, size_t ws_bytes,
+                      void *stream) {
+  if (!seqs || !n_ctx) return KV_ERR_NULL;
+  if (n_seq < 1 || n_seq > kMaxQ) return KV_ERR_SHAPE;
+  if (int e = check_attn_common(pool, &seqs[0], q, q_dtype, n_q_heads, out, 0)) return e;
+  if (!ws) return KV_ERR_WORKSPACE;
+  if (check_aligned16(ws)) return KV_ERR_ALIGN;
+  AttnCall c;
+  c.batch = true;
+  c.max_limit = 0;
+  for (int i = 0; i < kMaxQ; i++) c.limits[i] = 0;
+  for (int i = 0; i < n_seq; i++) {
+    if (int e = check_seq(&seqs[i], pool)) return e;
+    if (n_ctx[i] < 1) return KV_ERR_RANGE;
+    if (int e = check_range(pool, &seqs[i], 0, n_ctx[i])) return e;
+    c.limits[i] = n_ctx[i];
+    c.pts[i] = seqs[i].page_table;
+    if (n_ctx[i] > c.max_limit) c.max_limit = n_ctx[i];
+  }
+  c.pool = pool;
+  c.seq = &seqs[0];
+  c.q = q;
+  c.q_dtype = q_dtype;
+  c.n_q_heads = n_q_heads;
+  c.n_q = n_seq;
+  c.scale = pick_scale(scale);
+  c.out = out;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  c.stream = (hipStream_t)stream;
+  return launch_attn_splitk(c);
+}
+
 int attn_verify(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
                 int n_q_heads, int32_t n_q, const int32_t *n_visible, float scale, float *out,
                 void *ws, size_t ws_bytes, void *stream) {

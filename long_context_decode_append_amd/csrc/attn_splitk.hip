@@ -72,6 +72,10 @@ struct SplitArgs {
   const void *v_new;
   int kv_dtype;
   int append_pos;
+  // batch of sequences (decode of n_q independent sequences, 8 rows each):
+  // pass b reads table pts[b] over cells [0, limits[b])
+  int batch;
+  const int32_t *pts[kMaxQ];
 };
 
 // dim of output tile j held by column n of the PV MFMA.  q4_0 V: column n
@@ -116,8 +120,8 @@ struct Half {
 
 // page-table entry i through the constant address space: a scalar load
 // (the table is never written while a kernel reads it)
-__device__ __forceinline__ int pt_entry(const SplitArgs &a, int i) {
-  return ((const __attribute__((address_space(4))) int32_t *)a.pt)[i];
+__device__ __forceinline__ int pt_entry(const int32_t *pt, int i) {
+  return ((const __attribute__((address_space(4))) int32_t *)pt)[i];
 }
 
 __device__ __forceinline__ int page_of(const SplitArgs &a, int pos) {
@@ -153,10 +157,11 @@ __device__ __forceinline__ Half make_half(const SplitArgs &a, int g, int pos, in
 // the two halves of the step at c (c < c_end); page entries read here are
 // scalar loads
 template <int FMT>
-__device__ __forceinline__ void step_halves(const SplitArgs &a, int g, int c, int c_end, Half &h0, Half &h1) {
+__device__ __forceinline__ void step_halves(const SplitArgs &a, const int32_t *pt, int g, int c, int c_end, Half &h0,
+                                            Half &h1) {
   const int p1pos = (c + 16 < c_end) ? c + 16 : c;
-  const int pg0 = pt_entry(a, page_of(a, c));
-  const int pg1 = pt_entry(a, page_of(a, p1pos));
+  const int pg0 = pt_entry(pt, page_of(a, c));
+  const int pg1 = pt_entry(pt, page_of(a, p1pos));
   h0 = make_half<FMT>(a, g, c, pg0);
   h1 = make_half<FMT>(a, g, p1pos, pg1);
 }
@@ -165,7 +170,8 @@ __device__ __forceinline__ void step_halves(const SplitArgs &a, int g, int c, in
 // page-table entries are read together, so the kernel start waits for one
 // scalar round trip instead of two.
 template <int FMT>
-__device__ __forceinline__ void first_halves(const SplitArgs &a, int g, int c0, int c1, int c_end, Half &h0, Half &h1,
+__device__ __forceinline__ void first_halves(const SplitArgs &a, const int32_t *pt, int g, int c0, int c1, int c_end,
+                                             Half &h0, Half &h1,
                                              Half &n0, Half &n1) {
   const int pos[4] = {c0, (c0 + 16 < c_end) ? c0 + 16 : c0, c1, (c1 + 16 < c_end) ? c1 + 16 : c1};
   int pidx[4], pg[4];
@@ -174,7 +180,7 @@ __device__ __forceinline__ void first_halves(const SplitArgs &a, int g, int c0, 
   } else {
     for (int i = 0; i < 4; i++) pidx[i] = pos[i] / a.P;
   }
-  for (int i = 0; i < 4; i++) pg[i] = pt_entry(a, pidx[i]);
+  for (int i = 0; i < 4; i++) pg[i] = pt_entry(pt, pidx[i]);
   h0 = make_half<FMT>(a, g, pos[0], pg[0]);
   h1 = make_half<FMT>(a, g, pos[1], pg[1]);
   n0 = make_half<FMT>(a, g, pos[2], pg[2]);
@@ -194,7 +200,7 @@ __device__ __forceinline__ int q4_kslot(int t) { return (t & 4) | ((t & 1) << 1)
 template <bool QF32>
 __device__ __forceinline__ void append_token_partial(const SplitArgs &a, int g, int lane) {
   const int pos = a.append_pos;
-  const int page = pt_entry(a, page_of(a, pos));
+  const int page = pt_entry(a.pt, page_of(a, pos));
   const bool bad = page < 0 || page >= a.n_pages;
   const int slot = pos - page_of(a, pos) * a.P;
   const size_t tile = (size_t)(bad ? 0 : page) * a.H + g;
@@ -261,7 +267,10 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
   const int rows_here = min(a.rows_per_pass, a.n_rows - row_base);
 
   const int c_begin = split * a.steps_per_split * kStep;
-  const int c_end = min(a.max_limit, c_begin + a.steps_per_split * kStep);
+  // a batch of sequences: pass b is sequence b, with its own table and
+  // length (verify: every pass reads the one table up to the longest row)
+  const int32_t *const ptab = a.batch ? a.pts[pass] : a.pt;
+  const int c_end = min(a.batch ? a.limits[pass] : a.max_limit, c_begin + a.steps_per_split * kStep);
   const int stride = kWaves * kStep;
   const int c_first = c_begin + wave * kStep;
   const bool has_work = c_first < c_end;
@@ -351,7 +360,7 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
     // unconditional (a wave without work loads cell 0's step and never uses
     // it), so no control-flow join makes the compiler over-wait below
     const int cf = has_work ? c_first : 0, ce = has_work ? c_end : 16;
-    first_halves<FMT>(a, g, cf, has_work ? min(c_first + stride, c_last) : 0, ce, cur0, cur1, nxt0, nxt1);
+    first_halves<FMT>(a, ptab, g, cf, has_work ? min(c_first + stride, c_last) : 0, ce, cur0, cur1, nxt0, nxt1);
     const Half *hs[2] = {&cur0, &cur1};
     for (int h2 = 0; h2 < 2; h2++) {
       load_k(h2, *hs[h2]);
@@ -468,7 +477,7 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
     while (true) {
       // pages of the step after next
       Half nn0, nn1;
-      step_halves<FMT>(a, g, min(c + 2 * stride, c_last), c_end, nn0, nn1);
+      step_halves<FMT>(a, ptab, g, min(c + 2 * stride, c_last), c_end, nn0, nn1);
       const int badp[2] = {cur0.bad, cur1.bad};
       // whole step inside every valid row's limit and on valid pages: no
       // masking (rows past rows_here then hold harmless values that are never
@@ -812,10 +821,11 @@ int launch_attn_splitk(const AttnCall &c) {
   const int n_rows = c.n_q * kGqa;
   const bool qf32 = c.q_dtype == KV_DTYPE_F32;
   // one 16-row tile per workgroup; more rows run as passes (blockIdx.z) over
-  // the same splits, which share the split's KV reads through L2 / MALL
-  const int rows_per_pass = 16;
+  // the same splits, which share the split's KV reads through L2 / MALL; a
+  // batch runs one sequence (8 rows) per pass
+  const int rows_per_pass = c.batch ? kGqa : 16;
   const int passes = (n_rows + rows_per_pass - 1) / rows_per_pass;
-  if (passes > kMaxPasses) return KV_ERR_UNSUPPORTED;
+  if (passes > (c.batch ? kMaxQ : kMaxPasses)) return KV_ERR_UNSUPPORTED;
   if (c.max_limit > (1 << 30)) return KV_ERR_UNSUPPORTED;
   int target = attn_target_splits(H, n_rows) / passes;
   // passes of one split read the same cells: with splits x KV heads a
@@ -841,7 +851,9 @@ int launch_attn_splitk(const AttnCall &c) {
   a.ks = (const float *)pool->run[1];
   a.vq = (const uint8_t *)pool->run[2];
   a.vs = (const float *)pool->run[3];
-  a.pt = c.seq->page_table;
+  a.pt = c.batch ? c.pts[0] : c.seq->page_table;
+  a.batch = c.batch ? 1 : 0;
+  for (int i = 0; i < kMaxQ; i++) a.pts[i] = c.batch ? c.pts[i] : nullptr;
   a.q = c.q;
   a.out = c.out;
   a.part_ml = (float2 *)(base + ws.part_ml);
@@ -879,10 +891,14 @@ int launch_attn_splitk(const AttnCall &c) {
 
   dim3 grid(n_parts, H, passes);
   a.v_rotated = pool->fmt != KV_FMT_INT8;
-  // non-temporal KV loads for a single pass over a stream larger than half
-  // the 256 MB Infinity Cache (measured: 3 % faster at 240,000 cells, 1 %
-  // slower at 118,750, where the stream fits the cache)
-  const bool nt = passes == 1 && (size_t)c.max_limit * kv_cell_bytes(pool->fmt, H, kHeadDim) > ((size_t)128 << 20);
+  // non-temporal KV loads when no two passes share their reads and the
+  // stream is larger than half the 256 MB Infinity Cache (measured: 3 %
+  // faster at 240,000 cells, 1 % slower at 118,750, where the stream fits
+  // the cache; verify's row passes share their reads through L2)
+  size_t stream_cells = 0;
+  for (int i = 0; i < (c.batch ? c.n_q : 1); i++) stream_cells += (size_t)(c.batch ? c.limits[i] : c.max_limit);
+  const bool nt = (passes == 1 || c.batch) &&
+                  stream_cells * kv_cell_bytes(pool->fmt, H, kHeadDim) > ((size_t)128 << 20);
   switch (pool->fmt * 4 + (qf32 ? 2 : 0) + (nt ? 1 : 0)) {
 #define K8V4_SPLIT_CASE(F, Q, N) \
   case F * 4 + (Q ? 2 : 0) + (N ? 1 : 0): launch((attn_splitk_kernel<Q, F, N>), grid, dim3(256), c.stream, a); break;

@@ -53,6 +53,10 @@ struct AttnCall {
   const void *v_new = nullptr;
   int kv_dtype = 0;
   int append_pos = -1;
+  // batch decode: n_q independent sequences (8 rows each), sequence i with
+  // table pts[i] and length limits[i]; seq is then unused
+  bool batch = false;
+  const int32_t *pts[kMaxQ] = {};
 };
 int launch_attn_splitk(const AttnCall &c);
 

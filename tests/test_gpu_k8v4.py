@@ -420,3 +420,38 @@ def test_decode_append_32768_outliers(orc, k8, dev):
     err = rel_err(out.cpu().numpy(), ref)
     say(f"  rel err {err:.3e}")
     assert err <= TOL
+
+
+# ------------------------------------------------------------------ batched decode
+
+@pytest.mark.parametrize("lens", [[1024, 17, 600, 1], [333, 1024], [1000] * 16])
+def test_decode_batch_parity(orc, k8, dev, lens):
+    """Independent sequences with their own tables into one pool, one launch
+    sequence: each output against the oracle and against attn_decode alone."""
+    say(f"decode batch n_seq={len(lens)}")
+    import torch
+    n_seq, P, per = len(lens), 16, 64
+    n_pages = n_seq * per + 3
+    perm = synth.page_table(41, n_pages, n_pages)
+    gpool = k8.K8V4Pool(n_pages, P, 2, device=dev, fill=0xA5)
+    opool = orc.OraclePool(3, n_pages, P, 2, sentinel=0xA5)
+    tabs, gtabs = [], []
+    for b in range(n_seq):
+        pt = np.ascontiguousarray(perm[b * per:(b + 1) * per])
+        tabs.append(pt)
+        gtabs.append(t_(pt, dev))
+        k, v = synth.kv_tokens(50 + b, 0, 0, lens[b], 2, 256, np.float16)
+        k8.kv_append_k8v4(gpool, gtabs[b], t_(k, dev), t_(v, dev), 0)
+        opool.append(pt, k, v, 0)
+    q = synth.queries(42, 0, 0, n_seq, 16, 256, np.float16)
+    ws = k8.attn_workspace(gpool, n_seq, max(lens))
+    out = k8.attn_decode_batch(gpool, gtabs, t_(q, dev), lens, ws).cpu().numpy()
+    for b in range(n_seq):
+        ref = orc.attention_from_pool(opool, tabs[b], q[b:b + 1], [lens[b]])[0]
+        err = rel_err(out[b], ref)
+        ws1 = k8.attn_workspace(gpool, 1, lens[b])
+        one = k8.attn_decode(gpool, gtabs[b], t_(q[b], dev), lens[b], ws1).cpu().numpy()
+        err1 = rel_err(out[b], one)
+        say(f"  seq {b} len {lens[b]}: rel err {err:.3e}, vs single decode {err1:.3e}")
+        assert err <= TOL
+        assert err1 <= TOL
