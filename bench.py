@@ -446,6 +446,26 @@ def bench_extra(torch, k8, synth, dev, log):
     out["verify5_240000"] = {"us": round(v_ms * 1e3, 3), "gbs": round(b / v_ms / 1e6, 2),
                              "hbm_frac": round(b / v_ms / 1e6 / HBM_PEAK_GBS, 4),
                              "n_visible": nv}
+    # batched decode: 4 sequences of 59,904 cells (234 pages; their tables
+    # are quarters of each 240,000-cell table) in one call, against 4 single
+    # calls
+    nb, cb = 4, 234 * 256
+    pps = (cb + P - 1) // P
+    sub = [[tables[p][i * pps:(i + 1) * pps] for i in range(nb)] for p in range(n_pools)]
+    qb = synth.queries_device(4, 0, 1, nb, 16, 256, dev)
+    wsb = k8.attn_workspace(pools[0], nb, cb)
+    ms_b = graph_calls_ms(torch, lambda i: k8.attn_decode_batch(
+        pools[i % n_pools], sub[i % n_pools], qb, [cb] * nb, wsb), 2 * n_pools)
+    ws1b = k8.attn_workspace(pools[0], 1, cb)
+
+    def four_singles(i):
+        for j in range(nb):
+            k8.attn_decode(pools[i % n_pools], sub[i % n_pools][j], qb[j], cb, ws1b)
+    ms_s = graph_calls_ms(torch, four_singles, 2 * n_pools)
+    bb = nb * cb * CELL_BYTES
+    out["decode_batch_4x59904"] = {"us": round(ms_b * 1e3, 3), "gbs": round(bb / ms_b / 1e6, 2),
+                                   "hbm_frac": round(bb / ms_b / 1e6 / HBM_PEAK_GBS, 4),
+                                   "four_single_calls_us": round(ms_s * 1e3, 3)}
     # prefill chunk: 8,192 queries at [231,808, 240,000)
     pos0, n_new = 231808, 8192
     qp = synth.queries_device(5, 0, 0, n_new, 16, 256, dev)
