@@ -1,4 +1,4 @@
-// Split-K decode / verify attention over a k8v4 pool, for gfx950.
+// Split-K decode / verify attention over a paged pool, for gfx950.
 //
 // What it computes follows "#120 --kv k8v4: hybrid KV cache -- INT8 K +
 // Hadamard-rotated Q4_0 V (816 B/cell)", How and Tests: the fused attention
@@ -6,15 +6,19 @@
 // INT8 K (K = code * d per 128-dim group), runs a softmax over the visible
 // cells, accumulates the rotated Q4_0 V ((code - 8) * d16) and rotates the
 // result back with H/16; the batched (verify) form gives each query row its
-// own number of visible cells.
+// own number of visible cells.  The comparison formats of the same pages run
+// through the same kernel (template FMT): int8 (K and V INT8, no rotation)
+// and q4_0 (rotated K and V, scored against the rotated query).
 //
 // Mapping onto MI355X:
-//   * grid (splits, KV heads, row passes); a workgroup = 4 waves owns one
-//     contiguous logical cell range ("split") and one tile of 16 query rows
-//     (decode: the 8 heads of the KV head; verify: 2 queries per pass), its
-//     waves take 32-cell steps round robin, the loads of a wave's next step
-//     in flight while it computes the current one.  The split plan depends only on the context length, so
-//     identity and permuted page tables give bitwise-equal outputs.
+//   * grid (splits [+ 1 for a fused append], KV heads, row passes); a
+//     workgroup = 4 waves owns one contiguous logical cell range ("split")
+//     and one tile of 16 query rows (decode: the 8 heads of the KV head;
+//     verify: 2 queries per pass; a batch: one sequence per pass), its waves
+//     take 32-cell steps round robin, the loads of a wave's next step in
+//     flight while it computes the current one.  The split plan depends only
+//     on the context length, so identity and permuted page tables give
+//     bitwise-equal outputs.
 //   * per step a wave loads K codes / K scales / V nibbles / V scales
 //     straight into registers in the operand layouts of
 //     v_mfma_f32_16x16x32_f16 (16-byte K loads, 8-byte V loads), converts
@@ -33,6 +37,9 @@
 //     visible across XCDs (an in-kernel arrival-counter combine cost several
 //     device-scope round trips).  No float atomics: results are
 //     deterministic.
+//   * a fused append (decode of a k8v4 pool) adds one workgroup per KV head
+//     that quantizes the new token into its cell and writes it as one more
+//     partial, beside the streaming splits.
 #include <numeric>
 
 #include "device.hpp"
