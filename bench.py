@@ -494,8 +494,27 @@ def bench_extra(torch, k8, synth, dev, log):
         torch.cuda.empty_cache()
     out["prefill_8192_formats"] = fm
     out["formats_32768"] = bench_formats_32768(torch, k8, synth, dev, log)
+    out["page_copy_k8v4"] = bench_page_copy(torch, k8, pools[0], tables[0], dev, log)
     log(f"extra: {json.dumps(out)}")
     return out
+
+
+def bench_page_copy(torch, k8, pool, table, dev, log):
+    """The streamed cache's page moves (kv_copy_pages): 128 pages of 256
+    cells (26.7 MB of k8v4) between a pinned host mirror and device pools,
+    each direction graph-timed."""
+    n = 128
+    log("extra: page copies between host and device ...")
+    host = k8.KvPool(3, pool.n_pages, pool.page_size, pool.n_kv_heads, host=True)
+    win = k8.K8V4Pool(n, pool.page_size, pool.n_kv_heads, device=dev)
+    src = table[:n].contiguous()
+    slots = torch.arange(n, dtype=torch.int32, device=dev)
+    b = n * int(k8.lib().kv_cell_bytes(3, pool.n_kv_heads, 256)) * pool.page_size
+    d2h = graph_calls_ms(torch, lambda i: k8.kv_copy_pages(host, pool, src, src), 4)
+    h2d = graph_calls_ms(torch, lambda i: k8.kv_copy_pages(win, host, slots, src), 4)
+    d2d = graph_calls_ms(torch, lambda i: k8.kv_copy_pages(win, pool, slots, src), 4)
+    return {"bytes": b, "host_to_device_gbs": round(b / h2d / 1e6, 2),
+            "device_to_host_gbs": round(b / d2h / 1e6, 2), "device_to_device_gbs": round(b / d2d / 1e6, 2)}
 
 
 def bench_formats_32768(torch, k8, synth, dev, log):

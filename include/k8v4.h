@@ -183,6 +183,23 @@ size_t attn_workspace_bytes(const kv_pool *pool, int n_q_heads, int32_t n_q, int
  * `stream` (optional: the attention calls do not need it). */
 int kv_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Copy whole pages between two pools of the same format, KV-head count and
+ * page size ("kv: --kv k8v4 streams with --kv-resident", How: a streamed
+ * cache keeps all pages in host memory and a window in device memory, and
+ * moves a page as its byte runs -- three for k8v4): page src_pages[i] of src
+ * becomes page dst_pages[i] of dst, every run of it.  Either pool's runs may
+ * be device memory or mapped pinned host memory (hipHostMalloc); the copy is
+ * one kernel on `stream`.
+ *   dst_pages, src_pages: device int32 [n]; an entry outside its pool's
+ *   [0, n_pages) skips that pair.  No page may be both read and written.
+ * Errors: KV_ERR_NULL (a run of either pool, or a page list with n > 0),
+ * _UNSUPPORTED, _ALIGN, _SHAPE (pools that differ in format or shape),
+ * _RANGE (n < 0).  n == 0 is a no-op.
+ */
+int kv_copy_pages(const kv_pool *dst, const kv_pool *src, const int32_t *dst_pages, const int32_t *src_pages,
+                  int32_t n, void *stream);
+
 /* Measurement aid, not part of the method: one plain streaming read of the
  * first bytes / 16 16-byte words of buf (device, 16-byte aligned) with
  * non-temporal loads from 1,024 workgroups, the yardstick against which the

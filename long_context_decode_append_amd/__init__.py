@@ -45,6 +45,7 @@ SIGNATURES = {
     "attn_workspace_bytes": (_SZ, [_PP, _I, C.c_int32, C.c_int32]),
     "kv_workspace_init": (_I, [_P, _SZ, _P]),
     "kv_probe_read": (_I, [_P, _SZ, _P, _P]),
+    "kv_copy_pages": (_I, [_PP, _PP, _P, _P, C.c_int32, _P]),
     "kv_append": (_I, [_PP, _PS, _P, _P, _I, C.c_int32, C.c_int32, _P]),
     "kv_gather_runs": (_I, [_PP, _PS, C.c_int32, C.c_int32, _P, _P, _P, _P, _P]),
     "attn_decode": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, _F, _P, _P, _SZ, _P]),
@@ -136,11 +137,13 @@ def cell_bytes(fmt: int = KV_FMT_K8V4, n_kv_heads: int = 2, head_dim: int = HEAD
 
 
 class KvPool:
-    """A paged pool in device memory of format fmt (KV_FMT_INT8, KV_FMT_Q4_0
-    or KV_FMT_K8V4): its runs as the header lays them out."""
+    """A paged pool of format fmt (KV_FMT_INT8, KV_FMT_Q4_0 or KV_FMT_K8V4):
+    its runs as the header lays them out, in device memory, or with
+    host=True in pinned host memory (the host side of a streamed cache, for
+    kv_copy_pages only)."""
 
     def __init__(self, fmt: int, n_pages: int, page_size: int, n_kv_heads: int = 2, device="cuda",
-                 fill: int | None = None):
+                 fill: int | None = None, host: bool = False):
         torch = _torch()
         L = lib()
         self.n_pages, self.page_size, self.n_kv_heads = n_pages, page_size, n_kv_heads
@@ -151,7 +154,10 @@ class KvPool:
             if nb == 0:
                 self.runs.append(None)
                 continue
-            t = torch.empty(nb, dtype=torch.uint8, device=device)
+            if host:
+                t = torch.empty(nb, dtype=torch.uint8, pin_memory=True)
+            else:
+                t = torch.empty(nb, dtype=torch.uint8, device=device)
             if fill is not None:
                 t.fill_(fill)
             self.runs.append(t)
@@ -269,6 +275,20 @@ def attn_workspace(pool: KvPool, n_q: int, max_ctx: int, stream=None):
     ws = torch.empty(nb, dtype=torch.uint8, device=pool.runs[0].device)
     _check(lib().kv_workspace_init(_dev_ptr(ws, "ws"), nb, _stream(stream)), "kv_workspace_init")
     return ws
+
+
+def kv_copy_pages(dst: KvPool, src: KvPool, dst_pages, src_pages, stream=None) -> None:
+    """Copy page src_pages[i] of src to page dst_pages[i] of dst, every run
+    (device int32 page lists of one length; either pool may be host=True)."""
+    torch = _torch()
+    if dst_pages.dtype != torch.int32 or src_pages.dtype != torch.int32:
+        raise ValueError("page lists must be int32")
+    if dst_pages.numel() != src_pages.numel():
+        raise ValueError("page lists differ in length")
+    n = int(src_pages.numel())
+    _check(lib().kv_copy_pages(C.byref(dst.struct), C.byref(src.struct),
+                               _dev_ptr(dst_pages, "dst_pages"), _dev_ptr(src_pages, "src_pages"), n,
+                               _stream(stream)), "kv_copy_pages")
 
 
 def probe_read(buf, sink, stream=None):

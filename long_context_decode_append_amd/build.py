@@ -34,6 +34,7 @@ SOURCES = {
     "append_gather.hip": ["-ffp-contract=off"],
     "attn_splitk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "attn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "page_copy.hip": [],
     "api.cpp": ["-x", "hip"],
     "validate.cpp": ["-x", "hip"],
 }

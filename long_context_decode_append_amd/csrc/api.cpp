@@ -130,6 +130,18 @@ int kv_workspace_init(void *ws, size_t ws_bytes, void *stream) {
   return launch_fill_zero(ws, ws_bytes, (hipStream_t)stream);
 }
 
+int kv_copy_pages(const kv_pool *dst, const kv_pool *src, const int32_t *dst_pages, const int32_t *src_pages,
+                  int32_t n, void *stream) {
+  if (int e = check_pool(dst, 0)) return e;
+  if (int e = check_pool(src, 0)) return e;
+  if (dst->fmt != src->fmt || dst->n_kv_heads != src->n_kv_heads || dst->page_size != src->page_size)
+    return KV_ERR_SHAPE;
+  if (n < 0) return KV_ERR_RANGE;
+  if (n == 0) return KV_OK;
+  if (!dst_pages || !src_pages) return KV_ERR_NULL;
+  return launch_page_copy(dst, src, dst_pages, src_pages, n, (hipStream_t)stream);
+}
+
 int kv_probe_read(const void *buf, size_t bytes, void *sink, void *stream) {
   if (!buf || !sink) return KV_ERR_NULL;
   if (check_aligned16(buf) || check_aligned16(sink)) return KV_ERR_ALIGN;

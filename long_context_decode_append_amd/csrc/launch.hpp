@@ -29,6 +29,8 @@ int launch_append(const kv_pool *pool, const kv_seq *seq, const void *k, const v
                   int n, hipStream_t s);
 int launch_gather(const kv_pool *pool, const kv_seq *seq, int pos0, int n, void *const out[4], hipStream_t s);
 int launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+int launch_page_copy(const kv_pool *dst, const kv_pool *src, const int32_t *dst_pages, const int32_t *src_pages,
+                     int n, hipStream_t s);
 int launch_probe_read(const void *buf, size_t bytes, void *sink, hipStream_t s);
 
 // Decode / verify: n_q query rows of 8 heads per KV head, row i of query

@@ -129,6 +129,17 @@ def test_validation_errors_before_launch(k8):
     # the fused append + decode is k8v4 only
     assert L.attn_decode_append(P(_pool(k8, fmt=1, ptrs=(16, 32, 48, 64))), P(seq), dummy, dummy, 0,
                                 dummy, 0, 16, 3, 0.0, out, dummy, 1 << 20, None) == -5
+    # page copies: every run must be present (no silently skipped half), the
+    # two pools must match in format and shape
+    pl = C.c_void_p(64)
+    assert L.kv_copy_pages(P(_pool(k8, fmt=3, ptrs=(16, 32, 0, 0))), P(_pool(k8, fmt=3, ptrs=(16, 32, 48, 0))),
+                           pl, pl, 4, None) == -1
+    assert L.kv_copy_pages(P(_pool(k8, fmt=3, ptrs=(16, 32, 48, 0))), P(_pool(k8, fmt=1, ptrs=(16, 32, 48, 64))),
+                           pl, pl, 4, None) == -2
+    assert L.kv_copy_pages(P(_pool(k8, fmt=3, ptrs=(16, 32, 48, 0))), P(_pool(k8, fmt=3, ptrs=(16, 32, 48, 0))),
+                           None, pl, 4, None) == -1
+    assert L.kv_copy_pages(P(_pool(k8, fmt=3, ptrs=(16, 32, 48, 0))), P(_pool(k8, fmt=3, ptrs=(16, 32, 48, 0))),
+                           None, None, 0, None) == 0
     # the streaming-read yardstick
     assert L.kv_probe_read(None, 1024, dummy, None) == -1
     assert L.kv_probe_read(dummy, 1024, None, None) == -1
