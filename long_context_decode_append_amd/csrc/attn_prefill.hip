@@ -15,7 +15,8 @@
 //     dequantizes into LDS: INT8 K as exact fp16 codes (the two group scales
 //     applied to the two half-dots), q4_0 K as (code - 8) * d16, V as
 //     (code - 8) * d16 or code * d in fp16, stored transposed [dim][cell]
-//     (two cells per 4-byte write) so the P.V B-operand is two 8-byte reads;
+//     (two cells per 4-byte write, cells ordered so that the P.V B-operand
+//     of a lane is one 16-byte read);
 //   * two LDS tile buffers: tile i + 1 is dequantized into one while tile i
 //     is computed from the other, from registers loaded a tile earlier; the
 //     two waves of a SIMD take the halves in opposite order;
@@ -32,14 +33,18 @@ namespace k8v4 {
 constexpr int kPfWaves = 8;
 constexpr int kPfPos = kPfWaves * 16 / kGqa;  // query positions per workgroup (x 8 heads)
 constexpr int kPfTile = 32;                   // cells per tile
-constexpr int kKRow = 256 + 8;                // fp16 elements per K row in LDS (padded)
-constexpr int kVRow = kPfTile + 4;            // fp16 elements per transposed V row (72 bytes)
+constexpr int kKRow = 256 + 16;               // fp16 elements per K row in LDS (padded; measured best)
+constexpr int kVRow = kPfTile + 16;          // fp16 elements per transposed V row (16-byte multiple)
 constexpr int kVBlockPad = 32;                // fp16 elements after every 32 rows (one block)
 constexpr float kPfLazy = 8.0f;               // log2 headroom of the lazy softmax reference
 static_assert(kPfWaves * 64 == 512, "one tile load unit per thread");
 
 // offset of dim d0 + d (d0 a multiple of 32, 0 <= d < 32) in the V tile
 __device__ __forceinline__ int v_row(int d0, int d) { return (d0 + d) * kVRow + (d0 >> 5) * kVBlockPad; }
+// position of cell c (0..31) within a V row: the P.V B-operand of lane group
+// lg takes cells 4lg..4lg+3 and 16+4lg..16+4lg+3, stored side by side so one
+// 16-byte read fetches them (cells 2i, 2i+1 stay adjacent)
+__device__ __forceinline__ int v_pos(int c) { return 8 * ((c & 15) >> 2) + 4 * (c >> 4) + (c & 3); }
 
 struct PrefillArgs {
   const uint8_t *run[4];  // the pool's runs (format-dependent, as the header lays them out)
@@ -222,7 +227,7 @@ __device__ __forceinline__ void pf_store(const PfRaw &r, int u, _Float16 *lk, _F
     const f16x2 c72 = {(_Float16)72.0f, (_Float16)72.0f};
     const int b = (u >> 4) & 7, qq = u >> 7;
     const f16x2 dd = as_f16x2(r.vd);
-    _Float16 *vb = lv + v_row(32 * b, 4 * qq) + 2 * cp;  // element 4qq of block b
+    _Float16 *vb = lv + v_row(32 * b, 4 * qq) + v_pos(2 * cp);  // element 4qq of block b
     for (int e = 0; e < 4; e++) {
       // [a.byte, 0, b.byte, 0] for byte e of each cell: elements 4qq + e
       // (low nibbles) and 16 + 4qq + e (high nibbles)
@@ -236,7 +241,7 @@ __device__ __forceinline__ void pf_store(const PfRaw &r, int u, _Float16 *lk, _F
   } else {
     // INT8 V -> code * d rounded to fp16, transposed [dim][cell]
     const int dg = u >> 4;
-    _Float16 *vb = lv + v_row(32 * (dg >> 2), 8 * (dg & 3)) + 2 * cp;
+    _Float16 *vb = lv + v_row(32 * (dg >> 2), 8 * (dg & 3)) + v_pos(2 * cp);
     const uint32_t wa[2] = {r.va.x, r.va.y}, wb[2] = {r.vb.x, r.vb.y};
     for (int e = 0; e < 8; e++) {
       const float xa = (float)(int8_t)(wa[e >> 2] >> (8 * (e & 3))) * r.vsa;
@@ -405,10 +410,8 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
     // ---------------- O += P . V; B for dim tile j, column n: dim 16j + n,
     // k-slots = cells 4lg + 0..3 and 16 + 4lg + 0..3
     for (int j = 0; j < 16; j++) {
-      const _Float16 *vr = lv + v_row(32 * (j >> 1), 16 * (j & 1) + n) + 4 * lg;
-      const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr);
-      const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 16);
-      const f16x8 B = __builtin_bit_cast(f16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+      const _Float16 *vr = lv + v_row(32 * (j >> 1), 16 * (j & 1) + n) + 8 * lg;
+      const f16x8 B = *reinterpret_cast<const f16x8 *>(vr);
       o[j] = mfma16x16x32(pop, B, o[j]);
     }
   };
