@@ -8,6 +8,8 @@
  *    (816 B/cell)"  (sections What, How, Tests)  and
  *   "kv: --kv k8v4 streams with --kv-resident" (section How: a k8v4 block
  *    is moved as three byte runs -- K codes, K scales, V q4_0).
+ * The int8 and q4_0 formats those pages compare against run through the
+ * same entry points (kv_append, kv_gather_runs, attention).
  *
  * Conventions for every call below:
  *   - Pointers named "device" are HIP device memory owned by the caller;
@@ -171,11 +173,12 @@ int kv_gather_runs(const kv_pool *pool, const kv_seq *seq, int32_t pos0, int32_t
                    void *out1, void *out2, void *out3, void *stream);
 
 /*
- * Device workspace needed by attn_decode / attn_verify for n_q query rows
- * (1 for decode) over at most max_ctx cells: the split-K partial results.
- * Its contents need no initialization and are overwritten by every call;
- * calls that share a workspace must be ordered on one stream.  0 for an
- * unsupported request.
+ * Device workspace needed by attn_decode / attn_decode_append (n_q = 1),
+ * attn_verify (n_q queries) and attn_decode_batch (n_q = n_seq) over at
+ * most max_ctx cells: the split-K partial results (with room for the fused
+ * append's extra partial).  Its contents need no initialization and are
+ * overwritten by every call; calls that share a workspace must be ordered
+ * on one stream.  0 for an unsupported request.
  */
 size_t attn_workspace_bytes(const kv_pool *pool, int n_q_heads, int32_t n_q, int32_t max_ctx);
 
