@@ -267,6 +267,18 @@ def test_decode_118750_filled_in_chunks(orc, k8, dev):
     assert err <= TOL
     for r in range(3):
         assert np.array_equal(c.gpool.runs[r].cpu().numpy(), c.opool.runs[r])
+    # the bench step's call: the fused append of the token of cell 118,749
+    # over a pool holding cells [0, 118,749)
+    say("fused append + decode at 118,749")
+    d = Case(orc, k8, dev, 3, 118749, 256, 464, 464, chunk=8192)
+    k, v = synth.kv_tokens(3, 0, 118749, 1, 2, 256, np.float16)
+    out = k8.attn_decode_append(d.gpool, d.gpt, t_(k[0], dev), t_(v[0], dev), t_(q[0], dev), 118749, ws)
+    d.opool.append(d.pt, k, v, 118749)
+    for r in range(3):
+        assert np.array_equal(d.gpool.runs[r].cpu().numpy(), d.opool.runs[r])
+    err = rel_err(out.cpu().numpy(), d.oracle_attention(orc, q, [118750])[0])
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
 
 
 @pytest.mark.slow
