@@ -248,8 +248,11 @@ __device__ __forceinline__ void append_token_partial(const SplitArgs &a, int g, 
 // NT: the KV loads are non-temporal (a single pass reads each cell once, so
 // they should not displace other data from L2 / MALL; the row passes of a
 // verify share their reads through L2 and load normally)
-template <bool QF32, int FMT, bool NT>
-__global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) {
+// T: 16-row tiles per wave.  Verify runs T > 1: each step's K/V is loaded
+// and dequantized once and used for all T tiles (the accumulators of the
+// extra tiles spill into AGPRs, so one wave per SIMD).
+template <bool QF32, int FMT, bool NT, int T>
+__global__ __launch_bounds__(256, T == 1 ? 2 : 1) void attn_splitk_kernel(const SplitArgs a) {
   constexpr int kAux = NT ? 2 : 0;  // buffer-load cache policy bits: 2 = nt
   __shared__ __attribute__((aligned(16))) float lds_o[kWaves * 16 * 64 * 4];  // wave states, accumulator layout
   __shared__ __attribute__((aligned(16))) float lds_m[kWaves * 16];
@@ -340,26 +343,28 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
   };
   // the query loads go first: they depend only on the kernel arguments, so
   // their latency overlaps the page-table round trip of the first K/V loads
-  const int row = row_base + n;
-  const bool row_ok = n < rows_here;
-  int lim_row = a.limits[0];  // selects over the argument array keep it in scalar loads
-  for (int i = 1; i < kMaxQ; i++) lim_row = ((row >> 3) == i) ? a.limits[i] : lim_row;
-  const int lim_eff = min(row_ok ? lim_row : 0, c_end);
-  u32x4 qraw[QF32 ? 16 : 8];
-  {
+  bool row_ok[T];
+  int lim_eff[T];
+  u32x4 qraw[T][QF32 ? 16 : 8];
+  for (int t = 0; t < T; t++) {
+    const int row = row_base + 16 * t + n;
+    row_ok[t] = 16 * t + n < rows_here;
+    int lim_row = a.limits[0];  // selects over the argument array keep it in scalar loads
+    for (int i = 1; i < kMaxQ; i++) lim_row = ((row >> 3) == i) ? a.limits[i] : lim_row;
+    lim_eff[t] = min(row_ok[t] ? lim_row : 0, c_end);
     // padding rows read row_base's query (always present) and are zeroed
     // after the loads, which keeps the loads free of branches (so waiting
     // for them does not also wait for the K/V loads issued later)
-    const int rr = row_ok ? row : row_base;
+    const int rr = row_ok[t] ? row : row_base;
     const int qi = rr >> 3, hl = rr & 7;
     const size_t qbase = ((size_t)qi * a.n_q_heads + (size_t)g * kGqa + hl) * 256;
     for (int kk = 0; kk < 8; kk++) {
       const int d0 = 64 * (kk >> 1) + 16 * lg + 8 * (kk & 1);
       if (!QF32) {
-        qraw[kk] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.q) + qbase + d0);
+        qraw[t][kk] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.q) + qbase + d0);
       } else {
-        qraw[2 * kk] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const float *>(a.q) + qbase + d0);
-        qraw[2 * kk + 1] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const float *>(a.q) + qbase + d0 + 4);
+        qraw[t][2 * kk] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const float *>(a.q) + qbase + d0);
+        qraw[t][2 * kk + 1] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const float *>(a.q) + qbase + d0 + 4);
       }
     }
   }
@@ -384,19 +389,20 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
   // 64 (kk/2) + 16 lg + 8 (kk%2) + 0..7 (q4_0 K: in q4_kslot order).  The
   // q4_0 format scores against rotated keys, so q is rotated first,
   // q~ = H q / 16 (through this wave's part of lds_o).
-  f16x8 qop[8];
-  f16x8 qlo[QF32 ? 8 : 1];
-  float cbias[2] = {0.f, 0.f};
-  {
+  f16x8 qop[T][8];
+  f16x8 qlo[QF32 ? T : 1][QF32 ? 8 : 1];
+  float cbias[T][2];
+  for (int t = 0; t < T; t++) {
+    cbias[t][0] = cbias[t][1] = 0.f;
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
     float qv[8][8];
     for (int kk = 0; kk < 8; kk++) {
       if (!QF32) {
-        const f16x8 h = __builtin_bit_cast(f16x8, row_ok ? qraw[kk] : zero4);
+        const f16x8 h = __builtin_bit_cast(f16x8, row_ok[t] ? qraw[t][kk] : zero4);
         for (int e = 0; e < 8; e++) qv[kk][e] = (float)h[e];
       } else {
-        const f32x4 x0 = __builtin_bit_cast(f32x4, row_ok ? qraw[2 * kk] : zero4);
-        const f32x4 x1 = __builtin_bit_cast(f32x4, row_ok ? qraw[2 * kk + 1] : zero4);
+        const f32x4 x0 = __builtin_bit_cast(f32x4, row_ok[t] ? qraw[t][2 * kk] : zero4);
+        const f32x4 x1 = __builtin_bit_cast(f32x4, row_ok[t] ? qraw[t][2 * kk + 1] : zero4);
         for (int e = 0; e < 4; e++) {
           qv[kk][e] = x0[e];
           qv[kk][4 + e] = x1[e];
@@ -420,9 +426,9 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
         const int d0 = 64 * (kk >> 1) + 16 * lg + 8 * (kk & 1);
         const f32x4 x0 = *reinterpret_cast<const f32x4 *>(&qs[n * 256 + d0]);
         const f32x4 x1 = *reinterpret_cast<const f32x4 *>(&qs[n * 256 + d0 + 4]);
-        for (int t = 0; t < 8; t++) {
-          const int e = q4_kslot(t);
-          qv[kk][t] = e < 4 ? x0[e] : x1[e - 4];
+        for (int u = 0; u < 8; u++) {
+          const int e = q4_kslot(u);
+          qv[kk][u] = e < 4 ? x0[e] : x1[e - 4];
         }
       }
     }
@@ -443,23 +449,24 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
         }
       }
       if (kk < 4) s0 += ss; else s1 += ss;
-      qop[kk] = hi;
-      if (QF32) qlo[kk] = lo;
+      qop[t][kk] = hi;
+      if (QF32) qlo[t][kk] = lo;
     }
     if (kInt8K) {
       s0 += lane_xor(s0, 16);
       s0 += lane_xor(s0, 32);
       s1 += lane_xor(s1, 16);
       s1 += lane_xor(s1, 32);
-      cbias[0] = 1152.0f * s0;
-      cbias[1] = 1152.0f * s1;
+      cbias[t][0] = 1152.0f * s0;
+      cbias[t][1] = 1152.0f * s1;
     }
   }
   // smallest visible-cell limit over the valid rows of this tile (wave-
   // uniform): steps that end below it need no masking at all
   int lim_min;
   {
-    int lm = row_ok ? lim_eff : 0x7fffffff;
+    int lm = 0x7fffffff;
+    for (int t = 0; t < T; t++) lm = row_ok[t] ? min(lm, lim_eff[t]) : lm;
     for (int msk = 1; msk < 16; msk <<= 1) lm = min(lm, lane_xor(lm, msk));
     lim_min = __builtin_amdgcn_readfirstlane(lm);
   }
@@ -472,9 +479,13 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
   // entries are read two steps ahead.  The refill is unconditional (past the
   // end it re-reads the wave's last step) so every wait for current data
   // leaves the next step's loads outstanding.
-  float m = -1e30f, lsum = 0.f;
-  f32x4 o[16];
-  for (int j = 0; j < 16; j++) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[T], lsum[T];
+  f32x4 o[T][16];
+  for (int t = 0; t < T; t++) {
+    m[t] = -1e30f;
+    lsum[t] = 0.f;
+    for (int j = 0; j < 16; j++) o[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   const f16x2 c1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
   const f16x2 c72 = {(_Float16)72.0f, (_Float16)72.0f};
   const f16x2 c1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
@@ -493,9 +504,10 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
       const Half *nx[2] = {&nxt0, &nxt1};
 
       // ---- scores S^T = K . Q^T
-      float s[8];
+      float s[T][8];
       for (int h2 = 0; h2 < 2; h2++) {
-        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc0[T], acc1[T];
+        for (int t = 0; t < T; t++) acc0[t] = acc1[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int j = 0; j < 4; j++) {
           f16x8 ka, kb;
           if (kInt8K) {
@@ -522,39 +534,43 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
             ka = pack8(w[0], w[1], w[2], w[3]);
             kb = pack8(w[4], w[5], w[6], w[7]);
           }
-          if (!kInt8K || j < 2) {
-            acc0 = mfma16x16x32(ka, qop[2 * j], acc0);
-            acc0 = mfma16x16x32(kb, qop[2 * j + 1], acc0);
-            if (QF32) {
-              acc0 = mfma16x16x32(ka, qlo[2 * j], acc0);
-              acc0 = mfma16x16x32(kb, qlo[2 * j + 1], acc0);
-            }
-          } else {
-            acc1 = mfma16x16x32(ka, qop[2 * j], acc1);
-            acc1 = mfma16x16x32(kb, qop[2 * j + 1], acc1);
-            if (QF32) {
-              acc1 = mfma16x16x32(ka, qlo[2 * j], acc1);
-              acc1 = mfma16x16x32(kb, qlo[2 * j + 1], acc1);
+          for (int t = 0; t < T; t++) {
+            if (!kInt8K || j < 2) {
+              acc0[t] = mfma16x16x32(ka, qop[t][2 * j], acc0[t]);
+              acc0[t] = mfma16x16x32(kb, qop[t][2 * j + 1], acc0[t]);
+              if (QF32) {
+                acc0[t] = mfma16x16x32(ka, qlo[t][2 * j], acc0[t]);
+                acc0[t] = mfma16x16x32(kb, qlo[t][2 * j + 1], acc0[t]);
+              }
+            } else {
+              acc1[t] = mfma16x16x32(ka, qop[t][2 * j], acc1[t]);
+              acc1[t] = mfma16x16x32(kb, qop[t][2 * j + 1], acc1[t]);
+              if (QF32) {
+                acc1[t] = mfma16x16x32(ka, qlo[t][2 * j], acc1[t]);
+                acc1[t] = mfma16x16x32(kb, qlo[t][2 * j + 1], acc1[t]);
+              }
             }
           }
           // K chunk j of this half consumed: refill with the next step's
           kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + kstep_j * j, nx[h2]->k_soff, kAux);
         }
-        for (int i = 0; i < 4; i++) {
-          if (kInt8K) {
-            const f32x4 kq = ksr[h2][i >> 1];
-            const float d0 = kq[2 * (i & 1)], d1 = kq[2 * (i & 1) + 1];
-            s[4 * h2 + i] = a.scale2 * (d0 * (acc0[i] - cbias[0]) + d1 * (acc1[i] - cbias[1]));
-          } else {
-            s[4 * h2 + i] = a.scale2 * acc0[i];
-          }
-        }
-        if (!full_step) {
+        for (int t = 0; t < T; t++)
           for (int i = 0; i < 4; i++) {
-            const int cell = c + 16 * h2 + 4 * lg + i;
-            const float sv = cell < lim_eff ? s[4 * h2 + i] : -INFINITY;
-            s[4 * h2 + i] = badp[h2] ? __builtin_nanf("") : sv;
+            if (kInt8K) {
+              const f32x4 kq = ksr[h2][i >> 1];
+              const float d0 = kq[2 * (i & 1)], d1 = kq[2 * (i & 1) + 1];
+              s[t][4 * h2 + i] = a.scale2 * (d0 * (acc0[t][i] - cbias[t][0]) + d1 * (acc1[t][i] - cbias[t][1]));
+            } else {
+              s[t][4 * h2 + i] = a.scale2 * acc0[t][i];
+            }
           }
+        if (!full_step) {
+          for (int t = 0; t < T; t++)
+            for (int i = 0; i < 4; i++) {
+              const int cell = c + 16 * h2 + 4 * lg + i;
+              const float sv = cell < lim_eff[t] ? s[t][4 * h2 + i] : -INFINITY;
+              s[t][4 * h2 + i] = badp[h2] ? __builtin_nanf("") : sv;
+            }
         }
         load_ks(h2, *nx[h2]);
       }
@@ -562,30 +578,30 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
       // ---- online softmax against a reference max m that only moves when
       // a row's max exceeds it by more than 2^kLazy: p <= 2^kLazy stays exact
       // enough in fp16 and the accumulators are rarely rescaled
-      f16x8 pop;
-      {
-        float mx = s[0];
-        for (int e = 1; e < 8; e++) mx = fmaxf(mx, s[e]);
+      f16x8 pop[T];
+      for (int t = 0; t < T; t++) {
+        float mx = s[t][0];
+        for (int e = 1; e < 8; e++) mx = fmaxf(mx, s[t][e]);
         mx = fmaxf(mx, lane_xor(mx, 16));
         mx = fmaxf(mx, lane_xor(mx, 32));
-        if (__any(mx > m + kLazy)) {
-          const float mnew = fmaxf(m, mx);
-          const float alpha = fast_exp2(m - mnew);
-          lsum *= alpha;
-          m = mnew;
+        if (__any(mx > m[t] + kLazy)) {
+          const float mnew = fmaxf(m[t], mx);
+          const float alpha = fast_exp2(m[t] - mnew);
+          lsum[t] *= alpha;
+          m[t] = mnew;
           // O rows in the accumulator layout are 4*lg + i: fetch their factor
           float al[4];
           for (int i = 0; i < 4; i++) al[i] = lane_get(alpha, 4 * lg + i);
           for (int j = 0; j < 16; j++)
-            for (int i = 0; i < 4; i++) o[j][i] *= al[i];
+            for (int i = 0; i < 4; i++) o[t][j][i] *= al[i];
         }
         float ps = 0.f;
         for (int e = 0; e < 8; e++) {
-          const float p = fast_exp2(s[e] - m);
+          const float p = fast_exp2(s[t][e] - m[t]);
           ps += p;
-          pop[e] = (_Float16)p;
+          pop[t][e] = (_Float16)p;
         }
-        lsum += ps;
+        lsum[t] += ps;
       }
 
       // ---- O += P . V; the V scales of the cell pairs (k-slots 2k, 2k+1)
@@ -634,10 +650,10 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
             for (int h2 = 0; h2 < 2; h2++) load_v(h2, *nx[h2]);
           }
           const int jb = 2 * grp;
-          o[jb] = mfma16x16x32(pop, pack8(b0[0], b0[1], b0[2], b0[3]), o[jb]);          // tile jb     (byte lo nibble)
-          o[jb + 8] = mfma16x16x32(pop, pack8(b1[0], b1[1], b1[2], b1[3]), o[jb + 8]);  // tile jb + 8 (byte hi nibble)
-          o[jb + 1] = mfma16x16x32(pop, pack8(b2[0], b2[1], b2[2], b2[3]), o[jb + 1]);  // tile jb + 1
-          o[jb + 9] = mfma16x16x32(pop, pack8(b3[0], b3[1], b3[2], b3[3]), o[jb + 9]);  // tile jb + 9
+          for (int t = 0; t < T; t++) o[t][jb] = mfma16x16x32(pop[t], pack8(b0[0], b0[1], b0[2], b0[3]), o[t][jb]);          // tile jb     (byte lo nibble)
+          for (int t = 0; t < T; t++) o[t][jb + 8] = mfma16x16x32(pop[t], pack8(b1[0], b1[1], b1[2], b1[3]), o[t][jb + 8]);  // tile jb + 8 (byte hi nibble)
+          for (int t = 0; t < T; t++) o[t][jb + 1] = mfma16x16x32(pop[t], pack8(b2[0], b2[1], b2[2], b2[3]), o[t][jb + 1]);  // tile jb + 1
+          for (int t = 0; t < T; t++) o[t][jb + 9] = mfma16x16x32(pop[t], pack8(b3[0], b3[1], b3[2], b3[3]), o[t][jb + 9]);  // tile jb + 9
         }
       } else {
         // INT8 V: tile j holds dim 16 n + j; B = code * d in fp16, the code
@@ -653,7 +669,7 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
           if (j == 15) {
             for (int h2 = 0; h2 < 2; h2++) load_v(h2, *nx[h2]);
           }
-          o[j] = mfma16x16x32(pop, pack8(b[0], b[1], b[2], b[3]), o[j]);
+          for (int t = 0; t < T; t++) o[t][j] = mfma16x16x32(pop[t], pack8(b[0], b[1], b[2], b[3]), o[t][j]);
         }
       }
 
@@ -667,27 +683,30 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
   }
 
   // ---------------------------------------------------------------- workgroup merge
-  // every wave parks its state in LDS (accumulator layout), then all threads
-  // merge the 4 states element-wise in wave order
-  lsum += lane_xor(lsum, 16);
-  lsum += lane_xor(lsum, 32);
-  if (lg == 0) {
-    lds_m[wave * 16 + n] = m;
-    lds_l[wave * 16 + n] = lsum;
-  }
-  // lanes whose 4 rows are all padding (decode fills 8 of the 16) park nothing
-  if (4 * lg < rows_here)
-    for (int j = 0; j < 16; j++) *reinterpret_cast<f32x4 *>(&lds_o[((wave * 16 + j) * 64 + lane) * 4]) = o[j];
-  __syncthreads();
-
+  // per row tile, every wave parks its state in LDS (accumulator layout),
+  // then all threads merge the 4 states element-wise in wave order
   const size_t rows_total = (size_t)a.n_rows;
   const size_t sp = (size_t)g * a.n_parts + split;
-  {
+  for (int t = 0; t < T; t++) {
+    const int rows_t = rows_here - 16 * t;  // rows of this tile (may be <= 0)
+    if (t > 0) __syncthreads();              // the previous tile's readers are done
+    float lt = lsum[t];
+    lt += lane_xor(lt, 16);
+    lt += lane_xor(lt, 32);
+    if (lg == 0) {
+      lds_m[wave * 16 + n] = m[t];
+      lds_l[wave * 16 + n] = lt;
+    }
+    // lanes whose 4 rows are all padding (decode fills 8 of the 16) park nothing
+    if (4 * lg < rows_t)
+      for (int j = 0; j < 16; j++) *reinterpret_cast<f32x4 *>(&lds_o[((wave * 16 + j) * 64 + lane) * 4]) = o[t][j];
+    __syncthreads();
+
     // thread -> accumulator lane L and tiles 4 jq .. 4 jq + 3; the lane holds
     // rows 4 (L / 16) + i, i = 0..3, of each tile
     const int L = threadIdx.x & 63, jq = threadIdx.x >> 6;
     const int Ln = L & 15, Llg = L >> 4;
-    if (4 * Llg >= rows_here) return;  // rows 4 Llg .. 4 Llg + 3 are all padding
+    if (4 * Llg >= rows_t) continue;  // rows 4 Llg .. 4 Llg + 3 are all padding
     f32x4 mw[kWaves], lw[kWaves];
     for (int w = 0; w < kWaves; w++) {
       mw[w] = *reinterpret_cast<const f32x4 *>(&lds_m[w * 16 + 4 * Llg]);
@@ -711,12 +730,13 @@ __global__ __launch_bounds__(256, 2) void attn_splitk_kernel(const SplitArgs a) 
     }
     for (int i = 0; i < 4; i++) {
       const int r = 4 * Llg + i;
-      if (r >= rows_here) continue;
-      float *prow = a.part_o + (sp * rows_total + row_base + r) * 256;
+      if (r >= rows_t) continue;
+      const size_t grow = sp * rows_total + row_base + 16 * t + r;
+      float *prow = a.part_o + grow * 256;
       // tiles j, j+1 hold dims d, d+1 (j even)
       *reinterpret_cast<float2 *>(prow + o_dim<kQ4V>(Ln, 4 * jq)) = make_float2(val[0][i], val[1][i]);
       *reinterpret_cast<float2 *>(prow + o_dim<kQ4V>(Ln, 4 * jq + 2)) = make_float2(val[2][i], val[3][i]);
-      if (jq == 0 && Ln == 0) a.part_ml[sp * rows_total + row_base + r] = make_float2(M[i], Ls[i]);
+      if (jq == 0 && Ln == 0) a.part_ml[grow] = make_float2(M[i], Ls[i]);
     }
   }
 }
@@ -827,10 +847,14 @@ int launch_attn_splitk(const AttnCall &c) {
   const int H = pool->n_kv_heads;
   const int n_rows = c.n_q * kGqa;
   const bool qf32 = c.q_dtype == KV_DTYPE_F32;
-  // one 16-row tile per workgroup; more rows run as passes (blockIdx.z) over
-  // the same splits, which share the split's KV reads through L2 / MALL; a
-  // batch runs one sequence (8 rows) per pass
-  const int rows_per_pass = c.batch ? kGqa : 16;
+  // a workgroup takes T 16-row tiles (up to 3, half-precision queries: the
+  // extra accumulators leave no room for fp32 query halves); more rows run
+  // as passes (blockIdx.z) over the same splits, which share the split's KV
+  // reads through L2 / MALL; a batch runs one sequence (8 rows) per pass
+  const int tiles = (n_rows + 15) / 16;
+  const int tile_passes = (tiles + 2) / 3;
+  const int T = (c.batch || qf32) ? 1 : (tiles + tile_passes - 1) / tile_passes;
+  const int rows_per_pass = c.batch ? kGqa : 16 * T;
   const int passes = (n_rows + rows_per_pass - 1) / rows_per_pass;
   if (passes > (c.batch ? kMaxQ : kMaxPasses)) return KV_ERR_UNSUPPORTED;
   if (c.max_limit > (1 << 30)) return KV_ERR_UNSUPPORTED;
@@ -906,21 +930,24 @@ int launch_attn_splitk(const AttnCall &c) {
   for (int i = 0; i < (c.batch ? c.n_q : 1); i++) stream_cells += (size_t)(c.batch ? c.limits[i] : c.max_limit);
   const bool nt = (passes == 1 || c.batch) &&
                   stream_cells * kv_cell_bytes(pool->fmt, H, kHeadDim) > ((size_t)128 << 20);
-  switch (pool->fmt * 4 + (qf32 ? 2 : 0) + (nt ? 1 : 0)) {
-#define K8V4_SPLIT_CASE(F, Q, N) \
-  case F * 4 + (Q ? 2 : 0) + (N ? 1 : 0): launch((attn_splitk_kernel<Q, F, N>), grid, dim3(256), c.stream, a); break;
-    K8V4_SPLIT_CASE(KV_FMT_INT8, false, false)
-    K8V4_SPLIT_CASE(KV_FMT_INT8, false, true)
-    K8V4_SPLIT_CASE(KV_FMT_INT8, true, false)
-    K8V4_SPLIT_CASE(KV_FMT_INT8, true, true)
-    K8V4_SPLIT_CASE(KV_FMT_Q4_0, false, false)
-    K8V4_SPLIT_CASE(KV_FMT_Q4_0, false, true)
-    K8V4_SPLIT_CASE(KV_FMT_Q4_0, true, false)
-    K8V4_SPLIT_CASE(KV_FMT_Q4_0, true, true)
-    K8V4_SPLIT_CASE(KV_FMT_K8V4, false, false)
-    K8V4_SPLIT_CASE(KV_FMT_K8V4, false, true)
-    K8V4_SPLIT_CASE(KV_FMT_K8V4, true, false)
-    K8V4_SPLIT_CASE(KV_FMT_K8V4, true, true)
+  switch (((pool->fmt * 4 + (qf32 ? 2 : 0) + (nt ? 1 : 0)) << 2) + T) {
+#define K8V4_SPLIT_CASE(F, Q, N, T_) \
+  case ((F * 4 + (Q ? 2 : 0) + (N ? 1 : 0)) << 2) + T_: \
+    launch((attn_splitk_kernel<Q, F, N, T_>), grid, dim3(256), c.stream, a); \
+    break;
+#define K8V4_SPLIT_FMT(F)                \
+  K8V4_SPLIT_CASE(F, false, false, 1)    \
+  K8V4_SPLIT_CASE(F, false, true, 1)     \
+  K8V4_SPLIT_CASE(F, true, false, 1)     \
+  K8V4_SPLIT_CASE(F, true, true, 1)      \
+  K8V4_SPLIT_CASE(F, false, false, 2)    \
+  K8V4_SPLIT_CASE(F, false, true, 2)     \
+  K8V4_SPLIT_CASE(F, false, false, 3)    \
+  K8V4_SPLIT_CASE(F, false, true, 3)
+    K8V4_SPLIT_FMT(KV_FMT_INT8)
+    K8V4_SPLIT_FMT(KV_FMT_Q4_0)
+    K8V4_SPLIT_FMT(KV_FMT_K8V4)
+#undef K8V4_SPLIT_FMT
 #undef K8V4_SPLIT_CASE
     default: return KV_ERR_UNSUPPORTED;
   }
