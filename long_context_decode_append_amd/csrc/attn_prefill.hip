@@ -386,8 +386,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
     {
       float mx = s[0];
       for (int e = 1; e < 8; e++) mx = fmaxf(mx, s[e]);
-      mx = fmaxf(mx, lane_xor(mx, 16));
-      mx = fmaxf(mx, lane_xor(mx, 32));
+      mx = max_lg(mx);
       if (__any(mx > m + kPfLazy)) {
         const float mnew = fmaxf(m, mx);
         const float alpha = __builtin_amdgcn_exp2f(m - mnew);
@@ -442,8 +441,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
   // ---------------- epilogue: normalize, then (rotated V) the inverse
   // Walsh-Hadamard transform row by row through this wave's LDS slice (free
   // after the last barrier), and store
-  lsum += lane_xor(lsum, 16);
-  lsum += lane_xor(lsum, 32);
+  lsum = sum_lg(lsum);
   float inv[4];
   for (int i = 0; i < 4; i++) inv[i] = 1.0f / lane_get(lsum, 4 * lg + i);
   // value (row 4lg + i, dim 16j + n) lives in o[j][i]

@@ -60,11 +60,10 @@ struct SplitArgs {
   const void *q;
   float *out;
   float2 *part_ml;      // [H][splits][rows]: (m, l) of each split partial
-  float *part_o;        // [H][splits][rows][256]: unnormalized O (V's basis)
+  float *part_o;        // [H][splits][rows][256]: unnormalized O (unrotated basis)
   int n_pages, P, H;
   int p_shift;          // log2(P) when P is a power of two, else -1
   int k_bytes, ks_bytes, v_bytes, vs_bytes;  // run sizes (each < 2^31)
-  int v_rotated;        // V stored rotated: the combine applies H / 16
   int n_q_heads, n_rows, rows_per_pass;
   int limits[kMaxQ];
   int max_limit;
@@ -92,6 +91,14 @@ struct SplitArgs {
 template <bool kQ4V>
 __device__ __forceinline__ int o_dim(int n, int j) {
   return kQ4V ? 32 * (n >> 1) + 8 * (n & 1) + (j & 7) + 16 * (j >> 3) : 16 * n + j;
+}
+
+// LDS position of dim d in a merged 256-float row: bits 6 and 7 of d are
+// folded into bits 2 and 4, so the merge's stores (16 lanes of one row
+// 8 dims apart in bit 3 and 32 apart in bits 5..7) hit distinct banks; pairs
+// (d, d + 1), d even, and aligned quads stay together
+__device__ __forceinline__ int row_swz(int d) {
+  return d ^ (((d >> 6) & 1) << 2) ^ (((d >> 7) & 1) << 4);
 }
 
 __device__ __forceinline__ f16x8 pack8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -201,8 +208,8 @@ __device__ __forceinline__ int q4_kslot(int t) { return (t & 4) | ((t & 1) << 1)
 // Fused append of a decode (one wave, 4 dims per lane): quantize the new
 // token of KV head g with the append kernel's rules, store it into cell
 // append_pos, and write it as one more split partial of the 8 rows: m = its
-// score (q . K) * scale * log2(e) with K = code * d, l = 1, O = its rotated
-// V, (code - 8) * d rounded to fp16 as the streamed cells are.  A cell whose
+// score (q . K) * scale * log2(e) with K = code * d, l = 1, O = its V as
+// streamed cells see it ((code - 8) * d rounded to fp16), rotated back.  A cell whose
 // page-table entry is out of range is not written and gives the rows NaN.
 template <bool QF32>
 __device__ __forceinline__ void append_token_partial(const SplitArgs &a, int g, int lane) {
@@ -227,16 +234,16 @@ __device__ __forceinline__ void append_token_partial(const SplitArgs &a, int g, 
     store_q4(const_cast<uint8_t *>(a.vq), tile, a.P, slot, lane, vcodes, d16);
   }
   const _Float16 dh = __builtin_bit_cast(_Float16, d16);
-  float kd[4];
-  f32x4 vo;
+  float kd[4], vr[4];
   for (int i = 0; i < 4; i++) {
     kd[i] = (float)(int8_t)(kcodes >> (8 * i)) * dk;
-    vo[i] = (float)((_Float16)(float)((int)((vcodes >> (8 * i)) & 0xffu) - 8) * dh);
+    vr[i] = (float)((_Float16)(float)((int)((vcodes >> (8 * i)) & 0xffu) - 8) * dh);
   }
+  fwht256_lane4(vr, lane);  // partials are kept in the unrotated basis
+  const f32x4 vo = {vr[0], vr[1], vr[2], vr[3]};
   float dot[kGqa];
   for (int r = 0; r < kGqa; r++) dot[r] = qx[r][0] * kd[0] + qx[r][1] * kd[1] + qx[r][2] * kd[2] + qx[r][3] * kd[3];
-  for (int msk = 32; msk >= 1; msk >>= 1)
-    for (int r = 0; r < kGqa; r++) dot[r] += lane_xor(dot[r], msk);
+  for (int r = 0; r < kGqa; r++) dot[r] = wave_sum(dot[r]);
   const size_t rows_total = (size_t)a.n_rows;
   const size_t sp = (size_t)g * a.n_parts + a.n_splits;
   for (int r = 0; r < kGqa; r++) {
@@ -453,10 +460,8 @@ __global__ __launch_bounds__(256, T == 1 ? 2 : 1) void attn_splitk_kernel(const 
       if (QF32) qlo[t][kk] = lo;
     }
     if (kInt8K) {
-      s0 += lane_xor(s0, 16);
-      s0 += lane_xor(s0, 32);
-      s1 += lane_xor(s1, 16);
-      s1 += lane_xor(s1, 32);
+      s0 = sum_lg(s0);
+      s1 = sum_lg(s1);
       cbias[t][0] = 1152.0f * s0;
       cbias[t][1] = 1152.0f * s1;
     }
@@ -467,7 +472,10 @@ __global__ __launch_bounds__(256, T == 1 ? 2 : 1) void attn_splitk_kernel(const 
   {
     int lm = 0x7fffffff;
     for (int t = 0; t < T; t++) lm = row_ok[t] ? min(lm, lim_eff[t]) : lm;
-    for (int msk = 1; msk < 16; msk <<= 1) lm = min(lm, lane_xor(lm, msk));
+    lm = min(lm, lane_xor<1>(lm));
+    lm = min(lm, lane_xor<2>(lm));
+    lm = min(lm, lane_xor<4>(lm));
+    lm = min(lm, lane_xor<8>(lm));
     lim_min = __builtin_amdgcn_readfirstlane(lm);
   }
 
@@ -582,8 +590,7 @@ __global__ __launch_bounds__(256, T == 1 ? 2 : 1) void attn_splitk_kernel(const 
       for (int t = 0; t < T; t++) {
         float mx = s[t][0];
         for (int e = 1; e < 8; e++) mx = fmaxf(mx, s[t][e]);
-        mx = fmaxf(mx, lane_xor(mx, 16));
-        mx = fmaxf(mx, lane_xor(mx, 32));
+        mx = max_lg(mx);
         if (__any(mx > m[t] + kLazy)) {
           const float mnew = fmaxf(m[t], mx);
           const float alpha = fast_exp2(m[t] - mnew);
@@ -684,15 +691,17 @@ __global__ __launch_bounds__(256, T == 1 ? 2 : 1) void attn_splitk_kernel(const 
 
   // ---------------------------------------------------------------- workgroup merge
   // per row tile, every wave parks its state in LDS (accumulator layout),
-  // then all threads merge the 4 states element-wise in wave order
+  // then all threads merge the 4 states element-wise in wave order; the
+  // merged rows go back through LDS as plain rows, so each wave can take
+  // whole rows, undo the V rotation (H / 16 is its own inverse and linear,
+  // so the combine can sum partials in the unrotated basis) and store each
+  // row as one coalesced 1 KB write
   const size_t rows_total = (size_t)a.n_rows;
   const size_t sp = (size_t)g * a.n_parts + split;
   for (int t = 0; t < T; t++) {
     const int rows_t = rows_here - 16 * t;  // rows of this tile (may be <= 0)
     if (t > 0) __syncthreads();              // the previous tile's readers are done
-    float lt = lsum[t];
-    lt += lane_xor(lt, 16);
-    lt += lane_xor(lt, 32);
+    const float lt = sum_lg(lsum[t]);
     if (lg == 0) {
       lds_m[wave * 16 + n] = m[t];
       lds_l[wave * 16 + n] = lt;
@@ -706,74 +715,91 @@ __global__ __launch_bounds__(256, T == 1 ? 2 : 1) void attn_splitk_kernel(const 
     // rows 4 (L / 16) + i, i = 0..3, of each tile
     const int L = threadIdx.x & 63, jq = threadIdx.x >> 6;
     const int Ln = L & 15, Llg = L >> 4;
-    if (4 * Llg >= rows_t) continue;  // rows 4 Llg .. 4 Llg + 3 are all padding
-    f32x4 mw[kWaves], lw[kWaves];
-    for (int w = 0; w < kWaves; w++) {
-      mw[w] = *reinterpret_cast<const f32x4 *>(&lds_m[w * 16 + 4 * Llg]);
-      lw[w] = *reinterpret_cast<const f32x4 *>(&lds_l[w * 16 + 4 * Llg]);
-    }
-    f32x4 M = mw[0];
-    for (int w = 1; w < kWaves; w++)
-      for (int i = 0; i < 4; i++) M[i] = fmaxf(M[i], mw[w][i]);
-    f32x4 f[kWaves], Ls = {0.f, 0.f, 0.f, 0.f};
-    for (int w = 0; w < kWaves; w++)
-      for (int i = 0; i < 4; i++) {
-        f[w][i] = fast_exp2(mw[w][i] - M[i]);
-        Ls[i] += lw[w][i] * f[w][i];
+    const bool live = 4 * Llg < rows_t;  // rows 4 Llg .. 4 Llg + 3 not all padding
+    f32x4 val[4], M = {0.f, 0.f, 0.f, 0.f}, Ls = {0.f, 0.f, 0.f, 0.f};
+    if (live) {
+      f32x4 mw[kWaves], lw[kWaves];
+      for (int w = 0; w < kWaves; w++) {
+        mw[w] = *reinterpret_cast<const f32x4 *>(&lds_m[w * 16 + 4 * Llg]);
+        lw[w] = *reinterpret_cast<const f32x4 *>(&lds_l[w * 16 + 4 * Llg]);
       }
-    f32x4 val[4];
-    for (int jj = 0; jj < 4; jj++) {
-      const int j = 4 * jq + jj;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int w = 0; w < kWaves; w++) acc += f[w] * *reinterpret_cast<const f32x4 *>(&lds_o[((w * 16 + j) * 64 + L) * 4]);
-      val[jj] = acc;
+      M = mw[0];
+      for (int w = 1; w < kWaves; w++)
+        for (int i = 0; i < 4; i++) M[i] = fmaxf(M[i], mw[w][i]);
+      f32x4 f[kWaves];
+      for (int w = 0; w < kWaves; w++)
+        for (int i = 0; i < 4; i++) {
+          f[w][i] = fast_exp2(mw[w][i] - M[i]);
+          Ls[i] += lw[w][i] * f[w][i];
+        }
+      for (int jj = 0; jj < 4; jj++) {
+        const int j = 4 * jq + jj;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < kWaves; w++) acc += f[w] * *reinterpret_cast<const f32x4 *>(&lds_o[((w * 16 + j) * 64 + L) * 4]);
+        val[jj] = acc;
+      }
     }
-    for (int i = 0; i < 4; i++) {
-      const int r = 4 * Llg + i;
-      if (r >= rows_t) continue;
-      const size_t grow = sp * rows_total + row_base + 16 * t + r;
-      float *prow = a.part_o + grow * 256;
-      // tiles j, j+1 hold dims d, d+1 (j even)
-      *reinterpret_cast<float2 *>(prow + o_dim<kQ4V>(Ln, 4 * jq)) = make_float2(val[0][i], val[1][i]);
-      *reinterpret_cast<float2 *>(prow + o_dim<kQ4V>(Ln, 4 * jq + 2)) = make_float2(val[2][i], val[3][i]);
-      if (jq == 0 && Ln == 0) a.part_ml[grow] = make_float2(M[i], Ls[i]);
+    __syncthreads();  // the state reads above are done before lds_o holds rows
+    if (live) {
+      for (int i = 0; i < 4; i++) {
+        const int r = 4 * Llg + i;
+        if (r >= rows_t) continue;
+        // tiles j, j+1 hold dims d, d+1 (j even)
+        *reinterpret_cast<float2 *>(&lds_o[r * 256 + row_swz(o_dim<kQ4V>(Ln, 4 * jq))]) = make_float2(val[0][i], val[1][i]);
+        *reinterpret_cast<float2 *>(&lds_o[r * 256 + row_swz(o_dim<kQ4V>(Ln, 4 * jq + 2))]) = make_float2(val[2][i], val[3][i]);
+        if (jq == 0 && Ln == 0) a.part_ml[sp * rows_total + row_base + 16 * t + r] = make_float2(M[i], Ls[i]);
+      }
+    }
+    __syncthreads();
+    for (int r = wave; r < min(rows_t, 16); r += kWaves) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(&lds_o[r * 256 + row_swz(4 * lane)]);
+      float y[4] = {v[0], v[1], v[2], v[3]};
+      if (kQ4V) fwht256_lane4(y, lane);
+      *reinterpret_cast<f32x4 *>(a.part_o + (sp * rows_total + row_base + 16 * t + r) * 256 + 4 * lane) =
+          f32x4{y[0], y[1], y[2], y[3]};
     }
   }
 }
 
 // Combine of the split partials of one query row of one KV head, after the
-// split kernel (the kernel boundary makes every partial visible): the m of
-// all splits give the common max, each wave sums its strided share of the
-// O rows (loaded before they are needed) in ascending split order, the 8
-// wave sums add in fixed order, then O / l goes through the inverse
-// Walsh-Hadamard transform.  Deterministic for a given split plan.
-constexpr int kCombineWaves = 8;
-constexpr int kCombineBatch = 16;
+// split kernel (the kernel boundary makes every partial visible).  The
+// partials are in the unrotated basis, so the rows split into independent
+// 64-dim slices, one workgroup each: the m of all splits give the common
+// max, 16 split lanes of 16 threads (4 dims each) sum a strided share of the
+// slice rows (all loaded before they are needed) in ascending split order,
+// the lanes add in fixed order and O / l is stored.  Deterministic for a
+// given split plan.
+constexpr int kCombineWaves = 4;
+constexpr int kCombineParts = 4;                                    // 64-dim slices
+constexpr int kCombineLanes = kCombineWaves * 64 / 16;              // split lanes
+constexpr int kCombineBatch = kMaxSplitsPerHead / kCombineLanes;    // loads per thread
+static_assert(kCombineWaves * 64 >= kMaxSplitsPerHead, "one (m, l) per thread");
 
 __global__ __launch_bounds__(kCombineWaves * 64) void attn_combine_kernel(const SplitArgs a) {
   __shared__ float lds_w[kMaxSplitsPerHead];
   __shared__ float lds_red[kCombineWaves];
-  __shared__ f32x4 lds_acc[kCombineWaves][64];
-  const int row = blockIdx.x, g = blockIdx.y;
+  __shared__ f32x4 lds_acc[kCombineWaves][16];
+  const int row = blockIdx.x, g = blockIdx.y, part = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int dl = tid & 15, sl = tid >> 4;  // 4-dim lane, split lane
   const int S = a.n_parts;
   const size_t rows_total = (size_t)a.n_rows;
   const size_t base = (size_t)g * S;
-  const float *po = a.part_o + (base * rows_total + row) * 256 + 4 * lane;
+  const float *po = a.part_o + (base * rows_total + row) * 256 + 64 * part + 4 * dl;
   const size_t sstride = rows_total * 256;
 
-  // first batch of this wave's O rows, issued before the (m, l) pass
+  // this thread's slice rows, issued before the (m, l) pass
   f32x4 ov[kCombineBatch];
   for (int k = 0; k < kCombineBatch; k++) {
-    const int sidx = wave + kCombineWaves * k;
+    const int sidx = sl + kCombineLanes * k;
     if (sidx < S) ov[k] = *reinterpret_cast<const f32x4 *>(po + (size_t)sidx * sstride);
   }
   float2 ml = make_float2(-1e30f, 0.f);
   if (tid < S) ml = a.part_ml[(base + tid) * rows_total + row];
   // common max over the splits
   float mx = ml.x;
-  for (int msk = 32; msk >= 1; msk >>= 1) mx = fmaxf(mx, lane_xor(mx, msk));
+  mx = wave_max(mx);
   if (lane == 0) lds_red[wave] = mx;
   __syncthreads();
   float M = lds_red[0];
@@ -781,40 +807,31 @@ __global__ __launch_bounds__(kCombineWaves * 64) void attn_combine_kernel(const 
   const float wgt = tid < S ? fast_exp2(ml.x - M) : 0.f;
   if (tid < S) lds_w[tid] = wgt;
   float lw = wgt * ml.y;
-  for (int msk = 32; msk >= 1; msk >>= 1) lw += lane_xor(lw, msk);
+  lw = wave_sum(lw);
   __syncthreads();  // lds_red reads above are done before it is reused
   if (lane == 0) lds_red[wave] = lw;
   __syncthreads();
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int k = 0; k < kCombineBatch; k++) {
-    const int sidx = wave + kCombineWaves * k;
+    const int sidx = sl + kCombineLanes * k;
     if (sidx < S) acc += lds_w[sidx] * ov[k];
   }
-  for (int k0 = kCombineBatch; wave + kCombineWaves * k0 < S; k0 += kCombineBatch) {
-    for (int k = 0; k < kCombineBatch; k++) {
-      const int sidx = wave + kCombineWaves * (k0 + k);
-      if (sidx < S) ov[k] = *reinterpret_cast<const f32x4 *>(po + (size_t)sidx * sstride);
-    }
-    for (int k = 0; k < kCombineBatch; k++) {
-      const int sidx = wave + kCombineWaves * (k0 + k);
-      if (sidx < S) acc += lds_w[sidx] * ov[k];
-    }
+  // the 4 split lanes of a wave, then the waves
+  for (int i = 0; i < 4; i++) {
+    acc[i] = sum_lg(acc[i]);
   }
-  lds_acc[wave][lane] = acc;
+  if (lane < 16) lds_acc[wave][lane] = acc;
   __syncthreads();
-  if (wave != 0) return;
+  if (tid >= 16) return;
   float L = 0.f;
   for (int w = 0; w < kCombineWaves; w++) L += lds_red[w];
-  f32x4 tot = lds_acc[0][lane];
-  for (int w = 1; w < kCombineWaves; w++) tot += lds_acc[w][lane];
-  float y[4];
+  f32x4 tot = lds_acc[0][tid];
+  for (int w = 1; w < kCombineWaves; w++) tot += lds_acc[w][tid];
   const float inv = 1.0f / L;
-  for (int i = 0; i < 4; i++) y[i] = tot[i] * inv;
-  if (a.v_rotated) fwht256_lane4(y, lane);
   const int qi = row >> 3, hl = row & 7;
-  float *op = a.out + ((size_t)qi * a.n_q_heads + (size_t)g * kGqa + hl) * 256 + 4 * lane;
-  *reinterpret_cast<f32x4 *>(op) = f32x4{y[0], y[1], y[2], y[3]};
+  float *op = a.out + ((size_t)qi * a.n_q_heads + (size_t)g * kGqa + hl) * 256 + 64 * part + 4 * tid;
+  *reinterpret_cast<f32x4 *>(op) = f32x4{tot[0] * inv, tot[1] * inv, tot[2] * inv, tot[3] * inv};
 }
 
 // ---------------------------------------------------------------- host side
@@ -921,7 +938,6 @@ int launch_attn_splitk(const AttnCall &c) {
   a.append_pos = c.append_pos;
 
   dim3 grid(n_parts, H, passes);
-  a.v_rotated = pool->fmt != KV_FMT_INT8;
   // non-temporal KV loads when no two passes share their reads and the
   // stream is larger than half the 256 MB Infinity Cache (measured: 3 %
   // faster at 240,000 cells, 1 % slower at 118,750, where the stream fits
@@ -952,7 +968,7 @@ int launch_attn_splitk(const AttnCall &c) {
     default: return KV_ERR_UNSUPPORTED;
   }
   if (int e = launch_status()) return e;
-  launch(attn_combine_kernel, dim3(n_rows, H), dim3(kCombineWaves * 64), c.stream, a);
+  launch(attn_combine_kernel, dim3(n_rows, H, kCombineParts), dim3(kCombineWaves * 64), c.stream, a);
   return launch_status();
 }
 

@@ -12,9 +12,65 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Cross-lane exchange within a wave64 (ds_bpermute based).
-__device__ __forceinline__ float lane_xor(float x, int m) { return __shfl_xor(x, m, 64); }
-__device__ __forceinline__ int lane_xor(int x, int m) { return __shfl_xor(x, m, 64); }
+// x of lane (lane ^ M), M a power of two below 64, with every lane of the
+// wave active.  VALU only, no trip through the LDS crossbar: DPP inside
+// rows of 16 (quad_perm for 1 and 2; row_ror:n, which reads lane
+// (i - n) mod 16, for 4 and 8) and gfx950's permlane swaps across rows and
+// halves: swapping a value with itself leaves the lower row (half) in the
+// first result and the upper one in the second.
+template <int M>
+__device__ __forceinline__ int lane_xor(int x) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "lane_xor: M");
+  const int lane = __lane_id();
+  if constexpr (M == 1) {
+    return __builtin_amdgcn_mov_dpp(x, 0xb1, 0xf, 0xf, false);  // quad_perm [1, 0, 3, 2]
+  } else if constexpr (M == 2) {
+    return __builtin_amdgcn_mov_dpp(x, 0x4e, 0xf, 0xf, false);  // quad_perm [2, 3, 0, 1]
+  } else if constexpr (M == 4) {
+    const int up = __builtin_amdgcn_mov_dpp(x, 0x124, 0xf, 0xf, false);  // row_ror:4, lane i - 4
+    const int dn = __builtin_amdgcn_mov_dpp(x, 0x12c, 0xf, 0xf, false);  // row_ror:12, lane i + 4
+    return (lane & 4) ? up : dn;
+  } else if constexpr (M == 8) {
+    return __builtin_amdgcn_mov_dpp(x, 0x128, 0xf, 0xf, false);  // row_ror:8
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+    return (int)((lane & 16) ? r[0] : r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+    return (int)((lane & 32) ? r[0] : r[1]);
+  }
+}
+template <int M>
+__device__ __forceinline__ float lane_xor(float x) {
+  return __builtin_bit_cast(float, lane_xor<M>(__builtin_bit_cast(int, x)));
+}
+// Butterfly reductions over all 64 lanes and over the 16 lanes of one
+// 16-lane group (lanes sharing lane / 16).
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, lane_xor<32>(x));
+  x = fmaxf(x, lane_xor<16>(x));
+  x = fmaxf(x, lane_xor<8>(x));
+  x = fmaxf(x, lane_xor<4>(x));
+  x = fmaxf(x, lane_xor<2>(x));
+  return fmaxf(x, lane_xor<1>(x));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x += lane_xor<32>(x);
+  x += lane_xor<16>(x);
+  x += lane_xor<8>(x);
+  x += lane_xor<4>(x);
+  x += lane_xor<2>(x);
+  return x + lane_xor<1>(x);
+}
+// sum over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48
+__device__ __forceinline__ float sum_lg(float x) {
+  x += lane_xor<16>(x);
+  return x + lane_xor<32>(x);
+}
+__device__ __forceinline__ float max_lg(float x) {
+  x = fmaxf(x, lane_xor<16>(x));
+  return fmaxf(x, lane_xor<32>(x));
+}
 __device__ __forceinline__ float lane_get(float x, int src) { return __shfl(x, src, 64); }
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
@@ -54,6 +110,17 @@ __device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// one cross-lane butterfly of stride 4 M dims (lane stride M)
+template <int M>
+__device__ __forceinline__ void fwht_stage(float y[4], int lane) {
+#pragma clang fp contract(off)
+  const bool upper = (lane & M) != 0;
+  for (int i = 0; i < 4; i++) {
+    const float p = lane_xor<M>(y[i]);
+    y[i] = upper ? (p - y[i]) : (y[i] + p);
+  }
+}
+
 // Walsh-Hadamard transform of the 256 values held 4 per lane (lane l holds
 // dims 4l..4l+3): butterflies in ascending stride order 1, 2 (in-lane),
 // then 4..128 across lanes, each output one fp32 add or subtract (lower
@@ -65,13 +132,12 @@ __device__ __forceinline__ void fwht256_lane4(float y[4], int lane) {
   a = y[2]; b = y[3]; y[2] = a + b; y[3] = a - b;
   a = y[0]; b = y[2]; y[0] = a + b; y[2] = a - b;
   a = y[1]; b = y[3]; y[1] = a + b; y[3] = a - b;
-  for (int m = 1; m < 64; m <<= 1) {
-    const bool upper = (lane & m) != 0;
-    for (int i = 0; i < 4; i++) {
-      const float p = lane_xor(y[i], m);
-      y[i] = upper ? (p - y[i]) : (y[i] + p);
-    }
-  }
+  fwht_stage<1>(y, lane);
+  fwht_stage<2>(y, lane);
+  fwht_stage<4>(y, lane);
+  fwht_stage<8>(y, lane);
+  fwht_stage<16>(y, lane);
+  fwht_stage<32>(y, lane);
   for (int i = 0; i < 4; i++) y[i] = y[i] * 0.0625f;
 }
 

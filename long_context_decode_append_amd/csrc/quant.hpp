@@ -28,7 +28,11 @@ __device__ __forceinline__ void load4(const void *base, int dtype, size_t idx, f
 __device__ __forceinline__ uint32_t quant_k(const float x[4], float &d_out) {
 #pragma clang fp contract(off)
   float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
-  for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, lane_xor(amax, m));
+  amax = fmaxf(amax, lane_xor<16>(amax));
+  amax = fmaxf(amax, lane_xor<8>(amax));
+  amax = fmaxf(amax, lane_xor<4>(amax));
+  amax = fmaxf(amax, lane_xor<2>(amax));
+  amax = fmaxf(amax, lane_xor<1>(amax));
   const float d = amax / 127.0f;                 // correctly rounded division
   const float r = (d != 0.0f) ? 1.0f / d : 0.0f;
   uint32_t packed = 0;
@@ -54,12 +58,12 @@ __device__ __forceinline__ uint32_t quant_q4(const float y[4], int lane, uint16_
   }
   float bv = y[bi];
   int bidx = 4 * (lane & 7) + bi;
-  for (int m = 1; m < 8; m <<= 1) {
-    const float om = lane_xor(bm, m);
-    const float ov = lane_xor(bv, m);
-    const int oi = lane_xor(bidx, m);
+  auto take = [&](float om, float ov, int oi) {
     if (om > bm || (om == bm && oi < bidx)) { bm = om; bv = ov; bidx = oi; }
-  }
+  };
+  take(lane_xor<1>(bm), lane_xor<1>(bv), lane_xor<1>(bidx));
+  take(lane_xor<2>(bm), lane_xor<2>(bv), lane_xor<2>(bidx));
+  take(lane_xor<4>(bm), lane_xor<4>(bv), lane_xor<4>(bidx));
   const float d = bv / -8.0f;
   const float r = (d != 0.0f) ? 1.0f / d : 0.0f;
   uint32_t codes = 0;
@@ -86,7 +90,7 @@ __device__ __forceinline__ void store_int8(uint8_t *codes_run, uint8_t *scales_r
 // 4j..4j+3, lane j + 4 holds elements 16 + 4j..
 __device__ __forceinline__ void store_q4(uint8_t *run, size_t tile, int P, int slot, int lane, uint32_t codes,
                                          uint16_t d16) {
-  const uint32_t hi = (uint32_t)__shfl_xor((int)codes, 4, 64);
+  const uint32_t hi = (uint32_t)lane_xor<4>((int)codes);
   const int b = lane >> 3, j = lane & 7;
   uint8_t *vt = run + tile * 144 * P;
   if (j < 4) *reinterpret_cast<uint32_t *>(vt + (size_t)slot * 128 + b * 16 + 4 * j) = codes | (hi << 4);
