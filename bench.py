@@ -136,7 +136,26 @@ def stream_read_ceiling(torch, k8, dev):
     ms = graph_calls_ms(torch, lambda i: k8.probe_read(buf, sink), 5)
     del buf
     return {"gbs": round((1 << 30) / ms / 1e6, 1), "bytes": 1 << 30,
-            "kernel": "probe_read_kernel: 1,024 workgroups x 256 lanes, 4 x 16 B non-temporal loads in flight per lane"}
+            "kernel": "probe_read_kernel: 512 workgroups, each streaming its own contiguous 2 MiB with 256 lanes x 4 non-temporal 16 B loads per round"}
+
+
+def stream_read_same_size(torch, k8, dev, n_bufs=6):
+    """A plain streaming read of exactly one decode's KV bytes (118,750 and
+    240,000 cells x 816 B), one launch at a time over n_bufs rotated buffers
+    (beyond the Infinity Cache), timed like the split kernel (start/stop
+    events around each launch): what a single launch of that size attains,
+    start-up and tail included."""
+    out = {}
+    sink = torch.zeros(4096, dtype=torch.uint8, device=dev)
+    for cells in (118750, 240000):
+        b = cells * CELL_BYTES
+        bufs = [torch.empty(b, dtype=torch.uint8, device=dev).fill_(1) for _ in range(n_bufs)]
+        for i in range(n_bufs):
+            k8.probe_read(bufs[i], sink)
+        ms, _ = timed_launches(torch, k8, lambda i: k8.probe_read(bufs[i % n_bufs], sink), 8 * n_bufs)
+        out[str(cells)] = {"us": round(ms * 1e3, 3), "gbs": round(b / ms / 1e6, 1), "bytes": b}
+        del bufs
+    return out
 
 
 def cpu_baseline(ctx: int, target_s: float = 12.0):
@@ -179,9 +198,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", choices=["decode", "copy", "prefill", "verify"], default=None,
+    ap.add_argument("--only", choices=["decode", "decode240000", "copy", "prefill", "verify"], default=None,
                     help="profiling aids: 'decode' runs 24 eager fused append + decode calls at "
-                         "118,750 cells (8 layer pools); 'copy' runs 4 plain 1 GiB device copies "
+                         "118,750 cells (8 layer pools); 'decode240000' runs 12 decode calls at "
+                         "240,000 cells over 3 pools; 'copy' runs 4 plain 1 GiB device copies "
                          "(calibrates the HBM byte counters); 'prefill' runs the 8,192-query chunk "
                          "at 231,808 twice; 'verify' runs 4 five-query verify calls at 240,000")
     args = ap.parse_args()
@@ -284,6 +304,7 @@ def main():
         del graphs
         extra = bench_extra(torch, k8, synth, dev, log)
         extra["stream_read_ceiling"] = stream_read_ceiling(torch, k8, dev)
+        extra["stream_read_same_size"] = stream_read_same_size(torch, k8, dev)
         dc_ms = graph_calls_ms(torch, lambda i: k8.attn_decode(
             pools[i % layers], tables[i % layers], q_all[0][i % layers], ctx, ws,
             out=outs[i % layers]), layers, replays=2)
@@ -368,6 +389,22 @@ def profile_only(what, torch, k8, synth, dev):
                 k8.attn_verify(pool, pt, q, nv, ws)
             log(f"4 verify calls of 5 queries at {ctx}")
         torch.cuda.synchronize()
+        return
+    if what == "decode240000":
+        ctx, P, n_pages, n_pools = 240000, 256, 1024, 3
+        pools, tables = [], []
+        for i in range(n_pools):
+            pool = k8.K8V4Pool(n_pages, P, 2, device=dev)
+            pt = make_table(torch, synth, 4, i, (ctx + P - 1) // P, n_pages, dev)
+            fill_pool(k8, synth, pool, pt, 4, i, ctx, dev)
+            pools.append(pool)
+            tables.append(pt)
+        q = synth.queries_device(4, 0, 0, 1, 16, 256, dev)[0]
+        ws = k8.attn_workspace(pools[0], 1, ctx)
+        for i in range(4 * n_pools):
+            k8.attn_decode(pools[i % n_pools], tables[i % n_pools], q, ctx, ws)
+        torch.cuda.synchronize()
+        log(f"{4 * n_pools} decode calls at {ctx} cells over {n_pools} pools")
         return
     if what == "copy":
         n = 1 << 30

@@ -67,7 +67,12 @@ enum {
  * [physical page][kv head][slot], P = page_size slots per page, D = 256.
  *
  * k8v4 (fmt 3), 816 bytes per cell for 2 KV heads (408 per head):
- *   run[0] K codes  int8, byte ((page*H + g)*P + slot)*256 + c
+ *   run[0] K codes  int8, 256 per head-cell hc = (page*H + g)*P + slot,
+ *                   in 4096-byte blocks of 16 head-cells laid out
+ *                   [dim quarter][hc % 16][64 codes]: code c of hc at
+ *                   (hc/16)*4096 + (c/64)*1024 + (hc%16)*64 + c%64 (so a
+ *                   16-byte load per lane of 16 cells x 64 dims reads 1 KB
+ *                   of consecutive bytes)
  *   run[1] K scales fp32, element ((page*H + g)*P + slot)*2 + j, one scale
  *                   per 128 dims (j = c / 128)
  *   run[2] V q4_0   one tile of 144*P bytes per (page, head) at
@@ -85,9 +90,10 @@ enum {
  *
  * The comparison formats of the same pages ("#120", Measured) use the same
  * two kinds of half:
- * int8 (fmt 1), 1056 bytes per cell: run[0]/run[1] K codes/scales and
- *   run[2]/run[3] V codes/scales, each laid out like k8v4's run[0]/run[1]
- *   (V by the K rule, unrotated).
+ * int8 (fmt 1), 1056 bytes per cell: run[0]/run[1] K codes/scales laid out
+ *   like k8v4's and run[2]/run[3] V codes/scales (V by the K rule,
+ *   unrotated): V codes as plain rows, code c of hc at hc*256 + c, V scales
+ *   like the K scales.
  * q4_0 (fmt 2), 576 bytes per cell: run[0] K and run[2] V, each a q4_0 tile
  *   run like k8v4's run[2] (both halves rotated); run[1], run[3] unused.
  */
@@ -205,7 +211,8 @@ int kv_copy_pages(const kv_pool *dst, const kv_pool *src, const int32_t *dst_pag
 
 /* Measurement aid, not part of the method: one plain streaming read of the
  * first bytes / 16 16-byte words of buf (device, 16-byte aligned) with
- * non-temporal loads from 1,024 workgroups, the yardstick against which the
+ * non-temporal loads from 512 workgroups, each streaming its own contiguous
+ * share, the yardstick against which the
  * attention kernels' bytes per second are read.  sink: device, 16-byte
  * aligned, 4 KiB, written only in a case a repeated-byte fill cannot produce.
  * Returns KV_ERR_NULL / KV_ERR_ALIGN before launching. */

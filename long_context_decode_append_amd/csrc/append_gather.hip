@@ -57,14 +57,14 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
   } else {
     float d;
     const uint32_t codes = quant_k(x, d);
-    store_int8(a.run[0], a.run[1], cell, lane, codes, d);
+    store_int8<true>(a.run[0], a.run[1], cell, lane, codes, d);
   }
 
   load4(a.v, a.dtype, src, x);
   if (FMT == KV_FMT_INT8) {
     float d;
     const uint32_t codes = quant_k(x, d);
-    store_int8(a.run[2], a.run[3], cell, lane, codes, d);
+    store_int8<false>(a.run[2], a.run[3], cell, lane, codes, d);
   } else {
     fwht256_lane4(x, lane);
     uint16_t d16;
@@ -80,9 +80,11 @@ struct GatherArgs {
   int pos0, n, n_pages, P, H;
 };
 
+template <bool KLAYOUT>
 __device__ __forceinline__ void gather_int8(const uint8_t *codes_run, const uint8_t *scales_run, bool bad,
                                             size_t cell, size_t o, int lane, uint8_t *oc, uint8_t *os) {
-  uint32_t w = bad ? 0xffffffffu : *reinterpret_cast<const uint32_t *>(codes_run + cell * 256 + 4 * lane);
+  const size_t src = KLAYOUT ? k_code_off(cell, lane) : cell * 256 + 4 * lane;
+  uint32_t w = bad ? 0xffffffffu : *reinterpret_cast<const uint32_t *>(codes_run + src);
   *reinterpret_cast<uint32_t *>(oc + o * 256 + 4 * lane) = w;
   if (lane < 2)
     reinterpret_cast<float *>(os)[o * 2 + lane] =
@@ -117,8 +119,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
   const size_t o = (size_t)t * a.H + g;
   // an out-of-range table entry yields 0xff bytes / NaN scales, never a read outside the pool
   if (FMT == KV_FMT_Q4_0) gather_q4(a.run[0], bad, tile, a.P, slot, o, lane, a.out[0]);
-  else gather_int8(a.run[0], a.run[1], bad, cell, o, lane, a.out[0], a.out[1]);
-  if (FMT == KV_FMT_INT8) gather_int8(a.run[2], a.run[3], bad, cell, o, lane, a.out[2], a.out[3]);
+  else gather_int8<true>(a.run[0], a.run[1], bad, cell, o, lane, a.out[0], a.out[1]);
+  if (FMT == KV_FMT_INT8) gather_int8<false>(a.run[2], a.run[3], bad, cell, o, lane, a.out[2], a.out[3]);
   else gather_q4(a.run[2], bad, tile, a.P, slot, o, lane, a.out[2]);
 }
 
@@ -173,30 +175,33 @@ int launch_gather(const kv_pool *pool, const kv_seq *seq, int pos0, int n, void 
   return launch_status();
 }
 
-// Plain streaming read of `n16` 16-byte words (a bandwidth yardstick): each
-// lane keeps 4 non-temporal 16-byte loads in flight; one word per workgroup
-// is written only if the xor of everything read equals a value a fill with
-// a repeated byte cannot produce, so the loads are not optimized away.
+// Yardstick for attainable HBM read bandwidth: every workgroup streams its
+// own contiguous share of the buffer, its 256 lanes reading four
+// consecutive 4 KB blocks per round with non-temporal 16-byte loads.  (On
+// MI355X this pattern reads ~7.1 TB/s over GBs; a grid-stride pattern, where
+// all workgroups sweep one narrow window together, stays near 5.8 TB/s.)
+// One word per workgroup is written only if the xor of everything read
+// equals a value that a fill with a repeated byte cannot produce, so the
+// loads are not optimized away.
 __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4 *buf, size_t n16, u32x4 *sink) {
-  const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t nth = (size_t)gridDim.x * blockDim.x;
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t b0 = (size_t)blockIdx.x * per;
+  const size_t b1 = b0 + per < n16 ? b0 + per : n16;
   u32x4 acc = {0u, 0u, 0u, 0u};
-  size_t i = tid;
-  for (; i + 3 * nth < n16; i += 4 * nth) {
-    u32x4 v0 = __builtin_nontemporal_load(&buf[i]);
-    u32x4 v1 = __builtin_nontemporal_load(&buf[i + nth]);
-    u32x4 v2 = __builtin_nontemporal_load(&buf[i + 2 * nth]);
-    u32x4 v3 = __builtin_nontemporal_load(&buf[i + 3 * nth]);
-    acc ^= v0 ^ v1 ^ v2 ^ v3;
+  size_t i = b0 + threadIdx.x;
+  for (; i + 3 * 256 < b1; i += 4 * 256) {
+    u32x4 v[4];
+    for (int u = 0; u < 4; u++) v[u] = __builtin_nontemporal_load(&buf[i + 256 * u]);
+    for (int u = 0; u < 4; u++) acc ^= v[u];
   }
-  for (; i < n16; i += nth) acc ^= buf[i];
+  for (; i < b1; i += 256) acc ^= __builtin_nontemporal_load(&buf[i]);
   if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9e3779b9u) sink[blockIdx.x & 255] = acc;
 }
 
 int launch_probe_read(const void *buf, size_t bytes, void *sink, hipStream_t s) {
   const size_t n16 = bytes / 16;
   if (n16 == 0) return KV_OK;
-  launch(probe_read_kernel, dim3(1024), dim3(256), s, (const u32x4 *)buf, n16, (u32x4 *)sink);
+  launch(probe_read_kernel, dim3(512), dim3(256), s, (const u32x4 *)buf, n16, (u32x4 *)sink);
   return launch_status();
 }
 

@@ -123,8 +123,12 @@ __device__ __forceinline__ void pf_load(const PrefillArgs &a, const PfHalves &hv
   r.kd = a.scale2;
   if (FMT != KV_FMT_Q4_0) {
     const int cl = u >> 4, hf = cl >> 4;
+    // K-code run: 4 KB per 16 cells, [dim quarter][cell % 16][64 codes];
+    // a wave's 64 units read four 256-byte stretches
+    const int m = u & 15;
     if (c0 + cl < n_cells)
-      r.k = *reinterpret_cast<const u32x4 *>(a.run[0] + (hv.cell(hf) + (cl & 15)) * 256 + 16 * (u & 15));
+      r.k = *reinterpret_cast<const u32x4 *>(a.run[0] + hv.cell(hf) * 256 + (m >> 2) * 1024 + (cl & 15) * 64 +
+                                             16 * (m & 3));
     r.kd = 0.f;
     if (u < 2 * kPfTile) {
       const int cs = u >> 1, hs = cs >> 4;

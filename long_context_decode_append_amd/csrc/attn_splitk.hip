@@ -155,7 +155,7 @@ __device__ __forceinline__ Half make_half(const SplitArgs &a, int g, int pos, in
     h.k_soff = q4_tile + slot0 * 128;
     h.ks_soff = q4_tile + 128 * a.P + slot0 * 16;  // scale group slot0 / 16
   } else {
-    h.k_soff = cell * 256;
+    h.k_soff = cell * 256;  // = the start of the cell's 4 KB K-code block (cell % 16 == 0)
     h.ks_soff = cell * 8;
   }
   if (FMT == KV_FMT_INT8) {
@@ -229,7 +229,7 @@ __device__ __forceinline__ void append_token_partial(const SplitArgs &a, int g, 
   uint16_t d16;
   const uint32_t vcodes = quant_q4(y, lane, d16);
   if (!bad) {
-    store_int8(const_cast<uint8_t *>(reinterpret_cast<const uint8_t *>(a.kc)),
+    store_int8<true>(const_cast<uint8_t *>(reinterpret_cast<const uint8_t *>(a.kc)),
                const_cast<uint8_t *>(reinterpret_cast<const uint8_t *>(a.ks)), tile * a.P + slot, lane, kcodes, dk);
     store_q4(const_cast<uint8_t *>(a.vq), tile, a.P, slot, lane, vcodes, d16);
   }
@@ -301,16 +301,18 @@ __global__ __launch_bounds__(256, T == 1 ? 2 : 1) void attn_splitk_kernel(const 
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)a.vq, (short)0, a.v_bytes, kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc((void *)a.vs, (short)0, a.vs_bytes, kRsrcFlags);
   // lane-constant parts of the operand-layout loads
-  //   INT8 K:  + 64 j: 16 bytes (dims 64 j + 16 lg ..) of cell n
+  //   INT8 K:  + 1024 j: 16 bytes (dims 64 j + 16 lg ..) of cell n (the K-code
+  //            run's 16-cell blocks are [dim quarter][cell][64 codes], so
+  //            each of these loads reads 1 KB of consecutive bytes)
   //   q4_0 K:  + 32 j: the 16 nibble bytes of block 2 j + lg / 2 of cell n
   //            (low nibbles for even lg, high for odd), its scale at + 64 j
   //   q4_0 V:  + 128 i: bytes [8n, 8n+8) of cell 4lg+i; scales of block n/2
   //   INT8 V:  + 256 i: bytes [16n, 16n+16) of cell 4lg+i; scales of 4 cells
-  const int k_voff = kInt8K ? n * 256 + 16 * lg : n * 128 + 16 * (lg >> 1);
+  const int k_voff = kInt8K ? n * 64 + 16 * lg : n * 128 + 16 * (lg >> 1);
   const int ks_voff = kInt8K ? 32 * lg : 32 * (lg >> 1) + 2 * n;
   const int v_voff = kQ4V ? 4 * lg * 128 + 8 * n : 4 * lg * 256 + 16 * n;
   const int vd_voff = kQ4V ? (n >> 1) * 32 + 8 * lg : 32 * lg;
-  const int kstep_j = kInt8K ? 64 : 32;
+  const int kstep_j = kInt8K ? 1024 : 32;
   const uint32_t q4_shift = (lg & 1) ? 4u : 0u;  // q4_0 K: high nibbles for odd lg
   const int v8_grp = n >> 3;                     // INT8 V: scale group of this lane's dims
 

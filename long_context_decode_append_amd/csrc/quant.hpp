@@ -78,10 +78,21 @@ __device__ __forceinline__ uint32_t quant_q4(const float y[4], int lane, uint16_
   return codes;
 }
 
-// INT8 half of one head: codes [cell][256], fp32 scales [cell][2]
+// Byte of codes 4 lane .. 4 lane + 3 of head-cell `cell` in the K-code run:
+// every 16 head-cells form a 4 KB block [dim quarter][cell % 16][64 codes],
+// so the attention kernels' 16-byte operand loads (16 cells x 64 dims per
+// instruction) each read 1 KB of consecutive bytes.  (The page size is a
+// multiple of 16, so a block never straddles two (page, head) tiles.)
+__device__ __forceinline__ size_t k_code_off(size_t cell, int lane) {
+  return (cell >> 4) * 4096 + (size_t)(lane >> 4) * 1024 + (cell & 15) * 64 + (size_t)(lane & 15) * 4;
+}
+
+// INT8 half of one head: fp32 scales [cell][2]; codes in the K-code layout
+// (KLAYOUT) or as a plain [cell][256] row (the int8 format's V)
+template <bool KLAYOUT>
 __device__ __forceinline__ void store_int8(uint8_t *codes_run, uint8_t *scales_run, size_t cell, int lane,
                                            uint32_t codes, float d) {
-  *reinterpret_cast<uint32_t *>(codes_run + cell * 256 + 4 * lane) = codes;
+  *reinterpret_cast<uint32_t *>(codes_run + (KLAYOUT ? k_code_off(cell, lane) : cell * 256 + 4 * lane)) = codes;
   if ((lane & 31) == 0) reinterpret_cast<float *>(scales_run)[cell * 2 + (lane >> 5)] = d;
 }
 

@@ -164,6 +164,10 @@ class OraclePool:
     run 1: K scales (2 x fp32 per head-cell)
     run 2: V q4_0 tile (k8v4, q4_0) or V codes (int8 format)
     run 3: V scales (int8 format only)
+    K codes of head-cell hc = (page*H + head)*P + slot: each group of 16
+    head-cells is a 4096-byte block [dim quarter][hc % 16][64 codes], code c
+    at (hc//16)*4096 + (c//64)*1024 + (hc%16)*64 + c%64 (P a multiple of
+    16).  INT8 V codes (int8 format) are plain rows, code c at hc*256 + c.
     A q4_0 (page, head) tile is 144*P bytes: nibble bytes of block b of slot s
     at s*128 + b*16; the fp16 scale of block b of slot s at
     128*P + (s//16)*256 + b*32 + (s%16)*2 (scales grouped by 16 slots).

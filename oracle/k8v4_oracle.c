@@ -194,6 +194,11 @@ long orc_cell_bytes(int fmt, int n_kv_heads, int D) {
 /* slot s at s*128 + b*16; the fp16 scales after the 128*P nibble     */
 /* bytes, in groups of 16 slots (256 bytes each, [block][slot % 16]):  */
 /* block b of slot s at 128*P + (s/16)*256 + b*32 + (s%16)*2.          */
+/* K codes: head-cell hc = (page*H + head)*P + slot; each group of 16   */
+/* head-cells is a 4096-byte block [dim quarter][hc % 16][64 codes]:    */
+/* code c of hc at (hc/16)*4096 + (c/64)*1024 + (hc%16)*64 + c%64.      */
+/* (INT8 V codes of the int8 format stay [hc][256].)  P must be a       */
+/* multiple of 16, so a 16-cell group never straddles two tiles.        */
 /* ------------------------------------------------------------------ */
 
 typedef struct {
@@ -203,11 +208,22 @@ typedef struct {
 
 static size_t tile_index(int page, int g, int H) { return (size_t)page * H + g; }
 
+static size_t k_code_pos(size_t hc, int c) {
+  return (hc / 16) * 4096 + (size_t)(c / 64) * 1024 + (hc % 16) * 64 + (size_t)(c % 64);
+}
+
+/* one head's INT8 codes and scales; k_layout: codes in the K-code layout */
+/* above, else as a plain [hc][256] row                                 */
 static void put_int8_head(uint8_t *codes_run, uint8_t *scales_run, size_t ti, int P, int slot,
-                          const int8_t *codes, const float *scales) {
-  memcpy(codes_run + (ti * P + slot) * ORC_D, codes, ORC_D);
-  memcpy(scales_run + ((ti * P + slot) * (ORC_D / ORC_KGROUP)) * 4, scales,
-         4 * (ORC_D / ORC_KGROUP));
+                          const int8_t *codes, const float *scales, int k_layout) {
+  const size_t hc = ti * P + slot;
+  for (int c = 0; c < ORC_D; c++)
+    codes_run[k_layout ? k_code_pos(hc, c) : hc * ORC_D + c] = (uint8_t)codes[c];
+  memcpy(scales_run + (hc * (ORC_D / ORC_KGROUP)) * 4, scales, 4 * (ORC_D / ORC_KGROUP));
+}
+
+static void get_int8_codes(const uint8_t *codes_run, size_t hc, int k_layout, uint8_t *out) {
+  for (int c = 0; c < ORC_D; c++) out[c] = codes_run[k_layout ? k_code_pos(hc, c) : hc * ORC_D + c];
 }
 
 static size_t q4_scale_pos(int P, int slot, int b) {
@@ -255,7 +271,7 @@ static void quant_rot_q4(const float *x, uint8_t *blocks) {
 int orc_append(int fmt, int n_pages, int P, int H, uint8_t *run0, uint8_t *run1, uint8_t *run2,
                uint8_t *run3, const int32_t *pt, int n_table, const void *k, const void *v,
                int dtype, int pos0, int n) {
-  if (pos0 < 0 || n < 0 || (long)pos0 + n > (long)n_table * P) return -1;
+  if (P <= 0 || P % 16 || pos0 < 0 || n < 0 || (long)pos0 + n > (long)n_table * P) return -1;
   float kx[ORC_D], vx[ORC_D];
   int8_t codes[ORC_D];
   float scales[ORC_D / ORC_KGROUP];
@@ -273,14 +289,14 @@ int orc_append(int fmt, int n_pages, int P, int H, uint8_t *run0, uint8_t *run1,
       size_t ti = tile_index(page, g, H);
       if (fmt == 3) {
         quant_k_int8(kx, codes, scales);
-        put_int8_head(run0, run1, ti, P, slot, codes, scales);
+        put_int8_head(run0, run1, ti, P, slot, codes, scales, 1);
         quant_rot_q4(vx, blocks);
         put_q4_head(run2, ti, P, slot, blocks);
       } else if (fmt == 1) {
         quant_k_int8(kx, codes, scales);
-        put_int8_head(run0, run1, ti, P, slot, codes, scales);
+        put_int8_head(run0, run1, ti, P, slot, codes, scales, 1);
         quant_k_int8(vx, codes, scales);
-        put_int8_head(run2, run3, ti, P, slot, codes, scales);
+        put_int8_head(run2, run3, ti, P, slot, codes, scales, 0);
       } else if (fmt == 2) {
         quant_rot_q4(kx, blocks);
         put_q4_head(run0, ti, P, slot, blocks);
@@ -306,7 +322,7 @@ int orc_append(int fmt, int n_pages, int P, int H, uint8_t *run0, uint8_t *run1,
 int orc_gather(int fmt, int n_pages, int P, int H, const uint8_t *run0, const uint8_t *run1,
                const uint8_t *run2, const uint8_t *run3, const int32_t *pt, int n_table,
                int pos0, int n, uint8_t *out0, uint8_t *out1, uint8_t *out2, uint8_t *out3) {
-  if (pos0 < 0 || n < 0 || (long)pos0 + n > (long)n_table * P) return -1;
+  if (P <= 0 || P % 16 || pos0 < 0 || n < 0 || (long)pos0 + n > (long)n_table * P) return -1;
   const size_t nsc = ORC_D / ORC_KGROUP;
   const size_t qb = (ORC_D / ORC_QBLK) * ORC_QBYTES;
   for (int t = 0; t < n; t++) {
@@ -318,13 +334,13 @@ int orc_gather(int fmt, int n_pages, int P, int H, const uint8_t *run0, const ui
       size_t o = (size_t)t * H + g;
       size_t cell = ti * P + slot;
       if (fmt == 1 || fmt == 3) {
-        memcpy(out0 + o * ORC_D, run0 + cell * ORC_D, ORC_D);
+        get_int8_codes(run0, cell, 1, out0 + o * ORC_D);
         memcpy(out1 + o * nsc * 4, run1 + cell * nsc * 4, nsc * 4);
       } else {
         get_q4_head(run0, ti, P, slot, out0 + o * qb);
       }
       if (fmt == 1) {
-        memcpy(out2 + o * ORC_D, run2 + cell * ORC_D, ORC_D);
+        get_int8_codes(run2, cell, 0, out2 + o * ORC_D);
         memcpy(out3 + o * nsc * 4, run3 + cell * nsc * 4, nsc * 4);
       } else {
         get_q4_head(run2, ti, P, slot, out2 + o * qb);

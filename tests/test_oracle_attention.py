@@ -57,7 +57,9 @@ def test_pool_bytes_at_documented_offsets(orc):
         page, slot = pt[p // P], p % P
         for g in range(H):
             cell = (page * H + g) * P + slot
-            assert np.array_equal(r0[cell * 256:(cell + 1) * 256].view(np.int8), kc[p, g])
+            # K codes: 16-cell blocks of 4 KB, [dim quarter][cell % 16][64 codes]
+            kpos = (cell // 16) * 4096 + (np.arange(256) // 64) * 1024 + (cell % 16) * 64 + np.arange(256) % 64
+            assert np.array_equal(r0[kpos].view(np.int8), kc[p, g])
             assert np.array_equal(r1[cell * 8:(cell + 1) * 8].view(np.float32), ks[p, g])
             tile = (page * H + g) * 144 * P
             for b in range(8):
@@ -85,12 +87,13 @@ def test_unwritten_cells_keep_sentinel_and_wrong_table_is_detected(orc):
     P = 16
     pool, pt, _, _ = _pool_with(orc, 3, P=P, n_pages=10, n_table=6, n_tok=40, seed=4)
     used = set(int(x) for x in pt[:3])            # 40 tokens touch 3 pages, the third partly
-    r0 = pool.runs[0].reshape(10, 2, P, 256)
+    r0 = pool.runs[0].reshape(10, 2, P // 16, 4, 16, 64)  # [page][head][16-cell block][quarter][cell][64]
     for page in range(10):
         if page not in used:
             assert np.all(r0[page] == 0xA5)
     third = int(pt[2])
-    assert np.all(r0[third, :, 8:] == 0xA5) and not np.any(np.all(r0[third, :, :8] == 0xA5, axis=-1))
+    assert np.all(r0[third, :, :, :, 8:] == 0xA5)
+    assert not np.any(np.all(r0[third, :, :, :, :8] == 0xA5, axis=-1))
     # negative control: a table with two entries swapped reads other bytes
     bad = pt.copy()
     bad[[0, 1]] = bad[[1, 0]]
