@@ -27,7 +27,7 @@ D = 256          # head_dim
 KGROUP = 128     # INT8 scale group
 QBLK = 32        # Q4_0 block length
 QBYTES = 18      # Q4_0 block bytes
-FMT_INT8, FMT_Q4_0, FMT_K8V4 = 1, 2, 3
+FMT_F16, FMT_INT8, FMT_Q4_0, FMT_K8V4 = 0, 1, 2, 3
 
 
 def _load():
@@ -168,6 +168,10 @@ class OraclePool:
     head-cells is a 4096-byte block [dim quarter][hc % 16][64 codes], code c
     at (hc//16)*4096 + (c//64)*1024 + (hc%16)*64 + c%64 (P a multiple of
     16).  INT8 V codes (int8 format) are plain rows, code c at hc*256 + c.
+    fp16 format: K and V as fp16 in 8192-byte blocks of 16 head-cells; with
+    c = hc % 16, K element d at (hc//16)*8192 + (d//32)*1024 + ((d%32)//8)*256
+    + c*16 + (d%8)*2 and V element d at (hc//16)*8192 + ((d%16)//2)*1024 +
+    (c//4)*256 + (d//16)*16 + (d%2)*8 + (c%4)*2.
     A q4_0 (page, head) tile is 144*P bytes: nibble bytes of block b of slot s
     at s*128 + b*16; the fp16 scale of block b of slot s at
     128*P + (s//16)*256 + b*32 + (s%16)*2 (scales grouped by 16 slots).
@@ -184,6 +188,7 @@ class OraclePool:
             FMT_K8V4: [int8_codes, int8_scales, q4, 0],
             FMT_INT8: [int8_codes, int8_scales, int8_codes, int8_scales],
             FMT_Q4_0: [q4, 0, q4, 0],
+            FMT_F16: [cells * D * 2, 0, cells * D * 2, 0],
         }[fmt]
         self.runs = [np.full(s, sentinel, np.uint8) if s else None for s in sizes]
 
@@ -206,6 +211,7 @@ class OraclePool:
         k8v4 -> (k_codes [n][H][256] int8, k_scales [n][H][2] f32, v_blocks [n][H][8][18] u8)
         int8 -> (k_codes, k_scales, v_codes, v_scales)
         q4_0 -> (k_blocks, v_blocks)
+        fp16 -> (k [n][H][256] float16, v [n][H][256] float16)
         """
         H = self.H
         codes = lambda: np.empty((n, H, D), np.int8)
@@ -215,6 +221,8 @@ class OraclePool:
             outs = [codes(), scales(), blocks(), None]
         elif self.fmt == FMT_INT8:
             outs = [codes(), scales(), codes(), scales()]
+        elif self.fmt == FMT_F16:
+            outs = [np.empty((n, H, D), np.float16), None, np.empty((n, H, D), np.float16), None]
         else:
             outs = [blocks(), None, blocks(), None]
         pt = _c(page_table, np.int32)
@@ -233,6 +241,9 @@ def dequant_gathered(fmt: int, gathered):
     if fmt == FMT_INT8:
         kc, ks, vc, vs = gathered
         return dequant_int8(kc, ks), dequant_int8(vc, vs)
+    if fmt == FMT_F16:
+        kh, vh = gathered
+        return kh.astype(np.float64), vh.astype(np.float64)
     kb, vb = gathered
     return dequant_q4(kb), dequant_q4(vb)
 
@@ -270,4 +281,4 @@ def attention_from_pool(pool: OraclePool, page_table, q, n_visible, scale: float
     g = pool.gather(page_table, 0, n)
     kd, vd = dequant_gathered(pool.fmt, g)
     return attention(kd, vd, q, n_visible, scale, q_rotate=(pool.fmt == FMT_Q4_0),
-                     v_rotated=(pool.fmt != FMT_INT8))
+                     v_rotated=(pool.fmt not in (FMT_INT8, FMT_F16)))

@@ -178,6 +178,7 @@ static long q4_head_bytes(int D) { return (D / ORC_QBLK) * (long)ORC_QBYTES; }
 long orc_cell_bytes(int fmt, int n_kv_heads, int D) {
   if (D % ORC_KGROUP) return -1;
   switch (fmt) {
+    case 0: return (long)n_kv_heads * 2 * 2L * D;
     case 1: return (long)n_kv_heads * 2 * k_int8_head_bytes(D);
     case 2: return (long)n_kv_heads * 2 * q4_head_bytes(D);
     case 3: return (long)n_kv_heads * (k_int8_head_bytes(D) + q4_head_bytes(D));
@@ -199,6 +200,10 @@ long orc_cell_bytes(int fmt, int n_kv_heads, int D) {
 /* code c of hc at (hc/16)*4096 + (c/64)*1024 + (hc%16)*64 + c%64.      */
 /* (INT8 V codes of the int8 format stay [hc][256].)  P must be a       */
 /* multiple of 16, so a 16-cell group never straddles two tiles.        */
+/* fp16 format (0): K and V as fp16, 8192 bytes per 16 head-cells each; */
+/* with c = hc % 16, K element d at (hc/16)*8192 + (d/32)*1024 +        */
+/* ((d%32)/8)*256 + c*16 + (d%8)*2, V element d at (hc/16)*8192 +       */
+/* ((d%16)/2)*1024 + (c/4)*256 + (d/16)*16 + (d%2)*8 + (c%4)*2.          */
 /* ------------------------------------------------------------------ */
 
 typedef struct {
@@ -220,6 +225,36 @@ static void put_int8_head(uint8_t *codes_run, uint8_t *scales_run, size_t ti, in
   for (int c = 0; c < ORC_D; c++)
     codes_run[k_layout ? k_code_pos(hc, c) : hc * ORC_D + c] = (uint8_t)codes[c];
   memcpy(scales_run + (hc * (ORC_D / ORC_KGROUP)) * 4, scales, 4 * (ORC_D / ORC_KGROUP));
+}
+
+static size_t f16_k_pos(size_t hc, int d) {
+  return (hc / 16) * 8192 + (size_t)(d / 32) * 1024 + (size_t)((d % 32) / 8) * 256 + (hc % 16) * 16 +
+         (size_t)(d % 8) * 2;
+}
+
+static size_t f16_v_pos(size_t hc, int d) {
+  const size_t c = hc % 16;
+  return (hc / 16) * 8192 + (size_t)((d % 16) / 2) * 1024 + (c / 4) * 256 + (size_t)(d / 16) * 16 +
+         (size_t)(d % 2) * 8 + (c % 4) * 2;
+}
+
+/* one head of the fp16 format: each value rounded to fp16 (RNE), stored */
+/* little-endian at its position                                        */
+static void put_f16_head(uint8_t *run, size_t hc, const float *x, int is_v) {
+  for (int d = 0; d < ORC_D; d++) {
+    const uint16_t h = orc_f32_to_f16(x[d]);
+    const size_t at = is_v ? f16_v_pos(hc, d) : f16_k_pos(hc, d);
+    run[at] = (uint8_t)(h & 0xff);
+    run[at + 1] = (uint8_t)(h >> 8);
+  }
+}
+
+static void get_f16_head(const uint8_t *run, size_t hc, int is_v, uint8_t *out) {
+  for (int d = 0; d < ORC_D; d++) {
+    const size_t at = is_v ? f16_v_pos(hc, d) : f16_k_pos(hc, d);
+    out[2 * d] = run[at];
+    out[2 * d + 1] = run[at + 1];
+  }
 }
 
 static void get_int8_codes(const uint8_t *codes_run, size_t hc, int k_layout, uint8_t *out) {
@@ -287,7 +322,10 @@ int orc_append(int fmt, int n_pages, int P, int H, uint8_t *run0, uint8_t *run1,
         vx[c] = load_in(v, dtype, base + c);
       }
       size_t ti = tile_index(page, g, H);
-      if (fmt == 3) {
+      if (fmt == 0) {
+        put_f16_head(run0, ti * P + slot, kx, 0);
+        put_f16_head(run2, ti * P + slot, vx, 1);
+      } else if (fmt == 3) {
         quant_k_int8(kx, codes, scales);
         put_int8_head(run0, run1, ti, P, slot, codes, scales, 1);
         quant_rot_q4(vx, blocks);
@@ -318,6 +356,7 @@ int orc_append(int fmt, int n_pages, int P, int H, uint8_t *run0, uint8_t *run1,
  * k8v4: out0 = K codes, out1 = K scales, out2 = V blocks.
  * int8: out0..out3 = K codes, K scales, V codes, V scales.
  * q4_0: out0 = K blocks, out2 = V blocks.
+ * fp16: out0 = K, out2 = V, each [n][H][256] fp16 bits.
  */
 int orc_gather(int fmt, int n_pages, int P, int H, const uint8_t *run0, const uint8_t *run1,
                const uint8_t *run2, const uint8_t *run3, const int32_t *pt, int n_table,
@@ -333,6 +372,11 @@ int orc_gather(int fmt, int n_pages, int P, int H, const uint8_t *run0, const ui
       size_t ti = tile_index(page, g, H);
       size_t o = (size_t)t * H + g;
       size_t cell = ti * P + slot;
+      if (fmt == 0) {
+        get_f16_head(run0, cell, 0, out0 + o * 2 * ORC_D);
+        get_f16_head(run2, cell, 1, out2 + o * 2 * ORC_D);
+        continue;
+      }
       if (fmt == 1 || fmt == 3) {
         get_int8_codes(run0, cell, 1, out0 + o * ORC_D);
         memcpy(out1 + o * nsc * 4, run1 + cell * nsc * 4, nsc * 4);

@@ -230,3 +230,54 @@ def test_quantized_attention_close_to_exact(orc):
     out8 = orc.attention_from_pool(pool8, pt8, q, [n])
     rel8 = np.abs(out8 - exact).max(-1) / np.abs(exact).max(-1)
     assert rel8.max() < 0.03 and rel8.max() < rel.max()
+
+
+# ------------------------------------------------------------------ fp16 format (no quantization)
+
+def test_f16_cell_bytes(orc):
+    # 2 KV heads x 256 dims x (K and V) x 2 bytes
+    assert orc.cell_bytes(0, 2) == 2048 and orc.cell_bytes(0, 1) == 1024
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float16])
+def test_f16_gather_is_numpy_half_rounding(orc, dtype):
+    # the stored values are the inputs rounded to fp16 (numpy's own
+    # round-to-nearest-even cast), in logical order through a permuted table
+    pool, pt, k, v = _pool_with(orc, 0, P=32, n_pages=6, n_table=5, n_tok=150, seed=11, dtype=dtype)
+    gk, gv = pool.gather(pt, 0, 150)
+    assert np.array_equal(gk.view(np.uint16), k.astype(np.float16).view(np.uint16))
+    assert np.array_equal(gv.view(np.uint16), v.astype(np.float16).view(np.uint16))
+    # untouched pages keep the sentinel
+    used = set(int(x) for x in pt[:5])
+    r0 = pool.runs[0].reshape(6, -1)
+    for page in range(6):
+        if page not in used:
+            assert np.all(r0[page] == 0xA5)
+
+
+def test_f16_bytes_at_documented_offsets(orc):
+    P, H = 32, 2
+    pool, pt, k, v = _pool_with(orc, 0, P=P, n_pages=4, n_table=4, n_tok=70, seed=12)
+    r0, r2 = pool.runs[0].view(np.uint16), pool.runs[2].view(np.uint16)
+    d = np.arange(256)
+    for p in (0, 5, 16, 31, 32, 69):
+        page, slot = pt[p // P], p % P
+        for g in range(H):
+            hc = (page * H + g) * P + slot
+            c = hc % 16
+            kpos = (hc // 16) * 8192 + (d // 32) * 1024 + ((d % 32) // 8) * 256 + c * 16 + (d % 8) * 2
+            vpos = (hc // 16) * 8192 + ((d % 16) // 2) * 1024 + (c // 4) * 256 + (d // 16) * 16 + (d % 2) * 8 + (c % 4) * 2
+            assert np.array_equal(r0[kpos // 2], k[p, g].view(np.uint16))
+            assert np.array_equal(r2[vpos // 2], v[p, g].view(np.uint16))
+
+
+def test_f16_attention_matches_brute_force_tiny(orc):
+    # unrotated keys and values, the exact fp16 values: pure-Python softmax
+    pool, pt, k, v = _pool_with(orc, 0, P=16, n_pages=2, n_table=2, n_tok=7, seed=13)
+    rng = np.random.default_rng(13)
+    q = rng.standard_normal((1, 16, 256)).astype(np.float16)
+    out = orc.attention_from_pool(pool, pt, q, np.array([7], np.int32))
+    kd, vd = k.astype(np.float64), v.astype(np.float64)
+    for h in (0, 7, 8, 15):
+        ref = _brute(kd[:, h // 8].tolist(), vd[:, h // 8].tolist(), q[0, h], 7, 1 / 16, rotated=False)
+        assert np.allclose(out[0, h], ref, rtol=0, atol=1e-12)
