@@ -531,6 +531,7 @@ def bench_extra(torch, k8, synth, dev, log):
         torch.cuda.empty_cache()
     out["prefill_8192_formats"] = fm
     out["formats_32768"] = bench_formats_32768(torch, k8, synth, dev, log)
+    out["decode_240000_fp16"] = bench_fp16_240000(torch, k8, synth, dev, log)
     out["page_copy_k8v4"] = bench_page_copy(torch, k8, pools[0], tables[0], dev, log)
     log(f"extra: {json.dumps(out)}")
     return out
@@ -555,7 +556,7 @@ def bench_page_copy(torch, k8, pool, table, dev, log):
 
 
 def bench_formats_32768(torch, k8, synth, dev, log):
-    """Decode at 32,768 cells for the three formats on the same raw inputs:
+    """Decode at 32,768 cells for the four formats on the same raw inputs:
     3 outlier channels per KV head (x8 on K and V), P = 256, 128 pages drawn
     from a 256-page pool, 16 layer pools per format rotated (beyond the
     Infinity Cache).  Whole calls replayed from a graph."""
@@ -563,7 +564,7 @@ def bench_formats_32768(torch, k8, synth, dev, log):
     outl = synth.outlier_channels(2, 2, 256, 0.01)
     q = synth.queries_device(2, 0, 0, 1, 16, 256, dev)[0]
     res = {}
-    for fmt, name in ((3, "k8v4"), (1, "int8"), (2, "q4_0")):
+    for fmt, name in ((3, "k8v4"), (1, "int8"), (2, "q4_0"), (0, "fp16")):
         log(f"formats: filling {layers} {name} pools of {ctx} cells ...")
         pools, tables = [], []
         for l in range(layers):
@@ -586,6 +587,35 @@ def bench_formats_32768(torch, k8, synth, dev, log):
         del pools, tables
         torch.cuda.empty_cache()
     return res
+
+
+def bench_fp16_240000(torch, k8, synth, dev, log):
+    """The no-dequantization reference: decode at 240,000 cells of the fp16
+    format (2,048 B/cell, 491.5 MB per pool, 3 pools rotated), split kernel
+    alone, timed like the k8v4 decode."""
+    ctx, P, n_pages, n_pools = 240000, 256, 1024, 3
+    log(f"extra: filling {n_pools} fp16 pools of {ctx} cells ...")
+    pools, tables = [], []
+    for i in range(n_pools):
+        pool = k8.KvPool(0, n_pages, P, 2, device=dev)
+        pt = make_table(torch, synth, 4, i, (ctx + P - 1) // P, n_pages, dev)
+        for c, s in enumerate(range(0, ctx, synth.CHUNK)):
+            n = min(synth.CHUNK, ctx - s)
+            kk, vv = synth.kv_chunk_device(4, i, c, n, 2, 256, dev)
+            k8.kv_append(pool, pt, kk, vv, s)
+        pools.append(pool)
+        tables.append(pt)
+    q = synth.queries_device(4, 0, 0, 1, 16, 256, dev)[0]
+    ws = k8.attn_workspace(pools[0], 1, ctx)
+    for i in range(n_pools):
+        k8.attn_decode(pools[i], tables[i], q, ctx, ws)
+    ms, _ = timed_launches(torch, k8, lambda i: k8.attn_decode(pools[i % n_pools], tables[i % n_pools], q, ctx, ws),
+                           8 * n_pools)
+    b = ctx * 2048
+    del pools, tables
+    torch.cuda.empty_cache()
+    return {"us": round(ms * 1e3, 3), "gbs": round(b / ms / 1e6, 1), "hbm_frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4),
+            "cell_bytes": 2048, "kernel": "split kernel alone"}
 
 
 if __name__ == "__main__":

@@ -45,7 +45,7 @@ extern "C" {
 /* KV formats.  The numbering keeps k8v4 = 3, the number the pages give it
  * in the engine's format enum ("kv: --kv k8v4 streams with --kv-resident",
  * How).  1 and 2 are the int8 and q4_0 formats the pages compare against. */
-enum { KV_FMT_INT8 = 1, KV_FMT_Q4_0 = 2, KV_FMT_K8V4 = 3 };
+enum { KV_FMT_F16 = 0, KV_FMT_INT8 = 1, KV_FMT_Q4_0 = 2, KV_FMT_K8V4 = 3 };
 
 /* element type of K/V/q inputs */
 enum { KV_DTYPE_F16 = 0, KV_DTYPE_F32 = 1 };
@@ -96,6 +96,15 @@ enum {
  *   like the K scales.
  * q4_0 (fmt 2), 576 bytes per cell: run[0] K and run[2] V, each a q4_0 tile
  *   run like k8v4's run[2] (both halves rotated); run[1], run[3] unused.
+ * fp16 (fmt 0), 2048 bytes per cell, no quantization and no rotation (the
+ *   reference without dequantization): run[0] K and run[2] V as fp16 (inputs
+ *   rounded to nearest even), 8192 bytes per 16 head-cells each, laid out as
+ *   the attention kernel's matrix-core operands; with c = hc % 16:
+ *     K element d at (hc/16)*8192 + (d/32)*1024 + ((d%32)/8)*256 + c*16 + (d%8)*2
+ *     V element d at (hc/16)*8192 + ((d%16)/2)*1024 + (c/4)*256 + (d/16)*16
+ *                    + (d%2)*8 + (c%4)*2
+ *   run[1], run[3] unused.  Append, gather, decode, verify and the batched
+ *   decode take it; attn_prefill_chunk returns KV_ERR_UNSUPPORTED.
  */
 typedef struct kv_pool {
   int32_t fmt;        /* KV_FMT_*                               */
@@ -172,6 +181,8 @@ int kv_gather(const kv_pool *pool, const kv_seq *seq, int32_t pos0, int32_t n, v
  *   k8v4: out0 K codes, out1 K scales, out2 V blocks (out3 unused)
  *   int8: out0 K codes, out1 K scales, out2 V codes, out3 V scales
  *   q4_0: out0 K blocks, out2 V blocks (out1, out3 unused)
+ *   fp16: out0 K, out2 V, each fp16 [n][H][256], 16-byte aligned (out1,
+ *         out3 unused)
  * A table entry outside [0, n_pages) gives 0xff bytes and NaN scales for
  * its cells.  Errors: KV_ERR_NULL (a required output), _ALIGN, _RANGE.
  */

@@ -18,7 +18,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libk8v4.so")
 
-KV_FMT_INT8, KV_FMT_Q4_0, KV_FMT_K8V4 = 1, 2, 3
+KV_FMT_F16, KV_FMT_INT8, KV_FMT_Q4_0, KV_FMT_K8V4 = 0, 1, 2, 3
 KV_DTYPE_F16, KV_DTYPE_F32 = 0, 1
 HEAD_DIM = 256
 GQA = 8
@@ -137,7 +137,7 @@ def cell_bytes(fmt: int = KV_FMT_K8V4, n_kv_heads: int = 2, head_dim: int = HEAD
 
 
 class KvPool:
-    """A paged pool of format fmt (KV_FMT_INT8, KV_FMT_Q4_0 or KV_FMT_K8V4):
+    """A paged pool of format fmt (KV_FMT_F16, KV_FMT_INT8, KV_FMT_Q4_0 or KV_FMT_K8V4):
     its runs as the header lays them out, in device memory, or with
     host=True in pinned host memory (the host side of a streamed cache, for
     kv_copy_pages only)."""
@@ -219,7 +219,7 @@ def kv_gather_runs(pool: KvPool, page_table, pos0: int, n: int, stream=None):
     documents: int8-coded halves as (codes int8 [n][H][256], scales fp32
     [n][H][2]), q4_0-coded halves as blocks uint8 [n][H][8][18].  Returns
     (K..., V...) flattened: k8v4 (kc, ks, vb), int8 (kc, ks, vc, vs),
-    q4_0 (kb, vb)."""
+    q4_0 (kb, vb), fp16 (k, v) as float16 [n][H][256]."""
     torch = _torch()
     H = pool.n_kv_heads
     dev = pool.runs[0].device
@@ -233,7 +233,10 @@ def kv_gather_runs(pool: KvPool, page_table, pos0: int, n: int, stream=None):
     def blocks():
         return torch.empty((n, H, 8, 18), dtype=torch.uint8, device=dev)
 
-    if pool.fmt == KV_FMT_INT8:
+    if pool.fmt == KV_FMT_F16:
+        outs = [torch.empty((n, H, HEAD_DIM), dtype=torch.float16, device=dev) for _ in range(2)]
+        ptrs = [outs[0], None, outs[1], None]
+    elif pool.fmt == KV_FMT_INT8:
         outs = [codes(), scales(), codes(), scales()]
         ptrs = outs
     elif pool.fmt == KV_FMT_Q4_0:

@@ -109,9 +109,11 @@ int kv_gather_runs(const kv_pool *pool, const kv_seq *seq, int32_t pos0, int32_t
   void *const out[4] = {out0, out1, out2, out3};
   // int8-coded halves: codes (16-byte aligned) + scales (8-byte aligned);
   // q4_0-coded halves: one block array (any alignment)
-  const bool k_int8 = fmt != KV_FMT_Q4_0, v_int8 = fmt == KV_FMT_INT8;
+  // fp16 halves: one [n][H][256] fp16 array each (16-byte aligned)
+  const bool k_int8 = fmt == KV_FMT_INT8 || fmt == KV_FMT_K8V4, v_int8 = fmt == KV_FMT_INT8;
   if (!out0 || !out2 || (k_int8 && !out1) || (v_int8 && !out3)) return KV_ERR_NULL;
   if (int e = check_range(pool, seq, pos0, n)) return e;
+  if (fmt == KV_FMT_F16 && (check_aligned16(out0) || check_aligned16(out2))) return KV_ERR_ALIGN;
   if (k_int8 && (check_aligned16(out0) || ((uintptr_t)out1 & 7u))) return KV_ERR_ALIGN;
   if (v_int8 && (check_aligned16(out2) || ((uintptr_t)out3 & 7u))) return KV_ERR_ALIGN;
   if (n == 0) return KV_OK;
@@ -293,6 +295,7 @@ int attn_prefill_chunk(const kv_pool *pool, const kv_seq *seq, const void *q, in
   (void)ws;
   (void)ws_bytes;
   if (int e = check_attn_common(pool, seq, q, q_dtype, n_q_heads, out, 0)) return e;
+  if (pool->fmt == KV_FMT_F16) return KV_ERR_UNSUPPORTED;  // no fp16 prefill kernel
   if (pos0 < 0 || n_new < 0) return KV_ERR_RANGE;
   if (int e = check_range(pool, seq, 0, (int64_t)pos0 + n_new)) return e;
   if (n_new == 0) return KV_OK;

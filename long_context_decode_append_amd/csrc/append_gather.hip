@@ -49,6 +49,13 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
 
   float x[4];
   load4(a.k, a.dtype, src, x);
+  if (FMT == KV_FMT_F16) {
+    // no quantization: fp16 (round to nearest even) in the operand blocks
+    store_f16_k(a.run[0], cell, lane, x);
+    load4(a.v, a.dtype, src, x);
+    store_f16_v(a.run[2], cell, lane, x);
+    return;
+  }
   if (FMT == KV_FMT_Q4_0) {
     fwht256_lane4(x, lane);
     uint16_t d16;
@@ -103,6 +110,20 @@ __device__ __forceinline__ void gather_q4(const uint8_t *run, bool bad, size_t t
   }
 }
 
+// fp16 halves: K and V of head-cell `cell` back to [256] fp16 rows
+__device__ __forceinline__ void gather_f16(const uint8_t *krun, const uint8_t *vrun, bool bad, size_t cell, size_t o,
+                                           int lane, uint8_t *ok, uint8_t *ov) {
+  u32x2 kw = {0xffffffffu, 0xffffffffu}, vw = {0xffffffffu, 0xffffffffu};
+  if (!bad) {
+    kw = *reinterpret_cast<const u32x2 *>(krun + f16_k_off(cell, lane));
+    uint16_t h[4];
+    for (int e = 0; e < 4; e++) h[e] = *reinterpret_cast<const uint16_t *>(vrun + f16_v_off(cell, 4 * lane + e));
+    vw = u32x2{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
+  }
+  *reinterpret_cast<u32x2 *>(ok + o * 512 + 8 * lane) = kw;
+  *reinterpret_cast<u32x2 *>(ov + o * 512 + 8 * lane) = vw;
+}
+
 // one wave per (cell, KV head); outputs per format as kv_gather_runs documents
 template <int FMT>
 __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
@@ -118,6 +139,10 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
   const size_t cell = tile * a.P + slot;
   const size_t o = (size_t)t * a.H + g;
   // an out-of-range table entry yields 0xff bytes / NaN scales, never a read outside the pool
+  if (FMT == KV_FMT_F16) {
+    gather_f16(a.run[0], a.run[2], bad, cell, o, lane, a.out[0], a.out[2]);
+    return;
+  }
   if (FMT == KV_FMT_Q4_0) gather_q4(a.run[0], bad, tile, a.P, slot, o, lane, a.out[0]);
   else gather_int8<true>(a.run[0], a.run[1], bad, cell, o, lane, a.out[0], a.out[1]);
   if (FMT == KV_FMT_INT8) gather_int8<false>(a.run[2], a.run[3], bad, cell, o, lane, a.out[2], a.out[3]);
@@ -146,6 +171,7 @@ int launch_append(const kv_pool *pool, const kv_seq *seq, const void *k, const v
   const int64_t items = (int64_t)n * a.H;
   const unsigned blocks = (unsigned)((items + 3) / 4);
   switch (pool->fmt) {
+    case KV_FMT_F16: launch(append_kernel<KV_FMT_F16>, dim3(blocks), dim3(256), s, a); break;
     case KV_FMT_INT8: launch(append_kernel<KV_FMT_INT8>, dim3(blocks), dim3(256), s, a); break;
     case KV_FMT_Q4_0: launch(append_kernel<KV_FMT_Q4_0>, dim3(blocks), dim3(256), s, a); break;
     default: launch(append_kernel<KV_FMT_K8V4>, dim3(blocks), dim3(256), s, a); break;
@@ -168,6 +194,7 @@ int launch_gather(const kv_pool *pool, const kv_seq *seq, int pos0, int n, void 
   const int64_t items = (int64_t)n * a.H;
   const unsigned blocks = (unsigned)((items + 3) / 4);
   switch (pool->fmt) {
+    case KV_FMT_F16: launch(gather_kernel<KV_FMT_F16>, dim3(blocks), dim3(256), s, a); break;
     case KV_FMT_INT8: launch(gather_kernel<KV_FMT_INT8>, dim3(blocks), dim3(256), s, a); break;
     case KV_FMT_Q4_0: launch(gather_kernel<KV_FMT_Q4_0>, dim3(blocks), dim3(256), s, a); break;
     default: launch(gather_kernel<KV_FMT_K8V4>, dim3(blocks), dim3(256), s, a); break;

@@ -8,7 +8,9 @@
 // result back with H/16; the batched (verify) form gives each query row its
 // own number of visible cells.  The comparison formats of the same pages run
 // through the same kernel (template FMT): int8 (K and V INT8, no rotation)
-// and q4_0 (rotated K and V, scored against the rotated query).
+// and q4_0 (rotated K and V, scored against the rotated query); the fp16
+// format (no quantization, no rotation) is the no-dequantization reference:
+// its blocks hold the MFMA operands as they are loaded.
 //
 // Mapping onto MI355X:
 //   * grid (splits [+ 1 for a fused append], KV heads, row passes); a
@@ -151,6 +153,13 @@ __device__ __forceinline__ Half make_half(const SplitArgs &a, int g, int pos, in
   const int tile = pg * a.H + g;
   const int cell = tile * a.P + slot0;
   const int q4_tile = tile * 144 * a.P;
+  if (FMT == KV_FMT_F16) {
+    // 8 KB per 16 cells in each of K and V (cell % 16 == 0 here)
+    h.k_soff = cell * 512;
+    h.v_soff = cell * 512;
+    h.ks_soff = h.vd_soff = 0;
+    return h;
+  }
   if (FMT == KV_FMT_Q4_0) {
     h.k_soff = q4_tile + slot0 * 128;
     h.ks_soff = q4_tile + 128 * a.P + slot0 * 16;  // scale group slot0 / 16
@@ -258,14 +267,18 @@ __device__ __forceinline__ void append_token_partial(const SplitArgs &a, int g, 
 // T: 16-row tiles per wave.  Verify runs T > 1: each step's K/V is loaded
 // and dequantized once and used for all T tiles (the accumulators of the
 // extra tiles spill into AGPRs, so one wave per SIMD).
+// fp16 (T = 1 only): a step's raw K and V take 128 VGPRs, one workgroup per
+// CU (the split plan's target anyway).
 template <bool QF32, int FMT, bool NT, int T>
-__global__ __launch_bounds__(256, T == 1 ? 2 : 1) void attn_splitk_kernel(const SplitArgs a) {
+__global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void attn_splitk_kernel(const SplitArgs a) {
   constexpr int kAux = NT ? 2 : 0;  // buffer-load cache policy bits: 2 = nt
   __shared__ __attribute__((aligned(16))) float lds_o[kWaves * 16 * 64 * 4];  // wave states, accumulator layout
   __shared__ __attribute__((aligned(16))) float lds_m[kWaves * 16];
   __shared__ __attribute__((aligned(16))) float lds_l[kWaves * 16];
-  constexpr bool kInt8K = FMT != KV_FMT_Q4_0;   // K as INT8 codes (else rotated q4_0)
-  constexpr bool kQ4V = FMT != KV_FMT_INT8;     // V as rotated q4_0 (else INT8 codes)
+  constexpr bool kF16 = FMT == KV_FMT_F16;                 // K and V as fp16
+  constexpr bool kInt8K = FMT == KV_FMT_INT8 || FMT == KV_FMT_K8V4;   // K as INT8 codes
+  constexpr bool kQ4V = FMT == KV_FMT_Q4_0 || FMT == KV_FMT_K8V4;     // V as rotated q4_0
+  constexpr int kKLoads = kF16 ? 8 : 4;                    // K loads per 16-cell half
 
   // one field from each 64-byte line of the argument block, so all four
   // lines are fetched in one scalar round trip rather than one after another
@@ -308,27 +321,34 @@ __global__ __launch_bounds__(256, T == 1 ? 2 : 1) void attn_splitk_kernel(const 
   //            (low nibbles for even lg, high for odd), its scale at + 64 j
   //   q4_0 V:  + 128 i: bytes [8n, 8n+8) of cell 4lg+i; scales of block n/2
   //   INT8 V:  + 256 i: bytes [16n, 16n+16) of cell 4lg+i; scales of 4 cells
-  const int k_voff = kInt8K ? n * 64 + 16 * lg : n * 128 + 16 * (lg >> 1);
+  //   fp16 K:  + 1024 j: dims 32 j + 8 lg .. + 7 of cell n (one A operand)
+  //   fp16 V:  + 1024 u: dims 16 n + 2 u and 16 n + 2 u + 1 of cells 4 lg ..
+  //            4 lg + 3 (the B operands of output tiles 2 u and 2 u + 1)
+  const int k_voff = kF16 ? 256 * lg + 16 * n : kInt8K ? n * 64 + 16 * lg : n * 128 + 16 * (lg >> 1);
   const int ks_voff = kInt8K ? 32 * lg : 32 * (lg >> 1) + 2 * n;
-  const int v_voff = kQ4V ? 4 * lg * 128 + 8 * n : 4 * lg * 256 + 16 * n;
+  const int v_voff = kF16 ? 256 * lg + 16 * n : kQ4V ? 4 * lg * 128 + 8 * n : 4 * lg * 256 + 16 * n;
   const int vd_voff = kQ4V ? (n >> 1) * 32 + 8 * lg : 32 * lg;
-  const int kstep_j = kInt8K ? 1024 : 32;
+  const int kstep_j = (kInt8K || kF16) ? 1024 : 32;
   const uint32_t q4_shift = (lg & 1) ? 4u : 0u;  // q4_0 K: high nibbles for odd lg
   const int v8_grp = n >> 3;                     // INT8 V: scale group of this lane's dims
 
-  u32x4 kr[2][4];
+  u32x4 kr[2][kKLoads];
   f32x4 ksr[2][2];      // INT8 K scales
   uint32_t kdr[2][4];   // q4_0 K scales (fp16 bits)
   u32x2 vr[2][4];       // q4_0 V
   u32x2 vdr[2];
   u32x4 vr8[2][4];      // INT8 V
+  u32x4 vr16[2][kF16 ? 8 : 1];  // fp16 V
   f32x4 vsr[2][2];
   Half cur0, cur1, nxt0, nxt1;
   auto load_k = [&](int h2, const Half &h) {
-    for (int j = 0; j < 4; j++) kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + kstep_j * j, h.k_soff, kAux);
+    for (int j = 0; j < kKLoads; j++)
+      kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + kstep_j * j, h.k_soff, kAux);
   };
   auto load_ks = [&](int h2, const Half &h) {
-    if (kInt8K) {
+    if (kF16) {
+      // no scales
+    } else if (kInt8K) {
       ksr[h2][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, ks_voff, h.ks_soff, kAux));
       ksr[h2][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, ks_voff + 16, h.ks_soff, kAux));
     } else {
@@ -336,14 +356,18 @@ __global__ __launch_bounds__(256, T == 1 ? 2 : 1) void attn_splitk_kernel(const 
     }
   };
   auto load_v = [&](int h2, const Half &h) {
-    if (kQ4V) {
+    if (kF16) {
+      for (int u = 0; u < 8; u++) vr16[h2][u] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_voff + 1024 * u, h.v_soff, kAux);
+    } else if (kQ4V) {
       for (int i = 0; i < 4; i++) vr[h2][i] = __builtin_amdgcn_raw_buffer_load_b64(rv, v_voff + 128 * i, h.v_soff, kAux);
     } else {
       for (int i = 0; i < 4; i++) vr8[h2][i] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_voff + 256 * i, h.v_soff, kAux);
     }
   };
   auto load_vd = [&](int h2, const Half &h) {
-    if (kQ4V) {
+    if (kF16) {
+      // no scales
+    } else if (kQ4V) {
       vdr[h2] = __builtin_amdgcn_raw_buffer_load_b64(rv, vd_voff, h.vd_soff, kAux);
     } else {
       vsr[h2][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs, vd_voff, h.vd_soff, kAux));
@@ -368,7 +392,7 @@ __global__ __launch_bounds__(256, T == 1 ? 2 : 1) void attn_splitk_kernel(const 
     const int qi = rr >> 3, hl = rr & 7;
     const size_t qbase = ((size_t)qi * a.n_q_heads + (size_t)g * kGqa + hl) * 256;
     for (int kk = 0; kk < 8; kk++) {
-      const int d0 = 64 * (kk >> 1) + 16 * lg + 8 * (kk & 1);
+      const int d0 = kF16 ? 32 * kk + 8 * lg : 64 * (kk >> 1) + 16 * lg + 8 * (kk & 1);
       if (!QF32) {
         qraw[t][kk] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.q) + qbase + d0);
       } else {
@@ -395,7 +419,8 @@ __global__ __launch_bounds__(256, T == 1 ? 2 : 1) void attn_splitk_kernel(const 
 
   // ---------------------------------------------------------------- queries
   // B operand of the QK MFMA for k-step kk: lane (n, lg) holds row n, dims
-  // 64 (kk/2) + 16 lg + 8 (kk%2) + 0..7 (q4_0 K: in q4_kslot order).  The
+  // 64 (kk/2) + 16 lg + 8 (kk%2) + 0..7 (q4_0 K: in q4_kslot order; fp16 K:
+  // dims 32 kk + 8 lg + 0..7).  The
   // q4_0 format scores against rotated keys, so q is rotated first,
   // q~ = H q / 16 (through this wave's part of lds_o).
   f16x8 qop[T][8];
@@ -418,7 +443,7 @@ __global__ __launch_bounds__(256, T == 1 ? 2 : 1) void attn_splitk_kernel(const 
         }
       }
     }
-    if (!kInt8K) {
+    if (FMT == KV_FMT_Q4_0) {
       float *qs = &lds_o[wave * 16 * 64 * 4];  // [16 rows][256] fp32 of this wave
       for (int kk = 0; kk < 8; kk++) {
         const int d0 = 64 * (kk >> 1) + 16 * lg + 8 * (kk & 1);
@@ -518,8 +543,18 @@ __global__ __launch_bounds__(256, T == 1 ? 2 : 1) void attn_splitk_kernel(const 
       for (int h2 = 0; h2 < 2; h2++) {
         f32x4 acc0[T], acc1[T];
         for (int t = 0; t < T; t++) acc0[t] = acc1[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < 4; j++) {
+        for (int j = 0; j < kKLoads; j++) {
           f16x8 ka, kb;
+          if (kF16) {
+            // fp16 K: the load is the A operand of k-step j
+            ka = __builtin_bit_cast(f16x8, kr[h2][j]);
+            for (int t = 0; t < T; t++) {
+              acc0[t] = mfma16x16x32(ka, qop[t][j], acc0[t]);
+              if (QF32) acc0[t] = mfma16x16x32(ka, qlo[t][j], acc0[t]);
+            }
+            kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + kstep_j * j, nx[h2]->k_soff, kAux);
+            continue;
+          }
           if (kInt8K) {
             // INT8 codes -> fp16 code + 1152 (exact); the bias leaves the
             // score through cbias
@@ -615,8 +650,8 @@ __global__ __launch_bounds__(256, T == 1 ? 2 : 1) void attn_splitk_kernel(const 
 
       // ---- O += P . V; the V scales of the cell pairs (k-slots 2k, 2k+1)
       // as fp16 pairs, zeroed for cells past the split
-      uint32_t dsc[4];
-      for (int k = 0; k < 4; k++) {
+      uint32_t dsc[4] = {0u, 0u, 0u, 0u};
+      for (int k = 0; k < (kF16 ? 0 : 4); k++) {
         const int h2 = k >> 1;
         uint32_t w;
         if (kQ4V) {
@@ -634,7 +669,34 @@ __global__ __launch_bounds__(256, T == 1 ? 2 : 1) void attn_splitk_kernel(const 
         dsc[k] = w;
       }
       for (int h2 = 0; h2 < 2; h2++) load_vd(h2, *nx[h2]);
-      if (kQ4V) {
+      if (kF16) {
+        // fp16 V: one load holds the B operands of tiles 2u and 2u + 1.  The
+        // values of cells past the split end are zeroed first: they may hold
+        // any bits, and their P of 0 does not cancel a NaN.
+        if (c + kStep > c_end) {
+          for (int h2 = 0; h2 < 2; h2++) {
+            const int cb = c + 16 * h2 + 4 * lg;
+            const uint32_t m01 = (cb < c_end ? 0x0000ffffu : 0u) | (cb + 1 < c_end ? 0xffff0000u : 0u);
+            const uint32_t m23 = (cb + 2 < c_end ? 0x0000ffffu : 0u) | (cb + 3 < c_end ? 0xffff0000u : 0u);
+            for (int u = 0; u < 8; u++) {
+              vr16[h2][u].x &= m01;
+              vr16[h2][u].y &= m23;
+              vr16[h2][u].z &= m01;
+              vr16[h2][u].w &= m23;
+            }
+          }
+        }
+        for (int u = 0; u < 8; u++) {
+          const u32x4 v0 = vr16[0][u], v1 = vr16[1][u];
+          const f16x8 blo = pack8(v0.x, v0.y, v1.x, v1.y);  // tile 2u:     dim 16 n + 2 u
+          const f16x8 bhi = pack8(v0.z, v0.w, v1.z, v1.w);  // tile 2u + 1: dim 16 n + 2 u + 1
+          // chunk u of this step consumed: refill with the next step's
+          for (int h2 = 0; h2 < 2; h2++)
+            vr16[h2][u] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_voff + 1024 * u, nx[h2]->v_soff, kAux);
+          for (int t = 0; t < T; t++) o[t][2 * u] = mfma16x16x32(pop[t], blo, o[t][2 * u]);
+          for (int t = 0; t < T; t++) o[t][2 * u + 1] = mfma16x16x32(pop[t], bhi, o[t][2 * u + 1]);
+        }
+      } else if (kQ4V) {
         // B = (code - 8) * d16 in fp16, 4 tiles per byte pair
         for (int grp = 0; grp < 4; grp++) {
           const int dw = grp >> 1;
@@ -872,7 +934,7 @@ int launch_attn_splitk(const AttnCall &c) {
   // reads through L2 / MALL; a batch runs one sequence (8 rows) per pass
   const int tiles = (n_rows + 15) / 16;
   const int tile_passes = (tiles + 2) / 3;
-  const int T = (c.batch || qf32) ? 1 : (tiles + tile_passes - 1) / tile_passes;
+  const int T = (c.batch || qf32 || pool->fmt == KV_FMT_F16) ? 1 : (tiles + tile_passes - 1) / tile_passes;
   const int rows_per_pass = c.batch ? kGqa : 16 * T;
   const int passes = (n_rows + rows_per_pass - 1) / rows_per_pass;
   if (passes > (c.batch ? kMaxQ : kMaxPasses)) return KV_ERR_UNSUPPORTED;
@@ -962,6 +1024,10 @@ int launch_attn_splitk(const AttnCall &c) {
   K8V4_SPLIT_CASE(F, false, true, 2)     \
   K8V4_SPLIT_CASE(F, false, false, 3)    \
   K8V4_SPLIT_CASE(F, false, true, 3)
+    K8V4_SPLIT_CASE(KV_FMT_F16, false, false, 1)
+    K8V4_SPLIT_CASE(KV_FMT_F16, false, true, 1)
+    K8V4_SPLIT_CASE(KV_FMT_F16, true, false, 1)
+    K8V4_SPLIT_CASE(KV_FMT_F16, true, true, 1)
     K8V4_SPLIT_FMT(KV_FMT_INT8)
     K8V4_SPLIT_FMT(KV_FMT_Q4_0)
     K8V4_SPLIT_FMT(KV_FMT_K8V4)

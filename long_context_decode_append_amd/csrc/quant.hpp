@@ -87,6 +87,34 @@ __device__ __forceinline__ size_t k_code_off(size_t cell, int lane) {
   return (cell >> 4) * 4096 + (size_t)(lane >> 4) * 1024 + (cell & 15) * 64 + (size_t)(lane & 15) * 4;
 }
 
+// fp16 format: K and V of every 16 head-cells are 8 KB blocks laid out as
+// the attention kernel's MFMA operands (c = cell % 16):
+//   K element d at (cell/16)*8192 + (d/32)*1024 + ((d%32)/8)*256 + c*16 + (d%8)*2
+//   V element d at (cell/16)*8192 + ((d%16)/2)*1024 + (c/4)*256 + (d/16)*16
+//                  + (d%2)*8 + (c%4)*2
+// so every 16-byte load per lane of 16 cells reads 1 KB of consecutive bytes.
+__device__ __forceinline__ size_t f16_k_off(size_t cell, int lane) {  // elements 4 lane .. 4 lane + 3
+  const int d = 4 * lane;
+  return (cell >> 4) * 8192 + (size_t)(d >> 5) * 1024 + (size_t)((d & 31) >> 3) * 256 + (cell & 15) * 16 +
+         (size_t)(d & 7) * 2;
+}
+__device__ __forceinline__ size_t f16_v_off(size_t cell, int d) {
+  const size_t c = cell & 15;
+  return (cell >> 4) * 8192 + (size_t)((d & 15) >> 1) * 1024 + (c >> 2) * 256 + (size_t)(d >> 4) * 16 +
+         (size_t)(d & 1) * 8 + (c & 3) * 2;
+}
+// one head's 256 values, 4 per lane (dims 4 lane ..), rounded to fp16
+__device__ __forceinline__ void store_f16_k(uint8_t *run, size_t cell, int lane, const float x[4]) {
+  uint16_t h[4];
+  for (int e = 0; e < 4; e++) h[e] = f32_to_f16_bits(x[e]);
+  *reinterpret_cast<u32x2 *>(run + f16_k_off(cell, lane)) =
+      u32x2{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
+}
+__device__ __forceinline__ void store_f16_v(uint8_t *run, size_t cell, int lane, const float x[4]) {
+  for (int e = 0; e < 4; e++)
+    *reinterpret_cast<uint16_t *>(run + f16_v_off(cell, 4 * lane + e)) = f32_to_f16_bits(x[e]);
+}
+
 // INT8 half of one head: fp32 scales [cell][2]; codes in the K-code layout
 // (KLAYOUT) or as a plain [cell][256] row (the int8 format's V)
 template <bool KLAYOUT>

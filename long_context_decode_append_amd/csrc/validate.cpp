@@ -3,7 +3,9 @@
 
 namespace k8v4 {
 
-static bool fmt_known(int fmt) { return fmt == KV_FMT_INT8 || fmt == KV_FMT_Q4_0 || fmt == KV_FMT_K8V4; }
+static bool fmt_known(int fmt) {
+  return fmt == KV_FMT_F16 || fmt == KV_FMT_INT8 || fmt == KV_FMT_Q4_0 || fmt == KV_FMT_K8V4;
+}
 
 size_t cell_bytes(int fmt, int n_kv_heads, int head_dim) {
   if (!fmt_known(fmt) || n_kv_heads <= 0 || head_dim != kHeadDim) return 0;
@@ -11,6 +13,7 @@ size_t cell_bytes(int fmt, int n_kv_heads, int head_dim) {
   const size_t q4_half = (head_dim / 32) * 18;               // 18-byte blocks of 32
   size_t per_head = 0;
   switch (fmt) {
+    case KV_FMT_F16: per_head = 2 * 2 * (size_t)head_dim; break;
     case KV_FMT_INT8: per_head = 2 * int8_half; break;
     case KV_FMT_Q4_0: per_head = 2 * q4_half; break;
     default: per_head = int8_half + q4_half; break;
@@ -27,6 +30,7 @@ size_t run_bytes(int fmt, int run, int n_pages, int page_size, int n_kv_heads, i
   switch (fmt) {
     case KV_FMT_K8V4: return run == 0 ? codes : run == 1 ? scales : run == 2 ? q4 : 0;
     case KV_FMT_INT8: return run == 0 || run == 2 ? codes : scales;
+    case KV_FMT_F16: return run == 0 || run == 2 ? 2 * codes : 0;
     default: return run == 0 || run == 2 ? q4 : 0;
   }
 }

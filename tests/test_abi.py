@@ -51,6 +51,10 @@ def test_sizes_match_the_pages(k8):
     runs = [L.kv_run_bytes(3, r, pages, P, H, 256) for r in range(4)]
     assert runs == [pages * P * H * 256, pages * P * H * 8, pages * P * H * 144, 0]
     assert sum(runs) == pages * P * 816
+    # fp16 (no quantization): 2 heads x 256 dims x (K, V) x 2 bytes, runs 0 and 2
+    assert L.kv_cell_bytes(0, 2, 256) == 2048
+    runs = [L.kv_run_bytes(0, r, pages, P, H, 256) for r in range(4)]
+    assert runs == [pages * P * H * 512, 0, pages * P * H * 512, 0]
 
 
 def _pool(k8, fmt=3, P=16, pages=4, H=2, hd=256, ptrs=(16, 32, 48, 0)):
@@ -104,8 +108,8 @@ def test_validation_errors_before_launch(k8):
     assert L.attn_prefill_chunk(P(pool), P(seq), dummy, 0, 16, 60, 5, 0.0, out, None, 0, None) == -3
     assert L.attn_prefill_chunk(P(pool), P(seq), dummy, 0, 16, 10, 0, 0.0, out, None, 0, None) == 0
     assert L.kv_strerror(-6) == b"workspace missing or too small"
-    # generic append / gather over the three formats
-    for fmt, ptrs in ((1, (16, 32, 48, 64)), (2, (16, 0, 48, 0)), (3, (16, 32, 48, 0))):
+    # generic append / gather over the four formats
+    for fmt, ptrs in ((0, (16, 0, 48, 0)), (1, (16, 32, 48, 64)), (2, (16, 0, 48, 0)), (3, (16, 32, 48, 0))):
         pl = _pool(k8, fmt=fmt, ptrs=ptrs)
         assert L.kv_append(P(pl), P(seq), dummy, dummy, 0, 0, 0, None) == 0
         assert L.kv_append(P(pl), P(seq), None, dummy, 0, 0, 1, None) == -1
@@ -126,6 +130,14 @@ def test_validation_errors_before_launch(k8):
                                 0, 0.0, out, None, 0, None) == 0
     assert L.attn_prefill_chunk(P(_pool(k8, fmt=2, ptrs=(16, 0, 48, 0))), P(seq), dummy, 0, 16, 60,
                                 5, 0.0, out, None, 0, None) == -3
+    # fp16: both runs required, aligned outputs, no prefill kernel (refused before the range check)
+    assert L.kv_append(P(_pool(k8, fmt=0, ptrs=(16, 0, 0, 0))), P(seq), dummy, dummy, 0, 0, 1, None) == -1
+    assert L.kv_gather_runs(P(_pool(k8, fmt=0, ptrs=(16, 0, 48, 0))), P(seq), 0, 4, C.c_void_p(24), None,
+                            dummy, None, None) == -7
+    assert L.attn_prefill_chunk(P(_pool(k8, fmt=0, ptrs=(16, 0, 48, 0))), P(seq), dummy, 0, 16, 0,
+                                1, 0.0, out, None, 0, None) == -5
+    assert L.attn_decode(P(_pool(k8, fmt=0, ptrs=(16, 0, 48, 0))), P(seq), dummy, 0, 16, 65, 0.0,
+                         out, dummy, 1 << 20, None) == -3
     # the fused append + decode is k8v4 only
     assert L.attn_decode_append(P(_pool(k8, fmt=1, ptrs=(16, 32, 48, 64))), P(seq), dummy, dummy, 0,
                                 dummy, 0, 16, 3, 0.0, out, dummy, 1 << 20, None) == -5

@@ -1,7 +1,8 @@
 """GPU parity of the comparison formats (int8: INT8 K and V, 1,056 B/cell;
-q4_0: rotated Q4_0 K and V, 576 B/cell) through the C ABI against the CPU
-oracle: pool bytes and gathered bytes bit-exact, decode and verify within
-2e-3 max relative error per (query row, head)."""
+q4_0: rotated Q4_0 K and V, 576 B/cell; fp16: K and V unquantized, 2,048
+B/cell) through the C ABI against the CPU oracle: pool bytes and gathered
+bytes bit-exact, decode and verify within 2e-3 max relative error per
+(query row, head)."""
 import sys
 
 import numpy as np
@@ -12,7 +13,7 @@ from long_context_decode_append_amd import synth
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-3
-FMT_INT8, FMT_Q4_0, FMT_K8V4 = 1, 2, 3
+FMT_F16, FMT_INT8, FMT_Q4_0, FMT_K8V4 = 0, 1, 2, 3
 
 
 def say(*a):
@@ -64,7 +65,7 @@ class ArmCase:
             self.opool.append(self.pt, k, v, s)
 
 
-@pytest.mark.parametrize("fmt", [FMT_INT8, FMT_Q4_0])
+@pytest.mark.parametrize("fmt", [FMT_INT8, FMT_Q4_0, FMT_F16])
 @pytest.mark.parametrize("dtype,ctx,P,n_pages", [(np.float32, 1024, 16, 64),
                                                  (np.float16, 1000, 16, 70),
                                                  (np.float16, 700, 256, 4)])
@@ -98,7 +99,7 @@ def test_k8v4_append_through_generic_entry_equals_k8v4_entry(k8, dev):
         assert np.array_equal(a.runs[r].cpu().numpy(), b.runs[r].cpu().numpy())
 
 
-@pytest.fixture(scope="module", params=[FMT_INT8, FMT_Q4_0])
+@pytest.fixture(scope="module", params=[FMT_INT8, FMT_Q4_0, FMT_F16])
 def arm_tiny(request, orc, k8, dev):
     return ArmCase(orc, k8, dev, request.param, 0, 1024, 16, 64, 64, dtype=np.float32, chunk=1024)
 
@@ -137,7 +138,7 @@ def test_arm_verify_one_row_equals_decode_bitwise(k8, dev, arm_tiny):
     assert np.array_equal(a.view(np.uint32), b[0].view(np.uint32))
 
 
-@pytest.mark.parametrize("fmt", [FMT_INT8, FMT_Q4_0, FMT_K8V4])
+@pytest.mark.parametrize("fmt", [FMT_INT8, FMT_Q4_0, FMT_K8V4, FMT_F16])
 def test_arms_decode_32768_with_outlier_channels(orc, k8, dev, fmt):
     """The three formats on the same raw inputs: 32,768 cells, 3 outlier
     channels per KV head (x8 on K and V), P = 256, 128 pages drawn from a
@@ -196,3 +197,11 @@ def test_arm_prefill_32768_outliers_matches_verify(orc, k8, dev, fmt):
     err2 = rel_err(out[48:], ver)
     say(f"  rel diff vs verify {err2:.3e}")
     assert err2 <= 2 * TOL
+
+
+def test_f16_prefill_is_refused(orc, k8, dev):
+    # the fp16 format has no prefill kernel: an error before any launch
+    c = ArmCase(orc, k8, dev, FMT_F16, 7, 64, 16, 4, 4)
+    q = synth.queries(7, 0, 0, 8, 16, 256, np.float16)
+    with pytest.raises(k8.KvError):
+        k8.attn_prefill_chunk(c.gpool, c.gpt, t_(q, dev), 56)
