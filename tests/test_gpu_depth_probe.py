@@ -1,15 +1,18 @@
 """Quantization error against depth (the pages' "no growth with depth"
 claim for the KV formats, tested without a model).
 
-The same seeded N(0,1) K/V (fp16) are appended to an int8, a k8v4 and a
-q4_0 pool of 240,000 cells; one decode query attends to the first n cells
+The same seeded N(0,1) K/V (fp16) are appended to an int8, a k8v4, a q4_0
+and an fp16 pool of 240,000 cells; one decode query attends to the first n cells
 for n from 15,000 to 240,000.  Each GPU output is compared with the exact
 attention over the unquantized K/V (the oracle in fp64, no rotation).  The
 pages ("#729 KV int8 vs fp16 KLD compare at 240K context", the depth table
 and its remarks) report that int8 KV does not get worse with depth because
 the quantization noise of K and V averages out with the attention's
 averaging; here the relative error of each format must stay flat from 15K
-to 240K, and the formats must order by their bits (int8 < k8v4 < q4_0).
+to 240K, and the formats must order by their bits (fp16 < int8 < k8v4 <
+q4_0).  The fp16 pool holds the inputs exactly, so its error is the
+kernel's own arithmetic (fp16 P, fp32 accumulation): the floor under the
+quantized formats.
 """
 import sys
 
@@ -21,7 +24,7 @@ from long_context_decode_append_amd import synth
 pytestmark = pytest.mark.gpu
 
 DEPTHS = [15000, 30000, 60000, 120000, 240000]
-FMTS = [(1, "int8"), (3, "k8v4"), (2, "q4_0")]
+FMTS = [(0, "fp16"), (1, "int8"), (3, "k8v4"), (2, "q4_0")]
 
 
 def say(*a):
@@ -74,11 +77,11 @@ def test_error_does_not_grow_with_depth(orc):
             table[name].append(e)
             row.append(f"{e[0]:.3e} / {e[1]:.3e}")
         say(f"{n:7d}  " + "  ".join(f"{r:>22s}" for r in row))
-    for _, name in FMTS:
+    for _, name in FMTS[1:]:  # the quantized formats
         rms = [e[1] for e in table[name]]
         # flat: the deepest point within 1.5x of the shallowest, and no point
         # more than 1.5x the median
         assert rms[-1] <= 1.5 * rms[0], (name, rms)
         assert max(rms) <= 1.5 * float(np.median(rms)), (name, rms)
     for i in range(len(DEPTHS)):
-        assert table["int8"][i][1] < table["k8v4"][i][1] < table["q4_0"][i][1]
+        assert table["fp16"][i][1] < table["int8"][i][1] < table["k8v4"][i][1] < table["q4_0"][i][1]
