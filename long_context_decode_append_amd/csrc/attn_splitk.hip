@@ -1002,14 +1002,17 @@ int launch_attn_splitk(const AttnCall &c) {
   a.append_pos = c.append_pos;
 
   dim3 grid(n_parts, H, passes);
-  // non-temporal KV loads when no two passes share their reads and the
-  // stream is larger than half the 256 MB Infinity Cache (measured: 3 %
-  // faster at 240,000 cells, 1 % slower at 118,750, where the stream fits
-  // the cache; verify's row passes share their reads through L2)
+  // non-temporal KV loads when no two passes share their reads and one call
+  // streams more than 16 MiB: a call reads each cell once, and a long
+  // context's pages would only push other data out of L2 and the Infinity
+  // Cache (measured with the K-code blocks: 6.7 % faster per layer at
+  // 118,750 cells, 3 % at 240,000).  Small contexts keep plain loads, so a
+  // model whose whole cache fits the 256 MB Infinity Cache can reuse it
+  // from step to step; verify's row passes share their reads through L2.
   size_t stream_cells = 0;
   for (int i = 0; i < (c.batch ? c.n_q : 1); i++) stream_cells += (size_t)(c.batch ? c.limits[i] : c.max_limit);
   const bool nt = (passes == 1 || c.batch) &&
-                  stream_cells * kv_cell_bytes(pool->fmt, H, kHeadDim) > ((size_t)128 << 20);
+                  stream_cells * kv_cell_bytes(pool->fmt, H, kHeadDim) > ((size_t)16 << 20);
   switch (((pool->fmt * 4 + (qf32 ? 2 : 0) + (nt ? 1 : 0)) << 2) + T) {
 #define K8V4_SPLIT_CASE(F, Q, N, T_) \
   case ((F * 4 + (Q ? 2 : 0) + (N ? 1 : 0)) << 2) + T_: \
