@@ -516,7 +516,7 @@ def bench_extra(torch, k8, synth, dev, log):
                                      "flop": flops}
     # the same chunk over the comparison formats (one 240,000-cell pool each)
     fm = {}
-    for fmt, name in ((1, "int8"), (2, "q4_0")):
+    for fmt, name in ((1, "int8"), (2, "q4_0"), (0, "fp16")):
         log(f"extra: prefill chunk over a {name} pool ...")
         pool = k8.KvPool(fmt, n_pages, P, 2, device=dev)
         for c, s in enumerate(range(0, ctx, synth.CHUNK)):

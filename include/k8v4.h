@@ -103,8 +103,7 @@ enum {
  *     K element d at (hc/16)*8192 + (d/32)*1024 + ((d%32)/8)*256 + c*16 + (d%8)*2
  *     V element d at (hc/16)*8192 + ((d%16)/2)*1024 + (c/4)*256 + (d/16)*16
  *                    + (d%2)*8 + (c%4)*2
- *   run[1], run[3] unused.  Append, gather, decode, verify and the batched
- *   decode take it; attn_prefill_chunk returns KV_ERR_UNSUPPORTED.
+ *   run[1], run[3] unused.  Every any-format entry point takes it.
  */
 typedef struct kv_pool {
   int32_t fmt;        /* KV_FMT_*                               */
@@ -152,9 +151,10 @@ int kv_append_k8v4(const kv_pool *pool, const kv_seq *seq, const void *k, const 
                    int dtype, int32_t pos0, int32_t n_tokens, void *stream);
 
 /*
- * The same append for a pool of any of the three formats (fmt 1, 2, 3):
+ * The same append for a pool of any of the four formats (fmt 0, 1, 2, 3):
  * each half follows its kind's rule above (int8: K and V by the INT8 rule;
- * q4_0: K and V both rotated and Q4_0-coded; k8v4: as kv_append_k8v4).
+ * q4_0: K and V both rotated and Q4_0-coded; k8v4: as kv_append_k8v4;
+ * fp16: K and V rounded to fp16, unrotated).
  * Same arguments and errors as kv_append_k8v4, _UNSUPPORTED for an unknown
  * format.
  */
@@ -242,7 +242,8 @@ int kv_probe_read(const void *buf, size_t bytes, void *sink, void *stream);
  * The comparison formats run through the same entry: int8 scores q against
  * K = code * d and returns softmax(.) V with V = code * d (no rotation);
  * q4_0 scores (H q / 16) against the rotated K_rot = (code - 8) * d16 and
- * rotates the output back as k8v4 does.
+ * rotates the output back as k8v4 does; fp16 returns softmax(scale q K^T) V
+ * over the stored fp16 K and V.
  * Errors: KV_ERR_NULL, _UNSUPPORTED, _DTYPE, _RANGE (n_ctx < 1 or beyond
  * the table), _WORKSPACE.
  */
@@ -310,9 +311,9 @@ int attn_verify(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dty
  * prefill).  Dense contractions on the matrix cores (fp16 inputs, fp32
  * accumulation).
  *   q:   device, [n_new][n_q_heads][256];  out: device fp32 [n_new][n_q_heads][256]
- * Needs no workspace (ws may be NULL).  Any of the three formats, with the
+ * Needs no workspace (ws may be NULL).  Any of the four formats, with the
  * same rules as attn_decode (q4_0 scores the rotated query against rotated
- * keys; int8 returns softmax(.) V unrotated).
+ * keys; int8 and fp16 return softmax(.) V unrotated).
  * Errors: KV_ERR_NULL, _UNSUPPORTED, _DTYPE, _RANGE.
  */
 int attn_prefill_chunk(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,

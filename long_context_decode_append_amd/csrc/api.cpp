@@ -295,7 +295,6 @@ int attn_prefill_chunk(const kv_pool *pool, const kv_seq *seq, const void *q, in
   (void)ws;
   (void)ws_bytes;
   if (int e = check_attn_common(pool, seq, q, q_dtype, n_q_heads, out, 0)) return e;
-  if (pool->fmt == KV_FMT_F16) return KV_ERR_UNSUPPORTED;  // no fp16 prefill kernel
   if (pos0 < 0 || n_new < 0) return KV_ERR_RANGE;
   if (int e = check_range(pool, seq, 0, (int64_t)pos0 + n_new)) return e;
   if (n_new == 0) return KV_OK;

@@ -75,12 +75,17 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
 //           and 2 (u % 16) + 1, and the two blocks' scales
 //   INT8 V: codes of dims 8 (u / 16) .. + 7 of the same two cells, and the two
 //           cells' scales of that 128-dim group
+//   fp16 K: dims 16 (u % 16) .. + 15 of cell u / 16 (32 bytes, two loads)
+//   fp16 V: 32 consecutive bytes of half u / 256 of the tile: chunks 2i and
+//           2i + 1 (i = u % 256) of its 8 KB block, each 4 cells x 2 dims
 struct PfRaw {
   u32x4 k;          // INT8 K: 16 codes; q4_0 K: .x .y nibble bytes, .z scale
   float kd;         // INT8 K scale (x softmax scale); q4_0 K: the softmax scale
   u32x2 va, vb;     // V of the two cells (q4_0: .x only)
   uint32_t vd;      // q4_0 V: the two fp16 scales (lo: first cell)
   float vsa, vsb;   // INT8 V: the two cells' scales
+  u32x4 k2;         // fp16 K: dims 8 .. 15 of the unit
+  u32x4 v16[2];     // fp16 V: the unit's two 16-byte chunks
 };
 
 // Per tile: the physical (page, head) tile of each 16-cell half (P is a
@@ -121,6 +126,41 @@ __device__ __forceinline__ void pf_load(const PrefillArgs &a, const PfHalves &hv
                                         PfRaw &r) {
   r.k = u32x4{0u, 0u, 0u, 0u};
   r.kd = a.scale2;
+  if (FMT == KV_FMT_F16) {
+    // fp16 blocks (8 KB per 16 cells in each of K and V, the layout the
+    // decode kernel loads as MFMA operands); values of cells past the
+    // visible ones are zeroed (they may hold any bits)
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const int cl = u >> 4, hf = cl >> 4, m = u & 15;
+    r.k2 = z;
+    if (c0 + cl < n_cells) {
+      const uint8_t *kb = a.run[0] + hv.cell(hf) * 512 + (m >> 1) * 1024 + (m & 1) * 512 + (cl & 15) * 16;
+      r.k = *reinterpret_cast<const u32x4 *>(kb);
+      r.k2 = *reinterpret_cast<const u32x4 *>(kb + 256);
+    }
+    r.kd = 0.f;
+    if (u < 2 * kPfTile && c0 + (u >> 1) < n_cells) r.kd = a.scale2;
+    const int vh = u >> 8, idx = u & 255;
+    const int lq = (idx >> 3) & 3;  // cell quad of the two chunks
+    const uint8_t *vb = a.run[2] + hv.cell(vh) * 512 + 32 * idx;
+    r.v16[0] = r.v16[1] = z;
+    const int cq = c0 + 16 * vh + 4 * lq;
+    if (cq < n_cells) {
+      r.v16[0] = *reinterpret_cast<const u32x4 *>(vb);
+      r.v16[1] = *reinterpret_cast<const u32x4 *>(vb + 16);
+      if (cq + 3 >= n_cells) {
+        const uint32_t m01 = (cq < n_cells ? 0x0000ffffu : 0u) | (cq + 1 < n_cells ? 0xffff0000u : 0u);
+        const uint32_t m23 = (cq + 2 < n_cells ? 0x0000ffffu : 0u) | (cq + 3 < n_cells ? 0xffff0000u : 0u);
+        for (int q = 0; q < 2; q++) {
+          r.v16[q].x &= m01;
+          r.v16[q].y &= m23;
+          r.v16[q].z &= m01;
+          r.v16[q].w &= m23;
+        }
+      }
+    }
+    return;
+  }
   if (FMT != KV_FMT_Q4_0) {
     const int cl = u >> 4, hf = cl >> 4;
     // K-code run: 4 KB per 16 cells, [dim quarter][cell % 16][64 codes];
@@ -195,6 +235,26 @@ __device__ __forceinline__ void q4_word_to_f16(uint32_t w, f16x2 d, uint32_t lo[
 
 template <int FMT>
 __device__ __forceinline__ void pf_store(const PfRaw &r, int u, _Float16 *lk, _Float16 *lv, float *lks) {
+  if (FMT == KV_FMT_F16) {
+    // K as loaded, row-major [cell][dim]; V transposed [dim][cell]: chunk
+    // (uu, lq, nn) holds dims 16 nn + 2 uu (+1) of cells 4 lq .. 4 lq + 3
+    // of its half, which sit side by side in a V row (v_pos)
+    _Float16 *kd = lk + (u >> 4) * kKRow + 16 * (u & 15);
+    *reinterpret_cast<u32x4 *>(kd) = r.k;
+    *reinterpret_cast<u32x4 *>(kd + 8) = r.k2;
+    if (u < 2 * kPfTile) lks[u] = r.kd;
+    const int vh = u >> 8, idx = u & 255;
+    const int uu = idx >> 5, lq = (idx >> 3) & 3;
+    for (int q = 0; q < 2; q++) {
+      const int nn = 2 * (idx & 7) + q;
+      const int d = 16 * nn + 2 * uu;
+      _Float16 *v0 = lv + v_row(32 * (d >> 5), d & 31) + v_pos(16 * vh + 4 * lq);
+      _Float16 *v1 = lv + v_row(32 * ((d + 1) >> 5), (d + 1) & 31) + v_pos(16 * vh + 4 * lq);
+      *reinterpret_cast<u32x2 *>(v0) = u32x2{r.v16[q].x, r.v16[q].y};
+      *reinterpret_cast<u32x2 *>(v1) = u32x2{r.v16[q].z, r.v16[q].w};
+    }
+    return;
+  }
   if (FMT != KV_FMT_Q4_0) {
     // INT8 K -> exact fp16 codes, row-major [cell][dim]
     const f16x2 c1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
@@ -456,7 +516,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
     const int qw = qb0 + (rw >> 3);
     const f32x4 y4 = *reinterpret_cast<const f32x4 *>(&wrow[rr * 256 + 4 * lane]);
     float y[4] = {y4[0], y4[1], y4[2], y4[3]};
-    if (FMT != KV_FMT_INT8) fwht256_lane4(y, lane);
+    if (FMT == KV_FMT_Q4_0 || FMT == KV_FMT_K8V4) fwht256_lane4(y, lane);
     if (qw <= q_last) {
       float *op = a.out + ((size_t)qw * a.n_q_heads + (size_t)g * kGqa + (rw & 7)) * 256 + 4 * lane;
       *reinterpret_cast<f32x4 *>(op) = f32x4{y[0], y[1], y[2], y[3]};
@@ -485,6 +545,8 @@ int launch_attn_prefill(const kv_pool *pool, const kv_seq *seq, const void *q, i
   const dim3 grid((n_new + kPfPos - 1) / kPfPos, a.H), block(kPfWaves * 64);
   const bool qf32 = q_dtype == KV_DTYPE_F32;
   switch (pool->fmt * 2 + (qf32 ? 1 : 0)) {
+    case KV_FMT_F16 * 2: launch((attn_prefill_kernel<false, KV_FMT_F16>), grid, block, s, a); break;
+    case KV_FMT_F16 * 2 + 1: launch((attn_prefill_kernel<true, KV_FMT_F16>), grid, block, s, a); break;
     case KV_FMT_INT8 * 2: launch((attn_prefill_kernel<false, KV_FMT_INT8>), grid, block, s, a); break;
     case KV_FMT_INT8 * 2 + 1: launch((attn_prefill_kernel<true, KV_FMT_INT8>), grid, block, s, a); break;
     case KV_FMT_Q4_0 * 2: launch((attn_prefill_kernel<false, KV_FMT_Q4_0>), grid, block, s, a); break;

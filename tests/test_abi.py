@@ -130,12 +130,12 @@ def test_validation_errors_before_launch(k8):
                                 0, 0.0, out, None, 0, None) == 0
     assert L.attn_prefill_chunk(P(_pool(k8, fmt=2, ptrs=(16, 0, 48, 0))), P(seq), dummy, 0, 16, 60,
                                 5, 0.0, out, None, 0, None) == -3
-    # fp16: both runs required, aligned outputs, no prefill kernel (refused before the range check)
+    # fp16: both runs required, aligned outputs
     assert L.kv_append(P(_pool(k8, fmt=0, ptrs=(16, 0, 0, 0))), P(seq), dummy, dummy, 0, 0, 1, None) == -1
     assert L.kv_gather_runs(P(_pool(k8, fmt=0, ptrs=(16, 0, 48, 0))), P(seq), 0, 4, C.c_void_p(24), None,
                             dummy, None, None) == -7
-    assert L.attn_prefill_chunk(P(_pool(k8, fmt=0, ptrs=(16, 0, 48, 0))), P(seq), dummy, 0, 16, 0,
-                                1, 0.0, out, None, 0, None) == -5
+    assert L.attn_prefill_chunk(P(_pool(k8, fmt=0, ptrs=(16, 0, 48, 0))), P(seq), dummy, 0, 16, 60,
+                                5, 0.0, out, None, 0, None) == -3
     assert L.attn_decode(P(_pool(k8, fmt=0, ptrs=(16, 0, 48, 0))), P(seq), dummy, 0, 16, 65, 0.0,
                          out, dummy, 1 << 20, None) == -3
     # the fused append + decode is k8v4 only

@@ -154,7 +154,7 @@ def test_arms_decode_32768_with_outlier_channels(orc, k8, dev, fmt):
     assert err <= TOL
 
 
-@pytest.mark.parametrize("fmt", [FMT_INT8, FMT_Q4_0])
+@pytest.mark.parametrize("fmt", [FMT_INT8, FMT_Q4_0, FMT_F16])
 @pytest.mark.parametrize("n_new", [1, 17, 100])
 @pytest.mark.parametrize("qdtype", [np.float16, np.float32])
 def test_arm_prefill_parity(orc, k8, dev, fmt, n_new, qdtype):
@@ -172,7 +172,7 @@ def test_arm_prefill_parity(orc, k8, dev, fmt, n_new, qdtype):
     assert err <= TOL
 
 
-@pytest.mark.parametrize("fmt", [FMT_INT8, FMT_Q4_0])
+@pytest.mark.parametrize("fmt", [FMT_INT8, FMT_Q4_0, FMT_F16])
 def test_arm_prefill_32768_outliers_matches_verify(orc, k8, dev, fmt):
     """64 queries at the end of 32,768 cells with outlier channels: against
     the oracle, and row by row against the verify kernel (same limits)."""
@@ -198,10 +198,3 @@ def test_arm_prefill_32768_outliers_matches_verify(orc, k8, dev, fmt):
     say(f"  rel diff vs verify {err2:.3e}")
     assert err2 <= 2 * TOL
 
-
-def test_f16_prefill_is_refused(orc, k8, dev):
-    # the fp16 format has no prefill kernel: an error before any launch
-    c = ArmCase(orc, k8, dev, FMT_F16, 7, 64, 16, 4, 4)
-    q = synth.queries(7, 0, 0, 8, 16, 256, np.float16)
-    with pytest.raises(k8.KvError):
-        k8.attn_prefill_chunk(c.gpool, c.gpt, t_(q, dev), 56)
