@@ -828,20 +828,19 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
 // Combine of the split partials of one query row of one KV head, after the
 // split kernel (the kernel boundary makes every partial visible).  The
 // partials are in the unrotated basis, so the rows split into independent
-// 64-dim slices, one workgroup each: the m of all splits give the common
-// max, 16 split lanes of 16 threads (4 dims each) sum a strided share of the
-// slice rows (all loaded before they are needed) in ascending split order,
-// the lanes add in fixed order and O / l is stored.  Deterministic for a
-// given split plan.
+// 64-dim slices, one workgroup each: 16 split lanes of 16 threads (4 dims
+// each) load a strided share of the slice rows and their m up front; every
+// wave forms the common max and the weighted sum of l from all (m, l) by
+// itself (so only the final sum of the 4 waves needs a barrier), the split
+// lanes sum in ascending split order, the lanes and waves add in fixed order
+// and O / l is stored.  Deterministic for a given split plan.
 constexpr int kCombineWaves = 4;
 constexpr int kCombineParts = 4;                                    // 64-dim slices
 constexpr int kCombineLanes = kCombineWaves * 64 / 16;              // split lanes
 constexpr int kCombineBatch = kMaxSplitsPerHead / kCombineLanes;    // loads per thread
-static_assert(kCombineWaves * 64 >= kMaxSplitsPerHead, "one (m, l) per thread");
+static_assert(kMaxSplitsPerHead % 64 == 0, "whole (m, l) loads per lane");
 
 __global__ __launch_bounds__(kCombineWaves * 64) void attn_combine_kernel(const SplitArgs a) {
-  __shared__ float lds_w[kMaxSplitsPerHead];
-  __shared__ float lds_red[kCombineWaves];
   __shared__ f32x4 lds_acc[kCombineWaves][16];
   const int row = blockIdx.x, g = blockIdx.y, part = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -852,44 +851,43 @@ __global__ __launch_bounds__(kCombineWaves * 64) void attn_combine_kernel(const 
   const size_t base = (size_t)g * S;
   const float *po = a.part_o + (base * rows_total + row) * 256 + 64 * part + 4 * dl;
   const size_t sstride = rows_total * 256;
+  const float2 *pml = a.part_ml + base * rows_total + row;
 
-  // this thread's slice rows, issued before the (m, l) pass
+  // this thread's slice rows and their m, issued first
   f32x4 ov[kCombineBatch];
+  float mk[kCombineBatch];
   for (int k = 0; k < kCombineBatch; k++) {
     const int sidx = sl + kCombineLanes * k;
-    if (sidx < S) ov[k] = *reinterpret_cast<const f32x4 *>(po + (size_t)sidx * sstride);
+    if (sidx < S) {
+      ov[k] = *reinterpret_cast<const f32x4 *>(po + (size_t)sidx * sstride);
+      mk[k] = pml[(size_t)sidx * rows_total].x;
+    }
   }
-  float2 ml = make_float2(-1e30f, 0.f);
-  if (tid < S) ml = a.part_ml[(base + tid) * rows_total + row];
-  // common max over the splits
-  float mx = ml.x;
-  mx = wave_max(mx);
-  if (lane == 0) lds_red[wave] = mx;
-  __syncthreads();
-  float M = lds_red[0];
-  for (int w = 1; w < kCombineWaves; w++) M = fmaxf(M, lds_red[w]);
-  const float wgt = tid < S ? fast_exp2(ml.x - M) : 0.f;
-  if (tid < S) lds_w[tid] = wgt;
-  float lw = wgt * ml.y;
-  lw = wave_sum(lw);
-  __syncthreads();  // lds_red reads above are done before it is reused
-  if (lane == 0) lds_red[wave] = lw;
-  __syncthreads();
+  // every wave reads all (m, l) of the row and forms the common max M and
+  // L = sum l_s 2^(m_s - M) itself, so no workgroup barrier is needed
+  constexpr int kMl = kMaxSplitsPerHead / 64;
+  float2 mlw[kMl];
+  for (int i = 0; i < kMl; i++) {
+    const int s = lane + 64 * i;
+    mlw[i] = s < S ? pml[(size_t)s * rows_total] : make_float2(-1e30f, 0.f);
+  }
+  float mx = mlw[0].x;
+  for (int i = 1; i < kMl; i++) mx = fmaxf(mx, mlw[i].x);
+  const float M = wave_max(mx);
+  float lw = 0.f;
+  for (int i = 0; i < kMl; i++) lw += (lane + 64 * i < S) ? mlw[i].y * fast_exp2(mlw[i].x - M) : 0.f;
+  const float L = wave_sum(lw);
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int k = 0; k < kCombineBatch; k++) {
     const int sidx = sl + kCombineLanes * k;
-    if (sidx < S) acc += lds_w[sidx] * ov[k];
+    if (sidx < S) acc += fast_exp2(mk[k] - M) * ov[k];
   }
   // the 4 split lanes of a wave, then the waves
-  for (int i = 0; i < 4; i++) {
-    acc[i] = sum_lg(acc[i]);
-  }
+  for (int i = 0; i < 4; i++) acc[i] = sum_lg(acc[i]);
   if (lane < 16) lds_acc[wave][lane] = acc;
   __syncthreads();
   if (tid >= 16) return;
-  float L = 0.f;
-  for (int w = 0; w < kCombineWaves; w++) L += lds_red[w];
   f32x4 tot = lds_acc[0][tid];
   for (int w = 1; w < kCombineWaves; w++) tot += lds_acc[w][tid];
   const float inv = 1.0f / L;
