@@ -532,6 +532,7 @@ def bench_extra(torch, k8, synth, dev, log):
     out["prefill_8192_formats"] = fm
     out["formats_32768"] = bench_formats_32768(torch, k8, synth, dev, log)
     out["decode_240000_fp16"] = bench_fp16_240000(torch, k8, synth, dev, log)
+    out["decode_1048576"] = bench_decode_1m(torch, k8, synth, dev, log)
     out["page_copy_k8v4"] = bench_page_copy(torch, k8, pools[0], tables[0], dev, log)
     log(f"extra: {json.dumps(out)}")
     return out
@@ -616,6 +617,35 @@ def bench_fp16_240000(torch, k8, synth, dev, log):
     torch.cuda.empty_cache()
     return {"us": round(ms * 1e3, 3), "gbs": round(b / ms / 1e6, 1), "hbm_frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4),
             "cell_bytes": 2048, "kernel": "split kernel alone"}
+
+
+def bench_decode_1m(torch, k8, synth, dev, log):
+    """Decode at 1,048,576 cells (the longest context the pages run k8v4 at),
+    2 pools of 856 MB rotated, split kernel alone and whole call."""
+    ctx, P, n_pools = 1 << 20, 256, 2
+    n_pages = ctx // P
+    log(f"extra: filling {n_pools} k8v4 pools of {ctx} cells ...")
+    pools, tables = [], []
+    for i in range(n_pools):
+        pool = k8.K8V4Pool(n_pages, P, 2, device=dev)
+        pt = make_table(torch, synth, 6, i, n_pages, n_pages, dev)
+        fill_pool(k8, synth, pool, pt, 6, i, ctx, dev)
+        pools.append(pool)
+        tables.append(pt)
+    q = synth.queries_device(6, 0, 0, 1, 16, 256, dev)[0]
+    ws = k8.attn_workspace(pools[0], 1, ctx)
+    for i in range(n_pools):
+        k8.attn_decode(pools[i], tables[i], q, ctx, ws)
+    ms, _ = timed_launches(torch, k8, lambda i: k8.attn_decode(pools[i % n_pools], tables[i % n_pools], q, ctx, ws),
+                           8 * n_pools)
+    wc_ms = graph_calls_ms(torch, lambda i: k8.attn_decode(pools[i % n_pools], tables[i % n_pools], q, ctx, ws),
+                           2 * n_pools)
+    b = ctx * CELL_BYTES
+    del pools, tables
+    torch.cuda.empty_cache()
+    return {"us": round(ms * 1e3, 3), "gbs": round(b / ms / 1e6, 1), "hbm_frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4),
+            "kernel": "split kernel alone", "us_split_plus_combine": round(wc_ms * 1e3, 3),
+            "hbm_frac_split_plus_combine": round(b / wc_ms / 1e6 / HBM_PEAK_GBS, 4)}
 
 
 if __name__ == "__main__":
