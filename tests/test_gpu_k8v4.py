@@ -305,6 +305,26 @@ def test_verify_240000_sampled_rows(orc, k8, dev):
         assert rel_err(out[i], d) <= TOL
 
 
+def test_decode_1048576_pool_bytes_and_output(orc, k8, dev):
+    """The longest context the pages run the format at: 1,048,576 cells in
+    4,096 permuted pages of 256, appended in 8,192-token chunks.  The whole
+    pool image is bit-exact with the oracle's, and one decode over all
+    cells (the bench's decode call at this size) matches the oracle's fp64
+    attention."""
+    say("decode 1048576")
+    ctx = 1 << 20
+    c = Case(orc, k8, dev, 8, ctx, 256, 4096, 4096, chunk=8192)
+    for r in range(3):
+        assert np.array_equal(c.gpool.runs[r].cpu().numpy(), c.opool.runs[r]), f"run {r} differs"
+    q = synth.queries(8, 0, 0, 1, 16, 256, np.float16)
+    ws = k8.attn_workspace(c.gpool, 1, ctx)
+    out = k8.attn_decode(c.gpool, c.gpt, t_(q[0], dev), ctx, ws).cpu().numpy()
+    ref = c.oracle_attention(orc, q, [ctx])[0]
+    err = rel_err(out, ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+
+
 # ------------------------------------------------------------------ runtime / prefill
 
 def test_one_hip_runtime_in_process(k8, dev):
