@@ -7,8 +7,9 @@ imports the product: they share no code.
 
 Everything arithmetic lives in ``k8v4_oracle.c`` (plain C, fp32 quantizers
 rounded as written, fp64 attention by definition); this module only marshals
-numpy arrays through ctypes.  Formats: 1 = int8 K/V, 2 = q4_0 K/V (both
-rotated), 3 = k8v4 (INT8 K + rotated Q4_0 V), following the pages
+numpy arrays through ctypes.  Formats: 0 = fp16 K/V (unquantized), 1 = int8
+K/V, 2 = q4_0 K/V (both rotated), 3 = k8v4 (INT8 K + rotated Q4_0 V),
+following the pages
 "#120 --kv k8v4: hybrid KV cache" (What, How, Tests) and
 "kv: --kv k8v4 streams with --kv-resident" (How).
 """

@@ -1,7 +1,10 @@
 /*
  * k8v4_oracle.c -- plain, slow, obviously-correct CPU oracle for the hybrid
  * "k8v4" KV cache (INT8 K + Walsh-Hadamard-rotated Q4_0 V) and the attention
- * that reads it, plus the int8 and q4_0 comparison formats.
+ * that reads it, plus the int8 and q4_0 comparison formats and an unquantized
+ * fp16 format (K and V rounded to fp16, the reference without dequantization;
+ * "#729 KV int8 vs fp16 KLD compare at 240K context" uses fp16 KV as its
+ * baseline).
  *
  * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
  * cpu_baseline leg of bench.py may load this library.  It shares no code,
