@@ -205,7 +205,7 @@ int launch_gather(const kv_pool *pool, const kv_seq *seq, int pos0, int n, void 
 // Yardstick for attainable HBM read bandwidth: every workgroup streams its
 // own contiguous share of the buffer, its 256 lanes reading four
 // consecutive 4 KB blocks per round with non-temporal 16-byte loads.  (On
-// MI355X this pattern reads ~7.1 TB/s over GBs; a grid-stride pattern, where
+// MI355X this pattern reads 6.8-7.1 TB/s over GBs; a grid-stride pattern, where
 // all workgroups sweep one narrow window together, stays near 5.8 TB/s.)
 // One word per workgroup is written only if the xor of everything read
 // equals a value that a fill with a repeated byte cannot produce, so the
