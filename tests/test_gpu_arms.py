@@ -198,3 +198,31 @@ def test_arm_prefill_32768_outliers_matches_verify(orc, k8, dev, fmt):
     say(f"  rel diff vs verify {err2:.3e}")
     assert err2 <= 2 * TOL
 
+
+
+def test_f16_240000_decode_and_prefill_sampled(orc, k8, dev):
+    """The fp16 format at the bench's full size: 240,000 cells in a
+    262,144-cell pool (permuted pages of 256).  The whole pool image
+    bit-exact with the oracle's, a decode over all cells and sampled rows of
+    the 8,192-query prefill chunk at [231,808, 240,000) against the oracle."""
+    say("fp16 240000 decode + prefill")
+    ctx = 240000
+    c = ArmCase(orc, k8, dev, FMT_F16, 9, ctx, 256, 1024, 1024)
+    for r in (0, 2):
+        assert np.array_equal(c.gpool.runs[r].cpu().numpy(), c.opool.runs[r]), f"run {r} differs"
+    q1 = synth.queries(9, 0, 0, 1, 16, 256, np.float16)
+    ws = k8.attn_workspace(c.gpool, 1, ctx)
+    out = k8.attn_decode(c.gpool, c.gpt, t_(q1[0], dev), ctx, ws).cpu().numpy()
+    ref = orc.attention_from_pool(c.opool, c.pt, q1, [ctx])[0]
+    err = rel_err(out, ref)
+    say(f"  decode rel err {err:.3e}")
+    assert err <= TOL
+    pos0, n_new = 231808, 8192
+    q = synth.queries(9, 0, 1, n_new, 16, 256, np.float16)
+    outp = k8.attn_prefill_chunk(c.gpool, c.gpt, t_(q, dev), pos0).cpu().numpy()
+    assert np.all(np.isfinite(outp))
+    rows = [0, 4097, 8191]
+    refp = orc.attention_from_pool(c.opool, c.pt, q[rows], [pos0 + i + 1 for i in rows])
+    errp = rel_err(outp[rows], refp)
+    say(f"  prefill rel err {errp:.3e}")
+    assert errp <= TOL
