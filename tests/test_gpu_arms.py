@@ -200,16 +200,18 @@ def test_arm_prefill_32768_outliers_matches_verify(orc, k8, dev, fmt):
 
 
 
-def test_f16_240000_decode_and_prefill_sampled(orc, k8, dev):
-    """The fp16 format at the bench's full size: 240,000 cells in a
+@pytest.mark.parametrize("fmt", [FMT_F16, FMT_INT8, FMT_Q4_0])
+def test_arm_240000_decode_and_prefill_sampled(orc, k8, dev, fmt):
+    """The comparison formats at the bench's full size: 240,000 cells in a
     262,144-cell pool (permuted pages of 256).  The whole pool image
     bit-exact with the oracle's, a decode over all cells and sampled rows of
     the 8,192-query prefill chunk at [231,808, 240,000) against the oracle."""
-    say("fp16 240000 decode + prefill")
+    say(f"arm 240000 decode + prefill fmt={fmt}")
     ctx = 240000
-    c = ArmCase(orc, k8, dev, FMT_F16, 9, ctx, 256, 1024, 1024)
-    for r in (0, 2):
-        assert np.array_equal(c.gpool.runs[r].cpu().numpy(), c.opool.runs[r]), f"run {r} differs"
+    c = ArmCase(orc, k8, dev, fmt, 9, ctx, 256, 1024, 1024)
+    for r in range(4):
+        if c.opool.runs[r] is not None:
+            assert np.array_equal(c.gpool.runs[r].cpu().numpy(), c.opool.runs[r]), f"run {r} differs"
     q1 = synth.queries(9, 0, 0, 1, 16, 256, np.float16)
     ws = k8.attn_workspace(c.gpool, 1, ctx)
     out = k8.attn_decode(c.gpool, c.gpt, t_(q1[0], dev), ctx, ws).cpu().numpy()
