@@ -46,7 +46,7 @@ def page_block(pool, run, page):
     return pool.runs[run][page * nb:(page + 1) * nb]
 
 
-@pytest.mark.parametrize("fmt", [1, 2, 3])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 def test_streamed_window_equals_resident_bitwise(k8, dev, fmt):
     import torch
     P, n_res, n_tab, n_win, ctx = 16, 80, 64, 70, 1000
