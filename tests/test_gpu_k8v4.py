@@ -325,6 +325,28 @@ def test_decode_1048576_pool_bytes_and_output(orc, k8, dev):
     assert err <= TOL
 
 
+def test_verify_16_rows_240000_row_passes(orc, k8, dev):
+    """The largest verify window (16 queries = 128 rows: three 16-row tiles
+    per wave over three row passes that share each split's reads) at
+    240,000 cells with mixed per-query limits; sampled rows against the
+    oracle, every row against a single-row verify of the same limit."""
+    say("verify 16 rows 240000")
+    c = Case(orc, k8, dev, 10, 240000, 256, 1024, 1024, chunk=8192)
+    q = synth.queries(10, 0, 0, 16, 16, 256, np.float16)
+    nv = [240000 - 3 * i for i in range(15)] + [123457]
+    ws = k8.attn_workspace(c.gpool, 16, 240000)
+    out = k8.attn_verify(c.gpool, c.gpt, t_(q, dev), nv, ws).cpu().numpy()
+    sample = [0, 7, 15]
+    ref = c.oracle_attention(orc, q[sample], [nv[i] for i in sample])
+    err = rel_err(out[sample], ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+    ws1 = k8.attn_workspace(c.gpool, 1, 240000)
+    for i in range(16):
+        one = k8.attn_verify(c.gpool, c.gpt, t_(q[i:i + 1], dev), [nv[i]], ws1).cpu().numpy()
+        assert rel_err(out[i], one[0]) <= TOL, i
+
+
 # ------------------------------------------------------------------ runtime / prefill
 
 def test_one_hip_runtime_in_process(k8, dev):
