@@ -509,3 +509,28 @@ def test_decode_batch_parity(orc, k8, dev, lens):
         say(f"  seq {b} len {lens[b]}: rel err {err:.3e}, vs single decode {err1:.3e}")
         assert err <= TOL
         assert err1 <= TOL
+
+
+def test_decode_batch_4x59904_quarter_tables(orc, k8, dev):
+    """The batched decode as the bench times it: one pool of 240,000 cells
+    (1,024 permuted pages of 256) and 4 sequences of 59,904 cells whose
+    tables are the four quarters of the pool's table; each output against
+    the oracle (sequence 0 and 3) and against attn_decode alone."""
+    say("decode batch 4 x 59904")
+    c = Case(orc, k8, dev, 12, 240000, 256, 1024, 1024, chunk=8192)
+    nb, cb = 4, 234 * 256
+    pps = cb // 256
+    tabs = [np.ascontiguousarray(c.pt[i * pps:(i + 1) * pps]) for i in range(nb)]
+    gtabs = [t_(t, dev) for t in tabs]
+    q = synth.queries(12, 0, 0, nb, 16, 256, np.float16)
+    ws = k8.attn_workspace(c.gpool, nb, cb)
+    out = k8.attn_decode_batch(c.gpool, gtabs, t_(q, dev), [cb] * nb, ws).cpu().numpy()
+    ws1 = k8.attn_workspace(c.gpool, 1, cb)
+    for b in range(nb):
+        one = k8.attn_decode(c.gpool, gtabs[b], t_(q[b], dev), cb, ws1).cpu().numpy()
+        assert rel_err(out[b], one) <= TOL, b
+    for b in (0, 3):
+        ref = orc.attention_from_pool(c.opool, tabs[b], q[b:b + 1], [cb])[0]
+        err = rel_err(out[b], ref)
+        say(f"  seq {b}: rel err {err:.3e}")
+        assert err <= TOL
