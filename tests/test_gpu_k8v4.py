@@ -534,3 +534,38 @@ def test_decode_batch_4x59904_quarter_tables(orc, k8, dev):
         err = rel_err(out[b], ref)
         say(f"  seq {b}: rel err {err:.3e}")
         assert err <= TOL
+
+
+def test_calls_on_two_streams_with_own_workspaces(k8, dev):
+    """Every entry point takes a stream: decodes and verifies issued on two
+    side streams (default priority), each with its own workspace and output,
+    give bitwise the results of the same calls on the current stream."""
+    import torch
+    say("two streams")
+    ctx, P, n_pages = 32768, 256, 128
+    pool = k8.K8V4Pool(n_pages, P, 2, device=dev)
+    pt = t_(synth.page_table(13, n_pages, n_pages), dev)
+    for s0 in range(0, ctx, 8192):
+        k, v = synth.kv_tokens(13, 0, s0, 8192, 2, 256, np.float16)
+        k8.kv_append_k8v4(pool, pt, t_(k, dev), t_(v, dev), s0)
+    q = t_(synth.queries(13, 0, 0, 5, 16, 256, np.float16), dev)
+    nv = [ctx - 4, ctx - 3, ctx - 2, ctx - 1, ctx]
+    ws_a = k8.attn_workspace(pool, 5, ctx)
+    ref_d = k8.attn_decode(pool, pt, q[0], ctx, ws_a).clone()
+    ref_v = k8.attn_verify(pool, pt, q, nv, ws_a).clone()
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    ws_b = k8.attn_workspace(pool, 5, ctx)
+    outs_d, outs_v = [], []
+    cur = torch.cuda.current_stream()
+    sa.wait_stream(cur)
+    sb.wait_stream(cur)
+    for i in range(4):
+        s, ws = (sa, ws_a) if i % 2 == 0 else (sb, ws_b)
+        with torch.cuda.stream(s):
+            outs_d.append(k8.attn_decode(pool, pt, q[0], ctx, ws, stream=s))
+            outs_v.append(k8.attn_verify(pool, pt, q, nv, ws, stream=s))
+    torch.cuda.synchronize()
+    for d, v in zip(outs_d, outs_v):
+        assert torch.equal(d, ref_d)
+        assert torch.equal(v, ref_v)
