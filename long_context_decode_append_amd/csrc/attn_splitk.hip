@@ -599,8 +599,8 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
           // K chunk j of this half consumed: refill with the next step's
           kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + kstep_j * j, nx[h2]->k_soff, kAux);
         }
-        // the softmax scale folds into the cells' two K group scales once,
-        // for all row tiles
+        // several row tiles: the softmax scale folds into the cells' two K
+        // group scales once, for all of them
         float dk0[4], dk1[4];
         for (int i = 0; i < 4; i++) {
           const f32x4 kq = ksr[h2][i >> 1];
@@ -609,8 +609,12 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
         }
         for (int t = 0; t < T; t++)
           for (int i = 0; i < 4; i++) {
-            if (kInt8K) {
+            if (kInt8K && T > 1) {
               s[t][4 * h2 + i] = dk0[i] * (acc0[t][i] - cbias[t][0]) + dk1[i] * (acc1[t][i] - cbias[t][1]);
+            } else if (kInt8K) {
+              const f32x4 kq = ksr[h2][i >> 1];
+              const float d0 = kq[2 * (i & 1)], d1 = kq[2 * (i & 1) + 1];
+              s[t][4 * h2 + i] = a.scale2 * (d0 * (acc0[t][i] - cbias[t][0]) + d1 * (acc1[t][i] - cbias[t][1]));
             } else {
               s[t][4 * h2 + i] = a.scale2 * acc0[t][i];
             }
