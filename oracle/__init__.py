@@ -35,7 +35,10 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
+    # rebuilt whenever the C source is newer than the library, so an edit to
+    # the oracle can never be tested against a stale build
+    if (not os.path.exists(_LIB_PATH)
+            or os.path.getmtime(_LIB_PATH) < os.path.getmtime(os.path.join(_HERE, "k8v4_oracle.c"))):
         from . import build as _b
         _b.build()
     lib = C.CDLL(_LIB_PATH)
@@ -159,23 +162,18 @@ def cell_bytes(fmt: int, n_kv_heads: int, head_dim: int = D) -> int:
 # ---------------------------------------------------------------- pool image
 
 class OraclePool:
-    """Byte image of a paged pool: runs indexed [page][kv head][slot].
+    """Byte image of a paged pool in the plain order: every run is indexed
+    [page][kv head][slot], one record per head-cell
+    hc = (page*H + head)*P + slot (the pages fix the three runs of a k8v4
+    block and the bytes per cell, not the order inside a page):
 
-    run 0: K codes (int8, 256 B per head-cell) or K q4_0 tile (q4_0 format)
-    run 1: K scales (2 x fp32 per head-cell)
-    run 2: V q4_0 tile (k8v4, q4_0) or V codes (int8 format)
-    run 3: V scales (int8 format only)
-    K codes of head-cell hc = (page*H + head)*P + slot: each group of 16
-    head-cells is a 4096-byte block [dim quarter][hc % 16][64 codes], code c
-    at (hc//16)*4096 + (c//64)*1024 + (hc%16)*64 + c%64 (P a multiple of
-    16).  INT8 V codes (int8 format) are plain rows, code c at hc*256 + c.
-    fp16 format: K and V as fp16 in 8192-byte blocks of 16 head-cells; with
-    c = hc % 16, K element d at (hc//16)*8192 + (d//32)*1024 + ((d%32)//8)*256
-    + c*16 + (d%8)*2 and V element d at (hc//16)*8192 + ((d%16)//2)*1024 +
-    (c//4)*256 + (d//16)*16 + (d%2)*8 + (c%4)*2.
-    A q4_0 (page, head) tile is 144*P bytes: nibble bytes of block b of slot s
-    at s*128 + b*16; the fp16 scale of block b of slot s at
-    128*P + (s//16)*256 + b*32 + (s%16)*2 (scales grouped by 16 slots).
+    INT8 codes   256 int8 at hc*256          INT8 scales  2 fp32 at hc*8
+    Q4_0 blocks  8 x 18 bytes at hc*144      fp16 values  256 fp16 at hc*512
+
+    run 0: K codes (k8v4, int8), K blocks (q4_0) or K values (fp16)
+    run 1: K scales (k8v4, int8)
+    run 2: V blocks (k8v4, q4_0), V codes (int8) or V values (fp16)
+    run 3: V scales (int8)
     """
 
     def __init__(self, fmt: int, n_pages: int, page_size: int, n_kv_heads: int,

@@ -190,99 +190,49 @@ long orc_cell_bytes(int fmt, int n_kv_heads, int D) {
 }
 
 /* ------------------------------------------------------------------ */
-/* Pool placement.  The pool is a set of byte runs (K codes, K scales, */
-/* V data, V scales), each indexed [physical page][kv head][slot]      */
-/* [PR711, How: three runs for k8v4].  A logical cell p lives in       */
-/* physical page pt[p / P] at slot p % P.  Q4_0 data inside a          */
-/* (page, head) tile of 144*P bytes: the 16 nibble bytes of block b of */
-/* slot s at s*128 + b*16; the fp16 scales after the 128*P nibble     */
-/* bytes, in groups of 16 slots (256 bytes each, [block][slot % 16]):  */
-/* block b of slot s at 128*P + (s/16)*256 + b*32 + (s%16)*2.          */
-/* K codes: head-cell hc = (page*H + head)*P + slot; each group of 16   */
-/* head-cells is a 4096-byte block [dim quarter][hc % 16][64 codes]:    */
-/* code c of hc at (hc/16)*4096 + (c/64)*1024 + (hc%16)*64 + c%64.      */
-/* (INT8 V codes of the int8 format stay [hc][256].)  P must be a       */
-/* multiple of 16, so a 16-cell group never straddles two tiles.        */
-/* fp16 format (0): K and V as fp16, 8192 bytes per 16 head-cells each; */
-/* with c = hc % 16, K element d at (hc/16)*8192 + (d/32)*1024 +        */
-/* ((d%32)/8)*256 + c*16 + (d%8)*2, V element d at (hc/16)*8192 +       */
-/* ((d%16)/2)*1024 + (c/4)*256 + (d/16)*16 + (d%2)*8 + (c%4)*2.          */
+/* Pool placement [PR711, How: a k8v4 block is three byte runs -- K    */
+/* codes, K scales, V q4_0 -- moved as whole pages].  The pages fix    */
+/* the runs and the bytes per cell, not the order of bytes inside a    */
+/* page; this image takes the plain order.  Every run is indexed       */
+/* [physical page][kv head][slot], and a head-cell                     */
+/* hc = (page * H + head) * P + slot holds, in each run, one record:   */
+/*   INT8 codes:   256 int8, code c at byte hc * 256 + c               */
+/*   INT8 scales:  two fp32 (dims 0..127, 128..255) at hc * 8          */
+/*   Q4_0 blocks:  8 conventional 18-byte blocks (fp16 scale, then 16  */
+/*                 nibble bytes) at hc * 144 + b * 18                  */
+/*   fp16 values:  256 fp16 (little-endian) at hc * 512 + 2 d          */
+/* A logical cell p lives in physical page pt[p / P] at slot p % P.    */
+/* Run use per format: k8v4 = K codes, K scales, V blocks; int8 = K    */
+/* codes, K scales, V codes, V scales; q4_0 = K blocks, -, V blocks;   */
+/* fp16 = K values, -, V values.  (A library may order the bytes       */
+/* inside a page differently; its tests map its image onto this one.)  */
 /* ------------------------------------------------------------------ */
 
-typedef struct {
-  int fmt, n_pages, P, H;
-  uint8_t *run[4];
-} orc_pool;
+#define ORC_NSC (ORC_D / ORC_KGROUP)                 /* scales per head   */
+#define ORC_QHEAD ((ORC_D / ORC_QBLK) * ORC_QBYTES)  /* 144 B per head    */
 
-static size_t tile_index(int page, int g, int H) { return (size_t)page * H + g; }
-
-static size_t k_code_pos(size_t hc, int c) {
-  return (hc / 16) * 4096 + (size_t)(c / 64) * 1024 + (hc % 16) * 64 + (size_t)(c % 64);
+static size_t head_cell(int page, int g, int H, int P, int slot) {
+  return ((size_t)page * H + g) * P + slot;
 }
 
-/* one head's INT8 codes and scales; k_layout: codes in the K-code layout */
-/* above, else as a plain [hc][256] row                                 */
-static void put_int8_head(uint8_t *codes_run, uint8_t *scales_run, size_t ti, int P, int slot,
-                          const int8_t *codes, const float *scales, int k_layout) {
-  const size_t hc = ti * P + slot;
-  for (int c = 0; c < ORC_D; c++)
-    codes_run[k_layout ? k_code_pos(hc, c) : hc * ORC_D + c] = (uint8_t)codes[c];
-  memcpy(scales_run + (hc * (ORC_D / ORC_KGROUP)) * 4, scales, 4 * (ORC_D / ORC_KGROUP));
+static void put_int8_head(uint8_t *codes_run, uint8_t *scales_run, size_t hc, const int8_t *codes,
+                          const float *scales) {
+  memcpy(codes_run + hc * ORC_D, codes, ORC_D);
+  memcpy(scales_run + hc * ORC_NSC * 4, scales, ORC_NSC * 4);
 }
 
-static size_t f16_k_pos(size_t hc, int d) {
-  return (hc / 16) * 8192 + (size_t)(d / 32) * 1024 + (size_t)((d % 32) / 8) * 256 + (hc % 16) * 16 +
-         (size_t)(d % 8) * 2;
+static void get_int8_head(const uint8_t *codes_run, const uint8_t *scales_run, size_t hc, uint8_t *codes,
+                          uint8_t *scales) {
+  memcpy(codes, codes_run + hc * ORC_D, ORC_D);
+  memcpy(scales, scales_run + hc * ORC_NSC * 4, ORC_NSC * 4);
 }
 
-static size_t f16_v_pos(size_t hc, int d) {
-  const size_t c = hc % 16;
-  return (hc / 16) * 8192 + (size_t)((d % 16) / 2) * 1024 + (c / 4) * 256 + (size_t)(d / 16) * 16 +
-         (size_t)(d % 2) * 8 + (c % 4) * 2;
-}
-
-/* one head of the fp16 format: each value rounded to fp16 (RNE), stored */
-/* little-endian at its position                                        */
-static void put_f16_head(uint8_t *run, size_t hc, const float *x, int is_v) {
+/* one head of the fp16 format: each value rounded to fp16 (RNE) */
+static void put_f16_head(uint8_t *run, size_t hc, const float *x) {
   for (int d = 0; d < ORC_D; d++) {
     const uint16_t h = orc_f32_to_f16(x[d]);
-    const size_t at = is_v ? f16_v_pos(hc, d) : f16_k_pos(hc, d);
-    run[at] = (uint8_t)(h & 0xff);
-    run[at + 1] = (uint8_t)(h >> 8);
-  }
-}
-
-static void get_f16_head(const uint8_t *run, size_t hc, int is_v, uint8_t *out) {
-  for (int d = 0; d < ORC_D; d++) {
-    const size_t at = is_v ? f16_v_pos(hc, d) : f16_k_pos(hc, d);
-    out[2 * d] = run[at];
-    out[2 * d + 1] = run[at + 1];
-  }
-}
-
-static void get_int8_codes(const uint8_t *codes_run, size_t hc, int k_layout, uint8_t *out) {
-  for (int c = 0; c < ORC_D; c++) out[c] = codes_run[k_layout ? k_code_pos(hc, c) : hc * ORC_D + c];
-}
-
-static size_t q4_scale_pos(int P, int slot, int b) {
-  return (size_t)128 * P + (size_t)(slot / 16) * 256 + (size_t)b * 32 + (size_t)(slot % 16) * 2;
-}
-
-static void put_q4_head(uint8_t *run, size_t ti, int P, int slot, const uint8_t *blocks) {
-  uint8_t *tile = run + ti * (size_t)144 * P;
-  for (int b = 0; b < ORC_D / ORC_QBLK; b++) {
-    const uint8_t *blk = blocks + b * ORC_QBYTES;
-    memcpy(tile + (size_t)slot * 128 + b * 16, blk + 2, 16);
-    memcpy(tile + q4_scale_pos(P, slot, b), blk, 2);
-  }
-}
-
-static void get_q4_head(const uint8_t *run, size_t ti, int P, int slot, uint8_t *blocks) {
-  const uint8_t *tile = run + ti * (size_t)144 * P;
-  for (int b = 0; b < ORC_D / ORC_QBLK; b++) {
-    uint8_t *blk = blocks + b * ORC_QBYTES;
-    memcpy(blk, tile + q4_scale_pos(P, slot, b), 2);
-    memcpy(blk + 2, tile + (size_t)slot * 128 + b * 16, 16);
+    run[hc * 2 * ORC_D + 2 * d] = (uint8_t)(h & 0xff);
+    run[hc * 2 * ORC_D + 2 * d + 1] = (uint8_t)(h >> 8);
   }
 }
 
@@ -309,11 +259,10 @@ static void quant_rot_q4(const float *x, uint8_t *blocks) {
 int orc_append(int fmt, int n_pages, int P, int H, uint8_t *run0, uint8_t *run1, uint8_t *run2,
                uint8_t *run3, const int32_t *pt, int n_table, const void *k, const void *v,
                int dtype, int pos0, int n) {
-  if (P <= 0 || P % 16 || pos0 < 0 || n < 0 || (long)pos0 + n > (long)n_table * P) return -1;
+  if (P <= 0 || pos0 < 0 || n < 0 || (long)pos0 + n > (long)n_table * P) return -1;
   float kx[ORC_D], vx[ORC_D];
   int8_t codes[ORC_D];
   float scales[ORC_D / ORC_KGROUP];
-  uint8_t blocks[(ORC_D / ORC_QBLK) * ORC_QBYTES];
   for (int t = 0; t < n; t++) {
     int p = pos0 + t;
     int page = pt[p / P], slot = p % P;
@@ -324,25 +273,22 @@ int orc_append(int fmt, int n_pages, int P, int H, uint8_t *run0, uint8_t *run1,
         kx[c] = load_in(k, dtype, base + c);
         vx[c] = load_in(v, dtype, base + c);
       }
-      size_t ti = tile_index(page, g, H);
+      const size_t hc = head_cell(page, g, H, P, slot);
       if (fmt == 0) {
-        put_f16_head(run0, ti * P + slot, kx, 0);
-        put_f16_head(run2, ti * P + slot, vx, 1);
+        put_f16_head(run0, hc, kx);
+        put_f16_head(run2, hc, vx);
       } else if (fmt == 3) {
         quant_k_int8(kx, codes, scales);
-        put_int8_head(run0, run1, ti, P, slot, codes, scales, 1);
-        quant_rot_q4(vx, blocks);
-        put_q4_head(run2, ti, P, slot, blocks);
+        put_int8_head(run0, run1, hc, codes, scales);
+        quant_rot_q4(vx, run2 + hc * ORC_QHEAD);
       } else if (fmt == 1) {
         quant_k_int8(kx, codes, scales);
-        put_int8_head(run0, run1, ti, P, slot, codes, scales, 1);
+        put_int8_head(run0, run1, hc, codes, scales);
         quant_k_int8(vx, codes, scales);
-        put_int8_head(run2, run3, ti, P, slot, codes, scales, 0);
+        put_int8_head(run2, run3, hc, codes, scales);
       } else if (fmt == 2) {
-        quant_rot_q4(kx, blocks);
-        put_q4_head(run0, ti, P, slot, blocks);
-        quant_rot_q4(vx, blocks);
-        put_q4_head(run2, ti, P, slot, blocks);
+        quant_rot_q4(kx, run0 + hc * ORC_QHEAD);
+        quant_rot_q4(vx, run2 + hc * ORC_QHEAD);
       } else {
         return -1;
       }
@@ -364,34 +310,23 @@ int orc_append(int fmt, int n_pages, int P, int H, uint8_t *run0, uint8_t *run1,
 int orc_gather(int fmt, int n_pages, int P, int H, const uint8_t *run0, const uint8_t *run1,
                const uint8_t *run2, const uint8_t *run3, const int32_t *pt, int n_table,
                int pos0, int n, uint8_t *out0, uint8_t *out1, uint8_t *out2, uint8_t *out3) {
-  if (P <= 0 || P % 16 || pos0 < 0 || n < 0 || (long)pos0 + n > (long)n_table * P) return -1;
-  const size_t nsc = ORC_D / ORC_KGROUP;
-  const size_t qb = (ORC_D / ORC_QBLK) * ORC_QBYTES;
+  if (P <= 0 || pos0 < 0 || n < 0 || (long)pos0 + n > (long)n_table * P) return -1;
   for (int t = 0; t < n; t++) {
     int p = pos0 + t;
     int page = pt[p / P], slot = p % P;
     if (page < 0 || page >= n_pages) return -1;
     for (int g = 0; g < H; g++) {
-      size_t ti = tile_index(page, g, H);
-      size_t o = (size_t)t * H + g;
-      size_t cell = ti * P + slot;
+      const size_t hc = head_cell(page, g, H, P, slot);
+      const size_t o = (size_t)t * H + g;
       if (fmt == 0) {
-        get_f16_head(run0, cell, 0, out0 + o * 2 * ORC_D);
-        get_f16_head(run2, cell, 1, out2 + o * 2 * ORC_D);
+        memcpy(out0 + o * 2 * ORC_D, run0 + hc * 2 * ORC_D, 2 * ORC_D);
+        memcpy(out2 + o * 2 * ORC_D, run2 + hc * 2 * ORC_D, 2 * ORC_D);
         continue;
       }
-      if (fmt == 1 || fmt == 3) {
-        get_int8_codes(run0, cell, 1, out0 + o * ORC_D);
-        memcpy(out1 + o * nsc * 4, run1 + cell * nsc * 4, nsc * 4);
-      } else {
-        get_q4_head(run0, ti, P, slot, out0 + o * qb);
-      }
-      if (fmt == 1) {
-        get_int8_codes(run2, cell, 0, out2 + o * ORC_D);
-        memcpy(out3 + o * nsc * 4, run3 + cell * nsc * 4, nsc * 4);
-      } else {
-        get_q4_head(run2, ti, P, slot, out2 + o * qb);
-      }
+      if (fmt == 1 || fmt == 3) get_int8_head(run0, run1, hc, out0 + o * ORC_D, out1 + o * ORC_NSC * 4);
+      else memcpy(out0 + o * ORC_QHEAD, run0 + hc * ORC_QHEAD, ORC_QHEAD);
+      if (fmt == 1) get_int8_head(run2, run3, hc, out2 + o * ORC_D, out3 + o * ORC_NSC * 4);
+      else memcpy(out2 + o * ORC_QHEAD, run2 + hc * ORC_QHEAD, ORC_QHEAD);
     }
   }
   return 0;

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 from long_context_decode_append_amd import synth
+from pool_layout import assert_pool_equal
 
 pytestmark = pytest.mark.gpu
 
@@ -73,10 +74,8 @@ def test_arm_pool_bytes_and_gather_bitwise(orc, k8, dev, fmt, dtype, ctx, P, n_p
     say(f"arm append/gather fmt={fmt} dtype={dtype.__name__} ctx={ctx} P={P}")
     c = ArmCase(orc, k8, dev, fmt, 0, ctx, P, n_pages, (ctx + P - 1) // P, dtype=dtype, chunk=333)
     for r in range(4):
-        if c.opool.runs[r] is None:
-            assert c.gpool.runs[r] is None
-            continue
-        assert np.array_equal(c.gpool.runs[r].cpu().numpy(), c.opool.runs[r]), f"run {r} differs"
+        assert (c.opool.runs[r] is None) == (c.gpool.runs[r] is None), f"run {r} presence"
+    assert_pool_equal(c.gpool, c.opool)
     g = [x.cpu().numpy() for x in k8.kv_gather_runs(c.gpool, c.gpt, 0, ctx)]
     o = c.opool.gather(c.pt, 0, ctx)
     assert len(g) == len(o)
@@ -209,9 +208,7 @@ def test_arm_240000_decode_and_prefill_sampled(orc, k8, dev, fmt):
     say(f"arm 240000 decode + prefill fmt={fmt}")
     ctx = 240000
     c = ArmCase(orc, k8, dev, fmt, 9, ctx, 256, 1024, 1024)
-    for r in range(4):
-        if c.opool.runs[r] is not None:
-            assert np.array_equal(c.gpool.runs[r].cpu().numpy(), c.opool.runs[r]), f"run {r} differs"
+    assert_pool_equal(c.gpool, c.opool)
     q1 = synth.queries(9, 0, 0, 1, 16, 256, np.float16)
     ws = k8.attn_workspace(c.gpool, 1, ctx)
     out = k8.attn_decode(c.gpool, c.gpt, t_(q1[0], dev), ctx, ws).cpu().numpy()

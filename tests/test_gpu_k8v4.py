@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 from long_context_decode_append_amd import synth
+from pool_layout import assert_pool_equal
 
 pytestmark = pytest.mark.gpu
 
@@ -80,9 +81,7 @@ def test_append_pool_bytes_and_gather_bitwise(orc, k8, dev, dtype, ctx, P, n_pag
     say(f"append/gather dtype={dtype.__name__} ctx={ctx} P={P}")
     n_table = (ctx + P - 1) // P
     c = Case(orc, k8, dev, 0, ctx, P, n_pages, n_table, dtype=dtype, chunk=333)
-    for r in range(3):
-        g = c.gpool.runs[r].cpu().numpy()
-        assert np.array_equal(g, c.opool.runs[r]), f"run {r} differs"
+    assert_pool_equal(c.gpool, c.opool)
     gk, gs, gv = [x.cpu().numpy() for x in k8.kv_gather(c.gpool, c.gpt, 0, ctx)]
     ok, os_, ov = c.opool.gather(c.pt, 0, ctx)
     assert np.array_equal(gk, ok)
@@ -124,8 +123,7 @@ def test_quantizer_edge_values(orc, k8, dev):
     o = orc.OraclePool(3, 1, 16, 2, sentinel=0x5A)
     k8.kv_append_k8v4(g, t_(pt, dev), t_(x, dev), t_(x, dev), 0)
     o.append(pt, x, x, 0)
-    for r in range(3):
-        assert np.array_equal(g.runs[r].cpu().numpy(), o.runs[r])
+    assert_pool_equal(g, o)
 
 
 # ------------------------------------------------------------------ decode / verify
@@ -265,8 +263,7 @@ def test_decode_118750_filled_in_chunks(orc, k8, dev):
     err = rel_err(out, c.oracle_attention(orc, q, [118750])[0])
     say(f"  rel err {err:.3e}")
     assert err <= TOL
-    for r in range(3):
-        assert np.array_equal(c.gpool.runs[r].cpu().numpy(), c.opool.runs[r])
+    assert_pool_equal(c.gpool, c.opool)
     # the bench step's call: the fused append of the token of cell 118,749
     # over a pool holding cells [0, 118,749)
     say("fused append + decode at 118,749")
@@ -274,8 +271,7 @@ def test_decode_118750_filled_in_chunks(orc, k8, dev):
     k, v = synth.kv_tokens(3, 0, 118749, 1, 2, 256, np.float16)
     out = k8.attn_decode_append(d.gpool, d.gpt, t_(k[0], dev), t_(v[0], dev), t_(q[0], dev), 118749, ws)
     d.opool.append(d.pt, k, v, 118749)
-    for r in range(3):
-        assert np.array_equal(d.gpool.runs[r].cpu().numpy(), d.opool.runs[r])
+    assert_pool_equal(d.gpool, d.opool)
     err = rel_err(out.cpu().numpy(), d.oracle_attention(orc, q, [118750])[0])
     say(f"  rel err {err:.3e}")
     assert err <= TOL
@@ -314,8 +310,7 @@ def test_decode_1048576_pool_bytes_and_output(orc, k8, dev):
     say("decode 1048576")
     ctx = 1 << 20
     c = Case(orc, k8, dev, 8, ctx, 256, 4096, 4096, chunk=8192)
-    for r in range(3):
-        assert np.array_equal(c.gpool.runs[r].cpu().numpy(), c.opool.runs[r]), f"run {r} differs"
+    assert_pool_equal(c.gpool, c.opool)
     q = synth.queries(8, 0, 0, 1, 16, 256, np.float16)
     ws = k8.attn_workspace(c.gpool, 1, ctx)
     out = k8.attn_decode(c.gpool, c.gpt, t_(q[0], dev), ctx, ws).cpu().numpy()

@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 from long_context_decode_append_amd import synth
+from pool_layout import assert_pool_equal
 
 pytestmark = pytest.mark.gpu
 
@@ -62,9 +63,7 @@ def test_odd_pages_and_head_counts(orc, k8, dev, P, H, n_pages, n_table):
         k8.kv_append_k8v4(gpool, gpt, t_(k, dev), t_(v, dev), s)
         opool.append(pt, k, v, s)
     # every stored byte (sentinels included) equals the oracle's image
-    for r, (g, o) in enumerate(zip(gpool.runs, opool.runs)):
-        if g is not None:
-            assert np.array_equal(g.cpu().numpy(), o), f"run {r}"
+    assert_pool_equal(gpool, opool)
     Hq = 8 * H
     # decode at a few lengths, incl. one ending inside a page and the full fill
     for n_ctx in (1, P - 1, P + 17, ctx):
@@ -98,9 +97,7 @@ def test_odd_pages_and_head_counts(orc, k8, dev, P, H, n_pages, n_table):
     out = k8.attn_decode_append(gpool, gpt, t_(k[0], dev), t_(v[0], dev), t_(q[0], dev), ctx, ws)
     torch.cuda.synchronize()
     opool.append(pt, k, v, ctx)
-    for r, (g, o) in enumerate(zip(gpool.runs, opool.runs)):
-        if g is not None:
-            assert np.array_equal(g.cpu().numpy(), o), f"run {r} after the fused append"
+    assert_pool_equal(gpool, opool, "after the fused append")
     err = rel_err(out.cpu().numpy(), orc.attention_from_pool(opool, pt, q, [ctx + 1])[0])
     say(f"  decode_append rel err {err:.3e}")
     assert err <= TOL

@@ -48,25 +48,36 @@ def test_gather_returns_direct_quantization(orc, fmt):
         assert a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
-def test_pool_bytes_at_documented_offsets(orc):
-    P, H = 16, 2
-    pool, pt, k, v = _pool_with(orc, 3, P=P, n_pages=6, n_table=5, n_tok=70, seed=2)
-    kc, ks, vb = pool.gather(pt, 0, 70)
-    r0, r1, r2, _ = pool.runs
-    for p in (0, 1, 15, 16, 33, 69):
-        page, slot = pt[p // P], p % P
-        for g in range(H):
-            cell = (page * H + g) * P + slot
-            # K codes: 16-cell blocks of 4 KB, [dim quarter][cell % 16][64 codes]
-            kpos = (cell // 16) * 4096 + (np.arange(256) // 64) * 1024 + (cell % 16) * 64 + np.arange(256) % 64
-            assert np.array_equal(r0[kpos].view(np.int8), kc[p, g])
-            assert np.array_equal(r1[cell * 8:(cell + 1) * 8].view(np.float32), ks[p, g])
-            tile = (page * H + g) * 144 * P
-            for b in range(8):
-                q = r2[tile + slot * 128 + b * 16: tile + slot * 128 + b * 16 + 16]
-                so = tile + 128 * P + (slot // 16) * 256 + b * 32 + (slot % 16) * 2
-                s = r2[so: so + 2]
-                assert np.array_equal(q, vb[p, g, b, 2:]) and np.array_equal(s, vb[p, g, b, :2])
+@pytest.mark.parametrize("fmt", [3, 1, 2, 0])
+def test_pool_image_is_the_quantized_inputs_placed_by_page(orc, fmt):
+    """Each run is [physical page][kv head][slot][record]: logical page i's
+    records, head-major, sit in physical page pt[i] (checked by numpy
+    reshapes of the directly quantized inputs, not by offset formulas)."""
+    P, H, n_pages, n_table = 16, 2, 7, 6
+    n_tok = n_table * P
+    pool, pt, k, v = _pool_with(orc, fmt, P=P, n_pages=n_pages, n_table=n_table, n_tok=n_tok, seed=2)
+    kf, vf = k.astype(np.float32), v.astype(np.float32)
+    if fmt == 3:
+        kc, ks = orc.quant_int8(kf)
+        recs = [kc, ks, orc.quant_q4(orc.fwht256(vf)), None]
+    elif fmt == 1:
+        kc, ks = orc.quant_int8(kf)
+        vc, vs = orc.quant_int8(vf)
+        recs = [kc, ks, vc, vs]
+    elif fmt == 2:
+        recs = [orc.quant_q4(orc.fwht256(kf)), None, orc.quant_q4(orc.fwht256(vf)), None]
+    else:
+        recs = [k.astype(np.float16), None, v.astype(np.float16), None]
+    for r, rec in enumerate(recs):
+        if rec is None:
+            assert pool.runs[r] is None
+            continue
+        rb = np.ascontiguousarray(rec).view(np.uint8).reshape(n_table, P, H, -1)   # [logical page][slot][head][bytes]
+        by_page = rb.transpose(0, 2, 1, 3).reshape(n_table, -1)                   # [logical page][head][slot][bytes]
+        img = pool.runs[r].reshape(n_pages, -1)
+        assert np.array_equal(img[pt], by_page), f"run {r}"
+        unused = np.setdiff1d(np.arange(n_pages), pt)
+        assert np.all(img[unused] == 0xA5)
 
 
 def test_identity_vs_permuted_page_table(orc):
@@ -87,13 +98,13 @@ def test_unwritten_cells_keep_sentinel_and_wrong_table_is_detected(orc):
     P = 16
     pool, pt, _, _ = _pool_with(orc, 3, P=P, n_pages=10, n_table=6, n_tok=40, seed=4)
     used = set(int(x) for x in pt[:3])            # 40 tokens touch 3 pages, the third partly
-    r0 = pool.runs[0].reshape(10, 2, P // 16, 4, 16, 64)  # [page][head][16-cell block][quarter][cell][64]
+    r0 = pool.runs[0].reshape(10, 2, P, 256)      # [page][head][slot][256 codes]
     for page in range(10):
         if page not in used:
             assert np.all(r0[page] == 0xA5)
     third = int(pt[2])
-    assert np.all(r0[third, :, :, :, 8:] == 0xA5)
-    assert not np.any(np.all(r0[third, :, :, :, :8] == 0xA5, axis=-1))
+    assert np.all(r0[third, :, 8:] == 0xA5)
+    assert not np.any(np.all(r0[third, :, :8] == 0xA5, axis=-1))
     # negative control: a table with two entries swapped reads other bytes
     bad = pt.copy()
     bad[[0, 1]] = bad[[1, 0]]
@@ -255,20 +266,15 @@ def test_f16_gather_is_numpy_half_rounding(orc, dtype):
             assert np.all(r0[page] == 0xA5)
 
 
-def test_f16_bytes_at_documented_offsets(orc):
+def test_f16_values_placed_by_page(orc):
     P, H = 32, 2
-    pool, pt, k, v = _pool_with(orc, 0, P=P, n_pages=4, n_table=4, n_tok=70, seed=12)
-    r0, r2 = pool.runs[0].view(np.uint16), pool.runs[2].view(np.uint16)
-    d = np.arange(256)
-    for p in (0, 5, 16, 31, 32, 69):
-        page, slot = pt[p // P], p % P
-        for g in range(H):
-            hc = (page * H + g) * P + slot
-            c = hc % 16
-            kpos = (hc // 16) * 8192 + (d // 32) * 1024 + ((d % 32) // 8) * 256 + c * 16 + (d % 8) * 2
-            vpos = (hc // 16) * 8192 + ((d % 16) // 2) * 1024 + (c // 4) * 256 + (d // 16) * 16 + (d % 2) * 8 + (c % 4) * 2
-            assert np.array_equal(r0[kpos // 2], k[p, g].view(np.uint16))
-            assert np.array_equal(r2[vpos // 2], v[p, g].view(np.uint16))
+    pool, pt, k, v = _pool_with(orc, 0, P=P, n_pages=4, n_table=3, n_tok=70, seed=12)
+    for run, x in ((pool.runs[0], k), (pool.runs[2], v)):
+        img = run.view(np.uint16).reshape(4, H, P, 256)   # [page][head][slot][256]
+        for p in (0, 5, 16, 31, 32, 69):
+            page, slot = pt[p // P], p % P
+            for g in range(H):
+                assert np.array_equal(img[page, g, slot], x[p, g].view(np.uint16))
 
 
 def test_f16_attention_matches_brute_force_tiny(orc):

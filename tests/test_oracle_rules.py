@@ -115,20 +115,39 @@ def test_fwht_random_close_to_matrix_and_involution(orc):
     assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-5)
 
 
+def _butterfly_f32(x, strides):
+    """Independent numpy FWHT: per stride s, pairs (i, i+s) with i & s == 0
+    become (a + b, a - b), each a float32 numpy add or subtract; then * 1/16."""
+    y = np.array(x, np.float32, copy=True)
+    for s in strides:
+        blocks = y.reshape(y.shape[0], 256 // (2 * s), 2, s)
+        a, b = blocks[:, :, 0, :].copy(), blocks[:, :, 1, :].copy()
+        blocks[:, :, 0, :] = a + b
+        blocks[:, :, 1, :] = a - b
+    return y * np.float32(0.0625)
+
+
+def test_fwht_bits_equal_independent_ascending_butterfly(orc):
+    """The oracle's fp32 rotation bit for bit against a numpy butterfly with
+    strides 1, 2, ..., 128 (the order every Q4_0 code of V depends on),
+    on normal, heavy-tailed and wide-range inputs."""
+    rng = np.random.default_rng(17)
+    x = np.concatenate([
+        rng.standard_normal((200, 256)).astype(np.float32),
+        (rng.standard_cauchy((50, 256)) * 10).astype(np.float32),
+        (rng.standard_normal((50, 256)) * np.exp2(rng.integers(-30, 30, (50, 1)))).astype(np.float32),
+    ])
+    ref = _butterfly_f32(x, [1, 2, 4, 8, 16, 32, 64, 128])
+    ours = orc.fwht256(x)
+    assert np.array_equal(ours.view(np.uint32), ref.view(np.uint32))
+
+
 def test_fwht_stage_order_matters_in_fp32(orc):
     """Descending strides give other fp32 bits on random data, so the
     ascending-stride convention the oracle fixes is a real constraint."""
     rng = np.random.default_rng(5)
     x = rng.standard_normal((32, 256)).astype(np.float32)
-    y = x.copy()
-    s = 128
-    while s >= 1:
-        idx = np.arange(256)
-        lo = idx[(idx & s) == 0]
-        a, b = y[:, lo].copy(), y[:, lo + s].copy()
-        y[:, lo], y[:, lo + s] = a + b, a - b
-        s //= 2
-    y = y * np.float32(0.0625)
+    y = _butterfly_f32(x, [128, 64, 32, 16, 8, 4, 2, 1])
     ours = orc.fwht256(x)
     assert not np.array_equal(ours.view(np.uint32), y.view(np.uint32))
     assert np.allclose(ours, y, atol=1e-5)
