@@ -19,7 +19,10 @@
  *     NULL for the null stream) and return; device faults surface at the
  *     caller's next synchronization.
  *   - Every call returns KV_OK (0) or a negative KV_ERR_* code and launches
- *     nothing when it returns an error.  A required pointer that is NULL is
+ *     nothing when it returns an error found by its argument checks.  A HIP
+ *     error left by earlier, unrelated HIP calls on the calling thread is
+ *     cleared on entry, so KV_ERR_LAUNCH always reports the call's own
+ *     launch (kv_last_hip_error names it).  A required pointer that is NULL is
  *     an error (KV_ERR_NULL), never a silent skip: the pages report silent
  *     wrong output from writers that tested a pointer for presence and
  *     skipped the write.
@@ -342,8 +345,9 @@ const char *kv_last_hip_error(void);
  * duration.  Both are hipEvent_t created by the caller on the device of
  * the launch.  attn_decode and attn_verify launch the split kernel and then
  * a small combine kernel, so the hook times the split kernel; every other
- * entry point launches one kernel.  Calls that return before launching
- * (errors, empty work) leave the hook armed.  Errors: KV_ERR_NULL.
+ * entry point launches one kernel.  The hook applies to the next entry-point
+ * call only: a call that returns before launching (an error, empty work)
+ * disarms it.  Errors: KV_ERR_NULL.
  */
 int kv_time_next_launch(void *start_event, void *stop_event);
 

@@ -15,11 +15,14 @@ static thread_local char g_last_hip_error[256] = "no error";
 static thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 
 namespace k8v4 {
+void set_last_hip_error(hipError_t e) {
+  snprintf(g_last_hip_error, sizeof g_last_hip_error, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+}
+
 int launch_status() {
   const hipError_t e = hipGetLastError();
   if (e == hipSuccess) return KV_OK;
-  snprintf(g_last_hip_error, sizeof g_last_hip_error, "%s: %s", hipGetErrorName(e),
-           hipGetErrorString(e));
+  set_last_hip_error(e);
   return KV_ERR_LAUNCH;
 }
 
@@ -29,6 +32,24 @@ void take_launch_events(hipEvent_t *start, hipEvent_t *stop) {
   g_ev_start = g_ev_stop = nullptr;
 }
 }  // namespace k8v4
+
+namespace {
+// Scope of one entry-point call that may launch work.  On entry it clears
+// the HIP runtime's per-thread error slot, so a KV_ERR_LAUNCH returned by
+// this call is this call's own failure and never one left behind by an
+// earlier, unrelated HIP call.  On every return path it disarms a
+// kv_time_next_launch hook that this call did not consume (errors, empty
+// work), so the events never attach to a later, unrelated launch.
+struct CallScope {
+  CallScope() { (void)hipGetLastError(); }
+  ~CallScope() {
+    hipEvent_t a, b;
+    take_launch_events(&a, &b);
+  }
+  CallScope(const CallScope &) = delete;
+  CallScope &operator=(const CallScope &) = delete;
+};
+}  // namespace
 
 extern "C" {
 
@@ -67,6 +88,7 @@ int kv_time_next_launch(void *start_event, void *stop_event) {
 
 int kv_append_k8v4(const kv_pool *pool, const kv_seq *seq, const void *k, const void *v,
                    int dtype, int32_t pos0, int32_t n_tokens, void *stream) {
+  CallScope scope;
   if (int e = check_pool(pool, KV_FMT_K8V4)) return e;
   if (int e = check_seq(seq, pool)) return e;
   if (!k || !v) return KV_ERR_NULL;
@@ -79,6 +101,7 @@ int kv_append_k8v4(const kv_pool *pool, const kv_seq *seq, const void *k, const 
 
 int kv_append(const kv_pool *pool, const kv_seq *seq, const void *k, const void *v, int dtype, int32_t pos0,
               int32_t n_tokens, void *stream) {
+  CallScope scope;
   if (int e = check_pool(pool, 0)) return e;
   if (int e = check_seq(seq, pool)) return e;
   if (!k || !v) return KV_ERR_NULL;
@@ -91,6 +114,7 @@ int kv_append(const kv_pool *pool, const kv_seq *seq, const void *k, const void 
 
 int kv_gather(const kv_pool *pool, const kv_seq *seq, int32_t pos0, int32_t n, void *k_codes,
               void *k_scales, void *v_blocks, void *stream) {
+  CallScope scope;
   if (int e = check_pool(pool, KV_FMT_K8V4)) return e;
   if (int e = check_seq(seq, pool)) return e;
   if (!k_codes || !k_scales || !v_blocks) return KV_ERR_NULL;
@@ -103,6 +127,7 @@ int kv_gather(const kv_pool *pool, const kv_seq *seq, int32_t pos0, int32_t n, v
 
 int kv_gather_runs(const kv_pool *pool, const kv_seq *seq, int32_t pos0, int32_t n, void *out0, void *out1,
                    void *out2, void *out3, void *stream) {
+  CallScope scope;
   if (int e = check_pool(pool, 0)) return e;
   if (int e = check_seq(seq, pool)) return e;
   const int fmt = pool->fmt;
@@ -127,6 +152,7 @@ size_t attn_workspace_bytes(const kv_pool *pool, int n_q_heads, int32_t n_q, int
 }
 
 int kv_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+  CallScope scope;
   if (!ws) return KV_ERR_NULL;
   if (check_aligned16(ws)) return KV_ERR_ALIGN;
   return launch_fill_zero(ws, ws_bytes, (hipStream_t)stream);
@@ -134,6 +160,7 @@ int kv_workspace_init(void *ws, size_t ws_bytes, void *stream) {
 
 int kv_copy_pages(const kv_pool *dst, const kv_pool *src, const int32_t *dst_pages, const int32_t *src_pages,
                   int32_t n, void *stream) {
+  CallScope scope;
   if (int e = check_pool(dst, 0)) return e;
   if (int e = check_pool(src, 0)) return e;
   if (dst->fmt != src->fmt || dst->n_kv_heads != src->n_kv_heads || dst->page_size != src->page_size)
@@ -145,6 +172,7 @@ int kv_copy_pages(const kv_pool *dst, const kv_pool *src, const int32_t *dst_pag
 }
 
 int kv_probe_read(const void *buf, size_t bytes, void *sink, void *stream) {
+  CallScope scope;
   if (!buf || !sink) return KV_ERR_NULL;
   if (check_aligned16(buf) || check_aligned16(sink)) return KV_ERR_ALIGN;
   return launch_probe_read(buf, bytes, sink, (hipStream_t)stream);
@@ -165,14 +193,8 @@ static float pick_scale(float scale) {
   return scale > 0.0f ? scale : 1.0f / std::sqrt((float)kHeadDim);
 }
 
-int attn_decode(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
-                int n_q_heads, int32_t n_ctx, float scale, float *out, void *ws,
-                size_t ws_bytes, void *stream) {
-  if (int e = check_attn_common(pool, seq, q, q_dtype, n_q_heads, out, 0)) return e;
-  if (n_ctx < 1) return KV_ERR_RANGE;
-  if (int e = check_range(pool, seq, 0, n_ctx)) return e;
-  if (!ws) return KV_ERR_WORKSPACE;
-  if (check_aligned16(ws)) return KV_ERR_ALIGN;
+static int decode_call(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype, int n_q_heads,
+                       int32_t n_ctx, float scale, float *out, void *ws, size_t ws_bytes, void *stream) {
   AttnCall c;
   c.pool = pool;
   c.seq = seq;
@@ -191,9 +213,22 @@ int attn_decode(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dty
   return launch_attn_splitk(c);
 }
 
+int attn_decode(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
+                int n_q_heads, int32_t n_ctx, float scale, float *out, void *ws,
+                size_t ws_bytes, void *stream) {
+  CallScope scope;
+  if (int e = check_attn_common(pool, seq, q, q_dtype, n_q_heads, out, 0)) return e;
+  if (n_ctx < 1) return KV_ERR_RANGE;
+  if (int e = check_range(pool, seq, 0, n_ctx)) return e;
+  if (!ws) return KV_ERR_WORKSPACE;
+  if (check_aligned16(ws)) return KV_ERR_ALIGN;
+  return decode_call(pool, seq, q, q_dtype, n_q_heads, n_ctx, scale, out, ws, ws_bytes, stream);
+}
+
 int attn_decode_append(const kv_pool *pool, const kv_seq *seq, const void *k_new, const void *v_new,
                        int kv_dtype, const void *q, int q_dtype, int n_q_heads, int32_t pos, float scale,
                        float *out, void *ws, size_t ws_bytes, void *stream) {
+  CallScope scope;
   if (int e = check_attn_common(pool, seq, q, q_dtype, n_q_heads, out, KV_FMT_K8V4)) return e;
   if (!k_new || !v_new) return KV_ERR_NULL;
   if (int e = check_dtype(kv_dtype)) return e;
@@ -227,6 +262,7 @@ int attn_decode_append(const kv_pool *pool, const kv_seq *seq, const void *k_new
 int attn_decode_batch(const kv_pool *pool, const kv_seq *seqs, int32_t n_seq, const void *q, int q_dtype,
                       int n_q_heads, const int32_t *n_ctx, float scale, float *out, void *ws, size_t ws_bytes,
                       void *stream) {
+  CallScope scope;
   if (!seqs || !n_ctx) return KV_ERR_NULL;
   if (n_seq < 1 || n_seq > kMaxQ) return KV_ERR_SHAPE;
   if (int e = check_attn_common(pool, &seqs[0], q, q_dtype, n_q_heads, out, 0)) return e;
@@ -261,6 +297,7 @@ int attn_decode_batch(const kv_pool *pool, const kv_seq *seqs, int32_t n_seq, co
 int attn_verify(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
                 int n_q_heads, int32_t n_q, const int32_t *n_visible, float scale, float *out,
                 void *ws, size_t ws_bytes, void *stream) {
+  CallScope scope;
   if (int e = check_attn_common(pool, seq, q, q_dtype, n_q_heads, out, 0)) return e;
   if (!n_visible) return KV_ERR_NULL;
   if (n_q < 1 || n_q > kMaxQ) return KV_ERR_SHAPE;
@@ -292,6 +329,7 @@ int attn_verify(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dty
 int attn_prefill_chunk(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
                        int n_q_heads, int32_t pos0, int32_t n_new, float scale, float *out,
                        void *ws, size_t ws_bytes, void *stream) {
+  CallScope scope;
   (void)ws;
   (void)ws_bytes;
   if (int e = check_attn_common(pool, seq, q, q_dtype, n_q_heads, out, 0)) return e;
@@ -303,6 +341,7 @@ int attn_prefill_chunk(const kv_pool *pool, const kv_seq *seq, const void *q, in
 }
 
 int kv_check_page_table(const kv_pool *pool, const kv_seq *seq, int32_t n_cells, int32_t *n_bad) {
+  CallScope scope;
   if (int e = check_pool(pool, 0)) return e;
   if (int e = check_seq(seq, pool)) return e;
   if (!n_bad) return KV_ERR_NULL;

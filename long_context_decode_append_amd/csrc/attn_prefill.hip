@@ -94,6 +94,7 @@ struct PfRaw {
 struct PfHalves {
   int tile[2];
   int slot0[2];
+  int bad[2];  // page-table entry out of range: read page 0 instead, give NaN scores
   int P;
   // first cell of half hf in the pool's cell order (a select: hf varies by lane)
   __device__ __forceinline__ size_t cell(int hf) const {
@@ -110,10 +111,12 @@ __device__ __forceinline__ PfHalves pf_halves(const PrefillArgs &a, int g, int c
     const int c = c0 + 16 * i;
     h.tile[i] = 0;
     h.slot0[i] = 0;
+    h.bad[i] = 0;
     if (c < n_cells) {  // page-table entries past the visible cells are never read
       const int pidx = a.p_shift >= 0 ? (c >> a.p_shift) : c / a.P;
       int page = a.pt[pidx];
-      page = (page < 0 || page >= a.n_pages) ? 0 : page;
+      h.bad[i] = page < 0 || page >= a.n_pages;
+      page = h.bad[i] ? 0 : page;
       h.tile[i] = page * a.H + g;
       h.slot0[i] = c - pidx * a.P;
     }
@@ -122,8 +125,25 @@ __device__ __forceinline__ PfHalves pf_halves(const PrefillArgs &a, int g, int c
 }
 
 template <int FMT>
+__device__ __forceinline__ void pf_load_units(const PrefillArgs &a, const PfHalves &hv, int c0, int n_cells, int u,
+                                              PfRaw &r);
+
+// The tile's raw pages for work unit u; the K scale slots (units u < 64,
+// cell u / 2) of a half whose page-table entry is out of range hold NaN, so
+// every row whose causal window reaches that half returns NaN (rows that
+// stop before it mask those cells to -inf), while the loads read page 0
+// and never leave the pool.
+template <int FMT>
 __device__ __forceinline__ void pf_load(const PrefillArgs &a, const PfHalves &hv, int c0, int n_cells, int u,
                                         PfRaw &r) {
+  pf_load_units<FMT>(a, hv, c0, n_cells, u, r);
+  if (u < 2 * kPfTile && c0 + (u >> 1) < n_cells && (((u >> 5) ? hv.bad[1] : hv.bad[0]) != 0))
+    r.kd = __builtin_nanf("");
+}
+
+template <int FMT>
+__device__ __forceinline__ void pf_load_units(const PrefillArgs &a, const PfHalves &hv, int c0, int n_cells, int u,
+                                              PfRaw &r) {
   r.k = u32x4{0u, 0u, 0u, 0u};
   r.kd = a.scale2;
   if (FMT == KV_FMT_F16) {

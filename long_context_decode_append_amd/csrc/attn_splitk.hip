@@ -42,6 +42,7 @@
 //   * a fused append (decode of a k8v4 pool) adds one workgroup per KV head
 //     that quantizes the new token into its cell and writes it as one more
 //     partial, beside the streaming splits.
+#include <atomic>
 #include <numeric>
 
 #include "device.hpp"
@@ -661,22 +662,40 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
       // ---- O += P . V; the V scales of the cell pairs (k-slots 2k, 2k+1)
       // as fp16 pairs, zeroed for cells past the split
       uint32_t dsc[4] = {0u, 0u, 0u, 0u};
+      // INT8 V: the fp32 scales of the cell pairs, and whether any nonzero
+      // one lies below fp16's normal range (then this step forms code * d in
+      // fp32 and rounds once, since an fp16 scale would lose its bits)
+      float dsf[kQ4V || kF16 ? 1 : 4][2];
+      bool v8_tiny = false;
       for (int k = 0; k < (kF16 ? 0 : 4); k++) {
         const int h2 = k >> 1;
         uint32_t w;
+        float da = 0.f, db = 0.f;
         if (kQ4V) {
           w = (k & 1) ? vdr[h2].y : vdr[h2].x;
         } else {
           const f32x4 vs = vsr[h2][k & 1];
-          const float da = v8_grp ? vs[1] : vs[0], db = v8_grp ? vs[3] : vs[2];
+          da = v8_grp ? vs[1] : vs[0];
+          db = v8_grp ? vs[3] : vs[2];
           w = as_u32(f16x2{(_Float16)da, (_Float16)db});
         }
         if (c + kStep > c_end) {
           const int ca = c + 16 * h2 + 4 * lg + 2 * (k & 1);
-          if (ca >= c_end) w &= 0xffff0000u;      // zero the scale of cells past the split
-          if (ca + 1 >= c_end) w &= 0x0000ffffu;
+          if (ca >= c_end) {  // zero the scale of cells past the split
+            w &= 0xffff0000u;
+            da = 0.f;
+          }
+          if (ca + 1 >= c_end) {
+            w &= 0x0000ffffu;
+            db = 0.f;
+          }
         }
         dsc[k] = w;
+        if (!kQ4V) {
+          dsf[k][0] = da;
+          dsf[k][1] = db;
+          v8_tiny |= (da != 0.f && fabsf(da) < 6.103515625e-05f) || (db != 0.f && fabsf(db) < 6.103515625e-05f);
+        }
       }
       for (int h2 = 0; h2 < 2; h2++) load_vd(h2, *nx[h2]);
       if (kF16) {
@@ -739,13 +758,19 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
       } else {
         // INT8 V: tile j holds dim 16 n + j; B = code * d in fp16, the code
         // made exact as fp16 1152 + code by one xor under the 0x64 exponent
+        const bool tiny = __any(v8_tiny);  // wave-uniform
         for (int j = 0; j < 16; j++) {
           const uint32_t sel = (0x0cu << 24) | ((4u + (j & 3)) << 16) | (0x0cu << 8) | (uint32_t)(j & 3);
           uint32_t b[4];
           for (int k = 0; k < 4; k++) {
             const int h2 = k >> 1, ia = 2 * (k & 1);
             const uint32_t x = perm(vr8[h2][ia + 1][j >> 2], vr8[h2][ia][j >> 2], sel);  // [a_j, 0, b_j, 0]
-            b[k] = as_u32((as_f16x2(x ^ 0x64806480u) - c1152) * as_f16x2(dsc[k]));
+            const f16x2 code = as_f16x2(x ^ 0x64806480u) - c1152;  // exact
+            if (!tiny) {
+              b[k] = as_u32(code * as_f16x2(dsc[k]));
+            } else {
+              b[k] = as_u32(f16x2{(_Float16)((float)code[0] * dsf[k][0]), (_Float16)((float)code[1] * dsf[k][1])});
+            }
           }
           if (j == 15) {
             for (int h2 = 0; h2 < 2; h2++) load_v(h2, *nx[h2]);
@@ -908,21 +933,24 @@ __global__ __launch_bounds__(kCombineWaves * 64) void attn_combine_kernel(const 
 
 // ---------------------------------------------------------------- host side
 
-// Compute units of the current device, cached per device.  The split plan
+// Compute units of the current device, cached per device (relaxed atomics:
+// concurrent first calls may both query, and store the same value).  The split plan
 // targets one 4-wave workgroup per CU and KV head share: measured on
 // MI355X, one workgroup per CU (1 wave per SIMD, 128 splits per KV head)
 // beats two (256 splits) for decode at 118,750 and 240,000 cells.
 static int device_cus() {
-  static int cached_dev = -1, cached_cus = 0;
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];  // 0 = not yet queried
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (dev != cached_dev) {
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 256;
-    cached_cus = prop.multiProcessorCount;
-    cached_dev = dev;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
   }
-  return cached_cus;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess || prop.multiProcessorCount <= 0) return 256;
+  if (dev >= 0 && dev < kMaxDevices) cached[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+  return prop.multiProcessorCount;
 }
 
 int attn_target_splits(int n_kv_heads, int n_rows) {

@@ -12,6 +12,9 @@ namespace k8v4 {
 // per thread for kv_last_hip_error).
 int launch_status();
 
+// Record e as the calling thread's HIP error for kv_last_hip_error.
+void set_last_hip_error(hipError_t e);
+
 // Start/stop events armed by kv_time_next_launch for the calling thread's
 // next kernel launch (both NULL when none); taking them disarms the hook.
 void take_launch_events(hipEvent_t *start, hipEvent_t *stop);

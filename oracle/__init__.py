@@ -69,6 +69,8 @@ def _load():
     lib.orc_gather.restype = i
     lib.orc_attention.argtypes = [P, P, i, i, P, i, i, i, P, d, i, i, P]
     lib.orc_attention.restype = i
+    lib.orc_attention_threads.argtypes = [P, P, i, i, P, i, i, i, P, d, i, i, P, i]
+    lib.orc_attention_threads.restype = i
     _lib = lib
     return lib
 
@@ -247,12 +249,20 @@ def dequant_gathered(fmt: int, gathered):
     return dequant_q4(kb), dequant_q4(vb)
 
 
+def default_threads() -> int:
+    """Threads the oracle's attention uses by default: the host's cores
+    (at most 16)."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
 def attention(kd, vd, q, n_visible, scale: float | None = None, *, q_rotate: bool = False,
-              v_rotated: bool = True) -> np.ndarray:
+              v_rotated: bool = True, threads: int | None = None) -> np.ndarray:
     """fp64 attention by definition.
 
     kd, vd: [n_cells][H][256] fp64.  q: [rows][Hq][256] fp16 or fp32.
     n_visible: [rows] leading cells each row attends to.  Returns [rows][Hq][256] fp64.
+    threads: the (row, head) pairs are spread over this many threads
+    (default: default_threads()); the result does not depend on it.
     """
     kd = _c(kd, np.float64)
     vd = _c(vd, np.float64)
@@ -267,17 +277,19 @@ def attention(kd, vd, q, n_visible, scale: float | None = None, *, q_rotate: boo
     if scale is None:
         scale = 1.0 / np.sqrt(D)
     out = np.empty((rows, Hq, D), np.float64)
-    rc = _load().orc_attention(_ptr(kd), _ptr(vd), n_cells, H, _ptr(qb), qd, rows, Hq, _ptr(nv),
-                               float(scale), int(q_rotate), int(v_rotated), _ptr(out))
+    nt = default_threads() if threads is None else int(threads)
+    rc = _load().orc_attention_threads(_ptr(kd), _ptr(vd), n_cells, H, _ptr(qb), qd, rows, Hq, _ptr(nv),
+                                       float(scale), int(q_rotate), int(v_rotated), _ptr(out), nt)
     if rc != 0:
         raise ValueError("oracle attention: bad arguments")
     return out
 
 
-def attention_from_pool(pool: OraclePool, page_table, q, n_visible, scale: float | None = None):
+def attention_from_pool(pool: OraclePool, page_table, q, n_visible, scale: float | None = None,
+                        threads: int | None = None):
     """Gather the visible prefix, dequantize, attend (format rules of pool.fmt)."""
     n = int(np.max(n_visible))
     g = pool.gather(page_table, 0, n)
     kd, vd = dequant_gathered(pool.fmt, g)
     return attention(kd, vd, q, n_visible, scale, q_rotate=(pool.fmt == FMT_Q4_0),
-                     v_rotated=(pool.fmt not in (FMT_INT8, FMT_F16)))
+                     v_rotated=(pool.fmt not in (FMT_INT8, FMT_F16)), threads=threads)

@@ -13,7 +13,7 @@ LIB = os.path.join(HERE, "liborc_k8v4.so")
 
 def build(verbose: bool = False) -> str:
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-frounding-math", "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC, "-lm"]
+           "-fno-fast-math", "-frounding-math", "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC, "-lm", "-lpthread"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)

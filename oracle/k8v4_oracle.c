@@ -36,6 +36,7 @@
  * pages carry no code or test vectors for them.
  */
 #include <math.h>
+#include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -363,6 +364,64 @@ void orc_hadamard_apply_f64(const double *in, double *out) {
   }
 }
 
+typedef struct {
+  const double *kd, *vd;
+  int n_cells, H;
+  const void *q;
+  int q_dtype, rows, Hq;
+  const int32_t *n_vis;
+  double scale;
+  int q_rotate, v_rotated;
+  double *out;
+} attn_job;
+
+/* one (row, query head) pair of orc_attention; s: n_cells doubles of scratch */
+static void attend_one(const attn_job *J, int r, int h, double *s) {
+  const int G = J->Hq / J->H, g = h / G, n = J->n_vis[r];
+  double qv[ORC_D], qr[ORC_D], u[ORC_D];
+  size_t qoff = ((size_t)r * J->Hq + h) * ORC_D;
+  for (int c = 0; c < ORC_D; c++) qv[c] = (double)load_in(J->q, J->q_dtype, qoff + c);
+  const double *qq = qv;
+  if (J->q_rotate) { orc_hadamard_apply_f64(qv, qr); qq = qr; }
+  double smax = -INFINITY;
+  for (int t = 0; t < n; t++) {
+    const double *kt = J->kd + ((size_t)t * J->H + g) * ORC_D;
+    double acc = 0.0;
+    for (int c = 0; c < ORC_D; c++) acc += qq[c] * kt[c];
+    s[t] = J->scale * acc;
+    if (s[t] > smax) smax = s[t];
+  }
+  double wsum = 0.0;
+  for (int c = 0; c < ORC_D; c++) u[c] = 0.0;
+  for (int t = 0; t < n; t++) {
+    double w = exp(s[t] - smax);
+    wsum += w;
+    const double *vt = J->vd + ((size_t)t * J->H + g) * ORC_D;
+    for (int c = 0; c < ORC_D; c++) u[c] += w * vt[c];
+  }
+  for (int c = 0; c < ORC_D; c++) u[c] /= wsum;
+  double *o = J->out + ((size_t)r * J->Hq + h) * ORC_D;
+  if (J->v_rotated) orc_hadamard_apply_f64(u, o);
+  else memcpy(o, u, sizeof u);
+}
+
+typedef struct {
+  const attn_job *J;
+  int first, stride;  /* this worker's (row, head) pairs: first, first + stride, ... */
+  int rc;
+} attn_worker;
+
+static void *attn_worker_run(void *arg) {
+  attn_worker *w = (attn_worker *)arg;
+  const attn_job *J = w->J;
+  double *s = (double *)malloc(sizeof(double) * (J->n_cells > 0 ? J->n_cells : 1));
+  if (!s) { w->rc = -1; return NULL; }
+  for (long i = w->first; i < (long)J->rows * J->Hq; i += w->stride) attend_one(J, (int)(i / J->Hq), (int)(i % J->Hq), s);
+  free(s);
+  w->rc = 0;
+  return NULL;
+}
+
 /*
  * Exact fp64 attention over dequantized K/V, by definition [PR120, How:
  * the fused decode/prefill/verify attention; Tests: step and batched
@@ -377,48 +436,50 @@ void orc_hadamard_apply_f64(const double *in, double *out) {
  *   out: [rows][Hq][256] fp64.  Row r, head h uses kv head h / (Hq / H).
  *   For row r, head h: s_t = scale * <q, k_t>, w_t = exp(s_t - max s),
  *   u = sum w_t v_t / sum w_t, and out = (1/16) H u when v_rotated.
+ * The (row, head) pairs are independent; n_threads > 1 hands them out
+ * round robin to that many threads, each computing its pairs exactly as
+ * one thread would (the result is bitwise the same).
  */
+int orc_attention_threads(const double *kd, const double *vd, int n_cells, int H, const void *q,
+                          int q_dtype, int rows, int Hq, const int32_t *n_vis, double scale,
+                          int q_rotate, int v_rotated, double *out, int n_threads) {
+  if (H <= 0 || Hq % H) return -1;
+  for (int r = 0; r < rows; r++)
+    if (n_vis[r] < 1 || n_vis[r] > n_cells) return -1;
+  attn_job J = {kd, vd, n_cells, H, q, q_dtype, rows, Hq, n_vis, scale, q_rotate, v_rotated, out};
+  if (n_threads < 1) n_threads = 1;
+  if (n_threads > 256) n_threads = 256;
+  attn_worker w[256];
+  pthread_t tid[256];
+  int started = 0, rc = 0;
+  for (int i = 0; i < n_threads; i++) {
+    w[i].J = &J;
+    w[i].first = i;
+    w[i].stride = n_threads;
+    w[i].rc = -1;
+  }
+  for (int i = 1; i < n_threads; i++) {
+    if (pthread_create(&tid[i], NULL, attn_worker_run, &w[i]) != 0) break;
+    started = i;
+  }
+  if (started < n_threads - 1) {
+    /* could not start them all: the calling thread does every pair itself */
+    for (int i = 1; i <= started; i++) pthread_join(tid[i], NULL);
+    w[0].stride = 1;
+    attn_worker_run(&w[0]);
+    return w[0].rc;
+  }
+  attn_worker_run(&w[0]);
+  for (int i = 1; i < n_threads; i++) pthread_join(tid[i], NULL);
+  for (int i = 0; i < n_threads; i++) rc |= w[i].rc;
+  return rc ? -1 : 0;
+}
+
 int orc_attention(const double *kd, const double *vd, int n_cells, int H, const void *q,
                   int q_dtype, int rows, int Hq, const int32_t *n_vis, double scale,
                   int q_rotate, int v_rotated, double *out) {
-  if (H <= 0 || Hq % H) return -1;
-  int G = Hq / H;
-  double *s = (double *)malloc(sizeof(double) * (n_cells > 0 ? n_cells : 1));
-  if (!s) return -1;
-  double qv[ORC_D], qr[ORC_D], u[ORC_D];
-  for (int r = 0; r < rows; r++) {
-    int n = n_vis[r];
-    if (n < 1 || n > n_cells) { free(s); return -1; }
-    for (int h = 0; h < Hq; h++) {
-      int g = h / G;
-      size_t qoff = ((size_t)r * Hq + h) * ORC_D;
-      for (int c = 0; c < ORC_D; c++) qv[c] = (double)load_in(q, q_dtype, qoff + c);
-      const double *qq = qv;
-      if (q_rotate) { orc_hadamard_apply_f64(qv, qr); qq = qr; }
-      double smax = -INFINITY;
-      for (int t = 0; t < n; t++) {
-        const double *kt = kd + ((size_t)t * H + g) * ORC_D;
-        double acc = 0.0;
-        for (int c = 0; c < ORC_D; c++) acc += qq[c] * kt[c];
-        s[t] = scale * acc;
-        if (s[t] > smax) smax = s[t];
-      }
-      double wsum = 0.0;
-      for (int c = 0; c < ORC_D; c++) u[c] = 0.0;
-      for (int t = 0; t < n; t++) {
-        double w = exp(s[t] - smax);
-        wsum += w;
-        const double *vt = vd + ((size_t)t * H + g) * ORC_D;
-        for (int c = 0; c < ORC_D; c++) u[c] += w * vt[c];
-      }
-      for (int c = 0; c < ORC_D; c++) u[c] /= wsum;
-      double *o = out + ((size_t)r * Hq + h) * ORC_D;
-      if (v_rotated) orc_hadamard_apply_f64(u, o);
-      else memcpy(o, u, sizeof u);
-    }
-  }
-  free(s);
-  return 0;
+  return orc_attention_threads(kd, vd, n_cells, H, q, q_dtype, rows, Hq, n_vis, scale, q_rotate, v_rotated,
+                               out, 1);
 }
 
 /* ------------------------------------------------------------------ */

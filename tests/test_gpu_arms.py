@@ -137,6 +137,37 @@ def test_arm_verify_one_row_equals_decode_bitwise(k8, dev, arm_tiny):
     assert np.array_equal(a.view(np.uint32), b[0].view(np.uint32))
 
 
+@pytest.mark.parametrize("v_scale", [1e-3, 3e-4])
+def test_int8_small_values_decode_and_verify(orc, k8, dev, v_scale):
+    """int8 format with V ~ N(0, v_scale^2): the V scales (max|V| / 127,
+    ~3e-5 and ~1e-5) lie below fp16's normal range, where an fp16 copy of a
+    scale loses its bits; the kernels form code * d in fp32 and round once
+    (decode, verify and prefill).  The values themselves stay at or above
+    the fp16 normal range for the most part: fp16 matrix-core operands
+    cannot hold values far below 2^-14 to the attention tolerance."""
+    say(f"int8 small V scale={v_scale}")
+    P, n_pages, ctx = 16, 70, 1000
+    pt = synth.page_table(14, 63, n_pages)
+    gpt = t_(pt, dev)
+    k, v = synth.kv_tokens(14, 0, 0, ctx, 2, 256, np.float32)
+    v = (v * np.float32(v_scale)).astype(np.float32)
+    gpool = k8.KvPool(FMT_INT8, n_pages, P, 2, device=dev, fill=0)
+    opool = orc.OraclePool(FMT_INT8, n_pages, P, 2, sentinel=0)
+    k8.kv_append(gpool, gpt, t_(k, dev), t_(v, dev), 0)
+    opool.append(pt, k, v, 0)
+    q = synth.queries(14, 0, 0, 3, 16, 256, np.float16)
+    ws = k8.attn_workspace(gpool, 3, ctx)
+    out = k8.attn_decode(gpool, gpt, t_(q[0], dev), ctx, ws).cpu().numpy()
+    e1 = rel_err(out, orc.attention_from_pool(opool, pt, q[:1], [ctx])[0])
+    nv = [ctx, 517, 33]
+    outv = k8.attn_verify(gpool, gpt, t_(q, dev), nv, ws).cpu().numpy()
+    e2 = rel_err(outv, orc.attention_from_pool(opool, pt, q, nv))
+    outp = k8.attn_prefill_chunk(gpool, gpt, t_(q, dev), ctx - 3).cpu().numpy()
+    e3 = rel_err(outp, orc.attention_from_pool(opool, pt, q, [ctx - 2, ctx - 1, ctx]))
+    say(f"  rel err decode {e1:.3e} verify {e2:.3e} prefill {e3:.3e}")
+    assert max(e1, e2, e3) <= TOL
+
+
 @pytest.mark.parametrize("fmt", [FMT_INT8, FMT_Q4_0, FMT_K8V4, FMT_F16])
 def test_arms_decode_32768_with_outlier_channels(orc, k8, dev, fmt):
     """The three formats on the same raw inputs: 32,768 cells, 3 outlier

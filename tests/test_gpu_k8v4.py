@@ -455,6 +455,35 @@ def test_decode_append_out_of_range_entry_gives_nan_and_no_write(orc, k8, dev):
             assert torch.equal(ra, rb)
 
 
+@pytest.mark.parametrize("fmt", [3, 1, 2, 0])
+def test_prefill_out_of_range_entry_gives_nan_rows(orc, k8, dev, fmt):
+    """A page-table entry out of the pool: prefill rows whose causal window
+    reaches that page return NaN, rows that stop before it match the oracle
+    (the kernel reads page 0 instead, never outside the pool)."""
+    say(f"prefill with an out-of-range entry fmt={fmt}")
+    P, n_pages, n_table, ctx = 16, 70, 66, 1000
+    pt = synth.page_table(13, n_table, n_pages)
+    gpt = t_(pt, dev)
+    gpool = k8.KvPool(fmt, n_pages, P, 2, device=dev, fill=0)
+    opool = orc.OraclePool(fmt, n_pages, P, 2, sentinel=0)
+    k, v = synth.kv_tokens(13, 0, 0, ctx, 2, 256, np.float16)
+    k8.kv_append(gpool, gpt, t_(k, dev), t_(v, dev), 0)
+    opool.append(pt, k, v, 0)
+    bad = pt.copy()
+    bad_page = 45                     # cells [720, 736)
+    bad[bad_page] = 10_000
+    pos0, n_new = 700, 60             # rows at positions 700..759
+    q = synth.queries(13, 0, 1, n_new, 16, 256, np.float16)
+    out = k8.attn_prefill_chunk(gpool, t_(bad, dev), t_(q, dev), pos0).cpu().numpy()
+    first_bad_row = bad_page * P - pos0          # row 20 sees cell 720
+    assert np.isnan(out[first_bad_row:]).all()
+    assert np.isfinite(out[:first_bad_row]).all()
+    ref = orc.attention_from_pool(opool, pt, q[:first_bad_row], [pos0 + i + 1 for i in range(first_bad_row)])
+    err = rel_err(out[:first_bad_row], ref)
+    say(f"  rows before the bad page: rel err {err:.3e}")
+    assert err <= TOL
+
+
 def test_decode_append_32768_outliers(orc, k8, dev):
     say("decode_append at 32,767 with outlier channels")
     pos = 32767

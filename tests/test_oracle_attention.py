@@ -287,3 +287,16 @@ def test_f16_attention_matches_brute_force_tiny(orc):
     for h in (0, 7, 8, 15):
         ref = _brute(kd[:, h // 8].tolist(), vd[:, h // 8].tolist(), q[0, h], 7, 1 / 16, rotated=False)
         assert np.allclose(out[0, h], ref, rtol=0, atol=1e-12)
+
+
+def test_threaded_attention_is_bitwise_the_single_thread_result(orc):
+    """The (row, head) pairs spread over threads compute exactly what one
+    thread computes (the threads only split the work)."""
+    pool, pt, _, _ = _pool_with(orc, 3, P=16, n_pages=12, n_table=12, n_tok=180, seed=21)
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((5, 16, 256)).astype(np.float16)
+    nv = np.array([180, 1, 57, 179, 100], np.int32)
+    kd, vd = orc.dequant_gathered(3, pool.gather(pt, 0, 180))
+    one = orc.attention(kd, vd, q, nv, threads=1)
+    for nt in (2, 3, 7, 16):
+        assert np.array_equal(orc.attention(kd, vd, q, nv, threads=nt).view(np.uint64), one.view(np.uint64))
