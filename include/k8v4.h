@@ -254,6 +254,33 @@ int attn_decode(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dty
                 int n_q_heads, int32_t n_ctx, float scale, float *out, void *ws,
                 size_t ws_bytes, void *stream);
 
+/* Size of the library's per-device scratch array (attn_decode_noalloc):
+ * 4 MiB.  A decode's split-K partials take about 8 KiB per split-K
+ * workgroup and the plan launches about one per compute unit, so this holds
+ * any decode on a GPU of up to ~500 compute units (MI355X: 256, ~2 MiB). */
+#define KV_SCRATCH_BYTES ((size_t)4 << 20)
+
+/*
+ * attn_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops that forbid allocation, harnesses that
+ * forbid hipMalloc.  Same arguments, result and errors as attn_decode,
+ * without the workspace: the split-K partials go to a scratch array of
+ * KV_SCRATCH_BYTES that the library keeps in each GPU's memory (one copy per
+ * device, held until the process ends, looked up on the first call on a
+ * device).  The call allocates and frees nothing.
+ *   - All calls on one GPU share that GPU's array, which keeps the last
+ *     call's partials (they need no clearing: every call overwrites what it
+ *     reads).  Calls that overlap on one GPU (on different streams, or from
+ *     different threads without ordering) race on it: order them on one
+ *     stream.
+ *   - KV_ERR_WORKSPACE (before launching) when the call's split plan needs
+ *     more than KV_SCRATCH_BYTES;
+ *     KV_ERR_LAUNCH if the runtime cannot resolve the array on the current
+ *     device.
+ */
+int attn_decode_noalloc(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
+                        int n_q_heads, int32_t n_ctx, float scale, float *out, void *stream);
+
 /*
  * One decode step with its append fused in ("#120 --kv k8v4: hybrid KV
  * cache", How: a decode step appends the new token's K/V, then attends over

@@ -49,6 +49,7 @@ SIGNATURES = {
     "kv_append": (_I, [_PP, _PS, _P, _P, _I, C.c_int32, C.c_int32, _P]),
     "kv_gather_runs": (_I, [_PP, _PS, C.c_int32, C.c_int32, _P, _P, _P, _P, _P]),
     "attn_decode": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, _F, _P, _P, _SZ, _P]),
+    "attn_decode_noalloc": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, _F, _P, _P]),
     "attn_decode_append": (_I, [_PP, _PS, _P, _P, _I, _P, _I, _I, C.c_int32, _F, _P, _P, _SZ, _P]),
     "attn_decode_batch": (_I, [_PP, _PS, C.c_int32, _P, _I, _I, _P, _F, _P, _P, _SZ, _P]),
     "attn_verify": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, _P, _F, _P, _P, _SZ, _P]),
@@ -314,6 +315,23 @@ def attn_decode(pool: KvPool, page_table, q, n_ctx: int, ws, scale: float = 0.0,
                            _dev_ptr(out, "out", (torch.float32,)), _dev_ptr(ws, "ws"),
                            ws.numel(), _stream(stream))
     _check(rc, "attn_decode")
+    return out
+
+
+def attn_decode_noalloc(pool: KvPool, page_table, q, n_ctx: int, scale: float = 0.0, out=None,
+                        stream=None):
+    """attn_decode without a workspace: the library's per-device scratch
+    array holds the split partials (calls on one GPU must be ordered)."""
+    torch = _torch()
+    if q.dim() != 2 or q.shape[1] != HEAD_DIM:
+        raise ValueError("q must be [n_q_heads][256]")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    seq = _seq(page_table)
+    rc = lib().attn_decode_noalloc(C.byref(pool.struct), C.byref(seq), _dev_ptr(q, "q"), _dtype_code(q),
+                                   int(q.shape[0]), int(n_ctx), float(scale),
+                                   _dev_ptr(out, "out", (torch.float32,)), _stream(stream))
+    _check(rc, "attn_decode_noalloc")
     return out
 
 

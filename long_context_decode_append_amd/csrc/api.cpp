@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <mutex>
 #include <vector>
 
 #include "launch.hpp"
@@ -32,6 +33,43 @@ void take_launch_events(hipEvent_t *start, hipEvent_t *stop) {
   g_ev_start = g_ev_stop = nullptr;
 }
 }  // namespace k8v4
+
+// ---------------------------------------------------------------- scratch
+// Split-K partials of attn_decode_noalloc (see there).  A decode plan has
+// about one split-K workgroup per compute unit, each writing 8 rows of
+// 258 floats, so KV_SCRATCH_BYTES (4 MiB) holds the partials of any decode on
+// a GPU of up to ~500 compute units.
+static __device__ __align__(256) unsigned char scratch[KV_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];  // device address of `scratch` per device, set under g_scratch_mu
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device).  KV_ERR_LAUNCH if the runtime cannot resolve it.
+int scratch_of_current_device(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess && (dev < 0 || dev >= kMaxDevices)) e = hipErrorInvalidDevice;
+  if (e == hipSuccess) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+      void *p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e == hipSuccess && !p) e = hipErrorInvalidSymbol;
+      if (e == hipSuccess) g_scratch[dev] = p;
+    }
+    *ptr = g_scratch[dev];
+  }
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    set_last_hip_error(e);
+    return KV_ERR_LAUNCH;
+  }
+  return KV_OK;
+}
+}  // namespace
 
 namespace {
 // Scope of one entry-point call that may launch work.  On entry it clears
@@ -364,6 +402,26 @@ int kv_check_page_table(const kv_pool *pool, const kv_seq *seq, int32_t n_cells,
   }
   *n_bad = bad;
   return KV_OK;
+}
+
+// attn_decode for callers that cannot allocate device memory: the split-K
+// partials go to `scratch`, a file-scope device array that every GPU the
+// library runs on holds (its own copy, at its own address) until the
+// process ends.  On the host the name `scratch` is only a stand-in for the
+// device symbol, never a device address: host code uses the address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device on the first call there and kept in g_scratch.
+int attn_decode_noalloc(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype, int n_q_heads,
+                        int32_t n_ctx, float scale, float *out, void *stream) {
+  CallScope scope;
+  if (int e = check_attn_common(pool, seq, q, q_dtype, n_q_heads, out, 0)) return e;
+  if (n_ctx < 1) return KV_ERR_RANGE;
+  if (int e = check_range(pool, seq, 0, n_ctx)) return e;
+  void *ws = nullptr;
+  if (int e = scratch_of_current_device(&ws)) return e;
+  // the launcher checks the plan's partials against this size and returns
+  // KV_ERR_WORKSPACE before launching when they do not fit
+  return decode_call(pool, seq, q, q_dtype, n_q_heads, n_ctx, scale, out, ws, KV_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"
