@@ -85,6 +85,7 @@ struct SplitArgs {
   // pass b reads table pts[b] over cells [0, limits[b])
   int batch;
   const int32_t *pts[kMaxQ];
+  int v_rot;            // V stored rotated (k8v4, q4_0): the combine finishes the inverse rotation
 };
 
 // dim of output tile j held by column n of the PV MFMA.  q4_0 V: column n
@@ -129,6 +130,8 @@ __device__ __forceinline__ float readlane(float x, int l) {
 // cells are masked and its V scales zeroed).
 struct Half {
   int bad;        // page-table entry out of range: rows that read it return NaN
+  int none;       // a step past the wave's last: its loads read through empty
+                  // buffer descriptors (zeros, no memory access)
   int k_soff;     // K data of the half's first cell (int8 codes, or q4_0 nibbles)
   int ks_soff;    // K scales (fp32 pairs, or the q4_0 scale group)
   int v_soff;     // V data (q4_0 nibbles, or int8 codes)
@@ -148,6 +151,7 @@ __device__ __forceinline__ int page_of(const SplitArgs &a, int pos) {
 template <int FMT>
 __device__ __forceinline__ Half make_half(const SplitArgs &a, int g, int pos, int page) {
   Half h;
+  h.none = 0;
   h.bad = page < 0 || page >= a.n_pages;
   const int pg = h.bad ? 0 : page;
   const int slot0 = pos - page_of(a, pos) * a.P;  // a multiple of 16
@@ -249,7 +253,7 @@ __device__ __forceinline__ void append_token_partial(const SplitArgs &a, int g, 
     kd[i] = (float)(int8_t)(kcodes >> (8 * i)) * dk;
     vr[i] = (float)((_Float16)(float)((int)((vcodes >> (8 * i)) & 0xffu) - 8) * dh);
   }
-  fwht256_lane4(vr, lane);  // partials are kept in the unrotated basis
+  fwht_hi(vr, lane);  // partials carry the strides-64/128 factor of the inverse rotation
   const f32x4 vo = {vr[0], vr[1], vr[2], vr[3]};
   float dot[kGqa];
   for (int r = 0; r < kGqa; r++) dot[r] = qx[r][0] * kd[0] + qx[r][1] * kd[1] + qx[r][2] * kd[2] + qx[r][3] * kd[3];
@@ -310,10 +314,16 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
 
   // buffer descriptors over whole runs; the hardware range check returns
   // zeros for any offset past a run
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)a.kc, (short)0, a.k_bytes, kRsrcFlags);
-  const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc((void *)a.ks, (short)0, a.ks_bytes, kRsrcFlags);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)a.vq, (short)0, a.v_bytes, kRsrcFlags);
-  const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc((void *)a.vs, (short)0, a.vs_bytes, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rk_ = __builtin_amdgcn_make_buffer_rsrc((void *)a.kc, (short)0, a.k_bytes, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rks_ = __builtin_amdgcn_make_buffer_rsrc((void *)a.ks, (short)0, a.ks_bytes, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rv_ = __builtin_amdgcn_make_buffer_rsrc((void *)a.vq, (short)0, a.v_bytes, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rvs_ = __builtin_amdgcn_make_buffer_rsrc((void *)a.vs, (short)0, a.vs_bytes, kRsrcFlags);
+  // the same runs with no records: a load through one returns zeros without
+  // touching memory (the unconditional prefetch past a wave's last step)
+  const __amdgpu_buffer_rsrc_t rk0 = __builtin_amdgcn_make_buffer_rsrc((void *)a.kc, (short)0, 0, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rks0 = __builtin_amdgcn_make_buffer_rsrc((void *)a.ks, (short)0, 0, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rv0 = __builtin_amdgcn_make_buffer_rsrc((void *)a.vq, (short)0, 0, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rvs0 = __builtin_amdgcn_make_buffer_rsrc((void *)a.vs, (short)0, 0, kRsrcFlags);
   // lane-constant parts of the operand-layout loads
   //   INT8 K:  + 1024 j: 16 bytes (dims 64 j + 16 lg ..) of cell n (the K-code
   //            run's 16-cell blocks are [dim quarter][cell][64 codes], so
@@ -343,10 +353,13 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
   f32x4 vsr[2][2];
   Half cur0, cur1, nxt0, nxt1;
   auto load_k = [&](int h2, const Half &h) {
+    const __amdgpu_buffer_rsrc_t rk = h.none ? rk0 : rk_;
     for (int j = 0; j < kKLoads; j++)
       kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + kstep_j * j, h.k_soff, kAux);
   };
   auto load_ks = [&](int h2, const Half &h) {
+    const __amdgpu_buffer_rsrc_t rks = h.none ? rks0 : rks_;
+    const __amdgpu_buffer_rsrc_t rk = h.none ? rk0 : rk_;
     if (kF16) {
       // no scales
     } else if (kInt8K) {
@@ -357,6 +370,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
     }
   };
   auto load_v = [&](int h2, const Half &h) {
+    const __amdgpu_buffer_rsrc_t rv = h.none ? rv0 : rv_;
     if (kF16) {
       for (int u = 0; u < 8; u++) vr16[h2][u] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_voff + 1024 * u, h.v_soff, kAux);
     } else if (kQ4V) {
@@ -366,6 +380,8 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
     }
   };
   auto load_vd = [&](int h2, const Half &h) {
+    const __amdgpu_buffer_rsrc_t rvs = h.none ? rvs0 : rvs_;
+    const __amdgpu_buffer_rsrc_t rv = h.none ? rv0 : rv_;
     if (kF16) {
       // no scales
     } else if (kQ4V) {
@@ -407,6 +423,9 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
     // it), so no control-flow join makes the compiler over-wait below
     const int cf = has_work ? c_first : 0, ce = has_work ? c_end : 16;
     first_halves<FMT>(a, ptab, g, cf, has_work ? min(c_first + stride, c_last) : 0, ce, cur0, cur1, nxt0, nxt1);
+    // loads of steps that do not exist fetch nothing
+    cur0.none = cur1.none = !has_work;
+    nxt0.none = nxt1.none = !has_work || c_first + stride > c_last;
     const Half *hs[2] = {&cur0, &cur1};
     for (int h2 = 0; h2 < 2; h2++) {
       load_k(h2, *hs[h2]);
@@ -532,6 +551,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
       // pages of the step after next
       Half nn0, nn1;
       step_halves<FMT>(a, ptab, g, min(c + 2 * stride, c_last), c_end, nn0, nn1);
+      nn0.none = nn1.none = c + 2 * stride > c_last;
       const int badp[2] = {cur0.bad, cur1.bad};
       // whole step inside every valid row's limit and on valid pages: no
       // masking (rows past rows_here then hold harmless values that are never
@@ -553,7 +573,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
               acc0[t] = mfma16x16x32(ka, qop[t][j], acc0[t]);
               if (QF32) acc0[t] = mfma16x16x32(ka, qlo[t][j], acc0[t]);
             }
-            kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + kstep_j * j, nx[h2]->k_soff, kAux);
+            kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(nx[h2]->none ? rk0 : rk_, k_voff + kstep_j * j, nx[h2]->k_soff, kAux);
             continue;
           }
           if (kInt8K) {
@@ -598,7 +618,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
             }
           }
           // K chunk j of this half consumed: refill with the next step's
-          kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + kstep_j * j, nx[h2]->k_soff, kAux);
+          kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(nx[h2]->none ? rk0 : rk_, k_voff + kstep_j * j, nx[h2]->k_soff, kAux);
         }
         // several row tiles: the softmax scale folds into the cells' two K
         // group scales once, for all of them
@@ -721,7 +741,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
           const f16x8 bhi = pack8(v0.z, v0.w, v1.z, v1.w);  // tile 2u + 1: dim 16 n + 2 u + 1
           // chunk u of this step consumed: refill with the next step's
           for (int h2 = 0; h2 < 2; h2++)
-            vr16[h2][u] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_voff + 1024 * u, nx[h2]->v_soff, kAux);
+            vr16[h2][u] = __builtin_amdgcn_raw_buffer_load_b128(nx[h2]->none ? rv0 : rv_, v_voff + 1024 * u, nx[h2]->v_soff, kAux);
           for (int t = 0; t < T; t++) o[t][2 * u] = mfma16x16x32(pop[t], blo, o[t][2 * u]);
           for (int t = 0; t < T; t++) o[t][2 * u + 1] = mfma16x16x32(pop[t], bhi, o[t][2 * u + 1]);
         }
@@ -789,81 +809,73 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
   }
 
   // ---------------------------------------------------------------- workgroup merge
-  // per row tile, every wave parks its state in LDS (accumulator layout),
-  // then all threads merge the 4 states element-wise in wave order; the
-  // merged rows go back through LDS as plain rows, so each wave can take
-  // whole rows, undo the V rotation (H / 16 is its own inverse and linear,
-  // so the combine can sum partials in the unrotated basis) and store each
-  // row as one coalesced 1 KB write
+  // per row tile, every wave parks its own state in LDS as plain 256-float
+  // rows, then after one barrier each wave takes whole rows: it merges the 4
+  // wave states of a row in wave order (4 dims per lane), applies the
+  // strides-64/128 factor of the inverse V rotation (H / 16 is linear, so the
+  // combine sums partials in this basis and applies the rest once, to each
+  // output slice) and stores the row as one coalesced 1 KB write
   const size_t rows_total = (size_t)a.n_rows;
   const size_t sp = (size_t)g * a.n_parts + split;
   for (int t = 0; t < T; t++) {
-    const int rows_t = rows_here - 16 * t;  // rows of this tile (may be <= 0)
-    if (t > 0) __syncthreads();              // the previous tile's readers are done
+    const int rows_t = min(rows_here - 16 * t, 16);  // rows of this tile (workgroup-uniform)
+    if (rows_t <= 0) break;
+    if (t > 0) __syncthreads();  // the previous tile's readers are done
     const float lt = sum_lg(lsum[t]);
     if (lg == 0) {
       lds_m[wave * 16 + n] = m[t];
       lds_l[wave * 16 + n] = lt;
     }
-    // lanes whose 4 rows are all padding (decode fills 8 of the 16) park nothing
-    if (4 * lg < rows_t)
-      for (int j = 0; j < 16; j++) *reinterpret_cast<f32x4 *>(&lds_o[((wave * 16 + j) * 64 + lane) * 4]) = o[t][j];
+    // lanes hold rows 4 lg + i; padding rows (decode fills 8 of 16) park
+    // nothing.  Tiles 4 q .. 4 q + 3 hold 4 consecutive dims of a row (a
+    // 4-aligned group, kept contiguous by the swizzle): one 16-byte write.
+    for (int i = 0; i < 4; i++) {
+      const int r = 4 * lg + i;
+      if (r < rows_t)
+        for (int qd = 0; qd < 4; qd++)
+          *reinterpret_cast<f32x4 *>(&lds_o[(wave * 16 + r) * 256 + row_swz(o_dim<kQ4V>(n, 4 * qd))]) =
+              f32x4{o[t][4 * qd][i], o[t][4 * qd + 1][i], o[t][4 * qd + 2][i], o[t][4 * qd + 3][i]};
+    }
     __syncthreads();
-
-    // thread -> accumulator lane L and tiles 4 jq .. 4 jq + 3; the lane holds
-    // rows 4 (L / 16) + i, i = 0..3, of each tile
-    const int L = threadIdx.x & 63, jq = threadIdx.x >> 6;
-    const int Ln = L & 15, Llg = L >> 4;
-    const bool live = 4 * Llg < rows_t;  // rows 4 Llg .. 4 Llg + 3 not all padding
-    f32x4 val[4], M = {0.f, 0.f, 0.f, 0.f}, Ls = {0.f, 0.f, 0.f, 0.f};
-    if (live) {
-      f32x4 mw[kWaves], lw[kWaves];
-      for (int w = 0; w < kWaves; w++) {
-        mw[w] = *reinterpret_cast<const f32x4 *>(&lds_m[w * 16 + 4 * Llg]);
-        lw[w] = *reinterpret_cast<const f32x4 *>(&lds_l[w * 16 + 4 * Llg]);
-      }
-      M = mw[0];
-      for (int w = 1; w < kWaves; w++)
-        for (int i = 0; i < 4; i++) M[i] = fmaxf(M[i], mw[w][i]);
-      f32x4 f[kWaves];
-      for (int w = 0; w < kWaves; w++)
-        for (int i = 0; i < 4; i++) {
-          f[w][i] = fast_exp2(mw[w][i] - M[i]);
-          Ls[i] += lw[w][i] * f[w][i];
+    // two rows at a time, so their dependency chains (LDS reads, the FWHT's
+    // cross-lane stages) overlap
+    for (int r0 = wave; r0 < rows_t; r0 += 2 * kWaves) {
+      const int nr = r0 + kWaves < rows_t ? 2 : 1;
+      float y[2][4], M[2], Ls[2];
+      for (int k = 0; k < 2; k++) {
+        const int r = k < nr ? r0 + kWaves * k : r0;
+        float mw[kWaves], lw[kWaves];
+        for (int w = 0; w < kWaves; w++) {
+          mw[w] = lds_m[w * 16 + r];
+          lw[w] = lds_l[w * 16 + r];
         }
-      for (int jj = 0; jj < 4; jj++) {
-        const int j = 4 * jq + jj;
+        M[k] = mw[0];
+        for (int w = 1; w < kWaves; w++) M[k] = fmaxf(M[k], mw[w]);
+        Ls[k] = 0.f;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int w = 0; w < kWaves; w++) acc += f[w] * *reinterpret_cast<const f32x4 *>(&lds_o[((w * 16 + j) * 64 + L) * 4]);
-        val[jj] = acc;
+        for (int w = 0; w < kWaves; w++) {
+          const float f = fast_exp2(mw[w] - M[k]);
+          Ls[k] += lw[w] * f;
+          acc += f * *reinterpret_cast<const f32x4 *>(&lds_o[(w * 16 + r) * 256 + row_swz(4 * lane)]);
+        }
+        for (int e = 0; e < 4; e++) y[k][e] = acc[e];
       }
-    }
-    __syncthreads();  // the state reads above are done before lds_o holds rows
-    if (live) {
-      for (int i = 0; i < 4; i++) {
-        const int r = 4 * Llg + i;
-        if (r >= rows_t) continue;
-        // tiles j, j+1 hold dims d, d+1 (j even)
-        *reinterpret_cast<float2 *>(&lds_o[r * 256 + row_swz(o_dim<kQ4V>(Ln, 4 * jq))]) = make_float2(val[0][i], val[1][i]);
-        *reinterpret_cast<float2 *>(&lds_o[r * 256 + row_swz(o_dim<kQ4V>(Ln, 4 * jq + 2))]) = make_float2(val[2][i], val[3][i]);
-        if (jq == 0 && Ln == 0) a.part_ml[sp * rows_total + row_base + 16 * t + r] = make_float2(M[i], Ls[i]);
+      if (kQ4V) fwht_hi_x2(y[0], y[1], lane);  // strides 64, 128; the combine does the rest
+      for (int k = 0; k < nr; k++) {
+        const size_t prow = sp * rows_total + row_base + 16 * t + r0 + kWaves * k;
+        *reinterpret_cast<f32x4 *>(a.part_o + prow * 256 + 4 * lane) = f32x4{y[k][0], y[k][1], y[k][2], y[k][3]};
+        if (lane == 0) a.part_ml[prow] = make_float2(M[k], Ls[k]);
       }
-    }
-    __syncthreads();
-    for (int r = wave; r < min(rows_t, 16); r += kWaves) {
-      const f32x4 v = *reinterpret_cast<const f32x4 *>(&lds_o[r * 256 + row_swz(4 * lane)]);
-      float y[4] = {v[0], v[1], v[2], v[3]};
-      if (kQ4V) fwht256_lane4(y, lane);
-      *reinterpret_cast<f32x4 *>(a.part_o + (sp * rows_total + row_base + 16 * t + r) * 256 + 4 * lane) =
-          f32x4{y[0], y[1], y[2], y[3]};
     }
   }
 }
 
 // Combine of the split partials of one query row of one KV head, after the
 // split kernel (the kernel boundary makes every partial visible).  The
-// partials are in the unrotated basis, so the rows split into independent
-// 64-dim slices, one workgroup each: 16 split lanes of 16 threads (4 dims
+// partials carry only the strides-64/128 butterflies of the inverse V
+// rotation, whose remaining butterflies (strides 1 .. 32) stay inside
+// 64-dim slices, so the rows split into independent slices, one workgroup
+// each: 16 split lanes of 16 threads (4 dims
 // each) load a strided share of the slice rows and their m up front; every
 // wave forms the common max and the weighted sum of l from all (m, l) by
 // itself (so only the final sum of the 4 waves needs a barrier), the split
@@ -927,8 +939,12 @@ __global__ __launch_bounds__(kCombineWaves * 64) void attn_combine_kernel(const 
   for (int w = 1; w < kCombineWaves; w++) tot += lds_acc[w][tid];
   const float inv = 1.0f / L;
   const int qi = row >> 3, hl = row & 7;
+  float y[4] = {tot[0] * inv, tot[1] * inv, tot[2] * inv, tot[3] * inv};
+  // rotated V: the partials carry the strides-64/128 factor of the inverse
+  // rotation; the strides 1 .. 32 (inside this 64-dim slice) and 1/16 finish it
+  if (a.v_rot) fwht_lo16(y, lane);
   float *op = a.out + ((size_t)qi * a.n_q_heads + (size_t)g * kGqa + hl) * 256 + 64 * part + 4 * tid;
-  *reinterpret_cast<f32x4 *>(op) = f32x4{tot[0] * inv, tot[1] * inv, tot[2] * inv, tot[3] * inv};
+  *reinterpret_cast<f32x4 *>(op) = f32x4{y[0], y[1], y[2], y[3]};
 }
 
 // ---------------------------------------------------------------- host side
@@ -1036,6 +1052,7 @@ int launch_attn_splitk(const AttnCall &c) {
   a.v_new = c.v_new;
   a.kv_dtype = c.kv_dtype;
   a.append_pos = c.append_pos;
+  a.v_rot = (pool->fmt == KV_FMT_K8V4 || pool->fmt == KV_FMT_Q4_0) ? 1 : 0;
 
   dim3 grid(n_parts, H, passes);
   // non-temporal KV loads when no two passes share their reads and one call

@@ -111,14 +111,35 @@ __device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
 }
 
 // one cross-lane butterfly of stride 4 M dims (lane stride M)
+// (lower index: a + b, upper index: a - b, formed as b + (-a) on the upper
+// lane, which IEEE addition rounds exactly like b - a; the sign flip is one
+// xor, so a stage is one cross-lane move and one add per value)
+template <int M>
+__device__ __forceinline__ float fwht_pair(float y, uint32_t neg) {
+#pragma clang fp contract(off)
+  if constexpr (M == 16 || M == 32) {
+    // swapping y with itself leaves the lower row (half) in the first
+    // result and the upper one in the second, in every lane: lower lanes
+    // form lo + hi, upper lanes lo + (-hi)
+    const auto r = M == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false)
+                           : __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1] ^ neg);
+  } else {
+    return lane_xor<M>(y) + __uint_as_float(__float_as_uint(y) ^ neg);
+  }
+}
+
 template <int M>
 __device__ __forceinline__ void fwht_stage(float y[4], int lane) {
-#pragma clang fp contract(off)
-  const bool upper = (lane & M) != 0;
-  for (int i = 0; i < 4; i++) {
-    const float p = lane_xor<M>(y[i]);
-    y[i] = upper ? (p - y[i]) : (y[i] + p);
-  }
+  const uint32_t neg = (lane & M) ? 0x80000000u : 0u;
+  for (int i = 0; i < 4; i++) y[i] = fwht_pair<M>(y[i], neg);
+}
+
+// the same stage on 8 values (two rows of 4)
+template <int M>
+__device__ __forceinline__ void fwht_stage8(float y[8], int lane) {
+  const uint32_t neg = (lane & M) ? 0x80000000u : 0u;
+  for (int i = 0; i < 8; i++) y[i] = fwht_pair<M>(y[i], neg);
 }
 
 // Walsh-Hadamard transform of the 256 values held 4 per lane (lane l holds
@@ -138,6 +159,42 @@ __device__ __forceinline__ void fwht256_lane4(float y[4], int lane) {
   fwht_stage<8>(y, lane);
   fwht_stage<16>(y, lane);
   fwht_stage<32>(y, lane);
+  for (int i = 0; i < 4; i++) y[i] = y[i] * 0.0625f;
+}
+
+// The inverse rotation of the attention output, split in two factors
+// (H = H_hi H_lo, the butterflies of strides 64 and 128, and of strides
+// 1 .. 32; the factors commute, and the output needs it only to within its
+// tolerance, not bit for bit):
+//   fwht_hi_x2: strides 64 and 128 (lane strides 16 and 32) on two rows of
+//     4 dims per lane, no scaling -- applied to each split partial;
+//   fwht_lo16: strides 1 .. 32 and the 1/16 scale on a 64-dim slice held by
+//     the 16 lanes of one row (lane l: dims 4l .. 4l + 3 of the slice) --
+//     applied once to each combined output slice.
+__device__ __forceinline__ void fwht_hi_x2(float y[4], float z[4], int lane) {
+  float w[8] = {y[0], y[1], y[2], y[3], z[0], z[1], z[2], z[3]};
+  fwht_stage8<16>(w, lane);
+  fwht_stage8<32>(w, lane);
+  for (int i = 0; i < 4; i++) {
+    y[i] = w[i];
+    z[i] = w[4 + i];
+  }
+}
+__device__ __forceinline__ void fwht_hi(float y[4], int lane) {
+  fwht_stage<16>(y, lane);
+  fwht_stage<32>(y, lane);
+}
+__device__ __forceinline__ void fwht_lo16(float y[4], int lane) {
+#pragma clang fp contract(off)
+  float a, b;
+  a = y[0]; b = y[1]; y[0] = a + b; y[1] = a - b;
+  a = y[2]; b = y[3]; y[2] = a + b; y[3] = a - b;
+  a = y[0]; b = y[2]; y[0] = a + b; y[2] = a - b;
+  a = y[1]; b = y[3]; y[1] = a + b; y[3] = a - b;
+  fwht_stage<1>(y, lane);
+  fwht_stage<2>(y, lane);
+  fwht_stage<4>(y, lane);
+  fwht_stage<8>(y, lane);
   for (int i = 0; i < 4; i++) y[i] = y[i] * 0.0625f;
 }
 
