@@ -351,6 +351,77 @@ int attn_prefill_chunk(const kv_pool *pool, const kv_seq *seq, const void *q, in
                        void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * A streamed cache ("kv: --kv k8v4 streams with --kv-resident", What and
+ * How; "#1188 --kv k8v4 produces degenerate repetition when --kv-resident
+ * streams", the engine log: a window of cells per layer in device memory,
+ * the whole K/V in pinned host memory).  Two pools of one format, KV-head
+ * count and page size hold the same logical pages:
+ *   mirror: every page of the context, in mapped pinned host memory
+ *           (hipHostMalloc); logical page i is mirror page mirror_table[i];
+ *   window: a device pool of fewer pages; logical page i is resident in
+ *           window slot window_map[i], or not resident when that is -1.
+ * window_owner[s] is the logical page in window slot s (-1: free).  The two
+ * maps are the caller's memory and state, written only by kv_stream_fetch
+ * (set them to -1 before first use).  stats accumulates [lookups, misses]
+ * of the streamed attention calls; fetch_list is scratch of
+ * 2 * window.n_pages int32 for kv_stream_fetch.  All device pointers.
+ */
+typedef struct kv_stream {
+  kv_pool window;
+  kv_pool mirror;
+  const int32_t *mirror_table; /* device [n_table]: logical page -> mirror page       */
+  int32_t *window_map;         /* device [n_table]: logical page -> window slot or -1  */
+  int32_t *window_owner;       /* device [window.n_pages]: slot -> logical page or -1  */
+  int32_t *stats;              /* device [2]: lookups, misses (accumulated)            */
+  int32_t *fetch_list;         /* device [2 * window.n_pages]: kv_stream_fetch scratch  */
+  int32_t n_table;             /* logical pages of the sequence                        */
+  int32_t reserved;            /* set to 0                                             */
+} kv_stream;
+
+/*
+ * Append n_tokens tokens at logical cells [pos0, pos0 + n_tokens) of a
+ * streamed cache: one kernel quantizes each token once (the format's rules,
+ * as kv_append) and writes every run of the cell to the mirror, and also to
+ * the window when the cell's page is resident.  Both copies of a cell are
+ * the same bytes.  Every run of both pools is required: a NULL run is
+ * KV_ERR_NULL, never a skipped copy -- the pages' bug was a writer that
+ * tested one half's pointer for presence and silently left out the host
+ * write of the other.
+ * Errors: as kv_append, plus KV_ERR_SHAPE (the pools differ in format,
+ * heads or page size).
+ */
+int kv_stream_append(const kv_stream *s, const void *k, const void *v, int dtype, int32_t pos0,
+                     int32_t n_tokens, void *stream);
+
+/*
+ * Miss service: make logical pages [first_page, first_page + n_pages)
+ * resident, as many as fit, the last ones first: page i goes to window slot
+ * i % window.n_pages (a ring over the window), whose previous page becomes
+ * non-resident; a page already in its slot is not copied; the others are
+ * copied from the mirror, every run (one kernel, as kv_copy_pages).  With
+ * n_pages > window.n_pages only the last window.n_pages pages are brought
+ * in.  Errors: KV_ERR_NULL, _SHAPE, _RANGE (pages outside [0, n_table)).
+ */
+int kv_stream_fetch(const kv_stream *s, int32_t first_page, int32_t n_pages, void *stream);
+
+/*
+ * attn_decode and attn_verify over a streamed cache: each 16-cell half of a
+ * page is read from the window when its page is resident and from the
+ * mirror otherwise (across the host link, inside the kernel), so the result
+ * is bitwise the result over a resident pool holding the same bytes (the
+ * split plan depends only on the context length).  Each call first counts,
+ * on the device, one lookup per logical page it reads and one miss per page
+ * not resident, into s->stats.  Same arguments, results and errors as
+ * attn_decode / attn_verify; ws as attn_workspace_bytes for the window
+ * pool.
+ */
+int attn_decode_stream(const kv_stream *s, const void *q, int q_dtype, int n_q_heads, int32_t n_ctx,
+                       float scale, float *out, void *ws, size_t ws_bytes, void *stream);
+int attn_verify_stream(const kv_stream *s, const void *q, int q_dtype, int n_q_heads, int32_t n_q,
+                       const int32_t *n_visible, float scale, float *out, void *ws, size_t ws_bytes,
+                       void *stream);
+
+/*
  * Debug check of a page table (synchronous: copies the table to the host).
  * Counts entries of the first ceil(n_cells / page_size) that are out of
  * [0, n_pages) or repeated; writes the count to *n_bad.

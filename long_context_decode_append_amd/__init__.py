@@ -34,9 +34,16 @@ class KvSeqStruct(C.Structure):
     _fields_ = [("page_table", C.c_void_p), ("n_table", C.c_int32), ("reserved", C.c_int32)]
 
 
+class KvStreamStruct(C.Structure):
+    _fields_ = [("window", KvPoolStruct), ("mirror", KvPoolStruct), ("mirror_table", C.c_void_p),
+                ("window_map", C.c_void_p), ("window_owner", C.c_void_p), ("stats", C.c_void_p),
+                ("fetch_list", C.c_void_p), ("n_table", C.c_int32), ("reserved", C.c_int32)]
+
+
 # name -> (restype, argtypes); the exported symbols of include/k8v4.h
 _P, _I, _SZ, _F = C.c_void_p, C.c_int, C.c_size_t, C.c_float
 _PP, _PS = C.POINTER(KvPoolStruct), C.POINTER(KvSeqStruct)
+_PST = C.POINTER(KvStreamStruct)
 SIGNATURES = {
     "kv_cell_bytes": (_SZ, [_I, _I, _I]),
     "kv_run_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
@@ -55,6 +62,10 @@ SIGNATURES = {
     "attn_verify": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, _P, _F, _P, _P, _SZ, _P]),
     "attn_prefill_chunk": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, C.c_int32, _F, _P, _P, _SZ, _P]),
     "kv_check_page_table": (_I, [_PP, _PS, C.c_int32, _P]),
+    "kv_stream_append": (_I, [_PST, _P, _P, _I, C.c_int32, C.c_int32, _P]),
+    "kv_stream_fetch": (_I, [_PST, C.c_int32, C.c_int32, _P]),
+    "attn_decode_stream": (_I, [_PST, _P, _I, _I, C.c_int32, _F, _P, _P, _SZ, _P]),
+    "attn_verify_stream": (_I, [_PST, _P, _I, _I, C.c_int32, _P, _F, _P, _P, _SZ, _P]),
     "kv_strerror": (C.c_char_p, [_I]),
     "kv_last_hip_error": (C.c_char_p, []),
     "kv_time_next_launch": (_I, [_P, _P]),
@@ -181,6 +192,82 @@ class K8V4Pool(KvPool):
     def __init__(self, n_pages: int, page_size: int, n_kv_heads: int = 2, device="cuda",
                  fill: int | None = None):
         super().__init__(KV_FMT_K8V4, n_pages, page_size, n_kv_heads, device, fill)
+
+
+class KvStream:
+    """A streamed cache: the whole context in a pinned host mirror and a
+    device window of fewer pages (include/k8v4.h, kv_stream).  mirror_table:
+    int32 device tensor, logical page -> mirror page.  The window map and
+    owner list start empty (-1); kv_stream_fetch places pages.  stats holds
+    [lookups, misses] of the streamed attention calls."""
+
+    def __init__(self, fmt: int, n_window: int, n_mirror: int, page_size: int, mirror_table,
+                 n_kv_heads: int = 2, device="cuda", fill: int | None = None):
+        torch = _torch()
+        self.window = KvPool(fmt, n_window, page_size, n_kv_heads, device=device, fill=fill)
+        self.mirror = KvPool(fmt, n_mirror, page_size, n_kv_heads, fill=fill, host=True)
+        if mirror_table.dtype != torch.int32 or not mirror_table.is_cuda:
+            raise ValueError("mirror_table must be an int32 device tensor")
+        self.mirror_table = mirror_table
+        n_table = int(mirror_table.numel())
+        self.window_map = torch.full((n_table,), -1, dtype=torch.int32, device=device)
+        self.window_owner = torch.full((n_window,), -1, dtype=torch.int32, device=device)
+        self.stats = torch.zeros(2, dtype=torch.int32, device=device)
+        self.fetch_list = torch.empty(2 * n_window, dtype=torch.int32, device=device)
+        self.n_table = n_table
+        self._struct = KvStreamStruct(self.window.struct, self.mirror.struct, mirror_table.data_ptr(),
+                                      self.window_map.data_ptr(), self.window_owner.data_ptr(),
+                                      self.stats.data_ptr(), self.fetch_list.data_ptr(), n_table, 0)
+
+    @property
+    def struct(self) -> KvStreamStruct:
+        return self._struct
+
+
+def kv_stream_append(s: KvStream, k, v, pos0: int, stream=None) -> None:
+    """Quantize k, v ([n][H][256]) once and write cells [pos0, pos0+n) to the
+    mirror, and to the window where their pages are resident."""
+    if k.shape != v.shape or k.dtype != v.dtype:
+        raise ValueError("k and v must have the same shape and dtype")
+    _check(lib().kv_stream_append(C.byref(s.struct), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dtype_code(k),
+                                  int(pos0), int(k.shape[0]), _stream(stream)), "kv_stream_append")
+
+
+def kv_stream_fetch(s: KvStream, first_page: int, n_pages: int, stream=None) -> None:
+    """Make logical pages [first_page, first_page + n_pages) resident (ring
+    placement, the last ones first when they do not all fit)."""
+    _check(lib().kv_stream_fetch(C.byref(s.struct), int(first_page), int(n_pages), _stream(stream)),
+           "kv_stream_fetch")
+
+
+def attn_decode_stream(s: KvStream, q, n_ctx: int, ws, scale: float = 0.0, out=None, stream=None):
+    """attn_decode over a streamed cache (window where resident, mirror otherwise)."""
+    torch = _torch()
+    if q.dim() != 2 or q.shape[1] != HEAD_DIM:
+        raise ValueError("q must be [n_q_heads][256]")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _check(lib().attn_decode_stream(C.byref(s.struct), _dev_ptr(q, "q"), _dtype_code(q), int(q.shape[0]),
+                                    int(n_ctx), float(scale), _dev_ptr(out, "out", (torch.float32,)),
+                                    _dev_ptr(ws, "ws"), ws.numel(), _stream(stream)), "attn_decode_stream")
+    return out
+
+
+def attn_verify_stream(s: KvStream, q, n_visible, ws, scale: float = 0.0, out=None, stream=None):
+    """attn_verify over a streamed cache."""
+    torch = _torch()
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [n_q][n_q_heads][256]")
+    n_q = int(q.shape[0])
+    if len(n_visible) != n_q:
+        raise ValueError("n_visible must have one entry per query row")
+    nv = (C.c_int32 * n_q)(*[int(x) for x in n_visible])
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _check(lib().attn_verify_stream(C.byref(s.struct), _dev_ptr(q, "q"), _dtype_code(q), int(q.shape[1]), n_q, nv,
+                                    float(scale), _dev_ptr(out, "out", (torch.float32,)), _dev_ptr(ws, "ws"),
+                                    ws.numel(), _stream(stream)), "attn_verify_stream")
+    return out
 
 
 def _seq(page_table) -> KvSeqStruct:

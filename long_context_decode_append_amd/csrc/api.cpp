@@ -404,6 +404,116 @@ int kv_check_page_table(const kv_pool *pool, const kv_seq *seq, int32_t n_cells,
   return KV_OK;
 }
 
+// ---------------------------------------------------------------- streamed cache
+
+static int check_stream(const kv_stream *s) {
+  if (!s) return KV_ERR_NULL;
+  if (int e = check_pool(&s->window, 0)) return e;
+  if (int e = check_pool(&s->mirror, 0)) return e;
+  if (s->window.fmt != s->mirror.fmt || s->window.n_kv_heads != s->mirror.n_kv_heads ||
+      s->window.page_size != s->mirror.page_size)
+    return KV_ERR_SHAPE;
+  if (!s->mirror_table || !s->window_map || !s->window_owner || !s->stats || !s->fetch_list) return KV_ERR_NULL;
+  if (s->n_table < 0) return KV_ERR_SHAPE;
+  if ((int64_t)s->n_table * s->window.page_size > ((int64_t)1 << 31) - 1) return KV_ERR_RANGE;
+  return KV_OK;
+}
+
+static kv_seq stream_seq(const kv_stream *s) {
+  kv_seq q;
+  q.page_table = s->window_map;
+  q.n_table = s->n_table;
+  q.reserved = 0;
+  return q;
+}
+
+int kv_stream_append(const kv_stream *s, const void *k, const void *v, int dtype, int32_t pos0, int32_t n_tokens,
+                     void *stream) {
+  CallScope scope;
+  if (int e = check_stream(s)) return e;
+  if (!k || !v) return KV_ERR_NULL;
+  if (int e = check_dtype(dtype)) return e;
+  kv_seq mq;
+  mq.page_table = s->mirror_table;
+  mq.n_table = s->n_table;
+  mq.reserved = 0;
+  if (int e = check_range(&s->mirror, &mq, pos0, n_tokens)) return e;
+  if (check_aligned16(k) || check_aligned16(v)) return KV_ERR_ALIGN;
+  if (n_tokens == 0) return KV_OK;
+  return launch_append(&s->mirror, &mq, k, v, dtype, pos0, n_tokens, (hipStream_t)stream, &s->window, s->window_map);
+}
+
+int kv_stream_fetch(const kv_stream *s, int32_t first_page, int32_t n_pages, void *stream) {
+  CallScope scope;
+  if (int e = check_stream(s)) return e;
+  if (first_page < 0 || n_pages < 0 || (int64_t)first_page + n_pages > s->n_table) return KV_ERR_RANGE;
+  if (n_pages == 0) return KV_OK;
+  return launch_stream_fetch(s, first_page, n_pages, (hipStream_t)stream);
+}
+
+int attn_decode_stream(const kv_stream *s, const void *q, int q_dtype, int n_q_heads, int32_t n_ctx, float scale,
+                       float *out, void *ws, size_t ws_bytes, void *stream) {
+  CallScope scope;
+  if (int e = check_stream(s)) return e;
+  const kv_seq seq = stream_seq(s);
+  if (int e = check_attn_common(&s->window, &seq, q, q_dtype, n_q_heads, out, 0)) return e;
+  if (n_ctx < 1) return KV_ERR_RANGE;
+  if (int e = check_range(&s->window, &seq, 0, n_ctx)) return e;
+  if (!ws) return KV_ERR_WORKSPACE;
+  if (check_aligned16(ws)) return KV_ERR_ALIGN;
+  AttnCall c;
+  c.pool = &s->window;
+  c.seq = &seq;
+  c.q = q;
+  c.q_dtype = q_dtype;
+  c.n_q_heads = n_q_heads;
+  c.n_q = 1;
+  for (int i = 0; i < kMaxQ; i++) c.limits[i] = 0;
+  c.limits[0] = n_ctx;
+  c.max_limit = n_ctx;
+  c.scale = pick_scale(scale);
+  c.out = out;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  c.stream = (hipStream_t)stream;
+  c.stream_s = s;
+  return launch_attn_splitk(c);
+}
+
+int attn_verify_stream(const kv_stream *s, const void *q, int q_dtype, int n_q_heads, int32_t n_q,
+                       const int32_t *n_visible, float scale, float *out, void *ws, size_t ws_bytes, void *stream) {
+  CallScope scope;
+  if (int e = check_stream(s)) return e;
+  const kv_seq seq = stream_seq(s);
+  if (int e = check_attn_common(&s->window, &seq, q, q_dtype, n_q_heads, out, 0)) return e;
+  if (!n_visible) return KV_ERR_NULL;
+  if (n_q < 1 || n_q > kMaxQ) return KV_ERR_SHAPE;
+  if (!ws) return KV_ERR_WORKSPACE;
+  if (check_aligned16(ws)) return KV_ERR_ALIGN;
+  AttnCall c;
+  c.max_limit = 0;
+  for (int i = 0; i < kMaxQ; i++) c.limits[i] = 0;
+  for (int i = 0; i < n_q; i++) {
+    if (n_visible[i] < 1) return KV_ERR_RANGE;
+    if (int e = check_range(&s->window, &seq, 0, n_visible[i])) return e;
+    c.limits[i] = n_visible[i];
+    if (n_visible[i] > c.max_limit) c.max_limit = n_visible[i];
+  }
+  c.pool = &s->window;
+  c.seq = &seq;
+  c.q = q;
+  c.q_dtype = q_dtype;
+  c.n_q_heads = n_q_heads;
+  c.n_q = n_q;
+  c.scale = pick_scale(scale);
+  c.out = out;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  c.stream = (hipStream_t)stream;
+  c.stream_s = s;
+  return launch_attn_splitk(c);
+}
+
 // attn_decode for callers that cannot allocate device memory: the split-K
 // partials go to `scratch`, a file-scope device array that every GPU the
 // library runs on holds (its own copy, at its own address) until the

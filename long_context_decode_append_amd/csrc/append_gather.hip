@@ -30,9 +30,17 @@ struct AppendArgs {
   const void *v;
   int dtype;       // 0 fp16, 1 fp32
   int pos0, n_tokens, n_pages, P, H;
+  // a second copy of the same cells (a streamed cache writes its mirror and
+  // its window): table pt2 into pool run2 (pt2 null: none); a cell whose
+  // entry is out of [0, n_pages2) is not resident there
+  uint8_t *run2[4];
+  const int32_t *pt2;
+  int n_pages2;
 };
 
-// one wave per (token, KV head); FMT selects the rule of each half
+// one wave per (token, KV head); FMT selects the rule of each half.  The
+// token is quantized once and stored into every destination that holds its
+// cell (all runs of each).
 template <int FMT>
 __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
   const int lane = threadIdx.x & 63;
@@ -40,43 +48,52 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
   if (item >= (int64_t)a.n_tokens * a.H) return;                       // whole wave exits
   const int t = (int)(item / a.H), g = (int)(item % a.H);
   const int p = a.pos0 + t;
-  const int page = a.pt[p / a.P];
-  if (page < 0 || page >= a.n_pages) return;                           // never write outside the pool
-  const int slot = p % a.P;
+  const int lp = p / a.P, slot = p % a.P;
+  const int page = a.pt[lp];
+  const bool ok = page >= 0 && page < a.n_pages;                       // never write outside a pool
+  const int page2 = a.pt2 ? a.pt2[lp] : -1;
+  const bool ok2 = page2 >= 0 && page2 < a.n_pages2;
+  if (!ok && !ok2) return;
   const size_t src = ((size_t)t * a.H + g) * 256 + 4 * lane;
-  const size_t tile = (size_t)page * a.H + g;
-  const size_t cell = tile * a.P + slot;
+  const size_t tile = (size_t)page * a.H + g, tile2 = (size_t)page2 * a.H + g;
+  const size_t cell = tile * a.P + slot, cell2 = tile2 * a.P + slot;
 
   float x[4];
   load4(a.k, a.dtype, src, x);
   if (FMT == KV_FMT_F16) {
     // no quantization: fp16 (round to nearest even) in the operand blocks
-    store_f16_k(a.run[0], cell, lane, x);
+    if (ok) store_f16_k(a.run[0], cell, lane, x);
+    if (ok2) store_f16_k(a.run2[0], cell2, lane, x);
     load4(a.v, a.dtype, src, x);
-    store_f16_v(a.run[2], cell, lane, x);
+    if (ok) store_f16_v(a.run[2], cell, lane, x);
+    if (ok2) store_f16_v(a.run2[2], cell2, lane, x);
     return;
   }
   if (FMT == KV_FMT_Q4_0) {
     fwht256_lane4(x, lane);
     uint16_t d16;
     const uint32_t codes = quant_q4(x, lane, d16);
-    store_q4(a.run[0], tile, a.P, slot, lane, codes, d16);
+    if (ok) store_q4(a.run[0], tile, a.P, slot, lane, codes, d16);
+    if (ok2) store_q4(a.run2[0], tile2, a.P, slot, lane, codes, d16);
   } else {
     float d;
     const uint32_t codes = quant_k(x, d);
-    store_int8<true>(a.run[0], a.run[1], cell, lane, codes, d);
+    if (ok) store_int8<true>(a.run[0], a.run[1], cell, lane, codes, d);
+    if (ok2) store_int8<true>(a.run2[0], a.run2[1], cell2, lane, codes, d);
   }
 
   load4(a.v, a.dtype, src, x);
   if (FMT == KV_FMT_INT8) {
     float d;
     const uint32_t codes = quant_k(x, d);
-    store_int8<false>(a.run[2], a.run[3], cell, lane, codes, d);
+    if (ok) store_int8<false>(a.run[2], a.run[3], cell, lane, codes, d);
+    if (ok2) store_int8<false>(a.run2[2], a.run2[3], cell2, lane, codes, d);
   } else {
     fwht256_lane4(x, lane);
     uint16_t d16;
     const uint32_t codes = quant_q4(x, lane, d16);
-    store_q4(a.run[2], tile, a.P, slot, lane, codes, d16);
+    if (ok) store_q4(a.run[2], tile, a.P, slot, lane, codes, d16);
+    if (ok2) store_q4(a.run2[2], tile2, a.P, slot, lane, codes, d16);
   }
 }
 
@@ -156,10 +173,15 @@ __global__ void fill_zero_kernel(uint32_t *p, size_t n_words) {
 }
 
 int launch_append(const kv_pool *pool, const kv_seq *seq, const void *k, const void *v, int dtype, int pos0,
-                  int n, hipStream_t s) {
+                  int n, hipStream_t s, const kv_pool *pool2, const int32_t *pt2) {
   AppendArgs a;
-  for (int r = 0; r < 4; r++) a.run[r] = (uint8_t *)pool->run[r];
+  for (int r = 0; r < 4; r++) {
+    a.run[r] = (uint8_t *)pool->run[r];
+    a.run2[r] = pool2 ? (uint8_t *)pool2->run[r] : nullptr;
+  }
   a.pt = seq->page_table;
+  a.pt2 = pool2 ? pt2 : nullptr;
+  a.n_pages2 = pool2 ? pool2->n_pages : 0;
   a.k = k;
   a.v = v;
   a.dtype = dtype;

@@ -67,6 +67,7 @@ struct SplitArgs {
   int n_pages, P, H;
   int p_shift;          // log2(P) when P is a power of two, else -1
   int k_bytes, ks_bytes, v_bytes, vs_bytes;  // run sizes (each < 2^31)
+  int k_bytes_m, ks_bytes_m, v_bytes_m, vs_bytes_m;  // the same for a streamed cache's mirror
   int n_q_heads, n_rows, rows_per_pass;
   int limits[kMaxQ];
   int max_limit;
@@ -86,6 +87,15 @@ struct SplitArgs {
   int batch;
   const int32_t *pts[kMaxQ];
   int v_rot;            // V stored rotated (k8v4, q4_0): the combine finishes the inverse rotation
+  // streamed cache: pt is the window map (logical page -> window slot, -1 when
+  // not resident) and the pool above the window; a page not resident is read
+  // from the mirror (mapped pinned host memory), at mirror_table[page]
+  const int32_t *mirror_table;
+  const int8_t *m_kc;
+  const float *m_ks;
+  const uint8_t *m_vq;
+  const float *m_vs;
+  int m_n_pages;
 };
 
 // dim of output tile j held by column n of the PV MFMA.  q4_0 V: column n
@@ -132,6 +142,7 @@ struct Half {
   int bad;        // page-table entry out of range: rows that read it return NaN
   int none;       // a step past the wave's last: its loads read through empty
                   // buffer descriptors (zeros, no memory access)
+  int host;       // streamed cache: the page is read from the mirror
   int k_soff;     // K data of the half's first cell (int8 codes, or q4_0 nibbles)
   int ks_soff;    // K scales (fp32 pairs, or the q4_0 scale group)
   int v_soff;     // V data (q4_0 nibbles, or int8 codes)
@@ -149,10 +160,11 @@ __device__ __forceinline__ int page_of(const SplitArgs &a, int pos) {
 }
 
 template <int FMT>
-__device__ __forceinline__ Half make_half(const SplitArgs &a, int g, int pos, int page) {
+__device__ __forceinline__ Half make_half(const SplitArgs &a, int g, int pos, int page, int host) {
   Half h;
   h.none = 0;
-  h.bad = page < 0 || page >= a.n_pages;
+  h.host = host;
+  h.bad = page < 0 || page >= (host ? a.m_n_pages : a.n_pages);
   const int pg = h.bad ? 0 : page;
   const int slot0 = pos - page_of(a, pos) * a.P;  // a multiple of 16
   const int tile = pg * a.H + g;
@@ -182,37 +194,54 @@ __device__ __forceinline__ Half make_half(const SplitArgs &a, int g, int pos, in
   return h;
 }
 
+// Where logical page idx lives: the table entry, or for a streamed cache
+// the window slot when resident and else the mirror page (both entries are
+// read, as scalar loads, so no branch waits for the first)
+template <bool STREAM>
+__device__ __forceinline__ void locate(const SplitArgs &a, const int32_t *pt, int idx, int &page, int &host) {
+  const int w = pt_entry(pt, idx);
+  if (STREAM) {
+    const int m = pt_entry(a.mirror_table, idx);
+    host = w < 0;
+    page = host ? m : w;
+  } else {
+    host = 0;
+    page = w;
+  }
+}
+
 // the two halves of the step at c (c < c_end); page entries read here are
 // scalar loads
-template <int FMT>
+template <int FMT, bool STREAM>
 __device__ __forceinline__ void step_halves(const SplitArgs &a, const int32_t *pt, int g, int c, int c_end, Half &h0,
                                             Half &h1) {
   const int p1pos = (c + 16 < c_end) ? c + 16 : c;
-  const int pg0 = pt_entry(pt, page_of(a, c));
-  const int pg1 = pt_entry(pt, page_of(a, p1pos));
-  h0 = make_half<FMT>(a, g, c, pg0);
-  h1 = make_half<FMT>(a, g, p1pos, pg1);
+  int pg0, pg1, hs0, hs1;
+  locate<STREAM>(a, pt, page_of(a, c), pg0, hs0);
+  locate<STREAM>(a, pt, page_of(a, p1pos), pg1, hs1);
+  h0 = make_half<FMT>(a, g, c, pg0, hs0);
+  h1 = make_half<FMT>(a, g, p1pos, pg1, hs1);
 }
 
 // The halves of the first two steps of a wave (at c0 and c1): the four
 // page-table entries are read together, so the kernel start waits for one
 // scalar round trip instead of two.
-template <int FMT>
+template <int FMT, bool STREAM>
 __device__ __forceinline__ void first_halves(const SplitArgs &a, const int32_t *pt, int g, int c0, int c1, int c_end,
                                              Half &h0, Half &h1,
                                              Half &n0, Half &n1) {
   const int pos[4] = {c0, (c0 + 16 < c_end) ? c0 + 16 : c0, c1, (c1 + 16 < c_end) ? c1 + 16 : c1};
-  int pidx[4], pg[4];
+  int pidx[4], pg[4], hs[4];
   if (a.p_shift >= 0) {
     for (int i = 0; i < 4; i++) pidx[i] = pos[i] >> a.p_shift;
   } else {
     for (int i = 0; i < 4; i++) pidx[i] = pos[i] / a.P;
   }
-  for (int i = 0; i < 4; i++) pg[i] = pt_entry(pt, pidx[i]);
-  h0 = make_half<FMT>(a, g, pos[0], pg[0]);
-  h1 = make_half<FMT>(a, g, pos[1], pg[1]);
-  n0 = make_half<FMT>(a, g, pos[2], pg[2]);
-  n1 = make_half<FMT>(a, g, pos[3], pg[3]);
+  for (int i = 0; i < 4; i++) locate<STREAM>(a, pt, pidx[i], pg[i], hs[i]);
+  h0 = make_half<FMT>(a, g, pos[0], pg[0], hs[0]);
+  h1 = make_half<FMT>(a, g, pos[1], pg[1], hs[1]);
+  n0 = make_half<FMT>(a, g, pos[2], pg[2], hs[2]);
+  n1 = make_half<FMT>(a, g, pos[3], pg[3], hs[3]);
 }
 
 // k-slot order inside an 8-dim q4_0 K operand: the nibble unpack yields the
@@ -274,7 +303,7 @@ __device__ __forceinline__ void append_token_partial(const SplitArgs &a, int g, 
 // extra tiles spill into AGPRs, so one wave per SIMD).
 // fp16 (T = 1 only): a step's raw K and V take 128 VGPRs, one workgroup per
 // CU (the split plan's target anyway).
-template <bool QF32, int FMT, bool NT, int T>
+template <bool QF32, int FMT, bool NT, int T, bool STREAM>
 __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void attn_splitk_kernel(const SplitArgs a) {
   constexpr int kAux = NT ? 2 : 0;  // buffer-load cache policy bits: 2 = nt
   __shared__ __attribute__((aligned(16))) float lds_o[kWaves * 16 * 64 * 4];  // wave states, accumulator layout
@@ -318,6 +347,11 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
   const __amdgpu_buffer_rsrc_t rks_ = __builtin_amdgcn_make_buffer_rsrc((void *)a.ks, (short)0, a.ks_bytes, kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rv_ = __builtin_amdgcn_make_buffer_rsrc((void *)a.vq, (short)0, a.v_bytes, kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rvs_ = __builtin_amdgcn_make_buffer_rsrc((void *)a.vs, (short)0, a.vs_bytes, kRsrcFlags);
+  // a streamed cache's mirror runs (mapped pinned host memory)
+  const __amdgpu_buffer_rsrc_t rkm = __builtin_amdgcn_make_buffer_rsrc((void *)a.m_kc, (short)0, STREAM ? a.k_bytes_m : 0, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rksm = __builtin_amdgcn_make_buffer_rsrc((void *)a.m_ks, (short)0, STREAM ? a.ks_bytes_m : 0, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rvm = __builtin_amdgcn_make_buffer_rsrc((void *)a.m_vq, (short)0, STREAM ? a.v_bytes_m : 0, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rvsm = __builtin_amdgcn_make_buffer_rsrc((void *)a.m_vs, (short)0, STREAM ? a.vs_bytes_m : 0, kRsrcFlags);
   // the same runs with no records: a load through one returns zeros without
   // touching memory (the unconditional prefetch past a wave's last step)
   const __amdgpu_buffer_rsrc_t rk0 = __builtin_amdgcn_make_buffer_rsrc((void *)a.kc, (short)0, 0, kRsrcFlags);
@@ -353,13 +387,13 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
   f32x4 vsr[2][2];
   Half cur0, cur1, nxt0, nxt1;
   auto load_k = [&](int h2, const Half &h) {
-    const __amdgpu_buffer_rsrc_t rk = h.none ? rk0 : rk_;
+    const __amdgpu_buffer_rsrc_t rk = h.none ? rk0 : (STREAM && h.host ? rkm : rk_);
     for (int j = 0; j < kKLoads; j++)
       kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + kstep_j * j, h.k_soff, kAux);
   };
   auto load_ks = [&](int h2, const Half &h) {
-    const __amdgpu_buffer_rsrc_t rks = h.none ? rks0 : rks_;
-    const __amdgpu_buffer_rsrc_t rk = h.none ? rk0 : rk_;
+    const __amdgpu_buffer_rsrc_t rks = h.none ? rks0 : (STREAM && h.host ? rksm : rks_);
+    const __amdgpu_buffer_rsrc_t rk = h.none ? rk0 : (STREAM && h.host ? rkm : rk_);
     if (kF16) {
       // no scales
     } else if (kInt8K) {
@@ -370,7 +404,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
     }
   };
   auto load_v = [&](int h2, const Half &h) {
-    const __amdgpu_buffer_rsrc_t rv = h.none ? rv0 : rv_;
+    const __amdgpu_buffer_rsrc_t rv = h.none ? rv0 : (STREAM && h.host ? rvm : rv_);
     if (kF16) {
       for (int u = 0; u < 8; u++) vr16[h2][u] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_voff + 1024 * u, h.v_soff, kAux);
     } else if (kQ4V) {
@@ -380,8 +414,8 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
     }
   };
   auto load_vd = [&](int h2, const Half &h) {
-    const __amdgpu_buffer_rsrc_t rvs = h.none ? rvs0 : rvs_;
-    const __amdgpu_buffer_rsrc_t rv = h.none ? rv0 : rv_;
+    const __amdgpu_buffer_rsrc_t rvs = h.none ? rvs0 : (STREAM && h.host ? rvsm : rvs_);
+    const __amdgpu_buffer_rsrc_t rv = h.none ? rv0 : (STREAM && h.host ? rvm : rv_);
     if (kF16) {
       // no scales
     } else if (kQ4V) {
@@ -422,7 +456,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
     // unconditional (a wave without work loads cell 0's step and never uses
     // it), so no control-flow join makes the compiler over-wait below
     const int cf = has_work ? c_first : 0, ce = has_work ? c_end : 16;
-    first_halves<FMT>(a, ptab, g, cf, has_work ? min(c_first + stride, c_last) : 0, ce, cur0, cur1, nxt0, nxt1);
+    first_halves<FMT, STREAM>(a, ptab, g, cf, has_work ? min(c_first + stride, c_last) : 0, ce, cur0, cur1, nxt0, nxt1);
     // loads of steps that do not exist fetch nothing
     cur0.none = cur1.none = !has_work;
     nxt0.none = nxt1.none = !has_work || c_first + stride > c_last;
@@ -550,7 +584,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
     while (true) {
       // pages of the step after next
       Half nn0, nn1;
-      step_halves<FMT>(a, ptab, g, min(c + 2 * stride, c_last), c_end, nn0, nn1);
+      step_halves<FMT, STREAM>(a, ptab, g, min(c + 2 * stride, c_last), c_end, nn0, nn1);
       nn0.none = nn1.none = c + 2 * stride > c_last;
       const int badp[2] = {cur0.bad, cur1.bad};
       // whole step inside every valid row's limit and on valid pages: no
@@ -573,7 +607,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
               acc0[t] = mfma16x16x32(ka, qop[t][j], acc0[t]);
               if (QF32) acc0[t] = mfma16x16x32(ka, qlo[t][j], acc0[t]);
             }
-            kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(nx[h2]->none ? rk0 : rk_, k_voff + kstep_j * j, nx[h2]->k_soff, kAux);
+            kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(nx[h2]->none ? rk0 : (STREAM && nx[h2]->host ? rkm : rk_), k_voff + kstep_j * j, nx[h2]->k_soff, kAux);
             continue;
           }
           if (kInt8K) {
@@ -618,7 +652,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
             }
           }
           // K chunk j of this half consumed: refill with the next step's
-          kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(nx[h2]->none ? rk0 : rk_, k_voff + kstep_j * j, nx[h2]->k_soff, kAux);
+          kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(nx[h2]->none ? rk0 : (STREAM && nx[h2]->host ? rkm : rk_), k_voff + kstep_j * j, nx[h2]->k_soff, kAux);
         }
         // several row tiles: the softmax scale folds into the cells' two K
         // group scales once, for all of them
@@ -741,7 +775,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
           const f16x8 bhi = pack8(v0.z, v0.w, v1.z, v1.w);  // tile 2u + 1: dim 16 n + 2 u + 1
           // chunk u of this step consumed: refill with the next step's
           for (int h2 = 0; h2 < 2; h2++)
-            vr16[h2][u] = __builtin_amdgcn_raw_buffer_load_b128(nx[h2]->none ? rv0 : rv_, v_voff + 1024 * u, nx[h2]->v_soff, kAux);
+            vr16[h2][u] = __builtin_amdgcn_raw_buffer_load_b128(nx[h2]->none ? rv0 : (STREAM && nx[h2]->host ? rvm : rv_), v_voff + 1024 * u, nx[h2]->v_soff, kAux);
           for (int t = 0; t < T; t++) o[t][2 * u] = mfma16x16x32(pop[t], blo, o[t][2 * u]);
           for (int t = 0; t < T; t++) o[t][2 * u + 1] = mfma16x16x32(pop[t], bhi, o[t][2 * u + 1]);
         }
@@ -947,6 +981,22 @@ __global__ __launch_bounds__(kCombineWaves * 64) void attn_combine_kernel(const 
   *reinterpret_cast<f32x4 *>(op) = f32x4{y[0], y[1], y[2], y[3]};
 }
 
+// Lookups of a streamed attention call: one per logical page [0, n_read),
+// a miss per page whose window map entry is negative (not resident).  One
+// workgroup; two device-scope additions to the caller's counters.
+__global__ __launch_bounds__(256) void stream_lookup_kernel(const int32_t *window_map, int n_read, int32_t *stats) {
+  __shared__ int lds_miss[4];
+  int miss = 0;
+  for (int i = threadIdx.x; i < n_read; i += 256) miss += window_map[i] < 0 ? 1 : 0;
+  for (int o = 32; o > 0; o >>= 1) miss += __shfl_xor(miss, o, 64);
+  if ((threadIdx.x & 63) == 0) lds_miss[threadIdx.x >> 6] = miss;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    atomicAdd(&stats[0], n_read);
+    atomicAdd(&stats[1], lds_miss[0] + lds_miss[1] + lds_miss[2] + lds_miss[3]);
+  }
+}
+
 // ---------------------------------------------------------------- host side
 
 // Compute units of the current device, cached per device (relaxed atomics:
@@ -1039,6 +1089,32 @@ int launch_attn_splitk(const AttnCall &c) {
     a.v_bytes = (int)vb;
     a.vs_bytes = (int)vsb;
   }
+  const bool stream = c.stream_s != nullptr;
+  a.mirror_table = nullptr;
+  a.m_kc = nullptr;
+  a.m_ks = nullptr;
+  a.m_vq = nullptr;
+  a.m_vs = nullptr;
+  a.m_n_pages = 0;
+  a.k_bytes_m = a.ks_bytes_m = a.v_bytes_m = a.vs_bytes_m = 0;
+  if (stream) {
+    const kv_pool *m = &c.stream_s->mirror;
+    const size_t kb = run_bytes(m->fmt, 0, m->n_pages, a.P, H, kHeadDim);
+    const size_t sb = run_bytes(m->fmt, 1, m->n_pages, a.P, H, kHeadDim);
+    const size_t vb = run_bytes(m->fmt, 2, m->n_pages, a.P, H, kHeadDim);
+    const size_t vsb = run_bytes(m->fmt, 3, m->n_pages, a.P, H, kHeadDim);
+    if (kb > 0x7fffffffu || sb > 0x7fffffffu || vb > 0x7fffffffu || vsb > 0x7fffffffu) return KV_ERR_UNSUPPORTED;
+    a.k_bytes_m = (int)kb;
+    a.ks_bytes_m = (int)sb;
+    a.v_bytes_m = (int)vb;
+    a.vs_bytes_m = (int)vsb;
+    a.mirror_table = c.stream_s->mirror_table;
+    a.m_kc = (const int8_t *)m->run[0];
+    a.m_ks = (const float *)m->run[1];
+    a.m_vq = (const uint8_t *)m->run[2];
+    a.m_vs = (const float *)m->run[3];
+    a.m_n_pages = m->n_pages;
+  }
   a.n_q_heads = c.n_q_heads;
   a.n_rows = n_rows;
   a.rows_per_pass = rows_per_pass;
@@ -1066,24 +1142,38 @@ int launch_attn_splitk(const AttnCall &c) {
   for (int i = 0; i < (c.batch ? c.n_q : 1); i++) stream_cells += (size_t)(c.batch ? c.limits[i] : c.max_limit);
   const bool nt = (passes == 1 || c.batch) &&
                   stream_cells * kv_cell_bytes(pool->fmt, H, kHeadDim) > ((size_t)16 << 20);
-  switch (((pool->fmt * 4 + (qf32 ? 2 : 0) + (nt ? 1 : 0)) << 2) + T) {
-#define K8V4_SPLIT_CASE(F, Q, N, T_) \
-  case ((F * 4 + (Q ? 2 : 0) + (N ? 1 : 0)) << 2) + T_: \
-    launch((attn_splitk_kernel<Q, F, N, T_>), grid, dim3(256), c.stream, a); \
+  if (stream) {
+    // device-side lookups: one per logical page the call reads, a miss per
+    // page not resident; counted before the attention reads them
+    const int n_read = (int)(((int64_t)c.max_limit + a.P - 1) / a.P);
+    launch(stream_lookup_kernel, dim3(1), dim3(256), c.stream, (const int32_t *)a.pt, n_read, c.stream_s->stats);
+    if (int e = launch_status()) return e;
+  }
+  const bool nt_k = nt && !stream;
+  switch ((((pool->fmt * 2 + (stream ? 1 : 0)) * 4 + (qf32 ? 2 : 0) + (nt_k ? 1 : 0)) << 2) + T) {
+#define K8V4_SPLIT_CASE(F, S, Q, N, T_) \
+  case (((F * 2 + (S ? 1 : 0)) * 4 + (Q ? 2 : 0) + (N ? 1 : 0)) << 2) + T_: \
+    launch((attn_splitk_kernel<Q, F, N, T_, S>), grid, dim3(256), c.stream, a); \
     break;
-#define K8V4_SPLIT_FMT(F)                \
-  K8V4_SPLIT_CASE(F, false, false, 1)    \
-  K8V4_SPLIT_CASE(F, false, true, 1)     \
-  K8V4_SPLIT_CASE(F, true, false, 1)     \
-  K8V4_SPLIT_CASE(F, true, true, 1)      \
-  K8V4_SPLIT_CASE(F, false, false, 2)    \
-  K8V4_SPLIT_CASE(F, false, true, 2)     \
-  K8V4_SPLIT_CASE(F, false, false, 3)    \
-  K8V4_SPLIT_CASE(F, false, true, 3)
-    K8V4_SPLIT_CASE(KV_FMT_F16, false, false, 1)
-    K8V4_SPLIT_CASE(KV_FMT_F16, false, true, 1)
-    K8V4_SPLIT_CASE(KV_FMT_F16, true, false, 1)
-    K8V4_SPLIT_CASE(KV_FMT_F16, true, true, 1)
+#define K8V4_SPLIT_FMT(F)                      \
+  K8V4_SPLIT_CASE(F, false, false, false, 1)   \
+  K8V4_SPLIT_CASE(F, false, false, true, 1)    \
+  K8V4_SPLIT_CASE(F, false, true, false, 1)    \
+  K8V4_SPLIT_CASE(F, false, true, true, 1)     \
+  K8V4_SPLIT_CASE(F, false, false, false, 2)   \
+  K8V4_SPLIT_CASE(F, false, false, true, 2)    \
+  K8V4_SPLIT_CASE(F, false, false, false, 3)   \
+  K8V4_SPLIT_CASE(F, false, false, true, 3)    \
+  K8V4_SPLIT_CASE(F, true, false, false, 1)    \
+  K8V4_SPLIT_CASE(F, true, true, false, 1)     \
+  K8V4_SPLIT_CASE(F, true, false, false, 2)    \
+  K8V4_SPLIT_CASE(F, true, false, false, 3)
+    K8V4_SPLIT_CASE(KV_FMT_F16, false, false, false, 1)
+    K8V4_SPLIT_CASE(KV_FMT_F16, false, false, true, 1)
+    K8V4_SPLIT_CASE(KV_FMT_F16, false, true, false, 1)
+    K8V4_SPLIT_CASE(KV_FMT_F16, false, true, true, 1)
+    K8V4_SPLIT_CASE(KV_FMT_F16, true, false, false, 1)
+    K8V4_SPLIT_CASE(KV_FMT_F16, true, true, false, 1)
     K8V4_SPLIT_FMT(KV_FMT_INT8)
     K8V4_SPLIT_FMT(KV_FMT_Q4_0)
     K8V4_SPLIT_FMT(KV_FMT_K8V4)

@@ -28,12 +28,17 @@ inline void launch(Kernel kernel, dim3 grid, dim3 block, hipStream_t s, Args... 
   hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
 }
 
+// pool2 / pt2 (optional): a second copy of the same cells (a streamed
+// cache's window), written from the same quantization
 int launch_append(const kv_pool *pool, const kv_seq *seq, const void *k, const void *v, int dtype, int pos0,
-                  int n, hipStream_t s);
+                  int n, hipStream_t s, const kv_pool *pool2 = nullptr, const int32_t *pt2 = nullptr);
 int launch_gather(const kv_pool *pool, const kv_seq *seq, int pos0, int n, void *const out[4], hipStream_t s);
 int launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 int launch_page_copy(const kv_pool *dst, const kv_pool *src, const int32_t *dst_pages, const int32_t *src_pages,
                      int n, hipStream_t s);
+// kv_stream_fetch: ring placement of logical pages [first, first + n) in the
+// window (bookkeeping kernel), then the page copies it lists
+int launch_stream_fetch(const kv_stream *st, int first, int n, hipStream_t s);
 int launch_probe_read(const void *buf, size_t bytes, void *sink, hipStream_t s);
 
 // Decode / verify: n_q query rows of 8 heads per KV head, row i of query
@@ -62,6 +67,9 @@ struct AttnCall {
   // table pts[i] and length limits[i]; seq is then unused
   bool batch = false;
   const int32_t *pts[kMaxQ] = {};
+  // streamed cache (decode / verify): pool is the window, seq's table the
+  // window map; pages not resident are read from the mirror
+  const kv_stream *stream_s = nullptr;
 };
 int launch_attn_splitk(const AttnCall &c);
 

@@ -61,4 +61,50 @@ int launch_page_copy(const kv_pool *dst, const kv_pool *src, const int32_t *dst_
   return launch_status();
 }
 
+// Miss service of a streamed cache (kv_stream_fetch): the last n_place
+// pages of the requested range, logical pages [first, first + n_place), are
+// placed in the window as a ring, page i in slot i % W.  A page already in
+// its slot stays; otherwise the slot's previous page becomes non-resident,
+// page i takes the slot and the pair (slot, its mirror page) is listed for
+// the copy kernel that follows (-1 pairs are skipped there).  One thread
+// per placed page: n_place <= W consecutive pages have distinct slots, and
+// a slot's previous page (the only other page the thread writes) lies
+// outside the placed range, so no two threads touch one entry.  A page
+// whose mirror entry is out of range is left non-resident (the attention
+// then reads it from the mirror, where it gives NaN rows).
+__global__ __launch_bounds__(256) void stream_place_kernel(int32_t *window_map, int32_t *owner,
+                                                           const int32_t *mirror_table, int m_n_pages, int first,
+                                                           int n_place, int W, int32_t *dst_list, int32_t *src_list) {
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k >= n_place) return;
+  const int i = first + k;
+  const int slot = i % W;
+  const int mp = mirror_table[i];
+  const bool fetchable = mp >= 0 && mp < m_n_pages;
+  int dst = -1, src = -1;
+  if (window_map[i] != slot || owner[slot] != i) {
+    const int old = owner[slot];
+    if (old >= 0 && old != i) window_map[old] = -1;
+    owner[slot] = fetchable ? i : -1;
+    window_map[i] = fetchable ? slot : -1;
+    if (fetchable) {
+      dst = slot;
+      src = mp;
+    }
+  }
+  dst_list[k] = dst;
+  src_list[k] = src;
+}
+
+int launch_stream_fetch(const kv_stream *st, int first, int n, hipStream_t s) {
+  const int W = st->window.n_pages;
+  const int n_place = n < W ? n : W;
+  if (n_place <= 0) return KV_OK;
+  int32_t *dst_list = st->fetch_list, *src_list = st->fetch_list + W;
+  launch(stream_place_kernel, dim3((unsigned)((n_place + 255) / 256)), dim3(256), s, st->window_map, st->window_owner,
+         st->mirror_table, st->mirror.n_pages, first + n - n_place, n_place, W, dst_list, src_list);
+  if (int e = launch_status()) return e;
+  return launch_page_copy(&st->window, &st->mirror, dst_list, src_list, n_place, s);
+}
+
 }  // namespace k8v4

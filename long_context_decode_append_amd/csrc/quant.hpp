@@ -74,7 +74,12 @@ __device__ __forceinline__ uint32_t quant_q4(const float y[4], int lane, uint16_
     c = c > 15 ? 15 : c;
     codes |= (uint32_t)c << (8 * i);
   }
-  d16 = f32_to_f16_bits(d);
+  // d is pinned as its own value first: otherwise the compiler may fold the
+  // multiply by -1/8 and the conversion into one mixed fma (x * y + 0),
+  // which turns the -0 scale of an all-zero block into +0
+  float dp = d;
+  asm volatile("" : "+v"(dp));
+  d16 = f32_to_f16_bits(dp);
   return codes;
 }
 

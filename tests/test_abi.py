@@ -166,3 +166,48 @@ def test_workspace_size_is_monotone_in_context(k8):
     assert L.attn_workspace_bytes(C.byref(pool), 16, 5, 240000) > sizes[-1]
     assert L.attn_workspace_bytes(C.byref(pool), 16, 17, 100) == 0
     assert L.attn_workspace_bytes(C.byref(pool), 12, 1, 100) == 0
+
+
+def _stream(k8, win=None, mir=None, n_table=4, ptrs=(80, 96, 112, 128, 144)):
+    win = win or _pool(k8, pages=2)
+    mir = mir or _pool(k8, pages=4, ptrs=(160, 176, 192, 0))
+    mt, wm, wo, st, fl = [C.c_void_p(p) if p else None for p in ptrs]
+    return k8.KvStreamStruct(win, mir, mt, wm, wo, st, fl, n_table, 0)
+
+
+def test_stream_validation_errors_before_launch(k8):
+    """The streamed cache refuses missing pieces and mismatched pools before
+    launching: every run of both copies and every map is required."""
+    L = k8.lib()
+    P = C.byref
+    dummy = C.c_void_p(16)
+    s = _stream(k8)
+    assert L.kv_stream_append(None, dummy, dummy, 0, 0, 1, None) == -1
+    # the mirror's V run missing: an error, never a skipped host write
+    s_nov = _stream(k8, mir=_pool(k8, pages=4, ptrs=(160, 176, 0, 0)))
+    assert L.kv_stream_append(P(s_nov), dummy, dummy, 0, 0, 1, None) == -1
+    s_nowin = _stream(k8, win=_pool(k8, pages=2, ptrs=(16, 32, 0, 0)))
+    assert L.kv_stream_append(P(s_nowin), dummy, dummy, 0, 0, 1, None) == -1
+    # maps and scratch are required
+    for i in range(5):
+        ptrs = [80, 96, 112, 128, 144]
+        ptrs[i] = 0
+        assert L.kv_stream_fetch(P(_stream(k8, ptrs=tuple(ptrs))), 0, 1, None) == -1
+    # pools of different formats or page sizes
+    assert L.kv_stream_append(P(_stream(k8, win=_pool(k8, fmt=1, pages=2, ptrs=(16, 32, 48, 64)))),
+                              dummy, dummy, 0, 0, 1, None) == -2
+    assert L.kv_stream_append(P(_stream(k8, win=_pool(k8, P=32, pages=2))), dummy, dummy, 0, 0, 1, None) == -2
+    # ranges: cells beyond the table, pages beyond it
+    assert L.kv_stream_append(P(s), dummy, dummy, 0, 60, 5, None) == -3
+    assert L.kv_stream_fetch(P(s), 3, 2, None) == -3
+    assert L.kv_stream_fetch(P(s), -1, 1, None) == -3
+    assert L.kv_stream_fetch(P(s), 0, 0, None) == 0
+    q = C.c_void_p(256)
+    out = C.c_void_p(512)
+    ws = C.c_void_p(1024)
+    assert L.attn_decode_stream(P(s), q, 0, 16, 65, 0.0, out, ws, 1 << 20, None) == -3
+    assert L.attn_decode_stream(P(s), q, 0, 16, 0, 0.0, out, ws, 1 << 20, None) == -3
+    assert L.attn_decode_stream(P(s), q, 0, 16, 10, 0.0, out, None, 0, None) == -6
+    nv = (C.c_int32 * 2)(10, 70)
+    assert L.attn_verify_stream(P(s), q, 0, 16, 2, nv, 0.0, out, ws, 1 << 20, None) == -3
+    assert L.attn_verify_stream(P(s), q, 0, 16, 0, nv, 0.0, out, ws, 1 << 20, None) == -2

@@ -1,9 +1,14 @@
-"""Streamed cache pieces on the GPU ("kv: --kv k8v4 streams with
---kv-resident", Tests): all pages mirrored to pinned host memory, the pages
-of a context copied back into a device window at other slots, and attention
-over the window through its own table bitwise equal to attention over the
-resident pool (decode, verify, prefill), for the three formats.  Negative
-control: a window missing one page is detected.
+"""The streamed cache on the GPU ("kv: --kv k8v4 streams with
+--kv-resident", How and Tests): appends that write the pinned host mirror
+and the device window from one quantization, miss service into a ring
+window, and streamed decode / verify (window where resident, mirror where
+not) bitwise equal to the same calls on a resident pool, whose output is
+checked against the oracle, for the four formats; lookups and misses
+counted on the device; negative controls (a mirror page's V half left out;
+a mirror missing its V run is refused).  Also the page mover alone: all
+pages mirrored to pinned host memory and copied back into a window at other
+slots, attention through the window's table bitwise equal to the resident
+pool (decode, verify, prefill), with a window missing one page detected.
 """
 import sys
 
@@ -44,6 +49,115 @@ def page_block(pool, run, page):
     """The bytes of one page in one run (runs are [page][head][slot])."""
     nb = pool.runs[run].numel() // pool.n_pages
     return pool.runs[run][page * nb:(page + 1) * nb]
+
+
+TOL = 2e-3
+
+
+def rel_err(out, ref):
+    out, ref = np.asarray(out, np.float64), np.asarray(ref, np.float64)
+    return float((np.abs(out - ref).max(-1) / np.abs(ref).max(-1)).max())
+
+
+@pytest.mark.parametrize("fmt", [3, 0, 1, 2])
+def test_streamed_cache_equals_resident_and_oracle(orc, k8, dev, fmt):
+    """A streamed cache ("kv: --kv k8v4 streams with --kv-resident", How and
+    Tests): the context grows in batches through kv_stream_append (one
+    quantization, written to the pinned host mirror and to the window where
+    resident), each batch followed by miss service (kv_stream_fetch: the
+    newest pages into a 16-page window, ring placement).  After every batch
+    the streamed decode and verify (window where resident, mirror where
+    not) are bitwise equal to the same calls on a resident pool, whose
+    output is checked against the oracle; the mirror image equals the
+    oracle's; lookups and misses are counted on the device."""
+    import torch
+    from pool_layout import gpu_plain_runs
+    P, ctx, n_mirror, W, n_res = 16, 1000, 70, 16, 80
+    n_table = (ctx + P - 1) // P
+    say(f"streamed cache fmt={fmt}")
+    mt = synth.page_table(71, n_table, n_mirror)
+    s = k8.KvStream(fmt, W, n_mirror, P, t_(mt, dev), fill=0x22)
+    t_res = synth.page_table(72, n_table, n_res)
+    res = k8.KvPool(fmt, n_res, P, 2, device=dev, fill=0x11)
+    g_res = t_(t_res, dev)
+    opool = orc.OraclePool(fmt, n_mirror, P, 2, sentinel=0x22)
+    k, v = synth.kv_tokens(73, 0, 0, ctx, 2, 256, np.float16)
+    q = synth.queries(74, 0, 0, 5, 16, 256, np.float16)
+    qt = t_(q, dev)
+    ws = k8.attn_workspace(res, 5, ctx)
+    batches, lookups, misses, pos = 0, 0, 0, 0
+    for n in (1, 15, 17, 100, 128, 250, 489):
+        k8.kv_stream_append(s, t_(k[pos:pos + n], dev), t_(v[pos:pos + n], dev), pos)
+        k8.kv_append(res, g_res, t_(k[pos:pos + n], dev), t_(v[pos:pos + n], dev), pos)
+        opool.append(mt, k[pos:pos + n], v[pos:pos + n], pos)
+        pos += n
+        n_pages = (pos + P - 1) // P
+        k8.kv_stream_fetch(s, 0, n_pages)
+        torch.cuda.synchronize()
+        wm = s.window_map.cpu().numpy()
+        resident = [i for i in range(n_pages) if wm[i] >= 0]
+        assert resident == list(range(max(0, n_pages - W), n_pages)), (pos, resident)
+        assert all(wm[i] == i % W for i in resident)
+        for nc in sorted({1, max(1, pos - 200), pos}):
+            a = k8.attn_decode(res, g_res, qt[0], nc, ws).cpu().numpy()
+            b = k8.attn_decode_stream(s, qt[0], nc, ws).cpu().numpy()
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), (pos, nc)
+            lookups += (nc + P - 1) // P
+            misses += sum(1 for i in range((nc + P - 1) // P) if wm[i] < 0)
+            batches += 1
+        nv = [pos, max(1, pos - 1), max(1, pos // 2), 1, max(1, pos - 17)]
+        a = k8.attn_verify(res, g_res, qt, nv, ws).cpu().numpy()
+        b = k8.attn_verify_stream(s, qt, nv, ws).cpu().numpy()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), (pos, nv)
+        lookups += (max(nv) + P - 1) // P
+        misses += sum(1 for i in range((max(nv) + P - 1) // P) if wm[i] < 0)
+        batches += 1
+    st = s.stats.cpu().numpy()
+    say(f"  {batches} batches, {int(st[0])} page lookups, {int(st[1])} misses, 0 failures")
+    assert int(st[0]) == lookups and int(st[1]) == misses and misses > 0
+    # the resident side against the oracle's exact attention
+    ref = orc.attention_from_pool(opool, mt, q, [ctx, ctx - 1, ctx // 2, 1, ctx - 17])
+    out = k8.attn_verify(res, g_res, qt, [ctx, ctx - 1, ctx // 2, 1, ctx - 17], ws).cpu().numpy()
+    err = rel_err(out, ref)
+    say(f"  resident vs oracle rel err {err:.3e}")
+    assert err <= TOL
+    # the mirror holds the oracle's image (sentinels included); the window's
+    # resident pages hold the same bytes as their mirror pages
+    plain = gpu_plain_runs(s.mirror)
+    for r in range(4):
+        if opool.runs[r] is not None:
+            assert np.array_equal(plain[r], opool.runs[r]), f"mirror run {r}"
+    wm = s.window_map.cpu().numpy()
+    for i in range(n_table):
+        if wm[i] >= 0:
+            for r in range(4):
+                if s.window.runs[r] is not None:
+                    assert torch.equal(page_block(s.window, r, int(wm[i])).cpu(),
+                                       page_block(s.mirror, r, int(mt[i])).cpu()), (i, r)
+    # negative control (the pages' trap: a V half whose host write was left
+    # out): one non-resident page's V run in the mirror cleared
+    gone = next(i for i in range(n_table) if wm[i] < 0)
+    page_block(s.mirror, 2, int(mt[gone])).zero_()
+    torch.cuda.synchronize()
+    a = k8.attn_decode(res, g_res, qt[0], ctx, ws).cpu().numpy()
+    b = k8.attn_decode_stream(s, qt[0], ctx, ws).cpu().numpy()
+    assert not np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_stream_append_refuses_a_missing_run(k8, dev):
+    """Every run of both copies is required: a mirror without its V run is
+    an error before anything is written, never a skipped host write."""
+    import ctypes as C
+    mt = t_(synth.page_table(75, 8, 8), dev)
+    s = k8.KvStream(3, 4, 8, 16, mt, fill=0)
+    k = t_(np.zeros((3, 2, 256), np.float16), dev)
+    st = s.struct
+    saved = st.mirror.run[2]
+    st.mirror.run[2] = None
+    rc = k8.lib().kv_stream_append(C.byref(st), C.c_void_p(k.data_ptr()), C.c_void_p(k.data_ptr()), 0, 0, 3, None)
+    st.mirror.run[2] = saved
+    assert rc == -1  # KV_ERR_NULL
+
 
 
 @pytest.mark.parametrize("fmt", [0, 1, 2, 3])
