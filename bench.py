@@ -16,7 +16,9 @@ Prints one JSON line on stdout:
   roofline: the decode kernel alone, algorithmic bytes (cells x 816 B per
             launch) over its mean duration from start/stop events recorded
             by hipExtLaunchKernelGGL around each launch,
-  cpu_baseline: the CPU oracle on a bounded sample (one layer's decode),
+  cpu_baseline: the CPU oracle on the host's cores on a bounded sample (one
+            layer's decode, 1 thread and the default thread count; append,
+            verify and a prefill sample under extra.cpu_oracle),
   extra: decode / verify at 240,000 cells and the 8,192-query prefill chunk.
 Progress goes to stderr.
 """
@@ -158,37 +160,84 @@ def stream_read_same_size(torch, k8, dev, n_bufs=6):
     return out
 
 
-def cpu_baseline(ctx: int, target_s: float = 12.0):
-    """Time the oracle's decode attention (gather, dequantize, fp64 softmax
-    attention) for one layer at ctx cells, from an oracle pool built from
-    the numpy stream of the same recipe."""
+def cpu_info():
+    """CPU model, logical CPUs of the host and those this process may use."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": os.cpu_count() or 1, "usable_cpus": usable}
+
+
+def cpu_baseline():
+    """The oracle on the host's cores, on bounded samples of the workloads:
+    one 240,000-cell oracle pool built by appends of 8,192-token chunks
+    (timed per chunk), then decode at 118,750 cells with 1 thread and with
+    the oracle's default thread count (the headline value), decode and the
+    5-query verify at 240,000 cells, and 32 sampled rows of the 8,192-query
+    prefill chunk at [231,808, 240,000) (first 8, last 8, 16 seeded others),
+    extrapolated to the whole chunk.  Inputs follow the numpy stream of the
+    same recipe."""
     import numpy as np
 
     import oracle
     from long_context_decode_append_amd import synth
-    P = 256
-    n_table = (ctx + P - 1) // P
-    pt = synth.page_table(3, n_table, n_table)
-    pool = oracle.OraclePool(3, n_table, P, 2)
+    P, ctx, n_pages = 256, 240000, 1024
+    threads = oracle.default_threads()
+    pt = synth.page_table(4, (ctx + P - 1) // P, n_pages)
+    pool = oracle.OraclePool(3, n_pages, P, 2)
+    app = []
     for s in range(0, ctx, synth.CHUNK):
         n = min(synth.CHUNK, ctx - s)
-        k, v = synth.kv_tokens(3, 0, s, n, 2, 256, np.float16)
-        pool.append(pt, k, v, s)
-    q = synth.queries(3, 0, 0, 1, 16, 256, np.float16)
-    times = []
-    t_start = time.perf_counter()
-    while True:
+        k, v = synth.kv_tokens(4, 0, s, n, 2, 256, np.float16)
         t0 = time.perf_counter()
-        oracle.attention_from_pool(pool, pt, q, [ctx])
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > target_s or len(times) >= 20:
-            break
-    t = sum(times) / len(times)
-    return {"value": round(ctx * CELL_BYTES / t / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"one layer of the 48: a {ctx}-cell decode step (gather, dequantize, fp64 "
-                      f"attention for 16 heads), {len(times)} run(s), {t:.2f} s each, "
-                      f"single-threaded C"}
+        pool.append(pt, k, v, s)
+        if n == synth.CHUNK:
+            app.append(time.perf_counter() - t0)
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    q1 = synth.queries(3, 0, 0, 1, 16, 256, np.float16)
+    d1 = timed(lambda: oracle.attention_from_pool(pool, pt, q1, [118750], threads=1))
+    dn = timed(lambda: oracle.attention_from_pool(pool, pt, q1, [118750], threads=threads))
+    d240 = timed(lambda: oracle.attention_from_pool(pool, pt, q1, [ctx], threads=threads))
+    q5 = synth.queries(4, 0, 1, 5, 16, 256, np.float16)
+    v5 = timed(lambda: oracle.attention_from_pool(pool, pt, q5, [ctx - 4 + i for i in range(5)], threads=threads))
+    pos0, n_new = 231808, 8192
+    rows = list(range(8)) + list(range(n_new - 8, n_new)) + sorted(
+        np.random.default_rng(5).choice(np.arange(8, n_new - 8), 16, replace=False).tolist())
+    qp = synth.queries(5, 0, 0, n_new, 16, 256, np.float16)[rows]
+    pf = timed(lambda: oracle.attention_from_pool(pool, pt, qp, [pos0 + r + 1 for r in rows], threads=threads))
+    flops_rows = sum(1024.0 * 16 * (pos0 + r + 1) for r in rows)
+    flops_all = sum(1024.0 * 16 * (pos0 + i + 1) for i in range(n_new))
+    b118 = 118750 * CELL_BYTES
+    info = cpu_info()
+    base = {"value": round(b118 / dn / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"one layer of the 48: a 118,750-cell decode step (gather, dequantize, fp64 attention "
+                      f"for 16 heads) by the C oracle with {threads} threads, {dn:.2f} s",
+            "single_thread_gbs": round(b118 / d1 / 1e9, 4), "single_thread_s": round(d1, 3),
+            **info}
+    extra = {"threads": threads, **info,
+             "append_8192_tokens_s": round(float(np.mean(app)), 4),
+             "append_tokens_per_s": round(synth.CHUNK / float(np.mean(app)), 1),
+             "decode_118750_s": {"1_thread": round(d1, 3), f"{threads}_threads": round(dn, 3)},
+             "decode_240000_s": round(d240, 3), "decode_240000_gbs": round(ctx * CELL_BYTES / d240 / 1e9, 4),
+             "verify5_240000_s": round(v5, 3),
+             "prefill_32_sampled_rows_s": round(pf, 3),
+             "prefill_8192_at_231808_s_extrapolated": round(pf * flops_all / flops_rows, 1),
+             "prefill_extrapolation": "time of the 32 sampled rows scaled by the chunk's flops over theirs"}
+    return base, extra
 
 
 def main():
@@ -331,7 +380,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        cpu = cpu_baseline(ctx)
+        cpu, extra["cpu_oracle"] = cpu_baseline()
 
     line = {
         "metric": METRIC,
