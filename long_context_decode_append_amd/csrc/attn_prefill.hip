@@ -73,22 +73,27 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
 }
 
 // Raw pages of one tile, in the registers of the thread that dequantizes
-// them.  Work unit u in [0, 512), two per thread:
-//   INT8 K: 16 codes of cell u / 16, dims 16 (u % 16) ..; scale (u < 64) of
-//           cell u / 2, group u % 2
-//   q4_0 K: bytes 8 (u % 2) .. + 7 of block (u % 16) / 2 of cell u / 16 and
+// them.  Work unit u in [0, 512), two per thread (u = tid and tid + 256); a
+// unit's cells lie in half u / 256 of the tile, so every load of a wave
+// reads one half (a wave-uniform base plus a fixed lane offset).  With
+// i = u % 256:
+//   INT8 K: 16 codes of cell 16 (u / 256) + i / 16, dims 16 (i % 16) ..
+//   q4_0 K: bytes 8 (i % 2) .. + 7 of block (i % 16) / 2 of the same cell and
 //           that block's fp16 scale
-//   q4_0 V: bytes 4 (u / 128) .. + 3 of block (u / 16) % 8 of cells 2 (u % 16)
-//           and 2 (u % 16) + 1, and the two blocks' scales
-//   INT8 V: codes of dims 8 (u / 16) .. + 7 of the same two cells, and the two
-//           cells' scales of that 128-dim group
-//   fp16 K: dims 16 (u % 16) .. + 15 of cell u / 16 (32 bytes, two loads)
-//   fp16 V: 32 consecutive bytes of half u / 256 of the tile: chunks 2i and
-//           2i + 1 (i = u % 256) of its 8 KB block, each 4 cells x 2 dims
+//   q4_0 V: bytes 4 (i / 64) .. + 3 of block (i / 8) % 8 of cells 2 j and
+//           2 j + 1 of the half, j = i % 8, and the two blocks' scales
+//   INT8 V: codes of dims 8 ((i / 8) % 32) .. + 7 of the same two cells, and
+//           the two cells' scales of that 128-dim group
+//   fp16 K: dims 16 (i % 16) .. + 15 of cell 16 (u / 256) + i / 16
+//   fp16 V: 32 consecutive bytes of the half: chunks 2i and 2i + 1 of its
+//           8 KB block, each 4 cells x 2 dims
+//   K scales (the first unit only): slot tid % 64, that is cell (tid % 64) / 2,
+//           group tid % 2 (waves 1 .. 3 repeat wave 0's loads)
 // The loads are unconditional (every address lies in the pool: a half past
-// the visible cells reads page 0, a cell past them lies in its half's page);
-// the values of cells past the visible ones are zeroed when stored, so the
-// loads can be issued a tile ahead and consumed a tile later.
+// the visible cells reads the last visible half again, a cell past them lies
+// in its half's page); the values of cells past the visible ones are zeroed
+// when stored, so the loads can be issued a tile ahead and consumed a tile
+// later.
 struct PfRaw {
   u32x4 k;          // INT8 K: 16 codes; q4_0 K: .x .y nibble bytes, .z scale; fp16 K: dims 0 .. 7
   u32x4 k2;         // fp16 K: dims 8 .. 15 of the unit
@@ -135,57 +140,63 @@ __device__ __forceinline__ PfHalves pf_halves(const PrefillArgs &a, int g, int c
   return h;
 }
 
-template <int FMT, bool SCALE>
-__device__ __forceinline__ void pf_load(const PrefillArgs &a, const PfHalves &hv, int u, PfRaw &r) {
+template <int FMT, int HF, bool SCALE>
+__device__ __forceinline__ void pf_load(const PrefillArgs &a, const PfHalves &hv, int tid, PfRaw &r) {
+  const int i = tid;  // unit u = tid + 256 HF
+  const size_t cell0 = (size_t)hv.tile[HF] * a.P + hv.slot0[HF];  // first cell of the half, pool order
   if (FMT == KV_FMT_F16) {
     // fp16 blocks: 8 KB per 16 cells in each of K and V, the layout the
     // decode kernel loads as MFMA operands
-    const int cl = u >> 4, hf = cl >> 4, m = u & 15;
-    const uint8_t *kb = a.run[0] + hv.cell(hf) * 512 + (m >> 1) * 1024 + (m & 1) * 512 + (cl & 15) * 16;
-    r.k = *reinterpret_cast<const u32x4 *>(kb);
-    r.k2 = *reinterpret_cast<const u32x4 *>(kb + 256);
-    const uint8_t *vb = a.run[2] + hv.cell(u >> 8) * 512 + 32 * (u & 255);
-    r.v16[0] = *reinterpret_cast<const u32x4 *>(vb);
-    r.v16[1] = *reinterpret_cast<const u32x4 *>(vb + 16);
+    const int m = i & 15;
+    const uint8_t *kb = a.run[0] + cell0 * 512;
+    const uint32_t ko = (uint32_t)((m >> 1) * 1024 + (m & 1) * 512 + ((i >> 4) & 15) * 16);
+    r.k = *reinterpret_cast<const u32x4 *>(kb + ko);
+    r.k2 = *reinterpret_cast<const u32x4 *>(kb + ko + 256);
+    const uint8_t *vb = a.run[2] + cell0 * 512;
+    r.v16[0] = *reinterpret_cast<const u32x4 *>(vb + 32u * (uint32_t)i);
+    r.v16[1] = *reinterpret_cast<const u32x4 *>(vb + 32u * (uint32_t)i + 16u);
     return;
   }
+  const uint8_t *tile_base = a.run[0] + (size_t)hv.tile[HF] * 144 * a.P;  // q4_0 K tile of the half
   if (FMT != KV_FMT_Q4_0) {
     // K-code run: 4 KB per 16 cells, [dim quarter][cell % 16][64 codes];
     // a wave's 64 units read four 256-byte stretches
-    const int cl = u >> 4, hf = cl >> 4, m = u & 15;
-    r.k = *reinterpret_cast<const u32x4 *>(a.run[0] + hv.cell(hf) * 256 + (m >> 2) * 1024 + (cl & 15) * 64 +
-                                           16 * (m & 3));
-    if (SCALE) {  // scale slot u % 64: cell (u % 64) / 2, group u % 2
-      const int cs = (u & 63) >> 1;
-      r.ks = reinterpret_cast<const float *>(a.run[1])[(hv.cell(cs >> 4) + (cs & 15)) * 2 + (u & 1)];
-    }
+    const int m = i & 15;
+    const uint32_t ko = (uint32_t)((m >> 2) * 1024 + ((i >> 4) & 15) * 64 + 16 * (m & 3));
+    r.k = *reinterpret_cast<const u32x4 *>(a.run[0] + cell0 * 256 + ko);
   } else {
-    const int cl = u >> 4, hf = cl >> 4, b = (u & 15) >> 1, hh = u & 1;
-    const uint8_t *kt = a.run[0] + (size_t)hv.tile_of(hf) * 144 * a.P;
-    const int slot = hv.slot_of(hf) + (cl & 15);
-    const u32x2 w = *reinterpret_cast<const u32x2 *>(kt + (size_t)slot * 128 + 16 * b + 8 * hh);
+    const int b = (i & 15) >> 1, hh = i & 1, c = (i >> 4) & 15;
+    const uint8_t *kt = tile_base + (size_t)hv.slot0[HF] * 128;
+    const u32x2 w = *reinterpret_cast<const u32x2 *>(kt + (uint32_t)(c * 128 + 16 * b + 8 * hh));
     r.k.x = w.x;
     r.k.y = w.y;
-    r.k.z = *reinterpret_cast<const uint16_t *>(kt + q4_scale_off(a.P, slot, b));
+    r.k.z = *reinterpret_cast<const uint16_t *>(tile_base + q4_scale_off(a.P, hv.slot0[HF], 0) +
+                                                (uint32_t)(b * 32 + c * 2));
   }
-  const int cp = u & 15;
-  const int hf = cp >> 3;  // cells 2cp, 2cp+1 lie in half cp / 8
-  const int slot = hv.slot_of(hf) + 2 * (cp & 7);
+  if (SCALE) {  // scale slot tid % 64 of the tile: both halves, selected per lane
+    const int cs = (tid & 63) >> 1;
+    const size_t c0 = (size_t)hv.tile[0] * a.P + hv.slot0[0], c1 = (size_t)hv.tile[1] * a.P + hv.slot0[1];
+    const float *ks = reinterpret_cast<const float *>(a.run[1]) + (cs >> 4 ? c1 : c0) * 2;
+    r.ks = ks[(cs & 15) * 2 + (tid & 1)];
+  }
+  const int j = i & 7;  // cells 2 j, 2 j + 1 of the half
   if (FMT != KV_FMT_INT8) {
-    const int b = (u >> 4) & 7, qq = u >> 7;
-    const uint8_t *vt = a.run[2] + (size_t)hv.tile_of(hf) * 144 * a.P;
-    // slot is even, so the two cells' block-b scales are one aligned word
-    r.va.x = *reinterpret_cast<const uint32_t *>(vt + (size_t)slot * 128 + 16 * b + 4 * qq);
-    r.vb.x = *reinterpret_cast<const uint32_t *>(vt + (size_t)(slot + 1) * 128 + 16 * b + 4 * qq);
-    r.vd = *reinterpret_cast<const uint32_t *>(vt + q4_scale_off(a.P, slot, b));
+    const int b = (i >> 3) & 7, qq = i >> 6;
+    const uint8_t *vt = a.run[2] + (size_t)hv.tile[HF] * 144 * a.P;
+    const uint8_t *vs = vt + (size_t)hv.slot0[HF] * 128;
+    const uint32_t vo = (uint32_t)(2 * j * 128 + 16 * b + 4 * qq);
+    r.va.x = *reinterpret_cast<const uint32_t *>(vs + vo);
+    r.vb.x = *reinterpret_cast<const uint32_t *>(vs + vo + 128);
+    // the two cells' block-b scales are one aligned word
+    r.vd = *reinterpret_cast<const uint32_t *>(vt + q4_scale_off(a.P, hv.slot0[HF], 0) + (uint32_t)(b * 32 + 4 * j));
   } else {
-    const int dg = u >> 4;  // dims 8 dg .. 8 dg + 7, scale group dg / 16
-    const size_t ca = (size_t)hv.tile_of(hf) * a.P + slot;
-    const float *vs = reinterpret_cast<const float *>(a.run[3]);
-    r.va = *reinterpret_cast<const u32x2 *>(a.run[2] + ca * 256 + 8 * dg);
-    r.vb = *reinterpret_cast<const u32x2 *>(a.run[2] + (ca + 1) * 256 + 8 * dg);
-    r.vsa = vs[ca * 2 + (dg >> 4)];
-    r.vsb = vs[(ca + 1) * 2 + (dg >> 4)];
+    const int dg = (i >> 3) & 31;  // dims 8 dg .. 8 dg + 7, scale group dg / 16
+    const uint8_t *vc = a.run[2] + cell0 * 256;
+    const float *vsc = reinterpret_cast<const float *>(a.run[3]) + cell0 * 2;
+    r.va = *reinterpret_cast<const u32x2 *>(vc + (uint32_t)(2 * j * 256 + 8 * dg));
+    r.vb = *reinterpret_cast<const u32x2 *>(vc + (uint32_t)((2 * j + 1) * 256 + 8 * dg));
+    r.vsa = vsc[(2 * j) * 2 + (dg >> 4)];
+    r.vsb = vsc[(2 * j + 1) * 2 + (dg >> 4)];
   }
 }
 
@@ -208,14 +219,15 @@ __device__ __forceinline__ void q4_word_to_f16(uint32_t w, f16x2 d, uint32_t lo[
 // scale slots of a half whose page-table entry is out of range hold NaN, so
 // every row whose causal window reaches that half returns NaN (rows that stop
 // before it mask those cells to -inf).
-template <int FMT, bool SCALE>
-__device__ __forceinline__ void pf_store(const PfRaw &r, int u, int c0, int n_cells, int bad, float scale2,
+template <int FMT, int HF, bool SCALE>
+__device__ __forceinline__ void pf_store(const PfRaw &r, int tid, int c0, int n_cells, int bad, float scale2,
                                          _Float16 *lk, _Float16 *lv, float *lks) {
-  if (SCALE) {  // slots u >= 64 are written and never read (no branch)
-    const int cs = (u & 63) >> 1;
+  const int u = tid + 256 * HF, i = tid;
+  if (SCALE) {  // slots tid >= 64 are written and never read (no branch)
+    const int cs = (tid & 63) >> 1;
     const float sc = FMT == KV_FMT_INT8 || FMT == KV_FMT_K8V4 ? scale2 * r.ks : scale2;
     const float kd = ((bad >> (cs >> 4)) & 1) ? __builtin_nanf("") : sc;
-    lks[u] = c0 + cs < n_cells ? kd : 0.f;
+    lks[tid] = c0 + cs < n_cells ? kd : 0.f;
   }
   const int cl = u >> 4;
   const bool k_ok = c0 + cl < n_cells;
@@ -267,7 +279,7 @@ __device__ __forceinline__ void pf_store(const PfRaw &r, int u, int c0, int n_ce
     *reinterpret_cast<u32x4 *>(kd) = u32x4{lo[0], lo[1], lo[2], lo[3]};
     *reinterpret_cast<u32x4 *>(kd + 16) = u32x4{hi[0], hi[1], hi[2], hi[3]};
   }
-  const int cp = u & 15;
+  const int cp = 8 * HF + (i & 7);  // cells 2 cp, 2 cp + 1 of the tile
   const bool ok_a = c0 + 2 * cp < n_cells, ok_b = c0 + 2 * cp + 1 < n_cells;
   if (FMT != KV_FMT_INT8) {
     // q4_0 V -> (code - 8) * d16, transposed [dim][cell]; byte i of the block
@@ -275,7 +287,7 @@ __device__ __forceinline__ void pf_store(const PfRaw &r, int u, int c0, int n_ce
     // past the visible ones gets scale 0 (its slot may hold any bits)
     const f16x2 c1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
     const f16x2 c72 = {(_Float16)72.0f, (_Float16)72.0f};
-    const int b = (u >> 4) & 7, qq = u >> 7;
+    const int b = (i >> 3) & 7, qq = i >> 6;
     const f16x2 dd = as_f16x2(r.vd & ((ok_a ? 0x0000FFFFu : 0u) | (ok_b ? 0xFFFF0000u : 0u)));
     _Float16 *vb = lv + v_row(32 * b + 4 * qq) + v_pos(2 * cp);  // element 4qq of block b
     for (int e = 0; e < 4; e++) {
@@ -290,7 +302,7 @@ __device__ __forceinline__ void pf_store(const PfRaw &r, int u, int c0, int n_ce
     }
   } else {
     // INT8 V -> code * d rounded to fp16, transposed [dim][cell]
-    const int dg = u >> 4;
+    const int dg = (i >> 3) & 31;
     const float sa = ok_a ? r.vsa : 0.f, sb = ok_b ? r.vsb : 0.f;
     _Float16 *vb = lv + v_row(8 * dg) + v_pos(2 * cp);
     const uint32_t wa[2] = {r.va.x, r.va.y}, wb[2] = {r.vb.x, r.vb.y};
@@ -323,8 +335,8 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
   constexpr bool kRotV = FMT == KV_FMT_Q4_0 || FMT == KV_FMT_K8V4;
   constexpr int kKElems = kPfTile * kKRow, kVElems = 256 * kVRow + 8 * kVBlockPad;
   constexpr int kBufElems = kKElems + kVElems;
-  __shared__ __attribute__((aligned(16))) _Float16 lds_kv[2 * kBufElems];
-  __shared__ __attribute__((aligned(16))) float lds_ks[2 * kPfWaves * 64];  // [buffer][unit]; units < 64 used
+  __shared__ __attribute__((aligned(16))) _Float16 lds_kv[3 * kBufElems];
+  __shared__ __attribute__((aligned(16))) float lds_ks[3 * kPfWaves * 64];  // [buffer][unit]; units < 64 used
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -403,46 +415,28 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
   for (int jd = 0; jd < 8; jd++)
     for (int e = 0; e < 16; e++) o[jd][e] = 0.f;
 
+  auto kbuf = [&](int b) { return lds_kv + b * kBufElems; };
+  auto sbuf = [&](int b) { return lds_ks + b * kPfWaves * 64; };
+
   PfRaw raw[2];
   int raw_bad = 0;
   // the page-table entries of a tile are read one step before its raw loads
   // (a scalar load waits for every LDS read in flight)
   auto load_tile = [&](const PfHalves &hv) {
     raw_bad = hv.bad;
-    pf_load<FMT, true>(a, hv, tid, raw[0]);
-    pf_load<FMT, false>(a, hv, tid + 256, raw[1]);
+    pf_load<FMT, 0, true>(a, hv, tid, raw[0]);
+    pf_load<FMT, 1, false>(a, hv, tid, raw[1]);
   };
-  auto store_tile = [&](int buf, int c) {
-    _Float16 *lk = lds_kv + buf * kBufElems;
-    float *ks = lds_ks + buf * kPfWaves * 64;
-    pf_store<FMT, true>(raw[0], tid, c, n_cells, raw_bad, a.scale2, lk, lk + kKElems, ks);
-    pf_store<FMT, false>(raw[1], tid + 256, c, n_cells, raw_bad, a.scale2, lk, lk + kKElems, ks);
+  auto store_tile = [&](int b, int c) {
+    _Float16 *lk = kbuf(b);
+    pf_store<FMT, 0, true>(raw[0], tid, c, n_cells, raw_bad, a.scale2, lk, lk + kKElems, sbuf(b));
+    pf_store<FMT, 1, false>(raw[1], tid, c, n_cells, raw_bad, a.scale2, lk, lk + kKElems, sbuf(b));
   };
-
-  PfHalves hv_next;
-  // One tile: S^T = K.Q^T, the next tile's dequantization and the raw loads
-  // of the one after interleaved with its MFMAs; online softmax; O += P.V.
-  // This lane's scores are row col, cells 8 (e / 4) + 4 h + e % 4 (element e
-  // of the 32 x 32 accumulator).
-  auto step = [&](int c0, int buf, auto mtag) {
-    constexpr bool MASKED = decltype(mtag)::value;
-    const _Float16 *lk = lds_kv + buf * kBufElems;
-    const _Float16 *lv = lk + kKElems;
-    const float *lks = lds_ks + buf * kPfWaves * 64;
-    f16x8 kop[16], vop[8][2];
-    const _Float16 *kr = lk + col * kKRow + 8 * h;
+  // S^T = K.Q^T of the tile in buffer b: 16 (fp32 queries: 32) MFMAs
+  auto qk = [&](int b, f32x16 (&acc)[NG]) {
+    const _Float16 *kr = kbuf(b) + col * kKRow + 8 * h;
+    f16x8 kop[16];
     for (int kk = 0; kk < 16; kk++) kop[kk] = *reinterpret_cast<const f16x8 *>(kr + 16 * kk);
-    for (int jd = 0; jd < 8; jd++) {
-      const _Float16 *vr = lv + v_row(32 * jd + col) + 8 * h;
-      for (int st = 0; st < 2; st++) vop[jd][st] = *reinterpret_cast<const f16x8 *>(vr + 16 * st);
-    }
-    // scales of this lane's cells 8 j + 4 h .. + 3: [cell][group] pairs
-    f32x4 dks[8];
-    for (int j = 0; j < 4; j++) {
-      dks[2 * j] = *reinterpret_cast<const f32x4 *>(&lks[(8 * j + 4 * h) * 2]);
-      dks[2 * j + 1] = *reinterpret_cast<const f32x4 *>(&lks[(8 * j + 4 * h) * 2 + 4]);
-    }
-    f32x16 acc[NG];
     for (int gg = 0; gg < NG; gg++)
       for (int e = 0; e < 16; e++) acc[gg][e] = 0.f;
     for (int kk = 0; kk < 16; kk++) {
@@ -450,28 +444,42 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
       acc[gg] = mfma32(kop[kk], qop[kk], acc[gg]);
       if (QF32) acc[gg] = mfma32(kop[kk], qlo[kk], acc[gg]);
     }
-    store_tile(buf ^ 1, c0 + kPfTile);
-    load_tile(hv_next);
-    for (int kk = 0; kk < (QF32 ? 32 : 16); kk++) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+  };
+
+  // One step of the pipeline, for the tile at c0 held in buffer b0 (the
+  // next two tiles in b1 and b2), whose scores are in `cur`:
+  //   phase A: the MFMAs of the next tile's scores (into `nxt`) run while the
+  //            VALU does this tile's online softmax;
+  //   phase B: this tile's P.V MFMAs run while the VALU dequantizes the tile
+  //            after next (raw registers -> buffer b2) and the raw pages of
+  //            the one after that are loaded.
+  // This lane's scores are row col, cells 8 (e / 4) + 4 h + e % 4 (element e
+  // of the 32 x 32 accumulator).
+  PfHalves hv_next;
+  auto step = [&](int c0, int b0, int b1, int b2, f32x16 (&cur)[NG], f32x16 (&nxt)[NG], auto mtag) {
+    constexpr bool MASKED = decltype(mtag)::value;
+    // ---------------- scores and the reference max (this tile's scores are
+    // already in registers), the rare O rescale, then phase A
+    const float *lks = sbuf(b0);
+    f32x4 dks[8];  // scales of this lane's cells 8 j + 4 h .. + 3: [cell][group] pairs
+    for (int j = 0; j < 4; j++) {
+      dks[2 * j] = *reinterpret_cast<const f32x4 *>(&lks[(8 * j + 4 * h) * 2]);
+      dks[2 * j + 1] = *reinterpret_cast<const f32x4 *>(&lks[(8 * j + 4 * h) * 2 + 4]);
     }
-    // ---------------- online softmax: the row's 32 cells are in lanes col
-    // and col + 32; the reference max moves only when a row's max exceeds it
-    // by more than 2^kPfLazy
     float s[16];
     for (int e = 0; e < 16; e++) {
       const f32x4 d2 = dks[2 * (e >> 2) + ((e & 3) >> 1)];
       const float k0 = d2[2 * (e & 1)], k1 = d2[2 * (e & 1) + 1];
-      float sv = NG == 2 ? k0 * acc[0][e] + k1 * acc[1][e] : k0 * acc[0][e];
+      float sv = NG == 2 ? k0 * cur[0][e] + k1 * cur[1][e] : k0 * cur[0][e];
       if (MASKED) {
         const int cell = c0 + 8 * (e >> 2) + 4 * h + (e & 3);
         sv = (qvalid && cell <= qpos) ? sv : -INFINITY;
       }
       s[e] = sv;
     }
+    // online softmax: the row's 32 cells are in lanes col and col + 32; the
+    // reference max moves (for every row, to at least its max) only when
+    // some row's max exceeds it by more than 2^kPfLazy
     float mx = s[0];
     for (int e = 1; e < 16; e++) mx = fmaxf(mx, s[e]);
     mx = fmaxf(mx, lane_xor<32>(mx));
@@ -487,6 +495,9 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
         for (int jd = 0; jd < 8; jd++) o[jd][e] *= al;
       }
     }
+    // ---------------- phase A: the next tile's scores on the MFMAs, this
+    // tile's probabilities on the VALU
+    qk(b1, nxt);
     f16x8 pop[2];
     float ps = 0.f;
     for (int e = 0; e < 16; e++) {
@@ -495,30 +506,62 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
       pop[e >> 3][e & 7] = (_Float16)p;
     }
     lsum += ps;
-    // ---------------- O += P . V; B for dim tile jd, k-step st: dim 32 jd +
-    // col, the lane half's 8 cells of the step (v_pos)
+    for (int kk = 0; kk < (QF32 ? 32 : 16); kk++) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 3, 0);
+    }
+    // ---------------- phase B: O += P . V; B for dim tile jd, k-step st:
+    // dim 32 jd + col, the lane half's 8 cells of the step (v_pos)
+    f16x8 vop[8][2];
+    const _Float16 *lv = kbuf(b0) + kKElems;
+    for (int jd = 0; jd < 8; jd++) {
+      const _Float16 *vr = lv + v_row(32 * jd + col) + 8 * h;
+      for (int st = 0; st < 2; st++) vop[jd][st] = *reinterpret_cast<const f16x8 *>(vr + 16 * st);
+    }
     for (int jd = 0; jd < 8; jd++)
       for (int st = 0; st < 2; st++) o[jd] = mfma32(pop[st], vop[jd][st], o[jd]);
-    hv_next = pf_halves(a, g, c0 + 3 * kPfTile, n_cells);
+    store_tile(b2, c0 + 2 * kPfTile);
+    load_tile(hv_next);
+    for (int kk = 0; kk < 16; kk++) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+    }
+    hv_next = pf_halves(a, g, c0 + 4 * kPfTile, n_cells);
+    __syncthreads();
   };
 
-  // Tile i + 1 is dequantized into buffer (i + 1) % 2 and the raw pages of
-  // tile i + 2 are loaded while tile i is computed from buffer i % 2.  Tiles
-  // that every row of the block sees whole skip the causal mask.
+  // Prologue: tiles 0 and 1 dequantized, tile 2's raw pages loaded, tile 0's
+  // scores computed.  Tiles that every row of the block sees whole skip the
+  // causal mask; both loops take tiles in pairs (the score registers swap
+  // roles), the masked one past the visible cells if need be (such a tile is
+  // masked out whole and its values are zero).
   load_tile(pf_halves(a, g, 0, n_cells));
   store_tile(0, 0);
   load_tile(pf_halves(a, g, kPfTile, n_cells));
-  hv_next = pf_halves(a, g, 2 * kPfTile, n_cells);
+  store_tile(1, kPfTile);
+  load_tile(pf_halves(a, g, 2 * kPfTile, n_cells));
+  hv_next = pf_halves(a, g, 3 * kPfTile, n_cells);
   __syncthreads();
-  const int full_end = a.pos0 + qb0 + 1;  // cells [0, full_end) are visible to every row
-  int c0 = 0, buf = 0;
-  for (; c0 + kPfTile <= full_end; c0 += kPfTile, buf ^= 1) {
-    step(c0, buf, std::false_type{});
-    __syncthreads();
+  f32x16 sa[NG], sb[NG];
+  qk(0, sa);
+  const int n_tiles = (n_cells + kPfTile - 1) / kPfTile;
+  const int n_full = ((a.pos0 + qb0 + 1) / kPfTile) & ~1;  // tiles every row sees whole, even
+  const int n_end = n_full + ((n_tiles - n_full + 1) & ~1);
+  int t = 0, b0 = 0;
+  auto nb = [](int b) { return b == 2 ? 0 : b + 1; };
+  for (; t < n_full; t += 2) {
+    step(t * kPfTile, b0, nb(b0), nb(nb(b0)), sa, sb, std::false_type{});
+    b0 = nb(b0);
+    step((t + 1) * kPfTile, b0, nb(b0), nb(nb(b0)), sb, sa, std::false_type{});
+    b0 = nb(b0);
   }
-  for (; c0 < n_cells; c0 += kPfTile, buf ^= 1) {
-    step(c0, buf, std::true_type{});
-    __syncthreads();
+  for (; t < n_end; t += 2) {
+    step(t * kPfTile, b0, nb(b0), nb(nb(b0)), sa, sb, std::true_type{});
+    b0 = nb(b0);
+    step((t + 1) * kPfTile, b0, nb(b0), nb(nb(b0)), sb, sa, std::true_type{});
+    b0 = nb(b0);
   }
 
   // ---------------- epilogue: O / l; the lane holds dim 32 jd + col of rows
