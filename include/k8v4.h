@@ -341,14 +341,28 @@ int attn_verify(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dty
  * prefill).  Dense contractions on the matrix cores (fp16 inputs, fp32
  * accumulation).
  *   q:   device, [n_new][n_q_heads][256];  out: device fp32 [n_new][n_q_heads][256]
- * Needs no workspace (ws may be NULL).  Any of the four formats, with the
- * same rules as attn_decode (q4_0 scores the rotated query against rotated
- * keys; int8 and fp16 return softmax(.) V unrotated).
- * Errors: KV_ERR_NULL, _UNSUPPORTED, _DTYPE, _RANGE.
+ *   ws:  device, attn_prefill_workspace_bytes(pool, pos0 + n_new) bytes,
+ *        16-byte aligned; overwritten by the call (no initialisation needed;
+ *        calls that share it must be ordered).  Two kernels run: the first
+ *        dequantizes every 32-cell tile of each KV head once into ws, the
+ *        second computes the attention from there.  An armed timing pair
+ *        (kv_time_next_launch) brackets both.
+ * Any of the four formats, with the same rules as attn_decode (q4_0 scores
+ * the rotated query against rotated keys; int8 and fp16 return
+ * softmax(.) V unrotated).  A page-table entry outside [0, n_pages) makes
+ * the rows whose window reaches its cells NaN (the reads stay in the pool).
+ * Errors: KV_ERR_NULL, _UNSUPPORTED, _DTYPE, _RANGE, _ALIGN, _WORKSPACE
+ * (ws NULL or smaller than attn_prefill_workspace_bytes).
  */
 int attn_prefill_chunk(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
                        int n_q_heads, int32_t pos0, int32_t n_new, float scale, float *out,
                        void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes of attn_prefill_chunk over n_cells = pos0 + n_new cells:
+ * n_kv_heads * ceil(n_cells / 32) tile images of 37,888 bytes (fp16 K and
+ * transposed V of 32 cells with their row padding, and 64 fp32 K scales).
+ * 0 for a NULL pool or n_cells < 1. */
+size_t attn_prefill_workspace_bytes(const kv_pool *pool, int32_t n_cells);
 
 /*
  * A streamed cache ("kv: --kv k8v4 streams with --kv-resident", What and

@@ -61,6 +61,7 @@ SIGNATURES = {
     "attn_decode_batch": (_I, [_PP, _PS, C.c_int32, _P, _I, _I, _P, _F, _P, _P, _SZ, _P]),
     "attn_verify": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, _P, _F, _P, _P, _SZ, _P]),
     "attn_prefill_chunk": (_I, [_PP, _PS, _P, _I, _I, C.c_int32, C.c_int32, _F, _P, _P, _SZ, _P]),
+    "attn_prefill_workspace_bytes": (_SZ, [_PP, C.c_int32]),
     "kv_check_page_table": (_I, [_PP, _PS, C.c_int32, _P]),
     "kv_stream_append": (_I, [_PST, _P, _P, _I, C.c_int32, C.c_int32, _P]),
     "kv_stream_fetch": (_I, [_PST, C.c_int32, C.c_int32, _P]),
@@ -490,19 +491,33 @@ def attn_verify(pool: KvPool, page_table, q, n_visible, ws, scale: float = 0.0, 
     return out
 
 
-def attn_prefill_chunk(pool: K8V4Pool, page_table, q, pos0: int, scale: float = 0.0, out=None,
-                       stream=None):
-    """q: [n_new][Hq][256] at positions [pos0, pos0+n_new); row i attends [0, pos0+i]."""
+def attn_prefill_workspace(pool: KvPool, n_cells: int):
+    """Allocate the workspace of attn_prefill_chunk over n_cells = pos0 + n_new
+    cells (no initialisation needed)."""
+    torch = _torch()
+    nb = int(lib().attn_prefill_workspace_bytes(C.byref(pool.struct), int(n_cells)))
+    if nb == 0:
+        raise ValueError("bad workspace request")
+    return torch.empty(nb, dtype=torch.uint8, device=pool.runs[0].device)
+
+
+def attn_prefill_chunk(pool: KvPool, page_table, q, pos0: int, scale: float = 0.0, out=None,
+                       ws=None, stream=None):
+    """q: [n_new][Hq][256] at positions [pos0, pos0+n_new); row i attends [0, pos0+i].
+    ws: attn_prefill_workspace(pool, pos0 + n_new), allocated here when None."""
     torch = _torch()
     if q.dim() != 3 or q.shape[2] != HEAD_DIM:
         raise ValueError("q must be [n_new][n_q_heads][256]")
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if ws is None and q.shape[0] > 0:
+        ws = attn_prefill_workspace(pool, int(pos0) + int(q.shape[0]))
     seq = _seq(page_table)
     rc = lib().attn_prefill_chunk(C.byref(pool.struct), C.byref(seq), _dev_ptr(q, "q"),
                                   _dtype_code(q), int(q.shape[1]), int(pos0), int(q.shape[0]),
-                                  float(scale), _dev_ptr(out, "out", (torch.float32,)), None, 0,
-                                  _stream(stream))
+                                  float(scale), _dev_ptr(out, "out", (torch.float32,)),
+                                  None if ws is None else _dev_ptr(ws, "ws"),
+                                  0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "attn_prefill_chunk")
     return out
 

@@ -368,14 +368,19 @@ int attn_prefill_chunk(const kv_pool *pool, const kv_seq *seq, const void *q, in
                        int n_q_heads, int32_t pos0, int32_t n_new, float scale, float *out,
                        void *ws, size_t ws_bytes, void *stream) {
   CallScope scope;
-  (void)ws;
-  (void)ws_bytes;
   if (int e = check_attn_common(pool, seq, q, q_dtype, n_q_heads, out, 0)) return e;
   if (pos0 < 0 || n_new < 0) return KV_ERR_RANGE;
   if (int e = check_range(pool, seq, 0, (int64_t)pos0 + n_new)) return e;
   if (n_new == 0) return KV_OK;
-  return launch_attn_prefill(pool, seq, q, q_dtype, n_q_heads, pos0, n_new, pick_scale(scale), out,
+  if (!ws || ws_bytes < prefill_workspace_bytes(pool, (int64_t)pos0 + n_new)) return KV_ERR_WORKSPACE;
+  if (int e = check_aligned16(ws)) return e;
+  return launch_attn_prefill(pool, seq, q, q_dtype, n_q_heads, pos0, n_new, pick_scale(scale), out, ws,
                              (hipStream_t)stream);
+}
+
+size_t attn_prefill_workspace_bytes(const kv_pool *pool, int32_t n_cells) {
+  if (!pool || pool->n_kv_heads <= 0 || n_cells <= 0) return 0;
+  return prefill_workspace_bytes(pool, n_cells);
 }
 
 int kv_check_page_table(const kv_pool *pool, const kv_seq *seq, int32_t n_cells, int32_t *n_bad) {

@@ -54,6 +54,14 @@ __device__ __forceinline__ int v_row(int d) { return d * kVRow + (d >> 5) * kVBl
 // + b (bits 2 and 3 of c swapped), so one 16-byte read fetches them
 __device__ __forceinline__ int v_pos(int c) { return (c & 19) | ((c & 4) << 1) | ((c & 8) >> 1); }
 
+// A staged tile: K [32 cells][kKRow] fp16, V [256 dims][v_pos] fp16 with a
+// pad after every 32 dims, then the 64 K scales [cell][group] -- the LDS
+// image the attention kernel computes from, copied there unchanged.
+constexpr int kKElems = kPfTile * kKRow, kVElems = 256 * kVRow + 8 * kVBlockPad;
+constexpr int kImgKV = 2 * (kKElems + kVElems);     // bytes of K and V
+constexpr int kPfImageBytes = kImgKV + 2 * kPfTile * 4;
+static_assert(kPfImageBytes % 1024 == 0, "whole 1 KB copy units");
+
 struct PrefillArgs {
   const uint8_t *run[4];  // the pool's runs (format-dependent, as the header lays them out)
   const int32_t *pt;
@@ -63,6 +71,8 @@ struct PrefillArgs {
   int n_q_heads;
   int pos0, n_new;
   float scale2;           // softmax scale * log2(e)
+  uint8_t *img;           // tile images [kv head][tile][kPfImageBytes] (the workspace)
+  int n_tiles;            // tiles staged per KV head: ceil((pos0 + n_new) / 32)
 };
 
 // (x & m) | c in one VALU op (the compiler splits it when both are literals)
@@ -213,22 +223,12 @@ __device__ __forceinline__ void q4_word_to_f16(uint32_t w, f16x2 d, uint32_t lo[
   }
 }
 
-// Dequantize work unit u of the tile at c0 into the LDS tile buffer (K
-// [cell][dim], V [dim][v_pos(cell)], K scales [cell][group] times softmax
-// scale x log2 e).  Cells at or past n_cells store zero K, V and scale; the
-// scale slots of a half whose page-table entry is out of range hold NaN, so
-// every row whose causal window reaches that half returns NaN (rows that stop
-// before it mask those cells to -inf).
-template <int FMT, int HF, bool SCALE>
-__device__ __forceinline__ void pf_store(const PfRaw &r, int tid, int c0, int n_cells, int bad, float scale2,
-                                         _Float16 *lk, _Float16 *lv, float *lks) {
+// Dequantize work unit u of the tile at c0 into its tile image (K
+// [cell][dim], V [dim][v_pos(cell)]).  Cells at or past n_cells store zero
+// K and V.
+template <int FMT, int HF>
+__device__ __forceinline__ void pf_store(const PfRaw &r, int tid, int c0, int n_cells, _Float16 *lk, _Float16 *lv) {
   const int u = tid + 256 * HF, i = tid;
-  if (SCALE) {  // slots tid >= 64 are written and never read (no branch)
-    const int cs = (tid & 63) >> 1;
-    const float sc = FMT == KV_FMT_INT8 || FMT == KV_FMT_K8V4 ? scale2 * r.ks : scale2;
-    const float kd = ((bad >> (cs >> 4)) & 1) ? __builtin_nanf("") : sc;
-    lks[tid] = c0 + cs < n_cells ? kd : 0.f;
-  }
   const int cl = u >> 4;
   const bool k_ok = c0 + cl < n_cells;
   if (FMT == KV_FMT_F16) {
@@ -315,6 +315,17 @@ __device__ __forceinline__ void pf_store(const PfRaw &r, int tid, int c0, int n_
   }
 }
 
+// K scale slot tid (< 64) of the tile at c0: cell tid / 2, group tid % 2,
+// times softmax scale x log2 e; 0 past n_cells, NaN in a half whose
+// page-table entry is out of range
+template <int FMT>
+__device__ __forceinline__ float pf_scale(const PfRaw &r, int tid, int c0, int n_cells, int bad, float scale2) {
+  const int cs = tid >> 1;
+  const float sc = FMT == KV_FMT_INT8 || FMT == KV_FMT_K8V4 ? scale2 * r.ks : scale2;
+  const float kd = ((bad >> (cs >> 4)) & 1) ? __builtin_nanf("") : sc;
+  return c0 + cs < n_cells ? kd : 0.f;
+}
+
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
@@ -326,17 +337,32 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
 __device__ __forceinline__ float lane_at(float x, int src) { return __shfl(x, src, 64); }
 
 // instruction classes of the scheduling-group hints
-constexpr int kSchedMfma = 0x008, kSchedValu = 0x002, kSchedVmemRead = 0x020, kSchedDsWrite = 0x200;
+// Staging: one workgroup per (tile, KV head) loads the tile's raw pages and
+// writes its image (the dequantization every attention workgroup of that
+// head would otherwise repeat).  Cells at or past n_cells = pos0 + n_new
+// are zero.
+template <int FMT>
+__global__ __launch_bounds__(256) void prefill_stage_kernel(const PrefillArgs a) {
+  const int t = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int c0 = t * kPfTile, n_cells = a.pos0 + a.n_new;
+  const PfHalves hv = pf_halves(a, g, c0, n_cells);
+  PfRaw r0, r1;
+  pf_load<FMT, 0, true>(a, hv, tid, r0);
+  pf_load<FMT, 1, false>(a, hv, tid, r1);
+  uint8_t *im = a.img + ((size_t)g * a.n_tiles + t) * kPfImageBytes;
+  _Float16 *lk = reinterpret_cast<_Float16 *>(im), *lv = lk + kKElems;
+  pf_store<FMT, 0>(r0, tid, c0, n_cells, lk, lv);
+  pf_store<FMT, 1>(r1, tid, c0, n_cells, lk, lv);
+  if (tid < 2 * kPfTile)
+    reinterpret_cast<float *>(im + kImgKV)[tid] = pf_scale<FMT>(r0, tid, c0, n_cells, hv.bad, a.scale2);
+}
 
 template <bool QF32, int FMT>
 __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const PrefillArgs a) {
   constexpr int kPos = kPfWaves * 32 / kGqa;          // query positions per workgroup
   constexpr int NG = (FMT == KV_FMT_INT8 || FMT == KV_FMT_K8V4) ? 2 : 1;  // K scale groups
   constexpr bool kRotV = FMT == KV_FMT_Q4_0 || FMT == KV_FMT_K8V4;
-  constexpr int kKElems = kPfTile * kKRow, kVElems = 256 * kVRow + 8 * kVBlockPad;
-  constexpr int kBufElems = kKElems + kVElems;
-  __shared__ __attribute__((aligned(16))) _Float16 lds_kv[3 * kBufElems];
-  __shared__ __attribute__((aligned(16))) float lds_ks[3 * kPfWaves * 64];  // [buffer][unit]; units < 64 used
+  __shared__ __attribute__((aligned(16))) uint8_t lds_img[3 * kPfImageBytes];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -415,28 +441,31 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
   for (int jd = 0; jd < 8; jd++)
     for (int e = 0; e < 16; e++) o[jd][e] = 0.f;
 
-  auto kbuf = [&](int b) { return lds_kv + b * kBufElems; };
-  auto sbuf = [&](int b) { return lds_ks + b * kPfWaves * 64; };
-
-  PfRaw raw[2];
-  int raw_bad = 0;
-  // the page-table entries of a tile are read one step before its raw loads
-  // (a scalar load waits for every LDS read in flight)
-  auto load_tile = [&](const PfHalves &hv) {
-    raw_bad = hv.bad;
-    pf_load<FMT, 0, true>(a, hv, tid, raw[0]);
-    pf_load<FMT, 1, false>(a, hv, tid, raw[1]);
+  auto kbuf = [&](int b) { return reinterpret_cast<const _Float16 *>(lds_img + b * kPfImageBytes); };
+  auto sbuf = [&](int b) { return reinterpret_cast<const float *>(lds_img + b * kPfImageBytes + kImgKV); };
+  // Copy tile t's image into buffer b: 1 KB per wave and instruction straight
+  // into LDS (lane l's 16 bytes land at 16 l), no registers.  A tile past the
+  // staged ones (a pair's second tile, masked out whole) copies the last one.
+  const uint8_t *img_head = a.img + (size_t)g * a.n_tiles * kPfImageBytes + wave * 1024 + lane * 16;
+  auto copy_tile = [&](int b, int t) {
+    const uint8_t *src = img_head + (size_t)min(t, a.n_tiles - 1) * kPfImageBytes;
+    uint8_t *dst = lds_img + b * kPfImageBytes + wave * 1024;
+    for (int r = 0; r < (kPfImageBytes / 1024 + kPfWaves - 1) / kPfWaves; r++)
+      if (r * kPfWaves + wave < kPfImageBytes / 1024)  // wave-uniform
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src + r * kPfWaves * 1024),
+                                         (__attribute__((address_space(3))) void *)(dst + r * kPfWaves * 1024),
+                                         16, 0, 0);
   };
-  auto store_tile = [&](int b, int c) {
-    _Float16 *lk = kbuf(b);
-    pf_store<FMT, 0, true>(raw[0], tid, c, n_cells, raw_bad, a.scale2, lk, lk + kKElems, sbuf(b));
-    pf_store<FMT, 1, false>(raw[1], tid, c, n_cells, raw_bad, a.scale2, lk, lk + kKElems, sbuf(b));
-  };
-  // S^T = K.Q^T of the tile in buffer b: 16 (fp32 queries: 32) MFMAs
-  auto qk = [&](int b, f32x16 (&acc)[NG]) {
+  // the copies issued so far have landed (each wave waits for its own; the
+  // barrier that follows makes every wave's visible)
+  auto copies_done = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  // S^T = K.Q^T of the tile in buffer b: its 16 K operands, then 16 (fp32
+  // queries: 32) MFMAs
+  auto k_operands = [&](int b, f16x8 (&kop)[16]) {
     const _Float16 *kr = kbuf(b) + col * kKRow + 8 * h;
-    f16x8 kop[16];
     for (int kk = 0; kk < 16; kk++) kop[kk] = *reinterpret_cast<const f16x8 *>(kr + 16 * kk);
+  };
+  auto qk = [&](const f16x8 (&kop)[16], f32x16 (&acc)[NG]) {
     for (int gg = 0; gg < NG; gg++)
       for (int e = 0; e < 16; e++) acc[gg][e] = 0.f;
     for (int kk = 0; kk < 16; kk++) {
@@ -446,31 +475,37 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
     }
   };
 
-  // One step of the pipeline, for the tile at c0 held in buffer b0 (the
-  // next two tiles in b1 and b2), whose scores are in `cur`:
-  //   phase A: the MFMAs of the next tile's scores (into `nxt`) run while the
-  //            VALU does this tile's online softmax;
-  //   phase B: this tile's P.V MFMAs run while the VALU dequantizes the tile
-  //            after next (raw registers -> buffer b2) and the raw pages of
-  //            the one after that are loaded.
-  // This lane's scores are row col, cells 8 (e / 4) + 4 h + e % 4 (element e
-  // of the 32 x 32 accumulator).
-  PfHalves hv_next;
-  auto step = [&](int c0, int b0, int b1, int b2, f32x16 (&cur)[NG], f32x16 (&nxt)[NG], auto mtag) {
-    constexpr bool MASKED = decltype(mtag)::value;
-    // ---------------- scores and the reference max (this tile's scores are
-    // already in registers), the rare O rescale, then phase A
-    const float *lks = sbuf(b0);
-    f32x4 dks[8];  // scales of this lane's cells 8 j + 4 h .. + 3: [cell][group] pairs
+  // Scores of the tile in buffer b from its accumulators: the per-cell K
+  // scales (times softmax scale x log2 e) of each 128-dim group; this lane's
+  // cells are 8 j + 4 h .. + 3 ([cell][group] pairs in the image)
+  auto scale_scores = [&](int b, const f32x16 (&acc)[NG], float (&sc)[16]) {
+    const float *lks = sbuf(b);
     for (int j = 0; j < 4; j++) {
-      dks[2 * j] = *reinterpret_cast<const f32x4 *>(&lks[(8 * j + 4 * h) * 2]);
-      dks[2 * j + 1] = *reinterpret_cast<const f32x4 *>(&lks[(8 * j + 4 * h) * 2 + 4]);
+      const f32x4 d01 = *reinterpret_cast<const f32x4 *>(&lks[(8 * j + 4 * h) * 2]);
+      const f32x4 d23 = *reinterpret_cast<const f32x4 *>(&lks[(8 * j + 4 * h) * 2 + 4]);
+      for (int i = 0; i < 4; i++) {
+        const f32x4 &d = i < 2 ? d01 : d23;
+        float v = d[2 * (i & 1)] * acc[0][4 * j + i];
+        if constexpr (NG == 2) v += d[2 * (i & 1) + 1] * acc[1][4 * j + i];
+        sc[4 * j + i] = v;
+      }
     }
+  };
+
+  // One step of the pipeline, for tile t (cells c0 = 32 t ..) held in buffer
+  // b0, the next tile in b1, with this tile's scores in `cur`: the copy of
+  // tile t + 2 into b2 is issued; the next tile's scores are computed (into
+  // `nxt`) on the MFMAs while this tile's softmax runs on the VALU; then
+  // O += P.V.  This lane's scores are row col, cells 8 (e / 4) + 4 h + e % 4
+  // (element e of the 32 x 32 accumulator).
+  auto step = [&](int t, int b0, int b1, int b2, const float (&cur)[16], float (&nxt)[16], auto mtag) {
+    constexpr bool MASKED = decltype(mtag)::value;
+    const int c0 = t * kPfTile;
+    copy_tile(b2, t + 2);
+    // ---------------- the reference max and the rare O rescale
     float s[16];
     for (int e = 0; e < 16; e++) {
-      const f32x4 d2 = dks[2 * (e >> 2) + ((e & 3) >> 1)];
-      const float k0 = d2[2 * (e & 1)], k1 = d2[2 * (e & 1) + 1];
-      float sv = NG == 2 ? k0 * cur[0][e] + k1 * cur[1][e] : k0 * cur[0][e];
+      float sv = cur[e];
       if (MASKED) {
         const int cell = c0 + 8 * (e >> 2) + 4 * h + (e & 3);
         sv = (qvalid && cell <= qpos) ? sv : -INFINITY;
@@ -495,9 +530,18 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
         for (int jd = 0; jd < 8; jd++) o[jd][e] *= al;
       }
     }
-    // ---------------- phase A: the next tile's scores on the MFMAs, this
-    // tile's probabilities on the VALU
-    qk(b1, nxt);
+    // ---------------- the next tile's scores on the MFMAs, this tile's
+    // probabilities on the VALU; this tile's P.V operands (B for dim tile jd,
+    // k-step st: dim 32 jd + col, the lane half's 8 cells of the step, v_pos)
+    f16x8 kop[16], vop[8][2];
+    k_operands(b1, kop);
+    const _Float16 *lv = kbuf(b0) + kKElems;
+    for (int jd = 0; jd < 8; jd++) {
+      const _Float16 *vr = lv + v_row(32 * jd + col) + 8 * h;
+      for (int st = 0; st < 2; st++) vop[jd][st] = *reinterpret_cast<const f16x8 *>(vr + 16 * st);
+    }
+    f32x16 acc[NG];
+    qk(kop, acc);
     f16x8 pop[2];
     float ps = 0.f;
     for (int e = 0; e < 16; e++) {
@@ -506,61 +550,44 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
       pop[e >> 3][e & 7] = (_Float16)p;
     }
     lsum += ps;
-    for (int kk = 0; kk < (QF32 ? 32 : 16); kk++) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 3, 0);
-    }
-    // ---------------- phase B: O += P . V; B for dim tile jd, k-step st:
-    // dim 32 jd + col, the lane half's 8 cells of the step (v_pos)
-    f16x8 vop[8][2];
-    const _Float16 *lv = kbuf(b0) + kKElems;
-    for (int jd = 0; jd < 8; jd++) {
-      const _Float16 *vr = lv + v_row(32 * jd + col) + 8 * h;
-      for (int st = 0; st < 2; st++) vop[jd][st] = *reinterpret_cast<const f16x8 *>(vr + 16 * st);
-    }
     for (int jd = 0; jd < 8; jd++)
       for (int st = 0; st < 2; st++) o[jd] = mfma32(pop[st], vop[jd][st], o[jd]);
-    store_tile(b2, c0 + 2 * kPfTile);
-    load_tile(hv_next);
-    for (int kk = 0; kk < 16; kk++) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 5, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-    }
-    hv_next = pf_halves(a, g, c0 + 4 * kPfTile, n_cells);
+    scale_scores(b1, acc, nxt);
+    copies_done();
     __syncthreads();
   };
 
-  // Prologue: tiles 0 and 1 dequantized, tile 2's raw pages loaded, tile 0's
-  // scores computed.  Tiles that every row of the block sees whole skip the
-  // causal mask; both loops take tiles in pairs (the score registers swap
-  // roles), the masked one past the visible cells if need be (such a tile is
-  // masked out whole and its values are zero).
-  load_tile(pf_halves(a, g, 0, n_cells));
-  store_tile(0, 0);
-  load_tile(pf_halves(a, g, kPfTile, n_cells));
-  store_tile(1, kPfTile);
-  load_tile(pf_halves(a, g, 2 * kPfTile, n_cells));
-  hv_next = pf_halves(a, g, 3 * kPfTile, n_cells);
+  // Prologue: tiles 0 and 1 copied, tile 0's scores computed.  Tiles that
+  // every row of the block sees whole skip the causal mask; both loops take
+  // tiles in pairs (the score registers swap roles), the masked one past the
+  // visible cells if need be (such a tile is masked out whole).
+  copy_tile(0, 0);
+  copy_tile(1, 1);
+  copies_done();
   __syncthreads();
-  f32x16 sa[NG], sb[NG];
-  qk(0, sa);
+  float sa[16], sb[16];
+  {
+    f16x8 kop[16];
+    f32x16 acc[NG];
+    k_operands(0, kop);
+    qk(kop, acc);
+    scale_scores(0, acc, sa);
+  }
   const int n_tiles = (n_cells + kPfTile - 1) / kPfTile;
   const int n_full = ((a.pos0 + qb0 + 1) / kPfTile) & ~1;  // tiles every row sees whole, even
   const int n_end = n_full + ((n_tiles - n_full + 1) & ~1);
   int t = 0, b0 = 0;
   auto nb = [](int b) { return b == 2 ? 0 : b + 1; };
   for (; t < n_full; t += 2) {
-    step(t * kPfTile, b0, nb(b0), nb(nb(b0)), sa, sb, std::false_type{});
+    step(t, b0, nb(b0), nb(nb(b0)), sa, sb, std::false_type{});
     b0 = nb(b0);
-    step((t + 1) * kPfTile, b0, nb(b0), nb(nb(b0)), sb, sa, std::false_type{});
+    step(t + 1, b0, nb(b0), nb(nb(b0)), sb, sa, std::false_type{});
     b0 = nb(b0);
   }
   for (; t < n_end; t += 2) {
-    step(t * kPfTile, b0, nb(b0), nb(nb(b0)), sa, sb, std::true_type{});
+    step(t, b0, nb(b0), nb(nb(b0)), sa, sb, std::true_type{});
     b0 = nb(b0);
-    step((t + 1) * kPfTile, b0, nb(b0), nb(nb(b0)), sb, sa, std::true_type{});
+    step(t + 1, b0, nb(b0), nb(nb(b0)), sb, sa, std::true_type{});
     b0 = nb(b0);
   }
 
@@ -603,8 +630,13 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
   }
 }
 
+size_t prefill_workspace_bytes(const kv_pool *pool, int64_t n_cells) {
+  if (n_cells <= 0) return 0;
+  return (size_t)pool->n_kv_heads * (size_t)((n_cells + kPfTile - 1) / kPfTile) * kPfImageBytes;
+}
+
 int launch_attn_prefill(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
-                        int n_q_heads, int pos0, int n_new, float scale, float *out,
+                        int n_q_heads, int pos0, int n_new, float scale, float *out, void *ws,
                         hipStream_t s) {
   PrefillArgs a;
   for (int i = 0; i < 4; i++) a.run[i] = (const uint8_t *)pool->run[i];
@@ -618,18 +650,32 @@ int launch_attn_prefill(const kv_pool *pool, const kv_seq *seq, const void *q, i
   a.pos0 = pos0;
   a.n_new = n_new;
   a.scale2 = scale * 1.4426950408889634f;
+  a.img = (uint8_t *)ws;
+  a.n_tiles = (pos0 + n_new + kPfTile - 1) / kPfTile;
   const bool qf32 = q_dtype == KV_DTYPE_F32;
   const int pos_per_wg = kPfWaves * 32 / kGqa;
-  const dim3 grid((n_new + pos_per_wg - 1) / pos_per_wg, a.H), block(kPfWaves * 64);
+  const dim3 sgrid(a.n_tiles, a.H), grid((n_new + pos_per_wg - 1) / pos_per_wg, a.H), block(kPfWaves * 64);
+  // an armed timing pair brackets both kernels of the call
+  hipEvent_t e0, e1;
+  take_launch_events(&e0, &e1);
+  auto stage = [&](auto kernel) { hipExtLaunchKernelGGL(kernel, sgrid, block, 0, s, e0, nullptr, 0, a); };
+  auto attend = [&](auto kernel) { hipExtLaunchKernelGGL(kernel, grid, block, 0, s, nullptr, e1, 0, a); };
+  switch (pool->fmt) {
+    case KV_FMT_F16: stage(prefill_stage_kernel<KV_FMT_F16>); break;
+    case KV_FMT_INT8: stage(prefill_stage_kernel<KV_FMT_INT8>); break;
+    case KV_FMT_Q4_0: stage(prefill_stage_kernel<KV_FMT_Q4_0>); break;
+    case KV_FMT_K8V4: stage(prefill_stage_kernel<KV_FMT_K8V4>); break;
+    default: return KV_ERR_UNSUPPORTED;
+  }
   switch (pool->fmt * 2 + (qf32 ? 1 : 0)) {
-    case KV_FMT_F16 * 2: launch((attn_prefill_kernel<false, KV_FMT_F16>), grid, block, s, a); break;
-    case KV_FMT_F16 * 2 + 1: launch((attn_prefill_kernel<true, KV_FMT_F16>), grid, block, s, a); break;
-    case KV_FMT_INT8 * 2: launch((attn_prefill_kernel<false, KV_FMT_INT8>), grid, block, s, a); break;
-    case KV_FMT_INT8 * 2 + 1: launch((attn_prefill_kernel<true, KV_FMT_INT8>), grid, block, s, a); break;
-    case KV_FMT_Q4_0 * 2: launch((attn_prefill_kernel<false, KV_FMT_Q4_0>), grid, block, s, a); break;
-    case KV_FMT_Q4_0 * 2 + 1: launch((attn_prefill_kernel<true, KV_FMT_Q4_0>), grid, block, s, a); break;
-    case KV_FMT_K8V4 * 2: launch((attn_prefill_kernel<false, KV_FMT_K8V4>), grid, block, s, a); break;
-    case KV_FMT_K8V4 * 2 + 1: launch((attn_prefill_kernel<true, KV_FMT_K8V4>), grid, block, s, a); break;
+    case KV_FMT_F16 * 2: attend(attn_prefill_kernel<false, KV_FMT_F16>); break;
+    case KV_FMT_F16 * 2 + 1: attend(attn_prefill_kernel<true, KV_FMT_F16>); break;
+    case KV_FMT_INT8 * 2: attend(attn_prefill_kernel<false, KV_FMT_INT8>); break;
+    case KV_FMT_INT8 * 2 + 1: attend(attn_prefill_kernel<true, KV_FMT_INT8>); break;
+    case KV_FMT_Q4_0 * 2: attend(attn_prefill_kernel<false, KV_FMT_Q4_0>); break;
+    case KV_FMT_Q4_0 * 2 + 1: attend(attn_prefill_kernel<true, KV_FMT_Q4_0>); break;
+    case KV_FMT_K8V4 * 2: attend(attn_prefill_kernel<false, KV_FMT_K8V4>); break;
+    case KV_FMT_K8V4 * 2 + 1: attend(attn_prefill_kernel<true, KV_FMT_K8V4>); break;
     default: return KV_ERR_UNSUPPORTED;
   }
   return launch_status();

@@ -76,8 +76,12 @@ int launch_attn_splitk(const AttnCall &c);
 // Target number of split-K workgroups per KV head on the current device.
 int attn_target_splits(int n_kv_heads, int n_rows);
 
+// Prefill: a staging kernel writes each 32-cell tile of every KV head as
+// the attention kernel's LDS image into ws (prefill_workspace_bytes for
+// pos0 + n_new cells), then the attention kernel copies tiles from there.
+size_t prefill_workspace_bytes(const kv_pool *pool, int64_t n_cells);
 int launch_attn_prefill(const kv_pool *pool, const kv_seq *seq, const void *q, int q_dtype,
-                        int n_q_heads, int pos0, int n_new, float scale, float *out,
+                        int n_q_heads, int pos0, int n_new, float scale, float *out, void *ws,
                         hipStream_t s);
 
 }  // namespace k8v4
