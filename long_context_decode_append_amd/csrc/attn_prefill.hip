@@ -32,8 +32,6 @@
 //   * epilogue: O / l and (rotated V) the inverse Walsh-Hadamard transform
 //     in registers: a lane holds one dim of each 32-dim tile, so strides
 //     1 .. 16 are cross-lane butterflies and 32 .. 128 in-register ones.
-#include <type_traits>
-
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -444,17 +442,22 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
   auto kbuf = [&](int b) { return reinterpret_cast<const _Float16 *>(lds_img + b * kPfImageBytes); };
   auto sbuf = [&](int b) { return reinterpret_cast<const float *>(lds_img + b * kPfImageBytes + kImgKV); };
   // Copy tile t's image into buffer b: 1 KB per wave and instruction straight
-  // into LDS (lane l's 16 bytes land at 16 l), no registers.  A tile past the
-  // staged ones (a pair's second tile, masked out whole) copies the last one.
+  // into LDS (lane l's 16 bytes land at 16 l), no registers; chunk r of a
+  // wave is the image's KB 4 r + wave (37 KB: rounds 0 .. 8 for every wave,
+  // round 9 for wave 0).  A tile past the staged ones (a pair's second tile,
+  // masked out whole) copies the last one.
   const uint8_t *img_head = a.img + (size_t)g * a.n_tiles * kPfImageBytes + wave * 1024 + lane * 16;
+  constexpr int kCopyRounds = (kPfImageBytes / 1024 + kPfWaves - 1) / kPfWaves;
+  auto copy_chunk = [&](int b, int t, int r) {
+    if (r < kCopyRounds - 1 || r * kPfWaves + wave < kPfImageBytes / 1024) {
+      const uint8_t *src = img_head + (size_t)min(t, a.n_tiles - 1) * kPfImageBytes + r * kPfWaves * 1024;
+      uint8_t *dst = lds_img + b * kPfImageBytes + wave * 1024 + r * kPfWaves * 1024;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src),
+                                       (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+    }
+  };
   auto copy_tile = [&](int b, int t) {
-    const uint8_t *src = img_head + (size_t)min(t, a.n_tiles - 1) * kPfImageBytes;
-    uint8_t *dst = lds_img + b * kPfImageBytes + wave * 1024;
-    for (int r = 0; r < (kPfImageBytes / 1024 + kPfWaves - 1) / kPfWaves; r++)
-      if (r * kPfWaves + wave < kPfImageBytes / 1024)  // wave-uniform
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src + r * kPfWaves * 1024),
-                                         (__attribute__((address_space(3))) void *)(dst + r * kPfWaves * 1024),
-                                         16, 0, 0);
+    for (int r = 0; r < kCopyRounds; r++) copy_chunk(b, t, r);
   };
   // the copies issued so far have landed (each wave waits for its own; the
   // barrier that follows makes every wave's visible)
@@ -475,51 +478,50 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
     }
   };
 
-  // Scores of the tile in buffer b from its accumulators: the per-cell K
-  // scales (times softmax scale x log2 e) of each 128-dim group; this lane's
-  // cells are 8 j + 4 h .. + 3 ([cell][group] pairs in the image)
-  auto scale_scores = [&](int b, const f32x16 (&acc)[NG], float (&sc)[16]) {
-    const float *lks = sbuf(b);
-    for (int j = 0; j < 4; j++) {
-      const f32x4 d01 = *reinterpret_cast<const f32x4 *>(&lks[(8 * j + 4 * h) * 2]);
-      const f32x4 d23 = *reinterpret_cast<const f32x4 *>(&lks[(8 * j + 4 * h) * 2 + 4]);
-      for (int i = 0; i < 4; i++) {
-        const f32x4 &d = i < 2 ? d01 : d23;
-        float v = d[2 * (i & 1)] * acc[0][4 * j + i];
-        if constexpr (NG == 2) v += d[2 * (i & 1) + 1] * acc[1][4 * j + i];
-        sc[4 * j + i] = v;
+  // This lane's scores are row col, cells 8 (e / 4) + 4 h + e % 4 of a tile
+  // (element e of the 32 x 32 accumulator).  Their K scales (times softmax
+  // scale x log2 e) are [cell][group] pairs in the image: quad
+  // dks[2 (e / 4) + (e % 4) / 2], entries 2 (e % 2) and 2 (e % 2) + 1.
+  auto read_scale = [&](int b, int i) {
+    return *reinterpret_cast<const f32x4 *>(&sbuf(b)[(8 * (i >> 1) + 4 * h) * 2 + 4 * (i & 1)]);
+  };
+  auto scale_one = [&](const f32x4 (&dks)[8], const f32x16 (&acc)[NG], int e) {
+    const f32x4 &d = dks[2 * (e >> 2) + ((e & 3) >> 1)];
+    float v = d[2 * (e & 1)] * acc[0][e];
+    if constexpr (NG == 2) v += d[2 * (e & 1) + 1] * acc[1][e];
+    return v;
+  };
+  // tile u's cells past a row's position (and every cell of an invalid row)
+  // to -inf -- needed from the first tile some row does not see whole on;
+  // then the row max over the lane pair
+  auto mask_and_max = [&](int u, bool masked, float (&sc)[16]) {
+    if (masked)
+      for (int e = 0; e < 16; e++) {
+        const int cell = u * kPfTile + 8 * (e >> 2) + 4 * h + (e & 3);
+        sc[e] = (qvalid && cell <= qpos) ? sc[e] : -INFINITY;
       }
-    }
+    float mx = sc[0];
+    for (int e = 1; e < 16; e++) mx = fmaxf(mx, sc[e]);
+    return fmaxf(mx, lane_xor<32>(mx));
   };
 
-  // One step of the pipeline, for tile t (cells c0 = 32 t ..) held in buffer
-  // b0, the next tile in b1, with this tile's scores in `cur`: the copy of
-  // tile t + 2 into b2 is issued; the next tile's scores are computed (into
-  // `nxt`) on the MFMAs while this tile's softmax runs on the VALU; then
-  // O += P.V.  This lane's scores are row col, cells 8 (e / 4) + 4 h + e % 4
-  // (element e of the 32 x 32 accumulator).
-  auto step = [&](int t, int b0, int b1, int b2, const float (&cur)[16], float (&nxt)[16], auto mtag) {
-    constexpr bool MASKED = decltype(mtag)::value;
-    const int c0 = t * kPfTile;
-    copy_tile(b2, t + 2);
-    // ---------------- the reference max and the rare O rescale
-    float s[16];
-    for (int e = 0; e < 16; e++) {
-      float sv = cur[e];
-      if (MASKED) {
-        const int cell = c0 + 8 * (e >> 2) + 4 * h + (e & 3);
-        sv = (qvalid && cell <= qpos) ? sv : -INFINITY;
-      }
-      s[e] = sv;
-    }
-    // online softmax: the row's 32 cells are in lanes col and col + 32; the
-    // reference max moves (for every row, to at least its max) only when
+  // One step of the pipeline, for tile t held in buffer b0 (the next tile in
+  // b1), with this tile's masked scores in `cur` and their row max in mx_cur:
+  // the copy of tile t + 2 into b2 is issued (one chunk per section); the next tile's scores are
+  // computed (into `nxt`, mx_nxt) on the MFMAs while this tile's softmax runs
+  // on the VALU; then O += P.V.  The sections are hand-ordered (scheduling
+  // fences), each with one MFMA, the LDS read of an operand eight MFMAs ahead
+  // and a little VALU work: the compiler otherwise reads each operand just
+  // before its MFMA and waits out the LDS latency every time.
+  const int n_tiles = (n_cells + kPfTile - 1) / kPfTile;
+  const int n_full = ((a.pos0 + qb0 + 1) / kPfTile) & ~1;  // tiles every row sees whole, even
+  const int n_end = n_full + ((n_tiles - n_full + 1) & ~1);
+  auto step = [&](int t, int b0, int b1, int b2, const float (&cur)[16], float mx_cur, float (&nxt)[16],
+                  float &mx_nxt) {
+    // the reference max moves (for every row, to at least its max) only when
     // some row's max exceeds it by more than 2^kPfLazy
-    float mx = s[0];
-    for (int e = 1; e < 16; e++) mx = fmaxf(mx, s[e]);
-    mx = fmaxf(mx, lane_xor<32>(mx));
-    if (__any(mx > m + kPfLazy)) {
-      const float mnew = fmaxf(m, mx);
+    if (__any(mx_cur > m + kPfLazy)) {
+      const float mnew = fmaxf(m, mx_cur);
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);
       lsum *= alpha;
       m = mnew;
@@ -530,64 +532,77 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
         for (int jd = 0; jd < 8; jd++) o[jd][e] *= al;
       }
     }
-    // ---------------- the next tile's scores on the MFMAs, this tile's
-    // probabilities on the VALU; this tile's P.V operands (B for dim tile jd,
-    // k-step st: dim 32 jd + col, the lane half's 8 cells of the step, v_pos)
-    f16x8 kop[16], vop[8][2];
-    k_operands(b1, kop);
-    const _Float16 *lv = kbuf(b0) + kKElems;
-    for (int jd = 0; jd < 8; jd++) {
-      const _Float16 *vr = lv + v_row(32 * jd + col) + 8 * h;
-      for (int st = 0; st < 2; st++) vop[jd][st] = *reinterpret_cast<const f16x8 *>(vr + 16 * st);
-    }
+    // K operand i: dims 16 i + 8 h .. of cell col (tile t + 1); V operand
+    // i = 8 st + jd: dim 32 jd + col, the lane half's 8 cells of k-step st
+    f16x8 kop[16], vop[16];
+    f32x4 dks[8];
+    const _Float16 *kr = kbuf(b1) + col * kKRow + 8 * h;
+    const _Float16 *lv = kbuf(b0) + kKElems + 8 * h;
+    auto rd_k = [&](int i) { kop[i] = *reinterpret_cast<const f16x8 *>(kr + 16 * i); };
+    auto rd_v = [&](int i) {
+      vop[i] = *reinterpret_cast<const f16x8 *>(lv + v_row(32 * (i & 7) + col) + 16 * (i >> 3));
+    };
+    // QK order: the two 128-dim groups alternate (independent MFMAs back to back)
+    auto kk_of = [](int i) { return NG == 2 ? (i >> 1) + 8 * (i & 1) : i; };
     f32x16 acc[NG];
-    qk(kop, acc);
+    for (int gg = 0; gg < NG; gg++)
+      for (int e = 0; e < 16; e++) acc[gg][e] = 0.f;
     f16x8 pop[2];
     float ps = 0.f;
-    for (int e = 0; e < 16; e++) {
-      const float p = __builtin_amdgcn_exp2f(s[e] - m);
+    for (int i = 0; i < 8; i++) rd_k(kk_of(i));
+    __builtin_amdgcn_sched_barrier(0);
+    // the next tile's scores; this tile's probabilities
+    for (int i = 0; i < 16; i++) {
+      const int kk = kk_of(i), gg = NG == 2 ? (kk >> 3) : 0;
+      acc[gg] = mfma32(kop[kk], qop[kk], acc[gg]);
+      if (QF32) acc[gg] = mfma32(kop[kk], qlo[kk], acc[gg]);
+      if (i + 8 < 16) rd_k(kk_of(i + 8));
+      else rd_v(i - 8);
+      if (i < 8) dks[i] = read_scale(b1, i);
+      if (i < kCopyRounds) copy_chunk(b2, t + 2, i);  // tile t + 2, one KB per wave
+      const float p = __builtin_amdgcn_exp2f(cur[i] - m);
       ps += p;
-      pop[e >> 3][e & 7] = (_Float16)p;
+      pop[i >> 3][i & 7] = (_Float16)p;
+      __builtin_amdgcn_sched_barrier(0);
     }
     lsum += ps;
-    for (int jd = 0; jd < 8; jd++)
-      for (int st = 0; st < 2; st++) o[jd] = mfma32(pop[st], vop[jd][st], o[jd]);
-    scale_scores(b1, acc, nxt);
+    // this tile's O += P.V; the next tile's scaled scores
+    for (int i = 0; i < 16; i++) {
+      o[i & 7] = mfma32(pop[i >> 3], vop[i], o[i & 7]);
+      if (i + 8 < 16) rd_v(i + 8);
+      nxt[i] = scale_one(dks, acc, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mx_nxt = mask_and_max(t + 1, t + 1 >= n_full, nxt);
     copies_done();
     __syncthreads();
   };
 
-  // Prologue: tiles 0 and 1 copied, tile 0's scores computed.  Tiles that
-  // every row of the block sees whole skip the causal mask; both loops take
-  // tiles in pairs (the score registers swap roles), the masked one past the
-  // visible cells if need be (such a tile is masked out whole).
+  // Prologue: tiles 0 and 1 copied, tile 0's scores computed.  The loop takes
+  // tiles in pairs (the score registers swap roles), past the visible cells
+  // if need be (such a tile is masked out whole; its copy repeats the last
+  // staged tile).
   copy_tile(0, 0);
   copy_tile(1, 1);
   copies_done();
   __syncthreads();
-  float sa[16], sb[16];
+  float sa[16], sb[16], mxa, mxb;
   {
     f16x8 kop[16];
     f32x16 acc[NG];
+    f32x4 dks[8];
     k_operands(0, kop);
     qk(kop, acc);
-    scale_scores(0, acc, sa);
+    for (int i = 0; i < 8; i++) dks[i] = read_scale(0, i);
+    for (int e = 0; e < 16; e++) sa[e] = scale_one(dks, acc, e);
+    mxa = mask_and_max(0, 0 >= n_full, sa);
   }
-  const int n_tiles = (n_cells + kPfTile - 1) / kPfTile;
-  const int n_full = ((a.pos0 + qb0 + 1) / kPfTile) & ~1;  // tiles every row sees whole, even
-  const int n_end = n_full + ((n_tiles - n_full + 1) & ~1);
-  int t = 0, b0 = 0;
+  int b0 = 0;
   auto nb = [](int b) { return b == 2 ? 0 : b + 1; };
-  for (; t < n_full; t += 2) {
-    step(t, b0, nb(b0), nb(nb(b0)), sa, sb, std::false_type{});
+  for (int t = 0; t < n_end; t += 2) {
+    step(t, b0, nb(b0), nb(nb(b0)), sa, mxa, sb, mxb);
     b0 = nb(b0);
-    step(t + 1, b0, nb(b0), nb(nb(b0)), sb, sa, std::false_type{});
-    b0 = nb(b0);
-  }
-  for (; t < n_end; t += 2) {
-    step(t, b0, nb(b0), nb(nb(b0)), sa, sb, std::true_type{});
-    b0 = nb(b0);
-    step(t + 1, b0, nb(b0), nb(nb(b0)), sb, sa, std::true_type{});
+    step(t + 1, b0, nb(b0), nb(nb(b0)), sb, mxb, sa, mxa);
     b0 = nb(b0);
   }
 
