@@ -126,6 +126,12 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
   asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
   return r;
 }
+// the same with a per-lane mask
+__device__ __forceinline__ uint32_t and_or_v(uint32_t x, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(c));
+  return r;
+}
 
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit elements (gfx9 family)
 
@@ -374,7 +380,10 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
   const int v_voff = kF16 ? 256 * lg + 16 * n : kQ4V ? 4 * lg * 128 + 8 * n : 4 * lg * 256 + 16 * n;
   const int vd_voff = kQ4V ? (n >> 1) * 32 + 8 * lg : 32 * lg;
   const int kstep_j = (kInt8K || kF16) ? 1024 : 32;
-  const uint32_t q4_shift = (lg & 1) ? 4u : 0u;  // q4_0 K: high nibbles for odd lg
+  // q4_0 K: even lg takes the low nibbles (fp16 1024 + n under exponent 25),
+  // odd lg the high ones left in bits 4..7 (64 + n under exponent 21)
+  const uint32_t q4_mask = (lg & 1) ? 0x00F000F0u : 0x000F000Fu;
+  const uint32_t q4_expo = (lg & 1) ? 0x54005400u : 0x64006400u;
   const int v8_grp = n >> 3;                     // INT8 V: scale group of this lane's dims
 
   u32x4 kr[2][kKLoads];
@@ -498,22 +507,32 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
       }
     }
     if (FMT == KV_FMT_Q4_0) {
-      float *qs = &lds_o[wave * 16 * 64 * 4];  // [16 rows][256] fp32 of this wave
-      for (int kk = 0; kk < 8; kk++) {
-        const int d0 = 64 * (kk >> 1) + 16 * lg + 8 * (kk & 1);
-        *reinterpret_cast<f32x4 *>(&qs[n * 256 + d0]) = f32x4{qv[kk][0], qv[kk][1], qv[kk][2], qv[kk][3]};
-        *reinterpret_cast<f32x4 *>(&qs[n * 256 + d0 + 4]) = f32x4{qv[kk][4], qv[kk][5], qv[kk][6], qv[kk][7]};
-      }
-      for (int r = 0; r < 16; r++) {
-        f32x4 y4 = *reinterpret_cast<const f32x4 *>(&qs[r * 256 + 4 * lane]);
+      // Every wave of the workgroup holds the same rows: wave 0 writes them
+      // to a shared buffer (rows 260 floats apart, so the 16 rows' writes
+      // fall on different banks), each wave rotates the valid rows r with
+      // r % 4 == wave in place, and every wave reads the tile back.
+      constexpr int kQs = 256 + 4;
+      float *qs = lds_o;  // [16 rows][kQs]; lds_o is free until the merge
+      if (t > 0) __syncthreads();  // the previous tile's readers are done
+      if (wave == 0)
+        for (int kk = 0; kk < 8; kk++) {
+          const int d0 = 64 * (kk >> 1) + 16 * lg + 8 * (kk & 1);
+          *reinterpret_cast<f32x4 *>(&qs[n * kQs + d0]) = f32x4{qv[kk][0], qv[kk][1], qv[kk][2], qv[kk][3]};
+          *reinterpret_cast<f32x4 *>(&qs[n * kQs + d0 + 4]) = f32x4{qv[kk][4], qv[kk][5], qv[kk][6], qv[kk][7]};
+        }
+      __syncthreads();
+      const int rows_t = min(16, rows_here - 16 * t);  // valid rows of the tile (wave-uniform)
+      for (int r = wave; r < rows_t; r += kWaves) {
+        f32x4 y4 = *reinterpret_cast<const f32x4 *>(&qs[r * kQs + 4 * lane]);
         float y[4] = {y4[0], y4[1], y4[2], y4[3]};
         fwht256_lane4(y, lane);
-        *reinterpret_cast<f32x4 *>(&qs[r * 256 + 4 * lane]) = f32x4{y[0], y[1], y[2], y[3]};
+        *reinterpret_cast<f32x4 *>(&qs[r * kQs + 4 * lane]) = f32x4{y[0], y[1], y[2], y[3]};
       }
+      __syncthreads();
       for (int kk = 0; kk < 8; kk++) {
         const int d0 = 64 * (kk >> 1) + 16 * lg + 8 * (kk & 1);
-        const f32x4 x0 = *reinterpret_cast<const f32x4 *>(&qs[n * 256 + d0]);
-        const f32x4 x1 = *reinterpret_cast<const f32x4 *>(&qs[n * 256 + d0 + 4]);
+        const f32x4 x0 = *reinterpret_cast<const f32x4 *>(&qs[n * kQs + d0]);
+        const f32x4 x1 = *reinterpret_cast<const f32x4 *>(&qs[n * kQs + d0 + 4]);
         for (int u = 0; u < 8; u++) {
           const int e = q4_kslot(u);
           qv[kk][u] = e < 4 ? x0[e] : x1[e - 4];
@@ -547,6 +566,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
       cbias[t][1] = 1152.0f * s1;
     }
   }
+  if (FMT == KV_FMT_Q4_0) __syncthreads();  // every wave has read the rotated rows (lds_o is reused)
   // smallest visible-cell limit over the valid rows of this tile (wave-
   // uniform): steps that end below it need no masking at all
   int lim_min;
@@ -577,6 +597,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
   }
   const f16x2 c1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
   const f16x2 c72 = {(_Float16)72.0f, (_Float16)72.0f};
+  const f16x2 q4_bias = (lg & 1) ? c72 : c1032;  // q4_0 K: the nibble's offset + 8
   const f16x2 c1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
 
   if (has_work) {
@@ -626,10 +647,10 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
             const f16x2 dd = as_f16x2(d | (d << 16));
             uint32_t w[8];
             for (int q = 0; q < 4; q++) {
-              const uint32_t x = kr[h2][j][q] >> q4_shift;
+              const uint32_t x = kr[h2][j][q];
               const uint32_t y = x >> 8;
-              w[2 * q] = as_u32((as_f16x2(and_or(x, 0x000F000Fu, 0x64006400u)) - c1032) * dd);
-              w[2 * q + 1] = as_u32((as_f16x2(and_or(y, 0x000F000Fu, 0x64006400u)) - c1032) * dd);
+              w[2 * q] = as_u32((as_f16x2(and_or_v(x, q4_mask, q4_expo)) - q4_bias) * dd);
+              w[2 * q + 1] = as_u32((as_f16x2(and_or_v(y, q4_mask, q4_expo)) - q4_bias) * dd);
             }
             ka = pack8(w[0], w[1], w[2], w[3]);
             kb = pack8(w[4], w[5], w[6], w[7]);
