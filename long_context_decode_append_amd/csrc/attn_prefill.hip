@@ -9,26 +9,26 @@
 //
 // Here Q.K^T and P.V are dense contractions (every K/V tile serves all
 // query rows of a workgroup), so both run on the matrix cores with the
-// 32 x 32 x 16 fp16 MFMA (fp32 accumulation):
-//   * workgroup = 4 waves, one per SIMD; a wave owns 64 query rows (two
-//     32-row tiles: 8 positions x 8 GQA heads of one KV head; fp32 queries:
-//     one tile, carried as fp16 hi + lo halves), so a workgroup covers 256
-//     rows (128 with fp32 queries);
-//   * per 32-cell tile the workgroup loads the raw pages once and
-//     dequantizes them into LDS: INT8 K as exact fp16 codes [cell][dim] (the
-//     two 128-dim group scales, times softmax scale x log2 e, applied to the
-//     two half-dots), q4_0 K as (code - 8) * d16, V transposed [dim][cell]
-//     as (code - 8) * d16 or code * d, its cells ordered so that the P.V
-//     B-operand of a lane (8 cells) is one 16-byte read;
-//   * every K operand read from LDS (32 cells x 16 dims) and every V operand
-//     (16 cells x 32 dims) feeds the MFMAs of both row tiles, so a wave reads
-//     32 KB of operands per tile for 64 rows;
-//   * two LDS tile buffers: the raw pages of tile i + 2 are loaded and tile
-//     i + 1 is dequantized while tile i is computed; one barrier per tile;
+// 32 x 32 x 16 fp16 MFMA (fp32 accumulation).  A call is two kernels:
+//   * staging: one workgroup per (32-cell tile, KV head) loads the tile's
+//     raw pages once and writes its image to the workspace -- INT8 K as
+//     exact fp16 codes [cell][dim] with the two 128-dim group scales (times
+//     softmax scale x log2 e) beside them, q4_0 K as (code - 8) * d16, V
+//     transposed [dim][cell] as (code - 8) * d16 or code * d, its cells
+//     ordered so that the P.V B-operand of a lane (8 cells) is one 16-byte
+//     read.  Every attention workgroup of a KV head reads the same tiles, so
+//     this is the dequantization they would otherwise each repeat;
+//   * attention: workgroup = 4 waves, one per SIMD, each owning 32 query
+//     rows (4 positions x 8 GQA heads of one KV head; fp32 queries add an
+//     MFMA on the fp16 rounding remainder), 128 rows per workgroup.  Four
+//     LDS image buffers: tile t + 3 is copied in with direct global-to-LDS
+//     loads (no registers, no VALU) while tile t's P.V and tile t + 1's
+//     Q.K^T run; one barrier per tile;
 //   * S^T = K.Q^T puts a lane's query row in the column the P.V A-operand
 //     needs, so P never leaves registers; online softmax in base 2 against a
-//     lazily moved reference max; the causal mask only in tiles that reach
-//     a wave's rows;
+//     lazily moved reference max; the causal mask only from the first tile
+//     some row does not see whole; each tile step is hand-ordered (operand
+//     reads eight MFMAs ahead, VALU work beside the MFMAs);
 //   * epilogue: O / l and (rotated V) the inverse Walsh-Hadamard transform
 //     in registers: a lane holds one dim of each 32-dim tile, so strides
 //     1 .. 16 are cross-lane butterflies and 32 .. 128 in-register ones.
@@ -360,7 +360,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
   constexpr int kPos = kPfWaves * 32 / kGqa;          // query positions per workgroup
   constexpr int NG = (FMT == KV_FMT_INT8 || FMT == KV_FMT_K8V4) ? 2 : 1;  // K scale groups
   constexpr bool kRotV = FMT == KV_FMT_Q4_0 || FMT == KV_FMT_K8V4;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_img[3 * kPfImageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_img[4 * kPfImageBytes];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -462,6 +462,10 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
   // the copies issued so far have landed (each wave waits for its own; the
   // barrier that follows makes every wave's visible)
   auto copies_done = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  // every copy but this step's (a wave issues kCopyRounds = 10 or, past
+  // wave 0, 9 per step; vmcnt(9) leaves at most those outstanding)
+  static_assert(kCopyRounds == 10, "the wait below counts a step's copies");
+  auto older_copies_done = [] { asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); };
   // S^T = K.Q^T of the tile in buffer b: its 16 K operands, then 16 (fp32
   // queries: 32) MFMAs
   auto k_operands = [&](int b, f16x8 (&kop)[16]) {
@@ -507,7 +511,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
 
   // One step of the pipeline, for tile t held in buffer b0 (the next tile in
   // b1), with this tile's masked scores in `cur` and their row max in mx_cur:
-  // the copy of tile t + 2 into b2 is issued (one chunk per section); the next tile's scores are
+  // the copy of tile t + 3 into b3 is issued (one chunk per section); the next tile's scores are
   // computed (into `nxt`, mx_nxt) on the MFMAs while this tile's softmax runs
   // on the VALU; then O += P.V.  The sections are hand-ordered (scheduling
   // fences), each with one MFMA, the LDS read of an operand eight MFMAs ahead
@@ -516,7 +520,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
   const int n_tiles = (n_cells + kPfTile - 1) / kPfTile;
   const int n_full = ((a.pos0 + qb0 + 1) / kPfTile) & ~1;  // tiles every row sees whole, even
   const int n_end = n_full + ((n_tiles - n_full + 1) & ~1);
-  auto step = [&](int t, int b0, int b1, int b2, const float (&cur)[16], float mx_cur, float (&nxt)[16],
+  auto step = [&](int t, int b0, int b1, int b3, const float (&cur)[16], float mx_cur, float (&nxt)[16],
                   float &mx_nxt) {
     // the reference max moves (for every row, to at least its max) only when
     // some row's max exceeds it by more than 2^kPfLazy
@@ -559,7 +563,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
       if (i + 8 < 16) rd_k(kk_of(i + 8));
       else rd_v(i - 8);
       if (i < 8) dks[i] = read_scale(b1, i);
-      if (i < kCopyRounds) copy_chunk(b2, t + 2, i);  // tile t + 2, one KB per wave
+      if (i < kCopyRounds) copy_chunk(b3, t + 3, i);  // tile t + 3, one KB per wave
       const float p = __builtin_amdgcn_exp2f(cur[i] - m);
       ps += p;
       pop[i >> 3][i & 7] = (_Float16)p;
@@ -574,7 +578,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
       __builtin_amdgcn_sched_barrier(0);
     }
     mx_nxt = mask_and_max(t + 1, t + 1 >= n_full, nxt);
-    copies_done();
+    older_copies_done();
     __syncthreads();
   };
 
@@ -584,6 +588,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
   // staged tile).
   copy_tile(0, 0);
   copy_tile(1, 1);
+  copy_tile(2, 2);
   copies_done();
   __syncthreads();
   float sa[16], sb[16], mxa, mxb;
@@ -598,12 +603,11 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
     mxa = mask_and_max(0, 0 >= n_full, sa);
   }
   int b0 = 0;
-  auto nb = [](int b) { return b == 2 ? 0 : b + 1; };
   for (int t = 0; t < n_end; t += 2) {
-    step(t, b0, nb(b0), nb(nb(b0)), sa, mxa, sb, mxb);
-    b0 = nb(b0);
-    step(t + 1, b0, nb(b0), nb(nb(b0)), sb, mxb, sa, mxa);
-    b0 = nb(b0);
+    step(t, b0, (b0 + 1) & 3, (b0 + 3) & 3, sa, mxa, sb, mxb);
+    b0 = (b0 + 1) & 3;
+    step(t + 1, b0, (b0 + 1) & 3, (b0 + 3) & 3, sb, mxb, sa, mxa);
+    b0 = (b0 + 1) & 3;
   }
 
   // ---------------- epilogue: O / l; the lane holds dim 32 jd + col of rows
