@@ -515,6 +515,8 @@ def bench_extra(torch, k8, synth, dev, log):
         pools[i % n_pools], tables[i % n_pools], q1, ctx, ws1), 2 * n_pools)
     v_ms, _ = timed_launches(torch, k8, lambda i: k8.attn_verify(
         pools[i % n_pools], tables[i % n_pools], q5, nv, ws5), reps)
+    vc_ms = graph_calls_ms(torch, lambda i: k8.attn_verify(
+        pools[i % n_pools], tables[i % n_pools], q5, nv, ws5), 2 * n_pools)
     b = ctx * CELL_BYTES
     out["decode_240000"] = {"us": round(d_ms * 1e3, 3), "gbs": round(b / d_ms / 1e6, 2),
                             "hbm_frac": round(b / d_ms / 1e6 / HBM_PEAK_GBS, 4),
@@ -532,6 +534,9 @@ def bench_extra(torch, k8, synth, dev, log):
     out["decode_sweep_split_plus_combine"] = sweep
     out["verify5_240000"] = {"us": round(v_ms * 1e3, 3), "gbs": round(b / v_ms / 1e6, 2),
                              "hbm_frac": round(b / v_ms / 1e6 / HBM_PEAK_GBS, 4),
+                             "kernel": "split kernel alone",
+                             "us_split_plus_combine": round(vc_ms * 1e3, 3),
+                             "hbm_frac_split_plus_combine": round(b / vc_ms / 1e6 / HBM_PEAK_GBS, 4),
                              "n_visible": nv}
     # batched decode: 4 sequences of 59,904 cells (234 pages; their tables
     # are quarters of each 240,000-cell table) in one call, against 4 single

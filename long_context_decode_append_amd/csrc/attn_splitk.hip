@@ -305,8 +305,9 @@ __device__ __forceinline__ void append_token_partial(const SplitArgs &a, int g, 
 // they should not displace other data from L2 / MALL; the row passes of a
 // verify share their reads through L2 and load normally)
 // T: 16-row tiles per wave.  Verify runs T > 1: each step's K/V is loaded
-// and dequantized once and used for all T tiles (the accumulators of the
-// extra tiles spill into AGPRs, so one wave per SIMD).
+// and dequantized once and used for all T tiles (the queries' MFMA operands
+// are held in AGPRs and the extra tiles' accumulators take the registers a
+// second wave would use, so one wave per SIMD).
 // fp16 (T = 1 only): a step's raw K and V take 128 VGPRs, one workgroup per
 // CU (the split plan's target anyway).
 template <bool QF32, int FMT, bool NT, int T, bool STREAM>
@@ -557,6 +558,10 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
       }
       if (kk < 4) s0 += ss; else s1 += ss;
       qop[t][kk] = hi;
+      // several row tiles: the queries' operands live in AGPRs, where the
+      // Q.K^T MFMAs read them directly (left to the register allocator
+      // they are spilled there and copied back before every use)
+      if (T > 1) asm volatile("" : "+a"(qop[t][kk]));
       if (QF32) qlo[t][kk] = lo;
     }
     if (kInt8K) {
