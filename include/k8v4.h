@@ -451,15 +451,20 @@ const char *kv_strerror(int code);
 const char *kv_last_hip_error(void);
 
 /*
- * Profiling hook: the calling thread's next kernel launch by this library
- * records start_event when the kernel starts and stop_event when it ends
- * (hipExtLaunchKernelGGL), so hipEventElapsedTime gives that one kernel's
- * duration.  Both are hipEvent_t created by the caller on the device of
- * the launch.  attn_decode and attn_verify launch the split kernel and then
- * a small combine kernel, so the hook times the split kernel; every other
- * entry point launches one kernel.  The hook applies to the next entry-point
- * call only: a call that returns before launching (an error, empty work)
- * disarms it.  Errors: KV_ERR_NULL.
+ * Measurement aid, not part of the method.  Profiling hook: the calling
+ * thread's next kernel launch by this library records start_event when the
+ * kernel starts and stop_event when it ends (hipExtLaunchKernelGGL), so
+ * hipEventElapsedTime gives that one kernel's duration.  Both are hipEvent_t
+ * created by the caller on the device of the launch.  What it brackets, per
+ * entry point: attn_decode, attn_decode_append, attn_decode_batch,
+ * attn_verify and attn_decode_noalloc launch the split kernel and then a
+ * small combine kernel, so the hook times the split kernel;
+ * attn_decode_stream and attn_verify_stream launch a page-lookup kernel
+ * first, which is what the hook times; attn_prefill_chunk's two kernels are
+ * bracketed together (start of the staging kernel to the end of the
+ * attention kernel); every other entry point launches one kernel.  The hook
+ * applies to the next entry-point call only: a call that returns before
+ * launching (an error, empty work) disarms it.  Errors: KV_ERR_NULL.
  */
 int kv_time_next_launch(void *start_event, void *stop_event);
 
