@@ -14,7 +14,10 @@
  * Conventions for every call below:
  *   - Pointers named "device" are HIP device memory owned by the caller;
  *     "host" pointers are read during the call only.  The library never
- *     allocates, frees or synchronizes.
+ *     allocates or frees memory (attn_decode_noalloc uses a fixed
+ *     file-scope device array instead of a workspace) and never
+ *     synchronizes, except the debug call kv_check_page_table, which copies
+ *     the table to the host.
  *   - Calls that take a stream only enqueue work on it (a hipStream_t, or
  *     NULL for the null stream) and return; device faults surface at the
  *     caller's next synchronization.
