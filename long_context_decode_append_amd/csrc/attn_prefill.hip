@@ -11,13 +11,14 @@
 // query rows of a workgroup), so both run on the matrix cores with the
 // 32 x 32 x 16 fp16 MFMA (fp32 accumulation).  A call is two kernels:
 //   * staging: one workgroup per (32-cell tile, KV head) loads the tile's
-//     raw pages once and writes its image to the workspace -- INT8 K as
-//     exact fp16 codes [cell][dim] with the two 128-dim group scales (times
-//     softmax scale x log2 e) beside them, q4_0 K as (code - 8) * d16, V
-//     transposed [dim][cell] as (code - 8) * d16 or code * d, its cells
-//     ordered so that the P.V B-operand of a lane (8 cells) is one 16-byte
-//     read.  Every attention workgroup of a KV head reads the same tiles, so
-//     this is the dequantization they would otherwise each repeat;
+//     raw pages once and writes its image to the workspace -- K [cell][dim]
+//     as fp16 values already multiplied by softmax scale x log2 e (INT8
+//     code * group scale, q4_0 (code - 8) * d16, fp16 as stored; formed in
+//     fp32 and rounded once), V transposed [dim][cell] as (code - 8) * d16
+//     or code * d, its cells ordered so that the P.V B-operand of a lane
+//     (8 cells) is one 16-byte read.  Every attention workgroup of a KV head
+//     reads the same tiles, so this is the dequantization they would
+//     otherwise each repeat, and its scores need no scaling;
 //   * attention: workgroup = 4 waves, one per SIMD, each owning 32 query
 //     rows (4 positions x 8 GQA heads of one KV head; fp32 queries add an
 //     MFMA on the fp16 rounding remainder), 128 rows per workgroup.  Four
@@ -53,11 +54,11 @@ __device__ __forceinline__ int v_row(int d) { return d * kVRow + (d >> 5) * kVBl
 __device__ __forceinline__ int v_pos(int c) { return (c & 19) | ((c & 4) << 1) | ((c & 8) >> 1); }
 
 // A staged tile: K [32 cells][kKRow] fp16, V [256 dims][v_pos] fp16 with a
-// pad after every 32 dims, then the 64 K scales [cell][group] -- the LDS
+// pad after every 32 dims, the whole padded to a multiple of 1 KB -- the LDS
 // image the attention kernel computes from, copied there unchanged.
 constexpr int kKElems = kPfTile * kKRow, kVElems = 256 * kVRow + 8 * kVBlockPad;
 constexpr int kImgKV = 2 * (kKElems + kVElems);     // bytes of K and V
-constexpr int kPfImageBytes = kImgKV + 2 * kPfTile * 4;
+constexpr int kPfImageBytes = (kImgKV + 1023) & ~1023;
 static_assert(kPfImageBytes % 1024 == 0, "whole 1 KB copy units");
 
 struct PrefillArgs {
@@ -95,8 +96,7 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
 //   fp16 K: dims 16 (i % 16) .. + 15 of cell 16 (u / 256) + i / 16
 //   fp16 V: 32 consecutive bytes of the half: chunks 2i and 2i + 1 of its
 //           8 KB block, each 4 cells x 2 dims
-//   K scales (the first unit only): slot tid % 64, that is cell (tid % 64) / 2,
-//           group tid % 2 (waves 1 .. 3 repeat wave 0's loads)
+//   INT8 K scale: that of the unit's cell and 128-dim group
 // The loads are unconditional (every address lies in the pool: a half past
 // the visible cells reads the last visible half again, a cell past them lies
 // in its half's page); the values of cells past the visible ones are zeroed
@@ -105,7 +105,7 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
 struct PfRaw {
   u32x4 k;          // INT8 K: 16 codes; q4_0 K: .x .y nibble bytes, .z scale; fp16 K: dims 0 .. 7
   u32x4 k2;         // fp16 K: dims 8 .. 15 of the unit
-  float ks;         // INT8 K scale as stored
+  float ks;         // INT8 K: the unit's group scale as stored
   u32x2 va, vb;     // V of the two cells (q4_0: .x only)
   uint32_t vd;      // q4_0 V: the two fp16 scales (lo: first cell)
   float vsa, vsb;   // INT8 V: the two cells' scales
@@ -148,7 +148,7 @@ __device__ __forceinline__ PfHalves pf_halves(const PrefillArgs &a, int g, int c
   return h;
 }
 
-template <int FMT, int HF, bool SCALE>
+template <int FMT, int HF>
 __device__ __forceinline__ void pf_load(const PrefillArgs &a, const PfHalves &hv, int tid, PfRaw &r) {
   const int i = tid;  // unit u = tid + 256 HF
   const size_t cell0 = (size_t)hv.tile[HF] * a.P + hv.slot0[HF];  // first cell of the half, pool order
@@ -181,12 +181,8 @@ __device__ __forceinline__ void pf_load(const PrefillArgs &a, const PfHalves &hv
     r.k.z = *reinterpret_cast<const uint16_t *>(tile_base + q4_scale_off(a.P, hv.slot0[HF], 0) +
                                                 (uint32_t)(b * 32 + c * 2));
   }
-  if (SCALE) {  // scale slot tid % 64 of the tile: both halves, selected per lane
-    const int cs = (tid & 63) >> 1;
-    const size_t c0 = (size_t)hv.tile[0] * a.P + hv.slot0[0], c1 = (size_t)hv.tile[1] * a.P + hv.slot0[1];
-    const float *ks = reinterpret_cast<const float *>(a.run[1]) + (cs >> 4 ? c1 : c0) * 2;
-    r.ks = ks[(cs & 15) * 2 + (tid & 1)];
-  }
+  if (FMT != KV_FMT_Q4_0)  // [cell][group] floats in pool order
+    r.ks = reinterpret_cast<const float *>(a.run[1])[(cell0 + ((i >> 4) & 15)) * 2 + ((i & 15) >> 3)];
   const int j = i & 7;  // cells 2 j, 2 j + 1 of the half
   if (FMT != KV_FMT_INT8) {
     const int b = (i >> 3) & 7, qq = i >> 6;
@@ -221,22 +217,36 @@ __device__ __forceinline__ void q4_word_to_f16(uint32_t w, f16x2 d, uint32_t lo[
   }
 }
 
+// an fp16 pair times f, formed in fp32 and rounded once
+__device__ __forceinline__ uint32_t f16x2_scaled(uint32_t w, float f) {
+  const f16x2 h = as_f16x2(w);
+  const f16x2 y = {(_Float16)((float)h[0] * f), (_Float16)((float)h[1] * f)};
+  return as_u32(y);
+}
+
 // Dequantize work unit u of the tile at c0 into its tile image (K
-// [cell][dim], V [dim][v_pos(cell)]).  Cells at or past n_cells store zero
-// K and V.
+// [cell][dim] times softmax scale x log2 e, V [dim][v_pos(cell)]).  Cells
+// at or past n_cells store zero K and V; the K of a half whose page-table
+// entry is out of range (bad) is NaN, so rows that reach it return NaN and
+// rows that stop before it mask it.
 template <int FMT, int HF>
-__device__ __forceinline__ void pf_store(const PfRaw &r, int tid, int c0, int n_cells, _Float16 *lk, _Float16 *lv) {
+__device__ __forceinline__ void pf_store(const PfRaw &r, int tid, int c0, int n_cells, bool bad, float scale2,
+                                         _Float16 *lk, _Float16 *lv) {
   const int u = tid + 256 * HF, i = tid;
   const int cl = u >> 4;
   const bool k_ok = c0 + cl < n_cells;
+  const float kf_nan = __builtin_nanf("");
   if (FMT == KV_FMT_F16) {
     // K row-major [cell][dim]; V transposed [dim][cell]: chunk (uu, lq, nn)
     // holds dims 16 nn + 2 uu (+1) of cells 4 lq .. 4 lq + 3 of its half,
     // which sit side by side in a V row (v_pos)
-    const u32x4 z = {0u, 0u, 0u, 0u};
+    const float f = !k_ok ? 0.f : bad ? kf_nan : scale2;
+    const uint32_t kw[8] = {r.k.x, r.k.y, r.k.z, r.k.w, r.k2.x, r.k2.y, r.k2.z, r.k2.w};
+    uint32_t kf[8];
+    for (int e = 0; e < 8; e++) kf[e] = f16x2_scaled(kw[e], f);
     _Float16 *kd = lk + cl * kKRow + 16 * (u & 15);
-    *reinterpret_cast<u32x4 *>(kd) = k_ok ? r.k : z;
-    *reinterpret_cast<u32x4 *>(kd + 8) = k_ok ? r.k2 : z;
+    *reinterpret_cast<u32x4 *>(kd) = u32x4{kf[0], kf[1], kf[2], kf[3]};
+    *reinterpret_cast<u32x4 *>(kd + 8) = u32x4{kf[4], kf[5], kf[6], kf[7]};
     const int vh = u >> 8, idx = u & 255;
     const int uu = idx >> 5, lq = (idx >> 3) & 3;
     const int cq = c0 + 16 * vh + 4 * lq;
@@ -251,28 +261,35 @@ __device__ __forceinline__ void pf_store(const PfRaw &r, int tid, int c0, int n_
     return;
   }
   if (FMT != KV_FMT_Q4_0) {
-    // INT8 K -> exact fp16 codes, row-major [cell][dim]
+    // INT8 K -> code * scale * scale2, row-major [cell][dim] (the codes are
+    // exact in fp16 on the way)
     const f16x2 c1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
+    const float f = !k_ok ? 0.f : bad ? kf_nan : r.ks * scale2;
     uint32_t kf[8];
     const uint32_t kw[4] = {r.k.x, r.k.y, r.k.z, r.k.w};
     for (int i = 0; i < 4; i++) {
       uint32_t lo, hi;
       i8x4_to_f16_biased(kw[i], lo, hi);
-      kf[2 * i] = as_u32(as_f16x2(lo) - c1152);
-      kf[2 * i + 1] = as_u32(as_f16x2(hi) - c1152);
+      kf[2 * i] = f16x2_scaled(as_u32(as_f16x2(lo) - c1152), f);
+      kf[2 * i + 1] = f16x2_scaled(as_u32(as_f16x2(hi) - c1152), f);
     }
     _Float16 *kd = lk + cl * kKRow + 16 * (u & 15);
     *reinterpret_cast<u32x4 *>(kd) = u32x4{kf[0], kf[1], kf[2], kf[3]};
     *reinterpret_cast<u32x4 *>(kd + 8) = u32x4{kf[4], kf[5], kf[6], kf[7]};
   } else {
-    // q4_0 K -> (code - 8) * d16: elements 8hh .. 8hh + 7 (low nibbles) and
-    // 16 + 8hh .. (high nibbles) of block b
+    // q4_0 K -> (code - 8) * d16 * scale2: elements 8hh .. 8hh + 7 (low
+    // nibbles) and 16 + 8hh .. (high nibbles) of block b (code - 8 is exact
+    // in fp16 on the way)
     const int b = (u & 15) >> 1, hh = u & 1;
-    const uint32_t d16 = k_ok ? (r.k.z & 0xFFFFu) : 0u;
-    const f16x2 d = as_f16x2(d16 | (d16 << 16));
+    const float f = !k_ok ? 0.f : bad ? kf_nan : f16_bits_to_f32((uint16_t)(r.k.z & 0xFFFFu)) * scale2;
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
     uint32_t lo[4], hi[4];
-    q4_word_to_f16(r.k.x, d, lo, hi);
-    q4_word_to_f16(r.k.y, d, lo + 2, hi + 2);
+    q4_word_to_f16(r.k.x, one, lo, hi);
+    q4_word_to_f16(r.k.y, one, lo + 2, hi + 2);
+    for (int e = 0; e < 4; e++) {
+      lo[e] = f16x2_scaled(lo[e], f);
+      hi[e] = f16x2_scaled(hi[e], f);
+    }
     _Float16 *kd = lk + cl * kKRow + 32 * b + 8 * hh;
     *reinterpret_cast<u32x4 *>(kd) = u32x4{lo[0], lo[1], lo[2], lo[3]};
     *reinterpret_cast<u32x4 *>(kd + 16) = u32x4{hi[0], hi[1], hi[2], hi[3]};
@@ -313,17 +330,6 @@ __device__ __forceinline__ void pf_store(const PfRaw &r, int tid, int c0, int n_
   }
 }
 
-// K scale slot tid (< 64) of the tile at c0: cell tid / 2, group tid % 2,
-// times softmax scale x log2 e; 0 past n_cells, NaN in a half whose
-// page-table entry is out of range
-template <int FMT>
-__device__ __forceinline__ float pf_scale(const PfRaw &r, int tid, int c0, int n_cells, int bad, float scale2) {
-  const int cs = tid >> 1;
-  const float sc = FMT == KV_FMT_INT8 || FMT == KV_FMT_K8V4 ? scale2 * r.ks : scale2;
-  const float kd = ((bad >> (cs >> 4)) & 1) ? __builtin_nanf("") : sc;
-  return c0 + cs < n_cells ? kd : 0.f;
-}
-
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
@@ -345,20 +351,17 @@ __global__ __launch_bounds__(256) void prefill_stage_kernel(const PrefillArgs a)
   const int c0 = t * kPfTile, n_cells = a.pos0 + a.n_new;
   const PfHalves hv = pf_halves(a, g, c0, n_cells);
   PfRaw r0, r1;
-  pf_load<FMT, 0, true>(a, hv, tid, r0);
-  pf_load<FMT, 1, false>(a, hv, tid, r1);
+  pf_load<FMT, 0>(a, hv, tid, r0);
+  pf_load<FMT, 1>(a, hv, tid, r1);
   uint8_t *im = a.img + ((size_t)g * a.n_tiles + t) * kPfImageBytes;
   _Float16 *lk = reinterpret_cast<_Float16 *>(im), *lv = lk + kKElems;
-  pf_store<FMT, 0>(r0, tid, c0, n_cells, lk, lv);
-  pf_store<FMT, 1>(r1, tid, c0, n_cells, lk, lv);
-  if (tid < 2 * kPfTile)
-    reinterpret_cast<float *>(im + kImgKV)[tid] = pf_scale<FMT>(r0, tid, c0, n_cells, hv.bad, a.scale2);
+  pf_store<FMT, 0>(r0, tid, c0, n_cells, hv.bad & 1, a.scale2, lk, lv);
+  pf_store<FMT, 1>(r1, tid, c0, n_cells, (hv.bad >> 1) & 1, a.scale2, lk, lv);
 }
 
 template <bool QF32, int FMT>
 __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const PrefillArgs a) {
   constexpr int kPos = kPfWaves * 32 / kGqa;          // query positions per workgroup
-  constexpr int NG = (FMT == KV_FMT_INT8 || FMT == KV_FMT_K8V4) ? 2 : 1;  // K scale groups
   constexpr bool kRotV = FMT == KV_FMT_Q4_0 || FMT == KV_FMT_K8V4;
   __shared__ __attribute__((aligned(16))) uint8_t lds_img[4 * kPfImageBytes];
 
@@ -440,7 +443,6 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
     for (int e = 0; e < 16; e++) o[jd][e] = 0.f;
 
   auto kbuf = [&](int b) { return reinterpret_cast<const _Float16 *>(lds_img + b * kPfImageBytes); };
-  auto sbuf = [&](int b) { return reinterpret_cast<const float *>(lds_img + b * kPfImageBytes + kImgKV); };
   // Copy tile t's image into buffer b: 1 KB per wave and instruction straight
   // into LDS (lane l's 16 bytes land at 16 l), no registers; chunk r of a
   // wave is the image's KB 4 r + wave (37 KB: rounds 0 .. 8 for every wave,
@@ -467,33 +469,20 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
   static_assert(kCopyRounds == 10, "the wait below counts a step's copies");
   auto older_copies_done = [] { asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); };
   // S^T = K.Q^T of the tile in buffer b: its 16 K operands, then 16 (fp32
-  // queries: 32) MFMAs
+  // queries: 32) MFMAs.  The image's K carries the softmax scale (times
+  // log2 e), so these are the base-2 scores.  This lane's scores are row
+  // col, cells 8 (e / 4) + 4 h + e % 4 of a tile (element e of the 32 x 32
+  // accumulator).
   auto k_operands = [&](int b, f16x8 (&kop)[16]) {
     const _Float16 *kr = kbuf(b) + col * kKRow + 8 * h;
     for (int kk = 0; kk < 16; kk++) kop[kk] = *reinterpret_cast<const f16x8 *>(kr + 16 * kk);
   };
-  auto qk = [&](const f16x8 (&kop)[16], f32x16 (&acc)[NG]) {
-    for (int gg = 0; gg < NG; gg++)
-      for (int e = 0; e < 16; e++) acc[gg][e] = 0.f;
+  auto qk = [&](const f16x8 (&kop)[16], f32x16 &acc) {
+    for (int e = 0; e < 16; e++) acc[e] = 0.f;
     for (int kk = 0; kk < 16; kk++) {
-      const int gg = NG == 2 ? (kk >> 3) : 0;
-      acc[gg] = mfma32(kop[kk], qop[kk], acc[gg]);
-      if (QF32) acc[gg] = mfma32(kop[kk], qlo[kk], acc[gg]);
+      acc = mfma32(kop[kk], qop[kk], acc);
+      if (QF32) acc = mfma32(kop[kk], qlo[kk], acc);
     }
-  };
-
-  // This lane's scores are row col, cells 8 (e / 4) + 4 h + e % 4 of a tile
-  // (element e of the 32 x 32 accumulator).  Their K scales (times softmax
-  // scale x log2 e) are [cell][group] pairs in the image: quad
-  // dks[2 (e / 4) + (e % 4) / 2], entries 2 (e % 2) and 2 (e % 2) + 1.
-  auto read_scale = [&](int b, int i) {
-    return *reinterpret_cast<const f32x4 *>(&sbuf(b)[(8 * (i >> 1) + 4 * h) * 2 + 4 * (i & 1)]);
-  };
-  auto scale_one = [&](const f32x4 (&dks)[8], const f32x16 (&acc)[NG], int e) {
-    const f32x4 &d = dks[2 * (e >> 2) + ((e & 3) >> 1)];
-    float v = d[2 * (e & 1)] * acc[0][e];
-    if constexpr (NG == 2) v += d[2 * (e & 1) + 1] * acc[1][e];
-    return v;
   };
   // tile u's cells past a row's position (and every cell of an invalid row)
   // to -inf -- needed from the first tile some row does not see whole on;
@@ -539,30 +528,24 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
     // K operand i: dims 16 i + 8 h .. of cell col (tile t + 1); V operand
     // i = 8 st + jd: dim 32 jd + col, the lane half's 8 cells of k-step st
     f16x8 kop[16], vop[16];
-    f32x4 dks[8];
     const _Float16 *kr = kbuf(b1) + col * kKRow + 8 * h;
     const _Float16 *lv = kbuf(b0) + kKElems + 8 * h;
     auto rd_k = [&](int i) { kop[i] = *reinterpret_cast<const f16x8 *>(kr + 16 * i); };
     auto rd_v = [&](int i) {
       vop[i] = *reinterpret_cast<const f16x8 *>(lv + v_row(32 * (i & 7) + col) + 16 * (i >> 3));
     };
-    // QK order: the two 128-dim groups alternate (independent MFMAs back to back)
-    auto kk_of = [](int i) { return NG == 2 ? (i >> 1) + 8 * (i & 1) : i; };
-    f32x16 acc[NG];
-    for (int gg = 0; gg < NG; gg++)
-      for (int e = 0; e < 16; e++) acc[gg][e] = 0.f;
+    f32x16 acc;
+    for (int e = 0; e < 16; e++) acc[e] = 0.f;
     f16x8 pop[2];
     float ps = 0.f;
-    for (int i = 0; i < 8; i++) rd_k(kk_of(i));
+    for (int i = 0; i < 8; i++) rd_k(i);
     __builtin_amdgcn_sched_barrier(0);
     // the next tile's scores; this tile's probabilities
     for (int i = 0; i < 16; i++) {
-      const int kk = kk_of(i), gg = NG == 2 ? (kk >> 3) : 0;
-      acc[gg] = mfma32(kop[kk], qop[kk], acc[gg]);
-      if (QF32) acc[gg] = mfma32(kop[kk], qlo[kk], acc[gg]);
-      if (i + 8 < 16) rd_k(kk_of(i + 8));
+      acc = mfma32(kop[i], qop[i], acc);
+      if (QF32) acc = mfma32(kop[i], qlo[i], acc);
+      if (i + 8 < 16) rd_k(i + 8);
       else rd_v(i - 8);
-      if (i < 8) dks[i] = read_scale(b1, i);
       if (i < kCopyRounds) copy_chunk(b3, t + 3, i);  // tile t + 3, one KB per wave
       const float p = __builtin_amdgcn_exp2f(cur[i] - m);
       ps += p;
@@ -570,11 +553,11 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
       __builtin_amdgcn_sched_barrier(0);
     }
     lsum += ps;
-    // this tile's O += P.V; the next tile's scaled scores
+    // this tile's O += P.V
     for (int i = 0; i < 16; i++) {
       o[i & 7] = mfma32(pop[i >> 3], vop[i], o[i & 7]);
       if (i + 8 < 16) rd_v(i + 8);
-      nxt[i] = scale_one(dks, acc, i);
+      nxt[i] = acc[i];
       __builtin_amdgcn_sched_barrier(0);
     }
     mx_nxt = mask_and_max(t + 1, t + 1 >= n_full, nxt);
@@ -594,12 +577,10 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
   float sa[16], sb[16], mxa, mxb;
   {
     f16x8 kop[16];
-    f32x16 acc[NG];
-    f32x4 dks[8];
+    f32x16 acc;
     k_operands(0, kop);
     qk(kop, acc);
-    for (int i = 0; i < 8; i++) dks[i] = read_scale(0, i);
-    for (int e = 0; e < 16; e++) sa[e] = scale_one(dks, acc, e);
+    for (int e = 0; e < 16; e++) sa[e] = acc[e];
     mxa = mask_and_max(0, 0 >= n_full, sa);
   }
   int b0 = 0;
