@@ -362,9 +362,8 @@ int attn_prefill_chunk(const kv_pool *pool, const kv_seq *seq, const void *q, in
                        void *ws, size_t ws_bytes, void *stream);
 
 /* Workspace bytes of attn_prefill_chunk over n_cells = pos0 + n_new cells:
- * n_kv_heads * ceil(n_cells / 32) tile images of 37,888 bytes (fp16 K,
- * scaled, and transposed V of 32 cells with their row padding, padded to a
- * whole KB).
+ * n_kv_heads * ceil(n_cells / 32) tile images of 32,768 bytes (fp16 K,
+ * scaled, and fp16 V of 32 cells, in 16-byte chunks).
  * 0 for a NULL pool or n_cells < 1. */
 size_t attn_prefill_workspace_bytes(const kv_pool *pool, int32_t n_cells);
 

@@ -21,10 +21,10 @@
 //     otherwise each repeat, and its scores need no scaling;
 //   * attention: workgroup = 4 waves, one per SIMD, each owning 32 query
 //     rows (4 positions x 8 GQA heads of one KV head; fp32 queries add an
-//     MFMA on the fp16 rounding remainder), 128 rows per workgroup.  Four
-//     LDS image buffers: tile t + 3 is copied in with direct global-to-LDS
-//     loads (no registers, no VALU) while tile t's P.V and tile t + 1's
-//     Q.K^T run; one barrier per tile;
+//     MFMA on the fp16 rounding remainder), 128 rows per workgroup.  Five
+//     32 KB LDS image buffers (the whole LDS): tile t + 3 is copied in with
+//     direct global-to-LDS loads (no registers, no VALU) while tile t's P.V
+//     and tile t + 1's Q.K^T run; one barrier per two tiles;
 //   * S^T = K.Q^T puts a lane's query row in the column the P.V A-operand
 //     needs, so P never leaves registers; online softmax in base 2 against a
 //     lazily moved reference max; the causal mask only from the first tile
@@ -40,25 +40,29 @@ namespace k8v4 {
 
 constexpr int kPfWaves = 4;
 constexpr int kPfTile = 32;                   // cells per tile
-constexpr int kKRow = 256 + 8;                // fp16 elements per K row in LDS (bank spread)
-constexpr int kVRow = kPfTile + 8;            // fp16 elements per transposed V row (one dim)
-constexpr int kVBlockPad = 16;                // fp16 elements after every 32 dims
+constexpr int kPfBufs = 5;                    // LDS tile buffers of the attention kernel
 constexpr float kPfLazy = 8.0f;               // log2 headroom of the lazy softmax reference
 
-// offset of dim d's row in the V tile
-__device__ __forceinline__ int v_row(int d) { return d * kVRow + (d >> 5) * kVBlockPad; }
-// position of cell c (0..31) within a V row: the P.V B-operand of k-step s,
+// position of cell c (0..31) in the V order: the P.V B-operand of k-step s,
 // lane half h takes cells 16 s + 8 a + 4 h + b (a in {0, 1}, b in 0..3) --
 // the cells of that lane's scores -- stored side by side at 16 s + 8 h + 4 a
 // + b (bits 2 and 3 of c swapped), so one 16-byte read fetches them
 __device__ __forceinline__ int v_pos(int c) { return (c & 19) | ((c & 4) << 1) | ((c & 8) >> 1); }
 
-// A staged tile: K [32 cells][kKRow] fp16, V [256 dims][v_pos] fp16 with a
-// pad after every 32 dims, the whole padded to a multiple of 1 KB -- the LDS
-// image the attention kernel computes from, copied there unchanged.
-constexpr int kKElems = kPfTile * kKRow, kVElems = 256 * kVRow + 8 * kVBlockPad;
-constexpr int kImgKV = 2 * (kKElems + kVElems);     // bytes of K and V
-constexpr int kPfImageBytes = (kImgKV + 1023) & ~1023;
+// A staged tile (the LDS image the attention kernel computes from, copied
+// there unchanged), fp16, in 16-byte chunks of 8 elements:
+//   K: chunk (j, c) = dims 8 j .. 8 j + 7 of cell c, at chunk 32 j + c;
+//   V: chunk (j, d) = dim d of the cells at V positions 8 j .. 8 j + 7, at
+//      chunk 256 j + d.
+// An operand read (16 bytes per lane) then has the 16 lanes of each LDS pass
+// on 16 consecutive chunks -- every bank once, with no padding -- and the
+// operands of a tile lie at fixed offsets from a lane's first one.
+__device__ __forceinline__ int k_off(int c, int d) { return ((d >> 3) * kPfTile + c) * 8 + (d & 7); }
+// V element of dim d at V position p, and of dim d and cell c
+__device__ __forceinline__ int v_off_pos(int d, int p) { return ((p >> 3) * 256 + d) * 8 + (p & 7); }
+__device__ __forceinline__ int v_off(int d, int c) { return v_off_pos(d, v_pos(c)); }
+constexpr int kKElems = kPfTile * 256, kVElems = 256 * kPfTile;
+constexpr int kPfImageBytes = 2 * (kKElems + kVElems);  // 32 KB
 static_assert(kPfImageBytes % 1024 == 0, "whole 1 KB copy units");
 
 struct PrefillArgs {
@@ -224,8 +228,8 @@ __device__ __forceinline__ uint32_t f16x2_scaled(uint32_t w, float f) {
   return as_u32(y);
 }
 
-// Dequantize work unit u of the tile at c0 into its tile image (K
-// [cell][dim] times softmax scale x log2 e, V [dim][v_pos(cell)]).  Cells
+// Dequantize work unit u of the tile at c0 into its tile image (K times
+// softmax scale x log2 e at k_off, V at v_off).  Cells
 // at or past n_cells store zero K and V; the K of a half whose page-table
 // entry is out of range (bad) is NaN, so rows that reach it return NaN and
 // rows that stop before it mask it.
@@ -237,16 +241,15 @@ __device__ __forceinline__ void pf_store(const PfRaw &r, int tid, int c0, int n_
   const bool k_ok = c0 + cl < n_cells;
   const float kf_nan = __builtin_nanf("");
   if (FMT == KV_FMT_F16) {
-    // K row-major [cell][dim]; V transposed [dim][cell]: chunk (uu, lq, nn)
+    // K: dims 16 (u % 16) .. + 15 of cell u / 16; V: chunk (uu, lq, nn)
     // holds dims 16 nn + 2 uu (+1) of cells 4 lq .. 4 lq + 3 of its half,
-    // which sit side by side in a V row (v_pos)
+    // which sit side by side in a V chunk (v_pos)
     const float f = !k_ok ? 0.f : bad ? kf_nan : scale2;
     const uint32_t kw[8] = {r.k.x, r.k.y, r.k.z, r.k.w, r.k2.x, r.k2.y, r.k2.z, r.k2.w};
     uint32_t kf[8];
     for (int e = 0; e < 8; e++) kf[e] = f16x2_scaled(kw[e], f);
-    _Float16 *kd = lk + cl * kKRow + 16 * (u & 15);
-    *reinterpret_cast<u32x4 *>(kd) = u32x4{kf[0], kf[1], kf[2], kf[3]};
-    *reinterpret_cast<u32x4 *>(kd + 8) = u32x4{kf[4], kf[5], kf[6], kf[7]};
+    *reinterpret_cast<u32x4 *>(lk + k_off(cl, 16 * (u & 15))) = u32x4{kf[0], kf[1], kf[2], kf[3]};
+    *reinterpret_cast<u32x4 *>(lk + k_off(cl, 16 * (u & 15) + 8)) = u32x4{kf[4], kf[5], kf[6], kf[7]};
     const int vh = u >> 8, idx = u & 255;
     const int uu = idx >> 5, lq = (idx >> 3) & 3;
     const int cq = c0 + 16 * vh + 4 * lq;
@@ -254,15 +257,14 @@ __device__ __forceinline__ void pf_store(const PfRaw &r, int tid, int c0, int n_
     const uint32_t m23 = (cq + 2 < n_cells ? 0x0000ffffu : 0u) | (cq + 3 < n_cells ? 0xffff0000u : 0u);
     for (int q = 0; q < 2; q++) {
       const int d = 16 * (2 * (idx & 7) + q) + 2 * uu;
-      _Float16 *vd = lv + v_row(d) + v_pos(16 * vh + 4 * lq);
-      *reinterpret_cast<u32x2 *>(vd) = u32x2{r.v16[q].x & m01, r.v16[q].y & m23};
-      *reinterpret_cast<u32x2 *>(vd + kVRow) = u32x2{r.v16[q].z & m01, r.v16[q].w & m23};
+      *reinterpret_cast<u32x2 *>(lv + v_off(d, 16 * vh + 4 * lq)) = u32x2{r.v16[q].x & m01, r.v16[q].y & m23};
+      *reinterpret_cast<u32x2 *>(lv + v_off(d + 1, 16 * vh + 4 * lq)) = u32x2{r.v16[q].z & m01, r.v16[q].w & m23};
     }
     return;
   }
   if (FMT != KV_FMT_Q4_0) {
-    // INT8 K -> code * scale * scale2, row-major [cell][dim] (the codes are
-    // exact in fp16 on the way)
+    // INT8 K -> code * scale * scale2 (the codes are exact in fp16 on the
+    // way): dims 16 (u % 16) .. + 15 of cell u / 16
     const f16x2 c1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
     const float f = !k_ok ? 0.f : bad ? kf_nan : r.ks * scale2;
     uint32_t kf[8];
@@ -273,9 +275,8 @@ __device__ __forceinline__ void pf_store(const PfRaw &r, int tid, int c0, int n_
       kf[2 * i] = f16x2_scaled(as_u32(as_f16x2(lo) - c1152), f);
       kf[2 * i + 1] = f16x2_scaled(as_u32(as_f16x2(hi) - c1152), f);
     }
-    _Float16 *kd = lk + cl * kKRow + 16 * (u & 15);
-    *reinterpret_cast<u32x4 *>(kd) = u32x4{kf[0], kf[1], kf[2], kf[3]};
-    *reinterpret_cast<u32x4 *>(kd + 8) = u32x4{kf[4], kf[5], kf[6], kf[7]};
+    *reinterpret_cast<u32x4 *>(lk + k_off(cl, 16 * (u & 15))) = u32x4{kf[0], kf[1], kf[2], kf[3]};
+    *reinterpret_cast<u32x4 *>(lk + k_off(cl, 16 * (u & 15) + 8)) = u32x4{kf[4], kf[5], kf[6], kf[7]};
   } else {
     // q4_0 K -> (code - 8) * d16 * scale2: elements 8hh .. 8hh + 7 (low
     // nibbles) and 16 + 8hh .. (high nibbles) of block b (code - 8 is exact
@@ -290,9 +291,8 @@ __device__ __forceinline__ void pf_store(const PfRaw &r, int tid, int c0, int n_
       lo[e] = f16x2_scaled(lo[e], f);
       hi[e] = f16x2_scaled(hi[e], f);
     }
-    _Float16 *kd = lk + cl * kKRow + 32 * b + 8 * hh;
-    *reinterpret_cast<u32x4 *>(kd) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-    *reinterpret_cast<u32x4 *>(kd + 16) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    *reinterpret_cast<u32x4 *>(lk + k_off(cl, 32 * b + 8 * hh)) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    *reinterpret_cast<u32x4 *>(lk + k_off(cl, 32 * b + 16 + 8 * hh)) = u32x4{hi[0], hi[1], hi[2], hi[3]};
   }
   const int cp = 8 * HF + (i & 7);  // cells 2 cp, 2 cp + 1 of the tile
   const bool ok_a = c0 + 2 * cp < n_cells, ok_b = c0 + 2 * cp + 1 < n_cells;
@@ -304,7 +304,6 @@ __device__ __forceinline__ void pf_store(const PfRaw &r, int tid, int c0, int n_
     const f16x2 c72 = {(_Float16)72.0f, (_Float16)72.0f};
     const int b = (i >> 3) & 7, qq = i >> 6;
     const f16x2 dd = as_f16x2(r.vd & ((ok_a ? 0x0000FFFFu : 0u) | (ok_b ? 0xFFFF0000u : 0u)));
-    _Float16 *vb = lv + v_row(32 * b + 4 * qq) + v_pos(2 * cp);  // element 4qq of block b
     for (int e = 0; e < 4; e++) {
       // [a.byte, 0, b.byte, 0] for byte e of each cell: elements 4qq + e
       // (low nibbles) and 16 + 4qq + e (high nibbles)
@@ -312,20 +311,19 @@ __device__ __forceinline__ void pf_store(const PfRaw &r, int tid, int c0, int n_
       const uint32_t x = perm(r.vb.x, r.va.x, sel);
       const uint32_t lo = as_u32((as_f16x2(and_or(x, 0x000F000Fu, 0x64006400u)) - c1032) * dd);
       const uint32_t hi = as_u32((as_f16x2(and_or(x, 0x00F000F0u, 0x54005400u)) - c72) * dd);
-      *reinterpret_cast<uint32_t *>(vb + e * kVRow) = lo;
-      *reinterpret_cast<uint32_t *>(vb + (16 + e) * kVRow) = hi;
+      *reinterpret_cast<uint32_t *>(lv + v_off(32 * b + 4 * qq + e, 2 * cp)) = lo;
+      *reinterpret_cast<uint32_t *>(lv + v_off(32 * b + 16 + 4 * qq + e, 2 * cp)) = hi;
     }
   } else {
     // INT8 V -> code * d rounded to fp16, transposed [dim][cell]
     const int dg = (i >> 3) & 31;
     const float sa = ok_a ? r.vsa : 0.f, sb = ok_b ? r.vsb : 0.f;
-    _Float16 *vb = lv + v_row(8 * dg) + v_pos(2 * cp);
     const uint32_t wa[2] = {r.va.x, r.va.y}, wb[2] = {r.vb.x, r.vb.y};
     for (int e = 0; e < 8; e++) {
       const float xa = (float)(int8_t)(wa[e >> 2] >> (8 * (e & 3))) * sa;
       const float xb = (float)(int8_t)(wb[e >> 2] >> (8 * (e & 3))) * sb;
       const f16x2 pr = {(_Float16)xa, (_Float16)xb};
-      *reinterpret_cast<uint32_t *>(vb + e * kVRow) = as_u32(pr);
+      *reinterpret_cast<uint32_t *>(lv + v_off(8 * dg + e, 2 * cp)) = as_u32(pr);
     }
   }
 }
@@ -363,7 +361,7 @@ template <bool QF32, int FMT>
 __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const PrefillArgs a) {
   constexpr int kPos = kPfWaves * 32 / kGqa;          // query positions per workgroup
   constexpr bool kRotV = FMT == KV_FMT_Q4_0 || FMT == KV_FMT_K8V4;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_img[4 * kPfImageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_img[kPfBufs * kPfImageBytes];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -445,18 +443,16 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
   auto kbuf = [&](int b) { return reinterpret_cast<const _Float16 *>(lds_img + b * kPfImageBytes); };
   // Copy tile t's image into buffer b: 1 KB per wave and instruction straight
   // into LDS (lane l's 16 bytes land at 16 l), no registers; chunk r of a
-  // wave is the image's KB 4 r + wave (37 KB: rounds 0 .. 8 for every wave,
-  // round 9 for wave 0).  A tile past the staged ones (a pair's second tile,
-  // masked out whole) copies the last one.
+  // wave is the image's KB 4 r + wave (32 KB: 8 rounds).  A tile past the
+  // staged ones (a pair's second tile, masked out whole) copies the last one.
+  constexpr int kCopyRounds = kPfImageBytes / 1024 / kPfWaves;
+  static_assert(kCopyRounds * kPfWaves * 1024 == kPfImageBytes, "whole rounds");
   const uint8_t *img_head = a.img + (size_t)g * a.n_tiles * kPfImageBytes + wave * 1024 + lane * 16;
-  constexpr int kCopyRounds = (kPfImageBytes / 1024 + kPfWaves - 1) / kPfWaves;
   auto copy_chunk = [&](int b, int t, int r) {
-    if (r < kCopyRounds - 1 || r * kPfWaves + wave < kPfImageBytes / 1024) {
-      const uint8_t *src = img_head + (size_t)min(t, a.n_tiles - 1) * kPfImageBytes + r * kPfWaves * 1024;
-      uint8_t *dst = lds_img + b * kPfImageBytes + wave * 1024 + r * kPfWaves * 1024;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src),
-                                       (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
-    }
+    const uint8_t *src = img_head + (size_t)min(t, a.n_tiles - 1) * kPfImageBytes + r * kPfWaves * 1024;
+    uint8_t *dst = lds_img + b * kPfImageBytes + wave * 1024 + r * kPfWaves * 1024;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src),
+                                     (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
   };
   auto copy_tile = [&](int b, int t) {
     for (int r = 0; r < kCopyRounds; r++) copy_chunk(b, t, r);
@@ -464,18 +460,14 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
   // the copies issued so far have landed (each wave waits for its own; the
   // barrier that follows makes every wave's visible)
   auto copies_done = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
-  // every copy but this step's (a wave issues kCopyRounds = 10 or, past
-  // wave 0, 9 per step; vmcnt(9) leaves at most those outstanding)
-  static_assert(kCopyRounds == 10, "the wait below counts a step's copies");
-  auto older_copies_done = [] { asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); };
   // S^T = K.Q^T of the tile in buffer b: its 16 K operands, then 16 (fp32
   // queries: 32) MFMAs.  The image's K carries the softmax scale (times
   // log2 e), so these are the base-2 scores.  This lane's scores are row
   // col, cells 8 (e / 4) + 4 h + e % 4 of a tile (element e of the 32 x 32
   // accumulator).
   auto k_operands = [&](int b, f16x8 (&kop)[16]) {
-    const _Float16 *kr = kbuf(b) + col * kKRow + 8 * h;
-    for (int kk = 0; kk < 16; kk++) kop[kk] = *reinterpret_cast<const f16x8 *>(kr + 16 * kk);
+    const _Float16 *kr = kbuf(b) + k_off(col, 8 * h);
+    for (int kk = 0; kk < 16; kk++) kop[kk] = *reinterpret_cast<const f16x8 *>(kr + k_off(0, 16 * kk));
   };
   auto qk = [&](const f16x8 (&kop)[16], f32x16 &acc) {
     for (int e = 0; e < 16; e++) acc[e] = 0.f;
@@ -485,32 +477,42 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
     }
   };
   // tile u's cells past a row's position (and every cell of an invalid row)
-  // to -inf -- needed from the first tile some row does not see whole on;
-  // then the row max over the lane pair
-  auto mask_and_max = [&](int u, bool masked, float (&sc)[16]) {
-    if (masked)
-      for (int e = 0; e < 16; e++) {
-        const int cell = u * kPfTile + 8 * (e >> 2) + 4 * h + (e & 3);
-        sc[e] = (qvalid && cell <= qpos) ? sc[e] : -INFINITY;
-      }
+  // to -inf -- needed from the first tile some row does not see whole on
+  auto mask = [&](int u, float (&sc)[16]) {
+    for (int e = 0; e < 16; e++) {
+      const int cell = u * kPfTile + 8 * (e >> 2) + 4 * h + (e & 3);
+      sc[e] = (qvalid && cell <= qpos) ? sc[e] : -INFINITY;
+    }
+  };
+  auto lane_max = [](const float (&sc)[16]) {
     float mx = sc[0];
     for (int e = 1; e < 16; e++) mx = fmaxf(mx, sc[e]);
-    return fmaxf(mx, lane_xor<32>(mx));
+    return mx;
   };
+  // a row's max: the maxima of the lane pair that holds its scores
+  auto pair_max = [](float mx) { return fmaxf(mx, lane_xor<32>(mx)); };
 
   // One step of the pipeline, for tile t held in buffer b0 (the next tile in
   // b1), with this tile's masked scores in `cur` and their row max in mx_cur:
-  // the copy of tile t + 3 into b3 is issued (one chunk per section); the next tile's scores are
-  // computed (into `nxt`, mx_nxt) on the MFMAs while this tile's softmax runs
-  // on the VALU; then O += P.V.  The sections are hand-ordered (scheduling
-  // fences), each with one MFMA, the LDS read of an operand eight MFMAs ahead
-  // and a little VALU work: the compiler otherwise reads each operand just
-  // before its MFMA and waits out the LDS latency every time.
+  // the copy of tile t + 3 into b3 is issued (one chunk per section); the
+  // next tile's scores are computed (into `nxt`, mx_nxt) on the MFMAs while
+  // this tile's exponentials run on the VALU; then O += P.V, beside it this
+  // tile's row sum and the next tile's row max.  The sections are
+  // hand-ordered (scheduling fences), each with one MFMA, the LDS read of an
+  // operand eight MFMAs ahead and a little VALU work: the compiler otherwise
+  // reads each operand just before its MFMA and waits out the LDS latency
+  // every time, and gathers the sum and max chains after the last MFMA (an
+  // empty asm statement that takes them as inputs keeps each link in its
+  // section).  Tiles t .. t + 4 sit in five buffers, tile i in buffer i % 5.
+  // Steps run in pairs (t even, t + 1) with one barrier, after the pair, once
+  // each wave's copies have landed: the pair reads tiles t .. t + 2, all
+  // copied before the previous barrier, and writes tiles t + 3 and t + 4
+  // over tiles t - 2 and t - 1, last read before it.
   const int n_tiles = (n_cells + kPfTile - 1) / kPfTile;
   const int n_full = ((a.pos0 + qb0 + 1) / kPfTile) & ~1;  // tiles every row sees whole, even
   const int n_end = n_full + ((n_tiles - n_full + 1) & ~1);
   auto step = [&](int t, int b0, int b1, int b3, const float (&cur)[16], float mx_cur, float (&nxt)[16],
-                  float &mx_nxt) {
+                  float &mx_nxt, bool pair_end) {
     // the reference max moves (for every row, to at least its max) only when
     // some row's max exceeds it by more than 2^kPfLazy
     if (__any(mx_cur > m + kPfLazy)) {
@@ -528,16 +530,16 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
     // K operand i: dims 16 i + 8 h .. of cell col (tile t + 1); V operand
     // i = 8 st + jd: dim 32 jd + col, the lane half's 8 cells of k-step st
     f16x8 kop[16], vop[16];
-    const _Float16 *kr = kbuf(b1) + col * kKRow + 8 * h;
-    const _Float16 *lv = kbuf(b0) + kKElems + 8 * h;
-    auto rd_k = [&](int i) { kop[i] = *reinterpret_cast<const f16x8 *>(kr + 16 * i); };
+    const _Float16 *kr = kbuf(b1) + k_off(col, 8 * h);
+    const _Float16 *lv = kbuf(b0) + kKElems + v_off_pos(col, 8 * h);
+    auto rd_k = [&](int i) { kop[i] = *reinterpret_cast<const f16x8 *>(kr + k_off(0, 16 * i)); };
     auto rd_v = [&](int i) {
-      vop[i] = *reinterpret_cast<const f16x8 *>(lv + v_row(32 * (i & 7) + col) + 16 * (i >> 3));
+      vop[i] = *reinterpret_cast<const f16x8 *>(lv + v_off_pos(32 * (i & 7), 16 * (i >> 3)));
     };
     f32x16 acc;
     for (int e = 0; e < 16; e++) acc[e] = 0.f;
     f16x8 pop[2];
-    float ps = 0.f;
+    float pv[16];
     for (int i = 0; i < 8; i++) rd_k(i);
     __builtin_amdgcn_sched_barrier(0);
     // the next tile's scores; this tile's probabilities
@@ -547,25 +549,36 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
       if (i + 8 < 16) rd_k(i + 8);
       else rd_v(i - 8);
       if (i < kCopyRounds) copy_chunk(b3, t + 3, i);  // tile t + 3, one KB per wave
-      const float p = __builtin_amdgcn_exp2f(cur[i] - m);
-      ps += p;
-      pop[i >> 3][i & 7] = (_Float16)p;
+      pv[i] = __builtin_amdgcn_exp2f(cur[i] - m);
+      pop[i >> 3][i & 7] = (_Float16)pv[i];
       __builtin_amdgcn_sched_barrier(0);
     }
-    lsum += ps;
-    // this tile's O += P.V
+    // this tile's O += P.V; its row sum; the next tile's row max (unmasked;
+    // the scores are read two MFMAs after the last Q.K^T one was issued)
+    float ps = 0.f, mx = -INFINITY;
     for (int i = 0; i < 16; i++) {
       o[i & 7] = mfma32(pop[i >> 3], vop[i], o[i & 7]);
       if (i + 8 < 16) rd_v(i + 8);
+      ps += pv[i];
       nxt[i] = acc[i];
+      if (i >= 2) mx = fmaxf(mx, acc[i - 2]);
+      asm volatile("" ::"v"(ps), "v"(mx));
       __builtin_amdgcn_sched_barrier(0);
     }
-    mx_nxt = mask_and_max(t + 1, t + 1 >= n_full, nxt);
-    older_copies_done();
-    __syncthreads();
+    mx = fmaxf(mx, fmaxf(acc[14], acc[15]));
+    lsum += ps;
+    if (t + 1 >= n_full) {
+      mask(t + 1, nxt);
+      mx = lane_max(nxt);
+    }
+    mx_nxt = pair_max(mx);
+    if (pair_end) {
+      copies_done();
+      __syncthreads();
+    }
   };
 
-  // Prologue: tiles 0 and 1 copied, tile 0's scores computed.  The loop takes
+  // Prologue: tiles 0 .. 2 copied, tile 0's scores computed.  The loop takes
   // tiles in pairs (the score registers swap roles), past the visible cells
   // if need be (such a tile is masked out whole; its copy repeats the last
   // staged tile).
@@ -581,14 +594,13 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void attn_prefill_kernel(const Pr
     k_operands(0, kop);
     qk(kop, acc);
     for (int e = 0; e < 16; e++) sa[e] = acc[e];
-    mxa = mask_and_max(0, 0 >= n_full, sa);
+    if (0 >= n_full) mask(0, sa);
+    mxa = pair_max(lane_max(sa));
   }
-  int b0 = 0;
+  auto buf = [](int t) { return t % kPfBufs; };
   for (int t = 0; t < n_end; t += 2) {
-    step(t, b0, (b0 + 1) & 3, (b0 + 3) & 3, sa, mxa, sb, mxb);
-    b0 = (b0 + 1) & 3;
-    step(t + 1, b0, (b0 + 1) & 3, (b0 + 3) & 3, sb, mxb, sa, mxa);
-    b0 = (b0 + 1) & 3;
+    step(t, buf(t), buf(t + 1), buf(t + 3), sa, mxa, sb, mxb, false);
+    step(t + 1, buf(t + 1), buf(t + 2), buf(t + 4), sb, mxb, sa, mxa, true);
   }
 
   // ---------------- epilogue: O / l; the lane holds dim 32 jd + col of rows

@@ -107,10 +107,10 @@ def test_validation_errors_before_launch(k8):
     assert L.attn_verify(P(pool), P(seq), dummy, 0, 16, 3, None, 0.0, out, dummy, 1 << 20, None) == -1
     assert L.attn_prefill_chunk(P(pool), P(seq), dummy, 0, 16, 60, 5, 0.0, out, None, 0, None) == -3
     assert L.attn_prefill_chunk(P(pool), P(seq), dummy, 0, 16, 10, 0, 0.0, out, None, 0, None) == 0
-    # prefill workspace: one 37,888-byte tile image per 32 cells and KV head
+    # prefill workspace: one 32,768-byte tile image per 32 cells and KV head
     nb = L.attn_prefill_workspace_bytes(P(pool), 15)
-    assert nb == pool.n_kv_heads * 1 * 37888
-    assert L.attn_prefill_workspace_bytes(P(pool), 33) == pool.n_kv_heads * 2 * 37888
+    assert nb == pool.n_kv_heads * 1 * 32768
+    assert L.attn_prefill_workspace_bytes(P(pool), 33) == pool.n_kv_heads * 2 * 32768
     assert L.attn_prefill_workspace_bytes(P(pool), 0) == 0
     assert L.attn_prefill_workspace_bytes(None, 15) == 0
     assert L.attn_prefill_chunk(P(pool), P(seq), dummy, 0, 16, 10, 5, 0.0, out, None, 0, None) == -6
