@@ -168,6 +168,37 @@ def test_int8_small_values_decode_and_verify(orc, k8, dev, v_scale):
     assert max(e1, e2, e3) <= TOL
 
 
+@pytest.mark.parametrize("fmt", [FMT_K8V4, FMT_INT8, FMT_Q4_0, FMT_F16])
+@pytest.mark.parametrize("k_scale", [1e-3, 64.0])
+def test_k_magnitude_decode_verify_prefill(orc, k8, dev, fmt, k_scale):
+    """K ~ N(0, k_scale^2) and queries divided by k_scale, so the scores keep
+    their spread while K's magnitude moves: the prefill staging step rounds
+    K times the softmax scale (times log2 e) to fp16, where K of 1e-3 lands
+    partly in fp16's subnormal range, while decode and verify scale the
+    scores in fp32.  All three stay within the tolerance of the oracle."""
+    say(f"K magnitude fmt={fmt} k_scale={k_scale}")
+    P, n_pages, ctx = 16, 70, 1000
+    pt = synth.page_table(15, 63, n_pages)
+    gpt = t_(pt, dev)
+    k, v = synth.kv_tokens(15, 0, 0, ctx, 2, 256, np.float32)
+    k = (k * np.float32(k_scale)).astype(np.float32)
+    gpool = k8.KvPool(fmt, n_pages, P, 2, device=dev, fill=0)
+    opool = orc.OraclePool(fmt, n_pages, P, 2, sentinel=0)
+    k8.kv_append(gpool, gpt, t_(k, dev), t_(v, dev), 0)
+    opool.append(pt, k, v, 0)
+    q = (synth.queries(15, 0, 0, 3, 16, 256, np.float32) / np.float32(k_scale)).astype(np.float16)
+    ws = k8.attn_workspace(gpool, 3, ctx)
+    out = k8.attn_decode(gpool, gpt, t_(q[0], dev), ctx, ws).cpu().numpy()
+    e1 = rel_err(out, orc.attention_from_pool(opool, pt, q[:1], [ctx])[0])
+    nv = [ctx, 517, 33]
+    outv = k8.attn_verify(gpool, gpt, t_(q, dev), nv, ws).cpu().numpy()
+    e2 = rel_err(outv, orc.attention_from_pool(opool, pt, q, nv))
+    outp = k8.attn_prefill_chunk(gpool, gpt, t_(q, dev), ctx - 3).cpu().numpy()
+    e3 = rel_err(outp, orc.attention_from_pool(opool, pt, q, [ctx - 2, ctx - 1, ctx]))
+    say(f"  rel err decode {e1:.3e} verify {e2:.3e} prefill {e3:.3e}")
+    assert max(e1, e2, e3) <= TOL
+
+
 @pytest.mark.parametrize("fmt", [FMT_INT8, FMT_Q4_0, FMT_K8V4, FMT_F16])
 def test_arms_decode_32768_with_outlier_channels(orc, k8, dev, fmt):
     """The three formats on the same raw inputs: 32,768 cells, 3 outlier
