@@ -78,6 +78,17 @@ def event_mean_ms(torch, pairs):
     return sum(ts) / len(ts), ts
 
 
+def spread_us(ts):
+    """Median, 10th and 90th percentile (nearest rank) of per-launch times
+    given in ms, in us."""
+    s = sorted(ts)
+
+    def q(p):
+        return round(s[min(len(s) - 1, int(p * (len(s) - 1) + 0.5))] * 1e3, 3)
+
+    return {"launches": len(s), "median_us": q(0.5), "p10_us": q(0.1), "p90_us": q(0.9)}
+
+
 def timed_launches(torch, k8, fn, n):
     """Run fn() n times, each single kernel bracketed by start/stop events."""
     pairs = []
@@ -338,7 +349,7 @@ def main():
 
     # the decode kernel on its own: start/stop events around each launch
     log("per-kernel timing ...")
-    dec_ms, _ = timed_launches(torch, k8, lambda i: k8.attn_decode_append(
+    dec_ms, dec_ts = timed_launches(torch, k8, lambda i: k8.attn_decode_append(
         pools[i % layers], tables[i % layers], kv_new[0][i % layers][0][0], kv_new[0][i % layers][1][0],
         q_all[0][i % layers], ctx - 1, ws, out=outs[i % layers]), 2 * layers)
     app_ms, _ = timed_launches(torch, k8, lambda i: k8.kv_append_k8v4(
@@ -408,7 +419,7 @@ def main():
                      "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": ctx * CELL_BYTES, "traffic_bytes_per_launch": traffic_bytes,
-                     "mean_us": round(dec_ms * 1e3, 3),
+                     "mean_us": round(dec_ms * 1e3, 3), "spread": spread_us(dec_ts),
                      "append_mean_us": round(app_ms * 1e3, 3)},
         "cpu_baseline": cpu,
         "extra": extra,
@@ -508,12 +519,12 @@ def bench_extra(torch, k8, synth, dev, log):
     for i in range(n_pools):  # warm
         k8.attn_decode(pools[i], tables[i], q1, ctx, ws1)
         k8.attn_verify(pools[i], tables[i], q5, nv, ws5)
-    reps = 8 * n_pools
-    d_ms, _ = timed_launches(torch, k8, lambda i: k8.attn_decode(
+    reps = 9 * n_pools  # at least 50 launches over the pool rotation
+    d_ms, d_ts = timed_launches(torch, k8, lambda i: k8.attn_decode(
         pools[i % n_pools], tables[i % n_pools], q1, ctx, ws1), reps)
     dc_ms = graph_calls_ms(torch, lambda i: k8.attn_decode(
         pools[i % n_pools], tables[i % n_pools], q1, ctx, ws1), 2 * n_pools)
-    v_ms, _ = timed_launches(torch, k8, lambda i: k8.attn_verify(
+    v_ms, v_ts = timed_launches(torch, k8, lambda i: k8.attn_verify(
         pools[i % n_pools], tables[i % n_pools], q5, nv, ws5), reps)
     vc_ms = graph_calls_ms(torch, lambda i: k8.attn_verify(
         pools[i % n_pools], tables[i % n_pools], q5, nv, ws5), 2 * n_pools)
@@ -521,6 +532,7 @@ def bench_extra(torch, k8, synth, dev, log):
     out["decode_240000"] = {"us": round(d_ms * 1e3, 3), "gbs": round(b / d_ms / 1e6, 2),
                             "hbm_frac": round(b / d_ms / 1e6 / HBM_PEAK_GBS, 4),
                             "pools_rotated": n_pools, "kernel": "split kernel alone",
+                            "spread": spread_us(d_ts),
                             "us_split_plus_combine": round(dc_ms * 1e3, 3),
                             "hbm_frac_split_plus_combine": round(b / dc_ms / 1e6 / HBM_PEAK_GBS, 4)}
     # context sweep on the same pools: whole decode call (split + combine),
@@ -534,7 +546,7 @@ def bench_extra(torch, k8, synth, dev, log):
     out["decode_sweep_split_plus_combine"] = sweep
     out["verify5_240000"] = {"us": round(v_ms * 1e3, 3), "gbs": round(b / v_ms / 1e6, 2),
                              "hbm_frac": round(b / v_ms / 1e6 / HBM_PEAK_GBS, 4),
-                             "kernel": "split kernel alone",
+                             "kernel": "split kernel alone", "spread": spread_us(v_ts),
                              "us_split_plus_combine": round(vc_ms * 1e3, 3),
                              "hbm_frac_split_plus_combine": round(b / vc_ms / 1e6 / HBM_PEAK_GBS, 4),
                              "n_visible": nv}

@@ -47,3 +47,12 @@ def test_traffic_record_follows_the_kernel_source(tmp_path, monkeypatch):
     os.remove(tmp_path / "profiles" / "attn_splitk_decode_118750_traffic.json")
     assert bench.measured_traffic() is None
 
+
+
+def test_spread_is_nearest_rank_percentiles_in_us():
+    import bench
+    ts = [0.001 * i for i in range(1, 101)]  # 1 .. 100 us, in ms
+    sp = bench.spread_us(list(reversed(ts)))
+    assert sp == {"launches": 100, "median_us": 51.0, "p10_us": 11.0, "p90_us": 90.0}
+    one = bench.spread_us([0.02])
+    assert one["median_us"] == one["p10_us"] == one["p90_us"] == 20.0

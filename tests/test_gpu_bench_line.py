@@ -38,5 +38,7 @@ def test_bench_prints_one_consistent_json_line():
     assert 0 < rf["frac"] < 1 and rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"], rel=1e-3)
     # a decode launch cannot take longer than a layer's share of the step
     assert rf["mean_us"] * 48 <= d["ms_per_step"] * 1e3 * 1.3
+    sp = rf["spread"]
+    assert sp["launches"] == 96 and 0 < sp["p10_us"] <= sp["median_us"] <= sp["p90_us"]
     if rf["traffic"] is not None:
         assert rf["traffic_bytes_per_launch"] >= rf["bytes_per_launch"]
