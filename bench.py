@@ -192,8 +192,9 @@ def cpu_baseline():
     """The oracle on the host's cores, on bounded samples of the workloads:
     one 240,000-cell oracle pool built by appends of 8,192-token chunks
     (timed per chunk), then decode at 118,750 cells with 1 thread and with
-    the oracle's default thread count (the headline value), decode and the
-    5-query verify at 240,000 cells, and 32 sampled rows of the 8,192-query
+    the oracle's default thread count (the headline value), decode at the
+    sweep's other lengths (1,024 .. 131,072 cells), decode and the 5-query
+    verify at 240,000 cells, and 32 sampled rows of the 8,192-query
     prefill chunk at [231,808, 240,000) (first 8, last 8, 16 seeded others),
     extrapolated to the whole chunk.  Inputs follow the numpy stream of the
     same recipe."""
@@ -223,6 +224,9 @@ def cpu_baseline():
     d1 = timed(lambda: oracle.attention_from_pool(pool, pt, q1, [118750], threads=1))
     dn = timed(lambda: oracle.attention_from_pool(pool, pt, q1, [118750], threads=threads))
     d240 = timed(lambda: oracle.attention_from_pool(pool, pt, q1, [ctx], threads=threads))
+    # the decode context sweep's other lengths, same threads
+    sweep = {n: timed(lambda n=n: oracle.attention_from_pool(pool, pt, q1, [n], threads=threads))
+             for n in (1024, 4096, 16384, 32768, 65536, 131072)}
     q5 = synth.queries(4, 0, 1, 5, 16, 256, np.float16)
     v5 = timed(lambda: oracle.attention_from_pool(pool, pt, q5, [ctx - 4 + i for i in range(5)], threads=threads))
     pos0, n_new = 231808, 8192
@@ -244,6 +248,7 @@ def cpu_baseline():
              "append_tokens_per_s": round(synth.CHUNK / float(np.mean(app)), 1),
              "decode_118750_s": {"1_thread": round(d1, 3), f"{threads}_threads": round(dn, 3)},
              "decode_240000_s": round(d240, 3), "decode_240000_gbs": round(ctx * CELL_BYTES / d240 / 1e9, 4),
+             "decode_sweep_s": {str(n): round(t, 4) for n, t in sweep.items()},
              "verify5_240000_s": round(v5, 3),
              "prefill_32_sampled_rows_s": round(pf, 3),
              "prefill_8192_at_231808_s_extrapolated": round(pf * flops_all / flops_rows, 1),
