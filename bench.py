@@ -504,7 +504,8 @@ def profile_only(what, torch, k8, synth, dev):
 
 def bench_extra(torch, k8, synth, dev, log):
     """Decode and verify at 240,000 cells (6 rotated 262,144-cell pools,
-    1.28 GB, beyond the Infinity Cache) and the 8,192-query prefill chunk."""
+    1.28 GB, beyond the Infinity Cache), the 8,192-query prefill chunk and
+    the append of an 8,192-token chunk."""
     out = {}
     ctx, P, n_pages, n_pools = 240000, 256, 1024, 6
     n_table = (ctx + P - 1) // P
@@ -589,6 +590,18 @@ def bench_extra(torch, k8, synth, dev, log):
     out["prefill_8192_at_231808"] = {"ms": round(p_ms, 3), "tflops": round(flops / p_ms / 1e9, 2),
                                      "mfma_frac": round(flops / p_ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
                                      "flop": flops}
+    # append of one 8,192-token chunk (quantize K, rotate and quantize V,
+    # write the three runs): chunk 28 of each pool again, with the values it
+    # was filled with, so the pools keep their bytes
+    chunks = [synth.kv_chunk_device(4, i, 28, synth.CHUNK, 2, 256, dev) for i in range(n_pools)]
+    a_ms, a_ts = timed_launches(torch, k8, lambda i: k8.kv_append_k8v4(
+        pools[i % n_pools], tables[i % n_pools], chunks[i % n_pools][0], chunks[i % n_pools][1],
+        28 * synth.CHUNK), reps)
+    ab = synth.CHUNK * 2 * 256 * 2 * 2 + synth.CHUNK * CELL_BYTES  # fp16 K and V in, the cells out
+    out["append_8192_tokens"] = {"us": round(a_ms * 1e3, 3), "bytes": ab, "gbs": round(ab / a_ms / 1e6, 2),
+                                 "hbm_frac": round(ab / a_ms / 1e6 / HBM_PEAK_GBS, 4),
+                                 "spread": spread_us(a_ts)}
+    del chunks
     # the same chunk over the comparison formats (one 240,000-cell pool each)
     fm = {}
     for fmt, name in ((1, "int8"), (2, "q4_0"), (0, "fp16")):
