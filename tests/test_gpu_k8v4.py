@@ -366,6 +366,20 @@ def test_prefill_parity_tiny(orc, k8, dev, tiny, n_new, qdtype):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("pos0,n_new", [(0, 1), (0, 300), (37, 211), (993, 31)])
+def test_prefill_parity_unaligned_starts(orc, k8, dev, tiny, pos0, n_new):
+    """Chunks that start at the first cell (row 0 attends one cell, every
+    tile of the chunk is masked) or off the 16-query and 32-cell grids, so
+    a workgroup's rows straddle tiles and its last rows are past the chunk."""
+    say(f"prefill unaligned pos0={pos0} n_new={n_new}")
+    q = synth.queries(0, 0, 700 + pos0, n_new, 16, 256, np.float16)
+    out = k8.attn_prefill_chunk(tiny.gpool, tiny.gpt, t_(q, dev), pos0).cpu().numpy()
+    ref = tiny.oracle_attention(orc, q, [pos0 + i + 1 for i in range(n_new)])
+    err = rel_err(out, ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+
+
 def test_prefill_rows_match_verify(k8, dev, tiny):
     n_new, pos0 = 16, 1000
     q = synth.queries(0, 0, 9, n_new, 16, 256, np.float16)
