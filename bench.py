@@ -584,12 +584,12 @@ def bench_extra(torch, k8, synth, dev, log):
     k8.attn_prefill_chunk(pools[0], tables[0], qp, pos0, out=outp, ws=pws)
     # one call = the staging kernel (each 32-cell tile dequantized once per KV
     # head) and the attention kernel; the timing pair brackets both
-    p_ms, _ = timed_launches(torch, k8, lambda i: k8.attn_prefill_chunk(
-        pools[i % 2], tables[i % 2], qp, pos0, out=outp, ws=pws), 3)
+    p_ms, p_ts = timed_launches(torch, k8, lambda i: k8.attn_prefill_chunk(
+        pools[i % 2], tables[i % 2], qp, pos0, out=outp, ws=pws), 6)
     flops = sum(1024.0 * 16 * (pos0 + i + 1) for i in range(n_new))
     out["prefill_8192_at_231808"] = {"ms": round(p_ms, 3), "tflops": round(flops / p_ms / 1e9, 2),
                                      "mfma_frac": round(flops / p_ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
-                                     "flop": flops}
+                                     "flop": flops, "spread": spread_us(p_ts)}
     # append of one 8,192-token chunk (quantize K, rotate and quantize V,
     # write the three runs): chunk 28 of each pool again, with the values it
     # was filled with, so the pools keep their bytes
