@@ -620,6 +620,7 @@ def bench_extra(torch, k8, synth, dev, log):
     out["prefill_8192_formats"] = fm
     out["formats_32768"] = bench_formats_32768(torch, k8, synth, dev, log)
     out["decode_240000_fp16"] = bench_fp16_240000(torch, k8, synth, dev, log)
+    out["decode_240000_formats"] = bench_formats_240000(torch, k8, synth, dev, log)
     out["decode_1048576"] = bench_decode_1m(torch, k8, synth, dev, log)
     out["page_copy_k8v4"] = bench_page_copy(torch, k8, pools[0], tables[0], dev, log)
     log(f"extra: {json.dumps(out)}")
@@ -673,6 +674,42 @@ def bench_formats_32768(torch, k8, synth, dev, log):
         res[name] = {"us": round(ms * 1e3, 2), "mb_per_step": round(b / 1e6, 2),
                      "gbs": round(b / ms / 1e6, 1), "hbm_frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4),
                      "cell_bytes": cell}
+        del pools, tables
+        torch.cuda.empty_cache()
+    return res
+
+
+def bench_formats_240000(torch, k8, synth, dev, log):
+    """Decode at 240,000 cells over the int8 and q4_0 comparison formats (4
+    pools each, rotated beyond the Infinity Cache), timed like the k8v4
+    decode: split kernel alone (events) and the whole call (graph)."""
+    ctx, P, n_pages, n_pools = 240000, 256, 1024, 4
+    q = synth.queries_device(4, 0, 0, 1, 16, 256, dev)[0]
+    res = {}
+    for fmt, name in ((1, "int8"), (2, "q4_0")):
+        log(f"extra: filling {n_pools} {name} pools of {ctx} cells ...")
+        pools, tables = [], []
+        for i in range(n_pools):
+            pool = k8.KvPool(fmt, n_pages, P, 2, device=dev)
+            pt = make_table(torch, synth, 4, i, (ctx + P - 1) // P, n_pages, dev)
+            for c, s in enumerate(range(0, ctx, synth.CHUNK)):
+                kk, vv = synth.kv_chunk_device(4, i, c, min(synth.CHUNK, ctx - s), 2, 256, dev)
+                k8.kv_append(pool, pt, kk, vv, s)
+            pools.append(pool)
+            tables.append(pt)
+        ws = k8.attn_workspace(pools[0], 1, ctx)
+        for i in range(n_pools):
+            k8.attn_decode(pools[i], tables[i], q, ctx, ws)
+        ms, ts = timed_launches(torch, k8, lambda i: k8.attn_decode(
+            pools[i % n_pools], tables[i % n_pools], q, ctx, ws), 12 * n_pools)
+        wc = graph_calls_ms(torch, lambda i: k8.attn_decode(
+            pools[i % n_pools], tables[i % n_pools], q, ctx, ws), 2 * n_pools)
+        cell = int(k8.lib().kv_cell_bytes(fmt, 2, 256))
+        b = ctx * cell
+        res[name] = {"us": round(ms * 1e3, 3), "gbs": round(b / ms / 1e6, 2),
+                     "hbm_frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4), "spread": spread_us(ts),
+                     "us_split_plus_combine": round(wc * 1e3, 3), "cell_bytes": cell,
+                     "kernel": "split kernel alone"}
         del pools, tables
         torch.cuda.empty_cache()
     return res
