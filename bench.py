@@ -621,6 +621,7 @@ def bench_extra(torch, k8, synth, dev, log):
     out["formats_32768"] = bench_formats_32768(torch, k8, synth, dev, log)
     out["decode_240000_fp16"] = bench_fp16_240000(torch, k8, synth, dev, log)
     out["decode_240000_formats"] = bench_formats_240000(torch, k8, synth, dev, log)
+    out["decode_stream_240000"] = bench_stream_240000(torch, k8, synth, dev, log)
     out["decode_1048576"] = bench_decode_1m(torch, k8, synth, dev, log)
     out["page_copy_k8v4"] = bench_page_copy(torch, k8, pools[0], tables[0], dev, log)
     log(f"extra: {json.dumps(out)}")
@@ -675,6 +676,44 @@ def bench_formats_32768(torch, k8, synth, dev, log):
                      "gbs": round(b / ms / 1e6, 1), "hbm_frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4),
                      "cell_bytes": cell}
         del pools, tables
+        torch.cuda.empty_cache()
+    return res
+
+
+def bench_stream_240000(torch, k8, synth, dev, log):
+    """The streamed cache at 240,000 cells: a pinned host mirror holding every
+    page and a device window of the newest 128 pages (32,768 cells); the
+    streamed decode reads the window where a page is resident and the mirror
+    across the host link where not (whole call: the lookup kernel, the split
+    kernel and the combine, replayed from a graph).  Also a window of every
+    page (no misses): the streamed path's own cost against the resident
+    decode."""
+    ctx, P, n_mirror = 240000, 256, 1024
+    n_table = (ctx + P - 1) // P
+    mt = make_table(torch, synth, 4, 0, n_table, n_mirror, dev)
+    q = synth.queries_device(4, 0, 0, 1, 16, 256, dev)[0]
+    res = {}
+    for n_window in (128, n_mirror):
+        log(f"extra: streamed cache, window of {n_window} pages ...")
+        s = k8.KvStream(3, n_window, n_mirror, P, mt, fill=0)
+        for c, st in enumerate(range(0, ctx, synth.CHUNK)):
+            kk, vv = synth.kv_chunk_device(4, 0, c, min(synth.CHUNK, ctx - st), 2, 256, dev)
+            k8.kv_stream_append(s, kk, vv, st)
+        first = max(0, n_table - n_window)
+        k8.kv_stream_fetch(s, first, n_table - first)
+        ws = k8.attn_workspace(s.window, 1, ctx)
+        k8.attn_decode_stream(s, q, ctx, ws)
+        torch.cuda.synchronize()
+        s.stats.zero_()
+        reps = 4 if n_window < n_table else 16
+        ms = graph_calls_ms(torch, lambda i: k8.attn_decode_stream(s, q, ctx, ws), reps, replays=2)
+        lookups, misses = (x / (3 * reps) for x in s.stats.cpu().tolist())  # a warm-up and 2 timed replays
+        miss_bytes = misses * P * CELL_BYTES
+        res[f"window_{n_window}_pages"] = {
+            "us": round(ms * 1e3, 3), "lookups_per_call": lookups, "misses_per_call": misses,
+            "missed_bytes_per_call": int(miss_bytes),
+            "host_link_gbs_missed": round(miss_bytes / ms / 1e6, 2) if misses else None}
+        del s
         torch.cuda.empty_cache()
     return res
 

@@ -354,11 +354,6 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
   const __amdgpu_buffer_rsrc_t rks_ = __builtin_amdgcn_make_buffer_rsrc((void *)a.ks, (short)0, a.ks_bytes, kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rv_ = __builtin_amdgcn_make_buffer_rsrc((void *)a.vq, (short)0, a.v_bytes, kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rvs_ = __builtin_amdgcn_make_buffer_rsrc((void *)a.vs, (short)0, a.vs_bytes, kRsrcFlags);
-  // a streamed cache's mirror runs (mapped pinned host memory)
-  const __amdgpu_buffer_rsrc_t rkm = __builtin_amdgcn_make_buffer_rsrc((void *)a.m_kc, (short)0, STREAM ? a.k_bytes_m : 0, kRsrcFlags);
-  const __amdgpu_buffer_rsrc_t rksm = __builtin_amdgcn_make_buffer_rsrc((void *)a.m_ks, (short)0, STREAM ? a.ks_bytes_m : 0, kRsrcFlags);
-  const __amdgpu_buffer_rsrc_t rvm = __builtin_amdgcn_make_buffer_rsrc((void *)a.m_vq, (short)0, STREAM ? a.v_bytes_m : 0, kRsrcFlags);
-  const __amdgpu_buffer_rsrc_t rvsm = __builtin_amdgcn_make_buffer_rsrc((void *)a.m_vs, (short)0, STREAM ? a.vs_bytes_m : 0, kRsrcFlags);
   // the same runs with no records: a load through one returns zeros without
   // touching memory (the unconditional prefetch past a wave's last step)
   const __amdgpu_buffer_rsrc_t rk0 = __builtin_amdgcn_make_buffer_rsrc((void *)a.kc, (short)0, 0, kRsrcFlags);
@@ -387,6 +382,34 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
   const uint32_t q4_expo = (lg & 1) ? 0x54005400u : 0x64006400u;
   const int v8_grp = n >> 3;                     // INT8 V: scale group of this lane's dims
 
+  // The descriptor a half's loads use: its run's, the mirror's for a page
+  // of a streamed cache read from the host, or an empty one past the wave's
+  // last step.  The streamed variant builds it at each use from the base
+  // pointer and byte count (a few scalar instructions): its twelve live
+  // descriptors would exceed the scalar registers, and the compiler then
+  // keeps them in vector registers and scratch memory and wraps every load
+  // in a loop over the lanes.
+  auto desc = [&](const Half &h, const void *base, int bytes, const void *mbase, int mbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(h.host ? mbase : base), (short)0,
+                                             h.none ? 0 : (h.host ? mbytes : bytes), kRsrcFlags);
+  };
+  auto d_k = [&](const Half &h) {
+    if constexpr (STREAM) return desc(h, a.kc, a.k_bytes, a.m_kc, a.k_bytes_m);
+    else return h.none ? rk0 : rk_;
+  };
+  auto d_ks = [&](const Half &h) {
+    if constexpr (STREAM) return desc(h, a.ks, a.ks_bytes, a.m_ks, a.ks_bytes_m);
+    else return h.none ? rks0 : rks_;
+  };
+  auto d_v = [&](const Half &h) {
+    if constexpr (STREAM) return desc(h, a.vq, a.v_bytes, a.m_vq, a.v_bytes_m);
+    else return h.none ? rv0 : rv_;
+  };
+  auto d_vs = [&](const Half &h) {
+    if constexpr (STREAM) return desc(h, a.vs, a.vs_bytes, a.m_vs, a.vs_bytes_m);
+    else return h.none ? rvs0 : rvs_;
+  };
+
   u32x4 kr[2][kKLoads];
   f32x4 ksr[2][2];      // INT8 K scales
   uint32_t kdr[2][4];   // q4_0 K scales (fp16 bits)
@@ -397,13 +420,13 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
   f32x4 vsr[2][2];
   Half cur0, cur1, nxt0, nxt1;
   auto load_k = [&](int h2, const Half &h) {
-    const __amdgpu_buffer_rsrc_t rk = h.none ? rk0 : (STREAM && h.host ? rkm : rk_);
+    const __amdgpu_buffer_rsrc_t rk = d_k(h);
     for (int j = 0; j < kKLoads; j++)
       kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + kstep_j * j, h.k_soff, kAux);
   };
   auto load_ks = [&](int h2, const Half &h) {
-    const __amdgpu_buffer_rsrc_t rks = h.none ? rks0 : (STREAM && h.host ? rksm : rks_);
-    const __amdgpu_buffer_rsrc_t rk = h.none ? rk0 : (STREAM && h.host ? rkm : rk_);
+    const __amdgpu_buffer_rsrc_t rks = d_ks(h);
+    const __amdgpu_buffer_rsrc_t rk = d_k(h);
     if (kF16) {
       // no scales
     } else if (kInt8K) {
@@ -414,7 +437,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
     }
   };
   auto load_v = [&](int h2, const Half &h) {
-    const __amdgpu_buffer_rsrc_t rv = h.none ? rv0 : (STREAM && h.host ? rvm : rv_);
+    const __amdgpu_buffer_rsrc_t rv = d_v(h);
     if (kF16) {
       for (int u = 0; u < 8; u++) vr16[h2][u] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_voff + 1024 * u, h.v_soff, kAux);
     } else if (kQ4V) {
@@ -424,8 +447,8 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
     }
   };
   auto load_vd = [&](int h2, const Half &h) {
-    const __amdgpu_buffer_rsrc_t rvs = h.none ? rvs0 : (STREAM && h.host ? rvsm : rvs_);
-    const __amdgpu_buffer_rsrc_t rv = h.none ? rv0 : (STREAM && h.host ? rvm : rv_);
+    const __amdgpu_buffer_rsrc_t rvs = d_vs(h);
+    const __amdgpu_buffer_rsrc_t rv = d_v(h);
     if (kF16) {
       // no scales
     } else if (kQ4V) {
@@ -617,7 +640,15 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
       // masking (rows past rows_here then hold harmless values that are never
       // written out)
       const bool full_step = c + kStep <= lim_min && !(cur0.bad | cur1.bad);
+      // the next step's half h2: the streamed variant takes it through a
+      // select (with an array of pointers its halves went through scratch
+      // memory), the others through the array, which schedules the resident
+      // kernels better
       const Half *nx[2] = {&nxt0, &nxt1};
+      auto hx = [&](int h2) -> const Half & {
+        if constexpr (STREAM) return h2 ? nxt1 : nxt0;
+        else return *nx[h2];
+      };
 
       // ---- scores S^T = K . Q^T
       float s[T][8];
@@ -633,7 +664,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
               acc0[t] = mfma16x16x32(ka, qop[t][j], acc0[t]);
               if (QF32) acc0[t] = mfma16x16x32(ka, qlo[t][j], acc0[t]);
             }
-            kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(nx[h2]->none ? rk0 : (STREAM && nx[h2]->host ? rkm : rk_), k_voff + kstep_j * j, nx[h2]->k_soff, kAux);
+            kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(d_k(hx(h2)), k_voff + kstep_j * j, hx(h2).k_soff, kAux);
             continue;
           }
           if (kInt8K) {
@@ -678,7 +709,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
             }
           }
           // K chunk j of this half consumed: refill with the next step's
-          kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(nx[h2]->none ? rk0 : (STREAM && nx[h2]->host ? rkm : rk_), k_voff + kstep_j * j, nx[h2]->k_soff, kAux);
+          kr[h2][j] = __builtin_amdgcn_raw_buffer_load_b128(d_k(hx(h2)), k_voff + kstep_j * j, hx(h2).k_soff, kAux);
         }
         // several row tiles: the softmax scale folds into the cells' two K
         // group scales once, for all of them
@@ -708,7 +739,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
               s[t][4 * h2 + i] = badp[h2] ? __builtin_nanf("") : sv;
             }
         }
-        load_ks(h2, *nx[h2]);
+        load_ks(h2, hx(h2));
       }
 
       // ---- online softmax against a reference max m that only moves when
@@ -777,7 +808,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
           v8_tiny |= (da != 0.f && fabsf(da) < 6.103515625e-05f) || (db != 0.f && fabsf(db) < 6.103515625e-05f);
         }
       }
-      for (int h2 = 0; h2 < 2; h2++) load_vd(h2, *nx[h2]);
+      for (int h2 = 0; h2 < 2; h2++) load_vd(h2, hx(h2));
       if (kF16) {
         // fp16 V: one load holds the B operands of tiles 2u and 2u + 1.  The
         // values of cells past the split end are zeroed first: they may hold
@@ -801,7 +832,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
           const f16x8 bhi = pack8(v0.z, v0.w, v1.z, v1.w);  // tile 2u + 1: dim 16 n + 2 u + 1
           // chunk u of this step consumed: refill with the next step's
           for (int h2 = 0; h2 < 2; h2++)
-            vr16[h2][u] = __builtin_amdgcn_raw_buffer_load_b128(nx[h2]->none ? rv0 : (STREAM && nx[h2]->host ? rvm : rv_), v_voff + 1024 * u, nx[h2]->v_soff, kAux);
+            vr16[h2][u] = __builtin_amdgcn_raw_buffer_load_b128(d_v(hx(h2)), v_voff + 1024 * u, hx(h2).v_soff, kAux);
           for (int t = 0; t < T; t++) o[t][2 * u] = mfma16x16x32(pop[t], blo, o[t][2 * u]);
           for (int t = 0; t < T; t++) o[t][2 * u + 1] = mfma16x16x32(pop[t], bhi, o[t][2 * u + 1]);
         }
@@ -827,7 +858,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
           }
           if (grp == 3) {
             // every V byte of this step consumed: refill with the next step's
-            for (int h2 = 0; h2 < 2; h2++) load_v(h2, *nx[h2]);
+            for (int h2 = 0; h2 < 2; h2++) load_v(h2, hx(h2));
           }
           const int jb = 2 * grp;
           for (int t = 0; t < T; t++) o[t][jb] = mfma16x16x32(pop[t], pack8(b0[0], b0[1], b0[2], b0[3]), o[t][jb]);          // tile jb     (byte lo nibble)
@@ -853,7 +884,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
             }
           }
           if (j == 15) {
-            for (int h2 = 0; h2 < 2; h2++) load_v(h2, *nx[h2]);
+            for (int h2 = 0; h2 < 2; h2++) load_v(h2, hx(h2));
           }
           for (int t = 0; t < T; t++) o[t][j] = mfma16x16x32(pop[t], pack8(b[0], b[1], b[2], b[3]), o[t][j]);
         }
