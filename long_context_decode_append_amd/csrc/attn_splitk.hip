@@ -310,12 +310,13 @@ __device__ __forceinline__ void append_token_partial(const SplitArgs &a, int g, 
 // second wave would use, so one wave per SIMD).
 // fp16 (T = 1 only): a step's raw K and V take 128 VGPRs, one workgroup per
 // CU (the split plan's target anyway).
-template <bool QF32, int FMT, bool NT, int T, bool STREAM>
-__global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void attn_splitk_kernel(const SplitArgs a) {
+template <bool QF32, int FMT, bool NT, int T, bool STREAM, int W = kWaves>
+__global__ __launch_bounds__(W * 64, (W == kWaves && T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void attn_splitk_kernel(
+    const SplitArgs a) {
   constexpr int kAux = NT ? 2 : 0;  // buffer-load cache policy bits: 2 = nt
-  __shared__ __attribute__((aligned(16))) float lds_o[kWaves * 16 * 64 * 4];  // wave states, accumulator layout
-  __shared__ __attribute__((aligned(16))) float lds_m[kWaves * 16];
-  __shared__ __attribute__((aligned(16))) float lds_l[kWaves * 16];
+  __shared__ __attribute__((aligned(16))) float lds_o[W * 16 * 64 * 4];  // wave states, accumulator layout
+  __shared__ __attribute__((aligned(16))) float lds_m[W * 16];
+  __shared__ __attribute__((aligned(16))) float lds_l[W * 16];
   constexpr bool kF16 = FMT == KV_FMT_F16;                 // K and V as fp16
   constexpr bool kInt8K = FMT == KV_FMT_INT8 || FMT == KV_FMT_K8V4;   // K as INT8 codes
   constexpr bool kQ4V = FMT == KV_FMT_Q4_0 || FMT == KV_FMT_K8V4;     // V as rotated q4_0
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
   // length (verify: every pass reads the one table up to the longest row)
   const int32_t *const ptab = a.batch ? a.pts[pass] : a.pt;
   const int c_end = min(a.batch ? a.limits[pass] : a.max_limit, c_begin + a.steps_per_split * kStep);
-  const int stride = kWaves * kStep;
+  const int stride = W * kStep;
   const int c_first = c_begin + wave * kStep;
   const bool has_work = c_first < c_end;
   // last step start of this wave (wave-uniform)
@@ -546,7 +547,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
         }
       __syncthreads();
       const int rows_t = min(16, rows_here - 16 * t);  // valid rows of the tile (wave-uniform)
-      for (int r = wave; r < rows_t; r += kWaves) {
+      for (int r = wave; r < rows_t; r += W) {
         f32x4 y4 = *reinterpret_cast<const f32x4 *>(&qs[r * kQs + 4 * lane]);
         float y[4] = {y4[0], y4[1], y4[2], y4[3]};
         fwht256_lane4(y, lane);
@@ -930,21 +931,21 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
     __syncthreads();
     // two rows at a time, so their dependency chains (LDS reads, the FWHT's
     // cross-lane stages) overlap
-    for (int r0 = wave; r0 < rows_t; r0 += 2 * kWaves) {
-      const int nr = r0 + kWaves < rows_t ? 2 : 1;
+    for (int r0 = wave; r0 < rows_t; r0 += 2 * W) {
+      const int nr = r0 + W < rows_t ? 2 : 1;
       float y[2][4], M[2], Ls[2];
       for (int k = 0; k < 2; k++) {
-        const int r = k < nr ? r0 + kWaves * k : r0;
-        float mw[kWaves], lw[kWaves];
-        for (int w = 0; w < kWaves; w++) {
+        const int r = k < nr ? r0 + W * k : r0;
+        float mw[W], lw[W];
+        for (int w = 0; w < W; w++) {
           mw[w] = lds_m[w * 16 + r];
           lw[w] = lds_l[w * 16 + r];
         }
         M[k] = mw[0];
-        for (int w = 1; w < kWaves; w++) M[k] = fmaxf(M[k], mw[w]);
+        for (int w = 1; w < W; w++) M[k] = fmaxf(M[k], mw[w]);
         Ls[k] = 0.f;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int w = 0; w < kWaves; w++) {
+        for (int w = 0; w < W; w++) {
           const float f = fast_exp2(mw[w] - M[k]);
           Ls[k] += lw[w] * f;
           acc += f * *reinterpret_cast<const f32x4 *>(&lds_o[(w * 16 + r) * 256 + row_swz(4 * lane)]);
@@ -953,7 +954,7 @@ __global__ __launch_bounds__(256, (T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void at
       }
       if (kQ4V) fwht_hi_x2(y[0], y[1], lane);  // strides 64, 128; the combine does the rest
       for (int k = 0; k < nr; k++) {
-        const size_t prow = sp * rows_total + row_base + 16 * t + r0 + kWaves * k;
+        const size_t prow = sp * rows_total + row_base + 16 * t + r0 + W * k;
         *reinterpret_cast<f32x4 *>(a.part_o + prow * 256 + 4 * lane) = f32x4{y[k][0], y[k][1], y[k][2], y[k][3]};
         if (lane == 0) a.part_ml[prow] = make_float2(M[k], Ls[k]);
       }
@@ -1207,6 +1208,20 @@ int launch_attn_splitk(const AttnCall &c) {
     if (int e = launch_status()) return e;
   }
   const bool nt_k = nt && !stream;
+  // The int8 format with one 16-row tile runs eight waves per workgroup
+  // (two per SIMD) once a split has at least 12 steps: its 1,056-byte cells
+  // leave a wave per SIMD short of loads in flight (measured: 6-16 % faster
+  // from 49,152 cells on, equal at 32,768; slower for the other formats).
+  // A streamed call chooses the same way, so its result stays bitwise the
+  // resident one.
+  if (pool->fmt == KV_FMT_INT8 && T == 1 && !qf32 && plan.steps_per_split >= 12) {
+    if (stream)
+      launch((attn_splitk_kernel<false, KV_FMT_INT8, false, 1, true, 8>), grid, dim3(512), c.stream, a);
+    else if (nt_k)
+      launch((attn_splitk_kernel<false, KV_FMT_INT8, true, 1, false, 8>), grid, dim3(512), c.stream, a);
+    else
+      launch((attn_splitk_kernel<false, KV_FMT_INT8, false, 1, false, 8>), grid, dim3(512), c.stream, a);
+  } else
   switch ((((pool->fmt * 2 + (stream ? 1 : 0)) * 4 + (qf32 ? 2 : 0) + (nt_k ? 1 : 0)) << 2) + T) {
 #define K8V4_SPLIT_CASE(F, S, Q, N, T_) \
   case (((F * 2 + (S ? 1 : 0)) * 4 + (Q ? 2 : 0) + (N ? 1 : 0)) << 2) + T_: \

@@ -228,3 +228,33 @@ def test_copy_skips_out_of_range_entries(k8, dev):
             blk = r[p * nb:(p + 1) * nb]
             want = 0x44 if p == 6 else 0x55
             assert bool((blk == want).all()), (p, want)
+
+
+def test_streamed_int8_long_context_equals_resident_bitwise(k8, dev):
+    """The int8 format's decode runs eight waves per workgroup once a split
+    has at least 12 steps (65,536 cells: 16); the streamed call makes the
+    same choice, so with half the pages read from the host mirror its output
+    is still bitwise the resident call's, at that length and below the
+    switch (32,768 cells)."""
+    import torch
+    P, ctx, W = 256, 65536, 128
+    n_table = ctx // P
+    say("streamed int8 at 65,536 cells")
+    mt = synth.page_table(81, n_table, n_table)
+    s = k8.KvStream(1, W, n_table, P, t_(mt, dev), fill=0)
+    t_res = synth.page_table(82, n_table, n_table)
+    res = k8.KvPool(1, n_table, P, 2, device=dev, fill=0)
+    g_res = t_(t_res, dev)
+    for c, st in enumerate(range(0, ctx, synth.CHUNK)):
+        kk, vv = synth.kv_chunk_device(81, 0, c, synth.CHUNK, 2, 256, dev)
+        k8.kv_stream_append(s, kk, vv, st)
+        k8.kv_append(res, g_res, kk, vv, st)
+    k8.kv_stream_fetch(s, n_table - W, W)
+    q = synth.queries_device(81, 0, 0, 1, 16, 256, dev)[0]
+    ws = k8.attn_workspace(res, 1, ctx)
+    for nc in (ctx, 32768):
+        a = k8.attn_decode(res, g_res, q, nc, ws).cpu().numpy()
+        b = k8.attn_decode_stream(s, q, nc, ws).cpu().numpy()
+        torch.cuda.synchronize()
+        assert np.isfinite(a).all()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), nc
