@@ -310,6 +310,8 @@ __device__ __forceinline__ void append_token_partial(const SplitArgs &a, int g, 
 // second wave would use, so one wave per SIMD).
 // fp16 (T = 1 only): a step's raw K and V take 128 VGPRs, one workgroup per
 // CU (the split plan's target anyway).
+// W: waves per workgroup (4, one per SIMD; the int8 format's one-tile
+// decode of long contexts takes 8, see the launch).
 template <bool QF32, int FMT, bool NT, int T, bool STREAM, int W = kWaves>
 __global__ __launch_bounds__(W * 64, (W == kWaves && T == 1 && FMT != KV_FMT_F16) ? 2 : 1) void attn_splitk_kernel(
     const SplitArgs a) {
