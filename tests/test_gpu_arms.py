@@ -137,6 +137,38 @@ def test_arm_verify_one_row_equals_decode_bitwise(k8, dev, arm_tiny):
     assert np.array_equal(a.view(np.uint32), b[0].view(np.uint32))
 
 
+@pytest.mark.parametrize("fmt", [FMT_INT8, FMT_Q4_0, FMT_F16])
+def test_arm_decode_batch_parity(orc, k8, dev, fmt):
+    """attn_decode_batch over a pool of each comparison format: three
+    sequences with their own permuted tables and lengths (one of them a single
+    cell), each output against the oracle and against attn_decode alone."""
+    say(f"arm decode batch fmt={fmt}")
+    lens, P, per = [700, 1, 333], 16, 48
+    n_pages = len(lens) * per + 2
+    perm = synth.page_table(61, n_pages, n_pages)
+    gpool = k8.KvPool(fmt, n_pages, P, 2, device=dev, fill=0xA5)
+    opool = orc.OraclePool(fmt, n_pages, P, 2, sentinel=0xA5)
+    tabs, gtabs = [], []
+    for b, n in enumerate(lens):
+        pt = np.ascontiguousarray(perm[b * per:(b + 1) * per])
+        tabs.append(pt)
+        gtabs.append(t_(pt, dev))
+        k, v = synth.kv_tokens(70 + b, 0, 0, n, 2, 256, np.float16)
+        k8.kv_append(gpool, gtabs[b], t_(k, dev), t_(v, dev), 0)
+        opool.append(pt, k, v, 0)
+    q = synth.queries(62, 0, 0, len(lens), 16, 256, np.float16)
+    ws = k8.attn_workspace(gpool, len(lens), max(lens))
+    out = k8.attn_decode_batch(gpool, gtabs, t_(q, dev), lens, ws).cpu().numpy()
+    for b, n in enumerate(lens):
+        ref = orc.attention_from_pool(opool, tabs[b], q[b:b + 1], [n])[0]
+        ws1 = k8.attn_workspace(gpool, 1, n)
+        one = k8.attn_decode(gpool, gtabs[b], t_(q[b], dev), n, ws1).cpu().numpy()
+        err, err1 = rel_err(out[b], ref), rel_err(out[b], one)
+        say(f"  seq {b} len {n}: rel err {err:.3e}, vs single decode {err1:.3e}")
+        assert err <= TOL
+        assert err1 <= TOL
+
+
 @pytest.mark.parametrize("v_scale", [1e-3, 3e-4])
 def test_int8_small_values_decode_and_verify(orc, k8, dev, v_scale):
     """int8 format with V ~ N(0, v_scale^2): the V scales (max|V| / 127,
