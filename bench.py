@@ -89,8 +89,16 @@ def spread_us(ts):
     return {"launches": len(s), "median_us": q(0.5), "p10_us": q(0.1), "p90_us": q(0.9)}
 
 
+LEAD_CYCLES_PER_LAUNCH = 300_000
+
+
 def timed_launches(torch, k8, fn, n):
-    """Run fn() n times, each single kernel bracketed by start/stop events."""
+    """Run fn() n times, each single kernel bracketed by start/stop events.
+    A spin kernel enqueued first holds the GPU until the host has queued all
+    n calls, so the launches run back to back, as the kernels of a replayed
+    graph do, not each after an idle gap the host's enqueue time left (the
+    launch after such a gap runs up to ~20 % slower)."""
+    torch.cuda._sleep(LEAD_CYCLES_PER_LAUNCH * n)
     pairs = []
     for i in range(n):
         e0 = torch.cuda.Event(enable_timing=True)
